@@ -1,0 +1,182 @@
+"""Python binding of librece (RECE / SCE reduced cross-entropy on MI355X).
+
+Argument marshalling only: every step of the loss runs in librece's HIP
+kernels.  PyTorch supplies device memory (tensors) and the current stream.
+There is no fallback: if librece.so is missing or cannot be loaded, every
+entry point raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librece.so")
+
+RECE_F32, RECE_BF16 = 0, 1
+RECE_VARIANT_RECE, RECE_VARIANT_SCE = 0, 1
+FLAG_VALIDATE_IDS, FLAG_KEEP_STAGES = 1, 2
+
+STAGES = {
+    "bucket_x": 0, "bucket_y": 1, "perm_x": 2, "perm_y": 3, "thresh_id": 4,
+    "thresh_logit": 5, "neg_ids": 6, "lse": 7, "counters": 8,
+}
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small",
+          4: "HIP runtime error", 5: "device check failed", 6: "internal error"}
+
+EXPORTED = ["rece_plan", "rece_plan_destroy", "rece_workspace_bytes", "rece_forward",
+            "rece_backward", "rece_export", "rece_export_bytes", "rece_check",
+            "rece_status_string", "rece_last_error", "rece_version"]
+
+
+class ReceConfig(ctypes.Structure):
+    _fields_ = [("s", ctypes.c_int64), ("C", ctypes.c_int64), ("d", ctypes.c_int32),
+                ("n_b", ctypes.c_int32), ("n_c", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("rounds", ctypes.c_int32), ("b_x", ctypes.c_int32), ("b_y", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("variant", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+class ReceError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"librece: {STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load librece.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"librece.so not found at {LIB_PATH}; run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)
+        L.rece_plan.argtypes = [ctypes.POINTER(ReceConfig), ctypes.POINTER(vp)]
+        L.rece_plan_destroy.argtypes = [vp]
+        L.rece_workspace_bytes.argtypes = [vp, sz, sz]
+        L.rece_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.rece_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.rece_export.argtypes = [vp, vp, vp, i32, i32, vp]
+        L.rece_export_bytes.argtypes = [vp, i32, sz]
+        L.rece_check.argtypes = [vp, vp, vp]
+        L.rece_status_string.argtypes = [i32]
+        L.rece_status_string.restype = ctypes.c_char_p
+        L.rece_last_error.restype = ctypes.c_char_p
+        L.rece_version.restype = ctypes.c_char_p
+        for name in ("rece_plan", "rece_plan_destroy", "rece_workspace_bytes", "rece_forward",
+                     "rece_backward", "rece_export", "rece_export_bytes", "rece_check"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise ReceError(status, lib().rece_last_error().decode())
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None) -> int:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+class Plan:
+    """An immutable librece plan (host only) plus its workspace sizes."""
+
+    def __init__(self, s: int, C: int, d: int, n_b: int, n_c: int, k: int, rounds: int = 1,
+                 dtype: str = "bf16", variant: str = "rece", b_x: int = 0, b_y: int = 0,
+                 keep_stages: bool = False, validate_ids: bool = False):
+        self.cfg = ReceConfig(s, C, d, n_b, n_c, k, rounds, b_x, b_y,
+                              RECE_BF16 if dtype == "bf16" else RECE_F32,
+                              RECE_VARIANT_SCE if variant == "sce" else RECE_VARIANT_RECE,
+                              (FLAG_KEEP_STAGES if keep_stages else 0)
+                              | (FLAG_VALIDATE_IDS if validate_ids else 0))
+        self.dtype = dtype
+        self._h = ctypes.c_void_p()
+        _check(lib().rece_plan(ctypes.byref(self.cfg), ctypes.byref(self._h)))
+        sc, sv = ctypes.c_size_t(), ctypes.c_size_t()
+        _check(lib().rece_workspace_bytes(self._h, ctypes.byref(sc), ctypes.byref(sv)))
+        self.scratch_bytes, self.saved_bytes = sc.value, sv.value
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.rece_plan_destroy(h)
+            self._h = None
+
+    # -- argument checks (shapes, dtypes, devices); the library checks pointers again
+    def _check_inputs(self, X, Y, pos, B=None):
+        import torch
+        c = self.cfg
+        want = torch.bfloat16 if self.dtype == "bf16" else torch.float32
+        for name, t, shape in (("X", X, (c.s, c.d)), ("Y", Y, (c.C, c.d))):
+            if t.dtype != want or tuple(t.shape) != shape or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous CUDA {want} tensor of shape {shape}")
+        if pos.dtype != torch.int32 or tuple(pos.shape) != (c.s,) or not pos.is_cuda:
+            raise ValueError(f"pos must be a CUDA int32 tensor of shape ({c.s},)")
+        if B is not None:
+            shape = (c.rounds, c.d, c.n_b) if c.variant == RECE_VARIANT_RECE else (c.d, c.n_b)
+            if B.dtype != want or tuple(B.shape) != shape or not B.is_cuda or not B.is_contiguous():
+                raise ValueError(f"B must be a contiguous CUDA {want} tensor of shape {shape}")
+
+    def workspace(self, device="cuda"):
+        import torch
+        scratch = torch.empty(max(self.scratch_bytes, 16), dtype=torch.uint8, device=device)
+        saved = torch.empty(max(self.saved_bytes, 16), dtype=torch.uint8, device=device)
+        return scratch, saved
+
+    def forward(self, X, Y, pos, B, scratch=None, saved=None, loss_pp=True, stream=None):
+        """Returns (loss [1], loss_pp [s] or None, scratch, saved)."""
+        import torch
+        self._check_inputs(X, Y, pos, B)
+        if scratch is None or saved is None:
+            scratch, saved = self.workspace(X.device)
+        loss = torch.empty(1, dtype=torch.float32, device=X.device)
+        lpp = torch.empty(self.cfg.s, dtype=torch.float32, device=X.device) if loss_pp else None
+        _check(lib().rece_forward(self._h, _stream(stream), _ptr(X), _ptr(Y), _ptr(pos), _ptr(B),
+                                  _ptr(scratch), _ptr(saved), _ptr(loss), _ptr(lpp)))
+        return loss, lpp, scratch, saved
+
+    def backward(self, X, Y, pos, scratch, saved, dloss=None, dloss_pp=None, dX=None, dY=None,
+                 stream=None):
+        """Returns (dX [s, d] float32, dY [C, d] float32)."""
+        import torch
+        self._check_inputs(X, Y, pos)
+        c = self.cfg
+        if dloss is None and dloss_pp is None:
+            dloss = torch.ones(1, dtype=torch.float32, device=X.device)
+        if dX is None:
+            dX = torch.empty((c.s, c.d), dtype=torch.float32, device=X.device)
+        if dY is None:
+            dY = torch.empty((c.C, c.d), dtype=torch.float32, device=X.device)
+        _check(lib().rece_backward(self._h, _stream(stream), _ptr(X), _ptr(Y), _ptr(pos),
+                                   _ptr(dloss), _ptr(dloss_pp), _ptr(scratch), _ptr(saved),
+                                   _ptr(dX), _ptr(dY)))
+        return dX, dY
+
+    def export(self, saved, stage: str, round: int = 0, stream=None):
+        import torch
+        st = STAGES[stage]
+        nb = ctypes.c_size_t()
+        _check(lib().rece_export_bytes(self._h, st, ctypes.byref(nb)))
+        dt = {"thresh_logit": torch.float64, "lse": torch.float32, "counters": torch.int32}.get(stage, torch.int32)
+        n = nb.value // torch.empty(0, dtype=dt).element_size()
+        out = torch.empty(n, dtype=dt, device=saved.device)
+        _check(lib().rece_export(self._h, _stream(stream), _ptr(saved), st, round, _ptr(out)))
+        if stage == "neg_ids":
+            out = out.view(self.cfg.s, max(self.cfg.k, 1))
+        return out
+
+    def check(self, saved, stream=None):
+        _check(lib().rece_check(self._h, _stream(stream), _ptr(saved)))
+
+
+def version() -> str:
+    return lib().rece_version().decode()

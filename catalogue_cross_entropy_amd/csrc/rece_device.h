@@ -1,0 +1,168 @@
+// Device helpers shared by the librece kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rece {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Storage tag of a bfloat16 input element (raw bits).
+struct bf16 {
+  uint16_t bits;
+};
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16 v) { return __uint_as_float((uint32_t)v.bits << 16); }
+
+constexpr int WAVE = 64;
+constexpr float NEG_INF = -__builtin_huge_valf();
+
+__device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int l = lane_id();
+  return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+__device__ __forceinline__ int popc(uint64_t m) { return __popcll(m); }
+
+// Orders LDS traffic between lanes of one wave (no hardware barrier needed:
+// a wave executes its LDS instructions in order; this stops compiler motion).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fminf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ float wave_sumf(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Order-preserving map float -> uint32 (larger float -> larger key; -0 < +0).
+__device__ __forceinline__ uint32_t fkey(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Float64 scalar product summed in coordinate order t = 0..d-1.  Products of
+// float32 / bfloat16 values are exact in float64, so fma(a, b, acc) equals
+// acc + a*b rounded once: this is the reference value every selection uses.
+template <class E>
+__device__ double exact_dot(const E* __restrict__ a, const E* __restrict__ b, int d) {
+  double acc = 0.0;
+  for (int t = 0; t < d; ++t) acc = fma((double)to_f32(a[t]), (double)to_f32(b[t]), acc);
+  return acc;
+}
+
+// Outward rounding of a float64 interval end to float32.
+__device__ __forceinline__ float f_down(double v) { return __double2float_rd(v); }
+__device__ __forceinline__ float f_up(double v) { return __double2float_ru(v); }
+
+// ---------------------------------------------------------------------------
+// Matrix-core fragments.  A 16x16 output block C[m][n] = sum_t A[m][t] * B[n][t]
+// over D coordinates.  Lane l supplies row m = l % 16 of A and row n = l % 16 of
+// B (both "row = vector" layout); the block result lands as
+// C[4*(l/16) + v][l % 16] in element v of the lane's f32x4.
+//   bf16: v_mfma_f32_16x16x32_bf16, k-step of 32 coordinates, lane holds the 8
+//         coordinates 32*ks + 8*(l/16) .. +7 of its row (same map for A and B, so
+//         the pairing of coordinates is right whatever the unit's internal order);
+//   f32:  v_mfma_f32_16x16x4_f32, k-step of 4, lane holds coordinate 4*ks + l/16.
+// ---------------------------------------------------------------------------
+template <class E, int D> struct Frag;
+
+template <int D> struct Frag<bf16, D> {
+  static constexpr int KS = D / 32;
+  bf16x8 v[KS];
+  // Load the fragment of one row (row pointer; nullptr -> zeros).
+  __device__ __forceinline__ void load_global(const bf16* row) {
+    const int q = lane_id() >> 4;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (row) {
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(row + 32 * ks + 8 * q);
+        v[ks] = __builtin_bit_cast(bf16x8, raw);
+      } else {
+        v[ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+      }
+    }
+  }
+  __device__ __forceinline__ void load_lds(const bf16* row) {
+    const int q = lane_id() >> 4;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(row + 32 * ks + 8 * q);
+      v[ks] = __builtin_bit_cast(bf16x8, raw);
+    }
+  }
+};
+
+template <int D> struct Frag<float, D> {
+  static constexpr int KS = D / 4;
+  float v[KS];
+  __device__ __forceinline__ void load_global(const float* row) {
+    const int q = lane_id() >> 4;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) v[ks] = row ? row[4 * ks + q] : 0.0f;
+  }
+  __device__ __forceinline__ void load_lds(const float* row) {
+    const int q = lane_id() >> 4;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) v[ks] = row[4 * ks + q];
+  }
+};
+
+template <int D>
+__device__ __forceinline__ f32x4 mma_block(const Frag<bf16, D>& a, const Frag<bf16, D>& b, f32x4 acc) {
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks)
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v[ks], b.v[ks], acc, 0, 0, 0);
+  return acc;
+}
+template <int D>
+__device__ __forceinline__ f32x4 mma_block(const Frag<float, D>& a, const Frag<float, D>& b, f32x4 acc) {
+#pragma unroll
+  for (int ks = 0; ks < D / 4; ++ks)
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[ks], b.v[ks], acc, 0, 0, 0);
+  return acc;
+}
+
+// Row pitch (elements) of an LDS tile holding vectors of D coordinates.
+template <class E, int D> struct Pitch;
+template <int D> struct Pitch<bf16, D> { static constexpr int value = D + 8; };
+template <int D> struct Pitch<float, D> { static constexpr int value = D + 4; };
+
+// Chunk of sorted slot p among N slots cut into n_c chunks: floor(p * n_c / N).
+__device__ __forceinline__ int chunk_of(int64_t p, int64_t N, int n_c) {
+  return (int)((p * (int64_t)n_c) / N);
+}
+// First slot of chunk c: ceil(c * N / n_c).
+__host__ __device__ __forceinline__ int64_t chunk_start(int64_t c, int64_t N, int n_c) {
+  return (c * N + n_c - 1) / n_c;
+}
+// Is item-chunk cy in the window {cx-1, cx, cx+1} (mod n_c) of position-chunk cx?
+__device__ __forceinline__ bool in_window(int cx, int cy, int n_c) {
+  if (n_c <= 3) return true;
+  int dlt = cy - cx;
+  if (dlt < 0) dlt += n_c;
+  return dlt == 0 || dlt == 1 || dlt == n_c - 1;
+}
+
+}  // namespace rece

@@ -1,0 +1,428 @@
+// librece host side: plan validation, workspace layout and the launch sequence.
+// Every entry point is a C function returning rece_status; nothing here
+// allocates device memory or waits for the GPU (except rece_check).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "rece_internal.h"
+
+using namespace rece;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+rece_status fail(rece_status st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+rece_status hip_fail(hipError_t e, const char* where) {
+  return fail(RECE_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int bits_for(int64_t n) {   // smallest b with 2^b >= n
+  int b = 0;
+  while (((int64_t)1 << b) < n) ++b;
+  return b;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Layout {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  }
+};
+
+}  // namespace
+
+struct rece_plan_s {
+  rece_config cfg;
+  bool bf16;
+  int esize;
+  int nbits_b;
+  int selall;
+  int cap;
+  int waves_sel;
+  int tpc_sel;
+  int tpc_bwd;
+  int itiles;
+  int pos_passes;
+  float beta_coef;
+  // saved
+  size_t o_cnt, o_bx, o_by, o_px, o_ix, o_py, o_iy, o_te, o_tid, o_tlo, o_thi, o_msh, o_ssum, o_nmem, o_xnorm,
+      o_ymax, o_lse, o_lpos, o_negs, saved_bytes;
+  // scratch
+  size_t o_bt, o_bnorm, o_sort, o_part, o_pp0, o_pp1, o_ppart, scratch_bytes;
+};
+
+static rece_status validate_config(const rece_config* c) {
+  if (!c) return fail(RECE_ERR_INVALID_ARGUMENT, "config is NULL");
+  if (c->variant != RECE_VARIANT_RECE)
+    return fail(RECE_ERR_UNSUPPORTED, "only the RECE variant is available in this build");
+  if (c->s < 1) return fail(RECE_ERR_INVALID_ARGUMENT, "s must be >= 1");
+  if (c->C < 2) return fail(RECE_ERR_INVALID_ARGUMENT, "C must be >= 2");
+  if (c->s > ((int64_t)1 << 31) - 1 || c->C > ((int64_t)1 << 31) - 1)
+    return fail(RECE_ERR_UNSUPPORTED, "s and C must fit in int32");
+  if (c->d != 32 && c->d != 64 && c->d != 128 && c->d != 256)
+    return fail(RECE_ERR_UNSUPPORTED, "d must be one of 32, 64, 128, 256");
+  if (c->n_b < 1 || c->n_b > 4096) return fail(RECE_ERR_INVALID_ARGUMENT, "n_b must be in 1..4096");
+  if (c->n_c < 1 || c->n_c > c->s || c->n_c > c->C)
+    return fail(RECE_ERR_INVALID_ARGUMENT, "n_c must be in 1..min(s, C)");
+  if (c->k < 0 || c->k > c->C - 1) return fail(RECE_ERR_INVALID_ARGUMENT, "k must be in 0..C-1");
+  if (c->rounds < 1 || c->rounds > MAX_ROUNDS) return fail(RECE_ERR_INVALID_ARGUMENT, "rounds must be in 1..8");
+  if (c->dtype != RECE_F32 && c->dtype != RECE_BF16) return fail(RECE_ERR_INVALID_ARGUMENT, "unknown dtype");
+  if (c->flags & ~(RECE_FLAG_VALIDATE_IDS | RECE_FLAG_KEEP_STAGES))
+    return fail(RECE_ERR_INVALID_ARGUMENT, "unknown flag bits");
+  return RECE_OK;
+}
+
+extern "C" {
+
+rece_status rece_plan(const rece_config* cfg, rece_plan_t* out) {
+  if (!out) return fail(RECE_ERR_INVALID_ARGUMENT, "out is NULL");
+  *out = nullptr;
+  const rece_status vs = validate_config(cfg);
+  if (vs != RECE_OK) return vs;
+  rece_plan_s* p = new (std::nothrow) rece_plan_s();
+  if (!p) return fail(RECE_ERR_INTERNAL, "host allocation failed");
+  p->cfg = *cfg;
+  const rece_config& c = p->cfg;
+  const int64_t s = c.s, C = c.C;
+  const int d = c.d, r = c.rounds, k = c.k, n_c = c.n_c;
+  p->bf16 = c.dtype == RECE_BF16;
+  p->esize = p->bf16 ? 2 : 4;
+  p->nbits_b = bits_for(c.n_b);
+  const int64_t rows_chunk = (s + n_c - 1) / n_c;
+  const int64_t items_chunk = (C + n_c - 1) / n_c;
+  const int64_t wmax = n_c <= 3 ? C : std::min<int64_t>(C, 3 * items_chunk);
+  p->selall = (k >= wmax) || (n_c <= 3 && k >= C - 1);
+  // candidate list: the k kept + one tile of new entries + slack near the threshold
+  p->cap = p->selall ? 64 : (int)align_up((size_t)(k + 64 + std::max(64, k / 2)), 32);
+  p->waves_sel = 1;
+  for (int nw : {4, 2, 1}) {
+    if (select_lds_bytes(p->bf16, d, nw, p->cap) <= 128 * 1024) {
+      p->waves_sel = nw;
+      break;
+    }
+  }
+  if (select_lds_bytes(p->bf16, d, p->waves_sel, p->cap) > 160 * 1024) {
+    delete p;
+    return fail(RECE_ERR_UNSUPPORTED, "k too large for the on-chip candidate lists");
+  }
+  p->tpc_sel = (int)((rows_chunk + 16 * p->waves_sel - 1) / (16 * p->waves_sel));
+  p->tpc_bwd = (int)((rows_chunk + 63) / 64);
+  p->itiles = (int)((items_chunk + 63) / 64);
+  p->pos_passes = std::max(1, (bits_for(C) + 11) / 12);
+  // |float32 matrix-core dot - float64 coordinate-order dot| <= beta_coef * ||x|| * ||y||:
+  // d products and d additions, each with relative error at most 2^-23 (round or
+  // chop), doubled for safety; the float64 side adds d * 2^-53.
+  p->beta_coef = (float)(4.0 * (d + 2) * std::ldexp(1.0, -24) * (1.0 + 1e-6) + d * std::ldexp(1.0, -52));
+
+  Layout sv;
+  p->o_cnt = sv.take(NUM_COUNTERS * 4);
+  p->o_bx = sv.take((size_t)r * s * 4);
+  p->o_by = sv.take((size_t)r * C * 4);
+  p->o_px = sv.take((size_t)r * s * 4);
+  p->o_ix = sv.take((size_t)r * s * 4);
+  p->o_py = sv.take((size_t)r * C * 4);
+  p->o_iy = sv.take((size_t)r * C * 4);
+  p->o_te = sv.take((size_t)r * s * 8);
+  p->o_tid = sv.take((size_t)r * s * 4);
+  p->o_tlo = sv.take((size_t)r * s * 4);
+  p->o_thi = sv.take((size_t)r * s * 4);
+  p->o_msh = sv.take((size_t)r * s * 4);
+  p->o_ssum = sv.take((size_t)r * s * 4);
+  p->o_nmem = sv.take((size_t)r * s * 4);
+  p->o_xnorm = sv.take((size_t)s * 4);
+  p->o_ymax = sv.take(4);
+  p->o_lse = sv.take((size_t)s * 4);
+  p->o_lpos = sv.take((size_t)s * 4);
+  p->o_negs = (c.flags & RECE_FLAG_KEEP_STAGES) ? sv.take((size_t)r * s * std::max(k, 1) * 4) : 0;
+  p->saved_bytes = sv.off;
+
+  Layout sc;
+  p->o_bt = sc.take((size_t)r * c.n_b * d * p->esize);
+  p->o_bnorm = sc.take((size_t)r * 4);
+  const size_t sort_b = std::max({sort_scratch_bytes(s, 1 << p->nbits_b), sort_scratch_bytes(C, 1 << p->nbits_b),
+                                  sort_scratch_bytes(s, 1 << std::min(12, bits_for(C)))});
+  p->o_sort = sc.take(sort_b);
+  p->o_part = sc.take((size_t)ce_blocks(s) * 8);
+  p->o_pp0 = sc.take((size_t)s * 4);
+  p->o_pp1 = sc.take((size_t)s * 4);
+  p->o_ppart = sc.take(pos_partial_bytes(s, d));
+  p->scratch_bytes = sc.off;
+  *out = p;
+  return RECE_OK;
+}
+
+rece_status rece_plan_destroy(rece_plan_t plan) {
+  delete plan;
+  return RECE_OK;
+}
+
+rece_status rece_workspace_bytes(rece_plan_t plan, size_t* scratch_bytes, size_t* saved_bytes) {
+  if (!plan) return fail(RECE_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (scratch_bytes) *scratch_bytes = plan->scratch_bytes;
+  if (saved_bytes) *saved_bytes = plan->saved_bytes;
+  return RECE_OK;
+}
+
+#define RECE_HIP(call, where)                 \
+  do {                                         \
+    hipError_t e_ = (call);                    \
+    if (e_ != hipSuccess) return hip_fail(e_, where); \
+  } while (0)
+
+rece_status rece_forward(rece_plan_t plan, void* stream, const void* X, const void* Y, const int32_t* pos,
+                         const void* B, void* scratch, void* saved, float* loss, float* loss_pp) {
+  if (!plan) return fail(RECE_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (!X || !Y || !pos || !B || !scratch || !saved || !loss)
+    return fail(RECE_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  if (!aligned16(X) || !aligned16(Y) || !aligned16(B) || !aligned16(scratch) || !aligned16(saved))
+    return fail(RECE_ERR_INVALID_ARGUMENT, "X, Y, B, scratch and saved must be 16-byte aligned");
+  const rece_plan_s& p = *plan;
+  const rece_config& c = p.cfg;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* sv = static_cast<char*>(saved);
+  char* sc = static_cast<char*>(scratch);
+  const int64_t s = c.s, C = c.C;
+  const int d = c.d;
+  uint32_t* counters = reinterpret_cast<uint32_t*>(sv + p.o_cnt);
+  float* ymax = reinterpret_cast<float*>(sv + p.o_ymax);
+  float* xnorm = reinterpret_cast<float*>(sv + p.o_xnorm);
+  float* bnorm = reinterpret_cast<float*>(sc + p.o_bnorm);
+  void* Bt = sc + p.o_bt;
+
+  RECE_HIP(launch_fill_u32(counters, 0u, NUM_COUNTERS, st), "clear counters");
+  RECE_HIP(launch_fill_u32(reinterpret_cast<uint32_t*>(ymax), 0u, 1, st), "clear norm max");
+  RECE_HIP(launch_prep_b(p.bf16, d, B, c.rounds, c.n_b, Bt, bnorm, st), "prepare random vectors");
+
+  for (int rho = 0; rho < c.rounds; ++rho) {
+    int32_t* bx = reinterpret_cast<int32_t*>(sv + p.o_bx) + (int64_t)rho * s;
+    int32_t* by = reinterpret_cast<int32_t*>(sv + p.o_by) + (int64_t)rho * C;
+    int32_t* px = reinterpret_cast<int32_t*>(sv + p.o_px) + (int64_t)rho * s;
+    int32_t* ix = reinterpret_cast<int32_t*>(sv + p.o_ix) + (int64_t)rho * s;
+    int32_t* py = reinterpret_cast<int32_t*>(sv + p.o_py) + (int64_t)rho * C;
+    int32_t* iy = reinterpret_cast<int32_t*>(sv + p.o_iy) + (int64_t)rho * C;
+    const void* Btr = static_cast<const char*>(Bt) + (size_t)rho * c.n_b * d * p.esize;
+    RECE_HIP(launch_project_argmax(p.bf16, d, X, s, Btr, c.n_b, bnorm + rho, p.beta_coef, bx,
+                                   rho == 0 ? xnorm : nullptr, nullptr, counters, st),
+             "bucket positions");
+    RECE_HIP(launch_project_argmax(p.bf16, d, Y, C, Btr, c.n_b, bnorm + rho, p.beta_coef, by, nullptr,
+                                   rho == 0 ? reinterpret_cast<uint32_t*>(ymax) : nullptr, counters, st),
+             "bucket items");
+    RECE_HIP(launch_counting_sort(bx, nullptr, s, 0, p.nbits_b, sc + p.o_sort, px, ix, st), "sort positions");
+    RECE_HIP(launch_counting_sort(by, nullptr, C, 0, p.nbits_b, sc + p.o_sort, py, iy, st), "sort items");
+
+    SelectArgs a{};
+    a.X = X;
+    a.Y = Y;
+    a.pos = pos;
+    a.perm_x = px;
+    a.perm_y = py;
+    a.inv_x = reinterpret_cast<const int32_t*>(sv + p.o_ix);
+    a.inv_y = reinterpret_cast<const int32_t*>(sv + p.o_iy);
+    a.s = s;
+    a.C = C;
+    a.n_c = c.n_c;
+    a.k = c.k;
+    a.cap = p.cap;
+    a.rho = rho;
+    a.selall = p.selall;
+    a.tiles_per_chunk = p.tpc_sel;
+    a.beta_coef = p.beta_coef;
+    a.xnorm = xnorm;
+    a.ynorm_max = ymax;
+    a.thr_e = reinterpret_cast<double*>(sv + p.o_te);
+    a.thr_id = reinterpret_cast<int32_t*>(sv + p.o_tid);
+    a.thr_lo = reinterpret_cast<float*>(sv + p.o_tlo);
+    a.thr_hi = reinterpret_cast<float*>(sv + p.o_thi);
+    a.mshift = reinterpret_cast<float*>(sv + p.o_msh);
+    a.ssum = reinterpret_cast<float*>(sv + p.o_ssum);
+    a.nmem = reinterpret_cast<int32_t*>(sv + p.o_nmem);
+    a.negs = p.o_negs ? reinterpret_cast<int32_t*>(sv + p.o_negs) : nullptr;
+    a.counters = counters;
+    RECE_HIP(launch_select(p.bf16, d, p.waves_sel, a, st), "chunk logits and top-k");
+  }
+
+  CeArgs ce{};
+  ce.X = X;
+  ce.Y = Y;
+  ce.pos = pos;
+  ce.s = s;
+  ce.C = C;
+  ce.rounds = c.rounds;
+  ce.mshift = reinterpret_cast<const float*>(sv + p.o_msh);
+  ce.ssum = reinterpret_cast<const float*>(sv + p.o_ssum);
+  ce.nmem = reinterpret_cast<const int32_t*>(sv + p.o_nmem);
+  ce.lse = reinterpret_cast<float*>(sv + p.o_lse);
+  ce.lpos = reinterpret_cast<float*>(sv + p.o_lpos);
+  ce.loss_pp = loss_pp;
+  ce.partial = reinterpret_cast<float*>(sc + p.o_part);
+  ce.counters = counters;
+  ce.validate = (c.flags & RECE_FLAG_VALIDATE_IDS) ? 1 : 0;
+  RECE_HIP(launch_ce(p.bf16, d, ce, loss, st), "loss");
+  return RECE_OK;
+}
+
+rece_status rece_backward(rece_plan_t plan, void* stream, const void* X, const void* Y, const int32_t* pos,
+                          const float* dloss, const float* dloss_pp, void* scratch, const void* saved, float* dX,
+                          float* dY) {
+  if (!plan) return fail(RECE_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (!X || !Y || !pos || !scratch || !saved || !dX || !dY || (!dloss && !dloss_pp))
+    return fail(RECE_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  if (!aligned16(X) || !aligned16(Y) || !aligned16(scratch) || !aligned16(saved) || !aligned16(dX) ||
+      !aligned16(dY))
+    return fail(RECE_ERR_INVALID_ARGUMENT, "X, Y, dX, dY, scratch and saved must be 16-byte aligned");
+  const rece_plan_s& p = *plan;
+  const rece_config& c = p.cfg;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const char* sv = static_cast<const char*>(saved);
+  char* sc = static_cast<char*>(scratch);
+  const int64_t s = c.s, C = c.C;
+  const int d = c.d;
+
+  BwdArgs b{};
+  b.X = X;
+  b.Y = Y;
+  b.pos = pos;
+  b.inv_x = reinterpret_cast<const int32_t*>(sv + p.o_ix);
+  b.inv_y = reinterpret_cast<const int32_t*>(sv + p.o_iy);
+  b.s = s;
+  b.C = C;
+  b.n_c = c.n_c;
+  b.tiles_per_chunk = p.tpc_bwd;
+  b.thr_e = reinterpret_cast<const double*>(sv + p.o_te);
+  b.thr_id = reinterpret_cast<const int32_t*>(sv + p.o_tid);
+  b.thr_lo = reinterpret_cast<const float*>(sv + p.o_tlo);
+  b.thr_hi = reinterpret_cast<const float*>(sv + p.o_thi);
+  b.lse = reinterpret_cast<const float*>(sv + p.o_lse);
+  b.lpos = reinterpret_cast<const float*>(sv + p.o_lpos);
+  b.dloss = dloss;
+  b.dloss_pp = dloss_pp;
+  b.dX = dX;
+  b.dY = dY;
+  b.counters = reinterpret_cast<uint32_t*>(const_cast<char*>(sv) + p.o_cnt);
+  for (int rho = 0; rho < c.rounds; ++rho) {
+    b.rho = rho;
+    b.perm_x = reinterpret_cast<const int32_t*>(sv + p.o_px) + (int64_t)rho * s;
+    b.perm_y = reinterpret_cast<const int32_t*>(sv + p.o_py) + (int64_t)rho * C;
+    RECE_HIP(launch_bwd_rows(p.bf16, d, 4, b, st), "dX");
+    RECE_HIP(launch_bwd_items(p.bf16, d, 4, b, p.itiles, st), "dY");
+  }
+  // positives: LSD counting sort of positions by positive id, then the segmented reduction
+  int32_t* bufs[2] = {reinterpret_cast<int32_t*>(sc + p.o_pp0), reinterpret_cast<int32_t*>(sc + p.o_pp1)};
+  const int total_bits = std::max(1, bits_for(C));
+  const int32_t* sorted = nullptr;
+  for (int pass = 0, shift = 0; shift < total_bits; ++pass, shift += 12) {
+    const int nb = std::min(12, total_bits - shift);
+    int32_t* outp = bufs[pass & 1];
+    RECE_HIP(launch_counting_sort(pos, sorted, s, shift, nb, sc + p.o_sort, outp, nullptr, st), "sort positives");
+    sorted = outp;
+  }
+  RECE_HIP(launch_pos_dy(p.bf16, d, b, sorted, reinterpret_cast<float*>(sc + p.o_ppart), st), "positive dY");
+  return RECE_OK;
+}
+
+rece_status rece_export_bytes(rece_plan_t plan, int stage, size_t* bytes) {
+  if (!plan || !bytes) return fail(RECE_ERR_INVALID_ARGUMENT, "NULL argument");
+  const rece_config& c = plan->cfg;
+  switch (stage) {
+    case RECE_STAGE_BUCKET_X:
+    case RECE_STAGE_PERM_X:
+    case RECE_STAGE_THRESH_ID:
+    case RECE_STAGE_LSE:
+      *bytes = (size_t)c.s * 4;
+      break;
+    case RECE_STAGE_BUCKET_Y:
+    case RECE_STAGE_PERM_Y:
+      *bytes = (size_t)c.C * 4;
+      break;
+    case RECE_STAGE_THRESH_LOGIT:
+      *bytes = (size_t)c.s * 8;
+      break;
+    case RECE_STAGE_NEG_IDS:
+      *bytes = plan->o_negs ? (size_t)c.s * std::max(c.k, 1) * 4 : 0;
+      break;
+    case RECE_STAGE_COUNTERS:
+      *bytes = NUM_COUNTERS * 4;
+      break;
+    default:
+      return fail(RECE_ERR_INVALID_ARGUMENT, "unknown stage");
+  }
+  return RECE_OK;
+}
+
+rece_status rece_export(rece_plan_t plan, void* stream, const void* saved, int stage, int round, void* dst) {
+  if (!plan || !saved || !dst) return fail(RECE_ERR_INVALID_ARGUMENT, "NULL argument");
+  const rece_plan_s& p = *plan;
+  const rece_config& c = p.cfg;
+  if (round < 0 || round >= c.rounds) return fail(RECE_ERR_INVALID_ARGUMENT, "round out of range");
+  size_t bytes = 0;
+  const rece_status bs = rece_export_bytes(plan, stage, &bytes);
+  if (bs != RECE_OK) return bs;
+  if (bytes == 0) return fail(RECE_ERR_INVALID_ARGUMENT, "stage not kept (plan without RECE_FLAG_KEEP_STAGES)");
+  const char* sv = static_cast<const char*>(saved);
+  const int64_t s = c.s, C = c.C;
+  size_t off = 0;
+  switch (stage) {
+    case RECE_STAGE_BUCKET_X: off = p.o_bx + (size_t)round * s * 4; break;
+    case RECE_STAGE_BUCKET_Y: off = p.o_by + (size_t)round * C * 4; break;
+    case RECE_STAGE_PERM_X: off = p.o_px + (size_t)round * s * 4; break;
+    case RECE_STAGE_PERM_Y: off = p.o_py + (size_t)round * C * 4; break;
+    case RECE_STAGE_THRESH_ID: off = p.o_tid + (size_t)round * s * 4; break;
+    case RECE_STAGE_THRESH_LOGIT: off = p.o_te + (size_t)round * s * 8; break;
+    case RECE_STAGE_NEG_IDS: off = p.o_negs + (size_t)round * s * std::max(c.k, 1) * 4; break;
+    case RECE_STAGE_LSE: off = p.o_lse; break;
+    case RECE_STAGE_COUNTERS: off = p.o_cnt; break;
+    default: return fail(RECE_ERR_INVALID_ARGUMENT, "unknown stage");
+  }
+  RECE_HIP(hipMemcpyAsync(dst, sv + off, bytes, hipMemcpyDeviceToDevice, reinterpret_cast<hipStream_t>(stream)),
+           "export");
+  return RECE_OK;
+}
+
+rece_status rece_check(rece_plan_t plan, void* stream, const void* saved) {
+  if (!plan || !saved) return fail(RECE_ERR_INVALID_ARGUMENT, "NULL argument");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  RECE_HIP(hipStreamSynchronize(st), "stream synchronize");
+  uint32_t cnt[NUM_COUNTERS];
+  RECE_HIP(hipMemcpy(cnt, static_cast<const char*>(saved) + plan->o_cnt, sizeof(cnt), hipMemcpyDeviceToHost),
+           "read counters");
+  if (cnt[CNT_ERROR] & ERRBIT_BAD_ID) return fail(RECE_ERR_DEVICE_CHECK, "positive id out of range [0, C)");
+  if (cnt[CNT_ERROR] & ERRBIT_OVERFLOW)
+    return fail(RECE_ERR_DEVICE_CHECK, "candidate list overflow (too many near-equal logits at the k-th place)");
+  return RECE_OK;
+}
+
+const char* rece_status_string(rece_status status) {
+  switch (status) {
+    case RECE_OK: return "ok";
+    case RECE_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case RECE_ERR_UNSUPPORTED: return "unsupported";
+    case RECE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case RECE_ERR_HIP: return "HIP runtime error";
+    case RECE_ERR_DEVICE_CHECK: return "device check failed";
+    case RECE_ERR_INTERNAL: return "internal error";
+  }
+  return "unknown status";
+}
+
+const char* rece_last_error(void) { return g_last_error.c_str(); }
+
+const char* rece_version(void) { return "librece 0.1 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,114 @@
+// Internal interface between the librece host code and its kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/rece.h"
+
+namespace rece {
+
+// Device counters (uint32), kept in the saved buffer.
+enum Counter {
+  CNT_ERROR = 0,          // bit flags, ERRBIT_*
+  CNT_ARGMAX_EXACT = 1,   // rows whose bucket was decided in float64
+  CNT_TOPK_EXACT = 2,     // rows whose k-th element needed more than one float64 value
+  CNT_LOGIT_EXACT = 3,    // logits recomputed in float64 (selection and dedup tests)
+  CNT_OVERFLOW = 4,       // selection buffers that could not be compacted
+  NUM_COUNTERS = 8
+};
+enum ErrBit : uint32_t { ERRBIT_BAD_ID = 1u, ERRBIT_OVERFLOW = 2u };
+
+constexpr int MAX_ROUNDS = 8;
+constexpr int SORT_SEG = 4096;      // keys per counting-sort segment (one wave each)
+constexpr int ALIST = 64;           // near-tie list capacity at the k-th boundary
+
+struct SelectArgs {
+  const void* X;
+  const void* Y;
+  const int32_t* pos;
+  const int32_t* perm_x;      // round rho
+  const int32_t* perm_y;      // round rho
+  const int32_t* inv_x;       // [rounds][s]
+  const int32_t* inv_y;       // [rounds][C]
+  int64_t s, C;
+  int n_c, k, cap, rho;
+  int selall;                 // 1: every window has at most k candidates; keep all
+  int tiles_per_chunk;
+  float beta_coef;            // error-bound coefficient of a float32 logit
+  const float* xnorm;         // [s]
+  const float* ynorm_max;     // [1]
+  double* thr_e;              // [rounds][s]
+  int32_t* thr_id;            // [rounds][s]
+  float* thr_lo;              // [rounds][s]
+  float* thr_hi;              // [rounds][s]
+  float* mshift;              // [rounds][s]
+  float* ssum;                // [rounds][s]
+  int32_t* nmem;              // [rounds][s]
+  int32_t* negs;              // [rounds][s][k] or nullptr
+  uint32_t* counters;
+};
+
+struct CeArgs {
+  const void* X;
+  const void* Y;
+  const int32_t* pos;
+  int64_t s, C;
+  int rounds;
+  const float* mshift;
+  const float* ssum;
+  const int32_t* nmem;
+  float* lse;
+  float* lpos;
+  float* loss_pp;             // nullable
+  float* partial;             // [num blocks]
+  uint32_t* counters;
+  int validate;
+};
+
+struct BwdArgs {
+  const void* X;
+  const void* Y;
+  const int32_t* pos;
+  const int32_t* perm_x;      // round rho
+  const int32_t* perm_y;      // round rho
+  const int32_t* inv_x;       // [rounds][s]
+  const int32_t* inv_y;       // [rounds][C]
+  int64_t s, C;
+  int n_c, rho;
+  int tiles_per_chunk;
+  const double* thr_e;
+  const int32_t* thr_id;
+  const float* thr_lo;
+  const float* thr_hi;
+  const float* lse;
+  const float* lpos;
+  const float* dloss;         // [1]
+  const float* dloss_pp;      // [s] or nullptr
+  float* dX;                  // [s][d]
+  float* dY;                  // [C][d]
+  uint32_t* counters;
+};
+
+// Launchers (defined in the .hip files).  All enqueue on `st`.
+hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t st);
+hipError_t launch_prep_b(bool is_bf16, int d, const void* B, int rounds, int n_b, void* Bt, float* bnorm_max,
+                         hipStream_t st);
+hipError_t launch_project_argmax(bool is_bf16, int d, const void* V, int64_t n, const void* Bt, int n_b,
+                                 const float* bnorm_max, float beta_coef, int32_t* ids, float* norms,
+                                 uint32_t* norm_max_bits, uint32_t* counters, hipStream_t st);
+size_t sort_scratch_bytes(int64_t n, int nbins);
+hipError_t launch_counting_sort(const int32_t* keys, const int32_t* in_perm, int64_t n, int shift, int nbits,
+                                void* scratch, int32_t* perm_out, int32_t* inv_out, hipStream_t st);
+hipError_t launch_select(bool is_bf16, int d, int waves, const SelectArgs& a, hipStream_t st);
+size_t select_lds_bytes(bool is_bf16, int d, int waves, int cap);
+int ce_blocks(int64_t s);
+hipError_t launch_ce(bool is_bf16, int d, const CeArgs& a, float* loss, hipStream_t st);
+hipError_t launch_bwd_rows(bool is_bf16, int d, int waves, const BwdArgs& a, hipStream_t st);
+hipError_t launch_bwd_items(bool is_bf16, int d, int waves, const BwdArgs& a, int item_tiles_per_chunk,
+                            hipStream_t st);
+size_t pos_partial_bytes(int64_t s, int d);
+hipError_t launch_pos_dy(bool is_bf16, int d, const BwdArgs& a, const int32_t* pos_perm, float* partial,
+                         hipStream_t st);
+
+}  // namespace rece

@@ -1,0 +1,152 @@
+/* rece.h - RECE / SCE reduced cross-entropy loss, forward and backward, on one
+ * AMD Instinct MI355X (gfx950).  C ABI of librece.
+ *
+ * What is computed (RECE page, "RECE: Reduced Cross-Entropy Loss for
+ * Large-Catalogue Sequential Recommenders", Section 3, Algorithm 1 and the
+ * method paragraph before it):
+ *   for every round rho = 0..r-1 (independent random vectors B_rho):
+ *     bucket of each position x_i and item y_j = argmax over the n_b random
+ *       vectors b of the signed scalar product b.v (ties: lowest index);
+ *     positions and items are stably sorted by bucket and cut into n_c equal
+ *       chunks (chunk c holds sorted slots p with c*N/n_c <= p < (c+1)*N/n_c);
+ *     a position in X-chunk c is scored against the items of chunks c-1, c, c+1
+ *       (modulo n_c), its own positive excluded, and keeps the k largest logits
+ *       (order: logit descending, item id ascending);
+ *   the kept pairs of all rounds form a set (the page's "minus ln(count)" rule
+ *   makes a pair kept in several rounds count once);
+ *   loss_i = logsumexp({x_i.y_pos_i} u {x_i.y_j : j kept}) - x_i.y_pos_i,
+ *   loss = mean over the s positions.
+ * The backward pass returns d loss / d X and d loss / d Y with the selection held
+ * fixed (Eq. 4 of the same page restricted to the kept set).
+ *
+ * Selection decisions (bucket argmax, top-k membership) are taken on the float64
+ * value of each scalar product summed in coordinate order; the kernels compute
+ * float32 matrix-core products with a proven error bound and recompute in
+ * float64 only where the bound cannot decide.  Loss and gradients are float32.
+ *
+ * SCE variant (SCE page, "Scalable Cross-Entropy Loss for Sequential
+ * Recommendations with Large Item Catalogs", abstract: softmax over a subset
+ * found by maximum inner product search): n_b projection buckets; bucket b
+ * takes the b_x positions and b_y items with the largest scores b.v, scores its
+ * positions against its items, and every position keeps the k largest logits
+ * over the union of the buckets that took it.
+ *
+ * Conventions for every entry point:
+ *   - device pointers are caller-owned, contiguous, row-major and at least
+ *     16-byte aligned; the library never allocates device memory;
+ *   - `stream` is a hipStream_t (NULL = the default stream); every call that
+ *     takes a stream only enqueues work on it and returns without waiting,
+ *     except rece_check, which waits for the stream;
+ *   - every call returns a rece_status; no C++ exception crosses the ABI;
+ *     rece_last_error() gives a thread-local message for the last failure.
+ */
+#ifndef RECE_H_
+#define RECE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RECE_OK = 0,
+  RECE_ERR_INVALID_ARGUMENT = 1,   /* bad config value, NULL or misaligned pointer */
+  RECE_ERR_UNSUPPORTED = 2,        /* valid but not built (e.g. d not a multiple of 32) */
+  RECE_ERR_WORKSPACE_TOO_SMALL = 3,
+  RECE_ERR_HIP = 4,                /* a HIP runtime call failed; see rece_last_error() */
+  RECE_ERR_DEVICE_CHECK = 5,       /* a device-side check failed (read by rece_check) */
+  RECE_ERR_INTERNAL = 6
+} rece_status;
+
+typedef enum { RECE_F32 = 0, RECE_BF16 = 1 } rece_dtype;
+typedef enum { RECE_VARIANT_RECE = 0, RECE_VARIANT_SCE = 1 } rece_variant;
+
+/* flags */
+#define RECE_FLAG_VALIDATE_IDS 1u  /* device check that 0 <= pos[i] < C (error word) */
+#define RECE_FLAG_KEEP_STAGES 2u   /* keep per-round kept-negative lists for rece_export */
+
+typedef struct {
+  int64_t s;        /* positions (batch x sequence length collapsed), >= 1 */
+  int64_t C;        /* catalogue size, >= 2 */
+  int32_t d;        /* embedding dimension: multiple of 32, 32..512 */
+  int32_t n_b;      /* random vectors (buckets) per round, 1..4096 */
+  int32_t n_c;      /* RECE chunks, 1..min(s, C); ignored by SCE */
+  int32_t k;        /* negatives kept per position (RECE: per round), 0..C-1 */
+  int32_t rounds;   /* RECE rounds r, 1..8; SCE: must be 1 */
+  int32_t b_x;      /* SCE: positions per bucket, 1..s; RECE: 0 */
+  int32_t b_y;      /* SCE: items per bucket, 1..C; RECE: 0 */
+  int32_t dtype;    /* rece_dtype of X, Y and B (float32 or bfloat16 bits) */
+  int32_t variant;  /* rece_variant */
+  uint32_t flags;   /* RECE_FLAG_* */
+} rece_config;
+
+typedef struct rece_plan_s* rece_plan_t;
+
+/* Validate `cfg` and build an immutable host-side plan (no GPU work, no device
+ * memory).  On error *out is NULL.  A plan may be used from several threads. */
+rece_status rece_plan(const rece_config* cfg, rece_plan_t* out);
+rece_status rece_plan_destroy(rece_plan_t plan);
+
+/* Bytes of the two caller-provided device buffers:
+ *   scratch: temporaries of one call; may be reused freely between calls;
+ *   saved:   written by rece_forward, read by rece_backward / rece_export /
+ *            rece_check; must stay untouched in between. */
+rece_status rece_workspace_bytes(rece_plan_t plan, size_t* scratch_bytes, size_t* saved_bytes);
+
+/* Forward pass.
+ *   X    [s][d]  dtype      hidden states, one row per position
+ *   Y    [C][d]  dtype      item embeddings
+ *   pos  [s]     int32      positive item id of each position, 0 <= pos < C
+ *   B    RECE: [rounds][d][n_b] dtype, column b of slice rho is random vector b
+ *        of round rho;  SCE: [d][n_b]
+ *   loss [1]     float32    out: mean loss
+ *   loss_pp [s]  float32    out: per-position loss, or NULL
+ * Uses (overwrites) scratch and saved. */
+rece_status rece_forward(rece_plan_t plan, void* stream, const void* X, const void* Y,
+                         const int32_t* pos, const void* B, void* scratch, void* saved,
+                         float* loss, float* loss_pp);
+
+/* Backward pass of the last rece_forward that wrote `saved` (same X, Y, pos).
+ *   dloss    [1] float32   upstream gradient of the mean loss (ignored if dloss_pp)
+ *   dloss_pp [s] float32   upstream gradient of each per-position loss, or NULL
+ *   dX [s][d], dY [C][d] float32   out: overwritten with the gradients (rows of
+ *                                  items that no position scored are zero). */
+rece_status rece_backward(rece_plan_t plan, void* stream, const void* X, const void* Y,
+                          const int32_t* pos, const float* dloss, const float* dloss_pp,
+                          void* scratch, const void* saved, float* dX, float* dY);
+
+/* Intermediate results kept in `saved`, copied asynchronously into `dst`. */
+typedef enum {
+  RECE_STAGE_BUCKET_X = 0,   /* int32 [s]  bucket of each position (round `round`) */
+  RECE_STAGE_BUCKET_Y = 1,   /* int32 [C]  bucket of each item */
+  RECE_STAGE_PERM_X = 2,     /* int32 [s]  sorted slot -> position */
+  RECE_STAGE_PERM_Y = 3,     /* int32 [C]  sorted slot -> item */
+  RECE_STAGE_THRESH_ID = 4,  /* int32 [s]  id of the k-th kept negative; -1 all kept; -2 none */
+  RECE_STAGE_THRESH_LOGIT = 5, /* float64 [s] its logit (float64, coordinate-order sum) */
+  RECE_STAGE_NEG_IDS = 6,    /* int32 [s][k] kept negatives, unordered, -1 padded (KEEP_STAGES) */
+  RECE_STAGE_LSE = 7,        /* float32 [s] log-sum-exp over positive + kept set (round ignored) */
+  RECE_STAGE_COUNTERS = 8    /* uint32 [8] device counters: [0] error bits, [1] argmax rows
+                                decided in float64, [2] top-k rows needing float64 values,
+                                [3] logits recomputed in float64, [4] buffer overflows */
+} rece_stage;
+
+rece_status rece_export(rece_plan_t plan, void* stream, const void* saved, int stage, int round,
+                        void* dst);
+/* Bytes rece_export writes for (stage); 0 if the stage is not kept by this plan. */
+rece_status rece_export_bytes(rece_plan_t plan, int stage, size_t* bytes);
+
+/* Waits for `stream`, then reads the device error word in `saved`:
+ * RECE_ERR_DEVICE_CHECK if an id was out of range (with VALIDATE_IDS) or a
+ * selection buffer overflowed; RECE_OK otherwise. */
+rece_status rece_check(rece_plan_t plan, void* stream, const void* saved);
+
+const char* rece_status_string(rece_status status);
+const char* rece_last_error(void);
+const char* rece_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RECE_H_ */

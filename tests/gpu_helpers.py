@@ -1,0 +1,51 @@
+"""Shared helpers of the GPU tests: run librece on a seeded workload and gather
+its outputs and kept stages as NumPy arrays."""
+import numpy as np
+import torch
+
+import catalogue_cross_entropy_amd as rece
+
+
+def to_device(inp):
+    dev = torch.device("cuda:0")
+    dt = torch.bfloat16 if inp.w.dtype == "bf16" else torch.float32
+    X = torch.from_numpy(inp.X).to(dev).to(dt).contiguous()
+    Y = torch.from_numpy(inp.Y).to(dev).to(dt).contiguous()
+    B = torch.from_numpy(inp.B).to(dev).to(dt).contiguous()
+    pos = torch.from_numpy(inp.pos).to(dev)
+    return X, Y, pos, B
+
+
+def run_rece(inp, keep_stages=True, backward=True, dloss_pp=None, tensors=None):
+    w = inp.w
+    X, Y, pos, B = tensors if tensors is not None else to_device(inp)
+    plan = rece.Plan(w.s, w.C, w.d, w.n_b, w.n_c, w.k, w.rounds, dtype=w.dtype,
+                     keep_stages=keep_stages, validate_ids=True)
+    print(f"[gpu] rece s={w.s} C={w.C} d={w.d} n_b={w.n_b} n_c={w.n_c} k={w.k} r={w.rounds} "
+          f"dtype={w.dtype} seed={w.seed}", flush=True)
+    loss, lpp, scratch, saved = plan.forward(X, Y, pos, B)
+    out = {"loss": None}
+    if backward:
+        dpp = None if dloss_pp is None else torch.from_numpy(dloss_pp.astype(np.float32)).cuda()
+        dX, dY = plan.backward(X, Y, pos, scratch, saved, dloss_pp=dpp)
+    plan.check(saved)
+    torch.cuda.synchronize()
+    out["loss"] = loss.item()
+    out["loss_pp"] = lpp.cpu().numpy()
+    if backward:
+        out["dX"] = dX.cpu().numpy()
+        out["dY"] = dY.cpu().numpy()
+    out["counters"] = plan.export(saved, "counters").cpu().numpy()
+    out["lse"] = plan.export(saved, "lse").cpu().numpy()
+    for r in range(w.rounds):
+        for st in ("bucket_x", "bucket_y", "perm_x", "perm_y", "thresh_id", "thresh_logit"):
+            out[(st, r)] = plan.export(saved, st, r).cpu().numpy()
+        if keep_stages:
+            out[("neg_ids", r)] = plan.export(saved, "neg_ids", r).cpu().numpy()
+    torch.cuda.synchronize()
+    out["plan"] = plan
+    return out
+
+
+def grad_err(a, b):
+    return float(np.abs(a - b).max() / max(np.abs(b).max(), 1e-30))
