@@ -1,0 +1,193 @@
+"""Benchmark: RECE forward + backward throughput on one MI355X.
+
+One step = rece_forward + rece_backward over one batch of the workload (all
+rounds: bucketing, sorting, chunk logits + top-k, loss, dX, dY).  Inputs are
+resident in HBM before the timed region.  Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload sasrec]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0      # dense bf16 matrix cores
+PEAK_FP32_TFLOPS = 157.3       # fp32 matrix cores
+RIDGE_BF16 = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+
+
+def chunk_starts(N, n_c):
+    return [(c * N + n_c - 1) // n_c for c in range(n_c + 1)]
+
+
+def window_logits(w):
+    """sum over positions of the window size of the position's chunk (logits per round)."""
+    xs, ys = chunk_starts(w.s, w.n_c), chunk_starts(w.C, w.n_c)
+    tot = 0
+    for c in range(w.n_c):
+        wins = {c, (c - 1) % w.n_c, (c + 1) % w.n_c}
+        W = sum(ys[q + 1] - ys[q] for q in wins)
+        tot += (xs[c + 1] - xs[c]) * W
+    return tot
+
+
+def algorithmic_work(w):
+    """Per-step algorithmic (flops, bytes) of each phase: what the method must compute and
+    move; logits never go to HBM, every vector is read once per pass."""
+    es = 2 if w.dtype == "bf16" else 4
+    s, C, d, r, nb = w.s, w.C, w.d, w.rounds, w.n_b
+    wl = window_logits(w)
+    state = 32            # per position and round: threshold (12 B), bounds, shift, sum, count
+    return {
+        "project": (2.0 * d * nb * (s + C) * r, r * ((s + C) * (d * es + 4) + nb * d * es)),
+        "sort": (0.0, r * (s + C) * 12 + s * 12),
+        "select": (2.0 * d * wl * r, r * ((s + C) * d * es + 8 * (s + C) + state * s)),
+        "loss": (2.0 * d * s, s * (2 * d * es + 12 + 12 * r)),
+        "bwd_dx": (2.0 * d * (w.k * r + 1) * s, r * ((s + C) * d * es + state * s) + s * d * 4),
+        "bwd_dy": (2.0 * d * w.k * r * s, r * ((s + C) * d * es + state * s) + C * d * 4),
+        "bwd_pos": (2.0 * d * s, s * (d * es + 16) + s * d * 4),
+    }
+
+
+def roofline(name, ms_per_launch, flops, nbytes, dtype):
+    ai = flops / max(nbytes, 1)
+    t = ms_per_launch * 1e-3
+    if name == "select" or (name == "project" and ai > RIDGE_BF16):
+        peak = PEAK_BF16_TFLOPS if dtype == "bf16" else PEAK_FP32_TFLOPS
+        ach = flops / t / 1e12
+        return {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak}
+    ach = nbytes / t / 1e9
+    return {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS}
+
+
+def cpu_baseline(inp, n_rows, seed=0):
+    """The float64 oracle, as it is, on a seeded sample of positions (all rounds, fwd + bwd)."""
+    import numpy as np
+    import oracle
+    w = inp.w
+    rows = np.sort(np.random.default_rng(seed).choice(w.s, size=n_rows, replace=False))
+    t0 = time.perf_counter()
+    fwd = oracle.rece_forward(inp.X, inp.Y, inp.pos, inp.B, w.n_c, w.k, rows=rows)
+    oracle.rece_backward(inp.X, inp.Y, inp.pos, fwd)
+    dt = time.perf_counter() - t0
+    return {"value": n_rows / dt, "unit": "positions/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_rows} of {w.s} positions (seeded), all {w.rounds} rounds, forward + backward; "
+                      f"bucketing and sorting of all {w.s}+{w.C} vectors included; {dt:.1f} s; "
+                      f"NumPy elementwise float64 (one thread)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="sasrec")
+    ap.add_argument("--cpu-rows", type=int, default=512)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the loss runs on a single MI355X, see the sharding notes in the design document)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import catalogue_cross_entropy_amd as rece
+    from rece_inputs import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    inp = make_inputs(w)
+    dev = torch.device("cuda:0")
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    X = torch.from_numpy(inp.X).to(dev).to(dt)
+    Y = torch.from_numpy(inp.Y).to(dev).to(dt)
+    B = torch.from_numpy(inp.B).to(dev).to(dt)
+    pos = torch.from_numpy(inp.pos).to(dev)
+    plan = rece.Plan(w.s, w.C, w.d, w.n_b, w.n_c, w.k, w.rounds, dtype=w.dtype)
+    scratch, saved = plan.workspace(dev)
+    dX = torch.empty((w.s, w.d), dtype=torch.float32, device=dev)
+    dY = torch.empty((w.C, w.d), dtype=torch.float32, device=dev)
+    dloss = torch.ones(1, dtype=torch.float32, device=dev)
+
+    def step():
+        plan.forward(X, Y, pos, B, scratch, saved, loss_pp=False)
+        plan.backward(X, Y, pos, scratch, saved, dloss=dloss, dX=dX, dY=dY)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    plan.check(saved)
+
+    # phase breakdown on a few untimed steps (events around every launch)
+    plan.profile()
+    nprof = 3
+    for _ in range(nprof):
+        step()
+    torch.cuda.synchronize()
+    phases = plan.profile_read()
+    plan.profile(enable=False)
+    work = algorithmic_work(w)
+    dom = max((k for k in work), key=lambda k: phases[k][0])
+
+    # timed region: events only around the dominant kernel's launches
+    plan.profile([dom])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    dom_ms, dom_launches = plan.profile_read()[dom]
+    plan.profile(enable=False)
+    plan.check(saved)
+    counters = plan.export(saved, "counters").cpu().tolist()
+
+    ms_step = elapsed * 1e3 / args.steps
+    flops, nbytes = work[dom]
+    per_launch = dom_launches / args.steps
+    rl = roofline(dom, dom_ms / dom_launches, flops / per_launch, nbytes / per_launch, w.dtype)
+    rl["kernel"] = dom
+    rl["traffic"] = None
+
+    breakdown = {}
+    for name, (f, b) in work.items():
+        ms, n = phases[name]
+        if n == 0:
+            continue
+        r = roofline(name, ms / n, f * nprof / n, b * nprof / n, w.dtype)
+        breakdown[name] = {"ms_per_step": ms / nprof, "launches_per_step": n / nprof,
+                           "bound": r["bound"], "frac": round(r["frac"], 4)}
+
+    out = {
+        "metric": "RECE fwd+bwd positions/sec at C items, d; % MFMA and % HBM peak",
+        "value": w.s / (ms_step * 1e-3),
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: s={w.s} ({w.seqs}x{w.seqlen}), C={w.C}, d={w.d}, "
+                               f"n_b={w.n_b}, n_c={w.n_c}, k={w.k}, rounds={w.rounds}, {w.dtype}, "
+                               f"positives {w.positives}", "parallelism": "single GPU"},
+        "roofline": rl,
+        "phases": breakdown,
+        "counters": {"argmax_rows_float64": counters[1], "topk_rows_near_tie": counters[2],
+                     "logits_float64": counters[3], "overflows": counters[4]},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_rows)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -26,7 +26,9 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too sm
 
 EXPORTED = ["rece_plan", "rece_plan_destroy", "rece_workspace_bytes", "rece_forward",
             "rece_backward", "rece_export", "rece_export_bytes", "rece_check",
+            "rece_profile_enable", "rece_profile_read",
             "rece_status_string", "rece_last_error", "rece_version"]
+PHASES = ["project", "sort", "select", "loss", "bwd_dx", "bwd_dy", "bwd_pos", "other"]
 
 
 class ReceConfig(ctypes.Structure):
@@ -61,12 +63,16 @@ def lib() -> ctypes.CDLL:
         L.rece_export.argtypes = [vp, vp, vp, i32, i32, vp]
         L.rece_export_bytes.argtypes = [vp, i32, sz]
         L.rece_check.argtypes = [vp, vp, vp]
+        L.rece_profile_enable.argtypes = [vp, i32]
+        L.rece_profile_read.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_double),
+                                        ctypes.POINTER(ctypes.c_int64)]
         L.rece_status_string.argtypes = [i32]
         L.rece_status_string.restype = ctypes.c_char_p
         L.rece_last_error.restype = ctypes.c_char_p
         L.rece_version.restype = ctypes.c_char_p
         for name in ("rece_plan", "rece_plan_destroy", "rece_workspace_bytes", "rece_forward",
-                     "rece_backward", "rece_export", "rece_export_bytes", "rece_check"):
+                     "rece_backward", "rece_export", "rece_export_bytes", "rece_check",
+                     "rece_profile_enable", "rece_profile_read"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -172,6 +178,28 @@ class Plan:
         _check(lib().rece_export(self._h, _stream(stream), _ptr(saved), st, round, _ptr(out)))
         if stage == "neg_ids":
             out = out.view(self.cfg.s, max(self.cfg.k, 1))
+        return out
+
+    def profile(self, phases=None, enable: bool = True):
+        """Start (clearing earlier records) or stop event timing of this plan's kernels.
+        phases: None for all, else an iterable of phase names."""
+        if not enable:
+            mask = 0
+        elif phases is None:
+            mask = -1
+        else:
+            mask = 0
+            for ph in phases:
+                mask |= 1 << PHASES.index(ph)
+        _check(lib().rece_profile_enable(self._h, mask))
+
+    def profile_read(self):
+        """{phase: (total ms, launches)} since profiling was last enabled (waits for the GPU)."""
+        out = {}
+        for i, name in enumerate(PHASES):
+            ms, n = ctypes.c_double(), ctypes.c_int64()
+            _check(lib().rece_profile_read(self._h, i, ctypes.byref(ms), ctypes.byref(n)))
+            out[name] = (ms.value, n.value)
         return out
 
     def check(self, saved, stream=None):

@@ -29,16 +29,6 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
-template <class E, int D>
-__device__ __forceinline__ bool member(float a, float lo, float hi, double te, int tid, const E* xrow,
-                                       const E* Y, int j, uint32_t* counters) {
-  if (a > hi) return true;
-  if (a < lo) return false;
-  const double e = exact_dot(xrow, Y + (int64_t)j * D, D);
-  atomicAdd(counters + CNT_LOGIT_EXACT, 1u);
-  return e > te || (e == te && j <= tid);
-}
-
 // Upstream gradient of position i's loss.
 __device__ __forceinline__ float gbar_of(const BwdArgs& p, int64_t i) {
   return p.dloss_pp ? p.dloss_pp[i] : p.dloss[0] / (float)p.s;
@@ -120,12 +110,6 @@ __device__ __forceinline__ void accumulate_gt(f32x4 (&acc)[D / 16], const float*
     }
   }
 }
-
-struct PrevRow {   // a position's threshold in an earlier round
-  double te;
-  float lo, hi;
-  int tid, cx;
-};
 
 template <class E, int D>
 __host__ __device__ constexpr size_t bwd_common_lds() {
@@ -237,11 +221,11 @@ __global__ __launch_bounds__(64 * NW) void k_bwd_rows(BwdArgs p) {
           float gv = 0.0f;
           if (rv[v] && j >= 0 && j != pos_v[v]) {
             const E* xrow = X + (int64_t)i_v[v] * D;
-            bool mem = member<E, D>(a, lo_v[v], hi_v[v], te_v[v], tid_v[v], xrow, Y, j, p.counters);
+            bool mem = beats<E, D>(a, lo_v[v], hi_v[v], te_v[v], tid_v[v], xrow, Y, j, p.counters);
             for (int r2 = 0; r2 < rho && mem; ++r2) {
               const PrevRow pr = prev[(4 * g + v) * MAX_ROUNDS + r2];
               if (!in_window(pr.cx, cy2s[r2 * 64 + n], n_c)) continue;
-              if (member<E, D>(a, pr.lo, pr.hi, pr.te, pr.tid, xrow, Y, j, p.counters)) mem = false;
+              if (beats<E, D>(a, pr.lo, pr.hi, pr.te, pr.tid, xrow, Y, j, p.counters)) mem = false;
             }
             if (mem) gv = expf(a - lse_v[v]) * gb_v[v];
           }
@@ -390,11 +374,11 @@ __global__ __launch_bounds__(64 * NW) void k_bwd_items(BwdArgs p, int itiles) {
           float gv = 0.0f;
           if (rv[v] && pi.i >= 0 && j != pi.pos) {
             const E* xrow = X + (int64_t)pi.i * D;
-            bool mem = member<E, D>(a, pi.lo, pi.hi, pi.te, pi.tid, xrow, Y, j, p.counters);
+            bool mem = beats<E, D>(a, pi.lo, pi.hi, pi.te, pi.tid, xrow, Y, j, p.counters);
             for (int r2 = 0; r2 < rho && mem; ++r2) {
               const PrevRow pr = pprev[n * MAX_ROUNDS + r2];
               if (!in_window(pr.cx, cy2w[(4 * g + v) * MAX_ROUNDS + r2], n_c)) continue;
-              if (member<E, D>(a, pr.lo, pr.hi, pr.te, pr.tid, xrow, Y, j, p.counters)) mem = false;
+              if (beats<E, D>(a, pr.lo, pr.hi, pr.te, pr.tid, xrow, Y, j, p.counters)) mem = false;
             }
             if (mem) gv = expf(a - pi.lse) * pi.gb;
           }

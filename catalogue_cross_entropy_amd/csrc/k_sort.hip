@@ -2,7 +2,7 @@
 // "X = X[argsort I]", "Y = Y[argsort J]"; stable ascending order).
 //
 // Three passes over the keys, no atomics on the output path:
-//   1. per segment of SORT_SEG keys, a histogram in LDS -> counts[bin][segment];
+//   1. per segment of keys (256 to SORT_SEG of them), a histogram in LDS -> counts[bin][segment];
 //   2. one exclusive scan of counts in (bin, segment) order gives every
 //      (bin, segment) its first output slot;
 //   3. one wave per segment walks its keys in order, 64 at a time: lanes with
@@ -26,15 +26,15 @@ __device__ __forceinline__ int key_at(const int32_t* __restrict__ keys, const in
 
 __global__ __launch_bounds__(256) void k_seg_hist(const int32_t* __restrict__ keys,
                                                   const int32_t* __restrict__ in_perm, int64_t n, int shift,
-                                                  int nbits, int nseg, uint32_t* __restrict__ counts) {
+                                                  int nbits, int seg_len, int nseg, uint32_t* __restrict__ counts) {
   extern __shared__ uint32_t hist[];
   const int nbins = 1 << nbits;
   const uint32_t mask = (uint32_t)nbins - 1u;
   for (int b = threadIdx.x; b < nbins; b += 256) hist[b] = 0u;
   __syncthreads();
   const int64_t seg = blockIdx.x;
-  const int64_t t0 = seg * SORT_SEG;
-  const int64_t t1 = min(n, t0 + SORT_SEG);
+  const int64_t t0 = seg * seg_len;
+  const int64_t t1 = min(n, t0 + seg_len);
   for (int64_t t = t0 + threadIdx.x; t < t1; t += 256) atomicAdd(&hist[key_at(keys, in_perm, t, shift, mask)], 1u);
   __syncthreads();
   for (int b = threadIdx.x; b < nbins; b += 256) counts[(int64_t)b * nseg + seg] = hist[b];
@@ -118,7 +118,7 @@ static hipError_t exclusive_scan(uint32_t* a, int64_t n, uint32_t* bsum, hipStre
 
 __global__ __launch_bounds__(256) void k_seg_scatter(const int32_t* __restrict__ keys,
                                                      const int32_t* __restrict__ in_perm, int64_t n, int shift,
-                                                     int nbits, int nseg, const uint32_t* __restrict__ offs,
+                                                     int nbits, int seg_len, int nseg, const uint32_t* __restrict__ offs,
                                                      int32_t* __restrict__ perm_out, int32_t* __restrict__ inv_out) {
   extern __shared__ uint32_t ctr_all[];
   const int nbins = 1 << nbits;
@@ -129,8 +129,8 @@ __global__ __launch_bounds__(256) void k_seg_scatter(const int32_t* __restrict__
   uint32_t* ctr = ctr_all + (int64_t)w * nbins;
   for (int b = l; b < nbins; b += WAVE) ctr[b] = offs[(int64_t)b * nseg + seg];
   wave_sync();
-  const int64_t t0 = seg * SORT_SEG;
-  const int64_t t1 = min(n, t0 + SORT_SEG);
+  const int64_t t0 = seg * seg_len;
+  const int64_t t1 = min(n, t0 + seg_len);
   for (int64_t tb = t0; tb < t1; tb += WAVE) {
     const int64_t t = tb + l;
     const bool valid = t < t1;
@@ -162,7 +162,16 @@ __global__ __launch_bounds__(256) void k_seg_scatter(const int32_t* __restrict__
   }
 }
 
-static int64_t num_segments(int64_t n) { return (n + SORT_SEG - 1) / SORT_SEG; }
+// Keys per segment: about 256 segments for small inputs (enough waves for the
+// scatter), at most SORT_SEG keys each for large ones (bounded histogram matrix).
+static int64_t seg_len_for(int64_t n) {
+  int64_t L = ((n / 256) + 63) / 64 * 64;
+  return L < 256 ? 256 : (L > SORT_SEG ? SORT_SEG : L);
+}
+static int64_t num_segments(int64_t n) {
+  const int64_t L = seg_len_for(n);
+  return (n + L - 1) / L;
+}
 
 size_t sort_scratch_bytes(int64_t n, int nbins) {
   const int64_t cnt = num_segments(n) * (int64_t)nbins;
@@ -177,14 +186,15 @@ hipError_t launch_counting_sort(const int32_t* keys, const int32_t* in_perm, int
   const int64_t nseg = num_segments(n);
   uint32_t* counts = reinterpret_cast<uint32_t*>(scratch);
   uint32_t* bsum = counts + nseg * nbins;
+  const int seg_len = (int)seg_len_for(n);
   hipLaunchKernelGGL(k_seg_hist, dim3((unsigned)nseg), dim3(256), nbins * sizeof(uint32_t), st, keys, in_perm, n,
-                     shift, nbits, (int)nseg, counts);
+                     shift, nbits, seg_len, (int)nseg, counts);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = exclusive_scan(counts, nseg * nbins, bsum, st);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_seg_scatter, dim3((unsigned)((nseg + 3) / 4)), dim3(256), 4 * nbins * sizeof(uint32_t), st,
-                     keys, in_perm, n, shift, nbits, (int)nseg, counts, perm_out, inv_out);
+                     keys, in_perm, n, shift, nbits, seg_len, (int)nseg, counts, perm_out, inv_out);
   return hipGetLastError();
 }
 

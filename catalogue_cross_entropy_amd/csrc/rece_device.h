@@ -165,4 +165,26 @@ __device__ __forceinline__ bool in_window(int cx, int cy, int n_c) {
   return dlt == 0 || dlt == 1 || dlt == n_c - 1;
 }
 
+// Is pair (i, j) with float32 logit a in a round's kept set?  The set is given by
+// its k-th element (float64 logit te, item id tid) and the float32 bounds
+// lo <= te - beta, hi >= te + beta, beta bounding |a - float64 logit|:
+// above hi -> kept, below lo -> not kept, in between -> float64 comparison in the
+// order (logit desc, id asc).  lo = hi = -inf: every candidate kept; +inf: none.
+template <class E, int D>
+__device__ __forceinline__ bool beats(float a, float lo, float hi, double te, int tid, const E* xrow,
+                                      const E* Y, int j, uint32_t* counters) {
+  if (a > hi) return true;
+  if (a < lo) return false;
+  if (j == tid) return true;
+  const double e = exact_dot(xrow, Y + (int64_t)j * D, D);
+  atomicAdd(counters + 3, 1u);
+  return e > te || (e == te && j <= tid);
+}
+
+struct PrevRow {   // a position's kept-set threshold in an earlier round
+  double te;
+  float lo, hi;
+  int tid, cx;
+};
+
 }  // namespace rece

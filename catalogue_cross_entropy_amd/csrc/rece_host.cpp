@@ -9,6 +9,8 @@
 #include <cstring>
 #include <new>
 #include <string>
+#include <utility>
+#include <vector>
 
 #include "rece_internal.h"
 
@@ -48,8 +50,31 @@ struct Layout {
 
 }  // namespace
 
+#define RECE_HIP(call, where)                 \
+  do {                                         \
+    hipError_t e_ = (call);                    \
+    if (e_ != hipSuccess) return hip_fail(e_, where); \
+  } while (0)
+
+struct Profiler {
+  bool on = false;
+  uint32_t mask = 0;
+  std::vector<hipEvent_t> pool;
+  size_t used = 0;
+  std::vector<std::pair<int, std::pair<hipEvent_t, hipEvent_t>>> rec;
+  hipEvent_t get() {
+    if (used == pool.size()) {
+      hipEvent_t e = nullptr;
+      if (hipEventCreate(&e) != hipSuccess) return nullptr;
+      pool.push_back(e);
+    }
+    return pool[used++];
+  }
+};
+
 struct rece_plan_s {
   rece_config cfg;
+  mutable Profiler prof;
   bool bf16;
   int esize;
   int nbits_b;
@@ -67,6 +92,33 @@ struct rece_plan_s {
   // scratch
   size_t o_bt, o_bnorm, o_sort, o_part, o_pp0, o_pp1, o_ppart, scratch_bytes;
 };
+
+namespace {
+// Brackets the launches of one phase with events when profiling is on.
+struct PhaseScope {
+  Profiler& pr;
+  hipStream_t st;
+  int phase;
+  hipEvent_t a = nullptr, b = nullptr;
+  PhaseScope(Profiler& p, int ph, hipStream_t s) : pr(p), st(s), phase(ph) {
+    if (!pr.on || !((pr.mask >> ph) & 1u)) return;
+    a = pr.get();
+    b = pr.get();
+    if (a && b) hipEventRecord(a, st);
+  }
+  ~PhaseScope() {
+    if (!a || !b) return;
+    hipEventRecord(b, st);
+    pr.rec.push_back({phase, {a, b}});
+  }
+};
+}  // namespace
+
+#define RECE_PHASE(phase, call, where)                 \
+  do {                                                 \
+    PhaseScope ps_(p.prof, (phase), st);               \
+    RECE_HIP(call, where);                             \
+  } while (0)
 
 static rece_status validate_config(const rece_config* c) {
   if (!c) return fail(RECE_ERR_INVALID_ARGUMENT, "config is NULL");
@@ -109,18 +161,13 @@ rece_status rece_plan(const rece_config* cfg, rece_plan_t* out) {
   const int64_t items_chunk = (C + n_c - 1) / n_c;
   const int64_t wmax = n_c <= 3 ? C : std::min<int64_t>(C, 3 * items_chunk);
   p->selall = (k >= wmax) || (n_c <= 3 && k >= C - 1);
-  // candidate list: the k kept + one tile of new entries + slack near the threshold
-  p->cap = p->selall ? 64 : (int)align_up((size_t)(k + 64 + std::max(64, k / 2)), 32);
+  p->cap = 0;
   p->waves_sel = 1;
   for (int nw : {4, 2, 1}) {
-    if (select_lds_bytes(p->bf16, d, nw, p->cap) <= 128 * 1024) {
+    if (select_lds_bytes(p->bf16, d, nw, 0) <= 160 * 1024) {
       p->waves_sel = nw;
       break;
     }
-  }
-  if (select_lds_bytes(p->bf16, d, p->waves_sel, p->cap) > 160 * 1024) {
-    delete p;
-    return fail(RECE_ERR_UNSUPPORTED, "k too large for the on-chip candidate lists");
   }
   p->tpc_sel = (int)((rows_chunk + 16 * p->waves_sel - 1) / (16 * p->waves_sel));
   p->tpc_bwd = (int)((rows_chunk + 63) / 64);
@@ -169,7 +216,38 @@ rece_status rece_plan(const rece_config* cfg, rece_plan_t* out) {
 }
 
 rece_status rece_plan_destroy(rece_plan_t plan) {
+  if (plan)
+    for (hipEvent_t e : plan->prof.pool) hipEventDestroy(e);
   delete plan;
+  return RECE_OK;
+}
+
+rece_status rece_profile_enable(rece_plan_t plan, int mask) {
+  if (!plan) return fail(RECE_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (mask) {
+    plan->prof.rec.clear();
+    plan->prof.used = 0;
+  }
+  plan->prof.on = mask != 0;
+  plan->prof.mask = (uint32_t)mask;
+  return RECE_OK;
+}
+
+rece_status rece_profile_read(rece_plan_t plan, int phase, double* total_ms, int64_t* launches) {
+  if (!plan || !total_ms || !launches) return fail(RECE_ERR_INVALID_ARGUMENT, "NULL argument");
+  if (phase < 0 || phase >= RECE_NUM_PHASES) return fail(RECE_ERR_INVALID_ARGUMENT, "unknown phase");
+  double tot = 0.0;
+  int64_t n = 0;
+  for (auto& r : plan->prof.rec) {
+    if (r.first != phase) continue;
+    RECE_HIP(hipEventSynchronize(r.second.second), "profile: wait for event");
+    float ms = 0.0f;
+    RECE_HIP(hipEventElapsedTime(&ms, r.second.first, r.second.second), "profile: elapsed time");
+    tot += ms;
+    ++n;
+  }
+  *total_ms = tot;
+  *launches = n;
   return RECE_OK;
 }
 
@@ -179,12 +257,6 @@ rece_status rece_workspace_bytes(rece_plan_t plan, size_t* scratch_bytes, size_t
   if (saved_bytes) *saved_bytes = plan->saved_bytes;
   return RECE_OK;
 }
-
-#define RECE_HIP(call, where)                 \
-  do {                                         \
-    hipError_t e_ = (call);                    \
-    if (e_ != hipSuccess) return hip_fail(e_, where); \
-  } while (0)
 
 rece_status rece_forward(rece_plan_t plan, void* stream, const void* X, const void* Y, const int32_t* pos,
                          const void* B, void* scratch, void* saved, float* loss, float* loss_pp) {
@@ -206,9 +278,10 @@ rece_status rece_forward(rece_plan_t plan, void* stream, const void* X, const vo
   float* bnorm = reinterpret_cast<float*>(sc + p.o_bnorm);
   void* Bt = sc + p.o_bt;
 
-  RECE_HIP(launch_fill_u32(counters, 0u, NUM_COUNTERS, st), "clear counters");
-  RECE_HIP(launch_fill_u32(reinterpret_cast<uint32_t*>(ymax), 0u, 1, st), "clear norm max");
-  RECE_HIP(launch_prep_b(p.bf16, d, B, c.rounds, c.n_b, Bt, bnorm, st), "prepare random vectors");
+  RECE_PHASE(RECE_PHASE_OTHER, launch_fill_u32(counters, 0u, NUM_COUNTERS, st), "clear counters");
+  RECE_PHASE(RECE_PHASE_OTHER, launch_fill_u32(reinterpret_cast<uint32_t*>(ymax), 0u, 1, st), "clear norm max");
+  RECE_PHASE(RECE_PHASE_OTHER, launch_prep_b(p.bf16, d, B, c.rounds, c.n_b, Bt, bnorm, st),
+             "prepare random vectors");
 
   for (int rho = 0; rho < c.rounds; ++rho) {
     int32_t* bx = reinterpret_cast<int32_t*>(sv + p.o_bx) + (int64_t)rho * s;
@@ -218,14 +291,16 @@ rece_status rece_forward(rece_plan_t plan, void* stream, const void* X, const vo
     int32_t* py = reinterpret_cast<int32_t*>(sv + p.o_py) + (int64_t)rho * C;
     int32_t* iy = reinterpret_cast<int32_t*>(sv + p.o_iy) + (int64_t)rho * C;
     const void* Btr = static_cast<const char*>(Bt) + (size_t)rho * c.n_b * d * p.esize;
-    RECE_HIP(launch_project_argmax(p.bf16, d, X, s, Btr, c.n_b, bnorm + rho, p.beta_coef, bx,
+    RECE_PHASE(RECE_PHASE_PROJECT, launch_project_argmax(p.bf16, d, X, s, Btr, c.n_b, bnorm + rho, p.beta_coef, bx,
                                    rho == 0 ? xnorm : nullptr, nullptr, counters, st),
              "bucket positions");
-    RECE_HIP(launch_project_argmax(p.bf16, d, Y, C, Btr, c.n_b, bnorm + rho, p.beta_coef, by, nullptr,
+    RECE_PHASE(RECE_PHASE_PROJECT, launch_project_argmax(p.bf16, d, Y, C, Btr, c.n_b, bnorm + rho, p.beta_coef, by, nullptr,
                                    rho == 0 ? reinterpret_cast<uint32_t*>(ymax) : nullptr, counters, st),
              "bucket items");
-    RECE_HIP(launch_counting_sort(bx, nullptr, s, 0, p.nbits_b, sc + p.o_sort, px, ix, st), "sort positions");
-    RECE_HIP(launch_counting_sort(by, nullptr, C, 0, p.nbits_b, sc + p.o_sort, py, iy, st), "sort items");
+    RECE_PHASE(RECE_PHASE_SORT, launch_counting_sort(bx, nullptr, s, 0, p.nbits_b, sc + p.o_sort, px, ix, st),
+               "sort positions");
+    RECE_PHASE(RECE_PHASE_SORT, launch_counting_sort(by, nullptr, C, 0, p.nbits_b, sc + p.o_sort, py, iy, st),
+               "sort items");
 
     SelectArgs a{};
     a.X = X;
@@ -255,7 +330,7 @@ rece_status rece_forward(rece_plan_t plan, void* stream, const void* X, const vo
     a.nmem = reinterpret_cast<int32_t*>(sv + p.o_nmem);
     a.negs = p.o_negs ? reinterpret_cast<int32_t*>(sv + p.o_negs) : nullptr;
     a.counters = counters;
-    RECE_HIP(launch_select(p.bf16, d, p.waves_sel, a, st), "chunk logits and top-k");
+    RECE_PHASE(RECE_PHASE_SELECT, launch_select(p.bf16, d, p.waves_sel, a, st), "chunk logits and top-k");
   }
 
   CeArgs ce{};
@@ -274,7 +349,7 @@ rece_status rece_forward(rece_plan_t plan, void* stream, const void* X, const vo
   ce.partial = reinterpret_cast<float*>(sc + p.o_part);
   ce.counters = counters;
   ce.validate = (c.flags & RECE_FLAG_VALIDATE_IDS) ? 1 : 0;
-  RECE_HIP(launch_ce(p.bf16, d, ce, loss, st), "loss");
+  RECE_PHASE(RECE_PHASE_LOSS, launch_ce(p.bf16, d, ce, loss, st), "loss");
   return RECE_OK;
 }
 
@@ -320,8 +395,8 @@ rece_status rece_backward(rece_plan_t plan, void* stream, const void* X, const v
     b.rho = rho;
     b.perm_x = reinterpret_cast<const int32_t*>(sv + p.o_px) + (int64_t)rho * s;
     b.perm_y = reinterpret_cast<const int32_t*>(sv + p.o_py) + (int64_t)rho * C;
-    RECE_HIP(launch_bwd_rows(p.bf16, d, 4, b, st), "dX");
-    RECE_HIP(launch_bwd_items(p.bf16, d, 4, b, p.itiles, st), "dY");
+    RECE_PHASE(RECE_PHASE_BWD_DX, launch_bwd_rows(p.bf16, d, 4, b, st), "dX");
+    RECE_PHASE(RECE_PHASE_BWD_DY, launch_bwd_items(p.bf16, d, 4, b, p.itiles, st), "dY");
   }
   // positives: LSD counting sort of positions by positive id, then the segmented reduction
   int32_t* bufs[2] = {reinterpret_cast<int32_t*>(sc + p.o_pp0), reinterpret_cast<int32_t*>(sc + p.o_pp1)};
@@ -330,10 +405,12 @@ rece_status rece_backward(rece_plan_t plan, void* stream, const void* X, const v
   for (int pass = 0, shift = 0; shift < total_bits; ++pass, shift += 12) {
     const int nb = std::min(12, total_bits - shift);
     int32_t* outp = bufs[pass & 1];
-    RECE_HIP(launch_counting_sort(pos, sorted, s, shift, nb, sc + p.o_sort, outp, nullptr, st), "sort positives");
+    RECE_PHASE(RECE_PHASE_SORT, launch_counting_sort(pos, sorted, s, shift, nb, sc + p.o_sort, outp, nullptr, st),
+               "sort positives");
     sorted = outp;
   }
-  RECE_HIP(launch_pos_dy(p.bf16, d, b, sorted, reinterpret_cast<float*>(sc + p.o_ppart), st), "positive dY");
+  RECE_PHASE(RECE_PHASE_BWD_POS, launch_pos_dy(p.bf16, d, b, sorted, reinterpret_cast<float*>(sc + p.o_ppart), st),
+             "positive dY");
   return RECE_OK;
 }
 

@@ -53,7 +53,7 @@ extern "C" {
 typedef enum {
   RECE_OK = 0,
   RECE_ERR_INVALID_ARGUMENT = 1,   /* bad config value, NULL or misaligned pointer */
-  RECE_ERR_UNSUPPORTED = 2,        /* valid but not built (e.g. d not a multiple of 32) */
+  RECE_ERR_UNSUPPORTED = 2,        /* valid but not built (e.g. d outside {32,64,128,256}) */
   RECE_ERR_WORKSPACE_TOO_SMALL = 3,
   RECE_ERR_HIP = 4,                /* a HIP runtime call failed; see rece_last_error() */
   RECE_ERR_DEVICE_CHECK = 5,       /* a device-side check failed (read by rece_check) */
@@ -70,7 +70,7 @@ typedef enum { RECE_VARIANT_RECE = 0, RECE_VARIANT_SCE = 1 } rece_variant;
 typedef struct {
   int64_t s;        /* positions (batch x sequence length collapsed), >= 1 */
   int64_t C;        /* catalogue size, >= 2 */
-  int32_t d;        /* embedding dimension: multiple of 32, 32..512 */
+  int32_t d;        /* embedding dimension: 32, 64, 128 or 256 */
   int32_t n_b;      /* random vectors (buckets) per round, 1..4096 */
   int32_t n_c;      /* RECE chunks, 1..min(s, C); ignored by SCE */
   int32_t k;        /* negatives kept per position (RECE: per round), 0..C-1 */
@@ -84,8 +84,10 @@ typedef struct {
 
 typedef struct rece_plan_s* rece_plan_t;
 
-/* Validate `cfg` and build an immutable host-side plan (no GPU work, no device
- * memory).  On error *out is NULL.  A plan may be used from several threads. */
+/* Validate `cfg` and build a host-side plan (no GPU work, no device memory).
+ * On error *out is NULL.  A plan may be used from several threads (profiling
+ * aside, see rece_profile_enable); concurrent calls need their own scratch and
+ * saved buffers. */
 rece_status rece_plan(const rece_config* cfg, rece_plan_t* out);
 rece_status rece_plan_destroy(rece_plan_t plan);
 
@@ -141,6 +143,27 @@ rece_status rece_export_bytes(rece_plan_t plan, int stage, size_t* bytes);
  * RECE_ERR_DEVICE_CHECK if an id was out of range (with VALIDATE_IDS) or a
  * selection buffer overflowed; RECE_OK otherwise. */
 rece_status rece_check(rece_plan_t plan, void* stream, const void* saved);
+
+/* Kernel timing.  rece_profile_enable(plan, mask) with mask != 0 clears earlier
+ * records and, from then on, brackets the kernel launches of every phase p with
+ * bit p set in mask (mask = -1: all phases) with HIP events recorded on the
+ * caller's stream; mask = 0 stops recording.  rece_profile_read waits for the
+ * recorded events and returns the total milliseconds and the number of
+ * bracketed launches of one phase.  Profiling state is the one mutable part of
+ * a plan: do not profile one plan from two threads at once. */
+typedef enum {
+  RECE_PHASE_PROJECT = 0,   /* bucketing (projection + argmax) */
+  RECE_PHASE_SORT = 1,      /* counting sorts (buckets and positive ids) */
+  RECE_PHASE_SELECT = 2,    /* chunk logits + top-k */
+  RECE_PHASE_LOSS = 3,      /* positive logit, log-sum-exp, mean */
+  RECE_PHASE_BWD_DX = 4,    /* backward, dX */
+  RECE_PHASE_BWD_DY = 5,    /* backward, dY of the kept negatives */
+  RECE_PHASE_BWD_POS = 6,   /* backward, dY of the positives */
+  RECE_PHASE_OTHER = 7,     /* small set-up kernels */
+  RECE_NUM_PHASES = 8
+} rece_phase;
+rece_status rece_profile_enable(rece_plan_t plan, int mask);
+rece_status rece_profile_read(rece_plan_t plan, int phase, double* total_ms, int64_t* launches);
 
 const char* rece_status_string(rece_status status);
 const char* rece_last_error(void);
