@@ -20,13 +20,14 @@
 // rounds add, so every sum has a fixed order (bit-reproducible).
 #include "rece_device.h"
 #include "rece_internal.h"
+#include "rece_stream.h"
 
 namespace rece {
 
-__device__ __forceinline__ uint16_t bf16_rne(float f) {
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
   u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return u >> 16;
 }
 
 // Upstream gradient of position i's loss.
@@ -34,107 +35,80 @@ __device__ __forceinline__ float gbar_of(const BwdArgs& p, int64_t i) {
   return p.dloss_pp ? p.dloss_pp[i] : p.dloss[0] / (float)p.s;
 }
 
-template <class E> struct TPitch;
-template <> struct TPitch<bf16> { static constexpr int value = 72; };
-template <> struct TPitch<float> { static constexpr int value = 68; };
-constexpr int GP = 68;   // pitch of the per-wave gradient block [16][64]
+constexpr int GP = 68;   // pitch (floats) of the per-wave gradient block [16][TI]
 
-// Stage 64 vectors (ids[n] >= 0, else zeros) as a row-major tile [64][P] and a
-// transposed tile [D][TP].
+// acc[nb] += G[16][TI] . tile[TI][D] for the wave's 16 rows; G in LDS (float), the
+// tile in the swizzled row layout of the streamer (K = tile rows, N = coordinates).
 template <class E, int D>
-__device__ __forceinline__ void load_tiles(const E* __restrict__ src, const int32_t* ids, E* tile, E* tileT,
-                                           int nthreads) {
-  constexpr int P = Pitch<E, D>::value;
-  constexpr int TP = TPitch<E>::value;
-  constexpr int EPP = 16 / (int)sizeof(E);
-  constexpr int PIECES = D / EPP;
-  for (int pc = threadIdx.x; pc < 64 * PIECES; pc += nthreads) {
-    const int nb = pc / PIECES, part = pc % PIECES;
-    const int j = ids[nb];
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (j >= 0) val = *reinterpret_cast<const u32x4*>(src + (int64_t)j * D + part * EPP);
-    *reinterpret_cast<u32x4*>(tile + nb * P + part * EPP) = val;
-    const E* ev = reinterpret_cast<const E*>(&val);
-#pragma unroll
-    for (int t = 0; t < EPP; ++t) tileT[(part * EPP + t) * TP + nb] = ev[t];
-  }
-}
-
-// acc[nb] += G[16][64] . T[d][64]^T for the wave's 16 rows; G in LDS (float).
-template <class E, int D>
-__device__ __forceinline__ void accumulate_gt(f32x4 (&acc)[D / 16], const float* G, const E* tileT) {
-  constexpr int TP = TPitch<E>::value;
+__device__ __forceinline__ void accumulate_gt(f32x4 (&acc)[D / 16], const float* Gb, const char* rows) {
+  using G = TileGeom<E, D>;
   const int l = lane_id();
   const int q = l >> 4;
   if constexpr (sizeof(E) == 2) {
-    bf16x8 ahi[2], alo[2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      uint16_t h[8], lo[8];
+    for (int ks = 0; ks < G::TI / 32; ++ks) {
+      uint32_t ph[4], pl[4];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const float gv = G[(l & 15) * GP + 32 * ks + 8 * q + t];
-        h[t] = bf16_rne(gv);
-        lo[t] = bf16_rne(gv - __uint_as_float((uint32_t)h[t] << 16));
+      for (int t = 0; t < 8; t += 2) {
+        const float g0 = Gb[(l & 15) * GP + 32 * ks + 8 * q + t];
+        const float g1 = Gb[(l & 15) * GP + 32 * ks + 8 * q + t + 1];
+        const uint32_t h0 = bf16_rne(g0), h1 = bf16_rne(g1);
+        const uint32_t l0 = bf16_rne(g0 - __uint_as_float(h0 << 16)), l1 = bf16_rne(g1 - __uint_as_float(h1 << 16));
+        ph[t / 2] = h0 | (h1 << 16);
+        pl[t / 2] = l0 | (l1 << 16);
       }
-      u32x4 ph, pl;
+      const bf16x8 ahi = __builtin_bit_cast(bf16x8, u32x4{ph[0], ph[1], ph[2], ph[3]});
+      const bf16x8 alo = __builtin_bit_cast(bf16x8, u32x4{pl[0], pl[1], pl[2], pl[3]});
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        ph[t] = (uint32_t)h[2 * t] | ((uint32_t)h[2 * t + 1] << 16);
-        pl[t] = (uint32_t)lo[2 * t] | ((uint32_t)lo[2 * t + 1] << 16);
-      }
-      ahi[ks] = __builtin_bit_cast(bf16x8, ph);
-      alo[ks] = __builtin_bit_cast(bf16x8, pl);
-    }
+      for (int nb = 0; nb < D / 16; ++nb) {
+        const int dim = 16 * nb + (l & 15);
+        uint32_t bw[4];
 #pragma unroll
-    for (int nb = 0; nb < D / 16; ++nb) {
-      const E* trow = tileT + (16 * nb + (l & 15)) * TP;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const u32x4 raw = *reinterpret_cast<const u32x4*>(trow + 32 * ks + 8 * q);
-        const bf16x8 b = __builtin_bit_cast(bf16x8, raw);
-        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[ks], b, acc[nb], 0, 0, 0);
-        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[ks], b, acc[nb], 0, 0, 0);
+        for (int t = 0; t < 8; t += 2) {
+          const int item = 32 * ks + 8 * q + t;
+          bw[t / 2] = tile_bits16<D>(rows, item, dim) | (tile_bits16<D>(rows, item + 1, dim) << 16);
+        }
+        const bf16x8 b = __builtin_bit_cast(bf16x8, u32x4{bw[0], bw[1], bw[2], bw[3]});
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, b, acc[nb], 0, 0, 0);
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, b, acc[nb], 0, 0, 0);
       }
     }
   } else {
-    float av[16];
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) av[ks] = G[(l & 15) * GP + 4 * ks + q];
+    for (int ks = 0; ks < G::TI / 4; ++ks) {
+      const float a = Gb[(l & 15) * GP + 4 * ks + q];
 #pragma unroll
-    for (int nb = 0; nb < D / 16; ++nb) {
-      const float* trow = reinterpret_cast<const float*>(tileT) + (16 * nb + (l & 15)) * TP;
-#pragma unroll
-      for (int ks = 0; ks < 16; ++ks)
-        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[ks], trow[4 * ks + q], acc[nb], 0, 0, 0);
+      for (int nb = 0; nb < D / 16; ++nb)
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, tile_elem<float, D>(rows, 4 * ks + q, 16 * nb + (l & 15)),
+                                                        acc[nb], 0, 0, 0);
     }
   }
 }
 
-template <class E, int D>
-__host__ __device__ constexpr size_t bwd_common_lds() {
-  return (size_t)64 * Pitch<E, D>::value * sizeof(E) + (size_t)D * TPitch<E>::value * sizeof(E) + 64 * 4 +
-         (size_t)MAX_ROUNDS * 64 * 4;
-}
-
 // ------------------------------------------------------------------ dX
+__host__ __device__ constexpr size_t rows_slot_bytes(size_t row_bytes, int rounds) {
+  return row_bytes + 256 * (size_t)rounds;
+}
+constexpr size_t ROWS_WAVE_LDS = 16 * GP * 4 + 16 * MAX_ROUNDS * sizeof(PrevRow);
+
 template <class E, int D, int NW>
-__global__ __launch_bounds__(64 * NW) void k_bwd_rows(BwdArgs p) {
+__global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_bwd_rows(BwdArgs p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  constexpr int P = Pitch<E, D>::value;
+  using G = TileGeom<E, D>;
+  constexpr int TI = G::TI;
+  constexpr int NCB = TI / 16;
   constexpr int TR = 16 * NW;
-  const E* __restrict__ X = reinterpret_cast<const E*>(p.X);
   const E* __restrict__ Y = reinterpret_cast<const E*>(p.Y);
-  E* tile = reinterpret_cast<E*>(smem);
-  E* tileT = tile + 64 * P;
-  int32_t* yid = reinterpret_cast<int32_t*>(tileT + D * TPitch<E>::value);
-  int32_t* cy2s = yid + 64;   // [MAX_ROUNDS][64]
-  const int w = threadIdx.x >> 6, l = lane_id(), g = l >> 4;
-  char* wb = smem + bwd_common_lds<E, D>() + (size_t)w * (16 * GP * 4 + 16 * MAX_ROUNDS * sizeof(PrevRow));
-  float* G = reinterpret_cast<float*>(wb);
-  PrevRow* prev = reinterpret_cast<PrevRow*>(wb + 16 * GP * 4);
+  const E* __restrict__ Xs = reinterpret_cast<const E*>(p.Xs);
+  const E* __restrict__ Ys = reinterpret_cast<const E*>(p.Ys);
   const int n_c = p.n_c, rho = p.rho;
-  const int64_t s = p.s;
+  const int64_t s = p.s, C = p.C;
+  const size_t slot_bytes = rows_slot_bytes(G::ROW_BYTES, p.rounds);
+  char* ring = smem;
+  const int w = threadIdx.x >> 6, l = lane_id(), g = l >> 4;
+  char* wb = smem + 3 * slot_bytes + (size_t)w * ROWS_WAVE_LDS;
+  float* Gb = reinterpret_cast<float*>(wb);
+  PrevRow* prev = reinterpret_cast<PrevRow*>(wb + 16 * GP * 4);
 
   const int c = blockIdx.x / p.tiles_per_chunk;
   const int tile_i = blockIdx.x % p.tiles_per_chunk;
@@ -142,100 +116,83 @@ __global__ __launch_bounds__(64 * NW) void k_bwd_rows(BwdArgs p) {
   const int64_t tile0 = x0 + (int64_t)tile_i * TR;
   if (tile0 >= x1) return;
   const int64_t wrow0 = tile0 + 16 * w;
-
-  int wc[3];
-  int nwc = 0;
-  wc[nwc++] = c;
-  if (n_c >= 2) wc[nwc++] = (c + n_c - 1) % n_c;
-  if (n_c >= 3) wc[nwc++] = (c + 1) % n_c;
+  Ranges win;
+  win.init(c, n_c, C, TI);
+  const int ntiles = win.ntiles();
 
   const int64_t pA = wrow0 + (l & 15);
-  const int iA = pA < x1 ? p.perm_x[pA] : -1;
   Frag<E, D> afr;
-  afr.load_global(iA >= 0 ? X + (int64_t)iA * D : nullptr);
-  if (l < 16) {
-    for (int r2 = 0; r2 < rho; ++r2) {
-      PrevRow pr{0.0, 0.f, 0.f, 0, 0};
-      if (iA >= 0) {
-        const int64_t o2 = (int64_t)r2 * s + iA;
-        pr.te = p.thr_e[o2];
-        pr.lo = p.thr_lo[o2];
-        pr.hi = p.thr_hi[o2];
-        pr.tid = p.thr_id[o2];
-        pr.cx = chunk_of(p.inv_x[o2], s, n_c);
-      }
-      prev[l * MAX_ROUNDS + r2] = pr;
-    }
-  }
+  afr.load_global(pA < x1 ? Xs + pA * D : nullptr);
+  if (l < 16)
+    for (int r2 = 0; r2 < rho; ++r2)
+      prev[l * MAX_ROUNDS + r2] = pA < x1 ? p.prev[(int64_t)r2 * s + pA] : PrevRow{};
 
   int i_v[4], pos_v[4], tid_v[4];
-  float lse_v[4], gb_v[4], lo_v[4], hi_v[4];
+  float lse_v[4], gb_v[4], lo_v[4], hi_v[4], lpos_v[4];
   double te_v[4];
   bool rv[4];
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const int64_t pr = wrow0 + 4 * g + v;
     rv[v] = pr < x1;
-    const int i = rv[v] ? p.perm_x[pr] : 0;
-    const int64_t o = (int64_t)rho * s + i;
-    i_v[v] = i;
-    pos_v[v] = rv[v] ? p.pos[i] : -1;
-    lse_v[v] = p.lse[i];
-    gb_v[v] = gbar_of(p, i);
-    lo_v[v] = p.thr_lo[o];
-    hi_v[v] = p.thr_hi[o];
-    te_v[v] = p.thr_e[o];
-    tid_v[v] = p.thr_id[o];
+    const PosRec rc = p.rec[rv[v] ? pr : x0];
+    i_v[v] = rc.i;
+    pos_v[v] = rv[v] ? rc.pos : -1;
+    lse_v[v] = rc.lse;
+    gb_v[v] = rc.gb;
+    lo_v[v] = rc.lo;
+    hi_v[v] = rc.hi;
+    te_v[v] = rc.te;
+    tid_v[v] = rc.tid;
+    lpos_v[v] = rc.lpos;
   }
   f32x4 dacc[D / 16];
 #pragma unroll
   for (int nb = 0; nb < D / 16; ++nb) dacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int q = 0; q < nwc; ++q) {
-    const int64_t y0 = chunk_start(wc[q], p.C, n_c), y1 = chunk_start(wc[q] + 1, p.C, n_c);
-    for (int64_t q0 = y0; q0 < y1; q0 += 64) {
-      __syncthreads();
-      if (threadIdx.x < 64) {
-        const int j = q0 + threadIdx.x < y1 ? p.perm_y[q0 + threadIdx.x] : -1;
-        yid[threadIdx.x] = j;
-        for (int r2 = 0; r2 < rho; ++r2)
-          cy2s[r2 * 64 + threadIdx.x] = j >= 0 ? chunk_of(p.inv_y[(int64_t)r2 * p.C + j], p.C, n_c) : 0;
-      }
-      __syncthreads();
-      load_tiles<E, D>(Y, yid, tile, tileT, 64 * NW);
-      __syncthreads();
-      f32x4 acc[4];
+  const int ncopies = G::ROW_DMA + 1 + rho;
+  int my_copies = 0;
+  for (int u = w; u < ncopies; u += NW) ++my_copies;
+  __syncthreads();
+  issue_window_tile<E, D>(ring, slot_bytes, win, 0, Ys, p.perm_y, p.cyp, C, rho, w, NW);
+  if (ntiles > 1) issue_window_tile<E, D>(ring, slot_bytes, win, 1, Ys, p.perm_y, p.cyp, C, rho, w, NW);
+  for (int t = 0; t < ntiles; ++t) {
+    wait_vmcnt(t + 1 < ntiles ? my_copies : 0);
+    raw_barrier();
+    if (t + 2 < ntiles) issue_window_tile<E, D>(ring, slot_bytes, win, t + 2, Ys, p.perm_y, p.cyp, C, rho, w, NW);
+    const int64_t q0 = range_tile_start(win, t, TI), q1 = range_tile_end(win, t);
+    const char* slot = ring + (size_t)(t % 3) * slot_bytes;
+    const int32_t* tid_ = reinterpret_cast<const int32_t*>(slot + G::ROW_BYTES);
+    const int32_t* tcy = tid_ + 64;
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        Frag<E, D> bf;
-        bf.load_lds(tile + (cb * 16 + (l & 15)) * P);
-        acc[cb] = mma_block(afr, bf, f32x4{0.f, 0.f, 0.f, 0.f});
-      }
+    for (int cb = 0; cb < NCB; ++cb) {
+      const int n = cb * 16 + (l & 15);
+      Frag<E, D> bf;
+      TileFrag<E, D>::load(bf, slot, n);
+      const f32x4 acc = mma_block(afr, bf, f32x4{0.f, 0.f, 0.f, 0.f});
+      const bool nvalid = q0 + n < q1;
+      const int j = tid_[n];
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        const int n = cb * 16 + (l & 15);
-        const int j = yid[n];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float a = acc[cb][v];
-          float gv = 0.0f;
-          if (rv[v] && j >= 0 && j != pos_v[v]) {
-            const E* xrow = X + (int64_t)i_v[v] * D;
-            bool mem = beats<E, D>(a, lo_v[v], hi_v[v], te_v[v], tid_v[v], xrow, Y, j, p.counters);
-            for (int r2 = 0; r2 < rho && mem; ++r2) {
-              const PrevRow pr = prev[(4 * g + v) * MAX_ROUNDS + r2];
-              if (!in_window(pr.cx, cy2s[r2 * 64 + n], n_c)) continue;
-              if (beats<E, D>(a, pr.lo, pr.hi, pr.te, pr.tid, xrow, Y, j, p.counters)) mem = false;
-            }
-            if (mem) gv = expf(a - lse_v[v]) * gb_v[v];
+      for (int v = 0; v < 4; ++v) {
+        const float a = acc[v];
+        const int r = 4 * g + v;
+        float gv = 0.0f;
+        if (rv[v] && nvalid && j != pos_v[v]) {
+          const E* xrow = Xs + (wrow0 + r) * D;
+          bool mem = beats<E, D>(a, lo_v[v], hi_v[v], te_v[v], tid_v[v], xrow, Y, j, p.counters);
+          for (int r2 = 0; r2 < rho && mem; ++r2) {
+            const PrevRow pr = prev[r * MAX_ROUNDS + r2];
+            if (!in_window(pr.cx, tcy[64 * r2 + n], n_c)) continue;
+            if (beats<E, D>(a, pr.lo, pr.hi, pr.te, pr.tid, xrow, Y, j, p.counters)) mem = false;
           }
-          G[(4 * g + v) * GP + n] = gv;
+          if (mem) gv = expf(a - lse_v[v]) * gb_v[v];
         }
+        Gb[r * GP + n] = gv;
       }
-      wave_sync();
-      accumulate_gt<E, D>(dacc, G, tileT);
-      wave_sync();
     }
+    wave_sync();
+    accumulate_gt<E, D>(dacc, Gb, slot);
+    wave_sync();
   }
 
   // write: rows 4g+v, coordinates 16nb + (l & 15); round 0 adds the positive term
@@ -246,7 +203,7 @@ __global__ __launch_bounds__(64 * NW) void k_bwd_rows(BwdArgs p) {
     float gpos = 0.0f;
     const int pclamp = pos_v[v] < 0 ? 0 : (pos_v[v] >= p.C ? (int)(p.C - 1) : pos_v[v]);
     const E* ypos = Y + (int64_t)pclamp * D;
-    if (rho == 0) gpos = (expf(p.lpos[i_v[v]] - lse_v[v]) - 1.0f) * gb_v[v];
+    if (rho == 0) gpos = (expf(lpos_v[v] - lse_v[v]) - 1.0f) * gb_v[v];
 #pragma unroll
     for (int nb = 0; nb < D / 16; ++nb) {
       const int t = 16 * nb + (l & 15);
@@ -261,32 +218,54 @@ __global__ __launch_bounds__(64 * NW) void k_bwd_rows(BwdArgs p) {
 }
 
 // ------------------------------------------------------------------ dY (negatives)
-struct PosInfo {   // a position's data in the current round, staged per tile
-  float lse, gb, lo, hi;
-  double te;
-  int i, pos, tid, pad;
+template <class E, int D>
+struct ItemsLayout {
+  using G = TileGeom<E, D>;
+  using RC = RecCopy<sizeof(PosRec), G::TI>;
+  using PC = RecCopy<sizeof(PrevRow), G::TI>;
+  static __host__ __device__ constexpr size_t slot_bytes(int rounds) {
+    return (size_t)G::ROW_BYTES + RC::LDS_BYTES + (size_t)(rounds > 1 ? rounds - 1 : 0) * PC::LDS_BYTES;
+  }
 };
+constexpr size_t ITEMS_WAVE_LDS = 16 * GP * 4 + 16 * MAX_ROUNDS * 4;
+
+// Copies of position tile t: rows of the sorted positions, their records, and their
+// records of each earlier round, into ring slot t % 3.
+template <class E, int D>
+__device__ __forceinline__ void issue_items_tile(char* ring, size_t slot_bytes, Ranges r, int t, const E* xs,
+                                                 const PosRec* rec, const PrevRow* prev, int64_t s, int rho,
+                                                 int wave, int nwaves) {
+  using G = TileGeom<E, D>;
+  using LY = ItemsLayout<E, D>;
+  const int64_t q0 = range_tile_start(r, t, G::TI), q1 = range_tile_end(r, t);
+  char* slot = ring + (size_t)(t % 3) * slot_bytes;
+  dma_rows<E, D>(slot, xs, q0, q1, wave, nwaves);
+  char* rb = slot + G::ROW_BYTES;
+  LY::RC::issue(rb, rec, q0, q1, G::ROW_DMA, wave, nwaves);
+  for (int r2 = 0; r2 < rho; ++r2)
+    LY::PC::issue(rb + LY::RC::LDS_BYTES + (size_t)r2 * LY::PC::LDS_BYTES, prev + (int64_t)r2 * s, q0, q1,
+                  G::ROW_DMA + LY::RC::COPIES + r2 * LY::PC::COPIES, wave, nwaves);
+}
 
 template <class E, int D, int NW>
-__global__ __launch_bounds__(64 * NW) void k_bwd_items(BwdArgs p, int itiles) {
+__global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_bwd_items(BwdArgs p, int itiles) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  constexpr int P = Pitch<E, D>::value;
+  using G = TileGeom<E, D>;
+  using LY = ItemsLayout<E, D>;
+  constexpr int TI = G::TI;
+  constexpr int NCB = TI / 16;
   constexpr int TR = 16 * NW;
-  const E* __restrict__ X = reinterpret_cast<const E*>(p.X);
   const E* __restrict__ Y = reinterpret_cast<const E*>(p.Y);
-  E* tile = reinterpret_cast<E*>(smem);
-  E* tileT = tile + 64 * P;
-  int32_t* xid = reinterpret_cast<int32_t*>(tileT + D * TPitch<E>::value);
-  char* after = smem + bwd_common_lds<E, D>();
-  PosInfo* pinfo = reinterpret_cast<PosInfo*>(after);                          // [64]
-  PrevRow* pprev = reinterpret_cast<PrevRow*>(after + 64 * sizeof(PosInfo));   // [64][MAX_ROUNDS]
-  const int w = threadIdx.x >> 6, l = lane_id(), g = l >> 4;
-  char* wbase = after + 64 * sizeof(PosInfo) + 64 * MAX_ROUNDS * sizeof(PrevRow) +
-                (size_t)w * (16 * GP * 4 + 16 * MAX_ROUNDS * 4);
-  float* G = reinterpret_cast<float*>(wbase);
-  int32_t* cy2w = reinterpret_cast<int32_t*>(wbase + 16 * GP * 4);   // [16][MAX_ROUNDS]
+  const E* __restrict__ Xs = reinterpret_cast<const E*>(p.Xs);
+  const E* __restrict__ Ys = reinterpret_cast<const E*>(p.Ys);
   const int n_c = p.n_c, rho = p.rho;
   const int64_t s = p.s, C = p.C;
+  const size_t slot_bytes = LY::slot_bytes(p.rounds);
+  char* ring = smem;
+  const int w = threadIdx.x >> 6, l = lane_id(), g = l >> 4;
+  char* wb = smem + 3 * slot_bytes + (size_t)w * ITEMS_WAVE_LDS;
+  float* Gb = reinterpret_cast<float*>(wb);
+  int32_t* cy2w = reinterpret_cast<int32_t*>(wb + 16 * GP * 4);   // [16][MAX_ROUNDS]
 
   const int c = blockIdx.x / itiles;
   const int it = blockIdx.x % itiles;
@@ -294,14 +273,15 @@ __global__ __launch_bounds__(64 * NW) void k_bwd_items(BwdArgs p, int itiles) {
   const int64_t tile0 = y0 + (int64_t)it * TR;
   if (tile0 >= y1) return;
   const int64_t wq0 = tile0 + 16 * w;
+  Ranges xr;
+  xr.init(c, n_c, s, TI);   // X-chunks whose window holds item chunk c (the relation is symmetric)
+  const int ntiles = xr.ntiles();
 
   const int64_t qA = wq0 + (l & 15);
-  const int jA = qA < y1 ? p.perm_y[qA] : -1;
   Frag<E, D> afr;
-  afr.load_global(jA >= 0 ? Y + (int64_t)jA * D : nullptr);
+  afr.load_global(qA < y1 ? Ys + qA * D : nullptr);
   if (l < 16)
-    for (int r2 = 0; r2 < rho; ++r2)
-      cy2w[l * MAX_ROUNDS + r2] = jA >= 0 ? chunk_of(p.inv_y[(int64_t)r2 * C + jA], C, n_c) : 0;
+    for (int r2 = 0; r2 < rho; ++r2) cy2w[l * MAX_ROUNDS + r2] = qA < y1 ? p.cyp[(int64_t)r2 * C + qA] : 0;
 
   int j_v[4];
   bool rv[4];
@@ -315,80 +295,52 @@ __global__ __launch_bounds__(64 * NW) void k_bwd_items(BwdArgs p, int itiles) {
 #pragma unroll
   for (int nb = 0; nb < D / 16; ++nb) dacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // X-chunks whose window holds item chunk c (the window relation is symmetric)
-  int xc[3];
-  int nxc = 0;
-  xc[nxc++] = c;
-  if (n_c >= 2) xc[nxc++] = (c + n_c - 1) % n_c;
-  if (n_c >= 3) xc[nxc++] = (c + 1) % n_c;
+  const int ncopies = G::ROW_DMA + LY::RC::COPIES + rho * LY::PC::COPIES;
+  int my_copies = 0;
+  for (int u = w; u < ncopies; u += NW) ++my_copies;
 
-  for (int q = 0; q < nxc; ++q) {
-    const int64_t px0 = chunk_start(xc[q], s, n_c), px1 = chunk_start(xc[q] + 1, s, n_c);
-    for (int64_t p0 = px0; p0 < px1; p0 += 64) {
-      __syncthreads();
-      if (threadIdx.x < 64) {
-        const int64_t pp = p0 + threadIdx.x;
-        const int i = pp < px1 ? p.perm_x[pp] : -1;
-        xid[threadIdx.x] = i;
-        PosInfo pi{0.f, 0.f, 0.f, 0.f, 0.0, i, -1, 0, 0};
-        if (i >= 0) {
-          const int64_t o = (int64_t)rho * s + i;
-          pi.lse = p.lse[i];
-          pi.gb = gbar_of(p, i);
-          pi.lo = p.thr_lo[o];
-          pi.hi = p.thr_hi[o];
-          pi.te = p.thr_e[o];
-          pi.tid = p.thr_id[o];
-          pi.pos = p.pos[i];
-          for (int r2 = 0; r2 < rho; ++r2) {
-            const int64_t o2 = (int64_t)r2 * s + i;
-            PrevRow pr;
-            pr.te = p.thr_e[o2];
-            pr.lo = p.thr_lo[o2];
-            pr.hi = p.thr_hi[o2];
-            pr.tid = p.thr_id[o2];
-            pr.cx = chunk_of(p.inv_x[o2], s, n_c);
-            pprev[threadIdx.x * MAX_ROUNDS + r2] = pr;
+
+  __syncthreads();
+  issue_items_tile<E, D>(ring, slot_bytes, xr, 0, Xs, p.rec, p.prev, s, rho, w, NW);
+  if (ntiles > 1) issue_items_tile<E, D>(ring, slot_bytes, xr, 1, Xs, p.rec, p.prev, s, rho, w, NW);
+  for (int t = 0; t < ntiles; ++t) {
+    wait_vmcnt(t + 1 < ntiles ? my_copies : 0);
+    raw_barrier();
+    if (t + 2 < ntiles) issue_items_tile<E, D>(ring, slot_bytes, xr, t + 2, Xs, p.rec, p.prev, s, rho, w, NW);
+    const int64_t q0 = range_tile_start(xr, t, TI), q1 = range_tile_end(xr, t);
+    const char* slot = ring + (size_t)(t % 3) * slot_bytes;
+    const PosRec* recs = reinterpret_cast<const PosRec*>(slot + G::ROW_BYTES);
+    const PrevRow* prevs = reinterpret_cast<const PrevRow*>(slot + G::ROW_BYTES + LY::RC::LDS_BYTES);
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const int n = cb * 16 + (l & 15);
+      Frag<E, D> bf;
+      TileFrag<E, D>::load(bf, slot, n);
+      const f32x4 acc = mma_block(afr, bf, f32x4{0.f, 0.f, 0.f, 0.f});
+      const bool nvalid = q0 + n < q1;
+      const PosRec pi = recs[n];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float a = acc[v];
+        const int j = j_v[v];
+        const int r = 4 * g + v;
+        float gv = 0.0f;
+        if (rv[v] && nvalid && j != pi.pos) {
+          const E* xrow = Xs + (q0 + n) * D;
+          bool mem = beats<E, D>(a, pi.lo, pi.hi, pi.te, pi.tid, xrow, Y, j, p.counters);
+          for (int r2 = 0; r2 < rho && mem; ++r2) {
+            const PrevRow pr = prevs[(size_t)r2 * (LY::PC::LDS_BYTES / sizeof(PrevRow)) + n];
+            if (!in_window(pr.cx, cy2w[r * MAX_ROUNDS + r2], n_c)) continue;
+            if (beats<E, D>(a, pr.lo, pr.hi, pr.te, pr.tid, xrow, Y, j, p.counters)) mem = false;
           }
+          if (mem) gv = expf(a - pi.lse) * pi.gb;
         }
-        pinfo[threadIdx.x] = pi;
+        Gb[r * GP + n] = gv;
       }
-      __syncthreads();
-      load_tiles<E, D>(X, xid, tile, tileT, 64 * NW);
-      __syncthreads();
-      f32x4 acc[4];
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        Frag<E, D> bf;
-        bf.load_lds(tile + (cb * 16 + (l & 15)) * P);
-        acc[cb] = mma_block(afr, bf, f32x4{0.f, 0.f, 0.f, 0.f});
-      }
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        const int n = cb * 16 + (l & 15);
-        const PosInfo pi = pinfo[n];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float a = acc[cb][v];
-          const int j = j_v[v];
-          float gv = 0.0f;
-          if (rv[v] && pi.i >= 0 && j != pi.pos) {
-            const E* xrow = X + (int64_t)pi.i * D;
-            bool mem = beats<E, D>(a, pi.lo, pi.hi, pi.te, pi.tid, xrow, Y, j, p.counters);
-            for (int r2 = 0; r2 < rho && mem; ++r2) {
-              const PrevRow pr = pprev[n * MAX_ROUNDS + r2];
-              if (!in_window(pr.cx, cy2w[(4 * g + v) * MAX_ROUNDS + r2], n_c)) continue;
-              if (beats<E, D>(a, pr.lo, pr.hi, pr.te, pr.tid, xrow, Y, j, p.counters)) mem = false;
-            }
-            if (mem) gv = expf(a - pi.lse) * pi.gb;
-          }
-          G[(4 * g + v) * GP + n] = gv;
-        }
-      }
-      wave_sync();
-      accumulate_gt<E, D>(dacc, G, tileT);
-      wave_sync();
     }
+    wave_sync();
+    accumulate_gt<E, D>(dacc, Gb, slot);
+    wave_sync();
   }
 
 #pragma unroll
@@ -517,18 +469,17 @@ __global__ __launch_bounds__(256) void k_pos_combine(float* __restrict__ dY, con
 
 // ------------------------------------------------------------------ launchers
 template <class E, int D>
-static size_t rows_lds(int NW) {
-  return bwd_common_lds<E, D>() + (size_t)NW * (16 * GP * 4 + 16 * MAX_ROUNDS * sizeof(PrevRow));
+static size_t rows_lds(int NW, int rounds) {
+  return 3 * rows_slot_bytes(TileGeom<E, D>::ROW_BYTES, rounds) + (size_t)NW * ROWS_WAVE_LDS;
 }
 template <class E, int D>
-static size_t items_lds(int NW) {
-  return bwd_common_lds<E, D>() + 64 * sizeof(PosInfo) + 64 * MAX_ROUNDS * sizeof(PrevRow) +
-         (size_t)NW * (16 * GP * 4 + 16 * MAX_ROUNDS * 4);
+static size_t items_lds(int NW, int rounds) {
+  return 3 * ItemsLayout<E, D>::slot_bytes(rounds) + (size_t)NW * ITEMS_WAVE_LDS;
 }
 
 template <class E, int D, int NW>
 static hipError_t launch_rows_t(const BwdArgs& a, hipStream_t st) {
-  const size_t lds = rows_lds<E, D>(NW);
+  const size_t lds = rows_lds<E, D>(NW, a.rounds);
   auto kern = k_bwd_rows<E, D, NW>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -538,7 +489,7 @@ static hipError_t launch_rows_t(const BwdArgs& a, hipStream_t st) {
 }
 template <class E, int D, int NW>
 static hipError_t launch_items_t(const BwdArgs& a, int itiles, hipStream_t st) {
-  const size_t lds = items_lds<E, D>(NW);
+  const size_t lds = items_lds<E, D>(NW, a.rounds);
   auto kern = k_bwd_items<E, D, NW>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

@@ -186,7 +186,7 @@ __global__ __launch_bounds__(256) void k_project_argmax(
     double be = -__builtin_huge_val();
     int bi = 0x7fffffff;
     for (int b = l; b < n_b; b += WAVE) {
-      const double e = exact_dot(x, Bt + (int64_t)b * D, D);
+      const double e = exact_dot<E, D>(x, Bt + (int64_t)b * D);
       if (e > be) {
         be = e;
         bi = b;

@@ -62,13 +62,35 @@ __device__ __forceinline__ uint32_t fkey(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Float64 scalar product summed in coordinate order t = 0..d-1.  Products of
+// Float64 scalar product summed in coordinate order t = 0..D-1.  Products of
 // float32 / bfloat16 values are exact in float64, so fma(a, b, acc) equals
 // acc + a*b rounded once: this is the reference value every selection uses.
-template <class E>
-__device__ double exact_dot(const E* __restrict__ a, const E* __restrict__ b, int d) {
+// Both rows are read in 16-byte pieces, a batch of pieces in flight at a time;
+// only the additions are ordered.
+template <class E, int D>
+__device__ __forceinline__ double exact_dot(const E* __restrict__ a, const E* __restrict__ b) {
+  constexpr int EPP = 16 / (int)sizeof(E);     // elements per piece
+  constexpr int NP = D / EPP;                  // pieces per row
+  constexpr int BATCH = NP < 8 ? NP : 8;
+  const u32x4* pa = reinterpret_cast<const u32x4*>(a);
+  const u32x4* pb = reinterpret_cast<const u32x4*>(b);
   double acc = 0.0;
-  for (int t = 0; t < d; ++t) acc = fma((double)to_f32(a[t]), (double)to_f32(b[t]), acc);
+#pragma unroll
+  for (int p0 = 0; p0 < NP; p0 += BATCH) {
+    u32x4 ra[BATCH], rb[BATCH];
+#pragma unroll
+    for (int q = 0; q < BATCH; ++q) {
+      ra[q] = pa[p0 + q];
+      rb[q] = pb[p0 + q];
+    }
+#pragma unroll
+    for (int q = 0; q < BATCH; ++q) {
+      const E* ea = reinterpret_cast<const E*>(&ra[q]);
+      const E* eb = reinterpret_cast<const E*>(&rb[q]);
+#pragma unroll
+      for (int t = 0; t < EPP; ++t) acc = fma((double)to_f32(ea[t]), (double)to_f32(eb[t]), acc);
+    }
+  }
   return acc;
 }
 
@@ -176,15 +198,26 @@ __device__ __forceinline__ bool beats(float a, float lo, float hi, double te, in
   if (a > hi) return true;
   if (a < lo) return false;
   if (j == tid) return true;
-  const double e = exact_dot(xrow, Y + (int64_t)j * D, D);
+  const double e = exact_dot<E, D>(xrow, Y + (int64_t)j * D);
   atomicAdd(counters + 3, 1u);
   return e > te || (e == te && j <= tid);
 }
 
-struct PrevRow {   // a position's kept-set threshold in an earlier round
+struct PrevRow {   // a position's kept-set threshold in an earlier round (32 bytes)
   double te;
   float lo, hi;
   int tid, cx;
+  int pad0, pad1;
 };
+
+struct PosRec {    // a position's backward data in one round, stored in sorted order (48 bytes)
+  float lse, gb, lo, hi;
+  double te;
+  int tid, pos, i;
+  float lpos;
+  int pad0, pad1;
+};
+static_assert(sizeof(PosRec) == 48, "PosRec is streamed in 16-byte chunks");
+static_assert(sizeof(PrevRow) == 32, "PrevRow is streamed in 16-byte chunks");
 
 }  // namespace rece

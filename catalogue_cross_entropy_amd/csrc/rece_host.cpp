@@ -88,9 +88,9 @@ struct rece_plan_s {
   float beta_coef;
   // saved
   size_t o_cnt, o_bx, o_by, o_px, o_ix, o_py, o_iy, o_te, o_tid, o_tlo, o_thi, o_msh, o_ssum, o_nmem, o_xnorm,
-      o_ymax, o_lse, o_lpos, o_negs, saved_bytes;
+      o_ymax, o_lse, o_lpos, o_negs, o_xs, o_ys, o_cyp, saved_bytes;
   // scratch
-  size_t o_bt, o_bnorm, o_sort, o_part, o_pp0, o_pp1, o_ppart, scratch_bytes;
+  size_t o_bt, o_bnorm, o_sort, o_part, o_pp0, o_pp1, o_ppart, o_rec, o_prev, scratch_bytes;
 };
 
 namespace {
@@ -164,7 +164,7 @@ rece_status rece_plan(const rece_config* cfg, rece_plan_t* out) {
   p->cap = 0;
   p->waves_sel = 1;
   for (int nw : {4, 2, 1}) {
-    if (select_lds_bytes(p->bf16, d, nw, 0) <= 160 * 1024) {
+    if (select_lds_bytes(p->bf16, d, nw, r) <= 160 * 1024) {
       p->waves_sel = nw;
       break;
     }
@@ -198,6 +198,9 @@ rece_status rece_plan(const rece_config* cfg, rece_plan_t* out) {
   p->o_lse = sv.take((size_t)s * 4);
   p->o_lpos = sv.take((size_t)s * 4);
   p->o_negs = (c.flags & RECE_FLAG_KEEP_STAGES) ? sv.take((size_t)r * s * std::max(k, 1) * 4) : 0;
+  p->o_xs = sv.take((size_t)r * s * d * p->esize);
+  p->o_ys = sv.take((size_t)r * C * d * p->esize);
+  p->o_cyp = sv.take((size_t)std::max(1, r * (r - 1) / 2) * C * 4);
   p->saved_bytes = sv.off;
 
   Layout sc;
@@ -210,6 +213,8 @@ rece_status rece_plan(const rece_config* cfg, rece_plan_t* out) {
   p->o_pp0 = sc.take((size_t)s * 4);
   p->o_pp1 = sc.take((size_t)s * 4);
   p->o_ppart = sc.take(pos_partial_bytes(s, d));
+  p->o_rec = sc.take((size_t)r * s * sizeof(PosRec));
+  p->o_prev = sc.take((size_t)std::max(1, r * (r - 1) / 2) * s * sizeof(PrevRow));
   p->scratch_bytes = sc.off;
   *out = p;
   return RECE_OK;
@@ -301,10 +306,24 @@ rece_status rece_forward(rece_plan_t plan, void* stream, const void* X, const vo
                "sort positions");
     RECE_PHASE(RECE_PHASE_SORT, launch_counting_sort(by, nullptr, C, 0, p.nbits_b, sc + p.o_sort, py, iy, st),
                "sort items");
+    char* xs = sv + p.o_xs + (size_t)rho * s * d * p.esize;
+    char* ys = sv + p.o_ys + (size_t)rho * C * d * p.esize;
+    int32_t* cyp = reinterpret_cast<int32_t*>(sv + p.o_cyp) + (int64_t)(rho * (rho - 1) / 2) * C;
+    RECE_PHASE(RECE_PHASE_SORT, launch_gather_rows(X, px, s, d * p.esize, xs, st), "sorted positions");
+    RECE_PHASE(RECE_PHASE_SORT, launch_gather_rows(Y, py, C, d * p.esize, ys, st), "sorted items");
+    for (int r2 = 0; r2 < rho; ++r2)
+      RECE_PHASE(RECE_PHASE_SORT,
+                 launch_prev_chunks(py, reinterpret_cast<const int32_t*>(sv + p.o_iy) + (int64_t)r2 * C, C, c.n_c,
+                                    cyp + (int64_t)r2 * C, st),
+                 "earlier-round chunks");
 
     SelectArgs a{};
     a.X = X;
     a.Y = Y;
+    a.Xs = xs;
+    a.Ys = ys;
+    a.cyp = cyp;
+    a.rounds = c.rounds;
     a.pos = pos;
     a.perm_x = px;
     a.perm_y = py;
@@ -391,10 +410,21 @@ rece_status rece_backward(rece_plan_t plan, void* stream, const void* X, const v
   b.dX = dX;
   b.dY = dY;
   b.counters = reinterpret_cast<uint32_t*>(const_cast<char*>(sv) + p.o_cnt);
+  b.rounds = c.rounds;
+  PosRec* recs = reinterpret_cast<PosRec*>(sc + p.o_rec);
+  PrevRow* prevs = reinterpret_cast<PrevRow*>(sc + p.o_prev);
   for (int rho = 0; rho < c.rounds; ++rho) {
     b.rho = rho;
     b.perm_x = reinterpret_cast<const int32_t*>(sv + p.o_px) + (int64_t)rho * s;
     b.perm_y = reinterpret_cast<const int32_t*>(sv + p.o_py) + (int64_t)rho * C;
+    b.Xs = sv + p.o_xs + (size_t)rho * s * d * p.esize;
+    b.Ys = sv + p.o_ys + (size_t)rho * C * d * p.esize;
+    b.cyp = reinterpret_cast<const int32_t*>(sv + p.o_cyp) + (int64_t)(rho * (rho - 1) / 2) * C;
+    b.rec = recs + (int64_t)rho * s;
+    b.prev = prevs + (int64_t)(rho * (rho - 1) / 2) * s;
+    RECE_PHASE(RECE_PHASE_OTHER, launch_bwd_records(b, b.perm_x, rho, recs + (int64_t)rho * s,
+                                                    prevs + (int64_t)(rho * (rho - 1) / 2) * s, st),
+               "backward records");
     RECE_PHASE(RECE_PHASE_BWD_DX, launch_bwd_rows(p.bf16, d, 4, b, st), "dX");
     RECE_PHASE(RECE_PHASE_BWD_DY, launch_bwd_items(p.bf16, d, 4, b, p.itiles, st), "dY");
   }

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "../../include/rece.h"
+#include "rece_device.h"
 
 namespace rece {
 
@@ -26,13 +27,16 @@ constexpr int ALIST = 64;           // near-tie list capacity at the k-th bounda
 struct SelectArgs {
   const void* X;
   const void* Y;
+  const void* Xs;             // round rho: X rows in sorted order
+  const void* Ys;             // round rho: Y rows in sorted order
+  const int32_t* cyp;         // round rho: [rho][C] chunk of item perm_y[q] in rounds 0..rho-1
   const int32_t* pos;
   const int32_t* perm_x;      // round rho
   const int32_t* perm_y;      // round rho
   const int32_t* inv_x;       // [rounds][s]
   const int32_t* inv_y;       // [rounds][C]
   int64_t s, C;
-  int n_c, k, cap, rho;
+  int n_c, k, cap, rho, rounds;
   int selall;                 // 1: every window has at most k candidates; keep all
   int tiles_per_chunk;
   float beta_coef;            // error-bound coefficient of a float32 logit
@@ -69,6 +73,12 @@ struct CeArgs {
 struct BwdArgs {
   const void* X;
   const void* Y;
+  const void* Xs;             // round rho: X rows in sorted order
+  const void* Ys;             // round rho: Y rows in sorted order
+  const int32_t* cyp;         // round rho: [rho][C] chunk of item perm_y[q] in earlier rounds
+  const PosRec* rec;          // round rho: [s] per sorted position
+  const PrevRow* prev;        // round rho: [rho][s] per sorted position
+  int rounds;
   const int32_t* pos;
   const int32_t* perm_x;      // round rho
   const int32_t* perm_y;      // round rho
@@ -108,6 +118,12 @@ hipError_t launch_bwd_rows(bool is_bf16, int d, int waves, const BwdArgs& a, hip
 hipError_t launch_bwd_items(bool is_bf16, int d, int waves, const BwdArgs& a, int item_tiles_per_chunk,
                             hipStream_t st);
 size_t pos_partial_bytes(int64_t s, int d);
+hipError_t launch_gather_rows(const void* src, const int32_t* perm, int64_t n, int row_bytes, void* dst,
+                              hipStream_t st);
+hipError_t launch_prev_chunks(const int32_t* perm_y, const int32_t* inv_y2, int64_t C, int n_c, int32_t* out,
+                              hipStream_t st);
+hipError_t launch_bwd_records(const BwdArgs& a, const int32_t* perm_x, int rho, PosRec* rec, PrevRow* prev,
+                              hipStream_t st);
 hipError_t launch_pos_dy(bool is_bf16, int d, const BwdArgs& a, const int32_t* pos_perm, float* partial,
                          hipStream_t st);
 

@@ -1,0 +1,224 @@
+// Asynchronous tile streaming for gfx950: global -> LDS copies with
+// global_load_lds_dwordx4 (lane l of a wave writes 16 bytes at the LDS base
+// + 16*l), issued two tiles ahead into a ring of three LDS slots.
+//
+// A tile holds TI consecutive rows (vectors of D coordinates) of a row-major
+// array: rows of RB = D * sizeof(E) bytes, unpadded.  To keep the matrix-core
+// fragment reads free of bank conflicts, 16-byte chunk c of row n is stored at
+// chunk position c ^ (n & SWM); the DMA picks, per lane, the source chunk that
+// belongs at its fixed LDS destination.
+//
+// Waiting: the waves wait for their own copies with s_waitcnt vmcnt(N) (N = the
+// copies they issued after the tile they need, loads complete in order), then
+// meet at a raw s_barrier.  The workgroup-scope fence of __syncthreads() would
+// wait for every copy in flight, which would serialise the pipeline.
+#pragma once
+#include "rece_device.h"
+
+namespace rece {
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <class E, int D> struct TileGeom {
+  static constexpr int RB = D * (int)sizeof(E);             // bytes per row
+  static constexpr int TI = RB <= 256 ? 64 : (RB == 512 ? 32 : 16);   // rows per tile
+  static constexpr int CPR = RB / 16;                        // 16-byte chunks per row
+  static constexpr int SWM = (CPR < 8 ? CPR : 8) - 1;        // swizzle mask
+  static constexpr int ROW_BYTES = TI * RB;                  // bytes of the row block
+  static constexpr int ROW_DMA = ROW_BYTES / 1024;           // wave copies of the row block
+  static_assert(ROW_BYTES % 1024 == 0, "tile rows must fill whole 1 KiB wave copies");
+};
+
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+// s_waitcnt vmcnt(n) leaving the LDS and export counters alone (GFX9 encoding).
+__device__ __forceinline__ void wait_vmcnt(int n) {
+#define RECE_VMCNT_CASE(N) \
+  case N:                  \
+    __builtin_amdgcn_s_waitcnt(((N)&15) | (7 << 4) | (15 << 8) | ((((N) >> 4) & 3) << 14)); \
+    break;
+  switch (n) {
+    RECE_VMCNT_CASE(0) RECE_VMCNT_CASE(1) RECE_VMCNT_CASE(2) RECE_VMCNT_CASE(3)
+    RECE_VMCNT_CASE(4) RECE_VMCNT_CASE(5) RECE_VMCNT_CASE(6) RECE_VMCNT_CASE(7)
+    RECE_VMCNT_CASE(8) RECE_VMCNT_CASE(9) RECE_VMCNT_CASE(10) RECE_VMCNT_CASE(11)
+    RECE_VMCNT_CASE(12) RECE_VMCNT_CASE(13) RECE_VMCNT_CASE(14) RECE_VMCNT_CASE(15)
+    RECE_VMCNT_CASE(16) RECE_VMCNT_CASE(17) RECE_VMCNT_CASE(18) RECE_VMCNT_CASE(19)
+    RECE_VMCNT_CASE(20) RECE_VMCNT_CASE(21) RECE_VMCNT_CASE(22) RECE_VMCNT_CASE(23)
+    default:
+      __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // vmcnt(0)
+      break;
+  }
+#undef RECE_VMCNT_CASE
+}
+
+// Every wave: finish its LDS reads, then meet the others (no memory fence).
+__device__ __forceinline__ void raw_barrier() {
+  compiler_fence();
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  compiler_fence();
+}
+
+// Copy rows [r0, r0 + TI) of `src` (row-major, RB bytes per row) into a swizzled
+// LDS row block; rows at or beyond r_end repeat row r_end - 1 (callers mask them).
+// Copy u (0 <= u < ROW_DMA) is issued by wave (u % nwaves); returns this wave's count.
+template <class E, int D>
+__device__ __forceinline__ int dma_rows(char* lds_rows, const E* __restrict__ src, int64_t r0, int64_t r_end,
+                                        int wave, int nwaves) {
+  using G = TileGeom<E, D>;
+  const int l = lane_id();
+  int issued = 0;
+  for (int u = wave; u < G::ROW_DMA; u += nwaves) {
+    const int byte = u * 1024 + 16 * l;
+    const int n = byte / G::RB;
+    const int cp = (byte % G::RB) / 16;
+    const int c = cp ^ (n & G::SWM);
+    int64_t row = r0 + n;
+    if (row >= r_end) row = r_end - 1;
+    const char* g = reinterpret_cast<const char*>(src) + row * G::RB + c * 16;
+    __builtin_amdgcn_global_load_lds(g, (lds_void*)(lds_rows + u * 1024), 16, 0, 0);
+    ++issued;
+  }
+  return issued;
+}
+
+// Copy 64 int32 values src[i0 .. i0 + 63] (clamped to i_end - 1) into LDS (one wave).
+__device__ __forceinline__ void dma_ints(int32_t* lds, const int32_t* __restrict__ src, int64_t i0, int64_t i_end) {
+  int64_t i = i0 + lane_id();
+  if (i >= i_end) i = i_end - 1;
+  __builtin_amdgcn_global_load_lds(src + i, (lds_void*)lds, 4, 0, 0);
+}
+
+// Copy records [r0, r0 + NREC) of an array of REC_BYTES-byte records into LDS
+// (record n at lds + n * REC_BYTES).  The tile's copies are numbered; these are
+// copies first .. first + copies_of - 1, issued by wave (number % nwaves).
+// Records at or beyond r_end repeat record r_end - 1.  Returns this wave's count.
+template <int REC_BYTES, int NREC>
+struct RecCopy {
+  static constexpr int CH = REC_BYTES / 16;
+  static constexpr int COPIES = (NREC * CH + 63) / 64;
+  static constexpr int LDS_BYTES = COPIES * 1024;
+  static_assert(REC_BYTES % 16 == 0, "records must be whole 16-byte chunks");
+  static __device__ __forceinline__ int issue(char* lds, const void* src, int64_t r0, int64_t r_end, int first,
+                                              int wave, int nwaves) {
+    const int l = lane_id();
+    int issued = 0;
+    for (int u = 0; u < COPIES; ++u) {
+      if ((first + u) % nwaves != wave) continue;
+      const int cidx = u * 64 + l;
+      int64_t rr = r0 + cidx / CH;
+      if (rr >= r_end) rr = r_end - 1;
+      const char* g = static_cast<const char*>(src) + rr * REC_BYTES + (cidx % CH) * 16;
+      __builtin_amdgcn_global_load_lds(g, (lds_void*)(lds + u * 1024), 16, 0, 0);
+      ++issued;
+    }
+    return issued;
+  }
+};
+
+// Up to three chunks (chunk c first, then c-1 and c+1, cyclic and distinct) of N
+// sorted slots cut into n_c chunks, walked in tiles of TI slots.  Plain scalar
+// members: an indexed array here would be placed in scratch memory.
+struct Ranges {
+  int64_t s0, s1, s2, e0, e1, e2;   // slot ranges [s_q, e_q)
+  int c1, c2, c3;                    // cumulative tile counts
+  __device__ __forceinline__ void init(int c, int n_c, int64_t N, int TI) {
+    const int cm = (c + n_c - 1) % n_c, cp = (c + 1) % n_c;
+    s0 = chunk_start(c, N, n_c);
+    e0 = chunk_start(c + 1, N, n_c);
+    s1 = e1 = s2 = e2 = 0;
+    if (n_c >= 2) {
+      s1 = chunk_start(cm, N, n_c);
+      e1 = chunk_start(cm + 1, N, n_c);
+    }
+    if (n_c >= 3) {
+      s2 = chunk_start(cp, N, n_c);
+      e2 = chunk_start(cp + 1, N, n_c);
+    }
+    c1 = (int)((e0 - s0 + TI - 1) / TI);
+    c2 = c1 + (int)((e1 - s1 + TI - 1) / TI);
+    c3 = c2 + (int)((e2 - s2 + TI - 1) / TI);
+  }
+  __device__ __forceinline__ int ntiles() const { return c3; }
+};
+
+// Slot range [q0, q1_end) of tile t (tile rows are q0 .. q0 + TI - 1, clipped at q1_end).
+__device__ __forceinline__ int64_t range_tile_start(Ranges r, int t, int TI) {
+  const bool in0 = t < r.c1, in1 = t < r.c2;
+  const int64_t st = in0 ? r.s0 : (in1 ? r.s1 : r.s2);
+  const int base = in0 ? 0 : (in1 ? r.c1 : r.c2);
+  return st + (int64_t)(t - base) * TI;
+}
+__device__ __forceinline__ int64_t range_tile_end(Ranges r, int t) {
+  const bool in0 = t < r.c1, in1 = t < r.c2;
+  return in0 ? r.e0 : (in1 ? r.e1 : r.e2);
+}
+
+// Issue the copies of window tile t (rows from `rows_src`, then 64 ids from
+// `ids_src`, then `nmaps` chunk maps of C ints from `maps_src`) into ring slot t % 3.
+template <class E, int D>
+__device__ __forceinline__ void issue_window_tile(char* ring, size_t slot_bytes, Ranges r, int t,
+                                                  const E* rows_src, const int32_t* ids_src,
+                                                  const int32_t* maps_src, int64_t map_len, int nmaps, int wave,
+                                                  int nwaves) {
+  using G = TileGeom<E, D>;
+  const int64_t q0 = range_tile_start(r, t, G::TI), q1 = range_tile_end(r, t);
+  char* slot = ring + (size_t)(t % 3) * slot_bytes;
+  dma_rows<E, D>(slot, rows_src, q0, q1, wave, nwaves);
+  const int ncopies = G::ROW_DMA + 1 + nmaps;
+  for (int u = G::ROW_DMA + ((wave - G::ROW_DMA % nwaves + nwaves) % nwaves); u < ncopies; u += nwaves) {
+    const int m = u - G::ROW_DMA;
+    int32_t* dst = reinterpret_cast<int32_t*>(slot + G::ROW_BYTES) + 64 * m;
+    if (m == 0)
+      dma_ints(dst, ids_src, q0, q1);
+    else
+      dma_ints(dst, maps_src + (int64_t)(m - 1) * map_len, q0, q1);
+  }
+}
+
+// Matrix-core fragment of tile row n (B operand, "row = vector" layout).
+template <class E, int D> struct TileFrag;
+
+template <int D> struct TileFrag<bf16, D> {
+  static __device__ __forceinline__ void load(Frag<bf16, D>& f, const char* rows, int n) {
+    using G = TileGeom<bf16, D>;
+    const int q = lane_id() >> 4;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      const int c = (4 * ks + q) ^ (n & G::SWM);
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(rows + n * G::RB + c * 16);
+      f.v[ks] = __builtin_bit_cast(bf16x8, raw);
+    }
+  }
+};
+template <int D> struct TileFrag<float, D> {
+  static __device__ __forceinline__ void load(Frag<float, D>& f, const char* rows, int n) {
+    using G = TileGeom<float, D>;
+    const int q = lane_id() >> 4;
+#pragma unroll
+    for (int ks = 0; ks < D / 4; ++ks) {
+      const int c = ks ^ (n & G::SWM);
+      f.v[ks] = *reinterpret_cast<const float*>(rows + n * G::RB + c * 16 + 4 * q);
+    }
+  }
+};
+
+// Raw 16-bit pattern of element (row n, coordinate t) of a swizzled bf16 tile.
+template <int D>
+__device__ __forceinline__ uint32_t tile_bits16(const char* rows, int n, int t) {
+  using G = TileGeom<bf16, D>;
+  const int c = (t >> 3) ^ (n & G::SWM);
+  return *reinterpret_cast<const uint16_t*>(rows + n * G::RB + c * 16 + 2 * (t & 7));
+}
+
+// Element (row n, coordinate t) of a swizzled tile, as float.
+template <class E, int D>
+__device__ __forceinline__ float tile_elem(const char* rows, int n, int t) {
+  using G = TileGeom<E, D>;
+  constexpr int EPC = 16 / (int)sizeof(E);   // elements per chunk
+  const int c = (t / EPC) ^ (n & G::SWM);
+  const E* p = reinterpret_cast<const E*>(rows + n * G::RB + c * 16) + (t % EPC);
+  return to_f32(*p);
+}
+
+}  // namespace rece
