@@ -19,6 +19,12 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0      # dense bf16 matrix cores
 PEAK_FP32_TFLOPS = 157.3       # fp32 matrix cores
 RIDGE_BF16 = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+# vector ALU issue rate: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz lane-operations per second
+# (the fp32 vector peak of 157.3 TFLOP/s counts an FMA as 2 flops on 2 packed lanes)
+PEAK_ALU_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+ALU_OPS_PER_LOGIT = 4          # mask the positive, bin + count (histogram pass), compare (filter pass)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "select_sasrec_hbm_traffic.md")
+SELECT_SOURCES = ["k_select.hip", "rece_stream.h", "rece_device.h", "rece_internal.h"]
 
 
 def chunk_starts(N, n_c):
@@ -38,7 +44,9 @@ def window_logits(w):
 
 def algorithmic_work(w):
     """Per-step algorithmic (flops, bytes) of each phase: what the method must compute and
-    move; logits never go to HBM, every vector is read once per pass."""
+    move; logits never go to HBM, every vector is read once per pass.  The chunk kernel's
+    flops entry is its vector-ALU work (ALU_OPS_PER_LOGIT per window logit), which bounds it
+    before the matrix cores do."""
     es = 2 if w.dtype == "bf16" else 4
     s, C, d, r, nb = w.s, w.C, w.d, w.rounds, w.n_b
     wl = window_logits(w)
@@ -46,7 +54,7 @@ def algorithmic_work(w):
     return {
         "project": (2.0 * d * nb * (s + C) * r, r * ((s + C) * (d * es + 4) + nb * d * es)),
         "sort": (0.0, r * (s + C) * 12 + s * 12),
-        "select": (2.0 * d * wl * r, r * ((s + C) * d * es + 8 * (s + C) + state * s)),
+        "select": (float(ALU_OPS_PER_LOGIT * wl * r), r * ((s + C) * d * es + 8 * (s + C) + state * s)),
         "loss": (2.0 * d * s, s * (2 * d * es + 12 + 12 * r)),
         "bwd_dx": (2.0 * d * (w.k * r + 1) * s, r * ((s + C) * d * es + state * s) + s * d * 4),
         "bwd_dy": (2.0 * d * w.k * r * s, r * ((s + C) * d * es + state * s) + C * d * 4),
@@ -57,12 +65,52 @@ def algorithmic_work(w):
 def roofline(name, ms_per_launch, flops, nbytes, dtype):
     ai = flops / max(nbytes, 1)
     t = ms_per_launch * 1e-3
-    if name == "select" or (name == "project" and ai > RIDGE_BF16):
+    if name == "select":
+        ach = flops / t / 1e12
+        return {"bound": "alu", "achieved": ach, "peak": PEAK_ALU_TOPS, "unit": "Tops/s",
+                "frac": ach / PEAK_ALU_TOPS}
+    if name == "project" and ai > RIDGE_BF16:
         peak = PEAK_BF16_TFLOPS if dtype == "bf16" else PEAK_FP32_TFLOPS
         ach = flops / t / 1e12
         return {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak}
     ach = nbytes / t / 1e9
     return {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS}
+
+
+def source_digest(names):
+    import hashlib
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "catalogue_cross_entropy_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of the chunk kernel from the committed counter summary, or None
+    when that summary is missing or was taken on other kernel sources."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    for line in text.splitlines():
+        if line.startswith("TRAFFIC "):
+            rec = json.loads(line[len("TRAFFIC "):])
+            if rec.get("kernel") == kernel and rec.get("sources") == source_digest(SELECT_SOURCES):
+                return rec["bytes_per_launch"]
+    return None
+
+
+def copy_probe(mb):
+    """One plain device copy of known size: the calibration dispatch for HBM byte counters."""
+    import torch
+    n = mb * (1 << 20)
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"copy probe: {n} bytes read, {n} bytes written", file=sys.stderr)
 
 
 def cpu_baseline(inp, n_rows, seed=0):
@@ -89,6 +137,8 @@ def main():
     ap.add_argument("--workload", default="sasrec")
     ap.add_argument("--cpu-rows", type=int, default=512)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="after the run, one device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -152,7 +202,7 @@ def main():
     per_launch = dom_launches / args.steps
     rl = roofline(dom, dom_ms / dom_launches, flops / per_launch, nbytes / per_launch, w.dtype)
     rl["kernel"] = dom
-    rl["traffic"] = None
+    rl["traffic"] = measured_traffic(f"select:{w.name}") if dom == "select" else None
 
     breakdown = {}
     for name, (f, b) in work.items():
@@ -186,7 +236,9 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_rows)
-    print(json.dumps(out))
+    print(json.dumps(out), flush=True)
+    if args.copy_probe_mb > 0:
+        copy_probe(args.copy_probe_mb)
 
 
 if __name__ == "__main__":

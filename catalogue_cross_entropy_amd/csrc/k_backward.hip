@@ -110,11 +110,13 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_bwd
   float* Gb = reinterpret_cast<float*>(wb);
   PrevRow* prev = reinterpret_cast<PrevRow*>(wb + 16 * GP * 4);
 
-  const int c = blockIdx.x / p.tiles_per_chunk;
-  const int tile_i = blockIdx.x % p.tiles_per_chunk;
+  const int lb = xcd_block(blockIdx.x, gridDim.x);
+  const int c = lb / p.tiles_per_chunk;
+  const int tile_i = lb % p.tiles_per_chunk;
   const int64_t x0 = chunk_start(c, s, n_c), x1 = chunk_start(c + 1, s, n_c);
   const int64_t tile0 = x0 + (int64_t)tile_i * TR;
   if (tile0 >= x1) return;
+  uint32_t nexact = 0;   // float64 logits computed by this lane
   const int64_t wrow0 = tile0 + 16 * w;
   Ranges win;
   win.init(c, n_c, C, TI);
@@ -179,11 +181,11 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_bwd
         float gv = 0.0f;
         if (rv[v] && nvalid && j != pos_v[v]) {
           const E* xrow = Xs + (wrow0 + r) * D;
-          bool mem = beats<E, D>(a, lo_v[v], hi_v[v], te_v[v], tid_v[v], xrow, Y, j, p.counters);
+          bool mem = beats<E, D>(a, lo_v[v], hi_v[v], te_v[v], tid_v[v], xrow, Y, j, nexact);
           for (int r2 = 0; r2 < rho && mem; ++r2) {
             const PrevRow pr = prev[r * MAX_ROUNDS + r2];
             if (!in_window(pr.cx, tcy[64 * r2 + n], n_c)) continue;
-            if (beats<E, D>(a, pr.lo, pr.hi, pr.te, pr.tid, xrow, Y, j, p.counters)) mem = false;
+            if (beats<E, D>(a, pr.lo, pr.hi, pr.te, pr.tid, xrow, Y, j, nexact)) mem = false;
           }
           if (mem) gv = expf(a - lse_v[v]) * gb_v[v];
         }
@@ -215,6 +217,7 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_bwd
       dst[t] = val;
     }
   }
+  flush_count(p.counters + CNT_LOGIT_EXACT, nexact);
 }
 
 // ------------------------------------------------------------------ dY (negatives)
@@ -267,11 +270,13 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_bwd
   float* Gb = reinterpret_cast<float*>(wb);
   int32_t* cy2w = reinterpret_cast<int32_t*>(wb + 16 * GP * 4);   // [16][MAX_ROUNDS]
 
-  const int c = blockIdx.x / itiles;
-  const int it = blockIdx.x % itiles;
+  const int lb = xcd_block(blockIdx.x, gridDim.x);
+  const int c = lb / itiles;
+  const int it = lb % itiles;
   const int64_t y0 = chunk_start(c, C, n_c), y1 = chunk_start(c + 1, C, n_c);
   const int64_t tile0 = y0 + (int64_t)it * TR;
   if (tile0 >= y1) return;
+  uint32_t nexact = 0;   // float64 logits computed by this lane
   const int64_t wq0 = tile0 + 16 * w;
   Ranges xr;
   xr.init(c, n_c, s, TI);   // X-chunks whose window holds item chunk c (the relation is symmetric)
@@ -327,11 +332,11 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_bwd
         float gv = 0.0f;
         if (rv[v] && nvalid && j != pi.pos) {
           const E* xrow = Xs + (q0 + n) * D;
-          bool mem = beats<E, D>(a, pi.lo, pi.hi, pi.te, pi.tid, xrow, Y, j, p.counters);
+          bool mem = beats<E, D>(a, pi.lo, pi.hi, pi.te, pi.tid, xrow, Y, j, nexact);
           for (int r2 = 0; r2 < rho && mem; ++r2) {
             const PrevRow pr = prevs[(size_t)r2 * (LY::PC::LDS_BYTES / sizeof(PrevRow)) + n];
             if (!in_window(pr.cx, cy2w[r * MAX_ROUNDS + r2], n_c)) continue;
-            if (beats<E, D>(a, pr.lo, pr.hi, pr.te, pr.tid, xrow, Y, j, p.counters)) mem = false;
+            if (beats<E, D>(a, pr.lo, pr.hi, pr.te, pr.tid, xrow, Y, j, nexact)) mem = false;
           }
           if (mem) gv = expf(a - pi.lse) * pi.gb;
         }
@@ -355,6 +360,7 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_bwd
       dst[t] = val;
     }
   }
+  flush_count(p.counters + CNT_LOGIT_EXACT, nexact);
 }
 
 // ------------------------------------------------------------------ dY (positives)

@@ -246,9 +246,11 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_sel
                     p.rounds);
   const int NP = nprev_of(p.rounds);
   (void)X;
+  uint32_t nexact = 0;   // float64 logits computed by this lane
 
-  const int c = blockIdx.x / p.tiles_per_chunk;
-  const int tile = blockIdx.x % p.tiles_per_chunk;
+  const int lb = xcd_block(blockIdx.x, gridDim.x);
+  const int c = lb / p.tiles_per_chunk;
+  const int tile = lb % p.tiles_per_chunk;
   const int64_t x0 = chunk_start(c, s, n_c), x1 = chunk_start(c + 1, s, n_c);
   const int64_t tile0 = x0 + (int64_t)tile * TR;
   if (tile0 >= x1) return;   // whole workgroup leaves together
@@ -374,7 +376,7 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_sel
               for (int r2 = 0; r2 < rho && !dup; ++r2) {
                 const PrevRow pr = L.prev[r * NP + r2];
                 if (!in_window(pr.cx, tcy[64 * r2 + n], n_c)) continue;
-                dup = beats<E, D>(a, pr.lo, pr.hi, pr.te, pr.tid, xrow, Y, j, p.counters);
+                dup = beats<E, D>(a, pr.lo, pr.hi, pr.te, pr.tid, xrow, Y, j, nexact);
               }
               if (!dup) {
                 if (selall && a > mx_v[v]) {   // no histogram pass ran: keep the shift at the maximum
@@ -620,7 +622,7 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_sel
     for (int e0 = 0; e0 < tot; e0 += WAVE)
       if (e0 + l < tot)
         L.ce[e0 + l] = exact_dot<E, D>(Xs + (wrow0 + L.cr[e0 + l]) * D, Y + (int64_t)L.cj[e0 + l] * D);
-    if (l == 0 && tot > 0) atomicAdd(p.counters + CNT_LOGIT_EXACT, (uint32_t)tot);
+    if (l == 0) nexact += (uint32_t)tot;
     wave_sync();
     // (C) thresholds and sums
     for (int r = r_next; r < r_end; ++r) {
@@ -700,7 +702,7 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_sel
               const PrevRow pr = L.prev[r * NP + r2];
               const int cy2 = chunk_of(p.inv_y[(int64_t)r2 * C + j], C, n_c);
               if (!in_window(pr.cx, cy2, n_c)) continue;
-              dup = beats<E, D>(a, pr.lo, pr.hi, pr.te, pr.tid, xrow, Y, j, p.counters);
+              dup = beats<E, D>(a, pr.lo, pr.hi, pr.te, pr.tid, xrow, Y, j, nexact);
             }
             if (!dup) {
               sl += __expf(a - mx);
@@ -735,6 +737,7 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_sel
     }
     r_next = r_end;
   }
+  flush_count(p.counters + CNT_LOGIT_EXACT, nexact);
 }
 
 size_t select_lds_bytes(bool is_bf16, int d, int waves, int rounds) {

@@ -67,11 +67,11 @@ __device__ __forceinline__ uint32_t fkey(float f) {
 // acc + a*b rounded once: this is the reference value every selection uses.
 // Both rows are read in 16-byte pieces, a batch of pieces in flight at a time;
 // only the additions are ordered.
-template <class E, int D>
+template <class E, int D, int MAXB = 8>
 __device__ __forceinline__ double exact_dot(const E* __restrict__ a, const E* __restrict__ b) {
   constexpr int EPP = 16 / (int)sizeof(E);     // elements per piece
   constexpr int NP = D / EPP;                  // pieces per row
-  constexpr int BATCH = NP < 8 ? NP : 8;
+  constexpr int BATCH = NP < MAXB ? NP : MAXB;   // pieces in flight (registers: 8 per piece)
   const u32x4* pa = reinterpret_cast<const u32x4*>(a);
   const u32x4* pb = reinterpret_cast<const u32x4*>(b);
   double acc = 0.0;
@@ -92,6 +92,17 @@ __device__ __forceinline__ double exact_dot(const E* __restrict__ a, const E* __
     }
   }
   return acc;
+}
+
+// The dispatcher deals workgroups to the 8 XCDs (each with its own L2) in turn:
+// block b runs on XCD b % 8.  Renumber so that every XCD gets one contiguous run
+// of logical blocks; neighbouring blocks (which read the same chunk window) then
+// share an L2.  A bijection of [0, nblocks) whatever the real placement.
+__device__ __forceinline__ int xcd_block(int b, int nblocks) {
+  constexpr int NX = 8;
+  const int per = nblocks / NX, rem = nblocks % NX;
+  const int x = b % NX;
+  return x * per + (x < rem ? x : rem) + b / NX;
 }
 
 // Outward rounding of a float64 interval end to float32.
@@ -192,15 +203,23 @@ __device__ __forceinline__ bool in_window(int cx, int cy, int n_c) {
 // lo <= te - beta, hi >= te + beta, beta bounding |a - float64 logit|:
 // above hi -> kept, below lo -> not kept, in between -> float64 comparison in the
 // order (logit desc, id asc).  lo = hi = -inf: every candidate kept; +inf: none.
+// nexact counts the float64 recomputations (a per-lane tally, flushed by flush_count).
 template <class E, int D>
 __device__ __forceinline__ bool beats(float a, float lo, float hi, double te, int tid, const E* xrow,
-                                      const E* Y, int j, uint32_t* counters) {
+                                      const E* Y, int j, uint32_t& nexact) {
   if (a > hi) return true;
   if (a < lo) return false;
   if (j == tid) return true;
-  const double e = exact_dot<E, D>(xrow, Y + (int64_t)j * D);
-  atomicAdd(counters + 3, 1u);
+  // rare path inside streaming loops: few pieces in flight, to keep registers free
+  const double e = exact_dot<E, D, 2>(xrow, Y + (int64_t)j * D);
+  ++nexact;
   return e > te || (e == te && j <= tid);
+}
+
+// Add a per-lane tally to a device counter: one atomic per wave.
+__device__ __forceinline__ void flush_count(uint32_t* counter, uint32_t v) {
+  const int t = wave_sum((int)v);
+  if (lane_id() == 0 && t != 0) atomicAdd(counter, (uint32_t)t);
 }
 
 struct PrevRow {   // a position's kept-set threshold in an earlier round (32 bytes)
