@@ -23,3 +23,7 @@ from .rece import (  # noqa: F401
     window_chunks, round_negatives, rece_forward, rece_backward, full_ce,
     full_ce_grad, logsumexp,
 )
+from .sce import (  # noqa: F401
+    projection_scores, column_top, bucket_lists, bucket_negatives, merge_negatives,
+    sce_forward, sce_backward,
+)
