@@ -72,8 +72,9 @@ def _top_k(ids, logits, k):
 def bucket_negatives(X, Y, pos, R, Q, k: int) -> dict:
     """Per bucket and taken position: the top-k of the bucket's items (positive excluded).
 
-    Returns {(b, i): (ids, logits)}.  Keeping only a bucket's top-k loses nothing:
-    a member of the top-k over a union is in the top-k of every part containing it.
+    Returns {(b, i): (ids, logits, n)} with n the number of candidates the bucket
+    offered.  Keeping only a bucket's top-k loses nothing: a member of the top-k
+    over a union is in the top-k of every part containing it.
     """
     out = {}
     for b in range(len(R)):
@@ -83,7 +84,7 @@ def bucket_negatives(X, Y, pos, R, Q, k: int) -> dict:
         L = seq_dot(X[R[b]], Y[items])
         for n, i in enumerate(R[b]):
             m = items != pos[i]
-            out[(b, int(i))] = _top_k(items[m], L[n][m], k)
+            out[(b, int(i))] = _top_k(items[m], L[n][m], k) + (int(m.sum()),)
     return out
 
 
@@ -91,19 +92,23 @@ def merge_negatives(per_bucket: dict, s: int, k: int):
     """N_i: the top-k over the duplicate-free union of a position's bucket lists.
 
     Returns {i: (ids, logits, thr)} with thr = (id, logit) of the k-th kept pair,
-    None when the union has at most k members (every member kept)."""
-    acc = {}
-    for (b, i), (ids, lg) in per_bucket.items():
+    None when the union of the candidates has at most k members (every one kept).
+    The union exceeds k when the pruned union does or some bucket offered more
+    than k candidates."""
+    acc, cut = {}, set()
+    for (b, i), (ids, lg, n) in per_bucket.items():
         d = acc.setdefault(i, {})
         for j, l in zip(ids.tolist(), lg.tolist()):
             d[j] = l        # the same pair has the same float64 logit in every bucket
+        if n > k:
+            cut.add(i)
     out = {}
     for i in range(s):
         d = acc.get(i, {})
         ids = np.array(sorted(d), dtype=np.int64)
         lg = np.array([d[j] for j in ids.tolist()], dtype=np.float64)
         kid, kl = _top_k(ids, lg, k)
-        thr = (int(kid[-1]), float(kl[-1])) if (len(ids) > k and k > 0) else None
+        thr = (int(kid[-1]), float(kl[-1])) if ((len(ids) > k or i in cut) and k > 0) else None
         out[i] = (kid, kl, thr)
     return out
 

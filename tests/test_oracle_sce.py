@@ -74,7 +74,7 @@ def _brute(X, Y, pos, B, b_x, b_y, k):
         py = [_dot(Y[j], B[:, b]) for j in range(C)]
         R.append(set(sorted(range(s), key=lambda i: (-px[i], i))[:b_x]))
         Q.append(set(sorted(range(C), key=lambda j: (-py[j], j))[:b_y]))
-    negs, loss = [], []
+    negs, loss, thr = [], [], []
     for i in range(s):
         U = set()
         for b in range(n_b):
@@ -86,14 +86,16 @@ def _brute(X, Y, pos, B, b_x, b_y, k):
         z = math.exp(lp) + sum(math.exp(lg[j]) for j in keep)
         negs.append(keep)
         loss.append(math.log(z) - lp)
-    return R, Q, negs, loss
+        thr.append((keep[-1], lg[keep[-1]]) if (len(U) > k and k > 0) else None)
+    return R, Q, negs, loss, thr
 
 
 @pytest.mark.parametrize("seed,b_x,b_y,k", [(1, 6, 15, 4), (2, 3, 30, 10), (3, 10, 5, 8), (4, 24, 60, 59)])
 def test_brute_force(seed, b_x, b_y, k):
     X, Y, pos, B = _case(seed)
-    R, Q, negs, loss = _brute(X, Y, pos, B, b_x, b_y, k)
+    R, Q, negs, loss, thr = _brute(X, Y, pos, B, b_x, b_y, k)
     f = oracle.sce_forward(X, Y, pos, B, b_x, b_y, k)
+    assert [f["negs"][0][i][2] for i in range(len(pos))] == thr
     assert [set(r.tolist()) for r in f["R"]] == R
     assert [set(q.tolist()) for q in f["Q"]] == Q
     assert [f["negs"][0][i][0].tolist() for i in range(len(pos))] == negs
