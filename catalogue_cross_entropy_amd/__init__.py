@@ -19,7 +19,7 @@ FLAG_VALIDATE_IDS, FLAG_KEEP_STAGES = 1, 2
 
 STAGES = {
     "bucket_x": 0, "bucket_y": 1, "perm_x": 2, "perm_y": 3, "thresh_id": 4,
-    "thresh_logit": 5, "neg_ids": 6, "lse": 7, "counters": 8,
+    "thresh_logit": 5, "neg_ids": 6, "lse": 7, "counters": 8, "sce_rows": 9, "sce_items": 10,
 }
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small",
           4: "HIP runtime error", 5: "device check failed", 6: "internal error"}
@@ -178,6 +178,10 @@ class Plan:
         _check(lib().rece_export(self._h, _stream(stream), _ptr(saved), st, round, _ptr(out)))
         if stage == "neg_ids":
             out = out.view(self.cfg.s, max(self.cfg.k, 1))
+        elif stage == "sce_rows":
+            out = out.view(self.cfg.n_b, self.cfg.b_x)
+        elif stage == "sce_items":
+            out = out.view(self.cfg.n_b, self.cfg.b_y)
         return out
 
     def profile(self, phases=None, enable: bool = True):

@@ -32,7 +32,18 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
 
 // Upstream gradient of position i's loss.
 __device__ __forceinline__ float gbar_of(const BwdArgs& p, int64_t i) {
-  return p.dloss_pp ? p.dloss_pp[i] : p.dloss[0] / (float)p.s;
+  return p.dloss_pp ? p.dloss_pp[i] : p.dloss[0] / (float)p.npos;
+}
+
+// Bucket variant: a pair (position, item) met in a bucket counts there only if no
+// earlier bucket of the position (the first m entries of its group, starting at
+// `start` in sce_sorted) also took the item.
+__device__ __forceinline__ bool sce_seen_before(const BwdArgs& p, int start, int m, int j) {
+  for (int e = 0; e < m; ++e) {
+    const int b2 = p.sce_sorted[start + e] / p.b_x;
+    if ((p.qbits[(int64_t)b2 * p.qwords + (j >> 5)] >> (j & 31)) & 1u) return true;
+  }
+  return false;
 }
 
 constexpr int GP = 68;   // pitch (floats) of the per-wave gradient block [16][TI]
@@ -91,7 +102,9 @@ __host__ __device__ constexpr size_t rows_slot_bytes(size_t row_bytes, int round
 }
 constexpr size_t ROWS_WAVE_LDS = 16 * GP * 4 + 16 * MAX_ROUNDS * sizeof(PrevRow);
 
-template <class E, int D, int NW>
+// SCE = true: bucket variant (rows are (bucket, position) slots, window = the
+// bucket's items, output = one partial row per slot, no positive term).
+template <class E, int D, int NW, bool SCE>
 __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_bwd_rows(BwdArgs p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   using G = TileGeom<E, D>;
@@ -119,7 +132,7 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_bwd
   uint32_t nexact = 0;   // float64 logits computed by this lane
   const int64_t wrow0 = tile0 + 16 * w;
   Ranges win;
-  win.init(c, n_c, C, TI);
+  win.init(c, n_c, C, TI, p.nwin);
   const int ntiles = win.ntiles();
 
   const int64_t pA = wrow0 + (l & 15);
@@ -130,6 +143,7 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_bwd
       prev[l * MAX_ROUNDS + r2] = pA < x1 ? p.prev[(int64_t)r2 * s + pA] : PrevRow{};
 
   int i_v[4], pos_v[4], tid_v[4];
+  int gst_v[4], gm_v[4];   // bucket variant: the position's group start, earlier slots
   float lse_v[4], gb_v[4], lo_v[4], hi_v[4], lpos_v[4];
   double te_v[4];
   bool rv[4];
@@ -147,6 +161,8 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_bwd
     te_v[v] = rc.te;
     tid_v[v] = rc.tid;
     lpos_v[v] = rc.lpos;
+    gst_v[v] = rc.pad0;
+    gm_v[v] = rc.pad1;
   }
   f32x4 dacc[D / 16];
 #pragma unroll
@@ -182,6 +198,7 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_bwd
         if (rv[v] && nvalid && j != pos_v[v]) {
           const E* xrow = Xs + (wrow0 + r) * D;
           bool mem = beats<E, D>(a, lo_v[v], hi_v[v], te_v[v], tid_v[v], xrow, Y, j, nexact);
+          if (SCE && mem && gm_v[v] > 0 && sce_seen_before(p, gst_v[v], gm_v[v], j)) mem = false;
           for (int r2 = 0; r2 < rho && mem; ++r2) {
             const PrevRow pr = prev[r * MAX_ROUNDS + r2];
             if (!in_window(pr.cx, tcy[64 * r2 + n], n_c)) continue;
@@ -201,6 +218,12 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_bwd
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     if (!rv[v]) continue;
+    if (SCE) {   // partial row of this slot
+      float* dst = p.dX + (wrow0 + 4 * g + v) * D;
+#pragma unroll
+      for (int nb = 0; nb < D / 16; ++nb) dst[16 * nb + (l & 15)] = dacc[nb][v];
+      continue;
+    }
     float* dst = p.dX + (int64_t)i_v[v] * D;
     float gpos = 0.0f;
     const int pclamp = pos_v[v] < 0 ? 0 : (pos_v[v] >= p.C ? (int)(p.C - 1) : pos_v[v]);
@@ -250,7 +273,7 @@ __device__ __forceinline__ void issue_items_tile(char* ring, size_t slot_bytes, 
                   G::ROW_DMA + LY::RC::COPIES + r2 * LY::PC::COPIES, wave, nwaves);
 }
 
-template <class E, int D, int NW>
+template <class E, int D, int NW, bool SCE>
 __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_bwd_items(BwdArgs p, int itiles) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   using G = TileGeom<E, D>;
@@ -279,7 +302,7 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_bwd
   uint32_t nexact = 0;   // float64 logits computed by this lane
   const int64_t wq0 = tile0 + 16 * w;
   Ranges xr;
-  xr.init(c, n_c, s, TI);   // X-chunks whose window holds item chunk c (the relation is symmetric)
+  xr.init(c, n_c, s, TI, p.nwin);   // X-chunks whose window holds item chunk c (the relation is symmetric)
   const int ntiles = xr.ntiles();
 
   const int64_t qA = wq0 + (l & 15);
@@ -333,6 +356,7 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_bwd
         if (rv[v] && nvalid && j != pi.pos) {
           const E* xrow = Xs + (q0 + n) * D;
           bool mem = beats<E, D>(a, pi.lo, pi.hi, pi.te, pi.tid, xrow, Y, j, nexact);
+          if (SCE && mem && pi.pad1 > 0 && sce_seen_before(p, pi.pad0, pi.pad1, j)) mem = false;
           for (int r2 = 0; r2 < rho && mem; ++r2) {
             const PrevRow pr = prevs[(size_t)r2 * (LY::PC::LDS_BYTES / sizeof(PrevRow)) + n];
             if (!in_window(pr.cx, cy2w[r * MAX_ROUNDS + r2], n_c)) continue;
@@ -351,7 +375,7 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_bwd
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     if (!rv[v]) continue;
-    float* dst = p.dY + (int64_t)j_v[v] * D;
+    float* dst = p.dY + (SCE ? wq0 + 4 * g + v : (int64_t)j_v[v]) * D;
 #pragma unroll
     for (int nb = 0; nb < D / 16; ++nb) {
       const int t = 16 * nb + (l & 15);
@@ -483,20 +507,20 @@ static size_t items_lds(int NW, int rounds) {
   return 3 * ItemsLayout<E, D>::slot_bytes(rounds) + (size_t)NW * ITEMS_WAVE_LDS;
 }
 
-template <class E, int D, int NW>
+template <class E, int D, int NW, bool SCE>
 static hipError_t launch_rows_t(const BwdArgs& a, hipStream_t st) {
   const size_t lds = rows_lds<E, D>(NW, a.rounds);
-  auto kern = k_bwd_rows<E, D, NW>;
+  auto kern = k_bwd_rows<E, D, NW, SCE>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)((int64_t)a.n_c * a.tiles_per_chunk)), dim3(64 * NW), lds, st, a);
   return hipGetLastError();
 }
-template <class E, int D, int NW>
+template <class E, int D, int NW, bool SCE>
 static hipError_t launch_items_t(const BwdArgs& a, int itiles, hipStream_t st) {
   const size_t lds = items_lds<E, D>(NW, a.rounds);
-  auto kern = k_bwd_items<E, D, NW>;
+  auto kern = k_bwd_items<E, D, NW, SCE>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -506,7 +530,7 @@ static hipError_t launch_items_t(const BwdArgs& a, int itiles, hipStream_t st) {
 
 hipError_t launch_bwd_rows(bool bf16v, int d, int waves, const BwdArgs& a, hipStream_t st) {
 #define RECE_R(E, DD) \
-  if (d == DD) return launch_rows_t<E, DD, 4>(a, st);
+  if (d == DD) return a.sce ? launch_rows_t<E, DD, 4, true>(a, st) : launch_rows_t<E, DD, 4, false>(a, st);
   (void)waves;
   if (bf16v) {
     RECE_R(bf16, 32) RECE_R(bf16, 64) RECE_R(bf16, 128) RECE_R(bf16, 256)
@@ -519,7 +543,8 @@ hipError_t launch_bwd_rows(bool bf16v, int d, int waves, const BwdArgs& a, hipSt
 
 hipError_t launch_bwd_items(bool bf16v, int d, int waves, const BwdArgs& a, int itiles, hipStream_t st) {
 #define RECE_I(E, DD) \
-  if (d == DD) return launch_items_t<E, DD, 4>(a, itiles, st);
+  if (d == DD)                                                                    \
+    return a.sce ? launch_items_t<E, DD, 4, true>(a, itiles, st) : launch_items_t<E, DD, 4, false>(a, itiles, st);
   (void)waves;
   if (bf16v) {
     RECE_I(bf16, 32) RECE_I(bf16, 64) RECE_I(bf16, 128) RECE_I(bf16, 256)

@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256) void k_bwd_records(BwdArgs a, const int32_t* _
   const int64_t o = (int64_t)rho * a.s + i;
   PosRec r;
   r.lse = a.lse[i];
-  r.gb = a.dloss_pp ? a.dloss_pp[i] : a.dloss[0] / (float)a.s;
+  r.gb = a.dloss_pp ? a.dloss_pp[i] : a.dloss[0] / (float)a.npos;
   r.lo = a.thr_lo[o];
   r.hi = a.thr_hi[o];
   r.te = a.thr_e[o];
@@ -64,6 +64,12 @@ __global__ __launch_bounds__(256) void k_bwd_records(BwdArgs a, const int32_t* _
   r.pos = a.pos[i];
   r.i = (int32_t)i;
   r.lpos = a.lpos[i];
+  r.pad0 = 0;
+  r.pad1 = 0;
+  if (a.sce) {   // the position's group of slots and this slot's place in it
+    r.pad0 = a.sce_pstart[i];
+    r.pad1 = a.sce_inv[p] - r.pad0;
+  }
   rec[p] = r;
   for (int r2 = 0; r2 < rho; ++r2) {
     const int64_t o2 = (int64_t)r2 * a.s + i;

@@ -1,0 +1,624 @@
+// Bucket (SCE) variant kernels.  The SCE page ("Scalable Cross-Entropy Loss for
+// Sequential Recommendations with Large Item Catalogs", abstract) scores each
+// position against a subset of the catalogue found by maximum inner product
+// search; in the bucket variant, each of n_b projection vectors (buckets) takes
+// the b_x positions and the b_y items with the largest scores and the positions
+// keep their k largest logits over the union of their buckets.
+//
+// Pipeline (the chunk kernel is shared with RECE: a bucket is a "chunk" whose
+// window is its own item list):
+//   k_project_scores  scores of every row against every bucket, float32 matrix
+//                     cores, stored one column per bucket (plus row norms);
+//   k_col_select      per bucket column, the b largest scores, decided exactly
+//                     (histogram -> boundary bin -> float64 recomputation of
+//                     the entries within 2*beta of the boundary);
+//   k_group_bounds    groups of a sorted key list (slots of each position,
+//                     slots of each item);
+//   k_sce_merge       per position, the exact top-k of the union of its bucket
+//                     lists (duplicates removed), its threshold and sums;
+//   k_mark_items      bitmap of the items of every bucket (backward dedup);
+//   k_sce_combine_*   backward: per-slot partial gradient rows summed per
+//                     position / item in slot order (no atomics).
+#include "rece_device.h"
+#include "rece_internal.h"
+#include "rece_kth.h"
+
+namespace rece {
+
+// ------------------------------------------------------------ projection scores
+// Block: 4 waves x 32 rows.  Bucket vectors stream through LDS in tiles of TB.
+template <class E, int D>
+__global__ __launch_bounds__(256) void k_project_scores(const E* __restrict__ V, int64_t n,
+                                                        const E* __restrict__ Bt, int n_b, float* __restrict__ PT,
+                                                        float* __restrict__ norms,
+                                                        uint32_t* __restrict__ norm_max_bits) {
+  constexpr int P = Pitch<E, D>::value;
+  constexpr int TB = D * (int)sizeof(E) > 512 ? 32 : 64;   // bucket rows per LDS tile
+  constexpr int CPR = D * (int)sizeof(E) / 16;             // 16-byte chunks per row
+  __shared__ __attribute__((aligned(16))) E tile[TB * P];
+  const int w = threadIdx.x >> 6, l = lane_id(), g = l >> 4;
+  const int64_t row0 = (int64_t)blockIdx.x * 128 + w * 32;
+  Frag<E, D> a[2];
+  float ss[2];
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    const int64_t r = row0 + 16 * f + (l & 15);
+    const E* rp = r < n ? V + r * D : nullptr;
+    a[f].load_global(rp);
+    // squared norm of row (l & 15) of fragment f: this lane's coordinates, then the 4 lanes of the row
+    float acc = 0.0f;
+    if (rp) {
+      if constexpr (sizeof(E) == 2) {
+        for (int ks = 0; ks < D / 32; ++ks)
+          for (int t = 0; t < 8; ++t) {
+            const float x = to_f32(rp[32 * ks + 8 * g + t]);
+            acc = fmaf(x, x, acc);
+          }
+      } else {
+        for (int ks = 0; ks < D / 4; ++ks) {
+          const float x = to_f32(rp[4 * ks + g]);
+          acc = fmaf(x, x, acc);
+        }
+      }
+    }
+    acc += __shfl_xor(acc, 16);
+    acc += __shfl_xor(acc, 32);
+    ss[f] = acc;
+  }
+  if (l < 16) {
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      const int64_t r = row0 + 16 * f + l;
+      if (r < n) {
+        // float32 sum of squares: relative error below d * 2^-24 < 2^-12; round the norm up
+        const float nrm = sqrtf(ss[f]) * (1.0f + 0.0005f);
+        if (norms) norms[r] = nrm;
+        if (norm_max_bits) atomicMax(norm_max_bits, __float_as_uint(nrm));
+      }
+    }
+  }
+
+  for (int b0 = 0; b0 < n_b; b0 += TB) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < TB * CPR; e += 256) {
+      const int rr = e / CPR, ch = e % CPR;
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      if (b0 + rr < n_b) v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(Bt + (int64_t)(b0 + rr) * D) + ch * 16);
+      *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(tile + rr * P) + ch * 16) = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int cb = 0; cb < TB / 16; ++cb) {
+      const int bb = b0 + cb * 16;
+      if (bb >= n_b) break;
+      Frag<E, D> bf;
+      bf.load_lds(tile + (cb * 16 + (l & 15)) * P);
+      const int bcol = bb + (l & 15);
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const f32x4 c = mma_block(a[f], bf, f32x4{0.f, 0.f, 0.f, 0.f});
+        if (bcol < n_b) {
+          float* dst = PT + (int64_t)bcol * n;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int64_t r = row0 + 16 * f + 4 * g + v;   // element v: row 4*(l/16)+v, bucket l%16
+            if (r < n) dst[r] = c[v];
+          }
+        }
+      }
+    }
+  }
+}
+
+template <class E, int D>
+static hipError_t launch_ps(const void* V, int64_t n, const void* Bt, int n_b, float* PT, float* norms,
+                            uint32_t* nmax, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL((k_project_scores<E, D>), dim3((unsigned)((n + 127) / 128)), dim3(256), 0, st,
+                     static_cast<const E*>(V), n, static_cast<const E*>(Bt), n_b, PT, norms, nmax);
+  return hipGetLastError();
+}
+
+hipError_t launch_project_scores(bool is_bf16, int d, const void* V, int64_t n, const void* Bt, int n_b, float* PT,
+                                 float* norms, uint32_t* norm_max_bits, hipStream_t st) {
+#define RECE_PS(E, DD) \
+  if (d == DD) return launch_ps<E, DD>(V, n, Bt, n_b, PT, norms, norm_max_bits, st);
+  if (is_bf16) {
+    RECE_PS(bf16, 32) RECE_PS(bf16, 64) RECE_PS(bf16, 128) RECE_PS(bf16, 256)
+  } else {
+    RECE_PS(float, 32) RECE_PS(float, 64) RECE_PS(float, 128) RECE_PS(float, 256)
+  }
+#undef RECE_PS
+  return hipErrorInvalidValue;
+}
+
+// ------------------------------------------------------------ column top-m
+constexpr int CS_BINS = 4096;
+constexpr int CS_NEAR = 2048;               // entries within the boundary band
+constexpr int CS_SLACK = 256;               // room for band entries outside the boundary bin
+constexpr float CS_XTOP = 4095.9998f;       // largest histogram coordinate below 4096
+constexpr int CS_THREADS = 1024;
+
+// One workgroup per bucket column.  Selection order: (float64 score desc, index asc).
+template <class E, int D>
+__global__ __launch_bounds__(CS_THREADS) void k_col_select(ColSelectArgs a) {
+  __shared__ uint32_t hist[CS_BINS];
+  __shared__ int32_t near_idx[CS_NEAR];
+  __shared__ float near_val[CS_NEAR];
+  __shared__ double near_e[CS_NEAR];
+  __shared__ uint32_t wtot[2][CS_THREADS / 64];
+  __shared__ int32_t bcast[4];
+  const int b = blockIdx.x;
+  const int64_t N = a.N;
+  const int m = a.m;
+  const float* __restrict__ col = a.PT + (int64_t)b * N;
+  int32_t* out = a.out + (int64_t)b * m;
+  const int tid = threadIdx.x, l = lane_id(), w = tid >> 6;
+  constexpr int NW = CS_THREADS / 64;
+  if ((int64_t)m >= N) {   // the bucket takes every entry
+    for (int64_t t = tid; t < N; t += CS_THREADS) out[t] = (int32_t)t;
+    return;
+  }
+  const E* V = static_cast<const E*>(a.V);
+  const E* brow = static_cast<const E*>(a.Bt) + (int64_t)b * D;
+  const float vmax = __uint_as_float(a.vmax_bits[0]), bn = a.bnorm_max[0];
+  const float beta = a.beta_coef * vmax * bn;   // bounds |float32 score - float64 score|
+  const float bnd = f_up((double)vmax * (double)bn * (1.0 + 1e-5) + 2.0 * (double)beta) + 1e-30f;
+  const float lo0 = -bnd, sc0 = (float)CS_BINS / (2.0f * bnd);
+
+  float xa = 0.0f, mul = 1.0f, tlo = 0.0f, thi = 0.0f;
+  int kk = m;
+  for (int pass = 0;; ++pass) {
+    for (int i = tid; i < CS_BINS; i += CS_THREADS) hist[i] = 0u;
+    __syncthreads();
+    for (int64_t t = tid; t < N; t += CS_THREADS) {
+      const float x = fminf(fmaxf((col[t] - lo0) * sc0, 0.0f), CS_XTOP);
+      const float y = (x - xa) * mul;
+      if (y >= 0.0f && y < (float)CS_BINS) atomicAdd(&hist[(int)y], 1u);
+    }
+    __syncthreads();
+    // thread tid owns bins 4*tid .. 4*tid+3; suffix sums from the top bin down
+    uint32_t h[4], own = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      h[q] = hist[4 * tid + q];
+      own += h[q];
+    }
+    uint32_t suf = own;   // inclusive suffix within the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_down(suf, o);
+      if (l + o < 64) suf += y;
+    }
+    if (l == 0) wtot[0][w] = suf;
+    __syncthreads();
+    uint32_t later = 0;
+    for (int q = w + 1; q < NW; ++q) later += wtot[0][q];
+    uint32_t acc = suf - own + later;   // entries in bins above this thread's
+#pragma unroll
+    for (int q = 3; q >= 0; --q) {
+      if (acc < (uint32_t)kk && acc + h[q] >= (uint32_t)kk) {
+        bcast[0] = 4 * tid + q;
+        bcast[1] = (int)acc;
+        bcast[2] = (int)h[q];
+      }
+      acc += h[q];
+    }
+    __syncthreads();
+    const int bstar = bcast[0], above = bcast[1], cnt = bcast[2];
+    __syncthreads();   // bcast and wtot are rewritten by the next pass
+    const float nxa = xa + (float)bstar / mul;   // exact: at most 24 significant bits
+    const double vlo = (double)lo0 + (double)nxa / (double)sc0;
+    const double vhi = (double)lo0 + ((double)nxa + 1.0 / (double)mul) / (double)sc0;
+    const double pad = (fabs(vlo) + fabs(vhi) + fabs((double)lo0)) * 1e-6 + 1e-30;
+    tlo = f_down(vlo - 2.0 * (double)beta - pad);
+    thi = f_up(vhi + 2.0 * (double)beta + pad);
+    // one nested level reaches the float spacing of the coordinate; finer gains nothing
+    if (cnt > CS_NEAR - CS_SLACK && pass < 1 && vhi - vlo > 4.0 * (double)beta) {
+      xa = nxa;
+      mul *= (float)CS_BINS;
+      kk -= above;
+      continue;
+    }
+    break;
+  }
+
+  // collect pass, in index order: sure members straight to the output, band entries to LDS
+  int base_s = 0, base_n = 0;
+  for (int64_t t0 = 0; t0 < N; t0 += CS_THREADS) {
+    const int64_t t = t0 + tid;
+    const float v = t < N ? col[t] : NEG_INF;
+    const bool sure = t < N && v > thi;
+    const bool band = t < N && v >= tlo && v <= thi;
+    const uint64_t ms = ballot(sure), mn = ballot(band);
+    if (l == 0) {
+      wtot[0][w] = (uint32_t)popc(ms);
+      wtot[1][w] = (uint32_t)popc(mn);
+    }
+    __syncthreads();
+    int off_s = base_s, off_n = base_n, tot_s = 0, tot_n = 0;
+    for (int q = 0; q < NW; ++q) {
+      const int cs = (int)wtot[0][q], cn = (int)wtot[1][q];
+      if (q < w) {
+        off_s += cs;
+        off_n += cn;
+      }
+      tot_s += cs;
+      tot_n += cn;
+    }
+    if (sure) {
+      const int dst = off_s + popc(ms & lanemask_lt());
+      if (dst < m) out[dst] = (int32_t)t;
+    }
+    if (band) {
+      const int dst = off_n + popc(mn & lanemask_lt());
+      if (dst < CS_NEAR) {
+        near_idx[dst] = (int32_t)t;
+        near_val[dst] = v;
+      }
+    }
+    base_s += tot_s;
+    base_n += tot_n;
+    __syncthreads();
+  }
+  const int n_sure = base_s, n_band = base_n < CS_NEAR ? base_n : CS_NEAR;
+  const int need = m - n_sure;
+  if (n_sure > m || base_n > CS_NEAR || need > n_band) {
+    if (tid == 0) {
+      atomicAdd(a.counters + CNT_OVERFLOW, 1u);
+      atomicOr(a.counters + CNT_ERROR, (uint32_t)ERRBIT_OVERFLOW);
+    }
+    return;
+  }
+  // float64 scores of the band, then rank by (score desc, index asc)
+  for (int e = tid; e < n_band; e += CS_THREADS) near_e[e] = exact_dot<E, D>(V + (int64_t)near_idx[e] * D, brow);
+  if (tid == 0 && n_band > 0) atomicAdd(a.counters + CNT_LOGIT_EXACT, (uint32_t)n_band);
+  __syncthreads();
+  uint32_t* chosen = hist;   // reuse
+  for (int e = tid; e < n_band; e += CS_THREADS) {
+    const double me = near_e[e];
+    const int mi = near_idx[e];
+    int rank = 0;
+    for (int u = 0; u < n_band; ++u) {
+      const double eu = near_e[u];
+      rank += (eu > me) || (eu == me && near_idx[u] < mi);
+    }
+    chosen[e] = rank < need ? 1u : 0u;
+  }
+  __syncthreads();
+  if (w == 0) {   // chosen band entries after the sure ones, in index order
+    int off = n_sure;
+    for (int base = 0; base < n_band; base += 64) {
+      const int e = base + l;
+      const bool c = e < n_band && chosen[e] != 0u;
+      const uint64_t mk = ballot(c);
+      if (c) out[off + popc(mk & lanemask_lt())] = near_idx[e];
+      off += popc(mk);
+    }
+  }
+}
+
+template <class E, int D>
+static hipError_t launch_cs(const ColSelectArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((k_col_select<E, D>), dim3((unsigned)a.n_b), dim3(CS_THREADS), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_col_select(bool is_bf16, int d, const ColSelectArgs& a, hipStream_t st) {
+#define RECE_CS(E, DD) \
+  if (d == DD) return launch_cs<E, DD>(a, st);
+  if (is_bf16) {
+    RECE_CS(bf16, 32) RECE_CS(bf16, 64) RECE_CS(bf16, 128) RECE_CS(bf16, 256)
+  } else {
+    RECE_CS(float, 32) RECE_CS(float, 64) RECE_CS(float, 128) RECE_CS(float, 256)
+  }
+#undef RECE_CS
+  return hipErrorInvalidValue;
+}
+
+// ------------------------------------------------------------ small helpers
+__global__ __launch_bounds__(256) void k_mark_items(const int32_t* __restrict__ Q, int64_t total, int b_y,
+                                                    int64_t qwords, uint32_t* __restrict__ qbits) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= total) return;
+  const int64_t b = e / b_y;
+  const int j = Q[e];
+  atomicOr(qbits + b * qwords + (j >> 5), 1u << (j & 31));
+}
+
+hipError_t launch_mark_items(const int32_t* Q, int n_b, int b_y, int64_t qwords, uint32_t* qbits, hipStream_t st) {
+  hipError_t e = launch_fill_u32(qbits, 0u, (int64_t)n_b * qwords, st);
+  if (e != hipSuccess) return e;
+  const int64_t total = (int64_t)n_b * b_y;
+  hipLaunchKernelGGL(k_mark_items, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, Q, total, b_y, qwords,
+                     qbits);
+  return hipGetLastError();
+}
+
+// start[key], end[key]: the range of sorted positions q whose element keys[sorted[q]] is key.
+__global__ __launch_bounds__(256) void k_group_bounds(const int32_t* __restrict__ keys,
+                                                      const int32_t* __restrict__ sorted, int64_t n,
+                                                      int32_t* __restrict__ start, int32_t* __restrict__ end) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (q >= n) return;
+  const int key = keys[sorted[q]];
+  if (q == 0 || keys[sorted[q - 1]] != key) start[key] = (int32_t)q;
+  if (q == n - 1 || keys[sorted[q + 1]] != key) end[key] = (int32_t)(q + 1);
+}
+
+hipError_t launch_group_bounds(const int32_t* keys, const int32_t* sorted, int64_t n, int32_t* start, int32_t* end,
+                               hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_group_bounds, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, keys, sorted, n, start,
+                     end);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ merge per position
+constexpr int MG_NEAR = 256;   // near-tie entries ranked in float64 per step
+
+struct MergeLds {
+  int32_t* ids;    // [2k]
+  float* vals;     // [2k]
+  uint32_t* khist; // [256]
+  float* cv;       // [64]
+  int32_t* ci;     // [MG_NEAR] list index
+  double* ce;      // [MG_NEAR] float64 logit
+};
+__host__ __device__ constexpr size_t merge_wave_bytes(int k) {
+  return (size_t)2 * k * 8 + 256 * 4 + 64 * 4 + MG_NEAR * 4 + MG_NEAR * 8;
+}
+size_t merge_lds_bytes(int k) { return 4 * ((merge_wave_bytes(k) + 15) / 16 * 16); }
+
+// Keep the k best of list[0..n) (n > k) in (float64 logit desc, id asc) order,
+// compacted to the front; returns the k-th kept element's float64 logit and id.
+template <class E, int D>
+__device__ void reduce_to_k(const MergeLds& L, int n, int k, float beta, const E* xrow, const E* Y, double& te,
+                            int& tid, uint32_t& nexact, uint32_t* counters) {
+  const int l = lane_id();
+  const float ak = wave_kth_largest(L.vals, n, k, L.khist, L.cv);
+  const float lo = f_down((double)ak - 2.0 * (double)beta);
+  const float hi = f_up((double)ak + 2.0 * (double)beta);
+  int nabove = 0, na = 0;
+  for (int base = 0; base < n; base += WAVE) {
+    const int t = base + l;
+    const float v = t < n ? L.vals[t] : NEG_INF;
+    nabove += popc(ballot(t < n && v > hi));
+    const bool nr = t < n && v >= lo && v <= hi;
+    const uint64_t mk = ballot(nr);
+    if (nr) {
+      const int dst = na + popc(mk & lanemask_lt());
+      if (dst < MG_NEAR) L.ci[dst] = t;
+    }
+    na += popc(mk);
+  }
+  if (na > MG_NEAR) {
+    if (l == 0) {
+      atomicAdd(counters + CNT_OVERFLOW, 1u);
+      atomicOr(counters + CNT_ERROR, (uint32_t)ERRBIT_OVERFLOW);
+    }
+    na = MG_NEAR;
+  }
+  wave_sync();
+  for (int e = l; e < na; e += WAVE) L.ce[e] = exact_dot<E, D>(xrow, Y + (int64_t)L.ids[L.ci[e]] * D);
+  if (l == 0) nexact += (uint32_t)na;
+  wave_sync();
+  const int need = k - nabove;   // near-ties kept (>= 1)
+  te = 0.0;
+  tid = 0;
+  for (int a0 = 0; a0 < na; a0 += WAVE) {
+    const int e = a0 + l;
+    int rank = 0;
+    double me = 0.0;
+    int mj = 0;
+    if (e < na) {
+      me = L.ce[e];
+      mj = L.ids[L.ci[e]];
+      for (int u = 0; u < na; ++u) {
+        const double eu = L.ce[u];
+        const int ju = L.ids[L.ci[u]];
+        rank += (eu > me) || (eu == me && ju < mj);
+      }
+    }
+    const uint64_t tm = ballot(e < na && rank == need - 1);
+    if (tm) {
+      const int tl = __builtin_ctzll(tm);
+      te = __shfl(me, tl);
+      tid = __shfl(mj, tl);
+    }
+    wave_sync();
+    if (e < na && rank >= need) L.vals[L.ci[e]] = NEG_INF;   // ranked out
+  }
+  wave_sync();
+  // compact the kept entries (value >= lo after the ranked-out near-ties were dropped)
+  int kept = 0;
+  for (int base = 0; base < n; base += WAVE) {
+    const int t = base + l;
+    const float v = t < n ? L.vals[t] : NEG_INF;
+    const int j = t < n ? L.ids[t] : -1;
+    const bool keep = t < n && v >= lo && v != NEG_INF;
+    const uint64_t mk = ballot(keep);
+    wave_sync();
+    if (keep) {
+      const int dst = kept + popc(mk & lanemask_lt());   // dst <= t: in-place is safe chunk by chunk
+      L.vals[dst] = v;
+      L.ids[dst] = j;
+    }
+    kept += popc(mk);
+    wave_sync();
+  }
+}
+
+template <class E, int D>
+__global__ __launch_bounds__(256) void k_sce_merge(MergeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int w = threadIdx.x >> 6, l = lane_id();
+  const int64_t i = (int64_t)blockIdx.x * 4 + w;
+  if (i >= a.s) return;   // whole wave leaves; no block barrier in this kernel
+  const int k = a.k;
+  char* base = smem + (size_t)w * ((merge_wave_bytes(k) + 15) / 16 * 16);
+  MergeLds L;
+  L.ids = reinterpret_cast<int32_t*>(base);
+  L.vals = reinterpret_cast<float*>(base + (size_t)2 * k * 4);
+  L.khist = reinterpret_cast<uint32_t*>(base + (size_t)2 * k * 8);
+  L.cv = reinterpret_cast<float*>(base + (size_t)2 * k * 8 + 1024);
+  L.ci = reinterpret_cast<int32_t*>(base + (size_t)2 * k * 8 + 1280);
+  L.ce = reinterpret_cast<double*>(base + (size_t)2 * k * 8 + 1280 + MG_NEAR * 4);
+  const E* X = static_cast<const E*>(a.X);
+  const E* Y = static_cast<const E*>(a.Y);
+  const E* xrow = X + i * D;
+  const float beta = a.beta_coef * a.xnorm[i] * __uint_as_float(a.ymax_bits[0]);
+  uint32_t nexact = 0;
+
+  const int g0 = a.pstart[i], g1 = a.pend[i];
+  int cnt = 0;
+  bool reduced = false, truncated = false;
+  double te = -__builtin_huge_val();
+  int tid = -1;
+  int trunc_slot = -1;
+  for (int q = g0; q < g1; ++q) {
+    const int slot = a.sorted[q];
+    if (a.slot_tid[slot] != -1) {   // this bucket had more than k candidates
+      if (!truncated) trunc_slot = slot;
+      truncated = true;
+    }
+    const int before = cnt;
+    for (int e0 = 0; e0 < k; e0 += WAVE) {
+      const int e = e0 + l;
+      const int j = e < k ? a.slot_negs[(int64_t)slot * k + e] : -1;
+      bool keep = j >= 0;
+      if (keep)
+        for (int u = 0; u < before; ++u)
+          if (L.ids[u] == j) {
+            keep = false;
+            break;
+          }
+      const uint64_t mk = ballot(keep);
+      if (keep) {
+        const int dst = cnt + popc(mk & lanemask_lt());
+        L.ids[dst] = j;
+        L.vals[dst] = a.slot_negl[(int64_t)slot * k + e];
+      }
+      cnt += popc(mk);
+      if (!ballot(j >= 0)) break;   // lists are -1 padded at the end
+    }
+    wave_sync();
+    if (cnt > k) {
+      reduce_to_k<E, D>(L, cnt, k, beta, xrow, Y, te, tid, nexact, a.counters);
+      cnt = k;
+      reduced = true;
+    }
+  }
+  if (!reduced && truncated) {   // the union is one bucket's list: its threshold stands
+    te = a.slot_te[trunc_slot];
+    tid = a.slot_tid[trunc_slot];
+  }
+  const bool none = g1 <= g0 || k == 0;
+  const bool all = !none && !reduced && !truncated;
+
+  float mx = NEG_INF;
+  for (int t = l; t < cnt; t += WAVE) mx = fmaxf(mx, L.vals[t]);
+  mx = wave_max(mx);
+  float se = 0.0f;
+  for (int t = l; t < cnt; t += WAVE) se += __expf(L.vals[t] - mx);
+  se = wave_sumf(se);
+  if (a.negs)
+    for (int t = l; t < k; t += WAVE) a.negs[i * k + t] = t < cnt ? L.ids[t] : -1;
+  if (l == 0) {
+    const double b2 = (double)beta * (1.0 + 1e-6);
+    if (none) {
+      a.thr_e[i] = __builtin_huge_val();
+      a.thr_id[i] = -2;
+      a.thr_lo[i] = a.thr_hi[i] = __builtin_huge_valf();
+    } else if (all) {
+      a.thr_e[i] = -__builtin_huge_val();
+      a.thr_id[i] = -1;
+      a.thr_lo[i] = a.thr_hi[i] = NEG_INF;
+    } else {
+      a.thr_e[i] = te;
+      a.thr_id[i] = tid;
+      a.thr_lo[i] = f_down(te - b2);
+      a.thr_hi[i] = f_up(te + b2);
+    }
+    a.mshift[i] = cnt > 0 ? mx : 0.0f;
+    a.ssum[i] = cnt > 0 ? se : 0.0f;
+    a.nmem[i] = cnt;
+  }
+  flush_count(a.counters + CNT_LOGIT_EXACT, nexact);
+}
+
+template <class E, int D>
+static hipError_t launch_mg(const MergeArgs& a, hipStream_t st) {
+  const size_t lds = merge_lds_bytes(a.k);
+  auto kern = k_sce_merge<E, D>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)((a.s + 3) / 4)), dim3(256), lds, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_sce_merge(bool is_bf16, int d, const MergeArgs& a, hipStream_t st) {
+#define RECE_MG(E, DD) \
+  if (d == DD) return launch_mg<E, DD>(a, st);
+  if (is_bf16) {
+    RECE_MG(bf16, 32) RECE_MG(bf16, 64) RECE_MG(bf16, 128) RECE_MG(bf16, 256)
+  } else {
+    RECE_MG(float, 32) RECE_MG(float, 64) RECE_MG(float, 128) RECE_MG(float, 256)
+  }
+#undef RECE_MG
+  return hipErrorInvalidValue;
+}
+
+// ------------------------------------------------------------ backward combines
+// out[i][t..t+3] = sum over the group of i (slots in order) of part[slot][t..t+3],
+// plus, for positions, the positive term (e^{l+ - lse} - 1) * gbar * y_pos.
+template <class E>
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part, const int32_t* __restrict__ sorted,
+                                                 const int32_t* __restrict__ start, const int32_t* __restrict__ end,
+                                                 int64_t n, int d, BwdArgs b, int with_pos, float* __restrict__ out) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int q4 = d / 4;
+  if (e >= n * q4) return;
+  const int64_t i = e / q4;
+  const int t = 4 * (int)(e % q4);
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int g1 = end[i];
+  for (int q = start[i]; q < g1; ++q) acc += *reinterpret_cast<const f32x4*>(part + (int64_t)sorted[q] * d + t);
+  if (with_pos) {
+    const float gb = b.dloss_pp ? b.dloss_pp[i] : b.dloss[0] / (float)b.npos;
+    const float gp = (expf(b.lpos[i] - b.lse[i]) - 1.0f) * gb;
+    int j = b.pos[i];
+    j = j < 0 ? 0 : (j >= b.C ? (int)(b.C - 1) : j);
+    const E* y = static_cast<const E*>(b.Y) + (int64_t)j * d + t;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[u] += gp * to_f32(y[u]);
+  }
+  *reinterpret_cast<f32x4*>(out + i * d + t) = acc;
+}
+
+hipError_t launch_sce_combine_rows(int d, const float* part, const int32_t* sorted, const int32_t* start,
+                                   const int32_t* end, int64_t n, const BwdArgs& b, bool is_bf16, float* out,
+                                   hipStream_t st) {
+  const int64_t total = n * (d / 4);
+  if (total <= 0) return hipSuccess;
+  if (is_bf16)
+    hipLaunchKernelGGL(k_combine<bf16>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, part, sorted, start,
+                       end, n, d, b, 1, out);
+  else
+    hipLaunchKernelGGL(k_combine<float>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, part, sorted,
+                       start, end, n, d, b, 1, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_sce_combine_items(int d, const float* part, const int32_t* sorted, const int32_t* start,
+                                    const int32_t* end, int64_t n, float* out, hipStream_t st) {
+  const int64_t total = n * (d / 4);
+  if (total <= 0) return hipSuccess;
+  BwdArgs none{};
+  hipLaunchKernelGGL(k_combine<float>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, part, sorted, start,
+                     end, n, d, none, 0, out);
+  return hipGetLastError();
+}
+
+}  // namespace rece

@@ -27,6 +27,7 @@
 #include "rece_device.h"
 #include "rece_internal.h"
 #include "rece_stream.h"
+#include "rece_kth.h"
 
 namespace rece {
 
@@ -35,129 +36,6 @@ constexpr int SEL_CAP = 64;      // candidate-list capacity per position
 constexpr int SEL_SLACK = 16;    // room kept for entries within 2*beta outside the k-th bin
 constexpr int MAX_REFINE = 2;    // histogram passes that may split a crowded bin
 constexpr float X_TOP = 255.99998f;   // largest histogram coordinate (below 256)
-
-__device__ __forceinline__ int bin_of(float v, float lo, float scale) {
-  const float x = fminf(fmaxf((v - lo) * scale, 0.0f), (float)(NBINS - 1));
-  return (int)x;
-}
-
-// Exact k-th largest (1-based) of vals[0..n), 1 <= k <= n.  Histogram refinement
-// until at most 64 values remain in range, then one value per lane, ranked by
-// broadcasting each lane's value in turn.
-__device__ float wave_kth_largest(const float* vals, int n, int k, uint32_t* hist, float* cand) {
-  const int l = lane_id();
-  float lo = __builtin_huge_valf(), hi = -__builtin_huge_valf();
-  for (int t = l; t < n; t += WAVE) {
-    const float v = vals[t];
-    lo = fminf(lo, v);
-    hi = fmaxf(hi, v);
-  }
-  lo = wave_min(lo);
-  hi = wave_max(hi);
-  int kk = k;
-  int m = n;
-  for (int iter = 0; iter < 12; ++iter) {
-    if (!(hi > lo)) return hi;
-    if (m <= WAVE) {
-      int cnt = 0;
-      for (int base = 0; base < n; base += WAVE) {
-        const int t = base + l;
-        const float v = t < n ? vals[t] : 0.0f;
-        const bool live = t < n && v >= lo && v <= hi;
-        const uint64_t mk = ballot(live);
-        if (live) cand[cnt + popc(mk & lanemask_lt())] = v;
-        cnt += popc(mk);
-      }
-      wave_sync();
-      const float c = l < m ? cand[l] : NEG_INF;
-      int gt = 0, ge = 0;
-      for (int u = 0; u < m; ++u) {
-        const float cu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), u));
-        gt += cu > c;
-        ge += cu >= c;
-      }
-      const uint64_t ok = ballot(l < m && gt < kk && kk <= ge);
-      const float r =
-          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), __builtin_ctzll(ok | (1ull << 63))));
-      wave_sync();
-      return r;
-    }
-    const float scale = (float)NBINS / (hi - lo);
-    for (int b = l; b < NBINS; b += WAVE) hist[b] = 0u;
-    wave_sync();
-    for (int t = l; t < n; t += WAVE) {
-      const float v = vals[t];
-      if (v >= lo && v <= hi) atomicAdd(&hist[bin_of(v, lo, scale)], 1u);
-    }
-    wave_sync();
-    uint32_t h[4];
-    uint32_t own = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      h[q] = hist[4 * l + q];
-      own += h[q];
-    }
-    uint32_t suf = own;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t y = __shfl_down(suf, o);
-      if (l + o < 64) suf += y;
-    }
-    int myb = -1;
-    uint32_t my_above = 0, my_cnt = 0;
-    {
-      uint32_t acc = suf - own;
-#pragma unroll
-      for (int q = 3; q >= 0; --q) {
-        if (myb < 0 && acc + h[q] >= (uint32_t)kk) {
-          myb = 4 * l + q;
-          my_above = acc;
-          my_cnt = h[q];
-        }
-        acc += h[q];
-      }
-    }
-    const uint64_t hit = ballot(myb >= 0);
-    const int src = 63 - __builtin_clzll(hit | 1ull);
-    const int bstar = __shfl(myb, src);
-    kk -= (int)__shfl(my_above, src);
-    m = (int)__shfl(my_cnt, src);
-    float nlo = __builtin_huge_valf(), nhi = -__builtin_huge_valf();
-    for (int t = l; t < n; t += WAVE) {
-      const float v = vals[t];
-      if (v >= lo && v <= hi && bin_of(v, lo, scale) == bstar) {
-        nlo = fminf(nlo, v);
-        nhi = fmaxf(nhi, v);
-      }
-    }
-    lo = wave_min(nlo);
-    hi = wave_max(nhi);
-  }
-  // more than 64 distinct values in a range that no longer splits: rank directly
-  float result = lo;
-  for (int base = 0; base < n; base += WAVE) {
-    const int t = base + l;
-    const float v = t < n ? vals[t] : 0.0f;
-    bool ok = false;
-    if (t < n && v >= lo && v <= hi) {
-      int gt = 0, ge = 0;
-      for (int u = 0; u < n; ++u) {
-        const float x = vals[u];
-        if (x >= lo && x <= hi) {
-          gt += x > v;
-          ge += x >= v;
-        }
-      }
-      ok = gt < kk && kk <= ge;
-    }
-    const uint64_t okm = ballot(ok);
-    if (okm) {
-      result = __shfl(v, __builtin_ctzll(okm));
-      break;
-    }
-  }
-  return result;
-}
 
 // Per-wave LDS region.
 constexpr int WLIST = 128;   // near-tie entries of one wave awaiting float64 values
@@ -258,7 +136,7 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_sel
 
   // window ranges (own chunk first), in tiles of TI items
   Ranges win;
-  win.init(c, n_c, C, TI);
+  win.init(c, n_c, C, TI, p.nwin);
   const int ntiles = win.ntiles();
 
   // fragments of this wave's 16 positions (sorted copy: contiguous rows)
@@ -310,7 +188,8 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_sel
     mx_v[v] = NEG_INF;   // row maximum (the exp shift), from the histogram pass
     if ((l & 15) == 0) {
       const int r = 4 * g + v;
-      L.ri[r * 8 + RI_I] = rv[v] ? i_v[v] : -1;
+      // output row: the position id, or the sorted slot when outputs are per slot
+      L.ri[r * 8 + RI_I] = rv[v] ? (p.slot_out ? (int)pr : i_v[v]) : -1;
       L.ri[r * 8 + RI_POS] = pos_v[v];
       L.rf[r * 8 + RF_BETA] = beta_v[v];
     }
@@ -392,7 +271,11 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_sel
               const uint32_t gm = (uint32_t)(m >> (16 * g)) & 0xFFFFu;
               if (sure) {
                 const int slotn = nsure_v[v] + __popc(gm & ((1u << (l & 15)) - 1u));
-                if (slotn < k) p.negs[((int64_t)rho * s + i_v[v]) * k + slotn] = j;
+                const int64_t orow = p.slot_out ? (wrow0 + r) : (int64_t)rho * s + i_v[v];
+                if (slotn < k) {
+                  p.negs[orow * k + slotn] = j;
+                  if (p.negl) p.negl[orow * k + slotn] = a;
+                }
               }
               nsure_v[v] += __popc(gm);
             } else {
@@ -472,7 +355,7 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_sel
       float ntlo, nthi, nxa = xa, nmul = mul;
       int nkk = 0;
       bool refine = false;
-      if ((int)total < kkr || !hit) {
+      if ((pass == 0 && (int)total <= kkr) || !hit) {
         // the whole window has at most k candidates (first pass only): keep them all
         ntlo = nthi = NEG_INF;
       } else {
@@ -635,7 +518,7 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_sel
       int nnew = L.ri[r * 8 + RI_NNEW];
       const int nsure = L.ri[r * 8 + RI_NSURE];
       const E* xrow = Xs + (wrow0 + r) * D;
-      const int64_t o = (int64_t)rho * s + i;
+      const int64_t o = p.slot_out ? (int64_t)i : (int64_t)rho * s + i;
       double te;
       int tid;
       float tlo, thi;
@@ -713,7 +596,10 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_sel
             const uint64_t km = ballot(kept);
             if (kept) {
               const int slotn = nsure + nk + popc(km & lanemask_lt());
-              if (slotn < k) p.negs[o * k + slotn] = j;
+              if (slotn < k) {
+                p.negs[o * k + slotn] = j;
+                if (p.negl) p.negl[o * k + slotn] = a;
+              }
             }
             nk += popc(km);
           }

@@ -91,6 +91,12 @@ struct rece_plan_s {
       o_ymax, o_lse, o_lpos, o_negs, o_xs, o_ys, o_cyp, saved_bytes;
   // scratch
   size_t o_bt, o_bnorm, o_sort, o_part, o_pp0, o_pp1, o_ppart, o_rec, o_prev, scratch_bytes;
+  // bucket variant: slots = (bucket, position) and (bucket, item) pairs
+  int64_t sx, sy;     // n_b * b_x, n_b * b_y
+  int64_t qwords;     // words of one bucket's item bitmap
+  size_t o_R, o_Q, o_xmax, o_ssort, o_sinv, o_pstart, o_pend, o_qbits;                  // saved
+  size_t o_pxt, o_pyt, o_ste, o_stid, o_stlo, o_sthi, o_smsh, o_sssum, o_snmem, o_snegs, o_snegl, o_stmp,
+      o_dxs, o_dys, o_isort, o_itmp, o_istart, o_iend;                                   // scratch
 };
 
 namespace {
@@ -122,8 +128,8 @@ struct PhaseScope {
 
 static rece_status validate_config(const rece_config* c) {
   if (!c) return fail(RECE_ERR_INVALID_ARGUMENT, "config is NULL");
-  if (c->variant != RECE_VARIANT_RECE)
-    return fail(RECE_ERR_UNSUPPORTED, "only the RECE variant is available in this build");
+  if (c->variant != RECE_VARIANT_RECE && c->variant != RECE_VARIANT_SCE)
+    return fail(RECE_ERR_INVALID_ARGUMENT, "unknown variant");
   if (c->s < 1) return fail(RECE_ERR_INVALID_ARGUMENT, "s must be >= 1");
   if (c->C < 2) return fail(RECE_ERR_INVALID_ARGUMENT, "C must be >= 2");
   if (c->s > ((int64_t)1 << 31) - 1 || c->C > ((int64_t)1 << 31) - 1)
@@ -131,13 +137,339 @@ static rece_status validate_config(const rece_config* c) {
   if (c->d != 32 && c->d != 64 && c->d != 128 && c->d != 256)
     return fail(RECE_ERR_UNSUPPORTED, "d must be one of 32, 64, 128, 256");
   if (c->n_b < 1 || c->n_b > 4096) return fail(RECE_ERR_INVALID_ARGUMENT, "n_b must be in 1..4096");
-  if (c->n_c < 1 || c->n_c > c->s || c->n_c > c->C)
+  if (c->variant == RECE_VARIANT_RECE && (c->n_c < 1 || c->n_c > c->s || c->n_c > c->C))
     return fail(RECE_ERR_INVALID_ARGUMENT, "n_c must be in 1..min(s, C)");
+  if (c->variant == RECE_VARIANT_SCE) {
+    if (c->rounds != 1) return fail(RECE_ERR_INVALID_ARGUMENT, "the bucket variant takes rounds = 1");
+    if (c->b_x < 1 || c->b_x > c->s) return fail(RECE_ERR_INVALID_ARGUMENT, "b_x must be in 1..s");
+    if (c->b_y < 1 || c->b_y > c->C) return fail(RECE_ERR_INVALID_ARGUMENT, "b_y must be in 1..C");
+    if ((int64_t)c->n_b * c->b_x > ((int64_t)1 << 31) - 1 || (int64_t)c->n_b * c->b_y > ((int64_t)1 << 31) - 1)
+      return fail(RECE_ERR_UNSUPPORTED, "n_b * b_x and n_b * b_y must fit in int32");
+    if (c->k > 1024) return fail(RECE_ERR_UNSUPPORTED, "the bucket variant keeps at most k = 1024");
+  }
   if (c->k < 0 || c->k > c->C - 1) return fail(RECE_ERR_INVALID_ARGUMENT, "k must be in 0..C-1");
   if (c->rounds < 1 || c->rounds > MAX_ROUNDS) return fail(RECE_ERR_INVALID_ARGUMENT, "rounds must be in 1..8");
   if (c->dtype != RECE_F32 && c->dtype != RECE_BF16) return fail(RECE_ERR_INVALID_ARGUMENT, "unknown dtype");
   if (c->flags & ~(RECE_FLAG_VALIDATE_IDS | RECE_FLAG_KEEP_STAGES))
     return fail(RECE_ERR_INVALID_ARGUMENT, "unknown flag bits");
+  return RECE_OK;
+}
+
+// Workspace of the bucket variant.
+static void plan_sce_layout(rece_plan_s* p) {
+  const rece_config& c = p->cfg;
+  const int64_t s = c.s, C = c.C;
+  const int d = c.d, k = std::max(c.k, 1), n_b = c.n_b;
+  p->sx = (int64_t)n_b * c.b_x;
+  p->sy = (int64_t)n_b * c.b_y;
+  p->qwords = (C + 31) / 32;
+  const int64_t sx = p->sx, sy = p->sy;
+  Layout sv;
+  p->o_cnt = sv.take(NUM_COUNTERS * 4);
+  p->o_R = sv.take((size_t)sx * 4);
+  p->o_Q = sv.take((size_t)sy * 4);
+  p->o_xs = sv.take((size_t)sx * d * p->esize);
+  p->o_ys = sv.take((size_t)sy * d * p->esize);
+  p->o_te = sv.take((size_t)s * 8);
+  p->o_tid = sv.take((size_t)s * 4);
+  p->o_tlo = sv.take((size_t)s * 4);
+  p->o_thi = sv.take((size_t)s * 4);
+  p->o_msh = sv.take((size_t)s * 4);
+  p->o_ssum = sv.take((size_t)s * 4);
+  p->o_nmem = sv.take((size_t)s * 4);
+  p->o_xnorm = sv.take((size_t)s * 4);
+  p->o_xmax = sv.take(4);
+  p->o_ymax = sv.take(4);
+  p->o_lse = sv.take((size_t)s * 4);
+  p->o_lpos = sv.take((size_t)s * 4);
+  p->o_negs = (c.flags & RECE_FLAG_KEEP_STAGES) ? sv.take((size_t)s * k * 4) : 0;
+  p->o_ssort = sv.take((size_t)sx * 4);
+  p->o_sinv = sv.take((size_t)sx * 4);
+  p->o_pstart = sv.take((size_t)s * 4);
+  p->o_pend = sv.take((size_t)s * 4);
+  p->o_qbits = sv.take((size_t)n_b * p->qwords * 4);
+  p->saved_bytes = sv.off;
+
+  Layout sc;
+  p->o_bt = sc.take((size_t)n_b * d * p->esize);
+  p->o_bnorm = sc.take(4);
+  const size_t sort_b = std::max({sort_scratch_bytes(sx, 1 << std::min(12, bits_for(s))),
+                                  sort_scratch_bytes(sy, 1 << std::min(12, bits_for(C))),
+                                  sort_scratch_bytes(s, 1 << std::min(12, bits_for(C)))});
+  p->o_sort = sc.take(sort_b);
+  p->o_part = sc.take((size_t)ce_blocks(s) * 8);
+  p->o_pp0 = sc.take((size_t)s * 4);
+  p->o_pp1 = sc.take((size_t)s * 4);
+  p->o_ppart = sc.take(pos_partial_bytes(s, d));
+  p->o_rec = sc.take((size_t)sx * sizeof(PosRec));
+  p->o_prev = sc.take(sizeof(PrevRow));
+  p->o_pxt = sc.take((size_t)n_b * s * 4);
+  p->o_pyt = sc.take((size_t)n_b * C * 4);
+  p->o_ste = sc.take((size_t)sx * 8);
+  p->o_stid = sc.take((size_t)sx * 4);
+  p->o_stlo = sc.take((size_t)sx * 4);
+  p->o_sthi = sc.take((size_t)sx * 4);
+  p->o_smsh = sc.take((size_t)sx * 4);
+  p->o_sssum = sc.take((size_t)sx * 4);
+  p->o_snmem = sc.take((size_t)sx * 4);
+  p->o_snegs = sc.take((size_t)sx * k * 4);
+  p->o_snegl = sc.take((size_t)sx * k * 4);
+  p->o_stmp = sc.take((size_t)sx * 4);
+  p->o_dxs = sc.take((size_t)sx * d * 4);
+  p->o_dys = sc.take((size_t)sy * d * 4);
+  p->o_isort = sc.take((size_t)sy * 4);
+  p->o_itmp = sc.take((size_t)sy * 4);
+  p->o_istart = sc.take((size_t)C * 4);
+  p->o_iend = sc.take((size_t)C * 4);
+  p->scratch_bytes = sc.off;
+}
+
+// Stable grouping of n elements by an integer key below `nkeys`: LSD passes of up
+// to 12 bits; out = element indices in (key, index) order, inv = its inverse.
+static rece_status group_by_key(const rece_plan_s& p, const int32_t* keys, int64_t n, int64_t nkeys, char* sort_scratch,
+                                int32_t* tmp, int32_t* out, int32_t* inv, hipStream_t st) {
+  const int total_bits = std::max(1, bits_for(nkeys));
+  const int npass = (total_bits + 11) / 12;
+  const int32_t* in = nullptr;
+  for (int pass = 0, shift = 0; pass < npass; ++pass, shift += 12) {
+    const int nb = std::min(12, total_bits - shift);
+    int32_t* dst = ((npass - 1 - pass) % 2 == 0) ? out : tmp;   // the last pass lands in out
+    RECE_PHASE(RECE_PHASE_SORT,
+               launch_counting_sort(keys, in, n, shift, nb, sort_scratch, dst, pass == npass - 1 ? inv : nullptr, st),
+               "group by key");
+    in = dst;
+  }
+  return RECE_OK;
+}
+
+// Forward pass of the bucket variant (SCE page, abstract; the bucket procedure
+// is described with the kernels).
+static rece_status sce_forward(const rece_plan_s& p, hipStream_t st, const void* X, const void* Y,
+                               const int32_t* pos, const void* B, char* sc, char* sv, float* loss, float* loss_pp) {
+  const rece_config& c = p.cfg;
+  const int64_t s = c.s, C = c.C;
+  const int d = c.d, k = c.k, n_b = c.n_b;
+  uint32_t* counters = reinterpret_cast<uint32_t*>(sv + p.o_cnt);
+  uint32_t* xmax = reinterpret_cast<uint32_t*>(sv + p.o_xmax);
+  uint32_t* ymax = reinterpret_cast<uint32_t*>(sv + p.o_ymax);
+  float* xnorm = reinterpret_cast<float*>(sv + p.o_xnorm);
+  float* bnorm = reinterpret_cast<float*>(sc + p.o_bnorm);
+  void* Bt = sc + p.o_bt;
+  int32_t* R = reinterpret_cast<int32_t*>(sv + p.o_R);
+  int32_t* Q = reinterpret_cast<int32_t*>(sv + p.o_Q);
+  float* pxt = reinterpret_cast<float*>(sc + p.o_pxt);
+  float* pyt = reinterpret_cast<float*>(sc + p.o_pyt);
+
+  RECE_PHASE(RECE_PHASE_OTHER, launch_fill_u32(counters, 0u, NUM_COUNTERS, st), "clear counters");
+  RECE_PHASE(RECE_PHASE_OTHER, launch_fill_u32(xmax, 0u, 1, st), "clear norm max");
+  RECE_PHASE(RECE_PHASE_OTHER, launch_fill_u32(ymax, 0u, 1, st), "clear norm max");
+  RECE_PHASE(RECE_PHASE_OTHER, launch_prep_b(p.bf16, d, B, 1, n_b, Bt, bnorm, st), "prepare projection vectors");
+  // K6a: projection scores of every position and item, one column per bucket
+  RECE_PHASE(RECE_PHASE_PROJECT, launch_project_scores(p.bf16, d, X, s, Bt, n_b, pxt, xnorm, xmax, st),
+             "position scores");
+  RECE_PHASE(RECE_PHASE_PROJECT, launch_project_scores(p.bf16, d, Y, C, Bt, n_b, pyt, nullptr, ymax, st),
+             "item scores");
+  // K6b: the b_x positions and b_y items of every bucket
+  ColSelectArgs ca{};
+  ca.Bt = Bt;
+  ca.n_b = n_b;
+  ca.beta_coef = p.beta_coef;
+  ca.bnorm_max = bnorm;
+  ca.counters = counters;
+  ca.PT = pxt;
+  ca.V = X;
+  ca.N = s;
+  ca.m = c.b_x;
+  ca.vmax_bits = xmax;
+  ca.out = R;
+  RECE_PHASE(RECE_PHASE_SORT, launch_col_select(p.bf16, d, ca, st), "bucket positions");
+  ca.PT = pyt;
+  ca.V = Y;
+  ca.N = C;
+  ca.m = c.b_y;
+  ca.vmax_bits = ymax;
+  ca.out = Q;
+  RECE_PHASE(RECE_PHASE_SORT, launch_col_select(p.bf16, d, ca, st), "bucket items");
+  char* xs = sv + p.o_xs;
+  char* ys = sv + p.o_ys;
+  RECE_PHASE(RECE_PHASE_SORT, launch_gather_rows(X, R, p.sx, d * p.esize, xs, st), "bucket position rows");
+  RECE_PHASE(RECE_PHASE_SORT, launch_gather_rows(Y, Q, p.sy, d * p.esize, ys, st), "bucket item rows");
+
+  // K6c: per (bucket, position) slot, the top-k of the bucket's items (the chunk kernel,
+  // one chunk per bucket, window = the chunk's own items)
+  SelectArgs a{};
+  a.X = X;
+  a.Y = Y;
+  a.Xs = xs;
+  a.Ys = ys;
+  a.rounds = 1;
+  a.pos = pos;
+  a.perm_x = R;
+  a.perm_y = Q;
+  a.s = p.sx;
+  a.C = p.sy;
+  a.n_c = n_b;
+  a.k = k;
+  a.rho = 0;
+  a.selall = p.selall;
+  a.tiles_per_chunk = p.tpc_sel;
+  a.beta_coef = p.beta_coef;
+  a.xnorm = xnorm;
+  a.ynorm_max = reinterpret_cast<const float*>(ymax);
+  a.thr_e = reinterpret_cast<double*>(sc + p.o_ste);
+  a.thr_id = reinterpret_cast<int32_t*>(sc + p.o_stid);
+  a.thr_lo = reinterpret_cast<float*>(sc + p.o_stlo);
+  a.thr_hi = reinterpret_cast<float*>(sc + p.o_sthi);
+  a.mshift = reinterpret_cast<float*>(sc + p.o_smsh);
+  a.ssum = reinterpret_cast<float*>(sc + p.o_sssum);
+  a.nmem = reinterpret_cast<int32_t*>(sc + p.o_snmem);
+  a.negs = reinterpret_cast<int32_t*>(sc + p.o_snegs);
+  a.negl = reinterpret_cast<float*>(sc + p.o_snegl);
+  a.slot_out = 1;
+  a.nwin = 1;
+  a.counters = counters;
+  RECE_PHASE(RECE_PHASE_SELECT, launch_select(p.bf16, d, p.waves_sel, a, st), "bucket logits and top-k");
+
+  // K6d: slots grouped by position (bucket order inside a group), then the merge
+  int32_t* ssort = reinterpret_cast<int32_t*>(sv + p.o_ssort);
+  int32_t* sinv = reinterpret_cast<int32_t*>(sv + p.o_sinv);
+  int32_t* pstart = reinterpret_cast<int32_t*>(sv + p.o_pstart);
+  int32_t* pend = reinterpret_cast<int32_t*>(sv + p.o_pend);
+  const rece_status gs =
+      group_by_key(p, R, p.sx, s, sc + p.o_sort, reinterpret_cast<int32_t*>(sc + p.o_stmp), ssort, sinv, st);
+  if (gs != RECE_OK) return gs;
+  RECE_PHASE(RECE_PHASE_OTHER, launch_fill_u32(reinterpret_cast<uint32_t*>(pstart), 0u, s, st), "clear groups");
+  RECE_PHASE(RECE_PHASE_OTHER, launch_fill_u32(reinterpret_cast<uint32_t*>(pend), 0u, s, st), "clear groups");
+  RECE_PHASE(RECE_PHASE_OTHER, launch_group_bounds(R, ssort, p.sx, pstart, pend, st), "position groups");
+  MergeArgs m{};
+  m.X = X;
+  m.Y = Y;
+  m.s = s;
+  m.k = k;
+  m.beta_coef = p.beta_coef;
+  m.xnorm = xnorm;
+  m.ymax_bits = ymax;
+  m.sorted = ssort;
+  m.pstart = pstart;
+  m.pend = pend;
+  m.slot_negs = a.negs;
+  m.slot_negl = a.negl;
+  m.slot_tid = a.thr_id;
+  m.slot_te = a.thr_e;
+  m.thr_e = reinterpret_cast<double*>(sv + p.o_te);
+  m.thr_id = reinterpret_cast<int32_t*>(sv + p.o_tid);
+  m.thr_lo = reinterpret_cast<float*>(sv + p.o_tlo);
+  m.thr_hi = reinterpret_cast<float*>(sv + p.o_thi);
+  m.mshift = reinterpret_cast<float*>(sv + p.o_msh);
+  m.ssum = reinterpret_cast<float*>(sv + p.o_ssum);
+  m.nmem = reinterpret_cast<int32_t*>(sv + p.o_nmem);
+  m.negs = p.o_negs ? reinterpret_cast<int32_t*>(sv + p.o_negs) : nullptr;
+  m.counters = counters;
+  RECE_PHASE(RECE_PHASE_SELECT, launch_sce_merge(p.bf16, d, m, st), "merge bucket lists");
+  RECE_PHASE(RECE_PHASE_OTHER,
+             launch_mark_items(Q, n_b, c.b_y, p.qwords, reinterpret_cast<uint32_t*>(sv + p.o_qbits), st),
+             "bucket item bitmaps");
+
+  CeArgs ce{};
+  ce.X = X;
+  ce.Y = Y;
+  ce.pos = pos;
+  ce.s = s;
+  ce.C = C;
+  ce.rounds = 1;
+  ce.mshift = m.mshift;
+  ce.ssum = m.ssum;
+  ce.nmem = m.nmem;
+  ce.lse = reinterpret_cast<float*>(sv + p.o_lse);
+  ce.lpos = reinterpret_cast<float*>(sv + p.o_lpos);
+  ce.loss_pp = loss_pp;
+  ce.partial = reinterpret_cast<float*>(sc + p.o_part);
+  ce.counters = counters;
+  ce.validate = (c.flags & RECE_FLAG_VALIDATE_IDS) ? 1 : 0;
+  RECE_PHASE(RECE_PHASE_LOSS, launch_ce(p.bf16, d, ce, loss, st), "loss");
+  return RECE_OK;
+}
+
+static rece_status sce_backward(const rece_plan_s& p, hipStream_t st, const void* X, const void* Y,
+                                const int32_t* pos, const float* dloss, const float* dloss_pp, char* sc,
+                                const char* sv, float* dX, float* dY) {
+  const rece_config& c = p.cfg;
+  const int64_t s = c.s, C = c.C;
+  const int d = c.d;
+  BwdArgs b{};
+  b.X = X;
+  b.Y = Y;
+  b.Xs = sv + p.o_xs;
+  b.Ys = sv + p.o_ys;
+  b.rounds = 1;
+  b.pos = pos;
+  b.perm_x = reinterpret_cast<const int32_t*>(sv + p.o_R);
+  b.perm_y = reinterpret_cast<const int32_t*>(sv + p.o_Q);
+  b.s = p.sx;
+  b.C = p.sy;
+  b.n_c = c.n_b;
+  b.rho = 0;
+  b.tiles_per_chunk = p.tpc_bwd;
+  b.thr_e = reinterpret_cast<const double*>(sv + p.o_te);
+  b.thr_id = reinterpret_cast<const int32_t*>(sv + p.o_tid);
+  b.thr_lo = reinterpret_cast<const float*>(sv + p.o_tlo);
+  b.thr_hi = reinterpret_cast<const float*>(sv + p.o_thi);
+  b.lse = reinterpret_cast<const float*>(sv + p.o_lse);
+  b.lpos = reinterpret_cast<const float*>(sv + p.o_lpos);
+  b.dloss = dloss;
+  b.dloss_pp = dloss_pp;
+  b.dX = reinterpret_cast<float*>(sc + p.o_dxs);
+  b.dY = reinterpret_cast<float*>(sc + p.o_dys);
+  b.counters = reinterpret_cast<uint32_t*>(const_cast<char*>(sv) + p.o_cnt);
+  b.sce = 1;
+  b.nwin = 1;
+  b.npos = s;
+  b.b_x = c.b_x;
+  b.sce_sorted = reinterpret_cast<const int32_t*>(sv + p.o_ssort);
+  b.sce_pstart = reinterpret_cast<const int32_t*>(sv + p.o_pstart);
+  b.sce_inv = reinterpret_cast<const int32_t*>(sv + p.o_sinv);
+  b.qbits = reinterpret_cast<const uint32_t*>(sv + p.o_qbits);
+  b.qwords = p.qwords;
+  PosRec* recs = reinterpret_cast<PosRec*>(sc + p.o_rec);
+  b.rec = recs;
+  RECE_PHASE(RECE_PHASE_OTHER, launch_bwd_records(b, b.perm_x, 0, recs, nullptr, st), "backward records");
+  RECE_PHASE(RECE_PHASE_BWD_DX, launch_bwd_rows(p.bf16, d, 4, b, st), "dX partial rows");
+  RECE_PHASE(RECE_PHASE_BWD_DY, launch_bwd_items(p.bf16, d, 4, b, p.itiles, st), "dY partial rows");
+  // per position: its slots' partial rows in bucket order, plus the positive term
+  BwdArgs bc = b;
+  bc.C = C;   // the catalogue (bounds of the positive ids), not the item slots
+  RECE_PHASE(RECE_PHASE_BWD_DX,
+             launch_sce_combine_rows(d, b.dX, b.sce_sorted, b.sce_pstart,
+                                     reinterpret_cast<const int32_t*>(sv + p.o_pend), s, bc, p.bf16, dX, st),
+             "dX");
+  // per item: its item slots' partial rows in bucket order
+  int32_t* isort = reinterpret_cast<int32_t*>(sc + p.o_isort);
+  int32_t* istart = reinterpret_cast<int32_t*>(sc + p.o_istart);
+  int32_t* iend = reinterpret_cast<int32_t*>(sc + p.o_iend);
+  const rece_status gs = group_by_key(p, b.perm_y, p.sy, C, sc + p.o_sort, reinterpret_cast<int32_t*>(sc + p.o_itmp),
+                                      isort, nullptr, st);
+  if (gs != RECE_OK) return gs;
+  RECE_PHASE(RECE_PHASE_OTHER, launch_fill_u32(reinterpret_cast<uint32_t*>(istart), 0u, C, st), "clear groups");
+  RECE_PHASE(RECE_PHASE_OTHER, launch_fill_u32(reinterpret_cast<uint32_t*>(iend), 0u, C, st), "clear groups");
+  RECE_PHASE(RECE_PHASE_OTHER, launch_group_bounds(b.perm_y, isort, p.sy, istart, iend, st), "item groups");
+  RECE_PHASE(RECE_PHASE_BWD_DY, launch_sce_combine_items(d, b.dY, isort, istart, iend, C, dY, st), "dY");
+  // positives, as in RECE: positions sorted by positive id, segmented reduction into dY
+  BwdArgs bp = b;
+  bp.s = s;
+  bp.C = C;
+  bp.dY = dY;
+  int32_t* bufs[2] = {reinterpret_cast<int32_t*>(sc + p.o_pp0), reinterpret_cast<int32_t*>(sc + p.o_pp1)};
+  const int total_bits = std::max(1, bits_for(C));
+  const int32_t* sorted = nullptr;
+  for (int pass = 0, shift = 0; shift < total_bits; ++pass, shift += 12) {
+    const int nb = std::min(12, total_bits - shift);
+    int32_t* outp = bufs[pass & 1];
+    RECE_PHASE(RECE_PHASE_SORT, launch_counting_sort(pos, sorted, s, shift, nb, sc + p.o_sort, outp, nullptr, st),
+               "sort positives");
+    sorted = outp;
+  }
+  RECE_PHASE(RECE_PHASE_BWD_POS, launch_pos_dy(p.bf16, d, bp, sorted, reinterpret_cast<float*>(sc + p.o_ppart), st),
+             "positive dY");
   return RECE_OK;
 }
 
@@ -153,14 +485,16 @@ rece_status rece_plan(const rece_config* cfg, rece_plan_t* out) {
   p->cfg = *cfg;
   const rece_config& c = p->cfg;
   const int64_t s = c.s, C = c.C;
-  const int d = c.d, r = c.rounds, k = c.k, n_c = c.n_c;
+  const bool sce = c.variant == RECE_VARIANT_SCE;
+  // bucket variant: a bucket is a chunk of b_x position slots whose window is its b_y item slots
+  const int d = c.d, r = c.rounds, k = c.k, n_c = sce ? c.n_b : c.n_c;
   p->bf16 = c.dtype == RECE_BF16;
   p->esize = p->bf16 ? 2 : 4;
   p->nbits_b = bits_for(c.n_b);
-  const int64_t rows_chunk = (s + n_c - 1) / n_c;
-  const int64_t items_chunk = (C + n_c - 1) / n_c;
-  const int64_t wmax = n_c <= 3 ? C : std::min<int64_t>(C, 3 * items_chunk);
-  p->selall = (k >= wmax) || (n_c <= 3 && k >= C - 1);
+  const int64_t rows_chunk = sce ? c.b_x : (s + n_c - 1) / n_c;
+  const int64_t items_chunk = sce ? c.b_y : (C + n_c - 1) / n_c;
+  const int64_t wmax = sce ? c.b_y : (n_c <= 3 ? C : std::min<int64_t>(C, 3 * items_chunk));
+  p->selall = sce ? (k >= c.b_y) : ((k >= wmax) || (n_c <= 3 && k >= C - 1));
   p->cap = 0;
   p->waves_sel = 1;
   for (int nw : {4, 2, 1}) {
@@ -177,6 +511,11 @@ rece_status rece_plan(const rece_config* cfg, rece_plan_t* out) {
   // d products and d additions, each with relative error at most 2^-23 (round or
   // chop), doubled for safety; the float64 side adds d * 2^-53.
   p->beta_coef = (float)(4.0 * (d + 2) * std::ldexp(1.0, -24) * (1.0 + 1e-6) + d * std::ldexp(1.0, -52));
+  if (sce) {
+    plan_sce_layout(p);
+    *out = p;
+    return RECE_OK;
+  }
 
   Layout sv;
   p->o_cnt = sv.take(NUM_COUNTERS * 4);
@@ -283,6 +622,7 @@ rece_status rece_forward(rece_plan_t plan, void* stream, const void* X, const vo
   float* bnorm = reinterpret_cast<float*>(sc + p.o_bnorm);
   void* Bt = sc + p.o_bt;
 
+  if (c.variant == RECE_VARIANT_SCE) return sce_forward(p, st, X, Y, pos, B, sc, sv, loss, loss_pp);
   RECE_PHASE(RECE_PHASE_OTHER, launch_fill_u32(counters, 0u, NUM_COUNTERS, st), "clear counters");
   RECE_PHASE(RECE_PHASE_OTHER, launch_fill_u32(reinterpret_cast<uint32_t*>(ymax), 0u, 1, st), "clear norm max");
   RECE_PHASE(RECE_PHASE_OTHER, launch_prep_b(p.bf16, d, B, c.rounds, c.n_b, Bt, bnorm, st),
@@ -348,6 +688,9 @@ rece_status rece_forward(rece_plan_t plan, void* stream, const void* X, const vo
     a.ssum = reinterpret_cast<float*>(sv + p.o_ssum);
     a.nmem = reinterpret_cast<int32_t*>(sv + p.o_nmem);
     a.negs = p.o_negs ? reinterpret_cast<int32_t*>(sv + p.o_negs) : nullptr;
+    a.negl = nullptr;
+    a.slot_out = 0;
+    a.nwin = 3;
     a.counters = counters;
     RECE_PHASE(RECE_PHASE_SELECT, launch_select(p.bf16, d, p.waves_sel, a, st), "chunk logits and top-k");
   }
@@ -388,8 +731,12 @@ rece_status rece_backward(rece_plan_t plan, void* stream, const void* X, const v
   char* sc = static_cast<char*>(scratch);
   const int64_t s = c.s, C = c.C;
   const int d = c.d;
+  if (c.variant == RECE_VARIANT_SCE) return sce_backward(p, st, X, Y, pos, dloss, dloss_pp, sc, sv, dX, dY);
 
   BwdArgs b{};
+  b.sce = 0;
+  b.nwin = 3;
+  b.npos = s;
   b.X = X;
   b.Y = Y;
   b.pos = pos;
@@ -447,16 +794,25 @@ rece_status rece_backward(rece_plan_t plan, void* stream, const void* X, const v
 rece_status rece_export_bytes(rece_plan_t plan, int stage, size_t* bytes) {
   if (!plan || !bytes) return fail(RECE_ERR_INVALID_ARGUMENT, "NULL argument");
   const rece_config& c = plan->cfg;
+  const bool sce = c.variant == RECE_VARIANT_SCE;
   switch (stage) {
     case RECE_STAGE_BUCKET_X:
     case RECE_STAGE_PERM_X:
+      *bytes = sce ? 0 : (size_t)c.s * 4;
+      break;
     case RECE_STAGE_THRESH_ID:
     case RECE_STAGE_LSE:
       *bytes = (size_t)c.s * 4;
       break;
     case RECE_STAGE_BUCKET_Y:
     case RECE_STAGE_PERM_Y:
-      *bytes = (size_t)c.C * 4;
+      *bytes = sce ? 0 : (size_t)c.C * 4;
+      break;
+    case RECE_STAGE_SCE_ROWS:
+      *bytes = sce ? (size_t)plan->sx * 4 : 0;
+      break;
+    case RECE_STAGE_SCE_ITEMS:
+      *bytes = sce ? (size_t)plan->sy * 4 : 0;
       break;
     case RECE_STAGE_THRESH_LOGIT:
       *bytes = (size_t)c.s * 8;
@@ -481,7 +837,8 @@ rece_status rece_export(rece_plan_t plan, void* stream, const void* saved, int s
   size_t bytes = 0;
   const rece_status bs = rece_export_bytes(plan, stage, &bytes);
   if (bs != RECE_OK) return bs;
-  if (bytes == 0) return fail(RECE_ERR_INVALID_ARGUMENT, "stage not kept (plan without RECE_FLAG_KEEP_STAGES)");
+  if (bytes == 0)
+    return fail(RECE_ERR_INVALID_ARGUMENT, "stage not kept by this plan (variant, or no RECE_FLAG_KEEP_STAGES)");
   const char* sv = static_cast<const char*>(saved);
   const int64_t s = c.s, C = c.C;
   size_t off = 0;
@@ -495,6 +852,8 @@ rece_status rece_export(rece_plan_t plan, void* stream, const void* saved, int s
     case RECE_STAGE_NEG_IDS: off = p.o_negs + (size_t)round * s * std::max(c.k, 1) * 4; break;
     case RECE_STAGE_LSE: off = p.o_lse; break;
     case RECE_STAGE_COUNTERS: off = p.o_cnt; break;
+    case RECE_STAGE_SCE_ROWS: off = p.o_R; break;
+    case RECE_STAGE_SCE_ITEMS: off = p.o_Q; break;
     default: return fail(RECE_ERR_INVALID_ARGUMENT, "unknown stage");
   }
   RECE_HIP(hipMemcpyAsync(dst, sv + off, bytes, hipMemcpyDeviceToDevice, reinterpret_cast<hipStream_t>(stream)),

@@ -50,6 +50,9 @@ struct SelectArgs {
   float* ssum;                // [rounds][s]
   int32_t* nmem;              // [rounds][s]
   int32_t* negs;              // [rounds][s][k] or nullptr
+  float* negl;                // [s][k] float32 logits of negs, or nullptr
+  int slot_out;               // 1: outputs indexed by sorted slot, not by position id
+  int nwin;                   // window chunks: 3 (c-1, c, c+1) or 1 (c only)
   uint32_t* counters;
 };
 
@@ -95,9 +98,19 @@ struct BwdArgs {
   const float* lpos;
   const float* dloss;         // [1]
   const float* dloss_pp;      // [s] or nullptr
-  float* dX;                  // [s][d]
-  float* dY;                  // [C][d]
+  float* dX;                  // [s][d]   (bucket variant: [slots][d] partial rows)
+  float* dY;                  // [C][d]   (bucket variant: [item slots][d] partial rows)
   uint32_t* counters;
+  // bucket variant: slots are (bucket, position) / (bucket, item) pairs, chunk = bucket
+  int sce;                    // 1: bucket variant
+  int nwin;                   // window chunks: 3 or 1
+  int64_t npos;               // positions (scale of dloss)
+  int b_x;                    // positions per bucket
+  const int32_t* sce_sorted;  // [slots] slots grouped by position, in bucket order
+  const int32_t* sce_pstart;  // [s] first index of each position's group in sce_sorted
+  const int32_t* sce_inv;     // [slots] index of each slot in sce_sorted
+  const uint32_t* qbits;      // [n_b][qwords] bit j: item j taken by the bucket
+  int64_t qwords;
 };
 
 // Launchers (defined in the .hip files).  All enqueue on `st`.
@@ -126,5 +139,58 @@ hipError_t launch_bwd_records(const BwdArgs& a, const int32_t* perm_x, int rho, 
                               hipStream_t st);
 hipError_t launch_pos_dy(bool is_bf16, int d, const BwdArgs& a, const int32_t* pos_perm, float* partial,
                          hipStream_t st);
+
+// Bucket (SCE) variant.
+struct ColSelectArgs {
+  const float* PT;            // [n_b][N] projection scores, one column per bucket
+  const void* V;              // [N][d] rows (float64 recomputation)
+  const void* Bt;             // [n_b][d] projection vectors
+  int64_t N;
+  int m;                      // entries taken per bucket
+  int n_b;
+  float beta_coef;
+  const uint32_t* vmax_bits;  // [1] max row norm (float bits)
+  const float* bnorm_max;     // [1] max projection-vector norm
+  int32_t* out;               // [n_b][m]
+  uint32_t* counters;
+};
+hipError_t launch_project_scores(bool is_bf16, int d, const void* V, int64_t n, const void* Bt, int n_b, float* PT,
+                                 float* norms, uint32_t* norm_max_bits, hipStream_t st);
+hipError_t launch_col_select(bool is_bf16, int d, const ColSelectArgs& a, hipStream_t st);
+hipError_t launch_mark_items(const int32_t* Q, int n_b, int b_y, int64_t qwords, uint32_t* qbits, hipStream_t st);
+hipError_t launch_group_bounds(const int32_t* keys, const int32_t* sorted, int64_t n, int32_t* start, int32_t* end,
+                               hipStream_t st);
+struct MergeArgs {
+  const void* Y;
+  const void* X;
+  int64_t s;
+  int k;
+  float beta_coef;
+  const float* xnorm;         // [s]
+  const uint32_t* ymax_bits;  // [1]
+  const int32_t* sorted;      // [slots] slots grouped by position
+  const int32_t* pstart;      // [s]
+  const int32_t* pend;        // [s]
+  const int32_t* slot_negs;   // [slots][k] per-slot kept ids, -1 padded
+  const float* slot_negl;     // [slots][k] their float32 logits
+  const int32_t* slot_tid;    // [slots] per-slot threshold id (-1: every candidate kept)
+  const double* slot_te;      // [slots] per-slot threshold logit (float64)
+  double* thr_e;              // [s]
+  int32_t* thr_id;
+  float* thr_lo;
+  float* thr_hi;
+  float* mshift;
+  float* ssum;
+  int32_t* nmem;
+  int32_t* negs;              // [s][k] or nullptr
+  uint32_t* counters;
+};
+size_t merge_lds_bytes(int k);
+hipError_t launch_sce_merge(bool is_bf16, int d, const MergeArgs& a, hipStream_t st);
+hipError_t launch_sce_combine_rows(int d, const float* part, const int32_t* sorted, const int32_t* start,
+                                   const int32_t* end, int64_t n, const BwdArgs& b, bool is_bf16, float* out,
+                                   hipStream_t st);
+hipError_t launch_sce_combine_items(int d, const float* part, const int32_t* sorted, const int32_t* start,
+                                    const int32_t* end, int64_t n, float* out, hipStream_t st);
 
 }  // namespace rece

@@ -122,11 +122,13 @@ struct RecCopy {
 struct Ranges {
   int64_t s0, s1, s2, e0, e1, e2;   // slot ranges [s_q, e_q)
   int c1, c2, c3;                    // cumulative tile counts
-  __device__ __forceinline__ void init(int c, int n_c, int64_t N, int TI) {
+  // nwin = 3: chunks c, c-1, c+1 (distinct ones); nwin = 1: chunk c only
+  __device__ __forceinline__ void init(int c, int n_c, int64_t N, int TI, int nwin) {
     const int cm = (c + n_c - 1) % n_c, cp = (c + 1) % n_c;
     s0 = chunk_start(c, N, n_c);
     e0 = chunk_start(c + 1, N, n_c);
     s1 = e1 = s2 = e2 = 0;
+    if (nwin == 1) n_c = 1;   // no neighbours
     if (n_c >= 2) {
       s1 = chunk_start(cm, N, n_c);
       e1 = chunk_start(cm + 1, N, n_c);

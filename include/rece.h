@@ -129,10 +129,16 @@ typedef enum {
   RECE_STAGE_THRESH_LOGIT = 5, /* float64 [s] its logit (float64, coordinate-order sum) */
   RECE_STAGE_NEG_IDS = 6,    /* int32 [s][k] kept negatives, unordered, -1 padded (KEEP_STAGES) */
   RECE_STAGE_LSE = 7,        /* float32 [s] log-sum-exp over positive + kept set (round ignored) */
-  RECE_STAGE_COUNTERS = 8    /* uint32 [8] device counters: [0] error bits, [1] argmax rows
+  RECE_STAGE_COUNTERS = 8,   /* uint32 [8] device counters: [0] error bits, [1] argmax rows
                                 decided in float64, [2] top-k rows needing float64 values,
                                 [3] logits recomputed in float64, [4] buffer overflows */
+  RECE_STAGE_SCE_ROWS = 9,   /* SCE: int32 [n_b][b_x] positions taken by each bucket (a set per
+                                bucket, in the library's order) */
+  RECE_STAGE_SCE_ITEMS = 10  /* SCE: int32 [n_b][b_y] items taken by each bucket (a set per bucket) */
 } rece_stage;
+/* Stages that a plan does not keep (BUCKET_* and PERM_* for SCE, SCE_* for RECE,
+ * NEG_IDS without RECE_FLAG_KEEP_STAGES) have 0 bytes; rece_export rejects them.
+ * For SCE, THRESH_*, NEG_IDS and LSE describe the final per-position set (round 0). */
 
 rece_status rece_export(rece_plan_t plan, void* stream, const void* saved, int stage, int round,
                         void* dst);

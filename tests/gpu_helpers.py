@@ -47,5 +47,34 @@ def run_rece(inp, keep_stages=True, backward=True, dloss_pp=None, tensors=None):
     return out
 
 
+def run_sce(inp, keep_stages=True, backward=True, dloss_pp=None):
+    """The bucket (SCE) variant on a seeded workload; B is the [d, n_b] slice."""
+    w = inp.w
+    X, Y, pos, B = to_device(inp)
+    B = B[0].contiguous()
+    plan = rece.Plan(w.s, w.C, w.d, w.n_b, 0, w.k, 1, dtype=w.dtype, variant="sce", b_x=w.b_x, b_y=w.b_y,
+                     keep_stages=keep_stages, validate_ids=True)
+    print(f"[gpu] sce s={w.s} C={w.C} d={w.d} n_b={w.n_b} b_x={w.b_x} b_y={w.b_y} k={w.k} "
+          f"dtype={w.dtype} seed={w.seed}", flush=True)
+    loss, lpp, scratch, saved = plan.forward(X, Y, pos, B)
+    out = {}
+    if backward:
+        dpp = None if dloss_pp is None else torch.from_numpy(dloss_pp.astype(np.float32)).cuda()
+        dX, dY = plan.backward(X, Y, pos, scratch, saved, dloss_pp=dpp)
+    plan.check(saved)
+    torch.cuda.synchronize()
+    out["loss"] = loss.item()
+    out["loss_pp"] = lpp.cpu().numpy()
+    if backward:
+        out["dX"] = dX.cpu().numpy()
+        out["dY"] = dY.cpu().numpy()
+    for st in ("counters", "lse", "thresh_id", "thresh_logit", "sce_rows", "sce_items"):
+        out[st] = plan.export(saved, st).cpu().numpy()
+    if keep_stages:
+        out["neg_ids"] = plan.export(saved, "neg_ids").cpu().numpy()
+    torch.cuda.synchronize()
+    return out
+
+
 def grad_err(a, b):
     return float(np.abs(a - b).max() / max(np.abs(b).max(), 1e-30))

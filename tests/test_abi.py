@@ -51,7 +51,10 @@ def _plan(**kw):
     (dict(d=48), 2),            # unsupported width
     (dict(s=0), 1),
     (dict(C=1, k=0, n_c=1), 1),
-    (dict(variant="sce", b_x=4, b_y=8), 2),
+    (dict(variant="sce", b_x=0, b_y=8), 1),          # bucket variant: b_x in 1..s
+    (dict(variant="sce", b_x=4, b_y=2001), 1),       # b_y in 1..C
+    (dict(variant="sce", b_x=4, b_y=8, rounds=2), 1),
+    (dict(variant="sce", b_x=4, b_y=1500, k=1025), 2),   # k above the merge capacity
 ])
 def test_plan_rejects_invalid(bad, status):
     with pytest.raises(rece.ReceError) as ei:
@@ -75,11 +78,12 @@ def test_plan_null_arguments():
     L.rece_plan_destroy(h)
 
 
-@pytest.mark.parametrize("name", ["tiny", "tiny_fullce", "sasrec", "million", "tenmillion"])
+@pytest.mark.parametrize("name", ["tiny", "tiny_fullce", "sasrec", "million", "tenmillion", "sce"])
 def test_workspace_never_holds_a_logit_tensor(name):
     from rece_inputs import WORKLOADS
     w = WORKLOADS[name]
-    p = rece.Plan(w.s, w.C, w.d, w.n_b, w.n_c, w.k, w.rounds, dtype=w.dtype)
+    p = rece.Plan(w.s, w.C, w.d, w.n_b, w.n_c, w.k, w.rounds, dtype=w.dtype, variant=w.variant,
+                  b_x=w.b_x, b_y=w.b_y)
     # no buffer of s*C*2 bytes (a bf16 [s, C] logit tensor) is ever needed
     assert p.scratch_bytes < w.s * w.C * 2
     assert p.saved_bytes < w.s * w.C * 2
@@ -107,3 +111,18 @@ def test_product_path_has_no_fallback():
         if f.endswith(".py"):
             text = open(os.path.join(ROOT, "catalogue_cross_entropy_amd", f)).read()
             assert "oracle" not in text, f
+
+
+def test_sce_plan_and_exports():
+    p = _plan(variant="sce", n_c=0, b_x=40, b_y=300, k=16, keep_stages=True)
+    L = rece.lib()
+    nb = ctypes.c_size_t()
+    sizes = {}
+    for name, st in rece.STAGES.items():
+        assert L.rece_export_bytes(p._h, st, ctypes.byref(nb)) == 0
+        sizes[name] = nb.value
+    assert sizes["sce_rows"] == 16 * 40 * 4 and sizes["sce_items"] == 16 * 300 * 4
+    assert sizes["bucket_x"] == sizes["perm_y"] == 0       # not kept by the bucket variant
+    assert sizes["neg_ids"] == 256 * 16 * 4 and sizes["lse"] == 256 * 4
+    r = _plan(keep_stages=True)
+    assert L.rece_export_bytes(r._h, rece.STAGES["sce_rows"], ctypes.byref(nb)) == 0 and nb.value == 0
