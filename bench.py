@@ -42,6 +42,23 @@ def window_logits(w):
     return tot
 
 
+def algorithmic_work_sce(w):
+    """Per-step algorithmic (flops, bytes) of the bucket variant's phases."""
+    es = 2 if w.dtype == "bf16" else 4
+    s, C, d, nb = w.s, w.C, w.d, w.n_b
+    sx, sy = nb * w.b_x, nb * w.b_y
+    logits = sx * w.b_y
+    return {
+        "project": (2.0 * d * nb * (s + C), (s + C) * d * es),
+        "sort": (0.0, nb * (s + C) * 4 + (sx + sy) * (d * es + 8)),      # score columns, bucket rows
+        "select": (float(ALU_OPS_PER_LOGIT * logits), (sx + sy) * d * es + sx * w.k * 8),
+        "loss": (2.0 * d * s, s * (2 * d * es + 24)),
+        "bwd_dx": (2.0 * d * logits, (sx + sy) * d * es + sx * d * 4 + s * d * 4),
+        "bwd_dy": (2.0 * d * logits, (sx + sy) * d * es + sy * d * 4 + C * d * 4),
+        "bwd_pos": (2.0 * d * s, s * (d * es + 16) + s * d * 4),
+    }
+
+
 def algorithmic_work(w):
     """Per-step algorithmic (flops, bytes) of each phase: what the method must compute and
     move; logits never go to HBM, every vector is read once per pass.  The chunk kernel's
@@ -157,8 +174,11 @@ def main():
     X = torch.from_numpy(inp.X).to(dev).to(dt)
     Y = torch.from_numpy(inp.Y).to(dev).to(dt)
     B = torch.from_numpy(inp.B).to(dev).to(dt)
+    if w.variant == "sce":
+        B = B[0].contiguous()
     pos = torch.from_numpy(inp.pos).to(dev)
-    plan = rece.Plan(w.s, w.C, w.d, w.n_b, w.n_c, w.k, w.rounds, dtype=w.dtype)
+    plan = rece.Plan(w.s, w.C, w.d, w.n_b, w.n_c, w.k, w.rounds, dtype=w.dtype, variant=w.variant,
+                     b_x=w.b_x, b_y=w.b_y)
     scratch, saved = plan.workspace(dev)
     dX = torch.empty((w.s, w.d), dtype=torch.float32, device=dev)
     dY = torch.empty((w.C, w.d), dtype=torch.float32, device=dev)
@@ -181,7 +201,7 @@ def main():
     torch.cuda.synchronize()
     phases = plan.profile_read()
     plan.profile(enable=False)
-    work = algorithmic_work(w)
+    work = algorithmic_work_sce(w) if w.variant == "sce" else algorithmic_work(w)
     dom = max((k for k in work), key=lambda k: phases[k][0])
 
     # timed region: events only around the dominant kernel's launches
@@ -226,15 +246,16 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": f"{w.name}: s={w.s} ({w.seqs}x{w.seqlen}), C={w.C}, d={w.d}, "
-                               f"n_b={w.n_b}, n_c={w.n_c}, k={w.k}, rounds={w.rounds}, {w.dtype}, "
-                               f"positives {w.positives}", "parallelism": "single GPU"},
+        "config": {"workload": (f"{w.name}: s={w.s} ({w.seqs}x{w.seqlen}), C={w.C}, d={w.d}, "
+                                + (f"n_b={w.n_b}, n_c={w.n_c}, k={w.k}, rounds={w.rounds}, " if w.variant == "rece"
+                                   else f"n_b={w.n_b}, b_x={w.b_x}, b_y={w.b_y}, k={w.k}, ")
+                                + f"{w.dtype}, positives {w.positives}"), "parallelism": "single GPU"},
         "roofline": rl,
         "phases": breakdown,
         "counters": {"argmax_rows_float64": counters[1], "topk_rows_near_tie": counters[2],
                      "logits_float64": counters[3], "overflows": counters[4]},
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and w.variant == "rece":
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_rows)
     print(json.dumps(out), flush=True)
     if args.copy_probe_mb > 0:
