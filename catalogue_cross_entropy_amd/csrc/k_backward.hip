@@ -8,8 +8,9 @@
 // pass (float32 bounds first, float64 recomputation inside the bounds).  A pair
 // already kept in an earlier round is skipped, so every kept pair counts once.
 //   * k_bwd_rows: per (X-chunk, position tile), dX += G . Y_window, G the 16x64
-//     gradient block of the tile (bf16 hi+lo split for bf16 inputs, so G keeps
-//     ~16 significant bits; float32 matrix cores for float32 inputs);
+//     gradient block of the tile, kept in registers in the operand layout of the
+//     product (bf16 hi+lo split for bf16 inputs, so G keeps ~16 significant bits;
+//     float32 matrix cores for float32 inputs);
 //   * k_bwd_items: per (item chunk, item tile), dY += G^T . X over the positions
 //     of the three X-chunks whose windows hold the tile - a reduction grouped by
 //     item in sorted order, no atomics;
@@ -46,53 +47,68 @@ __device__ __forceinline__ bool sce_seen_before(const BwdArgs& p, int start, int
   return false;
 }
 
-constexpr int GP = 68;   // pitch (floats) of the per-wave gradient block [16][TI]
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4v lds_short4;
 
-// acc[nb] += G[16][TI] . tile[TI][D] for the wave's 16 rows; G in LDS (float), the
-// tile in the swizzled row layout of the streamer (K = tile rows, N = coordinates).
+// Four 16-bit values of coordinate 16*nb + (l % 16) for items r0 .. r0 + 3 of a
+// swizzled bf16 tile, r0 = base + 4*(l/16): one LDS transpose read.  Within each
+// 16-lane group, source lane j names 4 coordinates of one item (item r0 + j/4,
+// coordinates 16*nb + 4*(j%4) .. +3); the read hands lane i coordinate i of the
+// group's 4 items.
+template <int D>
+__device__ __forceinline__ short4v tile_tr4(const char* rows, int base, int nb) {
+  using G = TileGeom<bf16, D>;
+  const int l = lane_id(), j = l & 15;
+  const int row = base + 4 * (l >> 4) + (j >> 2);
+  const int dim0 = 16 * nb + 4 * (j & 3);
+  const int ch = (dim0 >> 3) ^ (row & G::SWM);
+  const char* addr = rows + row * G::RB + ch * 16 + ((dim0 >> 2) & 1) * 8;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(addr));
+}
+
+// acc[nb] += G[16 positions][TI items] . tile[TI items][D] where lane l holds
+// G[position l % 16][item 16*cb + 4*(l/16) + v] in gv[cb][v].  bf16: G split into
+// bf16 hi + lo (~16 significant bits), k = 32 items per step, item order
+// (4 of block 2ks, 4 of block 2ks+1) on both operands; f32: k = 4 items per step.
 template <class E, int D>
-__device__ __forceinline__ void accumulate_gt(f32x4 (&acc)[D / 16], const float* Gb, const char* rows) {
+__device__ __forceinline__ void accumulate_rows(f32x4 (&acc)[D / 16], const float (&gv)[TileGeom<E, D>::TI / 16][4],
+                                                const char* rows) {
   using G = TileGeom<E, D>;
   const int l = lane_id();
-  const int q = l >> 4;
   if constexpr (sizeof(E) == 2) {
 #pragma unroll
     for (int ks = 0; ks < G::TI / 32; ++ks) {
       uint32_t ph[4], pl[4];
 #pragma unroll
-      for (int t = 0; t < 8; t += 2) {
-        const float g0 = Gb[(l & 15) * GP + 32 * ks + 8 * q + t];
-        const float g1 = Gb[(l & 15) * GP + 32 * ks + 8 * q + t + 1];
+      for (int e = 0; e < 8; e += 2) {
+        const float g0 = gv[2 * ks + (e >> 2)][e & 3], g1 = gv[2 * ks + (e >> 2)][(e & 3) + 1];
         const uint32_t h0 = bf16_rne(g0), h1 = bf16_rne(g1);
         const uint32_t l0 = bf16_rne(g0 - __uint_as_float(h0 << 16)), l1 = bf16_rne(g1 - __uint_as_float(h1 << 16));
-        ph[t / 2] = h0 | (h1 << 16);
-        pl[t / 2] = l0 | (l1 << 16);
+        ph[e / 2] = h0 | (h1 << 16);
+        pl[e / 2] = l0 | (l1 << 16);
       }
       const bf16x8 ahi = __builtin_bit_cast(bf16x8, u32x4{ph[0], ph[1], ph[2], ph[3]});
       const bf16x8 alo = __builtin_bit_cast(bf16x8, u32x4{pl[0], pl[1], pl[2], pl[3]});
 #pragma unroll
       for (int nb = 0; nb < D / 16; ++nb) {
-        const int dim = 16 * nb + (l & 15);
-        uint32_t bw[4];
-#pragma unroll
-        for (int t = 0; t < 8; t += 2) {
-          const int item = 32 * ks + 8 * q + t;
-          bw[t / 2] = tile_bits16<D>(rows, item, dim) | (tile_bits16<D>(rows, item + 1, dim) << 16);
-        }
-        const bf16x8 b = __builtin_bit_cast(bf16x8, u32x4{bw[0], bw[1], bw[2], bw[3]});
+        const short4v b0 = tile_tr4<D>(rows, 32 * ks, nb);
+        const short4v b1 = tile_tr4<D>(rows, 32 * ks + 16, nb);
+        const short4v b8[2] = {b0, b1};
+        const bf16x8 b = __builtin_bit_cast(bf16x8, b8);
         acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, b, acc[nb], 0, 0, 0);
         acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, b, acc[nb], 0, 0, 0);
       }
     }
   } else {
+    const int g = l >> 4;
 #pragma unroll
-    for (int ks = 0; ks < G::TI / 4; ++ks) {
-      const float a = Gb[(l & 15) * GP + 4 * ks + q];
+    for (int cb = 0; cb < G::TI / 16; ++cb)
 #pragma unroll
-      for (int nb = 0; nb < D / 16; ++nb)
-        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, tile_elem<float, D>(rows, 4 * ks + q, 16 * nb + (l & 15)),
-                                                        acc[nb], 0, 0, 0);
-    }
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int nb = 0; nb < D / 16; ++nb)
+          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+              gv[cb][v], tile_elem<float, D>(rows, 16 * cb + 4 * g + v, 16 * nb + (l & 15)), acc[nb], 0, 0, 0);
   }
 }
 
@@ -100,10 +116,16 @@ __device__ __forceinline__ void accumulate_gt(f32x4 (&acc)[D / 16], const float*
 __host__ __device__ constexpr size_t rows_slot_bytes(size_t row_bytes, int rounds) {
   return row_bytes + 256 * (size_t)rounds;
 }
-constexpr size_t ROWS_WAVE_LDS = 16 * GP * 4 + 16 * MAX_ROUNDS * sizeof(PrevRow);
+constexpr size_t ROWS_WAVE_LDS = 16 * MAX_ROUNDS * sizeof(PrevRow);
 
 // SCE = true: bucket variant (rows are (bucket, position) slots, window = the
 // bucket's items, output = one partial row per slot, no positive term).
+//
+// Layout: the logit block is computed transposed (items x positions), so lane l
+// holds position l % 16 for items 4*(l/16) + v of every 16-item block.  Those
+// are exactly the values the G . Y product needs as its A operand (k = items,
+// permuted identically on both sides), so G never goes through LDS; the B
+// operand (Y transposed) comes from the row tile with the LDS transpose read.
 template <class E, int D, int NW, bool SCE>
 __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_bwd_rows(BwdArgs p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -119,9 +141,7 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_bwd
   const size_t slot_bytes = rows_slot_bytes(G::ROW_BYTES, p.rounds);
   char* ring = smem;
   const int w = threadIdx.x >> 6, l = lane_id(), g = l >> 4;
-  char* wb = smem + 3 * slot_bytes + (size_t)w * ROWS_WAVE_LDS;
-  float* Gb = reinterpret_cast<float*>(wb);
-  PrevRow* prev = reinterpret_cast<PrevRow*>(wb + 16 * GP * 4);
+  PrevRow* prev = reinterpret_cast<PrevRow*>(smem + 3 * slot_bytes + (size_t)w * ROWS_WAVE_LDS);
 
   const int lb = xcd_block(blockIdx.x, gridDim.x);
   const int c = lb / p.tiles_per_chunk;
@@ -135,35 +155,20 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_bwd
   win.init(c, n_c, C, TI, p.nwin);
   const int ntiles = win.ntiles();
 
+  // this lane's position: row l % 16 of the wave
   const int64_t pA = wrow0 + (l & 15);
+  const bool rvA = pA < x1;
   Frag<E, D> afr;
-  afr.load_global(pA < x1 ? Xs + pA * D : nullptr);
+  afr.load_global(rvA ? Xs + pA * D : nullptr);
   if (l < 16)
-    for (int r2 = 0; r2 < rho; ++r2)
-      prev[l * MAX_ROUNDS + r2] = pA < x1 ? p.prev[(int64_t)r2 * s + pA] : PrevRow{};
+    for (int r2 = 0; r2 < rho; ++r2) prev[l * MAX_ROUNDS + r2] = rvA ? p.prev[(int64_t)r2 * s + pA] : PrevRow{};
+  const PosRec rc = p.rec[rvA ? pA : x0];
+  const int posA = rvA ? rc.pos : -1;
+  const float lseA = rc.lse, gbA = rc.gb, loA = rc.lo, hiA = rc.hi;
+  const double teA = rc.te;
+  const int tidA = rc.tid, gstA = rc.pad0, gmA = rc.pad1;
+  const E* xrowA = Xs + (rvA ? pA : x0) * D;
 
-  int i_v[4], pos_v[4], tid_v[4];
-  int gst_v[4], gm_v[4];   // bucket variant: the position's group start, earlier slots
-  float lse_v[4], gb_v[4], lo_v[4], hi_v[4], lpos_v[4];
-  double te_v[4];
-  bool rv[4];
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int64_t pr = wrow0 + 4 * g + v;
-    rv[v] = pr < x1;
-    const PosRec rc = p.rec[rv[v] ? pr : x0];
-    i_v[v] = rc.i;
-    pos_v[v] = rv[v] ? rc.pos : -1;
-    lse_v[v] = rc.lse;
-    gb_v[v] = rc.gb;
-    lo_v[v] = rc.lo;
-    hi_v[v] = rc.hi;
-    te_v[v] = rc.te;
-    tid_v[v] = rc.tid;
-    lpos_v[v] = rc.lpos;
-    gst_v[v] = rc.pad0;
-    gm_v[v] = rc.pad1;
-  }
   f32x4 dacc[D / 16];
 #pragma unroll
   for (int nb = 0; nb < D / 16; ++nb) dacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -182,53 +187,59 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_bwd
     const char* slot = ring + (size_t)(t % 3) * slot_bytes;
     const int32_t* tid_ = reinterpret_cast<const int32_t*>(slot + G::ROW_BYTES);
     const int32_t* tcy = tid_ + 64;
+    const int nlim = (int)(q1 - q0);   // valid rows of this tile
+    f32x4 acc[NCB];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
-      const int n = cb * 16 + (l & 15);
       Frag<E, D> bf;
-      TileFrag<E, D>::load(bf, slot, n);
-      const f32x4 acc = mma_block(afr, bf, f32x4{0.f, 0.f, 0.f, 0.f});
-      const bool nvalid = q0 + n < q1;
-      const int j = tid_[n];
+      TileFrag<E, D>::load(bf, slot, cb * 16 + (l & 15));
+      acc[cb] = mma_block(bf, afr, f32x4{0.f, 0.f, 0.f, 0.f});   // [item 4g+v][position l%16]
+    }
+    float gv[NCB][4];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const int n0 = cb * 16 + 4 * g;
+      const u32x4 jj = *reinterpret_cast<const u32x4*>(tid_ + n0);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const float a = acc[v];
-        const int r = 4 * g + v;
-        float gv = 0.0f;
-        if (rv[v] && nvalid && j != pos_v[v]) {
-          const E* xrow = Xs + (wrow0 + r) * D;
-          bool mem = beats<E, D>(a, lo_v[v], hi_v[v], te_v[v], tid_v[v], xrow, Y, j, nexact);
-          if (SCE && mem && gm_v[v] > 0 && sce_seen_before(p, gst_v[v], gm_v[v], j)) mem = false;
+        const int n = n0 + v;
+        const int j = (int)jj[v];
+        const float a = acc[cb][v];
+        const bool cand = rvA && n < nlim && j != posA;
+        bool mem = cand && a > hiA;
+        if (cand && !mem && a >= loA)   // inside the float32 bounds: float64 decides (rare)
+          mem = beats<E, D>(a, loA, hiA, teA, tidA, xrowA, Y, j, nexact);
+        if ((SCE || rho > 0) && mem) {
+          if (SCE && gmA > 0 && sce_seen_before(p, gstA, gmA, j)) mem = false;
           for (int r2 = 0; r2 < rho && mem; ++r2) {
-            const PrevRow pr = prev[r * MAX_ROUNDS + r2];
+            const PrevRow pr = prev[(l & 15) * MAX_ROUNDS + r2];
             if (!in_window(pr.cx, tcy[64 * r2 + n], n_c)) continue;
-            if (beats<E, D>(a, pr.lo, pr.hi, pr.te, pr.tid, xrow, Y, j, nexact)) mem = false;
+            if (beats<E, D>(a, pr.lo, pr.hi, pr.te, pr.tid, xrowA, Y, j, nexact)) mem = false;
           }
-          if (mem) gv = expf(a - lse_v[v]) * gb_v[v];
         }
-        Gb[r * GP + n] = gv;
+        gv[cb][v] = mem ? __expf(a - lseA) * gbA : 0.0f;
       }
     }
-    wave_sync();
-    accumulate_gt<E, D>(dacc, Gb, slot);
-    wave_sync();
+    accumulate_rows<E, D>(dacc, gv, slot);
   }
 
   // write: rows 4g+v, coordinates 16nb + (l & 15); round 0 adds the positive term
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    if (!rv[v]) continue;
+    const int64_t pr = wrow0 + 4 * g + v;
+    if (pr >= x1) continue;
     if (SCE) {   // partial row of this slot
-      float* dst = p.dX + (wrow0 + 4 * g + v) * D;
+      float* dst = p.dX + pr * D;
 #pragma unroll
       for (int nb = 0; nb < D / 16; ++nb) dst[16 * nb + (l & 15)] = dacc[nb][v];
       continue;
     }
-    float* dst = p.dX + (int64_t)i_v[v] * D;
+    const PosRec rv = p.rec[pr];
+    float* dst = p.dX + (int64_t)rv.i * D;
     float gpos = 0.0f;
-    const int pclamp = pos_v[v] < 0 ? 0 : (pos_v[v] >= p.C ? (int)(p.C - 1) : pos_v[v]);
+    const int pclamp = rv.pos < 0 ? 0 : (rv.pos >= p.C ? (int)(p.C - 1) : rv.pos);
     const E* ypos = Y + (int64_t)pclamp * D;
-    if (rho == 0) gpos = (expf(lpos_v[v] - lse_v[v]) - 1.0f) * gb_v[v];
+    if (rho == 0) gpos = (expf(rv.lpos - rv.lse) - 1.0f) * rv.gb;
 #pragma unroll
     for (int nb = 0; nb < D / 16; ++nb) {
       const int t = 16 * nb + (l & 15);
@@ -253,7 +264,7 @@ struct ItemsLayout {
     return (size_t)G::ROW_BYTES + RC::LDS_BYTES + (size_t)(rounds > 1 ? rounds - 1 : 0) * PC::LDS_BYTES;
   }
 };
-constexpr size_t ITEMS_WAVE_LDS = 16 * GP * 4 + 16 * MAX_ROUNDS * 4;
+constexpr size_t ITEMS_WAVE_LDS = 16 * MAX_ROUNDS * 4;
 
 // Copies of position tile t: rows of the sorted positions, their records, and their
 // records of each earlier round, into ring slot t % 3.
@@ -273,6 +284,9 @@ __device__ __forceinline__ void issue_items_tile(char* ring, size_t slot_bytes, 
                   G::ROW_DMA + LY::RC::COPIES + r2 * LY::PC::COPIES, wave, nwaves);
 }
 
+// Transposed logit block as in k_bwd_rows: lane l holds item l % 16 of the wave
+// and positions 4*(l/16) + v of every 16-position block of the tile, the A
+// operand of dY = G^T . X; X transposed comes from the tile by transpose reads.
 template <class E, int D, int NW, bool SCE>
 __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_bwd_items(BwdArgs p, int itiles) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -289,9 +303,7 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_bwd
   const size_t slot_bytes = LY::slot_bytes(p.rounds);
   char* ring = smem;
   const int w = threadIdx.x >> 6, l = lane_id(), g = l >> 4;
-  char* wb = smem + 3 * slot_bytes + (size_t)w * ITEMS_WAVE_LDS;
-  float* Gb = reinterpret_cast<float*>(wb);
-  int32_t* cy2w = reinterpret_cast<int32_t*>(wb + 16 * GP * 4);   // [16][MAX_ROUNDS]
+  int32_t* cy2w = reinterpret_cast<int32_t*>(smem + 3 * slot_bytes + (size_t)w * ITEMS_WAVE_LDS);   // [16][MAX_ROUNDS]
 
   const int lb = xcd_block(blockIdx.x, gridDim.x);
   const int c = lb / itiles;
@@ -305,20 +317,14 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_bwd
   xr.init(c, n_c, s, TI, p.nwin);   // X-chunks whose window holds item chunk c (the relation is symmetric)
   const int ntiles = xr.ntiles();
 
+  // this lane's item: row l % 16 of the wave
   const int64_t qA = wq0 + (l & 15);
+  const bool rvA = qA < y1;
+  const int jA = rvA ? p.perm_y[qA] : -1;
   Frag<E, D> afr;
-  afr.load_global(qA < y1 ? Ys + qA * D : nullptr);
+  afr.load_global(rvA ? Ys + qA * D : nullptr);
   if (l < 16)
-    for (int r2 = 0; r2 < rho; ++r2) cy2w[l * MAX_ROUNDS + r2] = qA < y1 ? p.cyp[(int64_t)r2 * C + qA] : 0;
-
-  int j_v[4];
-  bool rv[4];
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int64_t qr = wq0 + 4 * g + v;
-    rv[v] = qr < y1;
-    j_v[v] = rv[v] ? p.perm_y[qr] : -1;
-  }
+    for (int r2 = 0; r2 < rho; ++r2) cy2w[l * MAX_ROUNDS + r2] = rvA ? p.cyp[(int64_t)r2 * C + qA] : 0;
   f32x4 dacc[D / 16];
 #pragma unroll
   for (int nb = 0; nb < D / 16; ++nb) dacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -326,7 +332,6 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_bwd
   const int ncopies = G::ROW_DMA + LY::RC::COPIES + rho * LY::PC::COPIES;
   int my_copies = 0;
   for (int u = w; u < ncopies; u += NW) ++my_copies;
-
 
   __syncthreads();
   issue_items_tile<E, D>(ring, slot_bytes, xr, 0, Xs, p.rec, p.prev, s, rho, w, NW);
@@ -339,43 +344,46 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_bwd
     const char* slot = ring + (size_t)(t % 3) * slot_bytes;
     const PosRec* recs = reinterpret_cast<const PosRec*>(slot + G::ROW_BYTES);
     const PrevRow* prevs = reinterpret_cast<const PrevRow*>(slot + G::ROW_BYTES + LY::RC::LDS_BYTES);
+    const int nlim = (int)(q1 - q0);   // valid rows of this tile
+    f32x4 acc[NCB];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
-      const int n = cb * 16 + (l & 15);
       Frag<E, D> bf;
-      TileFrag<E, D>::load(bf, slot, n);
-      const f32x4 acc = mma_block(afr, bf, f32x4{0.f, 0.f, 0.f, 0.f});
-      const bool nvalid = q0 + n < q1;
-      const PosRec pi = recs[n];
+      TileFrag<E, D>::load(bf, slot, cb * 16 + (l & 15));
+      acc[cb] = mma_block(bf, afr, f32x4{0.f, 0.f, 0.f, 0.f});   // [position 4g+v][item l%16]
+    }
+    float gv[NCB][4];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const float a = acc[v];
-        const int j = j_v[v];
-        const int r = 4 * g + v;
-        float gv = 0.0f;
-        if (rv[v] && nvalid && j != pi.pos) {
-          const E* xrow = Xs + (q0 + n) * D;
-          bool mem = beats<E, D>(a, pi.lo, pi.hi, pi.te, pi.tid, xrow, Y, j, nexact);
-          if (SCE && mem && pi.pad1 > 0 && sce_seen_before(p, pi.pad0, pi.pad1, j)) mem = false;
+        const int n = cb * 16 + 4 * g + v;
+        const f32x4 hot = *reinterpret_cast<const f32x4*>(&recs[n].lse);   // lse, gb, lo, hi
+        const int pos_n = recs[n].pos;
+        const float a = acc[cb][v];
+        const bool cand = rvA && n < nlim && jA != pos_n;
+        bool mem = cand && a > hot[3];
+        if (cand && !mem && a >= hot[2])   // inside the float32 bounds: float64 decides (rare)
+          mem = beats<E, D>(a, hot[2], hot[3], recs[n].te, recs[n].tid, Xs + (q0 + n) * D, Y, jA, nexact);
+        if ((SCE || rho > 0) && mem) {
+          if (SCE && recs[n].pad1 > 0 && sce_seen_before(p, recs[n].pad0, recs[n].pad1, jA)) mem = false;
           for (int r2 = 0; r2 < rho && mem; ++r2) {
             const PrevRow pr = prevs[(size_t)r2 * (LY::PC::LDS_BYTES / sizeof(PrevRow)) + n];
-            if (!in_window(pr.cx, cy2w[r * MAX_ROUNDS + r2], n_c)) continue;
-            if (beats<E, D>(a, pr.lo, pr.hi, pr.te, pr.tid, xrow, Y, j, nexact)) mem = false;
+            if (!in_window(pr.cx, cy2w[(l & 15) * MAX_ROUNDS + r2], n_c)) continue;
+            if (beats<E, D>(a, pr.lo, pr.hi, pr.te, pr.tid, Xs + (q0 + n) * D, Y, jA, nexact)) mem = false;
           }
-          if (mem) gv = expf(a - pi.lse) * pi.gb;
         }
-        Gb[r * GP + n] = gv;
+        gv[cb][v] = mem ? __expf(a - hot[0]) * hot[1] : 0.0f;
       }
     }
-    wave_sync();
-    accumulate_gt<E, D>(dacc, Gb, slot);
-    wave_sync();
+    accumulate_rows<E, D>(dacc, gv, slot);
   }
 
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    if (!rv[v]) continue;
-    float* dst = p.dY + (SCE ? wq0 + 4 * g + v : (int64_t)j_v[v]) * D;
+    const int64_t qr = wq0 + 4 * g + v;
+    if (qr >= y1) continue;
+    float* dst = p.dY + (SCE ? qr : (int64_t)p.perm_y[qr]) * D;
 #pragma unroll
     for (int nb = 0; nb < D / 16; ++nb) {
       const int t = 16 * nb + (l & 15);

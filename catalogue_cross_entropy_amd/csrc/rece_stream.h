@@ -205,14 +205,6 @@ template <int D> struct TileFrag<float, D> {
   }
 };
 
-// Raw 16-bit pattern of element (row n, coordinate t) of a swizzled bf16 tile.
-template <int D>
-__device__ __forceinline__ uint32_t tile_bits16(const char* rows, int n, int t) {
-  using G = TileGeom<bf16, D>;
-  const int c = (t >> 3) ^ (n & G::SWM);
-  return *reinterpret_cast<const uint16_t*>(rows + n * G::RB + c * 16 + 2 * (t & 7));
-}
-
 // Element (row n, coordinate t) of a swizzled tile, as float.
 template <class E, int D>
 __device__ __forceinline__ float tile_elem(const char* rows, int n, int t) {
