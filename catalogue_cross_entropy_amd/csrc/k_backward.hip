@@ -47,23 +47,19 @@ __device__ __forceinline__ bool sce_seen_before(const BwdArgs& p, int start, int
   return false;
 }
 
-typedef short short4v __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) short4v lds_short4;
-
-// Four 16-bit values of coordinate 16*nb + (l % 16) for items r0 .. r0 + 3 of a
-// swizzled bf16 tile, r0 = base + 4*(l/16): one LDS transpose read.  Within each
-// 16-lane group, source lane j names 4 coordinates of one item (item r0 + j/4,
-// coordinates 16*nb + 4*(j%4) .. +3); the read hands lane i coordinate i of the
-// group's 4 items.
+// LDS address of the transpose read giving four 16-bit values of coordinate
+// 16*nb + (l % 16) for items r0 .. r0 + 3 of a swizzled bf16 tile, r0 = base +
+// 4*(l/16) (ds_read_b64_tr_b16).  Within each 16-lane group, source lane j names
+// 4 coordinates of one item (item r0 + j/4, coordinates 16*nb + 4*(j%4) .. +3);
+// the read hands lane i coordinate i of the group's 4 items.
 template <int D>
-__device__ __forceinline__ short4v tile_tr4(const char* rows, int base, int nb) {
+__device__ __forceinline__ const char* tile_tr4_addr(const char* rows, int base, int nb) {
   using G = TileGeom<bf16, D>;
   const int l = lane_id(), j = l & 15;
   const int row = base + 4 * (l >> 4) + (j >> 2);
   const int dim0 = 16 * nb + 4 * (j & 3);
   const int ch = (dim0 >> 3) ^ (row & G::SWM);
-  const char* addr = rows + row * G::RB + ch * 16 + ((dim0 >> 2) & 1) * 8;
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(addr));
+  return rows + row * G::RB + ch * 16 + ((dim0 >> 2) & 1) * 8;
 }
 
 // acc[nb] += G[16 positions][TI items] . tile[TI items][D] where lane l holds
@@ -91,8 +87,8 @@ __device__ __forceinline__ void accumulate_rows(f32x4 (&acc)[D / 16], const floa
       const bf16x8 alo = __builtin_bit_cast(bf16x8, u32x4{pl[0], pl[1], pl[2], pl[3]});
 #pragma unroll
       for (int nb = 0; nb < D / 16; ++nb) {
-        const short4v b0 = tile_tr4<D>(rows, 32 * ks, nb);
-        const short4v b1 = tile_tr4<D>(rows, 32 * ks + 16, nb);
+        short4v b0, b1;
+        lds_tr16_pair(tile_tr4_addr<D>(rows, 32 * ks, nb), tile_tr4_addr<D>(rows, 32 * ks + 16, nb), b0, b1);
         const short4v b8[2] = {b0, b1};
         const bf16x8 b = __builtin_bit_cast(bf16x8, b8);
         acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, b, acc[nb], 0, 0, 0);
@@ -177,12 +173,12 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_bwd
   int my_copies = 0;
   for (int u = w; u < ncopies; u += NW) ++my_copies;
   __syncthreads();
-  issue_window_tile<E, D>(ring, slot_bytes, win, 0, Ys, p.perm_y, p.cyp, C, rho, w, NW);
-  if (ntiles > 1) issue_window_tile<E, D>(ring, slot_bytes, win, 1, Ys, p.perm_y, p.cyp, C, rho, w, NW);
+  issue_window_tile<E, D, NW>(ring, slot_bytes, win, 0, Ys, p.perm_y, p.cyp, C, rho, w);
+  if (ntiles > 1) issue_window_tile<E, D, NW>(ring, slot_bytes, win, 1, Ys, p.perm_y, p.cyp, C, rho, w);
   for (int t = 0; t < ntiles; ++t) {
     wait_vmcnt(t + 1 < ntiles ? my_copies : 0);
     raw_barrier();
-    if (t + 2 < ntiles) issue_window_tile<E, D>(ring, slot_bytes, win, t + 2, Ys, p.perm_y, p.cyp, C, rho, w, NW);
+    if (t + 2 < ntiles) issue_window_tile<E, D, NW>(ring, slot_bytes, win, t + 2, Ys, p.perm_y, p.cyp, C, rho, w);
     const int64_t q0 = range_tile_start(win, t, TI), q1 = range_tile_end(win, t);
     const char* slot = ring + (size_t)(t % 3) * slot_bytes;
     const int32_t* tid_ = reinterpret_cast<const int32_t*>(slot + G::ROW_BYTES);
@@ -268,20 +264,20 @@ constexpr size_t ITEMS_WAVE_LDS = 16 * MAX_ROUNDS * 4;
 
 // Copies of position tile t: rows of the sorted positions, their records, and their
 // records of each earlier round, into ring slot t % 3.
-template <class E, int D>
+template <class E, int D, int NW>
 __device__ __forceinline__ void issue_items_tile(char* ring, size_t slot_bytes, Ranges r, int t, const E* xs,
                                                  const PosRec* rec, const PrevRow* prev, int64_t s, int rho,
-                                                 int wave, int nwaves) {
+                                                 int wave) {
   using G = TileGeom<E, D>;
   using LY = ItemsLayout<E, D>;
   const int64_t q0 = range_tile_start(r, t, G::TI), q1 = range_tile_end(r, t);
   char* slot = ring + (size_t)(t % 3) * slot_bytes;
-  dma_rows<E, D>(slot, xs, q0, q1, wave, nwaves);
+  dma_rows<E, D, NW>(slot, xs, q0, q1, wave);
   char* rb = slot + G::ROW_BYTES;
-  LY::RC::issue(rb, rec, q0, q1, G::ROW_DMA, wave, nwaves);
+  LY::RC::template issue<NW>(rb, rec, q0, q1, G::ROW_DMA, wave);
   for (int r2 = 0; r2 < rho; ++r2)
-    LY::PC::issue(rb + LY::RC::LDS_BYTES + (size_t)r2 * LY::PC::LDS_BYTES, prev + (int64_t)r2 * s, q0, q1,
-                  G::ROW_DMA + LY::RC::COPIES + r2 * LY::PC::COPIES, wave, nwaves);
+    LY::PC::template issue<NW>(rb + LY::RC::LDS_BYTES + (size_t)r2 * LY::PC::LDS_BYTES, prev + (int64_t)r2 * s, q0,
+                               q1, G::ROW_DMA + LY::RC::COPIES + r2 * LY::PC::COPIES, wave);
 }
 
 // Transposed logit block as in k_bwd_rows: lane l holds item l % 16 of the wave
@@ -334,12 +330,12 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_bwd
   for (int u = w; u < ncopies; u += NW) ++my_copies;
 
   __syncthreads();
-  issue_items_tile<E, D>(ring, slot_bytes, xr, 0, Xs, p.rec, p.prev, s, rho, w, NW);
-  if (ntiles > 1) issue_items_tile<E, D>(ring, slot_bytes, xr, 1, Xs, p.rec, p.prev, s, rho, w, NW);
+  issue_items_tile<E, D, NW>(ring, slot_bytes, xr, 0, Xs, p.rec, p.prev, s, rho, w);
+  if (ntiles > 1) issue_items_tile<E, D, NW>(ring, slot_bytes, xr, 1, Xs, p.rec, p.prev, s, rho, w);
   for (int t = 0; t < ntiles; ++t) {
     wait_vmcnt(t + 1 < ntiles ? my_copies : 0);
     raw_barrier();
-    if (t + 2 < ntiles) issue_items_tile<E, D>(ring, slot_bytes, xr, t + 2, Xs, p.rec, p.prev, s, rho, w, NW);
+    if (t + 2 < ntiles) issue_items_tile<E, D, NW>(ring, slot_bytes, xr, t + 2, Xs, p.rec, p.prev, s, rho, w);
     const int64_t q0 = range_tile_start(xr, t, TI), q1 = range_tile_end(xr, t);
     const char* slot = ring + (size_t)(t % 3) * slot_bytes;
     const PosRec* recs = reinterpret_cast<const PosRec*>(slot + G::ROW_BYTES);

@@ -24,10 +24,11 @@
 // Rounds: a pair already kept in an earlier round is skipped (the page's
 // minus-ln(count) rule makes the multiset of copies a set).  Outputs per position
 // and round: the threshold and the sum of exp(logit - shift) over the new pairs.
+#include <type_traits>
+
 #include "rece_device.h"
 #include "rece_internal.h"
 #include "rece_stream.h"
-#include "rece_kth.h"
 
 namespace rece {
 
@@ -47,8 +48,6 @@ struct WaveLds {
                     // aliased by vals/ids (collect pass)
   float* vals;      // [16][SEL_CAP]
   int32_t* ids;     // [16][SEL_CAP]
-  uint32_t* khist;  // [NBINS] scratch of wave_kth_largest
-  float* cv;        // [64] scratch of wave_kth_largest
   int32_t* ci;      // [WLIST] list index in the row's candidate list
   int32_t* cj;      // [WLIST] item id
   int32_t* cr;      // [WLIST] row
@@ -60,8 +59,8 @@ constexpr size_t WAVE_UNION = (size_t)16 * NBINS * 2 > (size_t)16 * SEL_CAP * 8 
 // earlier-round thresholds cached per row: rounds - 1 of them (at least one slot)
 __host__ __device__ constexpr int nprev_of(int rounds) { return rounds > 1 ? rounds - 1 : 1; }
 __host__ __device__ constexpr size_t wave_lds_bytes(int rounds) {
-  return 16 * (size_t)nprev_of(rounds) * sizeof(PrevRow) + WLIST * 8 + WAVE_UNION + NBINS * 4 + 64 * 4 +
-         WLIST * (4 + 4 + 4) + 16 * 8 * 4 + 16 * 8 * 4;
+  return 16 * (size_t)nprev_of(rounds) * sizeof(PrevRow) + WLIST * 8 + WAVE_UNION + WLIST * (4 + 4 + 4) +
+         16 * 8 * 4 + 16 * 8 * 4;
 }
 
 __device__ inline WaveLds carve(char* base, int rounds) {
@@ -75,10 +74,6 @@ __device__ inline WaveLds carve(char* base, int rounds) {
   L.vals = reinterpret_cast<float*>(p);
   L.ids = reinterpret_cast<int32_t*>(p + 16 * SEL_CAP * 4);
   p += WAVE_UNION;
-  L.khist = reinterpret_cast<uint32_t*>(p);
-  p += NBINS * 4;
-  L.cv = reinterpret_cast<float*>(p);
-  p += 64 * 4;
   L.ci = reinterpret_cast<int32_t*>(p);
   p += WLIST * 4;
   L.cj = reinterpret_cast<int32_t*>(p);
@@ -91,8 +86,8 @@ __device__ inline WaveLds carve(char* base, int rounds) {
   return L;
 }
 
-enum { RF_BETA = 0, RF_MX = 1, RF_SEXP = 2, RF_THI = 3, RF_NBUF = 4, RF_ALO = 5, RF_AHI = 6 };
-enum { RI_I = 0, RI_POS = 1, RI_NSURE = 2, RI_NNEW = 3, RI_NABOVE = 4, RI_AOFF = 5, RI_NA = 6, RI_MODE = 7 };
+enum { RF_BETA = 0, RF_MX = 1, RF_SEXP = 2, RF_THI = 3, RF_NBUF = 4, RF_ALO = 5 };
+enum { RI_I = 0, RI_KK = 1, RI_NSURE = 2, RI_NNEW = 3, RI_NABOVE = 4, RI_AOFF = 5, RI_NA = 6, RI_MODE = 7 };
 
 // One ring slot: the tile's rows, then 64 item ids, then for each earlier round
 // 64 chunk indices of those items in that round.
@@ -103,7 +98,9 @@ __host__ __device__ constexpr size_t sel_common_lds(size_t row_bytes, int rounds
   return 3 * sel_slot_bytes(row_bytes, rounds) + 16;
 }
 
-template <class E, int D, int NW>
+// NEGS: the kept ids are written out (p.negs set); a template flag keeps that
+// code out of the streaming loop when they are not.
+template <class E, int D, int NW, bool NEGS>
 __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_select(SelectArgs p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   using G = TileGeom<E, D>;
@@ -159,46 +156,45 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_sel
     }
   }
 
+  // Layout: logit blocks are computed transposed (items x positions), so lane l
+  // works for row r = l % 16 (its position) on items 4*(l/16) + v of every
+  // 16-item block; a row's four lanes are r, r+16, r+32, r+48.  Row state is
+  // one scalar per lane, kept equal in the row's four lanes.
+  const int r = l & 15;
+  const bool rv = pA < x1;
+  const uint64_t rowbits = 0x0001000100010001ull << r;   // the row's lanes
+  const uint64_t row_lt = rowbits & lanemask_lt();      // the row's lanes below this one
   const float ymax = p.ynorm_max[0];
   const bool selall = p.selall != 0;
-  // per-lane copies of the state of output rows r = 4g + v
-  int pos_v[4], i_v[4], kk_v[4];
-  bool rv[4];
-  // histogram coordinates: x = clamp((a - lo0) * sc0, 0, 256^-) maps the row's logits to
+  const int pos = rv ? p.pos[iA] : -1;
+  const float xn = rv ? p.xnorm[iA] : 0.0f;
+  const float beta = p.beta_coef * xn * ymax;
+  // histogram coordinates: x = clamp(a * sc0 + off0, 0, 256^-) maps the row's logits to
   // [0, 256); a pass at refinement level L counts y = (x - xa) * mul (mul = 256^L) when
   // 0 <= y < 256.  Both steps are exact in float for the values that matter, so every
   // level bins exactly the values whose x lies in the interval chosen one level up.
-  float beta_v[4], lo0_v[4], sc0_v[4], xa_v[4], mul_v[4], tlo_v[4], thi_v[4], mx_v[4];
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int64_t pr = wrow0 + 4 * g + v;
-    rv[v] = pr < x1;
-    i_v[v] = rv[v] ? p.perm_x[pr] : 0;
-    pos_v[v] = rv[v] ? p.pos[i_v[v]] : -1;
-    const float xn = rv[v] ? p.xnorm[i_v[v]] : 0.0f;
-    beta_v[v] = p.beta_coef * xn * ymax;
-    // every float32 logit of the row lies in [-bnd, bnd]
-    const float bnd = f_up((double)xn * (double)ymax * (1.0 + 1e-5) + 2.0 * (double)beta_v[v]) + 1e-30f;
-    lo0_v[v] = -bnd;
-    sc0_v[v] = (float)NBINS / (2.0f * bnd);
-    xa_v[v] = rv[v] ? 0.0f : __builtin_huge_valf();   // rows past the chunk count nothing
-    mul_v[v] = 1.0f;
-    kk_v[v] = rv[v] ? k : 0;
-    tlo_v[v] = thi_v[v] = selall ? NEG_INF : __builtin_huge_valf();
-    mx_v[v] = NEG_INF;   // row maximum (the exp shift), from the histogram pass
-    if ((l & 15) == 0) {
-      const int r = 4 * g + v;
-      // output row: the position id, or the sorted slot when outputs are per slot
-      L.ri[r * 8 + RI_I] = rv[v] ? (p.slot_out ? (int)pr : i_v[v]) : -1;
-      L.ri[r * 8 + RI_POS] = pos_v[v];
-      L.rf[r * 8 + RF_BETA] = beta_v[v];
-    }
+  // Every float32 logit of the row lies in [-bnd, bnd].
+  const float bnd = f_up((double)xn * (double)ymax * (1.0 + 1e-5) + 2.0 * (double)beta) + 1e-30f;
+  const float lo0 = -bnd, sc0 = (float)NBINS / (2.0f * bnd);
+  // bin coordinate x = med3(a * sc0 + off0, 0, 256^-), the same expression in every pass
+  const float off0 = -lo0 * sc0;
+  char* hist_row = reinterpret_cast<char*>(L.hist + r * (NBINS / 2));
+  float xa = rv ? 0.0f : __builtin_huge_valf();   // rows past the chunk count nothing
+  float mul = 1.0f;
+  int kk = rv ? k : 0;
+  float tlo = (selall && rv) ? NEG_INF : __builtin_huge_valf(), thi = tlo;   // rows past the chunk keep +inf
+  float mx = NEG_INF;   // row maximum (the exp shift), from the histogram pass
+  if (l < 16) {
+    // output row: the position id, or the sorted slot when outputs are per slot
+    L.ri[r * 8 + RI_I] = rv ? (p.slot_out ? (int)pA : iA) : -1;
+    L.rf[r * 8 + RF_BETA] = beta;
   }
+  const int64_t orow = p.slot_out ? pA : (int64_t)rho * s + iA;   // negs row (valid rows only)
 
   // mode 0: histogram pass; 1: collect pass; 2: nothing to do (k = 0)
   int mode = k == 0 ? 2 : (selall ? 1 : 0);
-  float sexp_v[4] = {0.f, 0.f, 0.f, 0.f};
-  int nnew_v[4] = {0, 0, 0, 0}, nsure_v[4] = {0, 0, 0, 0}, bcnt_v[4] = {0, 0, 0, 0};
+  float sexp = 0.0f;
+  int nnew = 0, nsure = 0, bcnt = 0;
 
   // copies of one tile: G::ROW_DMA row copies, then ids, then one chunk map per earlier round
   const int ncopies = G::ROW_DMA + 1 + rho;
@@ -209,91 +205,122 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_sel
     if (mode == 0)
       for (int b = l; b < 16 * NBINS / 2; b += WAVE) L.hist[b] = 0u;
     __syncthreads();
-    issue_window_tile<E, D>(ring, slot_bytes, win, 0, Ys, p.perm_y, p.cyp, C, rho, w, NW);
-    if (ntiles > 1) issue_window_tile<E, D>(ring, slot_bytes, win, 1, Ys, p.perm_y, p.cyp, C, rho, w, NW);
+    issue_window_tile<E, D, NW>(ring, slot_bytes, win, 0, Ys, p.perm_y, p.cyp, C, rho, w);
+    if (ntiles > 1) issue_window_tile<E, D, NW>(ring, slot_bytes, win, 1, Ys, p.perm_y, p.cyp, C, rho, w);
 
     for (int t = 0; t < ntiles; ++t) {
       wait_vmcnt(t + 1 < ntiles ? my_copies : 0);
       raw_barrier();
-      if (t + 2 < ntiles) issue_window_tile<E, D>(ring, slot_bytes, win, t + 2, Ys, p.perm_y, p.cyp, C, rho, w, NW);
+      if (t + 2 < ntiles) issue_window_tile<E, D, NW>(ring, slot_bytes, win, t + 2, Ys, p.perm_y, p.cyp, C, rho, w);
       const int64_t q0 = range_tile_start(win, t, TI), q1 = range_tile_end(win, t);
       const char* slot = ring + (size_t)(t % 3) * slot_bytes;
       const int32_t* tid_ = reinterpret_cast<const int32_t*>(slot + G::ROW_BYTES);
       const int32_t* tcy = tid_ + 64;
+      const int nlim = (int)(q1 - q0);   // valid items of this tile
+      f32x4 acc[NCB];
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
-        const int n = cb * 16 + (l & 15);
         Frag<E, D> bf;
-        TileFrag<E, D>::load(bf, slot, n);
-        const f32x4 acc = mma_block(afr, bf, f32x4{0.f, 0.f, 0.f, 0.f});
-        const bool nvalid = q0 + n < q1;
-        const int j = tid_[n];
-        if (mode == 0) {
+        TileFrag<E, D>::load(bf, slot, cb * 16 + r);
+        acc[cb] = mma_block(bf, afr, f32x4{0.f, 0.f, 0.f, 0.f});   // [item 4g+v][row r]
+      }
+      const bool full = nlim >= TI;   // no item beyond the range end in this tile
+      if (mode == 0) {
+        if (pass == 0 && full) {
+          // level 0 over a full tile: every value is binned; only the positive adds 0
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const float a = acc[v];
-            if (nvalid && j != pos_v[v]) {
-              mx_v[v] = fmaxf(mx_v[v], a);
-              const float x = fminf(fmaxf((a - lo0_v[v]) * sc0_v[v], 0.0f), X_TOP);
-              const float y = (x - xa_v[v]) * mul_v[v];
-              if (y >= 0.0f && y < (float)NBINS) {
-                const int b = (int)y;
-                atomicAdd(&L.hist[(4 * g + v) * (NBINS / 2) + (b >> 1)], 1u << (16 * (b & 1)));
-              }
+          for (int cb = 0; cb < NCB; ++cb) {
+            const u32x4 jj = *reinterpret_cast<const u32x4*>(tid_ + cb * 16 + 4 * g);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const int b = (int)__builtin_amdgcn_fmed3f(fmaf(acc[cb][v], sc0, off0), 0.0f, X_TOP);
+              lds_add_u32(hist_row + ((b >> 1) << 2), (int)jj[v] != pos ? 1u << ((b & 1) << 4) : 0u);
             }
           }
         } else {
+          // refinement levels and the last tile of a range: branch-free, every lane adds
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) {
+            const u32x4 jj = *reinterpret_cast<const u32x4*>(tid_ + cb * 16 + 4 * g);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const bool valid = cb * 16 + 4 * g + v < nlim && (int)jj[v] != pos;
+              const float x = __builtin_amdgcn_fmed3f(fmaf(acc[cb][v], sc0, off0), 0.0f, X_TOP);
+              const float y = (x - xa) * mul;
+              const bool hit = valid && y >= 0.0f && y < (float)NBINS;
+              const int b = hit ? (int)y : 0;
+              lds_add_u32(hist_row + ((b >> 1) << 2), hit ? 1u << ((b & 1) << 4) : 0u);
+            }
+          }
+        }
+      } else {
+        // collect: sure members (above thi) are counted and summed; the band [tlo, thi]
+        // goes to the row's list.  Rows past the chunk have tlo = thi = +inf.  The
+        // earlier-round test exists only in rounds after the first (two loop bodies).
+        auto collect = [&](auto ded) {
+          constexpr bool DEDUP = decltype(ded)::value;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          u32x4 jj = *reinterpret_cast<const u32x4*>(tid_ + cb * 16 + 4 * g);
+          bool inb[4];
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const float a = acc[v];
-            const int r = 4 * g + v;
-            const bool cand = rv[v] && nvalid && j != pos_v[v];
-            const bool sure = cand && a > thi_v[v];
-            if (sure) {
-              bool dup = false;
-              const E* xrow = Xs + (wrow0 + r) * D;
+            const int n = cb * 16 + 4 * g + v;
+            const int j = (int)jj[v];
+            const float a = acc[cb][v];
+            const bool cand = (full || n < nlim) && j != pos;
+            const bool sure = cand && a > thi;
+            inb[v] = cand && a >= tlo && a <= thi;
+            bool dup = false;
+            if (DEDUP && (sure || inb[v])) {
               for (int r2 = 0; r2 < rho && !dup; ++r2) {
                 const PrevRow pr = L.prev[r * NP + r2];
                 if (!in_window(pr.cx, tcy[64 * r2 + n], n_c)) continue;
-                dup = beats<E, D>(a, pr.lo, pr.hi, pr.te, pr.tid, xrow, Y, j, nexact);
-              }
-              if (!dup) {
-                if (selall && a > mx_v[v]) {   // no histogram pass ran: keep the shift at the maximum
-                  sexp_v[v] = mx_v[v] == NEG_INF ? 0.0f : sexp_v[v] * __expf(mx_v[v] - a);
-                  mx_v[v] = a;
-                }
-                sexp_v[v] += __expf(a - mx_v[v]);
-                nnew_v[v] += 1;
+                dup = beats<E, D>(a, pr.lo, pr.hi, pr.te, pr.tid, Xs + pA * D, Y, j, nexact);
               }
             }
-            if (p.negs) {
-              const uint64_t m = ballot(sure);
-              const uint32_t gm = (uint32_t)(m >> (16 * g)) & 0xFFFFu;
+            const bool nw = sure && !dup;
+            if (selall && nw && a > mx) {   // no histogram pass ran: keep the shift at the maximum
+              sexp = mx == NEG_INF ? 0.0f : sexp * __expf(mx - a);
+              mx = a;
+            }
+            sexp += nw ? __expf(a - mx) : 0.0f;
+            nnew += nw ? 1 : 0;
+            if (NEGS) {
+              const uint64_t ms = ballot(sure);
               if (sure) {
-                const int slotn = nsure_v[v] + __popc(gm & ((1u << (l & 15)) - 1u));
-                const int64_t orow = p.slot_out ? (wrow0 + r) : (int64_t)rho * s + i_v[v];
+                const int slotn = nsure + popc(ms & row_lt);
                 if (slotn < k) {
                   p.negs[orow * k + slotn] = j;
                   if (p.negl) p.negl[orow * k + slotn] = a;
                 }
               }
-              nsure_v[v] += __popc(gm);
+              nsure += popc(ms & rowbits);
             } else {
-              nsure_v[v] += sure ? 1 : 0;
+              nsure += sure ? 1 : 0;
             }
-            const bool inb = cand && a >= tlo_v[v] && a <= thi_v[v];
-            const uint64_t m2 = ballot(inb);
-            const uint32_t gm2 = (uint32_t)(m2 >> (16 * g)) & 0xFFFFu;
-            if (inb) {
-              const int slotn = bcnt_v[v] + __popc(gm2 & ((1u << (l & 15)) - 1u));
-              if (slotn < SEL_CAP) {
-                L.vals[r * SEL_CAP + slotn] = a;
-                L.ids[r * SEL_CAP + slotn] = j;
+            if (dup && inb[v]) jj[v] |= 0x80000000u;
+          }
+          if (ballot(inb[0] || inb[1] || inb[2] || inb[3])) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const uint64_t m2 = ballot(inb[v]);
+              if (inb[v]) {
+                const int slotn = bcnt + popc(m2 & row_lt);
+                if (slotn < SEL_CAP) {
+                  lds_store_u32(&L.vals[r * SEL_CAP + slotn], __float_as_uint(acc[cb][v]));
+                  lds_store_u32(&L.ids[r * SEL_CAP + slotn], jj[v]);
+                }
               }
+              bcnt += popc(m2 & rowbits);
             }
-            bcnt_v[v] += __popc(gm2);
           }
         }
+        };
+        if (rho > 0)
+          collect(std::true_type{});
+        else
+          collect(std::false_type{});
       }
     }
 
@@ -301,29 +328,16 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_sel
 
     // ---- after a histogram pass: locate the bin of the kk-th largest of each row
     wave_sync();
-#pragma unroll
-    for (int v = 0; v < 4; ++v)
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) mx_v[v] = fmaxf(mx_v[v], __shfl_xor(mx_v[v], o));
     bool more = false;
-    for (int r = 0; r < 16; ++r) {
-      const int gl = 16 * (r >> 2), vv = r & 3;
-      int kkr = 0;
-      float lo0 = 0.f, sc0 = 0.f, xa = 0.f, mul = 0.f, beta = 0.f;
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-        if (v == vv) {
-          kkr = __shfl(kk_v[v], gl);
-          lo0 = __shfl(lo0_v[v], gl);
-          sc0 = __shfl(sc0_v[v], gl);
-          xa = __shfl(xa_v[v], gl);
-          mul = __shfl(mul_v[v], gl);
-          beta = __shfl(beta_v[v], gl);
-        }
+    for (int rr = 0; rr < 16; ++rr) {
+      const int kkr = __shfl(kk, rr);
       if (kkr <= 0) continue;   // row settled in an earlier pass
+      const float xar = __shfl(xa, rr), mulr = __shfl(mul, rr), lo0r = __shfl(lo0, rr), sc0r = __shfl(sc0, rr);
+      const float off0r = __shfl(off0, rr);
+      const float betar = __shfl(beta, rr);
       uint32_t h[4];
       {
-        const uint32_t w0 = L.hist[r * (NBINS / 2) + 2 * l], w1 = L.hist[r * (NBINS / 2) + 2 * l + 1];
+        const uint32_t w0 = L.hist[rr * (NBINS / 2) + 2 * l], w1 = L.hist[rr * (NBINS / 2) + 2 * l + 1];
         h[0] = w0 & 0xFFFFu;
         h[1] = w0 >> 16;
         h[2] = w1 & 0xFFFFu;
@@ -340,19 +354,30 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_sel
       int myb = -1;
       uint32_t my_above = 0, my_cnt = 0;
       {
-        uint32_t acc = suf - own;
+        uint32_t a2 = suf - own;
 #pragma unroll
         for (int q = 3; q >= 0; --q) {
-          if (myb < 0 && acc + h[q] >= (uint32_t)kkr) {
+          if (myb < 0 && a2 + h[q] >= (uint32_t)kkr) {
             myb = 4 * l + q;
-            my_above = acc;
+            my_above = a2;
             my_cnt = h[q];
           }
-          acc += h[q];
+          a2 += h[q];
         }
       }
       const uint64_t hit = ballot(myb >= 0);
-      float ntlo, nthi, nxa = xa, nmul = mul;
+      float mxr = NEG_INF;   // exp shift: the top edge of the highest non-empty level-0 bin
+      if (pass == 0) {
+        const uint64_t nz = ballot(own > 0);
+        if (nz) {
+          const int tl = 63 - __builtin_clzll(nz);
+          const int hq = h[3] ? 3 : (h[2] ? 2 : (h[1] ? 1 : 0));
+          const int btop = 4 * tl + __shfl(hq, tl);
+          const double top = ((double)(btop + 1) - (double)off0r) / (double)sc0r;
+          mxr = f_up(top + (fabs(top) + fabs((double)lo0r)) * 1e-6 + 1e-30);
+        }
+      }
+      float ntlo, nthi, nxa = xar, nmul = mulr;
       int nkk = 0;
       bool refine = false;
       if ((pass == 0 && (int)total <= kkr) || !hit) {
@@ -363,29 +388,26 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_sel
         const int bstar = __shfl(myb, src);
         const int above = (int)__shfl(my_above, src);
         const int cnt = (int)__shfl(my_cnt, src);
-        nxa = xa + (float)bstar / mul;   // exact: a multiple of 256^-L below 256
-        nmul = mul * (float)NBINS;
+        nxa = xar + (float)bstar / mulr;   // exact: a multiple of 256^-L below 256
+        nmul = mulr * (float)NBINS;
         // the bin is x in [nxa, nxa + 1/mul): its logit interval, padded for the rounding of x
-        const double vlo = (double)lo0 + (double)nxa / (double)sc0;
-        const double vhi = (double)lo0 + ((double)nxa + 1.0 / (double)mul) / (double)sc0;
-        const double pad = (fabs(vlo) + fabs(vhi) + fabs((double)lo0)) * 1e-6 + 1e-30;
-        ntlo = f_down(vlo - 2.0 * (double)beta - pad);
-        nthi = f_up(vhi + 2.0 * (double)beta + pad);
-        if (cnt > SEL_CAP - SEL_SLACK && pass < MAX_REFINE && vhi - vlo > 4.0 * (double)beta) {
+        const double vlo = ((double)nxa - (double)off0r) / (double)sc0r;
+        const double vhi = ((double)nxa + 1.0 / (double)mulr - (double)off0r) / (double)sc0r;
+        const double pad = (fabs(vlo) + fabs(vhi) + fabs((double)lo0r)) * 1e-6 + 1e-30;
+        ntlo = f_down(vlo - 2.0 * (double)betar - pad);
+        nthi = f_up(vhi + 2.0 * (double)betar + pad);
+        if (cnt > SEL_CAP - SEL_SLACK && pass < MAX_REFINE && vhi - vlo > 4.0 * (double)betar) {
           refine = true;   // crowded bin: split it by another histogram pass
           nkk = kkr - above;
         }
       }
-      if (g == (r >> 2)) {
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          if (v == vv) {
-            tlo_v[v] = ntlo;
-            thi_v[v] = nthi;
-            kk_v[v] = refine ? nkk : 0;
-            xa_v[v] = refine ? nxa : __builtin_huge_valf();   // settled rows count nothing more
-            mul_v[v] = refine ? nmul : 1.0f;
-          }
+      if (r == rr) {
+        if (pass == 0) mx = mxr;
+        tlo = ntlo;
+        thi = nthi;
+        kk = refine ? nkk : 0;
+        xa = refine ? nxa : __builtin_huge_valf();   // settled rows count nothing more
+        mul = refine ? nmul : 1.0f;
       }
       more |= refine;
     }
@@ -396,42 +418,89 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_sel
     mode = *wg_flag ? 0 : 1;
   }
 
-  // ---- publish the per-row sums of the sure members (combine the 16 lanes of each row)
+  // ---- publish the per-row sums of the sure members (combine the row's four lanes)
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      const float m2 = __shfl_xor(mx_v[v], o);
-      const float s2 = __shfl_xor(sexp_v[v], o);
-      if (selall) {   // lanes saw different maxima: rescale before adding
-        const float mn = fmaxf(mx_v[v], m2);
-        const float a1 = mx_v[v] == NEG_INF ? 0.0f : sexp_v[v] * __expf(mx_v[v] - mn);
-        const float a2 = m2 == NEG_INF ? 0.0f : s2 * __expf(m2 - mn);
-        sexp_v[v] = a1 + a2;
-        mx_v[v] = mn;
-      } else {
-        sexp_v[v] += s2;
-      }
-      nnew_v[v] += __shfl_xor(nnew_v[v], o);
-      if (!p.negs) nsure_v[v] += __shfl_xor(nsure_v[v], o);
+  for (int o = 16; o < 64; o <<= 1) {
+    const float m2 = __shfl_xor(mx, o);
+    const float s2 = __shfl_xor(sexp, o);
+    if (selall) {   // lanes saw different maxima: rescale before adding
+      const float mn = fmaxf(mx, m2);
+      const float a1 = mx == NEG_INF ? 0.0f : sexp * __expf(mx - mn);
+      const float a2 = m2 == NEG_INF ? 0.0f : s2 * __expf(m2 - mn);
+      sexp = a1 + a2;
+      mx = mn;
+    } else {
+      sexp += s2;
     }
-    if ((l & 15) == 0) {
-      const int r = 4 * g + v;
-      L.rf[r * 8 + RF_MX] = mx_v[v];
-      L.rf[r * 8 + RF_SEXP] = sexp_v[v];
-      L.rf[r * 8 + RF_THI] = thi_v[v];
-      L.rf[r * 8 + RF_NBUF] = __int_as_float(bcnt_v[v]);
-      L.ri[r * 8 + RI_NSURE] = nsure_v[v];
-      L.ri[r * 8 + RI_NNEW] = nnew_v[v];
-    }
+    nnew += __shfl_xor(nnew, o);
+    if (!NEGS) nsure += __shfl_xor(nsure, o);
+  }
+  if (l < 16) {
+    L.rf[r * 8 + RF_MX] = mx;
+    L.rf[r * 8 + RF_SEXP] = sexp;
+    L.rf[r * 8 + RF_THI] = thi;
+    L.rf[r * 8 + RF_NBUF] = __int_as_float(bcnt);
+    L.ri[r * 8 + RI_NSURE] = nsure;
+    L.ri[r * 8 + RI_NNEW] = nnew;
   }
   wave_sync();
 
   // ---------------------------------------------------------------- epilogue
-  // Rows go through three steps in groups: (A) per row, the float32 k-th value a_k
-  // of its list and the near-tie entries within 2*beta of a_k, appended to the
-  // wave's list; (B) float64 logits of the whole list, one entry per lane;
-  // (C) per row, rank the near-ties, set the threshold, sum the kept entries.
+  // Rows go through three steps in groups.  (A) Per row: sort its list (at most
+  // 64 entries, one per lane) by (float32 value desc, id asc) with a bitonic
+  // network; the float32 k-th value a_k sits at rank kk - 1 (kk = k minus the
+  // sure members) and the near-ties, the entries within 2*beta of a_k, form one
+  // run of the sorted list; they join the wave's float64 batch.  (B) Float64
+  // logits of the batch, one entry per lane.  (C) Per row: rank the near-ties by
+  // (float64 logit desc, id asc); the k-th kept element is the row's threshold;
+  // the kept list entries are the sorted prefix before the near-ties plus the
+  // near-ties ranked within the count still missing.  A list id with bit 31 set
+  // marks a pair kept in an earlier round (counted, not summed again).
+  // Sort every row's list first, four rows at a time (independent shuffle chains
+  // in flight together), and write the sorted lists back.
+  for (int r0 = 0; r0 < 16; r0 += 4) {
+    float v[4];
+    int id[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = r0 + q;
+      const bool act = L.ri[r * 8 + RI_I] >= 0 && k > 0 && L.rf[r * 8 + RF_THI] != NEG_INF;
+      const int n = act ? min(__float_as_int(L.rf[r * 8 + RF_NBUF]), SEL_CAP) : 0;
+      v[q] = l < n ? L.vals[r * SEL_CAP + l] : NEG_INF;
+      id[q] = l < n ? L.ids[r * SEL_CAP + l] : 0x7FFFFFFF;
+    }
+    // bitonic network, order "precedes": larger value first, then smaller id
+#pragma unroll
+    for (int size = 2; size <= WAVE; size <<= 1) {
+#pragma unroll
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        const bool want_first = ((l & stride) == 0) == ((l & size) == 0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float pv = __shfl_xor(v[q], stride);
+          const int pid = __shfl_xor(id[q], stride);
+          const int mi = id[q] & 0x7FFFFFFF, pi = pid & 0x7FFFFFFF;
+          const bool p_first = pv > v[q] || (pv == v[q] && pi < mi);
+          const bool m_first = v[q] > pv || (v[q] == pv && mi < pi);
+          if (want_first ? p_first : m_first) {
+            v[q] = pv;
+            id[q] = pid;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = r0 + q;
+      const int n = min(__float_as_int(L.rf[r * 8 + RF_NBUF]), SEL_CAP);
+      if (l < n) {
+        L.vals[r * SEL_CAP + l] = v[q];
+        L.ids[r * SEL_CAP + l] = id[q];
+      }
+    }
+  }
+  wave_sync();
+
   int r_next = 0;
   while (r_next < 16) {
     int tot = 0;
@@ -445,55 +514,41 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_sel
         const int nsure = L.ri[r * 8 + RI_NSURE];
         const float beta = L.rf[r * 8 + RF_BETA];
         const int n = min(nb_all, SEL_CAP);
-        const int kk = k - nsure;
+        int kk = k - nsure;
         if (nb_all > SEL_CAP || kk < 1 || kk > n) {
           if (l == 0) {
             atomicAdd(p.counters + CNT_OVERFLOW, 1u);
             atomicOr(p.counters + CNT_ERROR, (uint32_t)ERRBIT_OVERFLOW);
           }
+          kk = max(1, min(kk, max(n, 1)));
         }
-        const float* vals = L.vals + r * SEL_CAP;
-        const float ak = n > 0 ? wave_kth_largest(vals, n, max(1, min(kk, n)), L.khist, L.cv) : 0.0f;
+        const float v = l < n ? L.vals[r * SEL_CAP + l] : NEG_INF;   // sorted above
+        const int id = l < n ? L.ids[r * SEL_CAP + l] : 0x7FFFFFFF;
+        const float ak = __shfl(v, kk - 1);
         const float lo = f_down((double)ak - 2.0 * (double)beta);
         const float hi = f_up((double)ak + 2.0 * (double)beta);
-        int nabove = 0, na = 0;
-        for (int base = 0; base < n; base += WAVE) {
-          const int t = base + l;
-          const float v = t < n ? vals[t] : NEG_INF;
-          nabove += (t < n && v > hi) ? 1 : 0;
-          na += popc(ballot(t < n && v >= lo && v <= hi));
-        }
-        nabove = wave_sum(nabove);
+        const int nabove = popc(ballot(l < n && v > hi));
+        int na = popc(ballot(l < n && v >= lo && v <= hi));   // lanes nabove .. nabove + na - 1
         if (tot + na > WLIST && r > r_next) break;   // next group
-        if (na > WLIST) {   // cannot rank more near-ties than the list holds
+        if (na > WLIST) {   // cannot rank more near-ties than the batch holds
           if (l == 0) {
             atomicAdd(p.counters + CNT_OVERFLOW, 1u);
             atomicOr(p.counters + CNT_ERROR, (uint32_t)ERRBIT_OVERFLOW);
           }
           na = WLIST;
         }
-        int w0 = 0;
-        for (int base = 0; base < n; base += WAVE) {
-          const int t = base + l;
-          const float v = t < n ? vals[t] : NEG_INF;
-          const bool inA = t < n && v >= lo && v <= hi;
-          const uint64_t m = ballot(inA);
-          if (inA) {
-            const int dst = w0 + popc(m & lanemask_lt());
-            if (dst < na) {
-              L.ci[tot + dst] = t;
-              L.cj[tot + dst] = L.ids[r * SEL_CAP + t];
-              L.cr[tot + dst] = r;
-            }
-          }
-          w0 += popc(m);
+        const int e = l - nabove;
+        if (e >= 0 && e < na) {
+          L.ci[tot + e] = l;
+          L.cj[tot + e] = id & 0x7FFFFFFF;
+          L.cr[tot + e] = r;
         }
         if (l == 0) {
           L.rf[r * 8 + RF_ALO] = lo;
-          L.rf[r * 8 + RF_AHI] = hi;
           L.ri[r * 8 + RI_NABOVE] = nabove;
           L.ri[r * 8 + RI_AOFF] = tot;
           L.ri[r * 8 + RI_NA] = na;
+          L.ri[r * 8 + RI_KK] = kk;
         }
         tot += na;
       }
@@ -517,7 +572,6 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_sel
       float se = L.rf[r * 8 + RF_SEXP];
       int nnew = L.ri[r * 8 + RI_NNEW];
       const int nsure = L.ri[r * 8 + RI_NSURE];
-      const E* xrow = Xs + (wrow0 + r) * D;
       const int64_t o = p.slot_out ? (int64_t)i : (int64_t)rho * s + i;
       double te;
       int tid;
@@ -533,82 +587,58 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_sel
         tlo = thi = NEG_INF;
         listed = nsure;
       } else {
-        float* vals = L.vals + r * SEL_CAP;
-        const int32_t* ids = L.ids + r * SEL_CAP;
         const int n = min(__float_as_int(L.rf[r * 8 + RF_NBUF]), SEL_CAP);
-        const float lo = L.rf[r * 8 + RF_ALO];
         const int nabove = L.ri[r * 8 + RI_NABOVE];
         const int aoff = L.ri[r * 8 + RI_AOFF];
         const int na = L.ri[r * 8 + RI_NA];
-        const int need = k - nsure - nabove;   // near-ties that are kept (>= 1)
-        // rank the row's near-ties (order: float64 logit desc, id asc); na may exceed 64
+        const int need = L.ri[r * 8 + RI_KK] - nabove;   // near-ties that are kept (>= 1)
+        // rank of this lane's near-tie (lane nabove + e holds near-tie e)
+        const int e = l - nabove;
+        int rank = WAVE;
+        double me = 0.0;
+        int mj = 0;
+        if (e >= 0 && e < na) {
+          me = L.ce[aoff + e];
+          mj = L.cj[aoff + e];
+          rank = 0;
+          for (int u = 0; u < na; ++u) {
+            const double eu = L.ce[aoff + u];
+            const int ju = L.cj[aoff + u];
+            rank += (eu > me) || (eu == me && ju < mj);
+          }
+        }
+        const uint64_t tm = ballot(rank == need - 1);
         te = 0.0;
         tid = 0;
-        for (int a0 = 0; a0 < na; a0 += WAVE) {
-          const int ea = a0 + l;
-          int rank = 0;
-          double me = 0.0;
-          int mj = 0;
-          if (ea < na) {
-            me = L.ce[aoff + ea];
-            mj = L.cj[aoff + ea];
-            for (int u = 0; u < na; ++u) {
-              const double eu = L.ce[aoff + u];
-              const int ju = L.cj[aoff + u];
-              rank += (eu > me) || (eu == me && ju < mj);
-            }
-          }
-          const uint64_t tm = ballot(ea < na && rank == need - 1);
-          if (tm) {
-            const int tl = __builtin_ctzll(tm);
-            te = __shfl(me, tl);
-            tid = __shfl(mj, tl);
-          }
-          if (ea < na && rank >= need) vals[L.ci[aoff + ea]] = NEG_INF;
+        if (tm) {
+          const int tl = __builtin_ctzll(tm);
+          te = __shfl(me, tl);
+          tid = __shfl(mj, tl);
         }
-        wave_sync();
         if (l == 0 && na > 1) atomicAdd(p.counters + CNT_TOPK_EXACT, 1u);
         const double b2 = (double)beta * (1.0 + 1e-6);
         tlo = f_down(te - b2);
         thi = f_up(te + b2);
-        // kept list entries: >= lo once the near-ties that ranked out are dropped
-        float sl = 0.0f;
-        int cl = 0, nk = 0;
-        for (int base = 0; base < n; base += WAVE) {
-          const int t = base + l;
-          const float a = t < n ? vals[t] : NEG_INF;
-          const int j = t < n ? ids[t] : -1;
-          const bool kept = t < n && a >= lo;
+        // kept list entries: the prefix before the near-ties and the near-ties ranked in
+        const float a = l < n ? L.vals[r * SEL_CAP + l] : NEG_INF;
+        const int jraw = l < n ? L.ids[r * SEL_CAP + l] : 0;
+        const bool kept = l < n && (l < nabove || rank < need);
+        const bool fresh = kept && (jraw & 0x80000000) == 0;
+        se += wave_sumf(fresh ? __expf(a - mx) : 0.0f);
+        nnew += popc(ballot(fresh));
+        if (NEGS) {
+          const uint64_t km = ballot(kept);
           if (kept) {
-            bool dup = false;
-            for (int r2 = 0; r2 < rho && !dup; ++r2) {
-              const PrevRow pr = L.prev[r * NP + r2];
-              const int cy2 = chunk_of(p.inv_y[(int64_t)r2 * C + j], C, n_c);
-              if (!in_window(pr.cx, cy2, n_c)) continue;
-              dup = beats<E, D>(a, pr.lo, pr.hi, pr.te, pr.tid, xrow, Y, j, nexact);
-            }
-            if (!dup) {
-              sl += __expf(a - mx);
-              ++cl;
+            const int slotn = nsure + popc(km & lanemask_lt());
+            if (slotn < k) {
+              p.negs[o * k + slotn] = jraw & 0x7FFFFFFF;
+              if (p.negl) p.negl[o * k + slotn] = a;
             }
           }
-          if (p.negs) {
-            const uint64_t km = ballot(kept);
-            if (kept) {
-              const int slotn = nsure + nk + popc(km & lanemask_lt());
-              if (slotn < k) {
-                p.negs[o * k + slotn] = j;
-                if (p.negl) p.negl[o * k + slotn] = a;
-              }
-            }
-            nk += popc(km);
-          }
+          listed = nsure + popc(km);
         }
-        se += wave_sumf(sl);
-        nnew += wave_sum(cl);
-        listed = nsure + nk;
       }
-      if (p.negs)
+      if (NEGS)
         for (int t = listed + l; t < k; t += WAVE) p.negs[o * k + t] = -1;
       if (l == 0) {
         p.thr_e[o] = te;
@@ -619,8 +649,8 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_sel
         p.ssum[o] = se;
         p.nmem[o] = nnew;
       }
-      wave_sync();
     }
+    wave_sync();
     r_next = r_end;
   }
   flush_count(p.counters + CNT_LOGIT_EXACT, nexact);
@@ -635,7 +665,7 @@ size_t select_lds_bytes(bool is_bf16, int d, int waves, int rounds) {
 template <class E, int D, int NW>
 static hipError_t launch_sel(const SelectArgs& a, hipStream_t st) {
   const size_t lds = select_lds_bytes(sizeof(E) == 2, D, NW, a.rounds);
-  auto kern = k_select<E, D, NW>;
+  auto kern = a.negs ? k_select<E, D, NW, true> : k_select<E, D, NW, false>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;

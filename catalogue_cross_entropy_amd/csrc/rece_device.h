@@ -203,6 +203,14 @@ __device__ __forceinline__ bool in_window(int cx, int cy, int n_c) {
 // lo <= te - beta, hi >= te + beta, beta bounding |a - float64 logit|:
 // above hi -> kept, below lo -> not kept, in between -> float64 comparison in the
 // order (logit desc, id asc).  lo = hi = -inf: every candidate kept; +inf: none.
+// The float64 comparison of beats(): out of line, so the streaming loops that
+// call beats() carry only its float32 fast path.
+template <class E, int D>
+__device__ __attribute__((noinline)) bool beats_exact(double te, int tid, const E* xrow, const E* Y, int j) {
+  const double e = exact_dot<E, D, 2>(xrow, Y + (int64_t)j * D);
+  return e > te || (e == te && j <= tid);
+}
+
 // nexact counts the float64 recomputations (a per-lane tally, flushed by flush_count).
 template <class E, int D>
 __device__ __forceinline__ bool beats(float a, float lo, float hi, double te, int tid, const E* xrow,
@@ -210,10 +218,8 @@ __device__ __forceinline__ bool beats(float a, float lo, float hi, double te, in
   if (a > hi) return true;
   if (a < lo) return false;
   if (j == tid) return true;
-  // rare path inside streaming loops: few pieces in flight, to keep registers free
-  const double e = exact_dot<E, D, 2>(xrow, Y + (int64_t)j * D);
   ++nexact;
-  return e > te || (e == te && j <= tid);
+  return beats_exact<E, D>(te, tid, xrow, Y, j);
 }
 
 // Add a per-lane tally to a device counter: one atomic per wave.

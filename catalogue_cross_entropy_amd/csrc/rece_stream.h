@@ -51,6 +51,35 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 #undef RECE_VMCNT_CASE
 }
 
+// LDS stores, atomics and transpose reads issued inside the streaming loops.
+// The compiler cannot tell that their addresses lie outside the destinations of
+// the asynchronous tile copies in flight, and would wait for every copy before
+// each of them (draining the prefetch).  As inline assembly they carry no such
+// wait: the stores and atomics have no outputs (later LDS reads of the same
+// wave are ordered behind them by the in-order LDS queue), and the transpose
+// reads wait for their own results inside the same asm block.  The tile data
+// they read has arrived: the loops wait for its copies before the barrier.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ void lds_add_u32(void* p, uint32_t v) {
+  asm volatile("ds_add_u32 %0, %1" ::"v"(lds_addr(p)), "v"(v) : "memory");
+}
+__device__ __forceinline__ void lds_store_u32(void* p, uint32_t v) {
+  asm volatile("ds_write_b32 %0, %1" ::"v"(lds_addr(p)), "v"(v) : "memory");
+}
+typedef short short4v __attribute__((ext_vector_type(4)));
+// Two ds_read_b64_tr_b16 (see tile_tr4 for the lane layout), complete on return.
+__device__ __forceinline__ void lds_tr16_pair(const void* a0, const void* a1, short4v& r0, short4v& r1) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %2\n\t"
+      "ds_read_b64_tr_b16 %1, %3\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1)
+      : "v"(lds_addr(a0)), "v"(lds_addr(a1))
+      : "memory");
+}
+
 // Every wave: finish its LDS reads, then meet the others (no memory fence).
 __device__ __forceinline__ void raw_barrier() {
   compiler_fence();
@@ -59,23 +88,38 @@ __device__ __forceinline__ void raw_barrier() {
   compiler_fence();
 }
 
+__host__ __device__ constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
+
 // Copy rows [r0, r0 + TI) of `src` (row-major, RB bytes per row) into a swizzled
 // LDS row block; rows at or beyond r_end repeat row r_end - 1 (callers mask them).
-// Copy u (0 <= u < ROW_DMA) is issued by wave (u % nwaves); returns this wave's count.
-template <class E, int D>
+// Copy u (0 <= u < ROW_DMA) is issued by wave (u % NW); returns this wave's count.
+// A full tile needs one address add per copy: the swizzle is a bit flip of the
+// byte offset inside the tile.
+template <class E, int D, int NW>
 __device__ __forceinline__ int dma_rows(char* lds_rows, const E* __restrict__ src, int64_t r0, int64_t r_end,
-                                        int wave, int nwaves) {
+                                        int wave) {
   using G = TileGeom<E, D>;
+  constexpr int LRB = ilog2(G::RB);
+  static_assert((1 << LRB) == G::RB, "row bytes must be a power of two");
   const int l = lane_id();
+  const bool full = r0 + G::TI <= r_end;
+  const char* base = reinterpret_cast<const char*>(src) + r0 * G::RB;
   int issued = 0;
-  for (int u = wave; u < G::ROW_DMA; u += nwaves) {
+#pragma unroll
+  for (int q = 0; q < (G::ROW_DMA + NW - 1) / NW; ++q) {
+    const int u = wave + q * NW;
+    if (u >= G::ROW_DMA) break;
     const int byte = u * 1024 + 16 * l;
-    const int n = byte / G::RB;
-    const int cp = (byte % G::RB) / 16;
-    const int c = cp ^ (n & G::SWM);
-    int64_t row = r0 + n;
-    if (row >= r_end) row = r_end - 1;
-    const char* g = reinterpret_cast<const char*>(src) + row * G::RB + c * 16;
+    const int n = byte >> LRB;
+    const int off = byte ^ ((n & G::SWM) << 4);   // chunk c of row n stored at c ^ (n & SWM)
+    const char* g;
+    if (full) {
+      g = base + off;
+    } else {
+      int64_t row = r0 + n;
+      if (row >= r_end) row = r_end - 1;
+      g = reinterpret_cast<const char*>(src) + row * G::RB + (off & (G::RB - 1));
+    }
     __builtin_amdgcn_global_load_lds(g, (lds_void*)(lds_rows + u * 1024), 16, 0, 0);
     ++issued;
   }
@@ -84,9 +128,10 @@ __device__ __forceinline__ int dma_rows(char* lds_rows, const E* __restrict__ sr
 
 // Copy 64 int32 values src[i0 .. i0 + 63] (clamped to i_end - 1) into LDS (one wave).
 __device__ __forceinline__ void dma_ints(int32_t* lds, const int32_t* __restrict__ src, int64_t i0, int64_t i_end) {
-  int64_t i = i0 + lane_id();
-  if (i >= i_end) i = i_end - 1;
-  __builtin_amdgcn_global_load_lds(src + i, (lds_void*)lds, 4, 0, 0);
+  const int l = lane_id();
+  const int32_t* g = src + i0 + l;
+  if (i0 + WAVE > i_end) g = src + (i0 + l < i_end ? i0 + l : i_end - 1);
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 4, 0, 0);
 }
 
 // Copy records [r0, r0 + NREC) of an array of REC_BYTES-byte records into LDS
@@ -99,16 +144,25 @@ struct RecCopy {
   static constexpr int COPIES = (NREC * CH + 63) / 64;
   static constexpr int LDS_BYTES = COPIES * 1024;
   static_assert(REC_BYTES % 16 == 0, "records must be whole 16-byte chunks");
+  template <int NW>
   static __device__ __forceinline__ int issue(char* lds, const void* src, int64_t r0, int64_t r_end, int first,
-                                              int wave, int nwaves) {
+                                              int wave) {
     const int l = lane_id();
+    const bool full = r0 + NREC <= r_end;
+    const char* base = static_cast<const char*>(src) + r0 * REC_BYTES;
     int issued = 0;
+#pragma unroll
     for (int u = 0; u < COPIES; ++u) {
-      if ((first + u) % nwaves != wave) continue;
+      if ((first + u) % NW != wave) continue;
       const int cidx = u * 64 + l;
-      int64_t rr = r0 + cidx / CH;
-      if (rr >= r_end) rr = r_end - 1;
-      const char* g = static_cast<const char*>(src) + rr * REC_BYTES + (cidx % CH) * 16;
+      const char* g;
+      if (full) {
+        g = base + cidx * 16;
+      } else {
+        int64_t rr = r0 + cidx / CH;
+        if (rr >= r_end) rr = r_end - 1;
+        g = static_cast<const char*>(src) + rr * REC_BYTES + (cidx % CH) * 16;
+      }
       __builtin_amdgcn_global_load_lds(g, (lds_void*)(lds + u * 1024), 16, 0, 0);
       ++issued;
     }
@@ -158,17 +212,16 @@ __device__ __forceinline__ int64_t range_tile_end(Ranges r, int t) {
 
 // Issue the copies of window tile t (rows from `rows_src`, then 64 ids from
 // `ids_src`, then `nmaps` chunk maps of C ints from `maps_src`) into ring slot t % 3.
-template <class E, int D>
+template <class E, int D, int NW>
 __device__ __forceinline__ void issue_window_tile(char* ring, size_t slot_bytes, Ranges r, int t,
                                                   const E* rows_src, const int32_t* ids_src,
-                                                  const int32_t* maps_src, int64_t map_len, int nmaps, int wave,
-                                                  int nwaves) {
+                                                  const int32_t* maps_src, int64_t map_len, int nmaps, int wave) {
   using G = TileGeom<E, D>;
   const int64_t q0 = range_tile_start(r, t, G::TI), q1 = range_tile_end(r, t);
   char* slot = ring + (size_t)(t % 3) * slot_bytes;
-  dma_rows<E, D>(slot, rows_src, q0, q1, wave, nwaves);
+  dma_rows<E, D, NW>(slot, rows_src, q0, q1, wave);
   const int ncopies = G::ROW_DMA + 1 + nmaps;
-  for (int u = G::ROW_DMA + ((wave - G::ROW_DMA % nwaves + nwaves) % nwaves); u < ncopies; u += nwaves) {
+  for (int u = G::ROW_DMA + ((wave - G::ROW_DMA % NW + NW) % NW); u < ncopies; u += NW) {
     const int m = u - G::ROW_DMA;
     int32_t* dst = reinterpret_cast<int32_t*>(slot + G::ROW_BYTES) + 64 * m;
     if (m == 0)
