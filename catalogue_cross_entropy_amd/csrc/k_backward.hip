@@ -164,6 +164,7 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_bwd
   const double teA = rc.te;
   const int tidA = rc.tid, gstA = rc.pad0, gmA = rc.pad1;
   const E* xrowA = Xs + (rvA ? pA : x0) * D;
+  const PrevRow p0 = rho > 0 ? p.prev[rvA ? pA : x0] : PrevRow{};   // round 0's set of this position
 
   f32x4 dacc[D / 16];
 #pragma unroll
@@ -207,7 +208,10 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_bwd
           mem = beats<E, D>(a, loA, hiA, teA, tidA, xrowA, Y, j, nexact);
         if ((SCE || rho > 0) && mem) {
           if (SCE && gmA > 0 && sce_seen_before(p, gstA, gmA, j)) mem = false;
-          for (int r2 = 0; r2 < rho && mem; ++r2) {
+          if (rho > 0 && mem && in_window(p0.cx, tcy[n], n_c) &&
+              beats<E, D>(a, p0.lo, p0.hi, p0.te, p0.tid, xrowA, Y, j, nexact))
+            mem = false;   // kept in round 0 (registers); rounds 1 .. rho-1 below
+          for (int r2 = 1; r2 < rho && mem; ++r2) {
             const PrevRow pr = prev[(l & 15) * MAX_ROUNDS + r2];
             if (!in_window(pr.cx, tcy[64 * r2 + n], n_c)) continue;
             if (beats<E, D>(a, pr.lo, pr.hi, pr.te, pr.tid, xrowA, Y, j, nexact)) mem = false;
@@ -317,6 +321,7 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_bwd
   const int64_t qA = wq0 + (l & 15);
   const bool rvA = qA < y1;
   const int jA = rvA ? p.perm_y[qA] : -1;
+  const int cy0 = (rho > 0 && rvA) ? p.cyp[qA] : 0;   // this item's chunk in round 0
   Frag<E, D> afr;
   afr.load_global(rvA ? Ys + qA * D : nullptr);
   if (l < 16)
@@ -364,8 +369,9 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_bwd
         if ((SCE || rho > 0) && mem) {
           if (SCE && recs[n].pad1 > 0 && sce_seen_before(p, recs[n].pad0, recs[n].pad1, jA)) mem = false;
           for (int r2 = 0; r2 < rho && mem; ++r2) {
+            const int cyr = r2 == 0 ? cy0 : cy2w[(l & 15) * MAX_ROUNDS + r2];
+            if (!in_window(prevs[(size_t)r2 * (LY::PC::LDS_BYTES / sizeof(PrevRow)) + n].cx, cyr, n_c)) continue;
             const PrevRow pr = prevs[(size_t)r2 * (LY::PC::LDS_BYTES / sizeof(PrevRow)) + n];
-            if (!in_window(pr.cx, cy2w[(l & 15) * MAX_ROUNDS + r2], n_c)) continue;
             if (beats<E, D>(a, pr.lo, pr.hi, pr.te, pr.tid, Xs + (q0 + n) * D, Y, jA, nexact)) mem = false;
           }
         }

@@ -259,6 +259,8 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_sel
         // earlier-round test exists only in rounds after the first (two loop bodies).
         auto collect = [&](auto ded) {
           constexpr bool DEDUP = decltype(ded)::value;
+          PrevRow p0{};
+          if (DEDUP) p0 = L.prev[r * NP];
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
           u32x4 jj = *reinterpret_cast<const u32x4*>(tid_ + cb * 16 + 4 * g);
@@ -273,7 +275,10 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_sel
             inb[v] = cand && a >= tlo && a <= thi;
             bool dup = false;
             if (DEDUP && (sure || inb[v])) {
-              for (int r2 = 0; r2 < rho && !dup; ++r2) {
+              // round 0's set in registers; rounds 1 .. rho-1 from LDS
+              if (in_window(p0.cx, tcy[n], n_c))
+                dup = beats<E, D>(a, p0.lo, p0.hi, p0.te, p0.tid, Xs + pA * D, Y, j, nexact);
+              for (int r2 = 1; r2 < rho && !dup; ++r2) {
                 const PrevRow pr = L.prev[r * NP + r2];
                 if (!in_window(pr.cx, tcy[64 * r2 + n], n_c)) continue;
                 dup = beats<E, D>(a, pr.lo, pr.hi, pr.te, pr.tid, Xs + pA * D, Y, j, nexact);
