@@ -10,6 +10,7 @@
 // row in float64 (rare).
 #include "rece_device.h"
 #include "rece_internal.h"
+#include "rece_stream.h"
 
 namespace rece {
 
@@ -59,167 +60,189 @@ hipError_t launch_prep_b(bool is_bf16, int d, const void* B, int rounds, int n_b
   return hipGetLastError();
 }
 
-// One workgroup = 4 waves x 16 rows.  The random vectors stream through LDS in
-// tiles of 64; each wave keeps its rows' fragments in registers.
-template <class E, int D>
+// One workgroup = 4 waves x 16*RF rows; each wave keeps the matrix-core
+// fragments of its rows in registers.  The random vectors stream through a
+// ring of three LDS tiles fed by asynchronous copies two tiles ahead, every
+// tile used by all the workgroup's rows (RF > 1 for large inputs: fewer loads
+// of the vectors per row).  Per output element the running best and
+// second-best scores are kept branch-free (the second best is the median of
+// best, second and the new score); equal scores leave best = second, which
+// sends the row to the float64 decision (lowest index among exact ties).
+template <class E, int D, int RF>
 __global__ __launch_bounds__(256) void k_project_argmax(
     const E* __restrict__ V, int64_t n, const E* __restrict__ Bt, int n_b,
     const float* __restrict__ bnorm_max, float beta_coef, int32_t* __restrict__ ids,
     float* __restrict__ norms, uint32_t* __restrict__ norm_max_bits, uint32_t* __restrict__ counters) {
-  constexpr int P = Pitch<E, D>::value;
-  __shared__ __attribute__((aligned(16))) E tile[64 * P];
+  using G = TileGeom<E, D>;
+  constexpr int NW = 4;
+  __shared__ __attribute__((aligned(1024))) char ring[3 * G::ROW_BYTES];
   const int w = threadIdx.x >> 6;
   const int l = lane_id();
   const int g = l >> 4;
-  const int64_t row0 = (int64_t)blockIdx.x * 64 + w * 16;
-  const int64_t rA = row0 + (l & 15);
+  const int nt = (n_b + G::TI - 1) / G::TI;
 
-  Frag<E, D> a;
-  a.load_global(rA < n ? V + rA * D : nullptr);
+  // the first two tiles of vectors are on their way while the rows load
+  int inflight[2] = {0, 0};
+  inflight[0] = dma_rows<E, D, NW>(ring, Bt, 0, n_b, w);
+  if (nt > 1) inflight[1] = dma_rows<E, D, NW>(ring + G::ROW_BYTES, Bt, G::TI, n_b, w);
 
-  // Squared norm of row (l & 15): each lane sums its fragment, then the 4 lanes of the row.
-  float ss = 0.0f;
-  {
+  Frag<E, D> a[RF];
+  float my_norm[RF];
+#pragma unroll
+  for (int f = 0; f < RF; ++f) {
+    const int64_t rA = ((int64_t)blockIdx.x * NW + w) * 16 * RF + 16 * f + (l & 15);
     const E* rp = rA < n ? V + rA * D : nullptr;
-    if (rp) {
-      const int q = g;
+    a[f].load_global(rp);
+    // squared norm of row (l & 15) from the fragment: each lane sums its part, then the 4 lanes of the row
+    float ss = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < Frag<E, D>::KS; ++ks) {
       if constexpr (sizeof(E) == 2) {
-        for (int ks = 0; ks < D / 32; ++ks)
-          for (int t = 0; t < 8; ++t) {
-            const float f = to_f32(rp[32 * ks + 8 * q + t]);
-            ss = fmaf(f, f, ss);
-          }
-      } else {
-        for (int ks = 0; ks < D / 4; ++ks) {
-          const float f = to_f32(rp[4 * ks + q]);
-          ss = fmaf(f, f, ss);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const float x = to_f32(a[f].v[ks][t]);
+          ss = fmaf(x, x, ss);
         }
+      } else {
+        ss = fmaf(a[f].v[ks], a[f].v[ks], ss);
       }
     }
     ss += __shfl_xor(ss, 16);
     ss += __shfl_xor(ss, 32);
+    // float32 sum of squares has relative error below d * 2^-24 < 2^-12 for d <= 512.
+    my_norm[f] = sqrtf(ss) * (1.0f + 0.0005f);
   }
-  // float32 sum of squares has relative error below d * 2^-24 < 2^-12 for d <= 512.
-  const float my_norm = sqrtf(ss) * (1.0f + 0.0005f);
 
-  float best1[4], best2[4];
-  int idx1[4];
+  float best1[RF][4], best2[RF][4];
+  int idx1[RF][4];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    best1[v] = NEG_INF;
-    best2[v] = NEG_INF;
-    idx1[v] = 0;
-  }
-
-  for (int b0 = 0; b0 < n_b; b0 += 64) {
-    __syncthreads();
-    // stage 64 random vectors (rows of Bt) in LDS, 16 bytes per thread per step
-    constexpr int PIECES = D * (int)sizeof(E) / 16;   // 16-byte pieces per vector
-    for (int pc = threadIdx.x; pc < 64 * PIECES; pc += 256) {
-      const int nb = pc / PIECES, part = pc % PIECES;
-      constexpr int EPP = 16 / (int)sizeof(E);
-      u32x4 val = {0u, 0u, 0u, 0u};
-      if (b0 + nb < n_b) val = *reinterpret_cast<const u32x4*>(Bt + (int64_t)(b0 + nb) * D + part * EPP);
-      *reinterpret_cast<u32x4*>(tile + nb * P + part * EPP) = val;
+  for (int f = 0; f < RF; ++f)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      best1[f][v] = NEG_INF;
+      best2[f][v] = NEG_INF;
+      idx1[f][v] = 0;
     }
-    __syncthreads();
+
+  for (int t = 0; t < nt; ++t) {
+    // tile t's copies are complete once only tile t+1's remain outstanding
+    wait_vmcnt(t + 1 < nt ? inflight[(t + 1) & 1] : 0);
+    raw_barrier();   // every wave's copies of tile t landed; slot (t+2) % 3 is free
+    if (t + 2 < nt)
+      inflight[t & 1] = dma_rows<E, D, NW>(ring + (size_t)((t + 2) % 3) * G::ROW_BYTES, Bt,
+                                           (int64_t)(t + 2) * G::TI, n_b, w);
+    const char* rows = ring + (size_t)(t % 3) * G::ROW_BYTES;
+    const int b0 = t * G::TI;
+    const bool full = b0 + G::TI <= n_b;
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-      if (b0 + cb * 16 >= n_b) break;
+    for (int cb = 0; cb < G::TI / 16; ++cb) {
       Frag<E, D> bf;
-      bf.load_lds(tile + (cb * 16 + (l & 15)) * P);
-      const f32x4 acc = mma_block(a, bf, f32x4{0.f, 0.f, 0.f, 0.f});
+      TileFrag<E, D>::load(bf, rows, cb * 16 + (l & 15));
       const int bcol = b0 + cb * 16 + (l & 15);
+      const bool valid = full || bcol < n_b;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float sc = bcol < n_b ? acc[v] : NEG_INF;
-        if (sc > best1[v]) {
-          best2[v] = best1[v];
-          best1[v] = sc;
-          idx1[v] = bcol;
-        } else if (sc > best2[v]) {
-          best2[v] = sc;
+      for (int f = 0; f < RF; ++f) {
+        const f32x4 acc = mma_block(a[f], bf, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float sc = valid ? acc[v] : NEG_INF;
+          idx1[f][v] = sc > best1[f][v] ? bcol : idx1[f][v];
+          best2[f][v] = __builtin_amdgcn_fmed3f(best1[f][v], best2[f][v], sc);
+          best1[f][v] = fmaxf(best1[f][v], sc);
         }
-      }
-    }
-  }
-
-  // Merge the top-2 summaries of the 16 lanes that hold each row.
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      const float ob1 = __shfl_xor(best1[v], o);
-      const float ob2 = __shfl_xor(best2[v], o);
-      const int oi = __shfl_xor(idx1[v], o);
-      const float lo1 = fminf(best1[v], ob1);
-      const bool take = ob1 > best1[v] || (ob1 == best1[v] && oi < idx1[v]);
-      best2[v] = fmaxf(lo1, fmaxf(best2[v], ob2));
-      if (take) {
-        best1[v] = ob1;
-        idx1[v] = oi;
       }
     }
   }
 
   const float bmax = bnorm_max[0];
-  uint64_t need_all = 0;
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int r = 4 * g + v;                       // row of this output element within the wave
-    const float nrm = __shfl(my_norm, r);          // lane r holds row r's norm
-    const int64_t row = row0 + r;
-    // |float32 score - float64 score| <= beta (matrix-core accumulation bound + float64 rounding)
-    const double beta = (double)beta_coef * (double)nrm * (double)bmax;
-    const bool decided = (double)best1[v] - (double)best2[v] > 2.0 * beta;
-    if (decided && (l & 15) == 0 && row < n) ids[row] = idx1[v];
-    const uint64_t und = ballot(!decided && row < n);
-    need_all |= (und & 0x0001000100010001ull) << v;    // bit 16*g + v
-  }
-  // Float64 fallback: the whole wave recomputes every score of an undecided row.
-  while (need_all) {
-    const int bit = __builtin_ctzll(need_all);
-    need_all &= need_all - 1;
-    const int r = 4 * (bit >> 4) + (bit & 15);
-    const int64_t row = row0 + r;
-    const E* x = V + row * D;
-    double be = -__builtin_huge_val();
-    int bi = 0x7fffffff;
-    for (int b = l; b < n_b; b += WAVE) {
-      const double e = exact_dot<E, D>(x, Bt + (int64_t)b * D);
-      if (e > be) {
-        be = e;
-        bi = b;
+  for (int f = 0; f < RF; ++f) {
+    const int64_t row0 = ((int64_t)blockIdx.x * NW + w) * 16 * RF + 16 * f;
+    // Merge the top-2 summaries of the 16 lanes that hold each row.
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        const float ob1 = __shfl_xor(best1[f][v], o);
+        const float ob2 = __shfl_xor(best2[f][v], o);
+        const int oi = __shfl_xor(idx1[f][v], o);
+        const float lo1 = fminf(best1[f][v], ob1);
+        const bool take = ob1 > best1[f][v] || (ob1 == best1[f][v] && oi < idx1[f][v]);
+        best2[f][v] = fmaxf(lo1, fmaxf(best2[f][v], ob2));
+        if (take) {
+          best1[f][v] = ob1;
+          idx1[f][v] = oi;
+        }
       }
     }
+    uint64_t need_all = 0;
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const double oe = __shfl_xor(be, o);
-      const int ob = __shfl_xor(bi, o);
-      if (oe > be || (oe == be && ob < bi)) {
-        be = oe;
-        bi = ob;
+    for (int v = 0; v < 4; ++v) {
+      const int r = 4 * g + v;                       // row of this output element within the fragment
+      const float nrm = __shfl(my_norm[f], r);       // lane r holds row r's norm
+      const int64_t row = row0 + r;
+      // |float32 score - float64 score| <= beta (matrix-core accumulation bound + float64 rounding)
+      const double beta = (double)beta_coef * (double)nrm * (double)bmax;
+      const bool decided = (double)best1[f][v] - (double)best2[f][v] > 2.0 * beta;
+      if (decided && (l & 15) == 0 && row < n) ids[row] = idx1[f][v];
+      const uint64_t und = ballot(!decided && row < n);
+      need_all |= (und & 0x0001000100010001ull) << v;    // bit 16*g + v
+    }
+    // Float64 fallback: the whole wave recomputes every score of an undecided row.
+    while (need_all) {
+      const int bit = __builtin_ctzll(need_all);
+      need_all &= need_all - 1;
+      const int r = 4 * (bit >> 4) + (bit & 15);
+      const int64_t row = row0 + r;
+      const E* x = V + row * D;
+      double be = -__builtin_huge_val();
+      int bi = 0x7fffffff;
+#pragma unroll 1
+      for (int b = l; b < n_b; b += WAVE) {
+        const double e = exact_dot<E, D, 4>(x, Bt + (int64_t)b * D);
+        if (e > be) {
+          be = e;
+          bi = b;
+        }
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        const double oe = __shfl_xor(be, o);
+        const int ob = __shfl_xor(bi, o);
+        if (oe > be || (oe == be && ob < bi)) {
+          be = oe;
+          bi = ob;
+        }
+      }
+      if (bi >= n_b) bi = 0;   // only reachable with NaN scores
+      if (l == 0) {
+        ids[row] = bi;
+        atomicAdd(counters + CNT_ARGMAX_EXACT, 1u);
       }
     }
-    if (bi >= n_b) bi = 0;   // only reachable with NaN scores
-    if (l == 0) {
-      ids[row] = bi;
-      atomicAdd(counters + CNT_ARGMAX_EXACT, 1u);
+    const int64_t rA = row0 + (l & 15);
+    if (l < 16 && rA < n) {
+      if (norms) norms[rA] = my_norm[f];
+      if (norm_max_bits) atomicMax(norm_max_bits, __float_as_uint(my_norm[f]));
     }
-  }
-
-  if (l < 16 && rA < n) {
-    if (norms) norms[rA] = my_norm;
-    if (norm_max_bits) atomicMax(norm_max_bits, __float_as_uint(my_norm));
   }
 }
 
 template <class E, int D>
 static hipError_t launch_pa(const void* V, int64_t n, const void* Bt, int n_b, const float* bmax, float beta,
                             int32_t* ids, float* norms, uint32_t* nmax, uint32_t* counters, hipStream_t st) {
-  const unsigned blocks = (unsigned)((n + 63) / 64);
-  hipLaunchKernelGGL((k_project_argmax<E, D>), dim3(blocks), dim3(256), 0, st, (const E*)V, n, (const E*)Bt,
-                     n_b, bmax, beta, ids, norms, nmax, counters);
+  // several row fragments per wave (as many as registers allow at two waves per
+  // SIMD) once the input still gives every CU several workgroups
+  constexpr int RF = D * (int)sizeof(E) >= 512 ? 2 : 4;
+  if (n >= (int64_t)64 * RF * 2048) {
+    const unsigned blocks = (unsigned)((n + 64 * RF - 1) / (64 * RF));
+    hipLaunchKernelGGL((k_project_argmax<E, D, RF>), dim3(blocks), dim3(256), 0, st, (const E*)V, n, (const E*)Bt,
+                       n_b, bmax, beta, ids, norms, nmax, counters);
+  } else {
+    const unsigned blocks = (unsigned)((n + 63) / 64);
+    hipLaunchKernelGGL((k_project_argmax<E, D, 1>), dim3(blocks), dim3(256), 0, st, (const E*)V, n, (const E*)Bt,
+                       n_b, bmax, beta, ids, norms, nmax, counters);
+  }
   return hipGetLastError();
 }
 

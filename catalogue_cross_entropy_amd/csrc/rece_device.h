@@ -66,12 +66,15 @@ __device__ __forceinline__ uint32_t fkey(float f) {
 // float32 / bfloat16 values are exact in float64, so fma(a, b, acc) equals
 // acc + a*b rounded once: this is the reference value every selection uses.
 // Both rows are read in 16-byte pieces, a batch of pieces in flight at a time;
-// only the additions are ordered.
+// only the additions are ordered.  The pointers pass through an empty asm
+// statement: in a loop over rows the compiler would otherwise keep a
+// loop-invariant row converted to float64 in 2*D registers (or scratch).
 template <class E, int D, int MAXB = 8>
 __device__ __forceinline__ double exact_dot(const E* __restrict__ a, const E* __restrict__ b) {
   constexpr int EPP = 16 / (int)sizeof(E);     // elements per piece
   constexpr int NP = D / EPP;                  // pieces per row
   constexpr int BATCH = NP < MAXB ? NP : MAXB;   // pieces in flight (registers: 8 per piece)
+  asm volatile("" : "+v"(a), "+v"(b));
   const u32x4* pa = reinterpret_cast<const u32x4*>(a);
   const u32x4* pb = reinterpret_cast<const u32x4*>(b);
   double acc = 0.0;
