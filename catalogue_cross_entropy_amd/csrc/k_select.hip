@@ -86,7 +86,7 @@ __device__ inline WaveLds carve(char* base, int rounds) {
   return L;
 }
 
-enum { RF_BETA = 0, RF_MX = 1, RF_SEXP = 2, RF_THI = 3, RF_NBUF = 4, RF_ALO = 5 };
+enum { RF_BETA = 0, RF_MX = 1, RF_SEXP = 2, RF_THI = 3, RF_NBUF = 4, RF_ALO = 5, RF_AHI = 6 };
 enum { RI_I = 0, RI_KK = 1, RI_NSURE = 2, RI_NNEW = 3, RI_NABOVE = 4, RI_AOFF = 5, RI_NA = 6, RI_MODE = 7 };
 
 // One ring slot: the tile's rows, then 64 item ids, then for each earlier round
@@ -260,10 +260,18 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_sel
         auto collect = [&](auto ded) {
           constexpr bool DEDUP = decltype(ded)::value;
           PrevRow p0{};
-          if (DEDUP) p0 = L.prev[r * NP];
+          int cxm = 0, cxp = 0;   // chunks c-1, c+1 of the position in round 0
+          if (DEDUP) {
+            p0 = L.prev[r * NP];
+            cxm = p0.cx == 0 ? n_c - 1 : p0.cx - 1;
+            cxp = p0.cx == n_c - 1 ? 0 : p0.cx + 1;
+          }
+          const bool allwin = n_c <= 3;
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
           u32x4 jj = *reinterpret_cast<const u32x4*>(tid_ + cb * 16 + 4 * g);
+          u32x4 cy4 = {0u, 0u, 0u, 0u};
+          if (DEDUP) cy4 = *reinterpret_cast<const u32x4*>(tcy + cb * 16 + 4 * g);
           bool inb[4];
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
@@ -274,14 +282,27 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_sel
             const bool sure = cand && a > thi;
             inb[v] = cand && a >= tlo && a <= thi;
             bool dup = false;
-            if (DEDUP && (sure || inb[v])) {
-              // round 0's set in registers; rounds 1 .. rho-1 from LDS
-              if (in_window(p0.cx, tcy[n], n_c))
-                dup = beats<E, D>(a, p0.lo, p0.hi, p0.te, p0.tid, Xs + pA * D, Y, j, nexact);
-              for (int r2 = 1; r2 < rho && !dup; ++r2) {
-                const PrevRow pr = L.prev[r * NP + r2];
-                if (!in_window(pr.cx, tcy[64 * r2 + n], n_c)) continue;
-                dup = beats<E, D>(a, pr.lo, pr.hi, pr.te, pr.tid, Xs + pA * D, Y, j, nexact);
+            if (DEDUP) {
+              // round 0's set (registers), branch-free: the pair was in round 0's window and
+              // lies above its bounds, or is its threshold pair; a candidate within the
+              // bounds is decided in float64 (rare)
+              const int cy = (int)cy4[v];
+              const bool w0 = allwin || cy == p0.cx || cy == cxm || cy == cxp;
+              dup = w0 && (a > p0.hi || (a >= p0.lo && j == p0.tid));
+              const bool near0 = w0 && !dup && a >= p0.lo && (sure || inb[v]);
+              if (ballot(near0)) {
+                if (near0) {
+                  ++nexact;
+                  dup = beats_exact<E, D>(p0.te, p0.tid, Xs + pA * D, Y, j);
+                }
+              }
+              // rounds 1 .. rho-1 from LDS (three rounds or more)
+              if (rho > 1 && (sure || inb[v]) && !dup) {
+                for (int r2 = 1; r2 < rho && !dup; ++r2) {
+                  const PrevRow pr = L.prev[r * NP + r2];
+                  if (!in_window(pr.cx, tcy[64 * r2 + n], n_c)) continue;
+                  dup = beats<E, D>(a, pr.lo, pr.hi, pr.te, pr.tid, Xs + pA * D, Y, j, nexact);
+                }
               }
             }
             const bool nw = sure && !dup;
@@ -461,51 +482,6 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_sel
   // the kept list entries are the sorted prefix before the near-ties plus the
   // near-ties ranked within the count still missing.  A list id with bit 31 set
   // marks a pair kept in an earlier round (counted, not summed again).
-  // Sort every row's list first, four rows at a time (independent shuffle chains
-  // in flight together), and write the sorted lists back.
-  for (int r0 = 0; r0 < 16; r0 += 4) {
-    float v[4];
-    int id[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int r = r0 + q;
-      const bool act = L.ri[r * 8 + RI_I] >= 0 && k > 0 && L.rf[r * 8 + RF_THI] != NEG_INF;
-      const int n = act ? min(__float_as_int(L.rf[r * 8 + RF_NBUF]), SEL_CAP) : 0;
-      v[q] = l < n ? L.vals[r * SEL_CAP + l] : NEG_INF;
-      id[q] = l < n ? L.ids[r * SEL_CAP + l] : 0x7FFFFFFF;
-    }
-    // bitonic network, order "precedes": larger value first, then smaller id
-#pragma unroll
-    for (int size = 2; size <= WAVE; size <<= 1) {
-#pragma unroll
-      for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        const bool want_first = ((l & stride) == 0) == ((l & size) == 0);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float pv = __shfl_xor(v[q], stride);
-          const int pid = __shfl_xor(id[q], stride);
-          const int mi = id[q] & 0x7FFFFFFF, pi = pid & 0x7FFFFFFF;
-          const bool p_first = pv > v[q] || (pv == v[q] && pi < mi);
-          const bool m_first = v[q] > pv || (v[q] == pv && mi < pi);
-          if (want_first ? p_first : m_first) {
-            v[q] = pv;
-            id[q] = pid;
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int r = r0 + q;
-      const int n = min(__float_as_int(L.rf[r * 8 + RF_NBUF]), SEL_CAP);
-      if (l < n) {
-        L.vals[r * SEL_CAP + l] = v[q];
-        L.ids[r * SEL_CAP + l] = id[q];
-      }
-    }
-  }
-  wave_sync();
-
   int r_next = 0;
   while (r_next < 16) {
     int tot = 0;
@@ -527,13 +503,25 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_sel
           }
           kk = max(1, min(kk, max(n, 1)));
         }
-        const float v = l < n ? L.vals[r * SEL_CAP + l] : NEG_INF;   // sorted above
+        const float v = l < n ? L.vals[r * SEL_CAP + l] : NEG_INF;
         const int id = l < n ? L.ids[r * SEL_CAP + l] : 0x7FFFFFFF;
-        const float ak = __shfl(v, kk - 1);
+        // a_k, the kk-th largest float value of the list: the value v of the lane with
+        // (#entries above v) < kk <= (#entries at or above v); the entries are counted
+        // against every list entry, read four at a time (one broadcast LDS read)
+        int cgt = 0, cge = 0;
+        for (int u = 0; u < n; u += 4) {
+          const float4 q = *reinterpret_cast<const float4*>(&L.vals[r * SEL_CAP + u]);
+          cgt += (q.x > v) + (u + 1 < n && q.y > v) + (u + 2 < n && q.z > v) + (u + 3 < n && q.w > v);
+          cge += (q.x >= v) + (u + 1 < n && q.y >= v) + (u + 2 < n && q.z >= v) + (u + 3 < n && q.w >= v);
+        }
+        const uint64_t at_k = ballot(l < n && cgt < kk && cge >= kk);
+        const float ak = __shfl(v, at_k ? __builtin_ctzll(at_k) : 0);
         const float lo = f_down((double)ak - 2.0 * (double)beta);
         const float hi = f_up((double)ak + 2.0 * (double)beta);
         const int nabove = popc(ballot(l < n && v > hi));
-        int na = popc(ballot(l < n && v >= lo && v <= hi));   // lanes nabove .. nabove + na - 1
+        const bool inb = l < n && v >= lo && v <= hi;
+        const uint64_t inbm = ballot(inb);
+        int na = popc(inbm);
         if (tot + na > WLIST && r > r_next) break;   // next group
         if (na > WLIST) {   // cannot rank more near-ties than the batch holds
           if (l == 0) {
@@ -542,13 +530,14 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_sel
           }
           na = WLIST;
         }
-        const int e = l - nabove;
-        if (e >= 0 && e < na) {
+        const int e = popc(inbm & lanemask_lt());   // near-tie e (list order)
+        if (inb && e < na) {
           L.ci[tot + e] = l;
           L.cj[tot + e] = id & 0x7FFFFFFF;
           L.cr[tot + e] = r;
         }
         if (l == 0) {
+          L.rf[r * 8 + RF_AHI] = hi;
           L.rf[r * 8 + RF_ALO] = lo;
           L.ri[r * 8 + RI_NABOVE] = nabove;
           L.ri[r * 8 + RI_AOFF] = tot;
@@ -597,12 +586,16 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_sel
         const int aoff = L.ri[r * 8 + RI_AOFF];
         const int na = L.ri[r * 8 + RI_NA];
         const int need = L.ri[r * 8 + RI_KK] - nabove;   // near-ties that are kept (>= 1)
-        // rank of this lane's near-tie (lane nabove + e holds near-tie e)
-        const int e = l - nabove;
+        // rank of this lane's near-tie (the e-th list entry within [lo, hi])
+        const float lo = L.rf[r * 8 + RF_ALO], hi = L.rf[r * 8 + RF_AHI];
+        const float a = l < n ? L.vals[r * SEL_CAP + l] : NEG_INF;
+        const int jraw = l < n ? L.ids[r * SEL_CAP + l] : 0;
+        const bool inb = l < n && a >= lo && a <= hi;
+        const int e = popc(ballot(inb) & lanemask_lt());
         int rank = WAVE;
         double me = 0.0;
         int mj = 0;
-        if (e >= 0 && e < na) {
+        if (inb && e < na) {
           me = L.ce[aoff + e];
           mj = L.cj[aoff + e];
           rank = 0;
@@ -624,10 +617,8 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_sel
         const double b2 = (double)beta * (1.0 + 1e-6);
         tlo = f_down(te - b2);
         thi = f_up(te + b2);
-        // kept list entries: the prefix before the near-ties and the near-ties ranked in
-        const float a = l < n ? L.vals[r * SEL_CAP + l] : NEG_INF;
-        const int jraw = l < n ? L.ids[r * SEL_CAP + l] : 0;
-        const bool kept = l < n && (l < nabove || rank < need);
+        // kept list entries: those above the near-ties and the near-ties ranked in
+        const bool kept = l < n && (a > hi || rank < need);
         const bool fresh = kept && (jraw & 0x80000000) == 0;
         se += wave_sumf(fresh ? __expf(a - mx) : 0.0f);
         nnew += popc(ballot(fresh));
