@@ -420,35 +420,52 @@ __global__ __launch_bounds__(256) void k_pos_pieces(BwdArgs p, const int32_t* __
   int head_item = -1, tail_item = -1;
   const int prev_item = t0 > 0 ? p.pos[sorted[t0 - 1]] : -1;
   const int next_item = t1 < s ? p.pos[sorted[t1]] : -1;
-  int cur = p.pos[sorted[t0]];
+  // lane e holds sorted position t0 + e: its id, positive item and coefficient (all
+  // loads in parallel); the walk below takes them with uniform lane reads
+  const int nt = (int)(t1 - t0);
+  const int i_l = l < nt ? sorted[t0 + l] : 0;
+  const int item_l = l < nt ? p.pos[i_l] : -1;
+  const float gp_l = l < nt ? (expf(p.lpos[i_l] - p.lse[i_l]) - 1.0f) * gbar_of(p, i_l) : 0.0f;
+  int cur = __builtin_amdgcn_readfirstlane(item_l);
   int64_t run_start = t0;
-  for (int64_t t = t0; t < t1; ++t) {
-    const int i = sorted[t];
-    const int item = p.pos[i];
-    if (item != cur) {
-      // flush the run [run_start, t) of item cur
-      if (run_start == t0 && prev_item == cur) {
-        head_item = cur;
-        flags |= 1;
+  constexpr int BATCH = 8;   // rows of X in flight
+  for (int tb = 0; tb < nt; tb += BATCH) {
+    float xv[BATCH][PER];
 #pragma unroll
-        for (int u = 0; u < PER; ++u)
-          if (l + 64 * u < D) partial[(piece * 2 + 0) * D + l + 64 * u] = acc[u];
-      } else if (cur >= 0 && cur < p.C) {
-        float* dst = p.dY + (int64_t)cur * D;
+    for (int q = 0; q < BATCH; ++q) {
+      const int i = __builtin_amdgcn_readlane(i_l, tb + q < nt ? tb + q : 0);
+      const E* xr = X + (int64_t)i * D;
 #pragma unroll
-        for (int u = 0; u < PER; ++u)
-          if (l + 64 * u < D) dst[l + 64 * u] += acc[u];
-      }
-#pragma unroll
-      for (int u = 0; u < PER; ++u) acc[u] = 0.0f;
-      cur = item;
-      run_start = t;
+      for (int u = 0; u < PER; ++u) xv[q][u] = (tb + q < nt && l + 64 * u < D) ? to_f32(xr[l + 64 * u]) : 0.0f;
     }
-    const float gp = (expf(p.lpos[i] - p.lse[i]) - 1.0f) * gbar_of(p, i);
-    const E* xr = X + (int64_t)i * D;
 #pragma unroll
-    for (int u = 0; u < PER; ++u)
-      if (l + 64 * u < D) acc[u] = fmaf(gp, to_f32(xr[l + 64 * u]), acc[u]);
+    for (int q = 0; q < BATCH; ++q) {
+      if (tb + q >= nt) break;
+      const int64_t t = t0 + tb + q;
+      const int item = __builtin_amdgcn_readlane(item_l, tb + q);
+      if (item != cur) {
+        // flush the run [run_start, t) of item cur
+        if (run_start == t0 && prev_item == cur) {
+          head_item = cur;
+          flags |= 1;
+#pragma unroll
+          for (int u = 0; u < PER; ++u)
+            if (l + 64 * u < D) partial[(piece * 2 + 0) * D + l + 64 * u] = acc[u];
+        } else if (cur >= 0 && cur < p.C) {
+          float* dst = p.dY + (int64_t)cur * D;
+#pragma unroll
+          for (int u = 0; u < PER; ++u)
+            if (l + 64 * u < D) dst[l + 64 * u] += acc[u];
+        }
+#pragma unroll
+        for (int u = 0; u < PER; ++u) acc[u] = 0.0f;
+        cur = item;
+        run_start = t;
+      }
+      const float gp = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gp_l), tb + q));
+#pragma unroll
+      for (int u = 0; u < PER; ++u) acc[u] = fmaf(gp, xv[q][u], acc[u]);
+    }
   }
   // last run [run_start, t1)
   const bool from_prev = run_start == t0 && prev_item == cur;
@@ -495,11 +512,28 @@ __global__ __launch_bounds__(256) void k_pos_combine(float* __restrict__ dY, con
   float acc[PER];
 #pragma unroll
   for (int u = 0; u < PER; ++u) acc[u] = l + 64 * u < D ? partial[(piece * 2 + 1) * D + l + 64 * u] : 0.0f;
-  for (int64_t q = piece + 1; q < npieces; ++q) {
+  // the run covers pieces piece+1 .. the first one whose head run does not continue
+  // (flag 2 clear) or the last piece; 64 flags are read at once, then the partial
+  // rows in order, several loads in flight
+  for (int64_t q0 = piece + 1; q0 < npieces; q0 += WAVE) {
+    const int64_t qq = q0 + l;
+    const int f = qq < npieces ? pflag[qq] : 0;
+    const uint64_t stop = ballot(qq >= npieces || !(f & 2));
+    const int nin = stop ? (int)min((int64_t)__builtin_ctzll(stop) + 1, npieces - q0) : WAVE;
+    constexpr int BATCH = 8;
+    for (int e0 = 0; e0 < nin; e0 += BATCH) {
+      float pv[BATCH][PER];
 #pragma unroll
-    for (int u = 0; u < PER; ++u)
-      if (l + 64 * u < D) acc[u] += partial[(q * 2 + 0) * D + l + 64 * u];
-    if (!(pflag[q] & 2)) break;
+      for (int e = 0; e < BATCH; ++e)
+#pragma unroll
+        for (int u = 0; u < PER; ++u)
+          pv[e][u] = (e0 + e < nin && l + 64 * u < D) ? partial[((q0 + e0 + e) * 2 + 0) * D + l + 64 * u] : 0.0f;
+#pragma unroll
+      for (int e = 0; e < BATCH; ++e)
+#pragma unroll
+        for (int u = 0; u < PER; ++u) acc[u] += pv[e][u];
+    }
+    if (stop) break;
   }
   float* dst = dY + (int64_t)item * D;
 #pragma unroll

@@ -36,11 +36,16 @@ __global__ void k_prep_b(const E* __restrict__ B, int d, int n_b, E* __restrict_
   const E* src = B + (int64_t)rho * d * n_b;
   E* dst = Bt + ((int64_t)rho * n_b + b) * d;
   double ss = 0.0;
-  for (int t = 0; t < d; ++t) {
-    const E v = src[(int64_t)t * n_b + b];
-    dst[t] = v;
-    const double f = (double)to_f32(v);
-    ss = fma(f, f, ss);
+  for (int t0 = 0; t0 < d; t0 += 8) {   // d is a multiple of 8: eight loads in flight
+    E v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = src[(int64_t)(t0 + u) * n_b + b];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      dst[t0 + u] = v[u];
+      const double f = (double)to_f32(v[u]);
+      ss = fma(f, f, ss);
+    }
   }
   const float nrm = f_up(sqrt(ss) * (1.0 + 1e-12));
   atomicMax(bnorm_max_bits + rho, __float_as_uint(nrm));

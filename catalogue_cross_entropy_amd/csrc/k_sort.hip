@@ -9,6 +9,10 @@
 //      equal keys find each other with one ballot per key bit, take ranks from
 //      the mask, and the group's running counter in LDS advances by the group
 //      size, so equal keys keep their input order.
+// When the count matrix is small (at most SMALL_COUNTS entries, at most 256
+// bins), step 2 is folded into step 3: every scatter workgroup reads the whole
+// matrix (L2-resident) and derives the slots of its own segments, which saves
+// the three launches of the scan.
 // The same kernels do the LSD passes of a wider radix sort: the key of input
 // slot t is (keys[in_perm[t]] >> shift) & (2^nbits - 1).
 #include "rece_device.h"
@@ -17,6 +21,8 @@
 namespace rece {
 
 constexpr int SCAN_BLOCK = 4096;   // elements per scan block (256 threads x 16)
+constexpr int64_t SMALL_COUNTS = 65536;   // count matrices scanned inside the scatter kernel
+constexpr int SMALL_BINS = 256;
 
 __device__ __forceinline__ int key_at(const int32_t* __restrict__ keys, const int32_t* __restrict__ in_perm,
                                       int64_t t, int shift, uint32_t mask) {
@@ -162,6 +168,87 @@ __global__ __launch_bounds__(256) void k_seg_scatter(const int32_t* __restrict__
   }
 }
 
+// Scatter with the scan folded in (small count matrices): the workgroup's four
+// segments get their first slots from the raw counts.  Thread b < nbins sums
+// bin b over all segments (its total) and over the segments before each of the
+// four; an exclusive scan of the totals over bins gives the bin bases.
+__global__ __launch_bounds__(256) void k_seg_scatter_small(const int32_t* __restrict__ keys,
+                                                           const int32_t* __restrict__ in_perm, int64_t n,
+                                                           int shift, int nbits, int seg_len, int nseg,
+                                                           const uint32_t* __restrict__ counts,
+                                                           int32_t* __restrict__ perm_out,
+                                                           int32_t* __restrict__ inv_out) {
+  __shared__ uint32_t ctr_all[4 * SMALL_BINS];
+  __shared__ uint32_t sh[4];
+  const int nbins = 1 << nbits;
+  const uint32_t mask = (uint32_t)nbins - 1u;
+  const int w = threadIdx.x >> 6, l = lane_id();
+  const int64_t seg0 = (int64_t)blockIdx.x * 4;
+  {
+    const int b = threadIdx.x;
+    uint32_t pre[4] = {0u, 0u, 0u, 0u};
+    uint32_t tot = 0;
+    if (b < nbins) {
+      const uint32_t* row = counts + (int64_t)b * nseg;
+      int q = 0;
+      for (; q + 4 <= nseg; q += 4) {
+        const uint32_t c0 = row[q], c1 = row[q + 1], c2 = row[q + 2], c3 = row[q + 3];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int64_t sg = seg0 + u;
+          pre[u] += (q < sg ? c0 : 0u) + (q + 1 < sg ? c1 : 0u) + (q + 2 < sg ? c2 : 0u) + (q + 3 < sg ? c3 : 0u);
+        }
+        tot += c0 + c1 + c2 + c3;
+      }
+      for (; q < nseg; ++q) {
+        const uint32_t c = row[q];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) pre[u] += q < seg0 + u ? c : 0u;
+        tot += c;
+      }
+    }
+    uint32_t total;
+    const uint32_t base = block_exclusive_scan_256(b < nbins ? tot : 0u, sh, &total);
+    if (b < nbins)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) ctr_all[u * SMALL_BINS + b] = base + pre[u];
+  }
+  __syncthreads();
+  const int64_t seg = seg0 + w;
+  if (seg >= nseg) return;   // whole wave leaves; no block barrier below
+  uint32_t* ctr = ctr_all + w * SMALL_BINS;
+  const int64_t t0 = seg * seg_len;
+  const int64_t t1 = min(n, t0 + seg_len);
+  for (int64_t tb = t0; tb < t1; tb += WAVE) {
+    const int64_t t = tb + l;
+    const bool valid = t < t1;
+    int key = 0;
+    int64_t e = 0;
+    if (valid) {
+      e = in_perm ? in_perm[t] : t;
+      key = (int)(((uint32_t)keys[e] >> shift) & mask);
+    }
+    uint64_t same = ballot(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool on = (key >> bit) & 1;
+      const uint64_t bm = ballot(on);
+      same &= on ? bm : ~bm;
+    }
+    const int rank = popc(same & lanemask_lt());
+    const int cnt = popc(same);
+    uint32_t base = 0;
+    if (valid) base = ctr[key];
+    wave_sync();
+    if (valid && rank == 0) ctr[key] = base + (uint32_t)cnt;
+    wave_sync();
+    if (valid) {
+      const uint32_t slot = base + (uint32_t)rank;
+      perm_out[slot] = (int32_t)e;
+      if (inv_out) inv_out[e] = (int32_t)slot;
+    }
+  }
+}
+
 // Keys per segment: about 256 segments for small inputs (enough waves for the
 // scatter), at most SORT_SEG keys each for large ones (bounded histogram matrix).
 static int64_t seg_len_for(int64_t n) {
@@ -172,6 +259,10 @@ static int64_t num_segments(int64_t n) {
   const int64_t L = seg_len_for(n);
   return (n + L - 1) / L;
 }
+
+// Digit width of an LSD pass over n keys: 8 bits when the count matrix then
+// stays small enough for the folded scan, else 12.
+int sort_digit_bits(int64_t n) { return num_segments(n) * SMALL_BINS <= SMALL_COUNTS ? 8 : 12; }
 
 size_t sort_scratch_bytes(int64_t n, int nbins) {
   const int64_t cnt = num_segments(n) * (int64_t)nbins;
@@ -191,6 +282,11 @@ hipError_t launch_counting_sort(const int32_t* keys, const int32_t* in_perm, int
                      shift, nbits, seg_len, (int)nseg, counts);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (nbins <= SMALL_BINS && nseg * nbins <= SMALL_COUNTS) {
+    hipLaunchKernelGGL(k_seg_scatter_small, dim3((unsigned)((nseg + 3) / 4)), dim3(256), 0, st, keys, in_perm, n,
+                       shift, nbits, seg_len, (int)nseg, counts, perm_out, inv_out);
+    return hipGetLastError();
+  }
   e = exclusive_scan(counts, nseg * nbins, bsum, st);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_seg_scatter, dim3((unsigned)((nseg + 3) / 4)), dim3(256), 4 * nbins * sizeof(uint32_t), st,

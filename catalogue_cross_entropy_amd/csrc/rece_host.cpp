@@ -229,10 +229,11 @@ static void plan_sce_layout(rece_plan_s* p) {
 static rece_status group_by_key(const rece_plan_s& p, const int32_t* keys, int64_t n, int64_t nkeys, char* sort_scratch,
                                 int32_t* tmp, int32_t* out, int32_t* inv, hipStream_t st) {
   const int total_bits = std::max(1, bits_for(nkeys));
-  const int npass = (total_bits + 11) / 12;
+  const int db = sort_digit_bits(n);
+  const int npass = (total_bits + db - 1) / db;
   const int32_t* in = nullptr;
-  for (int pass = 0, shift = 0; pass < npass; ++pass, shift += 12) {
-    const int nb = std::min(12, total_bits - shift);
+  for (int pass = 0, shift = 0; pass < npass; ++pass, shift += db) {
+    const int nb = std::min(db, total_bits - shift);
     int32_t* dst = ((npass - 1 - pass) % 2 == 0) ? out : tmp;   // the last pass lands in out
     RECE_PHASE(RECE_PHASE_SORT,
                launch_counting_sort(keys, in, n, shift, nb, sort_scratch, dst, pass == npass - 1 ? inv : nullptr, st),
@@ -460,9 +461,10 @@ static rece_status sce_backward(const rece_plan_s& p, hipStream_t st, const void
   bp.dY = dY;
   int32_t* bufs[2] = {reinterpret_cast<int32_t*>(sc + p.o_pp0), reinterpret_cast<int32_t*>(sc + p.o_pp1)};
   const int total_bits = std::max(1, bits_for(C));
+  const int db = sort_digit_bits(s);
   const int32_t* sorted = nullptr;
-  for (int pass = 0, shift = 0; shift < total_bits; ++pass, shift += 12) {
-    const int nb = std::min(12, total_bits - shift);
+  for (int pass = 0, shift = 0; shift < total_bits; ++pass, shift += db) {
+    const int nb = std::min(db, total_bits - shift);
     int32_t* outp = bufs[pass & 1];
     RECE_PHASE(RECE_PHASE_SORT, launch_counting_sort(pos, sorted, s, shift, nb, sc + p.o_sort, outp, nullptr, st),
                "sort positives");
@@ -506,7 +508,7 @@ rece_status rece_plan(const rece_config* cfg, rece_plan_t* out) {
   p->tpc_sel = (int)((rows_chunk + 16 * p->waves_sel - 1) / (16 * p->waves_sel));
   p->tpc_bwd = (int)((rows_chunk + 63) / 64);
   p->itiles = (int)((items_chunk + 63) / 64);
-  p->pos_passes = std::max(1, (bits_for(C) + 11) / 12);
+  p->pos_passes = std::max(1, (bits_for(C) + sort_digit_bits(c.s) - 1) / sort_digit_bits(c.s));
   // |float32 matrix-core dot - float64 coordinate-order dot| <= beta_coef * ||x|| * ||y||:
   // d products and d additions, each with relative error at most 2^-23 (round or
   // chop), doubled for safety; the float64 side adds d * 2^-53.
@@ -778,9 +780,10 @@ rece_status rece_backward(rece_plan_t plan, void* stream, const void* X, const v
   // positives: LSD counting sort of positions by positive id, then the segmented reduction
   int32_t* bufs[2] = {reinterpret_cast<int32_t*>(sc + p.o_pp0), reinterpret_cast<int32_t*>(sc + p.o_pp1)};
   const int total_bits = std::max(1, bits_for(C));
+  const int db = sort_digit_bits(s);
   const int32_t* sorted = nullptr;
-  for (int pass = 0, shift = 0; shift < total_bits; ++pass, shift += 12) {
-    const int nb = std::min(12, total_bits - shift);
+  for (int pass = 0, shift = 0; shift < total_bits; ++pass, shift += db) {
+    const int nb = std::min(db, total_bits - shift);
     int32_t* outp = bufs[pass & 1];
     RECE_PHASE(RECE_PHASE_SORT, launch_counting_sort(pos, sorted, s, shift, nb, sc + p.o_sort, outp, nullptr, st),
                "sort positives");

@@ -121,6 +121,7 @@ hipError_t launch_project_argmax(bool is_bf16, int d, const void* V, int64_t n, 
                                  const float* bnorm_max, float beta_coef, int32_t* ids, float* norms,
                                  uint32_t* norm_max_bits, uint32_t* counters, hipStream_t st);
 size_t sort_scratch_bytes(int64_t n, int nbins);
+int sort_digit_bits(int64_t n);
 hipError_t launch_counting_sort(const int32_t* keys, const int32_t* in_perm, int64_t n, int shift, int nbits,
                                 void* scratch, int32_t* perm_out, int32_t* inv_out, hipStream_t st);
 hipError_t launch_select(bool is_bf16, int d, int waves, const SelectArgs& a, hipStream_t st);
