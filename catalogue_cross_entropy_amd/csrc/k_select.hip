@@ -101,7 +101,7 @@ __host__ __device__ constexpr size_t sel_common_lds(size_t row_bytes, int rounds
 // NEGS: the kept ids are written out (p.negs set); a template flag keeps that
 // code out of the streaming loop when they are not.
 template <class E, int D, int NW, bool NEGS>
-__global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_select(SelectArgs p) {
+__global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 256) ? 2 : 1) void k_select(SelectArgs p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   using G = TileGeom<E, D>;
   constexpr int TI = G::TI;
@@ -652,10 +652,20 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 128) ? 2 : 1) void k_sel
   flush_count(p.counters + CNT_LOGIT_EXACT, nexact);
 }
 
+template <class E, int D>
+static size_t select_lds_bytes_t(int waves, int rounds) {
+  return sel_common_lds(TileGeom<E, D>::ROW_BYTES, rounds) + (size_t)waves * wave_lds_bytes(rounds);
+}
 size_t select_lds_bytes(bool is_bf16, int d, int waves, int rounds) {
-  const size_t rb = (size_t)d * (is_bf16 ? 2 : 4);
-  const size_t ti = rb <= 256 ? 64 : (rb == 512 ? 32 : 16);
-  return sel_common_lds(ti * rb, rounds) + (size_t)waves * wave_lds_bytes(rounds);
+#define RECE_L(E, DD) \
+  if (d == DD) return select_lds_bytes_t<E, DD>(waves, rounds);
+  if (is_bf16) {
+    RECE_L(bf16, 32) RECE_L(bf16, 64) RECE_L(bf16, 128) RECE_L(bf16, 256)
+  } else {
+    RECE_L(float, 32) RECE_L(float, 64) RECE_L(float, 128) RECE_L(float, 256)
+  }
+#undef RECE_L
+  return 0;
 }
 
 template <class E, int D, int NW>

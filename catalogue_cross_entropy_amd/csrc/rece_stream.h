@@ -21,7 +21,8 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 template <class E, int D> struct TileGeom {
   static constexpr int RB = D * (int)sizeof(E);             // bytes per row
-  static constexpr int TI = RB <= 256 ? 64 : (RB == 512 ? 32 : 16);   // rows per tile
+  // rows per tile: 8 KB row blocks where the matrix-core steps allow (bf16 needs 32 rows)
+  static constexpr int TI = RB <= 128 ? 64 : (RB <= 512 ? 32 : 16);
   static constexpr int CPR = RB / 16;                        // 16-byte chunks per row
   static constexpr int SWM = (CPR < 8 ? CPR : 8) - 1;        // swizzle mask
   static constexpr int ROW_BYTES = TI * RB;                  // bytes of the row block
