@@ -81,15 +81,15 @@ __global__ __launch_bounds__(256) void k_project_argmax(
   using G = TileGeom<E, D>;
   constexpr int NW = 4;
   __shared__ __attribute__((aligned(1024))) char ring[3 * G::ROW_BYTES];
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l = lane_id();
   const int g = l >> 4;
   const int nt = (n_b + G::TI - 1) / G::TI;
 
-  // the first two tiles of vectors are on their way while the rows load
-  int inflight[2] = {0, 0};
-  inflight[0] = dma_rows<E, D, NW>(ring, Bt, 0, n_b, w);
-  if (nt > 1) inflight[1] = dma_rows<E, D, NW>(ring + G::ROW_BYTES, Bt, G::TI, n_b, w);
+  // the first two tiles of vectors are on their way while the rows load; every
+  // tile takes the same number of copies from this wave
+  const int my_copies = dma_rows<E, D, NW>(ring, Bt, 0, n_b, w);
+  if (nt > 1) dma_rows<E, D, NW>(ring + G::ROW_BYTES, Bt, G::TI, n_b, w);
 
   Frag<E, D> a[RF];
   float my_norm[RF];
@@ -129,31 +129,36 @@ __global__ __launch_bounds__(256) void k_project_argmax(
       idx1[f][v] = 0;
     }
 
+  // +inf in a register the compiler cannot see through: med3(x, y, top) is max(x, y)
+  // without the canonicalising moves a folded maxnum would carry
+  float top = __builtin_huge_valf();
+  asm volatile("" : "+v"(top));
   for (int t = 0; t < nt; ++t) {
     // tile t's copies are complete once only tile t+1's remain outstanding
-    wait_vmcnt(t + 1 < nt ? inflight[(t + 1) & 1] : 0);
+    wait_vmcnt(t + 1 < nt ? my_copies : 0);
     raw_barrier();   // every wave's copies of tile t landed; slot (t+2) % 3 is free
     if (t + 2 < nt)
-      inflight[t & 1] = dma_rows<E, D, NW>(ring + (size_t)((t + 2) % 3) * G::ROW_BYTES, Bt,
-                                           (int64_t)(t + 2) * G::TI, n_b, w);
+      dma_rows<E, D, NW>(ring + (size_t)((t + 2) % 3) * G::ROW_BYTES, Bt, (int64_t)(t + 2) * G::TI, n_b, w);
     const char* rows = ring + (size_t)(t % 3) * G::ROW_BYTES;
     const int b0 = t * G::TI;
-    const bool full = b0 + G::TI <= n_b;
+    // vectors past n_b (last tile only) score -inf
+    const int nvalid = n_b - b0;
 #pragma unroll
     for (int cb = 0; cb < G::TI / 16; ++cb) {
       Frag<E, D> bf;
       TileFrag<E, D>::load(bf, rows, cb * 16 + (l & 15));
       const int bcol = b0 + cb * 16 + (l & 15);
-      const bool valid = full || bcol < n_b;
+      const float pad = cb * 16 + (l & 15) < nvalid ? 0.0f : NEG_INF;
 #pragma unroll
       for (int f = 0; f < RF; ++f) {
-        const f32x4 acc = mma_block(a[f], bf, f32x4{0.f, 0.f, 0.f, 0.f});
+        const f32x4 acc = mma_block(a[f], bf, f32x4{pad, pad, pad, pad});
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float sc = valid ? acc[v] : NEG_INF;
+          // med3 forms of max and second-best
+          const float sc = acc[v];
           idx1[f][v] = sc > best1[f][v] ? bcol : idx1[f][v];
           best2[f][v] = __builtin_amdgcn_fmed3f(best1[f][v], best2[f][v], sc);
-          best1[f][v] = fmaxf(best1[f][v], sc);
+          best1[f][v] = __builtin_amdgcn_fmed3f(best1[f][v], sc, top);
         }
       }
     }
