@@ -6,8 +6,10 @@
 // The scores are computed on the matrix cores in float32 (bf16 or f32 inputs)
 // and never stored.  The decision is the argmax of the float64 coordinate-order
 // sums: a row whose float32 top-2 gap exceeds twice the error bound is decided
-// by the float32 argmax; otherwise the wave recomputes all n_b scores of that
-// row in float64 (rare).
+// by the float32 argmax; the others (rare) are appended to a list, and a second
+// kernel recomputes all n_b scores of each listed row in float64, one wave per
+// row, so the slow rows neither stall the matrix-core kernel nor sit on its
+// critical path.
 #include "rece_device.h"
 #include "rece_internal.h"
 #include "rece_stream.h"
@@ -52,8 +54,9 @@ __global__ void k_prep_b(const E* __restrict__ B, int d, int n_b, E* __restrict_
 }
 
 hipError_t launch_prep_b(bool is_bf16, int d, const void* B, int rounds, int n_b, void* Bt, float* bnorm_max,
-                         hipStream_t st) {
-  hipError_t e = launch_fill_u32(reinterpret_cast<uint32_t*>(bnorm_max), 0u, rounds, st);
+                         int zero_words, hipStream_t st) {
+  // bnorm_max[0 .. rounds) and the zero_words following it are cleared
+  hipError_t e = launch_fill_u32(reinterpret_cast<uint32_t*>(bnorm_max), 0u, rounds + zero_words, st);
   if (e != hipSuccess) return e;
   dim3 grid((n_b + 255) / 256, rounds);
   if (is_bf16)
@@ -63,6 +66,33 @@ hipError_t launch_prep_b(bool is_bf16, int d, const void* B, int rounds, int n_b
     hipLaunchKernelGGL(k_prep_b<float>, grid, dim3(256), 0, st, (const float*)B, d, n_b, (float*)Bt,
                        reinterpret_cast<uint32_t*>(bnorm_max));
   return hipGetLastError();
+}
+
+// Wave-collective float64 argmax of x . b over the n_b vectors (lowest index
+// among ties): every lane scores n_b / 64 of them in coordinate order.
+template <class E, int D>
+__device__ __forceinline__ int argmax_exact_wave(const E* __restrict__ x, const E* __restrict__ Bt, int n_b) {
+  const int l = lane_id();
+  double be = -__builtin_huge_val();
+  int bi = 0x7fffffff;
+#pragma unroll 1
+  for (int b = l; b < n_b; b += WAVE) {
+    const double e = exact_dot<E, D, 4>(x, Bt + (int64_t)b * D);
+    if (e > be) {
+      be = e;
+      bi = b;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const double oe = __shfl_xor(be, o);
+    const int ob = __shfl_xor(bi, o);
+    if (oe > be || (oe == be && ob < bi)) {
+      be = oe;
+      bi = ob;
+    }
+  }
+  return bi;
 }
 
 // One workgroup = 4 waves x 16*RF rows; each wave keeps the matrix-core
@@ -77,7 +107,8 @@ template <class E, int D, int RF>
 __global__ __launch_bounds__(256) void k_project_argmax(
     const E* __restrict__ V, int64_t n, const E* __restrict__ Bt, int n_b,
     const float* __restrict__ bnorm_max, float beta_coef, int32_t* __restrict__ ids,
-    float* __restrict__ norms, uint32_t* __restrict__ norm_max_bits, uint32_t* __restrict__ counters) {
+    float* __restrict__ norms, uint32_t* __restrict__ norm_max_bits, int32_t* __restrict__ und,
+    uint32_t* __restrict__ und_n, uint32_t* __restrict__ counters) {
   using G = TileGeom<E, D>;
   constexpr int NW = 4;
   __shared__ __attribute__((aligned(1024))) char ring[3 * G::ROW_BYTES];
@@ -198,36 +229,29 @@ __global__ __launch_bounds__(256) void k_project_argmax(
       const uint64_t und = ballot(!decided && row < n);
       need_all |= (und & 0x0001000100010001ull) << v;    // bit 16*g + v
     }
-    // Float64 fallback: the whole wave recomputes every score of an undecided row.
-    while (need_all) {
-      const int bit = __builtin_ctzll(need_all);
-      need_all &= need_all - 1;
-      const int r = 4 * (bit >> 4) + (bit & 15);
-      const int64_t row = row0 + r;
-      const E* x = V + row * D;
-      double be = -__builtin_huge_val();
-      int bi = 0x7fffffff;
-#pragma unroll 1
-      for (int b = l; b < n_b; b += WAVE) {
-        const double e = exact_dot<E, D, 4>(x, Bt + (int64_t)b * D);
-        if (e > be) {
-          be = e;
-          bi = b;
-        }
+    // undecided rows: decided here by the whole wave (small inputs), or listed for
+    // the float64 kernel (one atomic per wave)
+    if (need_all && !und) {
+      uint32_t nfb = 0;
+      while (need_all) {
+        const int bit = __builtin_ctzll(need_all);
+        need_all &= need_all - 1;
+        const int64_t row = row0 + 4 * (bit >> 4) + (bit & 15);
+        int bi = argmax_exact_wave<E, D>(V + row * D, Bt, n_b);
+        if (bi >= n_b) bi = 0;   // only reachable with NaN scores
+        if (l == 0) ids[row] = bi;
+        ++nfb;
       }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        const double oe = __shfl_xor(be, o);
-        const int ob = __shfl_xor(bi, o);
-        if (oe > be || (oe == be && ob < bi)) {
-          be = oe;
-          bi = ob;
-        }
-      }
-      if (bi >= n_b) bi = 0;   // only reachable with NaN scores
-      if (l == 0) {
-        ids[row] = bi;
-        atomicAdd(counters + CNT_ARGMAX_EXACT, 1u);
+      if (l == 0) atomicAdd(counters + CNT_ARGMAX_EXACT, nfb);
+    }
+    if (need_all) {
+      uint32_t base = 0;
+      if (l == 0) base = atomicAdd(und_n, (uint32_t)__popcll(need_all));
+      base = __builtin_amdgcn_readfirstlane(base);
+      for (int e = 0; need_all; ++e) {
+        const int bit = __builtin_ctzll(need_all);
+        need_all &= need_all - 1;
+        if (l == 0) und[base + e] = (int32_t)(row0 + 4 * (bit >> 4) + (bit & 15));
       }
     }
     const int64_t rA = row0 + (l & 15);
@@ -238,30 +262,60 @@ __global__ __launch_bounds__(256) void k_project_argmax(
   }
 }
 
+// Float64 argmax of the listed rows: one wave per row (grid-stride over the list).
+template <class E, int D>
+__global__ __launch_bounds__(256) void k_argmax_exact(const E* __restrict__ V, const E* __restrict__ Bt, int n_b,
+                                                      const int32_t* __restrict__ und,
+                                                      const uint32_t* __restrict__ und_n, int32_t* __restrict__ ids,
+                                                      uint32_t* __restrict__ counters) {
+  const int l = lane_id();
+  const uint32_t nund = *und_n;
+  const uint32_t wv = blockIdx.x * 4 + (threadIdx.x >> 6), nwv = gridDim.x * 4;
+  uint32_t done = 0;
+  for (uint32_t u = wv; u < nund; u += nwv) {
+    const int64_t row = und[u];
+    int bi = argmax_exact_wave<E, D>(V + row * D, Bt, n_b);
+    if (bi >= n_b) bi = 0;   // only reachable with NaN scores
+    if (l == 0) ids[row] = bi;
+    ++done;
+  }
+  if (l == 0 && done) atomicAdd(counters + CNT_ARGMAX_EXACT, done);
+}
+
 template <class E, int D>
 static hipError_t launch_pa(const void* V, int64_t n, const void* Bt, int n_b, const float* bmax, float beta,
-                            int32_t* ids, float* norms, uint32_t* nmax, uint32_t* counters, hipStream_t st) {
+                            int32_t* ids, float* norms, uint32_t* nmax, int32_t* und, uint32_t* und_n,
+                            uint32_t* counters, hipStream_t st) {
   // several row fragments per wave (as many as registers allow at two waves per
   // SIMD) once the input still gives every CU several workgroups
   constexpr int RF = D * (int)sizeof(E) >= 512 ? 2 : 4;
   if (n >= (int64_t)64 * RF * 2048) {
     const unsigned blocks = (unsigned)((n + 64 * RF - 1) / (64 * RF));
     hipLaunchKernelGGL((k_project_argmax<E, D, RF>), dim3(blocks), dim3(256), 0, st, (const E*)V, n, (const E*)Bt,
-                       n_b, bmax, beta, ids, norms, nmax, counters);
-  } else {
+                       n_b, bmax, beta, ids, norms, nmax, und, und_n, counters);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // the listed rows: a wave per row, about one row in 2048 expected
+    const int64_t eb = n / 2048 > 2048 ? 2048 : n / 2048;
+    hipLaunchKernelGGL((k_argmax_exact<E, D>), dim3((unsigned)eb), dim3(256), 0, st, (const E*)V, (const E*)Bt, n_b,
+                       und, und_n, ids, counters);
+  } else {   // small input: undecided rows are decided inside the kernel
     const unsigned blocks = (unsigned)((n + 63) / 64);
     hipLaunchKernelGGL((k_project_argmax<E, D, 1>), dim3(blocks), dim3(256), 0, st, (const E*)V, n, (const E*)Bt,
-                       n_b, bmax, beta, ids, norms, nmax, counters);
+                       n_b, bmax, beta, ids, norms, nmax, (int32_t*)nullptr, (uint32_t*)nullptr, counters);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_project_argmax(bool is_bf16, int d, const void* V, int64_t n, const void* Bt, int n_b,
                                  const float* bnorm_max, float beta_coef, int32_t* ids, float* norms,
-                                 uint32_t* norm_max_bits, uint32_t* counters, hipStream_t st) {
+                                 uint32_t* norm_max_bits, int32_t* und, uint32_t* und_n, uint32_t* counters,
+                                 hipStream_t st) {
   if (n <= 0) return hipSuccess;
-#define RECE_PA(E, DD) \
-  if (d == DD) return launch_pa<E, DD>(V, n, Bt, n_b, bnorm_max, beta_coef, ids, norms, norm_max_bits, counters, st);
+#define RECE_PA(E, DD)                                                                                       \
+  if (d == DD)                                                                                               \
+    return launch_pa<E, DD>(V, n, Bt, n_b, bnorm_max, beta_coef, ids, norms, norm_max_bits, und, und_n, counters, \
+                            st);
   if (is_bf16) {
     RECE_PA(bf16, 32) RECE_PA(bf16, 64) RECE_PA(bf16, 128) RECE_PA(bf16, 256)
   } else {

@@ -90,7 +90,7 @@ struct rece_plan_s {
   size_t o_cnt, o_bx, o_by, o_px, o_ix, o_py, o_iy, o_te, o_tid, o_tlo, o_thi, o_msh, o_ssum, o_nmem, o_xnorm,
       o_ymax, o_lse, o_lpos, o_negs, o_xs, o_ys, o_cyp, saved_bytes;
   // scratch
-  size_t o_bt, o_bnorm, o_sort, o_part, o_pp0, o_pp1, o_ppart, o_rec, o_prev, scratch_bytes;
+  size_t o_bt, o_bnorm, o_und, o_sort, o_part, o_pp0, o_pp1, o_ppart, o_rec, o_prev, scratch_bytes;
   // bucket variant: slots = (bucket, position) and (bucket, item) pairs
   int64_t sx, sy;     // n_b * b_x, n_b * b_y
   int64_t qwords;     // words of one bucket's item bitmap
@@ -264,7 +264,7 @@ static rece_status sce_forward(const rece_plan_s& p, hipStream_t st, const void*
   RECE_PHASE(RECE_PHASE_OTHER, launch_fill_u32(counters, 0u, NUM_COUNTERS, st), "clear counters");
   RECE_PHASE(RECE_PHASE_OTHER, launch_fill_u32(xmax, 0u, 1, st), "clear norm max");
   RECE_PHASE(RECE_PHASE_OTHER, launch_fill_u32(ymax, 0u, 1, st), "clear norm max");
-  RECE_PHASE(RECE_PHASE_OTHER, launch_prep_b(p.bf16, d, B, 1, n_b, Bt, bnorm, st), "prepare projection vectors");
+  RECE_PHASE(RECE_PHASE_OTHER, launch_prep_b(p.bf16, d, B, 1, n_b, Bt, bnorm, 0, st), "prepare projection vectors");
   // K6a: projection scores of every position and item, one column per bucket
   RECE_PHASE(RECE_PHASE_PROJECT, launch_project_scores(p.bf16, d, X, s, Bt, n_b, pxt, xnorm, xmax, st),
              "position scores");
@@ -546,7 +546,8 @@ rece_status rece_plan(const rece_config* cfg, rece_plan_t* out) {
 
   Layout sc;
   p->o_bt = sc.take((size_t)r * c.n_b * d * p->esize);
-  p->o_bnorm = sc.take((size_t)r * 4);
+  p->o_bnorm = sc.take((size_t)r * 4 + (size_t)2 * r * 4);   // norms, then one list counter per bucketing launch
+  p->o_und = sc.take((size_t)std::max(s, C) * 4);
   const size_t sort_b = std::max({sort_scratch_bytes(s, 1 << p->nbits_b), sort_scratch_bytes(C, 1 << p->nbits_b),
                                   sort_scratch_bytes(s, 1 << std::min(12, bits_for(C)))});
   p->o_sort = sc.take(sort_b);
@@ -627,7 +628,9 @@ rece_status rece_forward(rece_plan_t plan, void* stream, const void* X, const vo
   if (c.variant == RECE_VARIANT_SCE) return sce_forward(p, st, X, Y, pos, B, sc, sv, loss, loss_pp);
   RECE_PHASE(RECE_PHASE_OTHER, launch_fill_u32(counters, 0u, NUM_COUNTERS, st), "clear counters");
   RECE_PHASE(RECE_PHASE_OTHER, launch_fill_u32(reinterpret_cast<uint32_t*>(ymax), 0u, 1, st), "clear norm max");
-  RECE_PHASE(RECE_PHASE_OTHER, launch_prep_b(p.bf16, d, B, c.rounds, c.n_b, Bt, bnorm, st),
+  uint32_t* und_n = reinterpret_cast<uint32_t*>(bnorm + c.rounds);   // cleared with the norms
+  int32_t* und = reinterpret_cast<int32_t*>(sc + p.o_und);
+  RECE_PHASE(RECE_PHASE_OTHER, launch_prep_b(p.bf16, d, B, c.rounds, c.n_b, Bt, bnorm, 2 * c.rounds, st),
              "prepare random vectors");
 
   for (int rho = 0; rho < c.rounds; ++rho) {
@@ -639,10 +642,11 @@ rece_status rece_forward(rece_plan_t plan, void* stream, const void* X, const vo
     int32_t* iy = reinterpret_cast<int32_t*>(sv + p.o_iy) + (int64_t)rho * C;
     const void* Btr = static_cast<const char*>(Bt) + (size_t)rho * c.n_b * d * p.esize;
     RECE_PHASE(RECE_PHASE_PROJECT, launch_project_argmax(p.bf16, d, X, s, Btr, c.n_b, bnorm + rho, p.beta_coef, bx,
-                                   rho == 0 ? xnorm : nullptr, nullptr, counters, st),
+                                   rho == 0 ? xnorm : nullptr, nullptr, und, und_n + 2 * rho, counters, st),
              "bucket positions");
     RECE_PHASE(RECE_PHASE_PROJECT, launch_project_argmax(p.bf16, d, Y, C, Btr, c.n_b, bnorm + rho, p.beta_coef, by, nullptr,
-                                   rho == 0 ? reinterpret_cast<uint32_t*>(ymax) : nullptr, counters, st),
+                                   rho == 0 ? reinterpret_cast<uint32_t*>(ymax) : nullptr, und, und_n + 2 * rho + 1,
+                                   counters, st),
              "bucket items");
     RECE_PHASE(RECE_PHASE_SORT, launch_counting_sort(bx, nullptr, s, 0, p.nbits_b, sc + p.o_sort, px, ix, st),
                "sort positions");

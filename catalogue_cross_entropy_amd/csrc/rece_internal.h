@@ -115,11 +115,15 @@ struct BwdArgs {
 
 // Launchers (defined in the .hip files).  All enqueue on `st`.
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t st);
+// bnorm_max[0 .. rounds) and the zero_words 32-bit words after it are cleared first.
 hipError_t launch_prep_b(bool is_bf16, int d, const void* B, int rounds, int n_b, void* Bt, float* bnorm_max,
-                         hipStream_t st);
+                         int zero_words, hipStream_t st);
+// und: room for n row ids; und_n: a zero counter (rows whose float32 decision is
+// not certain are listed there and decided in float64 by a second kernel).
 hipError_t launch_project_argmax(bool is_bf16, int d, const void* V, int64_t n, const void* Bt, int n_b,
                                  const float* bnorm_max, float beta_coef, int32_t* ids, float* norms,
-                                 uint32_t* norm_max_bits, uint32_t* counters, hipStream_t st);
+                                 uint32_t* norm_max_bits, int32_t* und, uint32_t* und_n, uint32_t* counters,
+                                 hipStream_t st);
 size_t sort_scratch_bytes(int64_t n, int nbins);
 int sort_digit_bits(int64_t n);
 hipError_t launch_counting_sort(const int32_t* keys, const int32_t* in_perm, int64_t n, int shift, int nbits,
