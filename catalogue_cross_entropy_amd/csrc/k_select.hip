@@ -37,6 +37,7 @@ constexpr int SEL_CAP = 64;      // candidate-list capacity per position
 constexpr int SEL_SLACK = 16;    // room kept for entries within 2*beta outside the k-th bin
 constexpr int MAX_REFINE = 2;    // histogram passes that may split a crowded bin
 constexpr float X_TOP = 255.99998f;   // largest histogram coordinate (below 256)
+constexpr float LOG2E_F = 1.44269504088896341f;
 
 // Per-wave LDS region.
 constexpr int WLIST = 128;   // near-tie entries of one wave awaiting float64 values
@@ -259,6 +260,7 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 256) ? 2 : 1) void k_sel
         // earlier-round test exists only in rounds after the first (two loop bodies).
         auto collect = [&](auto ded) {
           constexpr bool DEDUP = decltype(ded)::value;
+          float mxl = mx * LOG2E_F;
           PrevRow p0{};
           int cxm = 0, cxp = 0;   // chunks c-1, c+1 of the position in round 0
           if (DEDUP) {
@@ -309,9 +311,11 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 256) ? 2 : 1) void k_sel
             if (selall && nw && a > mx) {   // no histogram pass ran: keep the shift at the maximum
               sexp = mx == NEG_INF ? 0.0f : sexp * __expf(mx - a);
               mx = a;
+              mxl = mx * LOG2E_F;
             }
-            sexp += nw ? __expf(a - mx) : 0.0f;
-            nnew += nw ? 1 : 0;
+            // exp(a - mx) as 2^(a log2 e - mx log2 e), one fma before the exponential
+            sexp += nw ? __builtin_amdgcn_exp2f(fmaf(a, LOG2E_F, -mxl)) : 0.0f;
+            if (DEDUP) nnew += nw ? 1 : 0;   // without the earlier-round test every sure member is new
             if (NEGS) {
               const uint64_t ms = ballot(sure);
               if (sure) {
@@ -461,6 +465,7 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 256) ? 2 : 1) void k_sel
     nnew += __shfl_xor(nnew, o);
     if (!NEGS) nsure += __shfl_xor(nsure, o);
   }
+  if (rho == 0) nnew = nsure;   // round 0: the new members are the sure ones
   if (l < 16) {
     L.rf[r * 8 + RF_MX] = mx;
     L.rf[r * 8 + RF_SEXP] = sexp;
