@@ -171,10 +171,22 @@ __global__ __launch_bounds__(CS_THREADS) void k_col_select(ColSelectArgs a) {
   for (int pass = 0;; ++pass) {
     for (int i = tid; i < CS_BINS; i += CS_THREADS) hist[i] = 0u;
     __syncthreads();
-    for (int64_t t = tid; t < N; t += CS_THREADS) {
-      const float x = fminf(fmaxf((col[t] - lo0) * sc0, 0.0f), CS_XTOP);
-      const float y = (x - xa) * mul;
-      if (y >= 0.0f && y < (float)CS_BINS) atomicAdd(&hist[(int)y], 1u);
+    // eight loads in flight per thread before their bins are counted
+    constexpr int CS_BATCH = 8;
+    for (int64_t t0 = tid; t0 < N; t0 += (int64_t)CS_BATCH * CS_THREADS) {
+      float v[CS_BATCH];
+#pragma unroll
+      for (int q = 0; q < CS_BATCH; ++q) {
+        const int64_t t = t0 + (int64_t)q * CS_THREADS;
+        v[q] = t < N ? col[t] : 0.0f;
+      }
+#pragma unroll
+      for (int q = 0; q < CS_BATCH; ++q) {
+        const int64_t t = t0 + (int64_t)q * CS_THREADS;
+        const float x = fminf(fmaxf((v[q] - lo0) * sc0, 0.0f), CS_XTOP);
+        const float y = (x - xa) * mul;
+        if (t < N && y >= 0.0f && y < (float)CS_BINS) atomicAdd(&hist[(int)y], 1u);
+      }
     }
     __syncthreads();
     // thread tid owns bins 4*tid .. 4*tid+3; suffix sums from the top bin down
@@ -225,9 +237,21 @@ __global__ __launch_bounds__(CS_THREADS) void k_col_select(ColSelectArgs a) {
 
   // collect pass, in index order: sure members straight to the output, band entries to LDS
   int base_s = 0, base_n = 0;
+  constexpr int CS_CBATCH = 4;   // blocks of CS_THREADS entries whose loads are in flight together
+  float vb[CS_CBATCH];
   for (int64_t t0 = 0; t0 < N; t0 += CS_THREADS) {
+    const int qb = (int)((t0 / CS_THREADS) % CS_CBATCH);
+    if (qb == 0)
+#pragma unroll
+      for (int q = 0; q < CS_CBATCH; ++q) {
+        const int64_t tq = t0 + (int64_t)q * CS_THREADS + tid;
+        vb[q] = tq < N ? col[tq] : NEG_INF;
+      }
     const int64_t t = t0 + tid;
-    const float v = t < N ? col[t] : NEG_INF;
+    float v = vb[0];
+#pragma unroll
+    for (int q = 1; q < CS_CBATCH; ++q)
+      if (qb == q) v = vb[q];
     const bool sure = t < N && v > thi;
     const bool band = t < N && v >= tlo && v <= thi;
     const uint64_t ms = ballot(sure), mn = ballot(band);
