@@ -123,7 +123,7 @@ constexpr size_t ROWS_WAVE_LDS = 16 * MAX_ROUNDS * sizeof(PrevRow);
 // permuted identically on both sides), so G never goes through LDS; the B
 // operand (Y transposed) comes from the row tile with the LDS transpose read.
 template <class E, int D, int NW, bool SCE>
-__global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 256) ? 2 : 1) void k_bwd_rows(BwdArgs p) {
+__global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 512) ? 2 : 1) void k_bwd_rows(BwdArgs p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   using G = TileGeom<E, D>;
   constexpr int TI = G::TI;
@@ -288,7 +288,7 @@ __device__ __forceinline__ void issue_items_tile(char* ring, size_t slot_bytes, 
 // and positions 4*(l/16) + v of every 16-position block of the tile, the A
 // operand of dY = G^T . X; X transposed comes from the tile by transpose reads.
 template <class E, int D, int NW, bool SCE>
-__global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 256) ? 2 : 1) void k_bwd_items(BwdArgs p, int itiles) {
+__global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 512) ? 2 : 1) void k_bwd_items(BwdArgs p, int itiles) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   using G = TileGeom<E, D>;
   using LY = ItemsLayout<E, D>;
