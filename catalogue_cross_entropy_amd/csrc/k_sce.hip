@@ -98,11 +98,15 @@ __global__ __launch_bounds__(256) void k_project_scores(const E* __restrict__ V,
       for (int f = 0; f < 2; ++f) {
         const f32x4 c = mma_block(a[f], bf, f32x4{0.f, 0.f, 0.f, 0.f});
         if (bcol < n_b) {
+          // element v: row 4*(l/16)+v, bucket l%16: four consecutive rows of one column
           float* dst = PT + (int64_t)bcol * n;
+          const int64_t r = row0 + 16 * f + 4 * g;
+          if (r + 4 <= n && ((uintptr_t)(dst + r) & 15) == 0) {
+            *reinterpret_cast<f32x4*>(dst + r) = c;
+          } else {
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int64_t r = row0 + 16 * f + 4 * g + v;   // element v: row 4*(l/16)+v, bucket l%16
-            if (r < n) dst[r] = c[v];
+            for (int v = 0; v < 4; ++v)
+              if (r + v < n) dst[r + v] = c[v];
           }
         }
       }
