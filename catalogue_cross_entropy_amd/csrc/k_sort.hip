@@ -180,38 +180,54 @@ __global__ __launch_bounds__(256) void k_seg_scatter_small(const int32_t* __rest
                                                            int32_t* __restrict__ inv_out) {
   __shared__ uint32_t ctr_all[4 * SMALL_BINS];
   __shared__ uint32_t sh[4];
+  __shared__ uint32_t red[5 * 256];   // per (part, bin): total, then the four prefixes
   const int nbins = 1 << nbits;
   const uint32_t mask = (uint32_t)nbins - 1u;
   const int w = threadIdx.x >> 6, l = lane_id();
   const int64_t seg0 = (int64_t)blockIdx.x * 4;
   {
-    const int b = threadIdx.x;
+    // thread t sums bin t % nbins over its share of the segments (256 / nbins shares)
+    const int parts = 256 >> nbits;
+    const int b = threadIdx.x & (nbins - 1), part = threadIdx.x >> nbits;
+    const int per = (nseg + parts - 1) / parts;
+    const int q0 = part * per, q1 = min(nseg, q0 + per);
     uint32_t pre[4] = {0u, 0u, 0u, 0u};
     uint32_t tot = 0;
-    if (b < nbins) {
-      const uint32_t* row = counts + (int64_t)b * nseg;
-      int q = 0;
-      for (; q + 4 <= nseg; q += 4) {
-        const uint32_t c0 = row[q], c1 = row[q + 1], c2 = row[q + 2], c3 = row[q + 3];
+    const uint32_t* row = counts + (int64_t)b * nseg;
+    int q = q0;
+    for (; q + 4 <= q1; q += 4) {
+      const uint32_t c0 = row[q], c1 = row[q + 1], c2 = row[q + 2], c3 = row[q + 3];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int64_t sg = seg0 + u;
-          pre[u] += (q < sg ? c0 : 0u) + (q + 1 < sg ? c1 : 0u) + (q + 2 < sg ? c2 : 0u) + (q + 3 < sg ? c3 : 0u);
-        }
-        tot += c0 + c1 + c2 + c3;
+      for (int u = 0; u < 4; ++u) {
+        const int64_t sg = seg0 + u;
+        pre[u] += (q < sg ? c0 : 0u) + (q + 1 < sg ? c1 : 0u) + (q + 2 < sg ? c2 : 0u) + (q + 3 < sg ? c3 : 0u);
       }
-      for (; q < nseg; ++q) {
-        const uint32_t c = row[q];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) pre[u] += q < seg0 + u ? c : 0u;
-        tot += c;
-      }
+      tot += c0 + c1 + c2 + c3;
     }
-    uint32_t total;
-    const uint32_t base = block_exclusive_scan_256(b < nbins ? tot : 0u, sh, &total);
-    if (b < nbins)
+    for (; q < q1; ++q) {
+      const uint32_t c = row[q];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) ctr_all[u * SMALL_BINS + b] = base + pre[u];
+      for (int u = 0; u < 4; ++u) pre[u] += q < seg0 + u ? c : 0u;
+      tot += c;
+    }
+    red[threadIdx.x] = tot;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) red[(1 + u) * 256 + threadIdx.x] = pre[u];
+    __syncthreads();
+    // shares combined in order (exact integer sums), then the bin bases
+    uint32_t btot = 0, bpre[4] = {0u, 0u, 0u, 0u};
+    if (threadIdx.x < nbins)
+      for (int pt = 0; pt < parts; ++pt) {
+        const int t = pt * nbins + threadIdx.x;
+        btot += red[t];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) bpre[u] += red[(1 + u) * 256 + t];
+      }
+    uint32_t total;
+    const uint32_t base = block_exclusive_scan_256(threadIdx.x < nbins ? btot : 0u, sh, &total);
+    if (threadIdx.x < nbins)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) ctr_all[u * SMALL_BINS + threadIdx.x] = base + bpre[u];
   }
   __syncthreads();
   const int64_t seg = seg0 + w;
