@@ -45,18 +45,24 @@ constexpr int WLIST = 128;   // near-tie entries of one wave awaiting float64 va
 struct WaveLds {
   PrevRow* prev;    // [16][rounds - 1]
   double* ce;       // [WLIST]
-  uint32_t* hist;   // [16][NBINS / 2] two 16-bit counts per word (histogram passes),
+  uint32_t* hist;   // [16][HIST_STRIDE] two 16-bit counts per word (histogram passes),
                     // aliased by vals/ids (collect pass)
-  float* vals;      // [16][SEL_CAP]
-  int32_t* ids;     // [16][SEL_CAP]
+  float* vals;      // [16][LIST_STRIDE] (SEL_CAP used)
+  int32_t* ids;     // [16][LIST_STRIDE]
   int32_t* ci;      // [WLIST] list index in the row's candidate list
   int32_t* cj;      // [WLIST] item id
   int32_t* cr;      // [WLIST] row
   float* rf;        // [16][8] per-row floats
   int32_t* ri;      // [16][8] per-row ints
 };
-constexpr size_t WAVE_UNION = (size_t)16 * NBINS * 2 > (size_t)16 * SEL_CAP * 8 ? (size_t)16 * NBINS * 2
-                                                                                    : (size_t)16 * SEL_CAP * 8;
+// Row strides in LDS, padded so that the 16 rows of a wave start in different
+// banks (histogram: 129 words; lists: 68 entries, a multiple of four for the
+// 16-byte reads of the epilogue).
+constexpr int HIST_STRIDE = NBINS / 2 + 1;
+constexpr int LIST_STRIDE = SEL_CAP + 4;
+constexpr size_t WAVE_UNION = (size_t)16 * HIST_STRIDE * 4 > (size_t)16 * LIST_STRIDE * 8
+                                  ? (size_t)16 * HIST_STRIDE * 4
+                                  : (size_t)16 * LIST_STRIDE * 8;
 // earlier-round thresholds cached per row: rounds - 1 of them (at least one slot)
 __host__ __device__ constexpr int nprev_of(int rounds) { return rounds > 1 ? rounds - 1 : 1; }
 __host__ __device__ constexpr size_t wave_lds_bytes(int rounds) {
@@ -73,7 +79,7 @@ __device__ inline WaveLds carve(char* base, int rounds) {
   p += WLIST * 8;
   L.hist = reinterpret_cast<uint32_t*>(p);
   L.vals = reinterpret_cast<float*>(p);
-  L.ids = reinterpret_cast<int32_t*>(p + 16 * SEL_CAP * 4);
+  L.ids = reinterpret_cast<int32_t*>(p + 16 * LIST_STRIDE * 4);
   p += WAVE_UNION;
   L.ci = reinterpret_cast<int32_t*>(p);
   p += WLIST * 4;
@@ -179,7 +185,7 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 256) ? 2 : 1) void k_sel
   const float lo0 = -bnd, sc0 = (float)NBINS / (2.0f * bnd);
   // bin coordinate x = med3(a * sc0 + off0, 0, 256^-), the same expression in every pass
   const float off0 = -lo0 * sc0;
-  char* hist_row = reinterpret_cast<char*>(L.hist + r * (NBINS / 2));
+  char* hist_row = reinterpret_cast<char*>(L.hist + r * HIST_STRIDE);
   float xa = rv ? 0.0f : __builtin_huge_valf();   // rows past the chunk count nothing
   float mul = 1.0f;
   int kk = rv ? k : 0;
@@ -204,7 +210,7 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 256) ? 2 : 1) void k_sel
 
   for (int pass = 0; mode < 2; ++pass) {
     if (mode == 0)
-      for (int b = l; b < 16 * NBINS / 2; b += WAVE) L.hist[b] = 0u;
+      for (int b = l; b < 16 * HIST_STRIDE; b += WAVE) L.hist[b] = 0u;
     __syncthreads();
     issue_window_tile<E, D, NW>(ring, slot_bytes, win, 0, Ys, p.perm_y, p.cyp, C, rho, w);
     if (ntiles > 1) issue_window_tile<E, D, NW>(ring, slot_bytes, win, 1, Ys, p.perm_y, p.cyp, C, rho, w);
@@ -338,8 +344,8 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 256) ? 2 : 1) void k_sel
               if (inb[v]) {
                 const int slotn = bcnt + popc(m2 & row_lt);
                 if (slotn < SEL_CAP) {
-                  lds_store_u32(&L.vals[r * SEL_CAP + slotn], __float_as_uint(acc[cb][v]));
-                  lds_store_u32(&L.ids[r * SEL_CAP + slotn], jj[v]);
+                  lds_store_u32(&L.vals[r * LIST_STRIDE + slotn], __float_as_uint(acc[cb][v]));
+                  lds_store_u32(&L.ids[r * LIST_STRIDE + slotn], jj[v]);
                 }
               }
               bcnt += popc(m2 & rowbits);
@@ -367,7 +373,7 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 256) ? 2 : 1) void k_sel
       const float betar = __shfl(beta, rr);
       uint32_t h[4];
       {
-        const uint32_t w0 = L.hist[rr * (NBINS / 2) + 2 * l], w1 = L.hist[rr * (NBINS / 2) + 2 * l + 1];
+        const uint32_t w0 = L.hist[rr * HIST_STRIDE + 2 * l], w1 = L.hist[rr * HIST_STRIDE + 2 * l + 1];
         h[0] = w0 & 0xFFFFu;
         h[1] = w0 >> 16;
         h[2] = w1 & 0xFFFFu;
@@ -508,14 +514,14 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 256) ? 2 : 1) void k_sel
           }
           kk = max(1, min(kk, max(n, 1)));
         }
-        const float v = l < n ? L.vals[r * SEL_CAP + l] : NEG_INF;
-        const int id = l < n ? L.ids[r * SEL_CAP + l] : 0x7FFFFFFF;
+        const float v = l < n ? L.vals[r * LIST_STRIDE + l] : NEG_INF;
+        const int id = l < n ? L.ids[r * LIST_STRIDE + l] : 0x7FFFFFFF;
         // a_k, the kk-th largest float value of the list: the value v of the lane with
         // (#entries above v) < kk <= (#entries at or above v); the entries are counted
         // against every list entry, read four at a time (one broadcast LDS read)
         int cgt = 0, cge = 0;
         for (int u = 0; u < n; u += 4) {
-          const float4 q = *reinterpret_cast<const float4*>(&L.vals[r * SEL_CAP + u]);
+          const float4 q = *reinterpret_cast<const float4*>(&L.vals[r * LIST_STRIDE + u]);
           cgt += (q.x > v) + (u + 1 < n && q.y > v) + (u + 2 < n && q.z > v) + (u + 3 < n && q.w > v);
           cge += (q.x >= v) + (u + 1 < n && q.y >= v) + (u + 2 < n && q.z >= v) + (u + 3 < n && q.w >= v);
         }
@@ -593,8 +599,8 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 256) ? 2 : 1) void k_sel
         const int need = L.ri[r * 8 + RI_KK] - nabove;   // near-ties that are kept (>= 1)
         // rank of this lane's near-tie (the e-th list entry within [lo, hi])
         const float lo = L.rf[r * 8 + RF_ALO], hi = L.rf[r * 8 + RF_AHI];
-        const float a = l < n ? L.vals[r * SEL_CAP + l] : NEG_INF;
-        const int jraw = l < n ? L.ids[r * SEL_CAP + l] : 0;
+        const float a = l < n ? L.vals[r * LIST_STRIDE + l] : NEG_INF;
+        const int jraw = l < n ? L.ids[r * LIST_STRIDE + l] : 0;
         const bool inb = l < n && a >= lo && a <= hi;
         const int e = popc(ballot(inb) & lanemask_lt());
         int rank = WAVE;
