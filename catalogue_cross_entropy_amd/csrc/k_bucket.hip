@@ -255,10 +255,15 @@ __global__ __launch_bounds__(256) void k_project_argmax(
       }
     }
     const int64_t rA = row0 + (l & 15);
-    if (l < 16 && rA < n) {
-      if (norms) norms[rA] = my_norm[f];
-      if (norm_max_bits) atomicMax(norm_max_bits, __float_as_uint(my_norm[f]));
-    }
+    if (norms && l < 16 && rA < n) norms[rA] = my_norm[f];
+  }
+  if (norm_max_bits) {
+    // one atomic per wave: the largest norm of its rows (rows past n count 0)
+    float mx = 0.0f;
+#pragma unroll
+    for (int f = 0; f < RF; ++f) mx = fmaxf(mx, my_norm[f]);
+    mx = wave_max(mx);
+    if (l == 0) atomicMax(norm_max_bits, __float_as_uint(mx));
   }
 }
 

@@ -65,17 +65,18 @@ __global__ __launch_bounds__(256) void k_project_scores(const E* __restrict__ V,
     acc += __shfl_xor(acc, 32);
     ss[f] = acc;
   }
-  if (l < 16) {
+  float nmx = 0.0f;   // largest norm of the wave's rows (rows past n count 0)
 #pragma unroll
-    for (int f = 0; f < 2; ++f) {
-      const int64_t r = row0 + 16 * f + l;
-      if (r < n) {
-        // float32 sum of squares: relative error below d * 2^-24 < 2^-12; round the norm up
-        const float nrm = sqrtf(ss[f]) * (1.0f + 0.0005f);
-        if (norms) norms[r] = nrm;
-        if (norm_max_bits) atomicMax(norm_max_bits, __float_as_uint(nrm));
-      }
-    }
+  for (int f = 0; f < 2; ++f) {
+    const int64_t r = row0 + 16 * f + (l & 15);
+    // float32 sum of squares: relative error below d * 2^-24 < 2^-12; round the norm up
+    const float nrm = r < n ? sqrtf(ss[f]) * (1.0f + 0.0005f) : 0.0f;
+    if (norms && l < 16 && r < n) norms[r] = nrm;
+    nmx = fmaxf(nmx, nrm);
+  }
+  if (norm_max_bits) {   // one atomic per wave
+    nmx = wave_max(nmx);
+    if (l == 0) atomicMax(norm_max_bits, __float_as_uint(nmx));
   }
 
   for (int b0 = 0; b0 < n_b; b0 += TB) {
