@@ -129,6 +129,7 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 256) ? 2 : 1) void k_sel
   const int NP = nprev_of(p.rounds);
   (void)X;
   uint32_t nexact = 0;   // float64 logits computed by this lane
+  uint32_t ntopk = 0;    // rows whose k-th element needed a float64 ranking (same in every lane)
 
   const int lb = xcd_block(blockIdx.x, gridDim.x);
   const int c = lb / p.tiles_per_chunk;
@@ -624,7 +625,7 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 256) ? 2 : 1) void k_sel
           te = __shfl(me, tl);
           tid = __shfl(mj, tl);
         }
-        if (l == 0 && na > 1) atomicAdd(p.counters + CNT_TOPK_EXACT, 1u);
+        if (na > 1) ++ntopk;
         const double b2 = (double)beta * (1.0 + 1e-6);
         tlo = f_down(te - b2);
         thi = f_up(te + b2);
@@ -661,6 +662,7 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 256) ? 2 : 1) void k_sel
     r_next = r_end;
   }
   flush_count(p.counters + CNT_LOGIT_EXACT, nexact);
+  if (lane_id() == 0 && ntopk) atomicAdd(p.counters + CNT_TOPK_EXACT, ntopk);
 }
 
 template <class E, int D>
