@@ -72,9 +72,19 @@ struct Profiler {
   }
 };
 
+// A second stream of the plan (default priority) for launches with no data
+// dependence on the main chain, forked from and joined back into the caller's
+// stream with events; created on the device current at first use.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t join = nullptr;
+  std::vector<hipEvent_t> fork;
+};
+
 struct rece_plan_s {
   rece_config cfg;
   mutable Profiler prof;
+  mutable SideStream side;
   bool bf16;
   int esize;
   int nbits_b;
@@ -563,9 +573,26 @@ rece_status rece_plan(const rece_config* cfg, rece_plan_t* out) {
 }
 
 rece_status rece_plan_destroy(rece_plan_t plan) {
-  if (plan)
+  if (plan) {
     for (hipEvent_t e : plan->prof.pool) hipEventDestroy(e);
+    for (hipEvent_t e : plan->side.fork) hipEventDestroy(e);
+    if (plan->side.join) hipEventDestroy(plan->side.join);
+    if (plan->side.s) hipStreamDestroy(plan->side.s);
+  }
   delete plan;
+  return RECE_OK;
+}
+
+// The plan's side stream and nfork fork events (created once).
+static rece_status ensure_side(const rece_plan_s& p, int nfork) {
+  SideStream& sd = p.side;
+  if (!sd.s) RECE_HIP(hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking), "create side stream");
+  if (!sd.join) RECE_HIP(hipEventCreateWithFlags(&sd.join, hipEventDisableTiming), "create event");
+  while ((int)sd.fork.size() < nfork) {
+    hipEvent_t e = nullptr;
+    RECE_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming), "create event");
+    sd.fork.push_back(e);
+  }
   return RECE_OK;
 }
 
@@ -766,6 +793,11 @@ rece_status rece_backward(rece_plan_t plan, void* stream, const void* X, const v
   b.rounds = c.rounds;
   PosRec* recs = reinterpret_cast<PosRec*>(sc + p.o_rec);
   PrevRow* prevs = reinterpret_cast<PrevRow*>(sc + p.o_prev);
+  // dX (rounds in order) stays on the caller's stream; dY (rounds in order) runs on
+  // the side stream, each round after its records; the positive term joins them
+  const rece_status ss = ensure_side(p, c.rounds);
+  if (ss != RECE_OK) return ss;
+  hipStream_t side = p.side.s;
   for (int rho = 0; rho < c.rounds; ++rho) {
     b.rho = rho;
     b.perm_x = reinterpret_cast<const int32_t*>(sv + p.o_px) + (int64_t)rho * s;
@@ -778,10 +810,16 @@ rece_status rece_backward(rece_plan_t plan, void* stream, const void* X, const v
     RECE_PHASE(RECE_PHASE_OTHER, launch_bwd_records(b, b.perm_x, rho, recs + (int64_t)rho * s,
                                                     prevs + (int64_t)(rho * (rho - 1) / 2) * s, st),
                "backward records");
+    RECE_HIP(hipEventRecord(p.side.fork[rho], st), "fork");
     RECE_PHASE(RECE_PHASE_BWD_DX, launch_bwd_rows(p.bf16, d, 4, b, st), "dX");
-    RECE_PHASE(RECE_PHASE_BWD_DY, launch_bwd_items(p.bf16, d, 4, b, p.itiles, st), "dY");
+    RECE_HIP(hipStreamWaitEvent(side, p.side.fork[rho], 0), "fork");
+    {
+      hipStream_t st = side;
+      RECE_PHASE(RECE_PHASE_BWD_DY, launch_bwd_items(p.bf16, d, 4, b, p.itiles, st), "dY");
+    }
   }
-  // positives: LSD counting sort of positions by positive id, then the segmented reduction
+  // positives: LSD counting sort of positions by positive id (overlaps the side
+  // stream), then the segmented reduction into dY once the side stream is joined
   int32_t* bufs[2] = {reinterpret_cast<int32_t*>(sc + p.o_pp0), reinterpret_cast<int32_t*>(sc + p.o_pp1)};
   const int total_bits = std::max(1, bits_for(C));
   const int db = sort_digit_bits(s);
@@ -793,6 +831,8 @@ rece_status rece_backward(rece_plan_t plan, void* stream, const void* X, const v
                "sort positives");
     sorted = outp;
   }
+  RECE_HIP(hipEventRecord(p.side.join, side), "join");
+  RECE_HIP(hipStreamWaitEvent(st, p.side.join, 0), "join");
   RECE_PHASE(RECE_PHASE_BWD_POS, launch_pos_dy(p.bf16, d, b, sorted, reinterpret_cast<float*>(sc + p.o_ppart), st),
              "positive dY");
   return RECE_OK;
