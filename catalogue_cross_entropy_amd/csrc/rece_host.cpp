@@ -100,7 +100,7 @@ struct rece_plan_s {
   size_t o_cnt, o_bx, o_by, o_px, o_ix, o_py, o_iy, o_te, o_tid, o_tlo, o_thi, o_msh, o_ssum, o_nmem, o_xnorm,
       o_ymax, o_lse, o_lpos, o_negs, o_xs, o_ys, o_cyp, saved_bytes;
   // scratch
-  size_t o_bt, o_bnorm, o_und, o_sort, o_part, o_pp0, o_pp1, o_ppart, o_rec, o_prev, scratch_bytes;
+  size_t o_bt, o_bnorm, o_und, o_undy, o_sorty, o_sort, o_part, o_pp0, o_pp1, o_ppart, o_rec, o_prev, scratch_bytes;
   // bucket variant: slots = (bucket, position) and (bucket, item) pairs
   int64_t sx, sy;     // n_b * b_x, n_b * b_y
   int64_t qwords;     // words of one bucket's item bitmap
@@ -557,7 +557,9 @@ rece_status rece_plan(const rece_config* cfg, rece_plan_t* out) {
   Layout sc;
   p->o_bt = sc.take((size_t)r * c.n_b * d * p->esize);
   p->o_bnorm = sc.take((size_t)r * 4 + (size_t)2 * r * 4);   // norms, then one list counter per bucketing launch
-  p->o_und = sc.take((size_t)std::max(s, C) * 4);
+  p->o_und = sc.take((size_t)s * 4);    // undecided bucketing rows: positions,
+  p->o_undy = sc.take((size_t)C * 4);   // items (the item chain runs on the side stream)
+  p->o_sorty = sc.take(sort_scratch_bytes(C, 1 << p->nbits_b));
   const size_t sort_b = std::max({sort_scratch_bytes(s, 1 << p->nbits_b), sort_scratch_bytes(C, 1 << p->nbits_b),
                                   sort_scratch_bytes(s, 1 << std::min(12, bits_for(C)))});
   p->o_sort = sc.take(sort_b);
@@ -660,35 +662,54 @@ rece_status rece_forward(rece_plan_t plan, void* stream, const void* X, const vo
   RECE_PHASE(RECE_PHASE_OTHER, launch_prep_b(p.bf16, d, B, c.rounds, c.n_b, Bt, bnorm, 2 * c.rounds, st),
              "prepare random vectors");
 
+  // Item chain of every round (bucketing, sort, sorted copy, earlier-round chunks)
+  // on the side stream, position chain and chunk kernel on the caller's stream; the
+  // chunk kernel of round rho waits for the item chain of that round.
+  const rece_status ss = ensure_side(p, c.rounds + 1);
+  if (ss != RECE_OK) return ss;
+  hipStream_t side = p.side.s;
+  int32_t* undy = reinterpret_cast<int32_t*>(sc + p.o_undy);
+  RECE_HIP(hipEventRecord(p.side.fork[c.rounds], st), "fork");
+  RECE_HIP(hipStreamWaitEvent(side, p.side.fork[c.rounds], 0), "fork");
   for (int rho = 0; rho < c.rounds; ++rho) {
-    int32_t* bx = reinterpret_cast<int32_t*>(sv + p.o_bx) + (int64_t)rho * s;
+    hipStream_t st = side;
     int32_t* by = reinterpret_cast<int32_t*>(sv + p.o_by) + (int64_t)rho * C;
-    int32_t* px = reinterpret_cast<int32_t*>(sv + p.o_px) + (int64_t)rho * s;
-    int32_t* ix = reinterpret_cast<int32_t*>(sv + p.o_ix) + (int64_t)rho * s;
     int32_t* py = reinterpret_cast<int32_t*>(sv + p.o_py) + (int64_t)rho * C;
     int32_t* iy = reinterpret_cast<int32_t*>(sv + p.o_iy) + (int64_t)rho * C;
     const void* Btr = static_cast<const char*>(Bt) + (size_t)rho * c.n_b * d * p.esize;
-    RECE_PHASE(RECE_PHASE_PROJECT, launch_project_argmax(p.bf16, d, X, s, Btr, c.n_b, bnorm + rho, p.beta_coef, bx,
-                                   rho == 0 ? xnorm : nullptr, nullptr, und, und_n + 2 * rho, counters, st),
-             "bucket positions");
     RECE_PHASE(RECE_PHASE_PROJECT, launch_project_argmax(p.bf16, d, Y, C, Btr, c.n_b, bnorm + rho, p.beta_coef, by, nullptr,
-                                   rho == 0 ? reinterpret_cast<uint32_t*>(ymax) : nullptr, und, und_n + 2 * rho + 1,
+                                   rho == 0 ? reinterpret_cast<uint32_t*>(ymax) : nullptr, undy, und_n + 2 * rho + 1,
                                    counters, st),
              "bucket items");
-    RECE_PHASE(RECE_PHASE_SORT, launch_counting_sort(bx, nullptr, s, 0, p.nbits_b, sc + p.o_sort, px, ix, st),
-               "sort positions");
-    RECE_PHASE(RECE_PHASE_SORT, launch_counting_sort(by, nullptr, C, 0, p.nbits_b, sc + p.o_sort, py, iy, st),
+    RECE_PHASE(RECE_PHASE_SORT, launch_counting_sort(by, nullptr, C, 0, p.nbits_b, sc + p.o_sorty, py, iy, st),
                "sort items");
-    char* xs = sv + p.o_xs + (size_t)rho * s * d * p.esize;
     char* ys = sv + p.o_ys + (size_t)rho * C * d * p.esize;
     int32_t* cyp = reinterpret_cast<int32_t*>(sv + p.o_cyp) + (int64_t)(rho * (rho - 1) / 2) * C;
-    RECE_PHASE(RECE_PHASE_SORT, launch_gather_rows(X, px, s, d * p.esize, xs, st), "sorted positions");
     RECE_PHASE(RECE_PHASE_SORT, launch_gather_rows(Y, py, C, d * p.esize, ys, st), "sorted items");
     for (int r2 = 0; r2 < rho; ++r2)
       RECE_PHASE(RECE_PHASE_SORT,
                  launch_prev_chunks(py, reinterpret_cast<const int32_t*>(sv + p.o_iy) + (int64_t)r2 * C, C, c.n_c,
                                     cyp + (int64_t)r2 * C, st),
                  "earlier-round chunks");
+    RECE_HIP(hipEventRecord(p.side.fork[rho], side), "item chain done");
+  }
+
+  for (int rho = 0; rho < c.rounds; ++rho) {
+    int32_t* bx = reinterpret_cast<int32_t*>(sv + p.o_bx) + (int64_t)rho * s;
+    int32_t* px = reinterpret_cast<int32_t*>(sv + p.o_px) + (int64_t)rho * s;
+    int32_t* ix = reinterpret_cast<int32_t*>(sv + p.o_ix) + (int64_t)rho * s;
+    int32_t* py = reinterpret_cast<int32_t*>(sv + p.o_py) + (int64_t)rho * C;
+    const void* Btr = static_cast<const char*>(Bt) + (size_t)rho * c.n_b * d * p.esize;
+    RECE_PHASE(RECE_PHASE_PROJECT, launch_project_argmax(p.bf16, d, X, s, Btr, c.n_b, bnorm + rho, p.beta_coef, bx,
+                                   rho == 0 ? xnorm : nullptr, nullptr, und, und_n + 2 * rho, counters, st),
+             "bucket positions");
+    RECE_PHASE(RECE_PHASE_SORT, launch_counting_sort(bx, nullptr, s, 0, p.nbits_b, sc + p.o_sort, px, ix, st),
+               "sort positions");
+    char* xs = sv + p.o_xs + (size_t)rho * s * d * p.esize;
+    char* ys = sv + p.o_ys + (size_t)rho * C * d * p.esize;
+    int32_t* cyp = reinterpret_cast<int32_t*>(sv + p.o_cyp) + (int64_t)(rho * (rho - 1) / 2) * C;
+    RECE_PHASE(RECE_PHASE_SORT, launch_gather_rows(X, px, s, d * p.esize, xs, st), "sorted positions");
+    RECE_HIP(hipStreamWaitEvent(st, p.side.fork[rho], 0), "join item chain");
 
     SelectArgs a{};
     a.X = X;
