@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <utility>
@@ -76,6 +77,7 @@ struct Profiler {
 // dependence on the main chain, forked from and joined back into the caller's
 // stream with events; created on the device current at first use.
 struct SideStream {
+  std::mutex mu;   // one forward or backward enqueues on the side stream at a time
   hipStream_t s = nullptr;
   hipEvent_t join = nullptr;
   std::vector<hipEvent_t> fork;
@@ -655,6 +657,7 @@ rece_status rece_forward(rece_plan_t plan, void* stream, const void* X, const vo
   void* Bt = sc + p.o_bt;
 
   if (c.variant == RECE_VARIANT_SCE) return sce_forward(p, st, X, Y, pos, B, sc, sv, loss, loss_pp);
+  std::lock_guard<std::mutex> side_lock(p.side.mu);
   RECE_PHASE(RECE_PHASE_OTHER, launch_fill_u32(counters, 0u, NUM_COUNTERS, st), "clear counters");
   RECE_PHASE(RECE_PHASE_OTHER, launch_fill_u32(reinterpret_cast<uint32_t*>(ymax), 0u, 1, st), "clear norm max");
   uint32_t* und_n = reinterpret_cast<uint32_t*>(bnorm + c.rounds);   // cleared with the norms
@@ -786,6 +789,7 @@ rece_status rece_backward(rece_plan_t plan, void* stream, const void* X, const v
   const int64_t s = c.s, C = c.C;
   const int d = c.d;
   if (c.variant == RECE_VARIANT_SCE) return sce_backward(p, st, X, Y, pos, dloss, dloss_pp, sc, sv, dX, dY);
+  std::lock_guard<std::mutex> side_lock(p.side.mu);
 
   BwdArgs b{};
   b.sce = 0;

@@ -87,7 +87,14 @@ typedef struct rece_plan_s* rece_plan_t;
 /* Validate `cfg` and build a host-side plan (no GPU work, no device memory).
  * On error *out is NULL.  A plan may be used from several threads (profiling
  * aside, see rece_profile_enable); concurrent calls need their own scratch and
- * saved buffers. */
+ * saved buffers.  At its first forward or backward call a plan creates one
+ * extra HIP stream (default priority) and a few events on the current device,
+ * and uses that device from then on: the item-side steps of the forward and the
+ * dY chain of the backward run there, ordered with `stream` by events, so every
+ * result is complete in `stream` order when the call's work is.  Calls that
+ * use this stream take a per-plan lock while they enqueue.  rece_plan_destroy
+ * releases the stream and events (the caller makes sure no call is still
+ * running on the device). */
 rece_status rece_plan(const rece_config* cfg, rece_plan_t* out);
 rece_status rece_plan_destroy(rece_plan_t plan);
 
