@@ -21,7 +21,7 @@ import torch
 import catalogue_cross_entropy_amd as rece
 import oracle
 from gpu_helpers import grad_err, to_device
-from rece_inputs import WORKLOADS, make_inputs
+from rece_inputs import WORKLOADS, make_inputs, scaled
 
 pytestmark = pytest.mark.gpu
 
@@ -179,3 +179,29 @@ def test_sce_full_size_properties():
     assert np.all(lpp[uncovered] == 0.0)
     a, b = _bilinear(dX, dY, Xd, Yd)
     assert abs(a - b) <= 2e-3 * max(abs(a), abs(b), 1e-12)
+
+
+def test_bucketing_ties_on_large_input_decided_in_float64():
+    """Inputs large enough for the multi-fragment bucketing kernel, whose undecided
+    rows go to the float64 list kernel: random vector 1 equals vector 0, so every
+    row whose best vector is one of the two has a zero float32 gap and must get
+    index 0 (lowest index among equal float64 scores, the oracle's rule)."""
+    w = scaled("million", seqs=16, seqlen=256, C=600_000, n_b=64, n_c=64, k=32, rounds=1)
+    inp = make_inputs(w)
+    inp.B[0][:, 1] = inp.B[0][:, 0]
+    X, Y, pos, B = to_device(inp)
+    plan = rece.Plan(w.s, w.C, w.d, w.n_b, w.n_c, w.k, w.rounds, dtype=w.dtype, keep_stages=True,
+                     validate_ids=True)
+    print("[gpu] bucketing ties, C=600000", flush=True)
+    loss, lpp, scratch, saved = plan.forward(X, Y, pos, B)
+    plan.check(saved)
+    by = plan.export(saved, "bucket_y", 0).cpu().numpy()
+    cnt = plan.export(saved, "counters").cpu().numpy()
+    torch.cuda.synchronize()
+    assert not np.any(by == 1)                 # the duplicate never wins
+    rng = np.random.default_rng(11)
+    tied = np.flatnonzero(by == 0)
+    assert len(tied) > 1000                    # about 1 in 32 items
+    sy = np.concatenate([rng.choice(tied, 256, replace=False), rng.choice(w.C, 2048, replace=False)])
+    assert np.array_equal(by[sy], oracle.bucket_ids(inp.Y[sy], inp.B[0]))
+    assert cnt[1] >= len(tied)                 # each of them went through the float64 decision
