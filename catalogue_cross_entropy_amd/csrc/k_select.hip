@@ -39,19 +39,19 @@ constexpr int MAX_REFINE = 2;    // histogram passes that may split a crowded bi
 constexpr float X_TOP = 255.99998f;   // largest histogram coordinate (below 256)
 constexpr float LOG2E_F = 1.44269504088896341f;
 
-// Per-wave LDS region.
-constexpr int WLIST = 128;   // near-tie entries of one wave awaiting float64 values
+// Per-wave LDS region.  WL: near-tie entries of one wave awaiting float64 values
+// (128; 64 for 512-byte vectors, whose workgroups need the room to fit two per CU).
 
 struct WaveLds {
   PrevRow* prev;    // [16][rounds - 1]
-  double* ce;       // [WLIST]
+  double* ce;       // [WL]
   uint32_t* hist;   // [16][HIST_STRIDE] two 16-bit counts per word (histogram passes),
                     // aliased by vals/ids (collect pass)
   float* vals;      // [16][LIST_STRIDE] (SEL_CAP used)
   int32_t* ids;     // [16][LIST_STRIDE]
-  int32_t* ci;      // [WLIST] list index in the row's candidate list
-  int32_t* cj;      // [WLIST] item id
-  int32_t* cr;      // [WLIST] row
+  int32_t* ci;      // [WL] list index in the row's candidate list
+  int32_t* cj;      // [WL] item id
+  int32_t* cr;      // [WL] row
   float* rf;        // [16][8] per-row floats
   int32_t* ri;      // [16][8] per-row ints
 };
@@ -65,28 +65,28 @@ constexpr size_t WAVE_UNION = (size_t)16 * HIST_STRIDE * 4 > (size_t)16 * LIST_S
                                   : (size_t)16 * LIST_STRIDE * 8;
 // earlier-round thresholds cached per row: rounds - 1 of them (at least one slot)
 __host__ __device__ constexpr int nprev_of(int rounds) { return rounds > 1 ? rounds - 1 : 1; }
-__host__ __device__ constexpr size_t wave_lds_bytes(int rounds) {
-  return 16 * (size_t)nprev_of(rounds) * sizeof(PrevRow) + WLIST * 8 + WAVE_UNION + WLIST * (4 + 4 + 4) +
+__host__ __device__ constexpr size_t wave_lds_bytes(int rounds, int wl) {
+  return 16 * (size_t)nprev_of(rounds) * sizeof(PrevRow) + (size_t)wl * 8 + WAVE_UNION + (size_t)wl * (4 + 4 + 4) +
          16 * 8 * 4 + 16 * 8 * 4;
 }
 
-__device__ inline WaveLds carve(char* base, int rounds) {
+__device__ inline WaveLds carve(char* base, int rounds, int wl) {
   WaveLds L;
   char* p = base;
   L.prev = reinterpret_cast<PrevRow*>(p);
   p += 16 * (size_t)nprev_of(rounds) * sizeof(PrevRow);
   L.ce = reinterpret_cast<double*>(p);
-  p += WLIST * 8;
+  p += (size_t)wl * 8;
   L.hist = reinterpret_cast<uint32_t*>(p);
   L.vals = reinterpret_cast<float*>(p);
   L.ids = reinterpret_cast<int32_t*>(p + 16 * LIST_STRIDE * 4);
   p += WAVE_UNION;
   L.ci = reinterpret_cast<int32_t*>(p);
-  p += WLIST * 4;
+  p += (size_t)wl * 4;
   L.cj = reinterpret_cast<int32_t*>(p);
-  p += WLIST * 4;
+  p += (size_t)wl * 4;
   L.cr = reinterpret_cast<int32_t*>(p);
-  p += WLIST * 4;
+  p += (size_t)wl * 4;
   L.rf = reinterpret_cast<float*>(p);
   p += 16 * 8 * 4;
   L.ri = reinterpret_cast<int32_t*>(p);
@@ -101,14 +101,22 @@ enum { RI_I = 0, RI_KK = 1, RI_NSURE = 2, RI_NNEW = 3, RI_NABOVE = 4, RI_AOFF = 
 __host__ __device__ constexpr size_t sel_slot_bytes(size_t row_bytes, int rounds) {
   return row_bytes + 256 * (size_t)rounds;
 }
-__host__ __device__ constexpr size_t sel_common_lds(size_t row_bytes, int rounds) {
-  return 3 * sel_slot_bytes(row_bytes, rounds) + 16;
+__host__ __device__ constexpr size_t sel_common_lds(size_t row_bytes, int rounds, int ring) {
+  return (size_t)ring * sel_slot_bytes(row_bytes, rounds) + 16;
 }
+
+// Ring slots (tiles in flight: RING - 1) and near-tie batch: 512-byte vectors
+// take a two-slot ring and a 64-entry batch, so that two workgroups share a CU.
+template <class E, int D> struct SelGeom {
+  static constexpr bool WIDE = D * (int)sizeof(E) >= 512;
+  static constexpr int RING = WIDE ? 2 : 3;
+  static constexpr int WL = WIDE ? 64 : 128;
+};
 
 // NEGS: the kept ids are written out (p.negs set); a template flag keeps that
 // code out of the streaming loop when they are not.
 template <class E, int D, int NW, bool NEGS>
-__global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 256) ? 2 : 1) void k_select(SelectArgs p) {
+__global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 512) ? 2 : 1) void k_select(SelectArgs p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   using G = TileGeom<E, D>;
   constexpr int TI = G::TI;
@@ -122,10 +130,11 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 256) ? 2 : 1) void k_sel
   const int64_t s = p.s, C = p.C;
   const size_t slot_bytes = sel_slot_bytes(G::ROW_BYTES, p.rounds);
   char* ring = smem;
-  int32_t* wg_flag = reinterpret_cast<int32_t*>(smem + 3 * slot_bytes);
+  constexpr int RING = SelGeom<E, D>::RING, WLIST = SelGeom<E, D>::WL;
+  int32_t* wg_flag = reinterpret_cast<int32_t*>(smem + RING * slot_bytes);
   const int w = threadIdx.x >> 6, l = lane_id(), g = l >> 4;
-  WaveLds L = carve(smem + sel_common_lds(G::ROW_BYTES, p.rounds) + (size_t)w * wave_lds_bytes(p.rounds),
-                    p.rounds);
+  WaveLds L = carve(smem + sel_common_lds(G::ROW_BYTES, p.rounds, RING) + (size_t)w * wave_lds_bytes(p.rounds, WLIST),
+                    p.rounds, WLIST);
   const int NP = nprev_of(p.rounds);
   (void)X;
   uint32_t nexact = 0;   // float64 logits computed by this lane
@@ -213,15 +222,18 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 256) ? 2 : 1) void k_sel
     if (mode == 0)
       for (int b = l; b < 16 * HIST_STRIDE; b += WAVE) L.hist[b] = 0u;
     __syncthreads();
-    issue_window_tile<E, D, NW>(ring, slot_bytes, win, 0, Ys, p.perm_y, p.cyp, C, rho, w);
-    if (ntiles > 1) issue_window_tile<E, D, NW>(ring, slot_bytes, win, 1, Ys, p.perm_y, p.cyp, C, rho, w);
+    issue_window_tile<E, D, NW, RING>(ring, slot_bytes, win, 0, Ys, p.perm_y, p.cyp, C, rho, w);
+    if (RING == 3 && ntiles > 1)
+      issue_window_tile<E, D, NW, RING>(ring, slot_bytes, win, 1, Ys, p.perm_y, p.cyp, C, rho, w);
 
     for (int t = 0; t < ntiles; ++t) {
-      wait_vmcnt(t + 1 < ntiles ? my_copies : 0);
-      raw_barrier();
-      if (t + 2 < ntiles) issue_window_tile<E, D, NW>(ring, slot_bytes, win, t + 2, Ys, p.perm_y, p.cyp, C, rho, w);
+      // tile t's copies are complete once only those of later tiles remain outstanding
+      wait_vmcnt(RING == 3 && t + 1 < ntiles ? my_copies : 0);
+      raw_barrier();   // every wave's copies of tile t landed; slot (t + RING - 1) % RING is free
+      if (t + RING - 1 < ntiles)
+        issue_window_tile<E, D, NW, RING>(ring, slot_bytes, win, t + RING - 1, Ys, p.perm_y, p.cyp, C, rho, w);
       const int64_t q0 = range_tile_start(win, t, TI), q1 = range_tile_end(win, t);
-      const char* slot = ring + (size_t)(t % 3) * slot_bytes;
+      const char* slot = ring + (size_t)(t % RING) * slot_bytes;
       const int32_t* tid_ = reinterpret_cast<const int32_t*>(slot + G::ROW_BYTES);
       const int32_t* tcy = tid_ + 64;
       const int nlim = (int)(q1 - q0);   // valid items of this tile
@@ -667,7 +679,8 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 256) ? 2 : 1) void k_sel
 
 template <class E, int D>
 static size_t select_lds_bytes_t(int waves, int rounds) {
-  return sel_common_lds(TileGeom<E, D>::ROW_BYTES, rounds) + (size_t)waves * wave_lds_bytes(rounds);
+  return sel_common_lds(TileGeom<E, D>::ROW_BYTES, rounds, SelGeom<E, D>::RING) +
+         (size_t)waves * wave_lds_bytes(rounds, SelGeom<E, D>::WL);
 }
 size_t select_lds_bytes(bool is_bf16, int d, int waves, int rounds) {
 #define RECE_L(E, DD) \

@@ -212,14 +212,14 @@ __device__ __forceinline__ int64_t range_tile_end(Ranges r, int t) {
 }
 
 // Issue the copies of window tile t (rows from `rows_src`, then 64 ids from
-// `ids_src`, then `nmaps` chunk maps of C ints from `maps_src`) into ring slot t % 3.
-template <class E, int D, int NW>
+// `ids_src`, then `nmaps` chunk maps of C ints from `maps_src`) into ring slot t % RING.
+template <class E, int D, int NW, int RING = 3>
 __device__ __forceinline__ void issue_window_tile(char* ring, size_t slot_bytes, Ranges r, int t,
                                                   const E* rows_src, const int32_t* ids_src,
                                                   const int32_t* maps_src, int64_t map_len, int nmaps, int wave) {
   using G = TileGeom<E, D>;
   const int64_t q0 = range_tile_start(r, t, G::TI), q1 = range_tile_end(r, t);
-  char* slot = ring + (size_t)(t % 3) * slot_bytes;
+  char* slot = ring + (size_t)(t % RING) * slot_bytes;
   dma_rows<E, D, NW>(slot, rows_src, q0, q1, wave);
   const int ncopies = G::ROW_DMA + 1 + nmaps;
   for (int u = G::ROW_DMA + ((wave - G::ROW_DMA % NW + NW) % NW); u < ncopies; u += NW) {
