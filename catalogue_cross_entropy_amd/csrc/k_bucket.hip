@@ -27,6 +27,18 @@ hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Zero three small regions in one launch (block y = region).
+__global__ void k_zero3(uint32_t* a, int na, uint32_t* b, int nb, uint32_t* c, int nc) {
+  uint32_t* p = blockIdx.y == 0 ? a : (blockIdx.y == 1 ? b : c);
+  const int n = blockIdx.y == 0 ? na : (blockIdx.y == 1 ? nb : nc);
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
+}
+
+hipError_t launch_zero3(uint32_t* a, int na, uint32_t* b, int nb, uint32_t* c, int nc, hipStream_t st) {
+  hipLaunchKernelGGL(k_zero3, dim3(1, 3), dim3(256), 0, st, a, na, b, nb, c, nc);
+  return hipGetLastError();
+}
+
 // Bt[rho][b][t] = B[rho][t][b]; bnorm_max[rho] = max_b ||b_b||_2 (rounded up).
 // bnorm_max must be zero on entry.
 template <class E>
@@ -55,8 +67,10 @@ __global__ void k_prep_b(const E* __restrict__ B, int d, int n_b, E* __restrict_
 
 hipError_t launch_prep_b(bool is_bf16, int d, const void* B, int rounds, int n_b, void* Bt, float* bnorm_max,
                          int zero_words, hipStream_t st) {
-  // bnorm_max[0 .. rounds) and the zero_words following it are cleared
-  hipError_t e = launch_fill_u32(reinterpret_cast<uint32_t*>(bnorm_max), 0u, rounds + zero_words, st);
+  // bnorm_max[0 .. rounds) and the zero_words following it are cleared (zero_words < 0:
+  // the caller has cleared them)
+  hipError_t e = zero_words < 0 ? hipSuccess
+                                : launch_fill_u32(reinterpret_cast<uint32_t*>(bnorm_max), 0u, rounds + zero_words, st);
   if (e != hipSuccess) return e;
   dim3 grid((n_b + 255) / 256, rounds);
   if (is_bf16)

@@ -560,8 +560,8 @@ rece_status rece_plan(const rece_config* cfg, rece_plan_t* out) {
   p->o_bt = sc.take((size_t)r * c.n_b * d * p->esize);
   p->o_bnorm = sc.take((size_t)r * 4 + (size_t)2 * r * 4);   // norms, then one list counter per bucketing launch
   p->o_und = sc.take((size_t)s * 4);    // undecided bucketing rows: positions,
-  p->o_undy = sc.take((size_t)C * 4);   // items (the item chain runs on the side stream)
-  p->o_sorty = sc.take(sort_scratch_bytes(C, 1 << p->nbits_b));
+  p->o_undy = sc.take((size_t)std::max(s, C) * 4);   // chains on the side stream (items, later positions)
+  p->o_sorty = sc.take(std::max(sort_scratch_bytes(C, 1 << p->nbits_b), sort_scratch_bytes(s, 1 << p->nbits_b)));
   const size_t sort_b = std::max({sort_scratch_bytes(s, 1 << p->nbits_b), sort_scratch_bytes(C, 1 << p->nbits_b),
                                   sort_scratch_bytes(s, 1 << std::min(12, bits_for(C)))});
   p->o_sort = sc.take(sort_b);
@@ -658,11 +658,13 @@ rece_status rece_forward(rece_plan_t plan, void* stream, const void* X, const vo
 
   if (c.variant == RECE_VARIANT_SCE) return sce_forward(p, st, X, Y, pos, B, sc, sv, loss, loss_pp);
   std::lock_guard<std::mutex> side_lock(p.side.mu);
-  RECE_PHASE(RECE_PHASE_OTHER, launch_fill_u32(counters, 0u, NUM_COUNTERS, st), "clear counters");
-  RECE_PHASE(RECE_PHASE_OTHER, launch_fill_u32(reinterpret_cast<uint32_t*>(ymax), 0u, 1, st), "clear norm max");
   uint32_t* und_n = reinterpret_cast<uint32_t*>(bnorm + c.rounds);   // cleared with the norms
   int32_t* und = reinterpret_cast<int32_t*>(sc + p.o_und);
-  RECE_PHASE(RECE_PHASE_OTHER, launch_prep_b(p.bf16, d, B, c.rounds, c.n_b, Bt, bnorm, 2 * c.rounds, st),
+  RECE_PHASE(RECE_PHASE_OTHER,
+             launch_zero3(counters, NUM_COUNTERS, reinterpret_cast<uint32_t*>(ymax), 1,
+                          reinterpret_cast<uint32_t*>(bnorm), 3 * c.rounds, st),
+             "clear counters and maxima");
+  RECE_PHASE(RECE_PHASE_OTHER, launch_prep_b(p.bf16, d, B, c.rounds, c.n_b, Bt, bnorm, -1, st),
              "prepare random vectors");
 
   // Item chain of every round (bucketing, sort, sorted copy, earlier-round chunks)
@@ -694,6 +696,19 @@ rece_status rece_forward(rece_plan_t plan, void* stream, const void* X, const vo
                  launch_prev_chunks(py, reinterpret_cast<const int32_t*>(sv + p.o_iy) + (int64_t)r2 * C, C, c.n_c,
                                     cyp + (int64_t)r2 * C, st),
                  "earlier-round chunks");
+    if (rho > 0) {
+      // the position chain of later rounds too (it does not wait for earlier chunk kernels)
+      int32_t* bx = reinterpret_cast<int32_t*>(sv + p.o_bx) + (int64_t)rho * s;
+      int32_t* px = reinterpret_cast<int32_t*>(sv + p.o_px) + (int64_t)rho * s;
+      int32_t* ix = reinterpret_cast<int32_t*>(sv + p.o_ix) + (int64_t)rho * s;
+      RECE_PHASE(RECE_PHASE_PROJECT, launch_project_argmax(p.bf16, d, X, s, Btr, c.n_b, bnorm + rho, p.beta_coef,
+                                     bx, nullptr, nullptr, undy, und_n + 2 * rho, counters, st),
+                 "bucket positions");
+      RECE_PHASE(RECE_PHASE_SORT, launch_counting_sort(bx, nullptr, s, 0, p.nbits_b, sc + p.o_sorty, px, ix, st),
+                 "sort positions");
+      char* xs = sv + p.o_xs + (size_t)rho * s * d * p.esize;
+      RECE_PHASE(RECE_PHASE_SORT, launch_gather_rows(X, px, s, d * p.esize, xs, st), "sorted positions");
+    }
     RECE_HIP(hipEventRecord(p.side.fork[rho], side), "item chain done");
   }
 
@@ -702,17 +717,19 @@ rece_status rece_forward(rece_plan_t plan, void* stream, const void* X, const vo
     int32_t* px = reinterpret_cast<int32_t*>(sv + p.o_px) + (int64_t)rho * s;
     int32_t* ix = reinterpret_cast<int32_t*>(sv + p.o_ix) + (int64_t)rho * s;
     int32_t* py = reinterpret_cast<int32_t*>(sv + p.o_py) + (int64_t)rho * C;
-    const void* Btr = static_cast<const char*>(Bt) + (size_t)rho * c.n_b * d * p.esize;
-    RECE_PHASE(RECE_PHASE_PROJECT, launch_project_argmax(p.bf16, d, X, s, Btr, c.n_b, bnorm + rho, p.beta_coef, bx,
-                                   rho == 0 ? xnorm : nullptr, nullptr, und, und_n + 2 * rho, counters, st),
-             "bucket positions");
-    RECE_PHASE(RECE_PHASE_SORT, launch_counting_sort(bx, nullptr, s, 0, p.nbits_b, sc + p.o_sort, px, ix, st),
-               "sort positions");
     char* xs = sv + p.o_xs + (size_t)rho * s * d * p.esize;
     char* ys = sv + p.o_ys + (size_t)rho * C * d * p.esize;
     int32_t* cyp = reinterpret_cast<int32_t*>(sv + p.o_cyp) + (int64_t)(rho * (rho - 1) / 2) * C;
-    RECE_PHASE(RECE_PHASE_SORT, launch_gather_rows(X, px, s, d * p.esize, xs, st), "sorted positions");
-    RECE_HIP(hipStreamWaitEvent(st, p.side.fork[rho], 0), "join item chain");
+    if (rho == 0) {   // round 0's position chain here, alongside the first item chain
+      const void* Btr = Bt;
+      RECE_PHASE(RECE_PHASE_PROJECT, launch_project_argmax(p.bf16, d, X, s, Btr, c.n_b, bnorm, p.beta_coef, bx,
+                                     xnorm, nullptr, und, und_n, counters, st),
+                 "bucket positions");
+      RECE_PHASE(RECE_PHASE_SORT, launch_counting_sort(bx, nullptr, s, 0, p.nbits_b, sc + p.o_sort, px, ix, st),
+                 "sort positions");
+      RECE_PHASE(RECE_PHASE_SORT, launch_gather_rows(X, px, s, d * p.esize, xs, st), "sorted positions");
+    }
+    RECE_HIP(hipStreamWaitEvent(st, p.side.fork[rho], 0), "join item and position chains");
 
     SelectArgs a{};
     a.X = X;

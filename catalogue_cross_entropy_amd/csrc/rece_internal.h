@@ -115,7 +115,10 @@ struct BwdArgs {
 
 // Launchers (defined in the .hip files).  All enqueue on `st`.
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t st);
-// bnorm_max[0 .. rounds) and the zero_words 32-bit words after it are cleared first.
+// a[0..na), b[0..nb), c[0..nc) = 0 in one launch (each region at most a few thousand words).
+hipError_t launch_zero3(uint32_t* a, int na, uint32_t* b, int nb, uint32_t* c, int nc, hipStream_t st);
+// bnorm_max[0 .. rounds) and the zero_words 32-bit words after it are cleared first
+// (zero_words < 0: already cleared by the caller).
 hipError_t launch_prep_b(bool is_bf16, int d, const void* B, int rounds, int n_b, void* Bt, float* bnorm_max,
                          int zero_words, hipStream_t st);
 // und: room for n row ids; und_n: a zero counter (rows whose float32 decision is
