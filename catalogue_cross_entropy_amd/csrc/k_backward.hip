@@ -402,10 +402,19 @@ constexpr int PIECE = 64;   // sorted positions per piece (one wave)
 
 // pflag bits per piece: 1 = head run continues from the previous piece,
 // 2 = head run continues into the next piece, 4 = a tail run starts here and continues.
+// Runs that neither come from the previous piece nor continue into the next are
+// staged (item and row) and added to dY by k_pos_combine: the pieces kernel reads
+// and writes nothing of dY, so it can run while dY is still being written.
+struct PosStage {
+  int32_t* n;       // [npieces] staged runs of each piece
+  int32_t* items;   // [npieces * PIECE]
+  float* rows;      // [npieces * PIECE][D]
+};
+
 template <class E, int D>
 __global__ __launch_bounds__(256) void k_pos_pieces(BwdArgs p, const int32_t* __restrict__ sorted,
                                                     float* __restrict__ partial, int32_t* __restrict__ pitem,
-                                                    int32_t* __restrict__ pflag, int64_t npieces) {
+                                                    int32_t* __restrict__ pflag, PosStage stage, int64_t npieces) {
   constexpr int PER = (D + 63) / 64;   // coordinates per lane
   const E* __restrict__ X = reinterpret_cast<const E*>(p.X);
   const int w = threadIdx.x >> 6, l = lane_id();
@@ -418,6 +427,7 @@ __global__ __launch_bounds__(256) void k_pos_pieces(BwdArgs p, const int32_t* __
   for (int u = 0; u < PER; ++u) acc[u] = 0.0f;
   int flags = 0;
   int head_item = -1, tail_item = -1;
+  int nstage = 0;
   const int prev_item = t0 > 0 ? p.pos[sorted[t0 - 1]] : -1;
   const int next_item = t1 < s ? p.pos[sorted[t1]] : -1;
   // lane e holds sorted position t0 + e: its id, positive item and coefficient (all
@@ -452,10 +462,11 @@ __global__ __launch_bounds__(256) void k_pos_pieces(BwdArgs p, const int32_t* __
           for (int u = 0; u < PER; ++u)
             if (l + 64 * u < D) partial[(piece * 2 + 0) * D + l + 64 * u] = acc[u];
         } else if (cur >= 0 && cur < p.C) {
-          float* dst = p.dY + (int64_t)cur * D;
+          const int64_t slot = piece * PIECE + nstage++;
+          if (l == 0) stage.items[slot] = cur;
 #pragma unroll
           for (int u = 0; u < PER; ++u)
-            if (l + 64 * u < D) dst[l + 64 * u] += acc[u];
+            if (l + 64 * u < D) stage.rows[slot * D + l + 64 * u] = acc[u];
         }
 #pragma unroll
         for (int u = 0; u < PER; ++u) acc[u] = 0.0f;
@@ -484,28 +495,58 @@ __global__ __launch_bounds__(256) void k_pos_pieces(BwdArgs p, const int32_t* __
     for (int u = 0; u < PER; ++u)
       if (l + 64 * u < D) partial[(piece * 2 + 1) * D + l + 64 * u] = acc[u];
   } else if (cur >= 0 && cur < p.C) {
-    float* dst = p.dY + (int64_t)cur * D;
+    const int64_t slot = piece * PIECE + nstage++;
+    if (l == 0) stage.items[slot] = cur;
 #pragma unroll
     for (int u = 0; u < PER; ++u)
-      if (l + 64 * u < D) dst[l + 64 * u] += acc[u];
+      if (l + 64 * u < D) stage.rows[slot * D + l + 64 * u] = acc[u];
   }
   if (l == 0) {
     pitem[piece * 2 + 0] = head_item;
     pitem[piece * 2 + 1] = tail_item;
     pflag[piece] = flags;
+    stage.n[piece] = nstage;
   }
 }
 
-// A run that starts in piece q and continues: add the head partials of the
-// following pieces, in order, until the run ends.
+// Per piece: add its staged runs to dY (each item's positions form one run, so
+// no other wave writes those rows); then, for a run that starts in this piece and
+// continues, add the head partials of the following pieces, in order, until the
+// run ends.
 template <int D>
 __global__ __launch_bounds__(256) void k_pos_combine(float* __restrict__ dY, const float* __restrict__ partial,
                                                      const int32_t* __restrict__ pitem,
-                                                     const int32_t* __restrict__ pflag, int64_t npieces) {
+                                                     const int32_t* __restrict__ pflag, PosStage stage,
+                                                     int64_t npieces) {
   constexpr int PER = (D + 63) / 64;
   const int w = threadIdx.x >> 6, l = lane_id();
   const int64_t piece = (int64_t)blockIdx.x * 4 + w;
   if (piece >= npieces) return;
+  {
+    const int ns = stage.n[piece];
+    constexpr int BATCH = 8;
+    for (int e0 = 0; e0 < ns; e0 += BATCH) {
+      float rv[BATCH][PER], yv[BATCH][PER];
+      int64_t base[BATCH];
+#pragma unroll
+      for (int e = 0; e < BATCH; ++e) {
+        const bool in = e0 + e < ns;
+        const int64_t slot = piece * PIECE + e0 + (in ? e : 0);
+        base[e] = (int64_t)stage.items[slot] * D;
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+          const bool ok = in && l + 64 * u < D;
+          rv[e][u] = ok ? stage.rows[slot * D + l + 64 * u] : 0.0f;
+          yv[e][u] = ok ? dY[base[e] + l + 64 * u] : 0.0f;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < BATCH; ++e)
+#pragma unroll
+        for (int u = 0; u < PER; ++u)
+          if (e0 + e < ns && l + 64 * u < D) dY[base[e] + l + 64 * u] = yv[e][u] + rv[e][u];
+    }
+  }
   if (!(pflag[piece] & 4)) return;
   const int item = pitem[piece * 2 + 1];
   if (item < 0) return;
@@ -599,22 +640,51 @@ hipError_t launch_bwd_items(bool bf16v, int d, int waves, const BwdArgs& a, int 
   return hipErrorInvalidValue;
 }
 
+// The work area: head/tail partial rows [npieces][2][D] floats, staged rows
+// [npieces * PIECE][D] floats, then pitem [npieces][2], pflag [npieces], staged
+// counts [npieces] and staged items [npieces * PIECE], all int32.
+struct PosArea {
+  float* partial;
+  int32_t* pitem;
+  int32_t* pflag;
+  PosStage stage;
+  int64_t npieces;
+};
+static PosArea pos_area(float* base, int64_t s, int d) {
+  PosArea a;
+  a.npieces = (s + PIECE - 1) / PIECE;
+  a.partial = base;
+  a.stage.rows = base + a.npieces * 2 * d;
+  a.pitem = reinterpret_cast<int32_t*>(a.stage.rows + a.npieces * PIECE * d);
+  a.pflag = a.pitem + a.npieces * 2;
+  a.stage.n = a.pflag + a.npieces;
+  a.stage.items = a.stage.n + a.npieces;
+  return a;
+}
+
 template <class E, int D>
-static hipError_t launch_pos_t(const BwdArgs& a, const int32_t* sorted, float* partial, hipStream_t st) {
-  const int64_t npieces = (a.s + PIECE - 1) / PIECE;
-  int32_t* pitem = reinterpret_cast<int32_t*>(partial + npieces * 2 * D);
-  int32_t* pflag = pitem + npieces * 2;
-  const unsigned blocks = (unsigned)((npieces + 3) / 4);
-  hipLaunchKernelGGL((k_pos_pieces<E, D>), dim3(blocks), dim3(256), 0, st, a, sorted, partial, pitem, pflag,
-                     npieces);
-  hipLaunchKernelGGL((k_pos_combine<D>), dim3(blocks), dim3(256), 0, st, a.dY, partial, pitem, pflag, npieces);
+static hipError_t launch_pieces_t(const BwdArgs& a, const int32_t* sorted, float* area, hipStream_t st) {
+  const PosArea w = pos_area(area, a.s, D);
+  const unsigned blocks = (unsigned)((w.npieces + 3) / 4);
+  hipLaunchKernelGGL((k_pos_pieces<E, D>), dim3(blocks), dim3(256), 0, st, a, sorted, w.partial, w.pitem, w.pflag,
+                     w.stage, w.npieces);
   return hipGetLastError();
 }
 
-hipError_t launch_pos_dy(bool bf16v, int d, const BwdArgs& a, const int32_t* sorted, float* partial,
-                         hipStream_t st) {
+template <int D>
+static hipError_t launch_combine_t(int64_t s, float* dY, float* area, hipStream_t st) {
+  const PosArea w = pos_area(area, s, D);
+  const unsigned blocks = (unsigned)((w.npieces + 3) / 4);
+  hipLaunchKernelGGL((k_pos_combine<D>), dim3(blocks), dim3(256), 0, st, dY, w.partial, w.pitem, w.pflag, w.stage,
+                     w.npieces);
+  return hipGetLastError();
+}
+
+hipError_t launch_pos_pieces(bool bf16v, int d, const BwdArgs& a, const int32_t* sorted, float* area,
+                             hipStream_t st) {
+  if (a.s == 0) return hipSuccess;
 #define RECE_P(E, DD) \
-  if (d == DD) return launch_pos_t<E, DD>(a, sorted, partial, st);
+  if (d == DD) return launch_pieces_t<E, DD>(a, sorted, area, st);
   if (bf16v) {
     RECE_P(bf16, 32) RECE_P(bf16, 64) RECE_P(bf16, 128) RECE_P(bf16, 256)
   } else {
@@ -624,9 +694,27 @@ hipError_t launch_pos_dy(bool bf16v, int d, const BwdArgs& a, const int32_t* sor
   return hipErrorInvalidValue;
 }
 
+hipError_t launch_pos_combine(int d, int64_t s, float* dY, float* area, hipStream_t st) {
+  if (s == 0) return hipSuccess;
+  switch (d) {
+    case 32: return launch_combine_t<32>(s, dY, area, st);
+    case 64: return launch_combine_t<64>(s, dY, area, st);
+    case 128: return launch_combine_t<128>(s, dY, area, st);
+    case 256: return launch_combine_t<256>(s, dY, area, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_pos_dy(bool bf16v, int d, const BwdArgs& a, const int32_t* sorted, float* area,
+                         hipStream_t st) {
+  const hipError_t e = launch_pos_pieces(bf16v, d, a, sorted, area, st);
+  if (e != hipSuccess) return e;
+  return launch_pos_combine(d, a.s, a.dY, area, st);
+}
+
 size_t pos_partial_bytes(int64_t s, int d) {
   const int64_t npieces = (s + PIECE - 1) / PIECE;
-  return (size_t)npieces * 2 * d * 4 + (size_t)npieces * 3 * 4;
+  return (size_t)npieces * (2 + PIECE) * d * 4 + (size_t)npieces * (4 + PIECE) * 4;
 }
 
 }  // namespace rece

@@ -860,8 +860,8 @@ rece_status rece_backward(rece_plan_t plan, void* stream, const void* X, const v
       RECE_PHASE(RECE_PHASE_BWD_DY, launch_bwd_items(p.bf16, d, 4, b, p.itiles, st), "dY");
     }
   }
-  // positives: LSD counting sort of positions by positive id (overlaps the side
-  // stream), then the segmented reduction into dY once the side stream is joined
+  // positives: LSD counting sort of positions by positive id and the per-piece
+  // sums (overlapping the side stream), then, once it is joined, the sums into dY
   int32_t* bufs[2] = {reinterpret_cast<int32_t*>(sc + p.o_pp0), reinterpret_cast<int32_t*>(sc + p.o_pp1)};
   const int total_bits = std::max(1, bits_for(C));
   const int db = sort_digit_bits(s);
@@ -873,10 +873,11 @@ rece_status rece_backward(rece_plan_t plan, void* stream, const void* X, const v
                "sort positives");
     sorted = outp;
   }
+  float* parea = reinterpret_cast<float*>(sc + p.o_ppart);
+  RECE_PHASE(RECE_PHASE_BWD_POS, launch_pos_pieces(p.bf16, d, b, sorted, parea, st), "positive dY");
   RECE_HIP(hipEventRecord(p.side.join, side), "join");
   RECE_HIP(hipStreamWaitEvent(st, p.side.join, 0), "join");
-  RECE_PHASE(RECE_PHASE_BWD_POS, launch_pos_dy(p.bf16, d, b, sorted, reinterpret_cast<float*>(sc + p.o_ppart), st),
-             "positive dY");
+  RECE_PHASE(RECE_PHASE_BWD_POS, launch_pos_combine(d, s, dY, parea, st), "positive dY");
   return RECE_OK;
 }
 

@@ -145,7 +145,12 @@ hipError_t launch_prev_chunks(const int32_t* perm_y, const int32_t* inv_y2, int6
                               hipStream_t st);
 hipError_t launch_bwd_records(const BwdArgs& a, const int32_t* perm_x, int rho, PosRec* rec, PrevRow* prev,
                               hipStream_t st);
-hipError_t launch_pos_dy(bool is_bf16, int d, const BwdArgs& a, const int32_t* pos_perm, float* partial,
+// Positive term of dY: the pieces pass reads X and the sorted positions and writes
+// only the work area; the combine pass adds the work area into dY.
+hipError_t launch_pos_pieces(bool is_bf16, int d, const BwdArgs& a, const int32_t* pos_perm, float* area,
+                             hipStream_t st);
+hipError_t launch_pos_combine(int d, int64_t s, float* dY, float* area, hipStream_t st);
+hipError_t launch_pos_dy(bool is_bf16, int d, const BwdArgs& a, const int32_t* pos_perm, float* area,
                          hipStream_t st);
 
 // Bucket (SCE) variant.
