@@ -71,9 +71,11 @@ def algorithmic_work(w):
     return {
         "project": (2.0 * d * nb * (s + C) * r, r * ((s + C) * (d * es + 4) + nb * d * es)),
         "sort": (0.0, r * (s + C) * 12 + s * 12),
-        "select": (float(ALU_OPS_PER_LOGIT * wl * r), r * ((s + C) * d * es + 8 * (s + C) + state * s)),
+        "select": (float(ALU_OPS_PER_LOGIT * wl * r),
+                   r * ((s + C) * d * es + 8 * (s + C) + state * s + s * w.k * 4)),   # + kept lists
         "loss": (2.0 * d * s, s * (2 * d * es + 12 + 12 * r)),
-        "bwd_dx": (2.0 * d * (w.k * r + 1) * s, r * ((s + C) * d * es + state * s) + s * d * 4),
+        # kept lists, every vector once, per-position state, dX
+        "bwd_dx": (2.0 * d * (w.k * r + 1) * s, r * s * w.k * 4 + (s + C) * d * es + 12 * s + s * d * 4),
         "bwd_dy": (2.0 * d * w.k * r * s, r * ((s + C) * d * es + state * s) + C * d * 4),
         "bwd_pos": (2.0 * d * s, s * (d * es + 16) + s * d * 4),
     }

@@ -2,12 +2,15 @@
 // (RECE page, Section 3, Eq. 4: softmax minus one-hot, restricted to the scored
 // set {positive} u kept negatives; chained through logit = x . y).
 //
-// No list of kept pairs exists: each kernel walks the same chunk windows as the
-// forward pass, recomputes the logits on the matrix cores, and decides
-// membership of a pair against the per-position thresholds saved by the forward
-// pass (float32 bounds first, float64 recomputation inside the bounds).  A pair
-// already kept in an earlier round is skipped, so every kept pair counts once.
-//   * k_bwd_rows: per (X-chunk, position tile), dX += G . Y_window, G the 16x64
+// The position side reads the forward pass's kept lists; the item side has no
+// list by item, so it walks the same chunk windows as the forward pass,
+// recomputes the logits on the matrix cores, and decides membership of a pair
+// against the per-position thresholds saved by the forward pass (float32 bounds
+// first, float64 recomputation inside the bounds).  A pair already kept in an
+// earlier round is skipped, so every kept pair counts once.
+//   * k_dx_lists (RECE): per position, dX = sum over its listed pairs of
+//     gbar exp(logit - lse) y_j plus the positive term: one gathered row per pair;
+//   * k_bwd_rows (bucket variant): per (bucket, position tile), G . Y_window, G the 16x64
 //     gradient block of the tile, kept in registers in the operand layout of the
 //     product (bf16 hi+lo split for bf16 inputs, so G keeps ~16 significant bits;
 //     float32 matrix cores for float32 inputs);
@@ -397,6 +400,119 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 512) ? 2 : 1) void k_bwd
   flush_count(p.counters + CNT_LOGIT_EXACT, nexact);
 }
 
+// ------------------------------------------------------------------ dX from the kept lists
+// Sixteen bytes of a row as floats.
+__device__ __forceinline__ void load16f(const bf16* ptr, float (&v)[8]) {
+  const uint4 u = *reinterpret_cast<const uint4*>(ptr);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    v[2 * t] = __uint_as_float(w[t] << 16);
+    v[2 * t + 1] = __uint_as_float(w[t] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ void load16f(const float* ptr, float (&v)[4]) {
+  const float4 u = *reinterpret_cast<const float4*>(ptr);
+  v[0] = u.x;
+  v[1] = u.y;
+  v[2] = u.z;
+  v[3] = u.w;
+}
+
+// One wave per position i (RECE page, Eq. 4, the position side):
+//   dX_i = sum over the kept pairs (i, j) of every round that no earlier round
+//          kept (list ids >= 0) of gbar_i exp(x_i . y_j - lse_i) y_j
+//        + (exp(lpos_i - lse_i) - 1) gbar_i y_pos.
+// The logit is recomputed in float32 from the two rows the sum reads anyway.
+// Lanes work in groups of LPR, each lane on 16 bytes of a row: group q takes list
+// entry RPI * step + q, UNR steps in flight; at the end the groups' partial rows
+// are added in a fixed order, so the result is bit-reproducible.
+template <class E, int D>
+__global__ __launch_bounds__(256) void k_dx_lists(BwdArgs p) {
+  constexpr int EPL = 16 / (int)sizeof(E);   // elements per lane
+  constexpr int LPR = D / EPL;               // lanes per row
+  constexpr int RPI = WAVE / LPR;            // rows per step
+  constexpr int UNR = RPI >= 4 ? 4 : 8;      // steps in flight
+  static_assert(LPR >= 1 && LPR <= WAVE && (LPR & (LPR - 1)) == 0, "row split");
+  const E* __restrict__ X = reinterpret_cast<const E*>(p.X);
+  const E* __restrict__ Y = reinterpret_cast<const E*>(p.Y);
+  const int l = lane_id();
+  const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (i >= p.s) return;
+  const int q = l / LPR, sub = l % LPR;
+  float x[EPL];
+  load16f(X + i * D + sub * EPL, x);
+  const float lse = p.lse[i];
+  const float gb = gbar_of(p, i);
+  float acc[EPL];
+#pragma unroll
+  for (int t = 0; t < EPL; ++t) acc[t] = 0.0f;
+  const int k = p.k;
+  for (int rho = 0; rho < p.rounds; ++rho) {
+    const int32_t* list = p.negs + ((int64_t)rho * p.s + i) * k;
+    for (int e0 = 0; e0 < k; e0 += WAVE) {
+      const int ent = e0 + l < k ? list[e0 + l] : -1;
+      const uint64_t vm = ballot(ent >= 0);
+      if (!vm) continue;
+      const int nstep = (64 - __builtin_clzll(vm) + RPI - 1) / RPI;   // steps up to the last listed entry
+      for (int t0 = 0; t0 < nstep; t0 += UNR) {
+        float y[UNR][EPL];
+        int jj[UNR];
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+          const int e = (t0 + u) * RPI + q;
+          const int j = __shfl(ent, e < WAVE ? e : 0);
+          jj[u] = (t0 + u < nstep && e < WAVE) ? j : -1;
+          if (jj[u] >= 0) {
+            load16f(Y + (int64_t)jj[u] * D + sub * EPL, y[u]);
+          } else {
+#pragma unroll
+            for (int t = 0; t < EPL; ++t) y[u][t] = 0.0f;
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+          float dot = 0.0f;
+#pragma unroll
+          for (int t = 0; t < EPL; ++t) dot = fmaf(x[t], y[u][t], dot);
+#pragma unroll
+          for (int o = 1; o < LPR; o <<= 1) dot += __shfl_xor(dot, o);
+          const float g = jj[u] >= 0 ? __expf(dot - lse) * gb : 0.0f;
+#pragma unroll
+          for (int t = 0; t < EPL; ++t) acc[t] = fmaf(g, y[u][t], acc[t]);
+        }
+      }
+    }
+  }
+  // the positive term, in group 0
+  if (q == 0) {
+    const int pj = p.pos[i];
+    const int pc = pj < 0 ? 0 : (pj >= p.C ? (int)(p.C - 1) : pj);
+    const float gpos = (expf(p.lpos[i] - lse) - 1.0f) * gb;
+    float yp[EPL];
+    load16f(Y + (int64_t)pc * D + sub * EPL, yp);
+#pragma unroll
+    for (int t = 0; t < EPL; ++t) acc[t] = fmaf(gpos, yp[t], acc[t]);
+  }
+#pragma unroll
+  for (int o = LPR; o < WAVE; o <<= 1)
+#pragma unroll
+    for (int t = 0; t < EPL; ++t) acc[t] += __shfl_xor(acc[t], o);
+  if (q == 0) {
+    float4* dst = reinterpret_cast<float4*>(p.dX + i * D + sub * EPL);
+#pragma unroll
+    for (int t = 0; t < EPL / 4; ++t) dst[t] = float4{acc[4 * t], acc[4 * t + 1], acc[4 * t + 2], acc[4 * t + 3]};
+  }
+}
+
+__global__ void k_strip_mark(const int32_t* __restrict__ src, int64_t n, int32_t* __restrict__ dst) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t < n) {
+    const int v = src[t];
+    dst[t] = v == -1 ? -1 : (v & 0x7FFFFFFF);
+  }
+}
+
 // ------------------------------------------------------------------ dY (positives)
 constexpr int PIECE = 64;   // sorted positions per piece (one wave)
 
@@ -710,6 +826,29 @@ hipError_t launch_pos_dy(bool bf16v, int d, const BwdArgs& a, const int32_t* sor
   const hipError_t e = launch_pos_pieces(bf16v, d, a, sorted, area, st);
   if (e != hipSuccess) return e;
   return launch_pos_combine(d, a.s, a.dY, area, st);
+}
+
+hipError_t launch_dx_lists(bool bf16v, int d, const BwdArgs& a, hipStream_t st) {
+  if (a.s == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((a.s + 3) / 4);
+#define RECE_DXL(E, DD) \
+  if (d == DD) {        \
+    hipLaunchKernelGGL((k_dx_lists<E, DD>), dim3(blocks), dim3(256), 0, st, a); \
+    return hipGetLastError(); \
+  }
+  if (bf16v) {
+    RECE_DXL(bf16, 32) RECE_DXL(bf16, 64) RECE_DXL(bf16, 128) RECE_DXL(bf16, 256)
+  } else {
+    RECE_DXL(float, 32) RECE_DXL(float, 64) RECE_DXL(float, 128) RECE_DXL(float, 256)
+  }
+#undef RECE_DXL
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_strip_mark(const int32_t* src, int64_t n, int32_t* dst, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_strip_mark, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, src, n, dst);
+  return hipGetLastError();
 }
 
 size_t pos_partial_bytes(int64_t s, int d) {

@@ -19,7 +19,9 @@
 // The list then gives the float32 k-th value a_k; the few entries within 2*beta of
 // a_k are recomputed in float64 and ranked (logit desc, id asc).  The k-th kept
 // element (float64 logit, id) is the position's threshold: membership of any
-// later pair is decided against it, so no list of kept pairs is stored.
+// later pair is decided against it.  The kept ids themselves are also written
+// out when asked (NEGS), unordered and -1 padded, an id with bit 31 set marking a
+// pair already kept in an earlier round.
 //
 // Rounds: a pair already kept in an earlier round is skipped (the page's
 // minus-ln(count) rule makes the multiset of copies a set).  Outputs per position
@@ -340,7 +342,7 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 512) ? 2 : 1) void k_sel
               if (sure) {
                 const int slotn = nsure + popc(ms & row_lt);
                 if (slotn < k) {
-                  p.negs[orow * k + slotn] = j;
+                  p.negs[orow * k + slotn] = dup ? (j | (int)0x80000000u) : j;
                   if (p.negl) p.negl[orow * k + slotn] = a;
                 }
               }
@@ -651,7 +653,7 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 512) ? 2 : 1) void k_sel
           if (kept) {
             const int slotn = nsure + popc(km & lanemask_lt());
             if (slotn < k) {
-              p.negs[o * k + slotn] = jraw & 0x7FFFFFFF;
+              p.negs[o * k + slotn] = jraw;
               if (p.negl) p.negl[o * k + slotn] = a;
             }
           }

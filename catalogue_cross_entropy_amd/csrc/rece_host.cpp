@@ -550,7 +550,7 @@ rece_status rece_plan(const rece_config* cfg, rece_plan_t* out) {
   p->o_ymax = sv.take(4);
   p->o_lse = sv.take((size_t)s * 4);
   p->o_lpos = sv.take((size_t)s * 4);
-  p->o_negs = (c.flags & RECE_FLAG_KEEP_STAGES) ? sv.take((size_t)r * s * std::max(k, 1) * 4) : 0;
+  p->o_negs = sv.take((size_t)r * s * std::max(k, 1) * 4);   // kept lists: dX reads them
   p->o_xs = sv.take((size_t)r * s * d * p->esize);
   p->o_ys = sv.take((size_t)r * C * d * p->esize);
   p->o_cyp = sv.take((size_t)std::max(1, r * (r - 1) / 2) * C * 4);
@@ -833,10 +833,13 @@ rece_status rece_backward(rece_plan_t plan, void* stream, const void* X, const v
   b.dY = dY;
   b.counters = reinterpret_cast<uint32_t*>(const_cast<char*>(sv) + p.o_cnt);
   b.rounds = c.rounds;
+  b.negs = reinterpret_cast<const int32_t*>(sv + p.o_negs);
+  b.k = c.k;
   PosRec* recs = reinterpret_cast<PosRec*>(sc + p.o_rec);
   PrevRow* prevs = reinterpret_cast<PrevRow*>(sc + p.o_prev);
-  // dX (rounds in order) stays on the caller's stream; dY (rounds in order) runs on
-  // the side stream, each round after its records; the positive term joins them
+  // dY (rounds in order) runs on the side stream, each round after its records;
+  // dX (from the kept lists) and the positive sums stay on the caller's stream;
+  // the positive term of dY joins them
   const rece_status ss = ensure_side(p, c.rounds);
   if (ss != RECE_OK) return ss;
   hipStream_t side = p.side.s;
@@ -853,13 +856,13 @@ rece_status rece_backward(rece_plan_t plan, void* stream, const void* X, const v
                                                     prevs + (int64_t)(rho * (rho - 1) / 2) * s, st),
                "backward records");
     RECE_HIP(hipEventRecord(p.side.fork[rho], st), "fork");
-    RECE_PHASE(RECE_PHASE_BWD_DX, launch_bwd_rows(p.bf16, d, 4, b, st), "dX");
     RECE_HIP(hipStreamWaitEvent(side, p.side.fork[rho], 0), "fork");
     {
       hipStream_t st = side;
       RECE_PHASE(RECE_PHASE_BWD_DY, launch_bwd_items(p.bf16, d, 4, b, p.itiles, st), "dY");
     }
   }
+  RECE_PHASE(RECE_PHASE_BWD_DX, launch_dx_lists(p.bf16, d, b, st), "dX");
   // positives: LSD counting sort of positions by positive id and the per-piece
   // sums (overlapping the side stream), then, once it is joined, the sums into dY
   int32_t* bufs[2] = {reinterpret_cast<int32_t*>(sc + p.o_pp0), reinterpret_cast<int32_t*>(sc + p.o_pp1)};
@@ -908,7 +911,7 @@ rece_status rece_export_bytes(rece_plan_t plan, int stage, size_t* bytes) {
       *bytes = (size_t)c.s * 8;
       break;
     case RECE_STAGE_NEG_IDS:
-      *bytes = plan->o_negs ? (size_t)c.s * std::max(c.k, 1) * 4 : 0;
+      *bytes = (plan->o_negs && (c.flags & RECE_FLAG_KEEP_STAGES)) ? (size_t)c.s * std::max(c.k, 1) * 4 : 0;
       break;
     case RECE_STAGE_COUNTERS:
       *bytes = NUM_COUNTERS * 4;
@@ -945,6 +948,12 @@ rece_status rece_export(rece_plan_t plan, void* stream, const void* saved, int s
     case RECE_STAGE_SCE_ROWS: off = p.o_R; break;
     case RECE_STAGE_SCE_ITEMS: off = p.o_Q; break;
     default: return fail(RECE_ERR_INVALID_ARGUMENT, "unknown stage");
+  }
+  if (stage == RECE_STAGE_NEG_IDS) {   // ids without the earlier-round mark
+    RECE_HIP(launch_strip_mark(reinterpret_cast<const int32_t*>(sv + off), (int64_t)(bytes / 4),
+                               static_cast<int32_t*>(dst), reinterpret_cast<hipStream_t>(stream)),
+             "export");
+    return RECE_OK;
   }
   RECE_HIP(hipMemcpyAsync(dst, sv + off, bytes, hipMemcpyDeviceToDevice, reinterpret_cast<hipStream_t>(stream)),
            "export");

@@ -49,7 +49,7 @@ struct SelectArgs {
   float* mshift;              // [rounds][s]
   float* ssum;                // [rounds][s]
   int32_t* nmem;              // [rounds][s]
-  int32_t* negs;              // [rounds][s][k] or nullptr
+  int32_t* negs;              // [rounds][s][k] kept ids (bit 31: kept in an earlier round; -1 pad) or nullptr
   float* negl;                // [s][k] float32 logits of negs, or nullptr
   int slot_out;               // 1: outputs indexed by sorted slot, not by position id
   int nwin;                   // window chunks: 3 (c-1, c, c+1) or 1 (c only)
@@ -111,6 +111,8 @@ struct BwdArgs {
   const int32_t* sce_inv;     // [slots] index of each slot in sce_sorted
   const uint32_t* qbits;      // [n_b][qwords] bit j: item j taken by the bucket
   int64_t qwords;
+  const int32_t* negs;        // [rounds][s][k] kept ids of the forward pass (dX from the lists)
+  int k;
 };
 
 // Launchers (defined in the .hip files).  All enqueue on `st`.
@@ -136,6 +138,11 @@ size_t select_lds_bytes(bool is_bf16, int d, int waves, int cap);
 int ce_blocks(int64_t s);
 hipError_t launch_ce(bool is_bf16, int d, const CeArgs& a, float* loss, hipStream_t st);
 hipError_t launch_bwd_rows(bool is_bf16, int d, int waves, const BwdArgs& a, hipStream_t st);
+// dX of every position from the kept lists of all rounds plus the positive term
+// (writes all s rows of dX).
+hipError_t launch_dx_lists(bool is_bf16, int d, const BwdArgs& a, hipStream_t st);
+// dst[0..n) = src[0..n) with bit 31 cleared, -1 kept (exported kept lists).
+hipError_t launch_strip_mark(const int32_t* src, int64_t n, int32_t* dst, hipStream_t st);
 hipError_t launch_bwd_items(bool is_bf16, int d, int waves, const BwdArgs& a, int item_tiles_per_chunk,
                             hipStream_t st);
 size_t pos_partial_bytes(int64_t s, int d);
