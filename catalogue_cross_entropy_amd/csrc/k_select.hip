@@ -20,12 +20,15 @@
 // a_k are recomputed in float64 and ranked (logit desc, id asc).  The k-th kept
 // element (float64 logit, id) is the position's threshold: membership of any
 // later pair is decided against it.  The kept ids themselves are also written
-// out when asked (NEGS), unordered and -1 padded, an id with bit 31 set marking a
-// pair already kept in an earlier round.
+// out when asked (NEGS), unordered and -1 padded, with their float32 logits when
+// asked (negl).
 //
-// Rounds: a pair already kept in an earlier round is skipped (the page's
-// minus-ln(count) rule makes the multiset of copies a set).  Outputs per position
-// and round: the threshold and the sum of exp(logit - shift) over the new pairs.
+// Rounds: every round selects on its own window; which of its kept pairs were
+// already kept in an earlier round (the page's minus-ln(count) rule makes the
+// multiset of copies a set) does not change its selection, only which pairs its
+// sum counts, so that is settled afterwards from the kept lists (k_round_dedup)
+// and the rounds need not wait for one another.  Outputs per position and round:
+// the threshold and the sum of exp(logit - shift) over the kept pairs.
 #include <type_traits>
 
 #include "rece_device.h"
@@ -45,7 +48,6 @@ constexpr float LOG2E_F = 1.44269504088896341f;
 // (128; 64 for 512-byte vectors, whose workgroups need the room to fit two per CU).
 
 struct WaveLds {
-  PrevRow* prev;    // [16][rounds - 1]
   double* ce;       // [WL]
   uint32_t* hist;   // [16][HIST_STRIDE] two 16-bit counts per word (histogram passes),
                     // aliased by vals/ids (collect pass)
@@ -65,18 +67,13 @@ constexpr int LIST_STRIDE = SEL_CAP + 4;
 constexpr size_t WAVE_UNION = (size_t)16 * HIST_STRIDE * 4 > (size_t)16 * LIST_STRIDE * 8
                                   ? (size_t)16 * HIST_STRIDE * 4
                                   : (size_t)16 * LIST_STRIDE * 8;
-// earlier-round thresholds cached per row: rounds - 1 of them (at least one slot)
-__host__ __device__ constexpr int nprev_of(int rounds) { return rounds > 1 ? rounds - 1 : 1; }
-__host__ __device__ constexpr size_t wave_lds_bytes(int rounds, int wl) {
-  return 16 * (size_t)nprev_of(rounds) * sizeof(PrevRow) + (size_t)wl * 8 + WAVE_UNION + (size_t)wl * (4 + 4 + 4) +
-         16 * 8 * 4 + 16 * 8 * 4;
+__host__ __device__ constexpr size_t wave_lds_bytes(int wl) {
+  return (size_t)wl * 8 + WAVE_UNION + (size_t)wl * (4 + 4 + 4) + 16 * 8 * 4 + 16 * 8 * 4;
 }
 
-__device__ inline WaveLds carve(char* base, int rounds, int wl) {
+__device__ inline WaveLds carve(char* base, int wl) {
   WaveLds L;
   char* p = base;
-  L.prev = reinterpret_cast<PrevRow*>(p);
-  p += 16 * (size_t)nprev_of(rounds) * sizeof(PrevRow);
   L.ce = reinterpret_cast<double*>(p);
   p += (size_t)wl * 8;
   L.hist = reinterpret_cast<uint32_t*>(p);
@@ -98,13 +95,10 @@ __device__ inline WaveLds carve(char* base, int rounds, int wl) {
 enum { RF_BETA = 0, RF_MX = 1, RF_SEXP = 2, RF_THI = 3, RF_NBUF = 4, RF_ALO = 5, RF_AHI = 6 };
 enum { RI_I = 0, RI_KK = 1, RI_NSURE = 2, RI_NNEW = 3, RI_NABOVE = 4, RI_AOFF = 5, RI_NA = 6, RI_MODE = 7 };
 
-// One ring slot: the tile's rows, then 64 item ids, then for each earlier round
-// 64 chunk indices of those items in that round.
-__host__ __device__ constexpr size_t sel_slot_bytes(size_t row_bytes, int rounds) {
-  return row_bytes + 256 * (size_t)rounds;
-}
-__host__ __device__ constexpr size_t sel_common_lds(size_t row_bytes, int rounds, int ring) {
-  return (size_t)ring * sel_slot_bytes(row_bytes, rounds) + 16;
+// One ring slot: the tile's rows, then 64 item ids.
+__host__ __device__ constexpr size_t sel_slot_bytes(size_t row_bytes) { return row_bytes + 256; }
+__host__ __device__ constexpr size_t sel_common_lds(size_t row_bytes, int ring) {
+  return (size_t)ring * sel_slot_bytes(row_bytes) + 16;
 }
 
 // Ring slots (tiles in flight: RING - 1) and near-tie batch: 512-byte vectors
@@ -130,15 +124,14 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 512) ? 2 : 1) void k_sel
   const E* __restrict__ Ys = reinterpret_cast<const E*>(p.Ys);
   const int k = p.k, n_c = p.n_c, rho = p.rho;
   const int64_t s = p.s, C = p.C;
-  const size_t slot_bytes = sel_slot_bytes(G::ROW_BYTES, p.rounds);
+  const size_t slot_bytes = sel_slot_bytes(G::ROW_BYTES);
   char* ring = smem;
   constexpr int RING = SelGeom<E, D>::RING, WLIST = SelGeom<E, D>::WL;
   int32_t* wg_flag = reinterpret_cast<int32_t*>(smem + RING * slot_bytes);
   const int w = threadIdx.x >> 6, l = lane_id(), g = l >> 4;
-  WaveLds L = carve(smem + sel_common_lds(G::ROW_BYTES, p.rounds, RING) + (size_t)w * wave_lds_bytes(p.rounds, WLIST),
-                    p.rounds, WLIST);
-  const int NP = nprev_of(p.rounds);
+  WaveLds L = carve(smem + sel_common_lds(G::ROW_BYTES, RING) + (size_t)w * wave_lds_bytes(WLIST), WLIST);
   (void)X;
+  (void)n_c;
   uint32_t nexact = 0;   // float64 logits computed by this lane
   uint32_t ntopk = 0;    // rows whose k-th element needed a float64 ranking (same in every lane)
 
@@ -160,20 +153,6 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 512) ? 2 : 1) void k_sel
   const int iA = pA < x1 ? p.perm_x[pA] : -1;
   Frag<E, D> afr;
   afr.load_global(pA < x1 ? Xs + pA * D : nullptr);
-  if (l < 16) {
-    for (int r2 = 0; r2 < rho; ++r2) {
-      PrevRow pr{0.0, 0.f, 0.f, 0, 0};
-      if (iA >= 0) {
-        const int64_t o2 = (int64_t)r2 * s + iA;
-        pr.te = p.thr_e[o2];
-        pr.lo = p.thr_lo[o2];
-        pr.hi = p.thr_hi[o2];
-        pr.tid = p.thr_id[o2];
-        pr.cx = chunk_of(p.inv_x[o2], s, n_c);
-      }
-      L.prev[l * NP + r2] = pr;
-    }
-  }
 
   // Layout: logit blocks are computed transposed (items x positions), so lane l
   // works for row r = l % 16 (its position) on items 4*(l/16) + v of every
@@ -209,14 +188,15 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 512) ? 2 : 1) void k_sel
     L.rf[r * 8 + RF_BETA] = beta;
   }
   const int64_t orow = p.slot_out ? pA : (int64_t)rho * s + iA;   // negs row (valid rows only)
+  const int64_t lrow = p.slot_out ? pA : (int64_t)iA;              // negl row (one round's lists)
 
   // mode 0: histogram pass; 1: collect pass; 2: nothing to do (k = 0)
   int mode = k == 0 ? 2 : (selall ? 1 : 0);
   float sexp = 0.0f;
   int nnew = 0, nsure = 0, bcnt = 0;
 
-  // copies of one tile: G::ROW_DMA row copies, then ids, then one chunk map per earlier round
-  const int ncopies = G::ROW_DMA + 1 + rho;
+  // copies of one tile: G::ROW_DMA row copies, then the ids
+  const int ncopies = G::ROW_DMA + 1;
   int my_copies = 0;
   for (int u = w; u < ncopies; u += NW) ++my_copies;
 
@@ -224,20 +204,19 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 512) ? 2 : 1) void k_sel
     if (mode == 0)
       for (int b = l; b < 16 * HIST_STRIDE; b += WAVE) L.hist[b] = 0u;
     __syncthreads();
-    issue_window_tile<E, D, NW, RING>(ring, slot_bytes, win, 0, Ys, p.perm_y, p.cyp, C, rho, w);
+    issue_window_tile<E, D, NW, RING>(ring, slot_bytes, win, 0, Ys, p.perm_y, nullptr, C, 0, w);
     if (RING == 3 && ntiles > 1)
-      issue_window_tile<E, D, NW, RING>(ring, slot_bytes, win, 1, Ys, p.perm_y, p.cyp, C, rho, w);
+      issue_window_tile<E, D, NW, RING>(ring, slot_bytes, win, 1, Ys, p.perm_y, nullptr, C, 0, w);
 
     for (int t = 0; t < ntiles; ++t) {
       // tile t's copies are complete once only those of later tiles remain outstanding
       wait_vmcnt(RING == 3 && t + 1 < ntiles ? my_copies : 0);
       raw_barrier();   // every wave's copies of tile t landed; slot (t + RING - 1) % RING is free
       if (t + RING - 1 < ntiles)
-        issue_window_tile<E, D, NW, RING>(ring, slot_bytes, win, t + RING - 1, Ys, p.perm_y, p.cyp, C, rho, w);
+        issue_window_tile<E, D, NW, RING>(ring, slot_bytes, win, t + RING - 1, Ys, p.perm_y, nullptr, C, 0, w);
       const int64_t q0 = range_tile_start(win, t, TI), q1 = range_tile_end(win, t);
       const char* slot = ring + (size_t)(t % RING) * slot_bytes;
       const int32_t* tid_ = reinterpret_cast<const int32_t*>(slot + G::ROW_BYTES);
-      const int32_t* tcy = tid_ + 64;
       const int nlim = (int)(q1 - q0);   // valid items of this tile
       f32x4 acc[NCB];
 #pragma unroll
@@ -277,24 +256,11 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 512) ? 2 : 1) void k_sel
         }
       } else {
         // collect: sure members (above thi) are counted and summed; the band [tlo, thi]
-        // goes to the row's list.  Rows past the chunk have tlo = thi = +inf.  The
-        // earlier-round test exists only in rounds after the first (two loop bodies).
-        auto collect = [&](auto ded) {
-          constexpr bool DEDUP = decltype(ded)::value;
-          float mxl = mx * LOG2E_F;
-          PrevRow p0{};
-          int cxm = 0, cxp = 0;   // chunks c-1, c+1 of the position in round 0
-          if (DEDUP) {
-            p0 = L.prev[r * NP];
-            cxm = p0.cx == 0 ? n_c - 1 : p0.cx - 1;
-            cxp = p0.cx == n_c - 1 ? 0 : p0.cx + 1;
-          }
-          const bool allwin = n_c <= 3;
+        // goes to the row's list.  Rows past the chunk have tlo = thi = +inf.
+        float mxl = mx * LOG2E_F;
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
-          u32x4 jj = *reinterpret_cast<const u32x4*>(tid_ + cb * 16 + 4 * g);
-          u32x4 cy4 = {0u, 0u, 0u, 0u};
-          if (DEDUP) cy4 = *reinterpret_cast<const u32x4*>(tcy + cb * 16 + 4 * g);
+          const u32x4 jj = *reinterpret_cast<const u32x4*>(tid_ + cb * 16 + 4 * g);
           bool inb[4];
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
@@ -304,53 +270,26 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 512) ? 2 : 1) void k_sel
             const bool cand = (full || n < nlim) && j != pos;
             const bool sure = cand && a > thi;
             inb[v] = cand && a >= tlo && a <= thi;
-            bool dup = false;
-            if (DEDUP) {
-              // round 0's set (registers), branch-free: the pair was in round 0's window and
-              // lies above its bounds, or is its threshold pair; a candidate within the
-              // bounds is decided in float64 (rare)
-              const int cy = (int)cy4[v];
-              const bool w0 = allwin || cy == p0.cx || cy == cxm || cy == cxp;
-              dup = w0 && (a > p0.hi || (a >= p0.lo && j == p0.tid));
-              const bool near0 = w0 && !dup && a >= p0.lo && (sure || inb[v]);
-              if (ballot(near0)) {
-                if (near0) {
-                  ++nexact;
-                  dup = beats_exact<E, D>(p0.te, p0.tid, Xs + pA * D, Y, j);
-                }
-              }
-              // rounds 1 .. rho-1 from LDS (three rounds or more)
-              if (rho > 1 && (sure || inb[v]) && !dup) {
-                for (int r2 = 1; r2 < rho && !dup; ++r2) {
-                  const PrevRow pr = L.prev[r * NP + r2];
-                  if (!in_window(pr.cx, tcy[64 * r2 + n], n_c)) continue;
-                  dup = beats<E, D>(a, pr.lo, pr.hi, pr.te, pr.tid, Xs + pA * D, Y, j, nexact);
-                }
-              }
-            }
-            const bool nw = sure && !dup;
-            if (selall && nw && a > mx) {   // no histogram pass ran: keep the shift at the maximum
+            if (selall && sure && a > mx) {   // no histogram pass ran: keep the shift at the maximum
               sexp = mx == NEG_INF ? 0.0f : sexp * __expf(mx - a);
               mx = a;
               mxl = mx * LOG2E_F;
             }
             // exp(a - mx) as 2^(a log2 e - mx log2 e), one fma before the exponential
-            sexp += nw ? __builtin_amdgcn_exp2f(fmaf(a, LOG2E_F, -mxl)) : 0.0f;
-            if (DEDUP) nnew += nw ? 1 : 0;   // without the earlier-round test every sure member is new
+            sexp += sure ? __builtin_amdgcn_exp2f(fmaf(a, LOG2E_F, -mxl)) : 0.0f;
             if (NEGS) {
               const uint64_t ms = ballot(sure);
               if (sure) {
                 const int slotn = nsure + popc(ms & row_lt);
                 if (slotn < k) {
-                  p.negs[orow * k + slotn] = dup ? (j | (int)0x80000000u) : j;
-                  if (p.negl) p.negl[orow * k + slotn] = a;
+                  p.negs[orow * k + slotn] = j;
+                  if (p.negl) p.negl[lrow * k + slotn] = a;
                 }
               }
               nsure += popc(ms & rowbits);
             } else {
               nsure += sure ? 1 : 0;
             }
-            if (dup && inb[v]) jj[v] |= 0x80000000u;
           }
           if (ballot(inb[0] || inb[1] || inb[2] || inb[3])) {
 #pragma unroll
@@ -367,11 +306,6 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 512) ? 2 : 1) void k_sel
             }
           }
         }
-        };
-        if (rho > 0)
-          collect(std::true_type{});
-        else
-          collect(std::false_type{});
       }
     }
 
@@ -483,10 +417,9 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 512) ? 2 : 1) void k_sel
     } else {
       sexp += s2;
     }
-    nnew += __shfl_xor(nnew, o);
     if (!NEGS) nsure += __shfl_xor(nsure, o);
   }
-  if (rho == 0) nnew = nsure;   // round 0: the new members are the sure ones
+  nnew = nsure;
   if (l < 16) {
     L.rf[r * 8 + RF_MX] = mx;
     L.rf[r * 8 + RF_SEXP] = sexp;
@@ -506,8 +439,7 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 512) ? 2 : 1) void k_sel
   // logits of the batch, one entry per lane.  (C) Per row: rank the near-ties by
   // (float64 logit desc, id asc); the k-th kept element is the row's threshold;
   // the kept list entries are the sorted prefix before the near-ties plus the
-  // near-ties ranked within the count still missing.  A list id with bit 31 set
-  // marks a pair kept in an earlier round (counted, not summed again).
+  // near-ties ranked within the count still missing.
   int r_next = 0;
   while (r_next < 16) {
     int tot = 0;
@@ -645,16 +577,15 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 512) ? 2 : 1) void k_sel
         thi = f_up(te + b2);
         // kept list entries: those above the near-ties and the near-ties ranked in
         const bool kept = l < n && (a > hi || rank < need);
-        const bool fresh = kept && (jraw & 0x80000000) == 0;
-        se += wave_sumf(fresh ? __expf(a - mx) : 0.0f);
-        nnew += popc(ballot(fresh));
+        se += wave_sumf(kept ? __expf(a - mx) : 0.0f);
+        nnew += popc(ballot(kept));
         if (NEGS) {
           const uint64_t km = ballot(kept);
           if (kept) {
             const int slotn = nsure + popc(km & lanemask_lt());
             if (slotn < k) {
               p.negs[o * k + slotn] = jraw;
-              if (p.negl) p.negl[o * k + slotn] = a;
+              if (p.negl) p.negl[(int64_t)i * k + slotn] = a;
             }
           }
           listed = nsure + popc(km);
@@ -680,13 +611,14 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 512) ? 2 : 1) void k_sel
 }
 
 template <class E, int D>
-static size_t select_lds_bytes_t(int waves, int rounds) {
-  return sel_common_lds(TileGeom<E, D>::ROW_BYTES, rounds, SelGeom<E, D>::RING) +
-         (size_t)waves * wave_lds_bytes(rounds, SelGeom<E, D>::WL);
+static size_t select_lds_bytes_t(int waves) {
+  return sel_common_lds(TileGeom<E, D>::ROW_BYTES, SelGeom<E, D>::RING) +
+         (size_t)waves * wave_lds_bytes(SelGeom<E, D>::WL);
 }
 size_t select_lds_bytes(bool is_bf16, int d, int waves, int rounds) {
+  (void)rounds;   // every round selects on its own: the LDS does not grow with rounds
 #define RECE_L(E, DD) \
-  if (d == DD) return select_lds_bytes_t<E, DD>(waves, rounds);
+  if (d == DD) return select_lds_bytes_t<E, DD>(waves);
   if (is_bf16) {
     RECE_L(bf16, 32) RECE_L(bf16, 64) RECE_L(bf16, 128) RECE_L(bf16, 256)
   } else {

@@ -102,7 +102,9 @@ struct rece_plan_s {
   size_t o_cnt, o_bx, o_by, o_px, o_ix, o_py, o_iy, o_te, o_tid, o_tlo, o_thi, o_msh, o_ssum, o_nmem, o_xnorm,
       o_ymax, o_lse, o_lpos, o_negs, o_xs, o_ys, o_cyp, saved_bytes;
   // scratch
-  size_t o_bt, o_bnorm, o_und, o_undy, o_sorty, o_sort, o_part, o_pp0, o_pp1, o_ppart, o_rec, o_prev, scratch_bytes;
+  size_t o_bt, o_bnorm, o_und, o_undy, o_sorty, o_sort, o_part, o_pp0, o_pp1, o_ppart, o_rec, o_prev, o_negl,
+      scratch_bytes;
+  int dedup_bits;   // LDS hash size of the round dedup (log2 slots per wave, 0 = list scan)
   // bucket variant: slots = (bucket, position) and (bucket, item) pairs
   int64_t sx, sy;     // n_b * b_x, n_b * b_y
   int64_t qwords;     // words of one bucket's item bitmap
@@ -571,6 +573,9 @@ rece_status rece_plan(const rece_config* cfg, rece_plan_t* out) {
   p->o_ppart = sc.take(pos_partial_bytes(s, d));
   p->o_rec = sc.take((size_t)r * s * sizeof(PosRec));
   p->o_prev = sc.take((size_t)std::max(1, r * (r - 1) / 2) * s * sizeof(PrevRow));
+  // float32 logits of the kept lists of rounds >= 1 (the round dedup sums the new pairs)
+  p->o_negl = sc.take((size_t)(r - 1) * s * k * 4);
+  p->dedup_bits = dedup_hash_bits(r, k);
   p->scratch_bytes = sc.off;
   *out = p;
   return RECE_OK;
@@ -668,69 +673,25 @@ rece_status rece_forward(rece_plan_t plan, void* stream, const void* X, const vo
              "prepare random vectors");
 
   // Item chain of every round (bucketing, sort, sorted copy, earlier-round chunks)
-  // on the side stream, position chain and chunk kernel on the caller's stream; the
-  // chunk kernel of round rho waits for the item chain of that round.
-  const rece_status ss = ensure_side(p, c.rounds + 1);
+  // and the position chains of rounds >= 1 run on the side stream, followed there by
+  // the chunk kernels of rounds >= 1 (a round's selection does not depend on the
+  // other rounds); round 0's position chain and chunk kernel run on the caller's
+  // stream.  Events: fork[rounds] starts the side stream, fork[rounds + 1] marks the
+  // position norms of round 0 (every chunk kernel reads them), fork[0] the end of
+  // round 0's item chain, fork[rounds + 2] the end of the side stream.
+  const rece_status ss = ensure_side(p, c.rounds + 3);
   if (ss != RECE_OK) return ss;
   hipStream_t side = p.side.s;
   int32_t* undy = reinterpret_cast<int32_t*>(sc + p.o_undy);
   RECE_HIP(hipEventRecord(p.side.fork[c.rounds], st), "fork");
   RECE_HIP(hipStreamWaitEvent(side, p.side.fork[c.rounds], 0), "fork");
-  for (int rho = 0; rho < c.rounds; ++rho) {
-    hipStream_t st = side;
-    int32_t* by = reinterpret_cast<int32_t*>(sv + p.o_by) + (int64_t)rho * C;
-    int32_t* py = reinterpret_cast<int32_t*>(sv + p.o_py) + (int64_t)rho * C;
-    int32_t* iy = reinterpret_cast<int32_t*>(sv + p.o_iy) + (int64_t)rho * C;
-    const void* Btr = static_cast<const char*>(Bt) + (size_t)rho * c.n_b * d * p.esize;
-    RECE_PHASE(RECE_PHASE_PROJECT, launch_project_argmax(p.bf16, d, Y, C, Btr, c.n_b, bnorm + rho, p.beta_coef, by, nullptr,
-                                   rho == 0 ? reinterpret_cast<uint32_t*>(ymax) : nullptr, undy, und_n + 2 * rho + 1,
-                                   counters, st),
-             "bucket items");
-    RECE_PHASE(RECE_PHASE_SORT, launch_counting_sort(by, nullptr, C, 0, p.nbits_b, sc + p.o_sorty, py, iy, st),
-               "sort items");
-    char* ys = sv + p.o_ys + (size_t)rho * C * d * p.esize;
-    int32_t* cyp = reinterpret_cast<int32_t*>(sv + p.o_cyp) + (int64_t)(rho * (rho - 1) / 2) * C;
-    RECE_PHASE(RECE_PHASE_SORT, launch_gather_rows(Y, py, C, d * p.esize, ys, st), "sorted items");
-    for (int r2 = 0; r2 < rho; ++r2)
-      RECE_PHASE(RECE_PHASE_SORT,
-                 launch_prev_chunks(py, reinterpret_cast<const int32_t*>(sv + p.o_iy) + (int64_t)r2 * C, C, c.n_c,
-                                    cyp + (int64_t)r2 * C, st),
-                 "earlier-round chunks");
-    if (rho > 0) {
-      // the position chain of later rounds too (it does not wait for earlier chunk kernels)
-      int32_t* bx = reinterpret_cast<int32_t*>(sv + p.o_bx) + (int64_t)rho * s;
-      int32_t* px = reinterpret_cast<int32_t*>(sv + p.o_px) + (int64_t)rho * s;
-      int32_t* ix = reinterpret_cast<int32_t*>(sv + p.o_ix) + (int64_t)rho * s;
-      RECE_PHASE(RECE_PHASE_PROJECT, launch_project_argmax(p.bf16, d, X, s, Btr, c.n_b, bnorm + rho, p.beta_coef,
-                                     bx, nullptr, nullptr, undy, und_n + 2 * rho, counters, st),
-                 "bucket positions");
-      RECE_PHASE(RECE_PHASE_SORT, launch_counting_sort(bx, nullptr, s, 0, p.nbits_b, sc + p.o_sorty, px, ix, st),
-                 "sort positions");
-      char* xs = sv + p.o_xs + (size_t)rho * s * d * p.esize;
-      RECE_PHASE(RECE_PHASE_SORT, launch_gather_rows(X, px, s, d * p.esize, xs, st), "sorted positions");
-    }
-    RECE_HIP(hipEventRecord(p.side.fork[rho], side), "item chain done");
-  }
 
-  for (int rho = 0; rho < c.rounds; ++rho) {
-    int32_t* bx = reinterpret_cast<int32_t*>(sv + p.o_bx) + (int64_t)rho * s;
-    int32_t* px = reinterpret_cast<int32_t*>(sv + p.o_px) + (int64_t)rho * s;
-    int32_t* ix = reinterpret_cast<int32_t*>(sv + p.o_ix) + (int64_t)rho * s;
-    int32_t* py = reinterpret_cast<int32_t*>(sv + p.o_py) + (int64_t)rho * C;
+  auto select_args = [&](int rho) {
     char* xs = sv + p.o_xs + (size_t)rho * s * d * p.esize;
     char* ys = sv + p.o_ys + (size_t)rho * C * d * p.esize;
+    int32_t* px = reinterpret_cast<int32_t*>(sv + p.o_px) + (int64_t)rho * s;
+    int32_t* py = reinterpret_cast<int32_t*>(sv + p.o_py) + (int64_t)rho * C;
     int32_t* cyp = reinterpret_cast<int32_t*>(sv + p.o_cyp) + (int64_t)(rho * (rho - 1) / 2) * C;
-    if (rho == 0) {   // round 0's position chain here, alongside the first item chain
-      const void* Btr = Bt;
-      RECE_PHASE(RECE_PHASE_PROJECT, launch_project_argmax(p.bf16, d, X, s, Btr, c.n_b, bnorm, p.beta_coef, bx,
-                                     xnorm, nullptr, und, und_n, counters, st),
-                 "bucket positions");
-      RECE_PHASE(RECE_PHASE_SORT, launch_counting_sort(bx, nullptr, s, 0, p.nbits_b, sc + p.o_sort, px, ix, st),
-                 "sort positions");
-      RECE_PHASE(RECE_PHASE_SORT, launch_gather_rows(X, px, s, d * p.esize, xs, st), "sorted positions");
-    }
-    RECE_HIP(hipStreamWaitEvent(st, p.side.fork[rho], 0), "join item and position chains");
-
     SelectArgs a{};
     a.X = X;
     a.Y = Y;
@@ -762,11 +723,85 @@ rece_status rece_forward(rece_plan_t plan, void* stream, const void* X, const vo
     a.ssum = reinterpret_cast<float*>(sv + p.o_ssum);
     a.nmem = reinterpret_cast<int32_t*>(sv + p.o_nmem);
     a.negs = p.o_negs ? reinterpret_cast<int32_t*>(sv + p.o_negs) : nullptr;
-    a.negl = nullptr;
     a.slot_out = 0;
     a.nwin = 3;
     a.counters = counters;
+    a.negl = rho > 0 ? reinterpret_cast<float*>(sc + p.o_negl) + (int64_t)(rho - 1) * s * c.k : nullptr;
+    return a;
+  };
+
+  {   // round 0's position chain, alongside the first item chain
+    int32_t* bx = reinterpret_cast<int32_t*>(sv + p.o_bx);
+    int32_t* px = reinterpret_cast<int32_t*>(sv + p.o_px);
+    int32_t* ix = reinterpret_cast<int32_t*>(sv + p.o_ix);
+    char* xs = sv + p.o_xs;
+    RECE_PHASE(RECE_PHASE_PROJECT, launch_project_argmax(p.bf16, d, X, s, Bt, c.n_b, bnorm, p.beta_coef, bx,
+                                   xnorm, nullptr, und, und_n, counters, st),
+               "bucket positions");
+    RECE_HIP(hipEventRecord(p.side.fork[c.rounds + 1], st), "position norms");
+    RECE_PHASE(RECE_PHASE_SORT, launch_counting_sort(bx, nullptr, s, 0, p.nbits_b, sc + p.o_sort, px, ix, st),
+               "sort positions");
+    RECE_PHASE(RECE_PHASE_SORT, launch_gather_rows(X, px, s, d * p.esize, xs, st), "sorted positions");
+  }
+
+  for (int rho = 0; rho < c.rounds; ++rho) {
+    hipStream_t st = side;
+    int32_t* by = reinterpret_cast<int32_t*>(sv + p.o_by) + (int64_t)rho * C;
+    int32_t* py = reinterpret_cast<int32_t*>(sv + p.o_py) + (int64_t)rho * C;
+    int32_t* iy = reinterpret_cast<int32_t*>(sv + p.o_iy) + (int64_t)rho * C;
+    const void* Btr = static_cast<const char*>(Bt) + (size_t)rho * c.n_b * d * p.esize;
+    RECE_PHASE(RECE_PHASE_PROJECT, launch_project_argmax(p.bf16, d, Y, C, Btr, c.n_b, bnorm + rho, p.beta_coef, by, nullptr,
+                                   rho == 0 ? reinterpret_cast<uint32_t*>(ymax) : nullptr, undy, und_n + 2 * rho + 1,
+                                   counters, st),
+             "bucket items");
+    RECE_PHASE(RECE_PHASE_SORT, launch_counting_sort(by, nullptr, C, 0, p.nbits_b, sc + p.o_sorty, py, iy, st),
+               "sort items");
+    char* ys = sv + p.o_ys + (size_t)rho * C * d * p.esize;
+    int32_t* cyp = reinterpret_cast<int32_t*>(sv + p.o_cyp) + (int64_t)(rho * (rho - 1) / 2) * C;
+    RECE_PHASE(RECE_PHASE_SORT, launch_gather_rows(Y, py, C, d * p.esize, ys, st), "sorted items");
+    for (int r2 = 0; r2 < rho; ++r2)   // the backward's earlier-round tests read these
+      RECE_PHASE(RECE_PHASE_SORT,
+                 launch_prev_chunks(py, reinterpret_cast<const int32_t*>(sv + p.o_iy) + (int64_t)r2 * C, C, c.n_c,
+                                    cyp + (int64_t)r2 * C, st),
+                 "earlier-round chunks");
+    if (rho == 0) {
+      RECE_HIP(hipEventRecord(p.side.fork[0], side), "item chain done");
+      continue;
+    }
+    int32_t* bx = reinterpret_cast<int32_t*>(sv + p.o_bx) + (int64_t)rho * s;
+    int32_t* px = reinterpret_cast<int32_t*>(sv + p.o_px) + (int64_t)rho * s;
+    int32_t* ix = reinterpret_cast<int32_t*>(sv + p.o_ix) + (int64_t)rho * s;
+    RECE_PHASE(RECE_PHASE_PROJECT, launch_project_argmax(p.bf16, d, X, s, Btr, c.n_b, bnorm + rho, p.beta_coef,
+                                   bx, nullptr, nullptr, undy, und_n + 2 * rho, counters, st),
+               "bucket positions");
+    RECE_PHASE(RECE_PHASE_SORT, launch_counting_sort(bx, nullptr, s, 0, p.nbits_b, sc + p.o_sorty, px, ix, st),
+               "sort positions");
+    char* xs = sv + p.o_xs + (size_t)rho * s * d * p.esize;
+    RECE_PHASE(RECE_PHASE_SORT, launch_gather_rows(X, px, s, d * p.esize, xs, st), "sorted positions");
+    if (rho == 1) RECE_HIP(hipStreamWaitEvent(side, p.side.fork[c.rounds + 1], 0), "position norms");
+    const SelectArgs a = select_args(rho);
     RECE_PHASE(RECE_PHASE_SELECT, launch_select(p.bf16, d, p.waves_sel, a, st), "chunk logits and top-k");
+  }
+  RECE_HIP(hipEventRecord(p.side.fork[c.rounds + 2], side), "side stream done");
+
+  RECE_HIP(hipStreamWaitEvent(st, p.side.fork[0], 0), "join the first item chain");
+  {
+    const SelectArgs a = select_args(0);
+    RECE_PHASE(RECE_PHASE_SELECT, launch_select(p.bf16, d, p.waves_sel, a, st), "chunk logits and top-k");
+  }
+  RECE_HIP(hipStreamWaitEvent(st, p.side.fork[c.rounds + 2], 0), "join the side stream");
+  for (int rho = 1; rho < c.rounds && c.k > 0; ++rho) {
+    DedupArgs dd{};
+    dd.negs = reinterpret_cast<int32_t*>(sv + p.o_negs);
+    dd.negl = reinterpret_cast<const float*>(sc + p.o_negl) + (int64_t)(rho - 1) * s * c.k;
+    dd.mshift = reinterpret_cast<const float*>(sv + p.o_msh);
+    dd.ssum = reinterpret_cast<float*>(sv + p.o_ssum);
+    dd.nmem = reinterpret_cast<int32_t*>(sv + p.o_nmem);
+    dd.s = s;
+    dd.k = c.k;
+    dd.rho = rho;
+    dd.hash_bits = p.dedup_bits;
+    RECE_PHASE(RECE_PHASE_LOSS, launch_round_dedup(dd, st), "round dedup");
   }
 
   CeArgs ce{};

@@ -50,7 +50,7 @@ struct SelectArgs {
   float* ssum;                // [rounds][s]
   int32_t* nmem;              // [rounds][s]
   int32_t* negs;              // [rounds][s][k] kept ids (bit 31: kept in an earlier round; -1 pad) or nullptr
-  float* negl;                // [s][k] float32 logits of negs, or nullptr
+  float* negl;                // [s][k] float32 logits of this round's negs (row = position or slot), or nullptr
   int slot_out;               // 1: outputs indexed by sorted slot, not by position id
   int nwin;                   // window chunks: 3 (c-1, c, c+1) or 1 (c only)
   uint32_t* counters;
@@ -71,6 +71,19 @@ struct CeArgs {
   float* partial;             // [num blocks]
   uint32_t* counters;
   int validate;
+};
+
+// Round dedup (rounds >= 1): the pairs of round rho's kept list that an earlier
+// round also kept are marked (bit 31 of the id) and left out of the round's sum.
+struct DedupArgs {
+  int32_t* negs;              // [rounds][s][k] kept ids (-1 pad); earlier rounds read, round rho marked
+  const float* negl;          // [s][k] float32 logits of round rho's kept list
+  const float* mshift;        // [rounds][s]
+  float* ssum;                // [rounds][s] overwritten for round rho: sum over its new pairs
+  int32_t* nmem;              // [rounds][s] overwritten for round rho: its new pairs
+  int64_t s;
+  int k, rho;
+  int hash_bits;              // log2 of the LDS hash slots per wave; 0: linear scan of the earlier lists
 };
 
 struct BwdArgs {
@@ -137,6 +150,10 @@ hipError_t launch_select(bool is_bf16, int d, int waves, const SelectArgs& a, hi
 size_t select_lds_bytes(bool is_bf16, int d, int waves, int cap);
 int ce_blocks(int64_t s);
 hipError_t launch_ce(bool is_bf16, int d, const CeArgs& a, float* loss, hipStream_t st);
+// log2 of the per-wave hash slots k_round_dedup uses for rounds earlier lists of k
+// ids (0: too many for LDS, the kernel scans the lists instead).
+int dedup_hash_bits(int rounds, int k);
+hipError_t launch_round_dedup(const DedupArgs& a, hipStream_t st);
 hipError_t launch_bwd_rows(bool is_bf16, int d, int waves, const BwdArgs& a, hipStream_t st);
 // dX of every position from the kept lists of all rounds plus the positive term
 // (writes all s rows of dX).
