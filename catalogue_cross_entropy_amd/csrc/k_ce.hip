@@ -81,88 +81,183 @@ __global__ __launch_bounds__(256) void k_mean(const double* __restrict__ partial
 // Rounds (RECE page, Section 3: the procedure repeated over rounds, with a
 // minus-ln(count) term per logit).  The term makes the copies of a pair kept in
 // several rounds count once, so a round's sum covers only the pairs no earlier
-// round kept.  One wave per position: the earlier rounds' kept ids go into an LDS
-// hash table (open addressing, at most half full), then each entry of round rho's
-// list is looked up; a pair found is marked with bit 31 (the backward skips it),
-// the others are summed as exp(logit - shift) in list order and a fixed tree.
+// round kept.  16 lanes per position (four positions per wave); lane `sub` takes
+// eight consecutive list entries at a time (two 16-byte loads when k is a
+// multiple of 4, so every cache line a load misses on is used whole).  The
+// earlier rounds' kept ids go into the position's LDS hash table (open
+// addressing, at most half full), then each entry of round rho's list is looked
+// up; a pair found is marked with bit 31 (the backward skips it), the others are
+// summed as exp(logit - shift) in a fixed order (per lane in list order, then a
+// fixed tree over the 16 lanes).
 constexpr int DEDUP_WAVES = 4;
+constexpr int DEDUP_LPP = 16;                            // lanes per position
+constexpr int DEDUP_PPB = DEDUP_WAVES * WAVE / DEDUP_LPP;  // positions per workgroup
+constexpr int DEDUP_EPL = 8;                             // consecutive entries per lane and step
+constexpr int DEDUP_CHUNK = DEDUP_LPP * DEDUP_EPL;       // list entries per step
 
 __device__ __forceinline__ uint32_t dedup_hash(int id, int bits) {
   return ((uint32_t)id * 2654435761u) >> (32 - bits);
 }
 
+// Entries e0 + 8*sub .. +7 of a list of k (missing entries read as `pad`).
+template <bool VEC, class T>
+__device__ __forceinline__ void load8(const T* __restrict__ row, int e0, int sub, int k, T pad, T (&v)[DEDUP_EPL]) {
+  const int e = e0 + DEDUP_EPL * sub;
+  if constexpr (VEC) {   // k % 4 == 0: each quad is wholly inside or outside the list
+#pragma unroll
+    for (int h = 0; h < DEDUP_EPL / 4; ++h) {
+      if (e + 4 * h < k) {
+        typedef T T4 __attribute__((ext_vector_type(4)));
+        const T4 q = *reinterpret_cast<const T4*>(row + e + 4 * h);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[4 * h + u] = q[u];
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[4 * h + u] = pad;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < DEDUP_EPL; ++u) v[u] = e + u < k ? row[e + u] : pad;
+  }
+}
+
+// The eight entries of a lane walk their probe sequences (linear probing) in
+// step, so each step has eight independent LDS accesses in flight.  The table
+// always has a free slot, so every walk ends within the table size.
+// find: bit u of the result is set when id[u] (>= 0) is in the table.
+__device__ __forceinline__ uint32_t hash_find8(const int32_t* tab, int bits, const int (&id)[DEDUP_EPL]) {
+  const uint32_t mask = (1u << bits) - 1u;
+  uint32_t h[DEDUP_EPL];
+  uint32_t open = 0, found = 0;
+#pragma unroll
+  for (int u = 0; u < DEDUP_EPL; ++u) {
+    h[u] = dedup_hash(id[u], bits);
+    open |= id[u] >= 0 ? 1u << u : 0u;
+  }
+  for (uint32_t step = 0; open && step <= mask; ++step) {
+#pragma unroll
+    for (int u = 0; u < DEDUP_EPL; ++u) {
+      if (!((open >> u) & 1u)) continue;
+      const int v = tab[h[u]];
+      if (v == id[u]) found |= 1u << u;
+      if (v == id[u] || v == -1) open &= ~(1u << u);
+      h[u] = (h[u] + 1) & mask;
+    }
+  }
+  return found;
+}
+
+// insert every id[u] >= 0 (an id already present stays once).
+__device__ __forceinline__ void hash_insert8(int32_t* tab, int bits, const int (&id)[DEDUP_EPL]) {
+  const uint32_t mask = (1u << bits) - 1u;
+  uint32_t h[DEDUP_EPL];
+  uint32_t open = 0;
+#pragma unroll
+  for (int u = 0; u < DEDUP_EPL; ++u) {
+    h[u] = dedup_hash(id[u], bits);
+    open |= id[u] >= 0 ? 1u << u : 0u;
+  }
+  for (uint32_t step = 0; open && step <= mask; ++step) {
+#pragma unroll
+    for (int u = 0; u < DEDUP_EPL; ++u) {
+      if (!((open >> u) & 1u)) continue;
+      const int old = atomicCAS(&tab[h[u]], -1, id[u]);
+      if (old == -1 || old == id[u]) open &= ~(1u << u);
+      h[u] = (h[u] + 1) & mask;
+    }
+  }
+}
+
+// Whether `id` is in one of the lists of rounds 0 .. rho - 1 (the scan used when
+// the earlier ids do not fit the LDS tables).
+__device__ __forceinline__ bool scan_find(const DedupArgs& a, int64_t i, int id) {
+  for (int r2 = 0; r2 < a.rho; ++r2) {
+    const int32_t* lst = a.negs + ((int64_t)r2 * a.s + i) * a.k;
+    for (int t = 0; t < a.k; ++t) {
+      const int raw = lst[t];
+      if (raw != -1 && (raw & 0x7FFFFFFF) == id) return true;
+    }
+  }
+  return false;
+}
+
+template <bool VEC, bool HASH>
 __global__ __launch_bounds__(64 * DEDUP_WAVES) void k_round_dedup(DedupArgs a) {
   extern __shared__ int32_t tab_all[];
-  const int w = threadIdx.x >> 6, l = lane_id();
-  const int64_t i = (int64_t)blockIdx.x * DEDUP_WAVES + w;
+  const int q = threadIdx.x / DEDUP_LPP, sub = threadIdx.x % DEDUP_LPP;
+  const int64_t i = (int64_t)blockIdx.x * DEDUP_PPB + q;
   const int k = a.k, rho = a.rho, bits = a.hash_bits;
-  const int hs = bits ? 1 << bits : 0;
-  int32_t* tab = tab_all + (size_t)w * hs;
   const bool live = i < a.s;
-  for (int t = l; t < hs; t += WAVE) tab[t] = -1;
-  __syncthreads();
-  if (live && bits) {
-    for (int r2 = 0; r2 < rho; ++r2) {
-      const int32_t* lst = a.negs + ((int64_t)r2 * a.s + i) * k;
-      for (int e = l; e < k; e += WAVE) {
-        const int raw = lst[e];
-        if (raw == -1) continue;
-        const int id = raw & 0x7FFFFFFF;
-        uint32_t h = dedup_hash(id, bits);
-        for (int probe = 0; probe < hs; ++probe) {   // a free slot always exists
-          const int old = atomicCAS(&tab[h], -1, id);
-          if (old == -1 || old == id) break;
-          h = (h + 1) & (uint32_t)(hs - 1);
+  int32_t* tab = tab_all + (HASH ? (size_t)q << bits : 0);
+  if (HASH) {
+    for (int t = sub; t < (1 << bits); t += DEDUP_LPP) tab[t] = -1;
+    __syncthreads();
+    if (live) {
+      for (int r2 = 0; r2 < rho; ++r2) {
+        const int32_t* lst = a.negs + ((int64_t)r2 * a.s + i) * k;
+        for (int e0 = 0; e0 < k; e0 += DEDUP_CHUNK) {
+          int raw[DEDUP_EPL];
+          load8<VEC>(lst, e0, sub, k, -1, raw);
+#pragma unroll
+          for (int u = 0; u < DEDUP_EPL; ++u) raw[u] = raw[u] == -1 ? -1 : raw[u] & 0x7FFFFFFF;
+          hash_insert8(tab, bits, raw);
         }
       }
     }
+    __syncthreads();
   }
-  __syncthreads();
-  if (!live) return;
+  if (!live) return;   // the rest needs no barrier
   const int64_t o = (int64_t)rho * a.s + i;
   int32_t* mine = a.negs + o * k;
   const float* lg = a.negl + i * (int64_t)k;
   const float mx = a.mshift[o];
   float sum = 0.0f;
   int cnt = 0;
-  for (int e = l; e < k; e += WAVE) {
-    const int id = mine[e];
-    if (id < 0) continue;
-    bool dup = false;
-    if (bits) {
-      uint32_t h = dedup_hash(id, bits);
-      for (int probe = 0; probe < hs; ++probe) {
-        const int v = tab[h];
-        if (v == id) {
-          dup = true;
-          break;
-        }
-        if (v == -1) break;
-        h = (h + 1) & (uint32_t)(hs - 1);
-      }
+  for (int e0 = 0; e0 < k; e0 += DEDUP_CHUNK) {
+    int id[DEDUP_EPL];
+    float lv[DEDUP_EPL];
+    load8<VEC>(mine, e0, sub, k, -1, id);
+    load8<VEC>(lg, e0, sub, k, 0.0f, lv);
+    uint32_t dupm = 0;   // bit u: entry u was kept in an earlier round
+    if (HASH) {
+      dupm = hash_find8(tab, bits, id);
     } else {
-      for (int r2 = 0; r2 < rho && !dup; ++r2) {
-        const int32_t* lst = a.negs + ((int64_t)r2 * a.s + i) * k;
-        for (int u = 0; u < k; ++u) {
-          const int raw = lst[u];
-          if (raw != -1 && (raw & 0x7FFFFFFF) == id) {
-            dup = true;
-            break;
-          }
-        }
-      }
+#pragma unroll
+      for (int u = 0; u < DEDUP_EPL; ++u)
+        if (id[u] >= 0 && scan_find(a, i, id[u])) dupm |= 1u << u;
     }
-    if (dup) {
-      mine[e] = id | (int)0x80000000u;
-    } else {
-      sum += __expf(lg[e] - mx);
-      ++cnt;
+#pragma unroll
+    for (int u = 0; u < DEDUP_EPL; ++u) {
+      const bool fresh = id[u] >= 0 && ((dupm >> u) & 1u) == 0;
+      sum += fresh ? __expf(lv[u] - mx) : 0.0f;
+      cnt += fresh ? 1 : 0;
+    }
+    if (dupm) {   // write the lane's entries back with the marks
+      int outv[DEDUP_EPL];
+#pragma unroll
+      for (int u = 0; u < DEDUP_EPL; ++u) outv[u] = ((dupm >> u) & 1u) ? (id[u] | (int)0x80000000u) : id[u];
+      const int e = e0 + DEDUP_EPL * sub;
+      if constexpr (VEC) {
+#pragma unroll
+        for (int h = 0; h < DEDUP_EPL / 4; ++h)
+          if (e + 4 * h < k)
+            *reinterpret_cast<u32x4*>(mine + e + 4 * h) =
+                u32x4{(uint32_t)outv[4 * h], (uint32_t)outv[4 * h + 1], (uint32_t)outv[4 * h + 2],
+                      (uint32_t)outv[4 * h + 3]};
+      } else {
+#pragma unroll
+        for (int u = 0; u < DEDUP_EPL; ++u)
+          if ((dupm >> u) & 1u) mine[e + u] = outv[u];
+      }
     }
   }
-  sum = wave_sumf(sum);
 #pragma unroll
-  for (int off = 1; off < WAVE; off <<= 1) cnt += __shfl_xor(cnt, off);
-  if (l == 0) {
+  for (int off = 1; off < DEDUP_LPP; off <<= 1) {
+    sum += __shfl_xor(sum, off);
+    cnt += __shfl_xor(cnt, off);
+  }
+  if (sub == 0) {
     a.ssum[o] = sum;
     a.nmem[o] = cnt;
   }
@@ -170,21 +265,27 @@ __global__ __launch_bounds__(64 * DEDUP_WAVES) void k_round_dedup(DedupArgs a) {
 
 int dedup_hash_bits(int rounds, int k) {
   const int64_t n = (int64_t)std::max(rounds - 1, 1) * std::max(k, 1);
-  int bits = 6;
-  while (((int64_t)1 << bits) < 2 * n) ++bits;
-  // four waves of 2^bits int32 slots must fit the 160 KB of LDS a workgroup may take
-  return ((size_t)DEDUP_WAVES << bits) * 4 <= 128 * 1024 ? bits : 0;
+  // one table of 2^bits int32 slots per position of the workgroup, within 128 KB of
+  // LDS: at most a quarter full (short probe walks), else at most half full
+  for (int64_t fill : {4, 2}) {
+    int bits = 4;
+    while (((int64_t)1 << bits) < fill * n) ++bits;
+    if (((size_t)DEDUP_PPB << bits) * 4 <= 128 * 1024) return bits;
+  }
+  return 0;
 }
 
 hipError_t launch_round_dedup(const DedupArgs& a, hipStream_t st) {
-  const size_t lds = a.hash_bits ? ((size_t)DEDUP_WAVES << a.hash_bits) * 4 : 0;
+  const size_t lds = a.hash_bits ? ((size_t)DEDUP_PPB << a.hash_bits) * 4 : 0;
+  auto kern = a.hash_bits ? (a.k % 4 == 0 ? k_round_dedup<true, true> : k_round_dedup<false, true>)
+                          : (a.k % 4 == 0 ? k_round_dedup<true, false> : k_round_dedup<false, false>);
   if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_round_dedup),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  const unsigned blocks = (unsigned)((a.s + DEDUP_WAVES - 1) / DEDUP_WAVES);
-  hipLaunchKernelGGL(k_round_dedup, dim3(blocks), dim3(64 * DEDUP_WAVES), lds, st, a);
+  const unsigned blocks = (unsigned)((a.s + DEDUP_PPB - 1) / DEDUP_PPB);
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * DEDUP_WAVES), lds, st, a);
   return hipGetLastError();
 }
 
