@@ -100,7 +100,7 @@ struct rece_plan_s {
   float beta_coef;
   // saved
   size_t o_cnt, o_bx, o_by, o_px, o_ix, o_py, o_iy, o_te, o_tid, o_tlo, o_thi, o_msh, o_ssum, o_nmem, o_xnorm,
-      o_ymax, o_lse, o_lpos, o_negs, o_xs, o_ys, o_cyp, saved_bytes;
+      o_ymax, o_lse, o_lpos, o_negs, o_xs, o_ys, o_cyp, o_psort, saved_bytes;
   // scratch
   size_t o_bt, o_bnorm, o_und, o_undy, o_sorty, o_sort, o_part, o_pp0, o_pp1, o_ppart, o_rec, o_prev, o_negl,
       scratch_bytes;
@@ -551,6 +551,7 @@ rece_status rece_plan(const rece_config* cfg, rece_plan_t* out) {
   p->o_xnorm = sv.take((size_t)s * 4);
   p->o_ymax = sv.take(4);
   p->o_lse = sv.take((size_t)s * 4);
+  p->o_psort = sv.take((size_t)s * 4);   // positions sorted by positive id (stable)
   p->o_lpos = sv.take((size_t)s * 4);
   p->o_negs = sv.take((size_t)r * s * std::max(k, 1) * 4);   // kept lists: dX reads them
   p->o_xs = sv.take((size_t)r * s * d * p->esize);
@@ -789,6 +790,21 @@ rece_status rece_forward(rece_plan_t plan, void* stream, const void* X, const vo
     const SelectArgs a = select_args(0);
     RECE_PHASE(RECE_PHASE_SELECT, launch_select(p.bf16, d, p.waves_sel, a, st), "chunk logits and top-k");
   }
+  {   // positions sorted by positive id (LSD counting sort), for the positive term of dY; it
+      // needs only pos, and this stream would otherwise wait for the second stream here
+    int32_t* bufs[2] = {reinterpret_cast<int32_t*>(sc + p.o_pp0), reinterpret_cast<int32_t*>(sc + p.o_pp1)};
+    int32_t* final_out = reinterpret_cast<int32_t*>(sv + p.o_psort);
+    const int total_bits = std::max(1, bits_for(C));
+    const int db = sort_digit_bits(s);
+    const int32_t* sorted = nullptr;
+    for (int pass = 0, shift = 0; shift < total_bits; ++pass, shift += db) {
+      const int nb = std::min(db, total_bits - shift);
+      int32_t* outp = shift + db >= total_bits ? final_out : bufs[pass & 1];
+      RECE_PHASE(RECE_PHASE_SORT, launch_counting_sort(pos, sorted, s, shift, nb, sc + p.o_sort, outp, nullptr, st),
+                 "sort positives");
+      sorted = outp;
+    }
+  }
   RECE_HIP(hipStreamWaitEvent(st, p.side.fork[c.rounds + 2], 0), "join the side stream");
   for (int rho = 1; rho < c.rounds && c.k > 0; ++rho) {
     DedupArgs dd{};
@@ -898,19 +914,9 @@ rece_status rece_backward(rece_plan_t plan, void* stream, const void* X, const v
     }
   }
   RECE_PHASE(RECE_PHASE_BWD_DX, launch_dx_lists(p.bf16, d, b, st), "dX");
-  // positives: LSD counting sort of positions by positive id and the per-piece
-  // sums (overlapping the side stream), then, once it is joined, the sums into dY
-  int32_t* bufs[2] = {reinterpret_cast<int32_t*>(sc + p.o_pp0), reinterpret_cast<int32_t*>(sc + p.o_pp1)};
-  const int total_bits = std::max(1, bits_for(C));
-  const int db = sort_digit_bits(s);
-  const int32_t* sorted = nullptr;
-  for (int pass = 0, shift = 0; shift < total_bits; ++pass, shift += db) {
-    const int nb = std::min(db, total_bits - shift);
-    int32_t* outp = bufs[pass & 1];
-    RECE_PHASE(RECE_PHASE_SORT, launch_counting_sort(pos, sorted, s, shift, nb, sc + p.o_sort, outp, nullptr, st),
-               "sort positives");
-    sorted = outp;
-  }
+  // positives: the per-piece sums over the positions the forward pass sorted by
+  // positive id (overlapping the side stream), then, once it is joined, the sums into dY
+  const int32_t* sorted = reinterpret_cast<const int32_t*>(sv + p.o_psort);
   float* parea = reinterpret_cast<float*>(sc + p.o_ppart);
   RECE_PHASE(RECE_PHASE_BWD_POS, launch_pos_pieces(p.bf16, d, b, sorted, parea, st), "positive dY");
   RECE_HIP(hipEventRecord(p.side.join, side), "join");
