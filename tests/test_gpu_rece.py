@@ -30,6 +30,9 @@ CASES = {
     "chunk_per_position": scaled("tiny", seqs=1, seqlen=40, C=400, n_b=5, n_c=40, k=3, rounds=2),
     "k_zero": scaled("sasrec", seqs=2, seqlen=64, C=700, n_b=4, n_c=4, k=0, rounds=1),
     "k_one_8_rounds": scaled("sasrec", seqs=2, seqlen=96, C=1000, n_b=6, n_c=6, k=1, rounds=8),
+    # earlier rounds' kept ids too many for the dedup's LDS tables ((rounds - 1) * k > 2048):
+    # the dedup scans the earlier lists; windows of three of four chunks overlap partly
+    "dedup_scan": scaled("tiny", seqs=1, seqlen=64, C=4000, n_b=4, n_c=4, k=2100, rounds=2),
 }
 
 
