@@ -315,11 +315,10 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 512) ? 2 : 1) void k_sel
     wave_sync();
     bool more = false;
     for (int rr = 0; rr < 16; ++rr) {
-      const int kkr = __shfl(kk, rr);
+      const int kkr = lane_val(kk, rr);
       if (kkr <= 0) continue;   // row settled in an earlier pass
-      const float xar = __shfl(xa, rr), mulr = __shfl(mul, rr), lo0r = __shfl(lo0, rr), sc0r = __shfl(sc0, rr);
-      const float off0r = __shfl(off0, rr);
-      const float betar = __shfl(beta, rr);
+      const float xar = lane_val(xa, rr), mulr = lane_val(mul, rr), lo0r = lane_val(lo0, rr);
+      const float sc0r = lane_val(sc0, rr), off0r = lane_val(off0, rr), betar = lane_val(beta, rr);
       uint32_t h[4];
       {
         const uint32_t w0 = L.hist[rr * HIST_STRIDE + 2 * l], w1 = L.hist[rr * HIST_STRIDE + 2 * l + 1];
@@ -329,13 +328,10 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 512) ? 2 : 1) void k_sel
         h[3] = w1 >> 16;
       }
       const uint32_t own = h[0] + h[1] + h[2] + h[3];
-      uint32_t suf = own;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_down(suf, o);
-        if (l + o < 64) suf += y;
-      }
-      const uint32_t total = __shfl(suf, 0);
+      // suffix sum (bins at or above this lane's four), from the prefix sum
+      const uint32_t pre = wave_prefix_incl(own);
+      const uint32_t total = lane_val(pre, 63);
+      const uint32_t suf = total - pre + own;
       int myb = -1;
       uint32_t my_above = 0, my_cnt = 0;
       {
@@ -357,7 +353,7 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 512) ? 2 : 1) void k_sel
         if (nz) {
           const int tl = 63 - __builtin_clzll(nz);
           const int hq = h[3] ? 3 : (h[2] ? 2 : (h[1] ? 1 : 0));
-          const int btop = 4 * tl + __shfl(hq, tl);
+          const int btop = 4 * tl + lane_val(hq, tl);
           const double top = ((double)(btop + 1) - (double)off0r) / (double)sc0r;
           mxr = f_up(top + (fabs(top) + fabs((double)lo0r)) * 1e-6 + 1e-30);
         }
@@ -370,9 +366,9 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 512) ? 2 : 1) void k_sel
         ntlo = nthi = NEG_INF;
       } else {
         const int src = 63 - __builtin_clzll(hit);
-        const int bstar = __shfl(myb, src);
-        const int above = (int)__shfl(my_above, src);
-        const int cnt = (int)__shfl(my_cnt, src);
+        const int bstar = lane_val(myb, src);
+        const int above = (int)lane_val(my_above, src);
+        const int cnt = (int)lane_val(my_cnt, src);
         nxa = xar + (float)bstar / mulr;   // exact: a multiple of 256^-L below 256
         nmul = mulr * (float)NBINS;
         // the bin is x in [nxa, nxa + 1/mul): its logit interval, padded for the rounding of x
@@ -473,7 +469,7 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 512) ? 2 : 1) void k_sel
           cge += (q.x >= v) + (u + 1 < n && q.y >= v) + (u + 2 < n && q.z >= v) + (u + 3 < n && q.w >= v);
         }
         const uint64_t at_k = ballot(l < n && cgt < kk && cge >= kk);
-        const float ak = __shfl(v, at_k ? __builtin_ctzll(at_k) : 0);
+        const float ak = lane_val(v, at_k ? (int)__builtin_ctzll(at_k) : 0);
         const float lo = f_down((double)ak - 2.0 * (double)beta);
         const float hi = f_up((double)ak + 2.0 * (double)beta);
         const int nabove = popc(ballot(l < n && v > hi));
@@ -568,8 +564,8 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 512) ? 2 : 1) void k_sel
         tid = 0;
         if (tm) {
           const int tl = __builtin_ctzll(tm);
-          te = __shfl(me, tl);
-          tid = __shfl(mj, tl);
+          te = lane_val(me, tl);
+          tid = lane_val(mj, tl);
         }
         if (na > 1) ++ntopk;
         const double b2 = (double)beta * (1.0 + 1e-6);

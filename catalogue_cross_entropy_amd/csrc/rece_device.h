@@ -50,6 +50,37 @@ __device__ __forceinline__ int wave_sum(int v) {
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
   return v;
 }
+// Value of `v` in lane `lane`, which must be the same in every active lane (a
+// scalar read of the register, no LDS round trip as with __shfl).
+__device__ __forceinline__ int lane_val(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
+__device__ __forceinline__ uint32_t lane_val(uint32_t v, int lane) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, lane);
+}
+__device__ __forceinline__ float lane_val(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+__device__ __forceinline__ double lane_val(double v, int lane) {
+  const uint64_t u = __double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Inclusive prefix sum over the 64 lanes (lane l gets the sum of lanes 0..l), in
+// registers with data-parallel-primitive moves: shifts within each 16-lane row,
+// then the last lane of row 0 (and of row 2) added to row 1 (row 3), then lane 31
+// added to rows 2 and 3.  Every lane must be active.
+__device__ __forceinline__ uint32_t wave_prefix_incl(uint32_t v) {
+  int p = (int)v;
+  p += __builtin_amdgcn_update_dpp(0, p, 0x111, 0xF, 0xF, true);   // row_shr:1
+  p += __builtin_amdgcn_update_dpp(0, p, 0x112, 0xF, 0xF, true);   // row_shr:2
+  p += __builtin_amdgcn_update_dpp(0, p, 0x114, 0xF, 0xF, true);   // row_shr:4
+  p += __builtin_amdgcn_update_dpp(0, p, 0x118, 0xF, 0xF, true);   // row_shr:8
+  p += __builtin_amdgcn_update_dpp(0, p, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+  p += __builtin_amdgcn_update_dpp(0, p, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+  return (uint32_t)p;
+}
+
 __device__ __forceinline__ float wave_sumf(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
