@@ -56,8 +56,6 @@ struct WaveLds {
   int32_t* ci;      // [WL] list index in the row's candidate list
   int32_t* cj;      // [WL] item id
   int32_t* cr;      // [WL] row
-  float* rf;        // [16][8] per-row floats
-  int32_t* ri;      // [16][8] per-row ints
 };
 // Row strides in LDS, padded so that the 16 rows of a wave start in different
 // banks (histogram: 129 words; lists: 68 entries, a multiple of four for the
@@ -68,7 +66,7 @@ constexpr size_t WAVE_UNION = (size_t)16 * HIST_STRIDE * 4 > (size_t)16 * LIST_S
                                   ? (size_t)16 * HIST_STRIDE * 4
                                   : (size_t)16 * LIST_STRIDE * 8;
 __host__ __device__ constexpr size_t wave_lds_bytes(int wl) {
-  return (size_t)wl * 8 + WAVE_UNION + (size_t)wl * (4 + 4 + 4) + 16 * 8 * 4 + 16 * 8 * 4;
+  return (size_t)wl * 8 + WAVE_UNION + (size_t)wl * (4 + 4 + 4);
 }
 
 __device__ inline WaveLds carve(char* base, int wl) {
@@ -85,15 +83,9 @@ __device__ inline WaveLds carve(char* base, int wl) {
   L.cj = reinterpret_cast<int32_t*>(p);
   p += (size_t)wl * 4;
   L.cr = reinterpret_cast<int32_t*>(p);
-  p += (size_t)wl * 4;
-  L.rf = reinterpret_cast<float*>(p);
-  p += 16 * 8 * 4;
-  L.ri = reinterpret_cast<int32_t*>(p);
   return L;
 }
 
-enum { RF_BETA = 0, RF_MX = 1, RF_SEXP = 2, RF_THI = 3, RF_NBUF = 4, RF_ALO = 5, RF_AHI = 6 };
-enum { RI_I = 0, RI_KK = 1, RI_NSURE = 2, RI_NNEW = 3, RI_NABOVE = 4, RI_AOFF = 5, RI_NA = 6, RI_MODE = 7 };
 
 // One ring slot: the tile's rows, then 64 item ids.
 __host__ __device__ constexpr size_t sel_slot_bytes(size_t row_bytes) { return row_bytes + 256; }
@@ -182,11 +174,8 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 512) ? 2 : 1) void k_sel
   int kk = rv ? k : 0;
   float tlo = (selall && rv) ? NEG_INF : __builtin_huge_valf(), thi = tlo;   // rows past the chunk keep +inf
   float mx = NEG_INF;   // row maximum (the exp shift), from the histogram pass
-  if (l < 16) {
-    // output row: the position id, or the sorted slot when outputs are per slot
-    L.ri[r * 8 + RI_I] = rv ? (p.slot_out ? (int)pA : iA) : -1;
-    L.rf[r * 8 + RF_BETA] = beta;
-  }
+  // output row: the position id, or the sorted slot when outputs are per slot
+  const int rowid = rv ? (p.slot_out ? (int)pA : iA) : -1;
   const int64_t orow = p.slot_out ? pA : (int64_t)rho * s + iA;   // negs row (valid rows only)
   const int64_t lrow = p.slot_out ? pA : (int64_t)iA;              // negl row (one round's lists)
 
@@ -416,40 +405,35 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 512) ? 2 : 1) void k_sel
     if (!NEGS) nsure += __shfl_xor(nsure, o);
   }
   nnew = nsure;
-  if (l < 16) {
-    L.rf[r * 8 + RF_MX] = mx;
-    L.rf[r * 8 + RF_SEXP] = sexp;
-    L.rf[r * 8 + RF_THI] = thi;
-    L.rf[r * 8 + RF_NBUF] = __int_as_float(bcnt);
-    L.ri[r * 8 + RI_NSURE] = nsure;
-    L.ri[r * 8 + RI_NNEW] = nnew;
-  }
-  wave_sync();
 
   // ---------------------------------------------------------------- epilogue
-  // Rows go through three steps in groups.  (A) Per row: sort its list (at most
-  // 64 entries, one per lane) by (float32 value desc, id asc) with a bitonic
-  // network; the float32 k-th value a_k sits at rank kk - 1 (kk = k minus the
-  // sure members) and the near-ties, the entries within 2*beta of a_k, form one
-  // run of the sorted list; they join the wave's float64 batch.  (B) Float64
-  // logits of the batch, one entry per lane.  (C) Per row: rank the near-ties by
-  // (float64 logit desc, id asc); the k-th kept element is the row's threshold;
-  // the kept list entries are the sorted prefix before the near-ties plus the
+  // Rows go through three steps in groups.  (A) Per row: the float32 k-th value
+  // a_k of its list (at most 64 entries, one per lane; kk = k minus the sure
+  // members) by counting the entries above and at or above each one; the
+  // near-ties, the entries within 2*beta of a_k, join the wave's float64 batch.
+  // (B) Float64 logits of the batch, one entry per lane.  (C) Per row: rank the
+  // near-ties by (float64 logit desc, id asc); the k-th kept element is the row's
+  // threshold; the kept list entries are those above the near-ties plus the
   // near-ties ranked within the count still missing.
+  // A row's state is the same in its four lanes (r, r + 16, r + 32, r + 48), so
+  // the steps read it with readlane from lane r; what (A) hands to (C) is kept in
+  // lane r of the ep_* registers.
+  int ep_mode = 0, ep_nabove = 0, ep_aoff = 0, ep_na = 0, ep_kk = 0;
+  float ep_lo = 0.0f, ep_hi = 0.0f;
   int r_next = 0;
   while (r_next < 16) {
     int tot = 0;
     int r_end = r_next;
     for (int r = r_next; r < 16; ++r) {
-      const int i = L.ri[r * 8 + RI_I];
+      const int i = lane_val(rowid, r);
       int mode_r = 0;   // 0: skip, 1: no near-ties (k == 0 or all kept), 2: near-tie list
-      if (i >= 0) mode_r = (k == 0 || L.rf[r * 8 + RF_THI] == NEG_INF) ? 1 : 2;
+      if (i >= 0) mode_r = (k == 0 || lane_val(thi, r) == NEG_INF) ? 1 : 2;
       if (mode_r == 2) {
-        const int nb_all = __float_as_int(L.rf[r * 8 + RF_NBUF]);
-        const int nsure = L.ri[r * 8 + RI_NSURE];
-        const float beta = L.rf[r * 8 + RF_BETA];
+        const int nb_all = lane_val(bcnt, r);
+        const int nsure_r = lane_val(nsure, r);
+        const float beta_r = lane_val(beta, r);
         const int n = min(nb_all, SEL_CAP);
-        int kk = k - nsure;
+        int kk = k - nsure_r;
         if (nb_all > SEL_CAP || kk < 1 || kk > n) {
           if (l == 0) {
             atomicAdd(p.counters + CNT_OVERFLOW, 1u);
@@ -470,8 +454,8 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 512) ? 2 : 1) void k_sel
         }
         const uint64_t at_k = ballot(l < n && cgt < kk && cge >= kk);
         const float ak = lane_val(v, at_k ? (int)__builtin_ctzll(at_k) : 0);
-        const float lo = f_down((double)ak - 2.0 * (double)beta);
-        const float hi = f_up((double)ak + 2.0 * (double)beta);
+        const float lo = f_down((double)ak - 2.0 * (double)beta_r);
+        const float hi = f_up((double)ak + 2.0 * (double)beta_r);
         const int nabove = popc(ballot(l < n && v > hi));
         const bool inb = l < n && v >= lo && v <= hi;
         const uint64_t inbm = ballot(inb);
@@ -490,17 +474,17 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 512) ? 2 : 1) void k_sel
           L.cj[tot + e] = id & 0x7FFFFFFF;
           L.cr[tot + e] = r;
         }
-        if (l == 0) {
-          L.rf[r * 8 + RF_AHI] = hi;
-          L.rf[r * 8 + RF_ALO] = lo;
-          L.ri[r * 8 + RI_NABOVE] = nabove;
-          L.ri[r * 8 + RI_AOFF] = tot;
-          L.ri[r * 8 + RI_NA] = na;
-          L.ri[r * 8 + RI_KK] = kk;
+        if (l == r) {
+          ep_hi = hi;
+          ep_lo = lo;
+          ep_nabove = nabove;
+          ep_aoff = tot;
+          ep_na = na;
+          ep_kk = kk;
         }
         tot += na;
       }
-      if (l == 0) L.ri[r * 8 + RI_MODE] = mode_r;
+      if (l == r) ep_mode = mode_r;
       r_end = r + 1;
     }
     wave_sync();
@@ -512,14 +496,14 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 512) ? 2 : 1) void k_sel
     wave_sync();
     // (C) thresholds and sums
     for (int r = r_next; r < r_end; ++r) {
-      const int mode_r = L.ri[r * 8 + RI_MODE];
+      const int mode_r = lane_val(ep_mode, r);
       if (mode_r == 0) continue;
-      const int i = L.ri[r * 8 + RI_I];
-      const float beta = L.rf[r * 8 + RF_BETA];
-      const float mx = L.rf[r * 8 + RF_MX];
-      float se = L.rf[r * 8 + RF_SEXP];
-      int nnew = L.ri[r * 8 + RI_NNEW];
-      const int nsure = L.ri[r * 8 + RI_NSURE];
+      const int i = lane_val(rowid, r);
+      const float beta_r = lane_val(beta, r);
+      const float mx_r = lane_val(mx, r);
+      float se = lane_val(sexp, r);
+      int nnew_r = lane_val(nnew, r);
+      const int nsure_r = lane_val(nsure, r);
       const int64_t o = p.slot_out ? (int64_t)i : (int64_t)rho * s + i;
       double te;
       int tid;
@@ -533,15 +517,15 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 512) ? 2 : 1) void k_sel
         te = -__builtin_huge_val();   // every candidate kept (all summed as sure members)
         tid = -1;
         tlo = thi = NEG_INF;
-        listed = nsure;
+        listed = nsure_r;
       } else {
-        const int n = min(__float_as_int(L.rf[r * 8 + RF_NBUF]), SEL_CAP);
-        const int nabove = L.ri[r * 8 + RI_NABOVE];
-        const int aoff = L.ri[r * 8 + RI_AOFF];
-        const int na = L.ri[r * 8 + RI_NA];
-        const int need = L.ri[r * 8 + RI_KK] - nabove;   // near-ties that are kept (>= 1)
+        const int n = min(lane_val(bcnt, r), SEL_CAP);
+        const int nabove = lane_val(ep_nabove, r);
+        const int aoff = lane_val(ep_aoff, r);
+        const int na = lane_val(ep_na, r);
+        const int need = lane_val(ep_kk, r) - nabove;   // near-ties that are kept (>= 1)
         // rank of this lane's near-tie (the e-th list entry within [lo, hi])
-        const float lo = L.rf[r * 8 + RF_ALO], hi = L.rf[r * 8 + RF_AHI];
+        const float lo = lane_val(ep_lo, r), hi = lane_val(ep_hi, r);
         const float a = l < n ? L.vals[r * LIST_STRIDE + l] : NEG_INF;
         const int jraw = l < n ? L.ids[r * LIST_STRIDE + l] : 0;
         const bool inb = l < n && a >= lo && a <= hi;
@@ -568,23 +552,23 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 512) ? 2 : 1) void k_sel
           tid = lane_val(mj, tl);
         }
         if (na > 1) ++ntopk;
-        const double b2 = (double)beta * (1.0 + 1e-6);
+        const double b2 = (double)beta_r * (1.0 + 1e-6);
         tlo = f_down(te - b2);
         thi = f_up(te + b2);
         // kept list entries: those above the near-ties and the near-ties ranked in
         const bool kept = l < n && (a > hi || rank < need);
-        se += wave_sumf(kept ? __expf(a - mx) : 0.0f);
-        nnew += popc(ballot(kept));
+        se += wave_sum_dpp(kept ? __expf(a - mx_r) : 0.0f);
+        nnew_r += popc(ballot(kept));
         if (NEGS) {
           const uint64_t km = ballot(kept);
           if (kept) {
-            const int slotn = nsure + popc(km & lanemask_lt());
+            const int slotn = nsure_r + popc(km & lanemask_lt());
             if (slotn < k) {
               p.negs[o * k + slotn] = jraw;
               if (p.negl) p.negl[(int64_t)i * k + slotn] = a;
             }
           }
-          listed = nsure + popc(km);
+          listed = nsure_r + popc(km);
         }
       }
       if (NEGS)
@@ -594,9 +578,9 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 512) ? 2 : 1) void k_sel
         p.thr_id[o] = tid;
         p.thr_lo[o] = tlo;
         p.thr_hi[o] = thi;
-        p.mshift[o] = mx;
+        p.mshift[o] = mx_r;
         p.ssum[o] = se;
-        p.nmem[o] = nnew;
+        p.nmem[o] = nnew_r;
       }
     }
     wave_sync();

@@ -81,6 +81,22 @@ __device__ __forceinline__ uint32_t wave_prefix_incl(uint32_t v) {
   return (uint32_t)p;
 }
 
+// Sum over the 64 lanes in a fixed order (the prefix pattern above, in float),
+// returned in every lane.  Every lane must be active.
+template <int CTRL, int ROWS, bool BC>
+__device__ __forceinline__ float dpp_movf(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xF, BC));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_movf<0x111, 0xF, true>(v);
+  v += dpp_movf<0x112, 0xF, true>(v);
+  v += dpp_movf<0x114, 0xF, true>(v);
+  v += dpp_movf<0x118, 0xF, true>(v);
+  v += dpp_movf<0x142, 0xA, false>(v);
+  v += dpp_movf<0x143, 0xC, false>(v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 __device__ __forceinline__ float wave_sumf(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
