@@ -89,8 +89,9 @@ typedef struct rece_plan_s* rece_plan_t;
  * aside, see rece_profile_enable); concurrent calls need their own scratch and
  * saved buffers.  At its first forward or backward call a plan creates one
  * extra HIP stream (default priority) and a few events on the current device,
- * and uses that device from then on: the item-side steps of the forward and the
- * dY chain of the backward run there, ordered with `stream` by events, so every
+ * and uses that device from then on: the item-side steps of the forward, the
+ * position-side steps and chunk kernels of rounds after the first, and the dY
+ * chain of the backward run there, ordered with `stream` by events, so every
  * result is complete in `stream` order when the call's work is.  Calls that
  * use this stream take a per-plan lock while they enqueue.  rece_plan_destroy
  * releases the stream and events (the caller makes sure no call is still
