@@ -191,10 +191,24 @@ def main():
         plan.forward(X, Y, pos, B, scratch, saved, loss_pp=False)
         plan.backward(X, Y, pos, scratch, saved, dloss=dloss, dX=dX, dY=dY)
 
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats(dev)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     plan.check(saved)
+    # device memory of a whole step: the library allocates nothing itself, so torch's peak
+    # covers inputs, outputs and the two workspaces; a dense bf16 [s, C] logit tensor must
+    # be larger than every buffer the step holds
+    logit_bytes = 2 * w.s * w.C
+    largest = max(scratch.numel(), saved.numel(), dX.numel() * 4, dY.numel() * 4,
+                  X.numel() * X.element_size(), Y.numel() * Y.element_size())
+    memory = {"scratch_bytes": plan.scratch_bytes, "saved_bytes": plan.saved_bytes,
+              "peak_allocated_bytes": torch.cuda.max_memory_allocated(dev),
+              "largest_buffer_bytes": largest, "dense_logits_bf16_bytes": logit_bytes,
+              "no_dense_logits": largest < logit_bytes}
+    if not memory["no_dense_logits"]:
+        sys.exit(f"a buffer of {largest} bytes is at least the size of a dense [s, C] logit tensor")
 
     # phase breakdown on a few untimed steps (events around every launch)
     plan.profile()
@@ -255,6 +269,7 @@ def main():
                                 + f"{w.dtype}, positives {w.positives}"), "parallelism": "single GPU"},
         "roofline": rl,
         "phases": breakdown,
+        "memory": memory,
         "counters": {"argmax_rows_float64": counters[1], "topk_rows_near_tie": counters[2],
                      "logits_float64": counters[3], "overflows": counters[4]},
     }
