@@ -272,12 +272,12 @@ __global__ __launch_bounds__(256) void k_project_argmax(
     if (norms && l < 16 && rA < n) norms[rA] = my_norm[f];
   }
   if (norm_max_bits) {
-    // one atomic per wave: the largest norm of its rows (rows past n count 0)
+    // the largest norm of the wave's rows (rows past n count 0), at most one atomic
     float mx = 0.0f;
 #pragma unroll
     for (int f = 0; f < RF; ++f) mx = fmaxf(mx, my_norm[f]);
     mx = wave_max(mx);
-    if (l == 0) atomicMax(norm_max_bits, __float_as_uint(mx));
+    if (l == 0) raise_max_bits(norm_max_bits, mx);
   }
 }
 

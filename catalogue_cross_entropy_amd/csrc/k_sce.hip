@@ -74,9 +74,9 @@ __global__ __launch_bounds__(256) void k_project_scores(const E* __restrict__ V,
     if (norms && l < 16 && r < n) norms[r] = nrm;
     nmx = fmaxf(nmx, nrm);
   }
-  if (norm_max_bits) {   // one atomic per wave
+  if (norm_max_bits) {   // at most one atomic per wave
     nmx = wave_max(nmx);
-    if (l == 0) atomicMax(norm_max_bits, __float_as_uint(nmx));
+    if (l == 0) raise_max_bits(norm_max_bits, nmx);
   }
 
   for (int b0 = 0; b0 < n_b; b0 += TB) {

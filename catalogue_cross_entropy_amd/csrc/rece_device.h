@@ -40,6 +40,15 @@ __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   return v;
 }
+// Raise the device word *bits (a non-negative float's bit pattern, which orders
+// like the float) to v.  The atomic is skipped when the stored value already
+// covers v: the stored value only grows, so a stale read can cost an extra atomic
+// but never loses one.  Thousands of waves raising one word otherwise queue on
+// that address (same-address atomics run one at a time).
+__device__ __forceinline__ void raise_max_bits(uint32_t* bits, float v) {
+  const uint32_t b = __float_as_uint(v);
+  if (__hip_atomic_load(bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < b) atomicMax(bits, b);
+}
 __device__ __forceinline__ float wave_min(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fminf(v, __shfl_xor(v, o));
