@@ -44,18 +44,19 @@ constexpr int MAX_REFINE = 2;    // histogram passes that may split a crowded bi
 constexpr float X_TOP = 255.99998f;   // largest histogram coordinate (below 256)
 constexpr float LOG2E_F = 1.44269504088896341f;
 
-// Per-wave LDS region.  WL: near-tie entries of one wave awaiting float64 values
-// (128; 64 for 512-byte vectors, whose workgroups need the room to fit two per CU).
+// Per-wave LDS: the row histograms / candidate lists, and the batch of WL near-tie
+// entries awaiting float64 values.  The batch is used only after the streaming
+// passes, so it lives in the window ring, which is idle by then.
 
 struct WaveLds {
-  double* ce;       // [WL]
+  double* ce;       // [WL] (in the ring)
   uint32_t* hist;   // [16][HIST_STRIDE] two 16-bit counts per word (histogram passes),
                     // aliased by vals/ids (collect pass)
   float* vals;      // [16][LIST_STRIDE] (SEL_CAP used)
   int32_t* ids;     // [16][LIST_STRIDE]
-  int32_t* ci;      // [WL] list index in the row's candidate list
-  int32_t* cj;      // [WL] item id
-  int32_t* cr;      // [WL] row
+  int32_t* ci;      // [WL] list index in the row's candidate list (in the ring)
+  int32_t* cj;      // [WL] item id (in the ring)
+  int32_t* cr;      // [WL] row (in the ring)
 };
 // Row strides in LDS, padded so that the 16 rows of a wave start in different
 // banks (histogram: 129 words; lists: 68 entries, a multiple of four for the
@@ -65,19 +66,18 @@ constexpr int LIST_STRIDE = SEL_CAP + 4;
 constexpr size_t WAVE_UNION = (size_t)16 * HIST_STRIDE * 4 > (size_t)16 * LIST_STRIDE * 8
                                   ? (size_t)16 * HIST_STRIDE * 4
                                   : (size_t)16 * LIST_STRIDE * 8;
-__host__ __device__ constexpr size_t wave_lds_bytes(int wl) {
-  return (size_t)wl * 8 + WAVE_UNION + (size_t)wl * (4 + 4 + 4);
-}
+constexpr size_t WAVE_LDS = WAVE_UNION;
+constexpr size_t BATCH_ENTRY = 8 + 4 + 4 + 4;   // ce, ci, cj, cr
 
-__device__ inline WaveLds carve(char* base, int wl) {
+// base: the wave's histogram/list region; batch: the wave's part of the ring
+__device__ inline WaveLds carve(char* base, char* batch, int wl) {
   WaveLds L;
-  char* p = base;
+  L.hist = reinterpret_cast<uint32_t*>(base);
+  L.vals = reinterpret_cast<float*>(base);
+  L.ids = reinterpret_cast<int32_t*>(base + 16 * LIST_STRIDE * 4);
+  char* p = batch;
   L.ce = reinterpret_cast<double*>(p);
   p += (size_t)wl * 8;
-  L.hist = reinterpret_cast<uint32_t*>(p);
-  L.vals = reinterpret_cast<float*>(p);
-  L.ids = reinterpret_cast<int32_t*>(p + 16 * LIST_STRIDE * 4);
-  p += WAVE_UNION;
   L.ci = reinterpret_cast<int32_t*>(p);
   p += (size_t)wl * 4;
   L.cj = reinterpret_cast<int32_t*>(p);
@@ -93,12 +93,16 @@ __host__ __device__ constexpr size_t sel_common_lds(size_t row_bytes, int ring) 
   return (size_t)ring * sel_slot_bytes(row_bytes) + 16;
 }
 
-// Ring slots (tiles in flight: RING - 1) and near-tie batch: 512-byte vectors
-// take a two-slot ring and a 64-entry batch, so that two workgroups share a CU.
-template <class E, int D> struct SelGeom {
-  static constexpr bool WIDE = D * (int)sizeof(E) >= 512;
-  static constexpr int RING = WIDE ? 2 : 3;
-  static constexpr int WL = WIDE ? 64 : 128;
+// Ring slots (one tile in flight while the other is read) and the near-tie batch
+// per wave: 128 entries where NW waves' batches fit in the ring, else 64.  Up to
+// 256-byte vectors a workgroup of four waves then takes 51.7 KB of LDS, so three
+// share a CU (a third wave per SIMD hides more of the copy and LDS latency than a
+// third ring slot did).
+template <class E, int D, int NW> struct SelGeom {
+  static constexpr int RING = 2;
+  static constexpr size_t RING_BYTES = (size_t)RING * sel_slot_bytes(TileGeom<E, D>::ROW_BYTES);
+  static constexpr int WL = (size_t)NW * 128 * BATCH_ENTRY <= RING_BYTES ? 128 : 64;
+  static_assert((size_t)NW * WL * BATCH_ENTRY <= RING_BYTES, "near-tie batches must fit in the ring");
 };
 
 // NEGS: the kept ids are written out (p.negs set); a template flag keeps that
@@ -118,10 +122,11 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 512) ? 2 : 1) void k_sel
   const int64_t s = p.s, C = p.C;
   const size_t slot_bytes = sel_slot_bytes(G::ROW_BYTES);
   char* ring = smem;
-  constexpr int RING = SelGeom<E, D>::RING, WLIST = SelGeom<E, D>::WL;
+  constexpr int RING = SelGeom<E, D, NW>::RING, WLIST = SelGeom<E, D, NW>::WL;
   int32_t* wg_flag = reinterpret_cast<int32_t*>(smem + RING * slot_bytes);
   const int w = threadIdx.x >> 6, l = lane_id(), g = l >> 4;
-  WaveLds L = carve(smem + sel_common_lds(G::ROW_BYTES, RING) + (size_t)w * wave_lds_bytes(WLIST), WLIST);
+  WaveLds L = carve(smem + sel_common_lds(G::ROW_BYTES, RING) + (size_t)w * WAVE_LDS,
+                    smem + (size_t)w * WLIST * BATCH_ENTRY, WLIST);
   (void)X;
   (void)n_c;
   uint32_t nexact = 0;   // float64 logits computed by this lane
@@ -388,6 +393,10 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 512) ? 2 : 1) void k_sel
     mode = *wg_flag ? 0 : 1;
   }
 
+  // every wave has read its last ring tile and no copy is in flight: the ring now
+  // holds the near-tie batches
+  __syncthreads();
+
   // ---- publish the per-row sums of the sure members (combine the row's four lanes)
 #pragma unroll
   for (int o = 16; o < 64; o <<= 1) {
@@ -444,13 +453,13 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 512) ? 2 : 1) void k_sel
         const float v = l < n ? L.vals[r * LIST_STRIDE + l] : NEG_INF;
         const int id = l < n ? L.ids[r * LIST_STRIDE + l] : 0x7FFFFFFF;
         // a_k, the kk-th largest float value of the list: the value v of the lane with
-        // (#entries above v) < kk <= (#entries at or above v); the entries are counted
-        // against every list entry, read four at a time (one broadcast LDS read)
+        // (#entries above v) < kk <= (#entries at or above v); every lane counts against
+        // each list entry, taken from the lane that holds it (readlane: no memory trip)
         int cgt = 0, cge = 0;
-        for (int u = 0; u < n; u += 4) {
-          const float4 q = *reinterpret_cast<const float4*>(&L.vals[r * LIST_STRIDE + u]);
-          cgt += (q.x > v) + (u + 1 < n && q.y > v) + (u + 2 < n && q.z > v) + (u + 3 < n && q.w > v);
-          cge += (q.x >= v) + (u + 1 < n && q.y >= v) + (u + 2 < n && q.z >= v) + (u + 3 < n && q.w >= v);
+        for (int u = 0; u < n; ++u) {
+          const float q = lane_val(v, u);
+          cgt += q > v;
+          cge += q >= v;
         }
         const uint64_t at_k = ballot(l < n && cgt < kk && cge >= kk);
         const float ak = lane_val(v, at_k ? (int)__builtin_ctzll(at_k) : 0);
@@ -592,8 +601,7 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 512) ? 2 : 1) void k_sel
 
 template <class E, int D>
 static size_t select_lds_bytes_t(int waves) {
-  return sel_common_lds(TileGeom<E, D>::ROW_BYTES, SelGeom<E, D>::RING) +
-         (size_t)waves * wave_lds_bytes(SelGeom<E, D>::WL);
+  return sel_common_lds(TileGeom<E, D>::ROW_BYTES, SelGeom<E, D, 4>::RING) + (size_t)waves * WAVE_LDS;
 }
 size_t select_lds_bytes(bool is_bf16, int d, int waves, int rounds) {
   (void)rounds;   // every round selects on its own: the LDS does not grow with rounds
