@@ -117,8 +117,10 @@ __device__ __forceinline__ int argmax_exact_wave(const E* __restrict__ x, const 
 // second-best scores are kept branch-free (the second best is the median of
 // best, second and the new score); equal scores leave best = second, which
 // sends the row to the float64 decision (lowest index among exact ties).
+// 256-byte rows: three workgroups per CU (168 registers, a few spilled), which
+// hides more latency than the fourth of the registers it gives up.
 template <class E, int D, int RF>
-__global__ __launch_bounds__(256) void k_project_argmax(
+__global__ __launch_bounds__(256, (D * sizeof(E) == 256) ? 3 : 1) void k_project_argmax(
     const E* __restrict__ V, int64_t n, const E* __restrict__ Bt, int n_b,
     const float* __restrict__ bnorm_max, float beta_coef, int32_t* __restrict__ ids,
     float* __restrict__ norms, uint32_t* __restrict__ norm_max_bits, int32_t* __restrict__ und,
