@@ -5,6 +5,8 @@ k-th kept negative) and kept-negative sets are compared exactly: both sides
 take every selection decision on the float64 coordinate-order scalar product.
 Loss within 1e-5 relative (float32 inputs) or 1e-3 (bf16 inputs); gradients
 within 2e-3 of max|grad| (max-abs error normalised)."""
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -114,3 +116,30 @@ def test_run_twice_bit_identical():
     assert a["loss"] == b["loss"]
     assert np.array_equal(a["loss_pp"], b["loss_pp"])
     assert np.array_equal(a["dX"], b["dX"]) and np.array_equal(a["dY"], b["dY"])
+
+
+def test_exact_topk_ties_from_duplicate_items():
+    """Every item row appears four times (ids j, j + U, j + 2U, j + 3U): equal logits
+    at most k-th boundaries, so each row sends several entries through the float64
+    ranking, and the ties must go to the lowest ids as in the oracle."""
+    w = scaled("sasrec", seqs=2, seqlen=200, C=4000, n_b=8, n_c=8, k=64, rounds=2)
+    inp = make_inputs(w)
+    U = w.C // 4
+    Y = np.ascontiguousarray(inp.Y[np.arange(w.C) % U])
+    inp = dataclasses.replace(inp, Y=Y)
+    print("[gpu] duplicate items, C=4000 (1000 distinct rows)", flush=True)
+    g = run_rece(inp)
+    fwd = oracle.rece_forward(inp.X, inp.Y, inp.pos, inp.B, w.n_c, w.k)
+    _compare("duplicate_items", inp, g, fwd)
+    # the ties are real: most rows' k-th kept item has an equal copy left out
+    tied = 0
+    for i in range(w.s):
+        ids, _, thr = fwd["negs"][0][i]
+        if thr is not None:
+            kept = set(int(j) for j in ids)
+            tied += any(int(c) not in kept and int(c) != int(inp.pos[i])
+                        for c in (thr[1] % U + U * np.arange(4)))
+    assert tied > w.s // 4, tied
+    assert g["counters"][2] > 0   # rows whose k-th element needed the float64 ranking
+    gX, gY = oracle.rece_backward(inp.X, inp.Y, inp.pos, fwd)
+    assert grad_err(g["dX"], gX) <= 2e-3 and grad_err(g["dY"], gY) <= 2e-3
