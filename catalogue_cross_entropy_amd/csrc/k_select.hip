@@ -108,7 +108,7 @@ template <class E, int D, int NW> struct SelGeom {
 // NEGS: the kept ids are written out (p.negs set); a template flag keeps that
 // code out of the streaming loop when they are not.
 template <class E, int D, int NW, bool NEGS>
-__global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 512) ? 2 : 1) void k_select(SelectArgs p) {
+__global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 256) ? 3 : ((D * sizeof(E) <= 512) ? 2 : 1)) void k_select(SelectArgs p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   using G = TileGeom<E, D>;
   constexpr int TI = G::TI;
