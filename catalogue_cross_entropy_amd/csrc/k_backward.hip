@@ -639,28 +639,29 @@ __global__ __launch_bounds__(256) void k_pos_combine(float* __restrict__ dY, con
   const int64_t piece = (int64_t)blockIdx.x * 4 + w;
   if (piece >= npieces) return;
   {
+    // the piece's staged runs, each added once to its item's row: 16 bytes per lane,
+    // RPI rows per instruction, BATCH instructions in flight
+    static_assert(D % 4 == 0 && D <= 256, "rows of whole 16-byte chunks, at most 64 per row");
+    constexpr int LPR = D / 4, RPI = 64 / LPR, BATCH = 8;
+    const int q = l / LPR, sub = l % LPR;
     const int ns = stage.n[piece];
-    constexpr int BATCH = 8;
-    for (int e0 = 0; e0 < ns; e0 += BATCH) {
-      float rv[BATCH][PER], yv[BATCH][PER];
+    for (int e0 = 0; e0 < ns; e0 += RPI * BATCH) {
+      float4 rv[BATCH], yv[BATCH];
       int64_t base[BATCH];
 #pragma unroll
       for (int e = 0; e < BATCH; ++e) {
-        const bool in = e0 + e < ns;
-        const int64_t slot = piece * PIECE + e0 + (in ? e : 0);
-        base[e] = (int64_t)stage.items[slot] * D;
-#pragma unroll
-        for (int u = 0; u < PER; ++u) {
-          const bool ok = in && l + 64 * u < D;
-          rv[e][u] = ok ? stage.rows[slot * D + l + 64 * u] : 0.0f;
-          yv[e][u] = ok ? dY[base[e] + l + 64 * u] : 0.0f;
-        }
+        const int idx = e0 + e * RPI + q;
+        const bool in = q < RPI && idx < ns;
+        const int64_t slot = piece * PIECE + (in ? idx : 0);
+        base[e] = (int64_t)stage.items[slot] * D + 4 * sub;
+        rv[e] = in ? *reinterpret_cast<const float4*>(stage.rows + slot * D + 4 * sub) : float4{0.f, 0.f, 0.f, 0.f};
+        yv[e] = in ? *reinterpret_cast<const float4*>(dY + base[e]) : float4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
       for (int e = 0; e < BATCH; ++e)
-#pragma unroll
-        for (int u = 0; u < PER; ++u)
-          if (e0 + e < ns && l + 64 * u < D) dY[base[e] + l + 64 * u] = yv[e][u] + rv[e][u];
+        if (q < RPI && e0 + e * RPI + q < ns)
+          *reinterpret_cast<float4*>(dY + base[e]) =
+              float4{yv[e].x + rv[e].x, yv[e].y + rv[e].y, yv[e].z + rv[e].z, yv[e].w + rv[e].w};
     }
   }
   if (!(pflag[piece] & 4)) return;
