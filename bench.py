@@ -53,9 +53,7 @@ def algorithmic_work_sce(w):
         "sort": (0.0, nb * (s + C) * 4 + (sx + sy) * (d * es + 8)),      # score columns, bucket rows
         "select": (float(ALU_OPS_PER_LOGIT * logits), (sx + sy) * d * es + sx * w.k * 8),
         "loss": (2.0 * d * s, s * (2 * d * es + 24)),
-        "bwd_dx": (2.0 * d * logits, (sx + sy) * d * es + sx * d * 4 + s * d * 4),
-        "bwd_dy": (2.0 * d * logits, (sx + sy) * d * es + sy * d * 4 + C * d * 4),
-        "bwd_pos": (2.0 * d * s, s * (d * es + 16) + s * d * 4),
+        **backward_work(w, 1),
     }
 
 
@@ -74,10 +72,25 @@ def algorithmic_work(w):
         "select": (float(ALU_OPS_PER_LOGIT * wl * r),
                    r * ((s + C) * d * es + 8 * (s + C) + state * s + s * w.k * 4)),   # + kept lists
         "loss": (2.0 * d * s, s * (2 * d * es + 12 + 12 * r)),
+        **backward_work(w, r),
+    }
+
+
+def backward_work(w, r):
+    """Backward phases (both variants): dX from the kept lists; the (item, position)
+    records of the lists and positives sorted by item; dY from the sorted records."""
+    es = 2 if w.dtype == "bf16" else 4
+    s, C, d = w.s, w.C, w.d
+    pairs = r * s * w.k + s
+    kb = max(1, (C - 1).bit_length())
+    npass = (kb + 11) // 12
+    return {
         # kept lists, every vector once, per-position state, dX
-        "bwd_dx": (2.0 * d * (w.k * r + 1) * s, r * s * w.k * 4 + (s + C) * d * es + 12 * s + s * d * 4),
-        "bwd_dy": (2.0 * d * w.k * r * s, r * ((s + C) * d * es + state * s) + C * d * 4),
-        "bwd_pos": (2.0 * d * s, s * (d * es + 16) + s * d * 4),
+        "bwd_dx": (2.0 * 2 * d * (w.k * r + 1) * s, r * s * w.k * 4 + (s + C) * d * es + 12 * s + s * d * 4),
+        # read the lists once, then each pass reads and writes 8-byte records
+        "bwd_sort": (0.0, r * s * w.k * 4 + s * 4 + npass * 16 * pairs),
+        # sorted records, every vector once, per-position state, dY written once
+        "bwd_dy": (2.0 * 2 * d * pairs, 8 * pairs + (s + C) * d * es + 12 * s + C * d * 4),
     }
 
 

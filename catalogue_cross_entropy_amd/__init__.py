@@ -20,6 +20,7 @@ FLAG_VALIDATE_IDS, FLAG_KEEP_STAGES = 1, 2
 STAGES = {
     "bucket_x": 0, "bucket_y": 1, "perm_x": 2, "perm_y": 3, "thresh_id": 4,
     "thresh_logit": 5, "neg_ids": 6, "lse": 7, "counters": 8, "sce_rows": 9, "sce_items": 10,
+    "union_ids": 11,
 }
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small",
           4: "HIP runtime error", 5: "device check failed", 6: "internal error"}
@@ -28,14 +29,16 @@ EXPORTED = ["rece_plan", "rece_plan_destroy", "rece_workspace_bytes", "rece_forw
             "rece_backward", "rece_export", "rece_export_bytes", "rece_check",
             "rece_profile_enable", "rece_profile_read",
             "rece_status_string", "rece_last_error", "rece_version"]
-PHASES = ["project", "sort", "select", "loss", "bwd_dx", "bwd_dy", "bwd_pos", "other"]
+PHASES = ["project", "sort", "select", "loss", "bwd_dx", "bwd_dy", "bwd_sort", "other"]
 
 
 class ReceConfig(ctypes.Structure):
+    """Mirror of rece_config in include/rece.h (field order and types)."""
     _fields_ = [("s", ctypes.c_int64), ("C", ctypes.c_int64), ("d", ctypes.c_int32),
-                ("n_b", ctypes.c_int32), ("n_c", ctypes.c_int32), ("k", ctypes.c_int32),
-                ("rounds", ctypes.c_int32), ("b_x", ctypes.c_int32), ("b_y", ctypes.c_int32),
-                ("dtype", ctypes.c_int32), ("variant", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+                ("n_b", ctypes.c_int32), ("n_c", ctypes.c_int32), ("n_ec", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("rounds", ctypes.c_int32), ("b_x", ctypes.c_int32),
+                ("b_y", ctypes.c_int32), ("dtype", ctypes.c_int32), ("variant", ctypes.c_int32),
+                ("window_wrap", ctypes.c_int32), ("flags", ctypes.c_uint32)]
 
 
 class ReceError(RuntimeError):
@@ -98,10 +101,12 @@ class Plan:
 
     def __init__(self, s: int, C: int, d: int, n_b: int, n_c: int, k: int, rounds: int = 1,
                  dtype: str = "bf16", variant: str = "rece", b_x: int = 0, b_y: int = 0,
-                 keep_stages: bool = False, validate_ids: bool = False):
-        self.cfg = ReceConfig(s, C, d, n_b, n_c, k, rounds, b_x, b_y,
+                 keep_stages: bool = False, validate_ids: bool = False, n_ec: int = 1,
+                 window_wrap: bool = True):
+        self.cfg = ReceConfig(s, C, d, n_b, n_c, n_ec, k, rounds, b_x, b_y,
                               RECE_BF16 if dtype == "bf16" else RECE_F32,
                               RECE_VARIANT_SCE if variant == "sce" else RECE_VARIANT_RECE,
+                              int(window_wrap),
                               (FLAG_KEEP_STAGES if keep_stages else 0)
                               | (FLAG_VALIDATE_IDS if validate_ids else 0))
         self.dtype = dtype
@@ -125,12 +130,21 @@ class Plan:
         for name, t, shape in (("X", X, (c.s, c.d)), ("Y", Y, (c.C, c.d))):
             if t.dtype != want or tuple(t.shape) != shape or not t.is_cuda or not t.is_contiguous():
                 raise ValueError(f"{name} must be a contiguous CUDA {want} tensor of shape {shape}")
-        if pos.dtype != torch.int32 or tuple(pos.shape) != (c.s,) or not pos.is_cuda:
-            raise ValueError(f"pos must be a CUDA int32 tensor of shape ({c.s},)")
+        if (pos.dtype != torch.int32 or tuple(pos.shape) != (c.s,) or not pos.is_cuda
+                or not pos.is_contiguous()):
+            raise ValueError(f"pos must be a contiguous CUDA int32 tensor of shape ({c.s},)")
+        for name, t in (("Y", Y), ("pos", pos)) + ((("B", B),) if B is not None else ()):
+            if t.device != X.device:
+                raise ValueError(f"{name} must be on the same device as X ({X.device})")
         if B is not None:
             shape = (c.rounds, c.d, c.n_b) if c.variant == RECE_VARIANT_RECE else (c.d, c.n_b)
             if B.dtype != want or tuple(B.shape) != shape or not B.is_cuda or not B.is_contiguous():
                 raise ValueError(f"B must be a contiguous CUDA {want} tensor of shape {shape}")
+
+    def _check_workspace(self, scratch, saved, device):
+        for name, t, size in (("scratch", scratch, self.scratch_bytes), ("saved", saved, self.saved_bytes)):
+            if t.device != device or t.numel() * t.element_size() < size or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous buffer of at least {size} bytes on {device}")
 
     def workspace(self, device="cuda"):
         import torch
@@ -144,6 +158,7 @@ class Plan:
         self._check_inputs(X, Y, pos, B)
         if scratch is None or saved is None:
             scratch, saved = self.workspace(X.device)
+        self._check_workspace(scratch, saved, X.device)
         loss = torch.empty(1, dtype=torch.float32, device=X.device)
         lpp = torch.empty(self.cfg.s, dtype=torch.float32, device=X.device) if loss_pp else None
         _check(lib().rece_forward(self._h, _stream(stream), _ptr(X), _ptr(Y), _ptr(pos), _ptr(B),
@@ -162,6 +177,14 @@ class Plan:
             dX = torch.empty((c.s, c.d), dtype=torch.float32, device=X.device)
         if dY is None:
             dY = torch.empty((c.C, c.d), dtype=torch.float32, device=X.device)
+        for name, t, shape in (("dX", dX, (c.s, c.d)), ("dY", dY, (c.C, c.d)), ("dloss", dloss, (1,)),
+                               ("dloss_pp", dloss_pp, (c.s,))):
+            if t is None:
+                continue
+            if (t.dtype != torch.float32 or tuple(t.shape) != shape or not t.is_contiguous()
+                    or t.device != X.device):
+                raise ValueError(f"{name} must be a contiguous float32 tensor of shape {shape} on {X.device}")
+        self._check_workspace(scratch, saved, X.device)
         _check(lib().rece_backward(self._h, _stream(stream), _ptr(X), _ptr(Y), _ptr(pos),
                                    _ptr(dloss), _ptr(dloss_pp), _ptr(scratch), _ptr(saved),
                                    _ptr(dX), _ptr(dY)))
@@ -178,6 +201,9 @@ class Plan:
         _check(lib().rece_export(self._h, _stream(stream), _ptr(saved), st, round, _ptr(out)))
         if stage == "neg_ids":
             out = out.view(self.cfg.s, max(self.cfg.k, 1))
+        elif stage == "union_ids":
+            r = self.cfg.rounds if self.cfg.variant == RECE_VARIANT_RECE else 1
+            out = out.view(self.cfg.s, r * max(self.cfg.k, 1))
         elif stage == "sce_rows":
             out = out.view(self.cfg.n_b, self.cfg.b_x)
         elif stage == "sce_items":

@@ -1,424 +1,49 @@
 // Backward pass: d loss / d X and d loss / d Y with the selection held fixed
 // (RECE page, Section 3, Eq. 4: softmax minus one-hot, restricted to the scored
-// set {positive} u kept negatives; chained through logit = x . y).
+// set {positive} u kept negatives, chained through logit = x . y).
 //
-// The position side reads the forward pass's kept lists; the item side has no
-// list by item, so it walks the same chunk windows as the forward pass,
-// recomputes the logits on the matrix cores, and decides membership of a pair
-// against the per-position thresholds saved by the forward pass (float32 bounds
-// first, float64 recomputation inside the bounds).  A pair already kept in an
-// earlier round is skipped, so every kept pair counts once.
-//   * k_dx_lists (RECE): per position, dX = sum over its listed pairs of
-//     gbar exp(logit - lse) y_j plus the positive term: one gathered row per pair;
-//   * k_bwd_rows (bucket variant): per (bucket, position tile), G . Y_window, G the 16x64
-//     gradient block of the tile, kept in registers in the operand layout of the
-//     product (bf16 hi+lo split for bf16 inputs, so G keeps ~16 significant bits;
-//     float32 matrix cores for float32 inputs);
-//   * k_bwd_items: per (item chunk, item tile), dY += G^T . X over the positions
-//     of the three X-chunks whose windows hold the tile - a reduction grouped by
-//     item in sorted order, no atomics;
-//   * positives: positions sorted by positive id (LSD counting sort), then a
-//     segmented reduction in fixed-size pieces plus an in-order combine of the
-//     pieces of long segments.
-// Rounds run one after the other on the stream; round 0 writes dX and dY, later
-// rounds add, so every sum has a fixed order (bit-reproducible).
+// Both sides read the kept lists the forward pass wrote, negs[r][s][k] (item
+// ids, -1 padded, bit 31 set on a pair an earlier round also kept, so every
+// pair counts once), plus lse and the positive logit of each position.  No
+// window is revisited and no float atomics are used: every sum has a fixed
+// order and two runs give identical bits.
+//   * dX (k_dx_lists): one wave per position gathers the Y rows of its list
+//     entries and adds g * y_j, then the positive term;
+//   * dY: the pairs (item, position) of all lists plus one pair per position
+//     for its positive are sorted by item with a stable LSD counting sort of
+//     (key, value) records; the sorted array is cut into fixed sub-pieces of
+//     DY_SUB pairs, one lane group per sub-piece walks its pairs in order and
+//     sums g * x_i per item; an item that spans sub-pieces leaves partial rows
+//     that a second kernel adds in sub-piece order.  Every row of dY is
+//     written once (items no pair names get zero rows).
 #include "rece_device.h"
 #include "rece_internal.h"
-#include "rece_stream.h"
 
 namespace rece {
 
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
 // Upstream gradient of position i's loss.
 __device__ __forceinline__ float gbar_of(const BwdArgs& p, int64_t i) {
-  return p.dloss_pp ? p.dloss_pp[i] : p.dloss[0] / (float)p.npos;
+  return p.dloss_pp ? p.dloss_pp[i] : p.dloss[0] / (float)p.s;
 }
 
-// Bucket variant: a pair (position, item) met in a bucket counts there only if no
-// earlier bucket of the position (the first m entries of its group, starting at
-// `start` in sce_sorted) also took the item.
-__device__ __forceinline__ bool sce_seen_before(const BwdArgs& p, int start, int m, int j) {
-  for (int e = 0; e < m; ++e) {
-    const int b2 = p.sce_sorted[start + e] / p.b_x;
-    if ((p.qbits[(int64_t)b2 * p.qwords + (j >> 5)] >> (j & 31)) & 1u) return true;
-  }
-  return false;
-}
-
-// LDS address of the transpose read giving four 16-bit values of coordinate
-// 16*nb + (l % 16) for items r0 .. r0 + 3 of a swizzled bf16 tile, r0 = base +
-// 4*(l/16) (ds_read_b64_tr_b16).  Within each 16-lane group, source lane j names
-// 4 coordinates of one item (item r0 + j/4, coordinates 16*nb + 4*(j%4) .. +3);
-// the read hands lane i coordinate i of the group's 4 items.
-template <int D>
-__device__ __forceinline__ const char* tile_tr4_addr(const char* rows, int base, int nb) {
-  using G = TileGeom<bf16, D>;
-  const int l = lane_id(), j = l & 15;
-  const int row = base + 4 * (l >> 4) + (j >> 2);
-  const int dim0 = 16 * nb + 4 * (j & 3);
-  const int ch = (dim0 >> 3) ^ (row & G::SWM);
-  return rows + row * G::RB + ch * 16 + ((dim0 >> 2) & 1) * 8;
-}
-
-// acc[nb] += G[16 positions][TI items] . tile[TI items][D] where lane l holds
-// G[position l % 16][item 16*cb + 4*(l/16) + v] in gv[cb][v].  bf16: G split into
-// bf16 hi + lo (~16 significant bits), k = 32 items per step, item order
-// (4 of block 2ks, 4 of block 2ks+1) on both operands; f32: k = 4 items per step.
-template <class E, int D>
-__device__ __forceinline__ void accumulate_rows(f32x4 (&acc)[D / 16], const float (&gv)[TileGeom<E, D>::TI / 16][4],
-                                                const char* rows) {
-  using G = TileGeom<E, D>;
-  const int l = lane_id();
-  if constexpr (sizeof(E) == 2) {
+// Sixteen bytes of a row as floats.
+__device__ __forceinline__ void cvt16f(const u32x4 u, float (&v)[8]) {
 #pragma unroll
-    for (int ks = 0; ks < G::TI / 32; ++ks) {
-      uint32_t ph[4], pl[4];
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const float g0 = gv[2 * ks + (e >> 2)][e & 3], g1 = gv[2 * ks + (e >> 2)][(e & 3) + 1];
-        const uint32_t h0 = bf16_rne(g0), h1 = bf16_rne(g1);
-        const uint32_t l0 = bf16_rne(g0 - __uint_as_float(h0 << 16)), l1 = bf16_rne(g1 - __uint_as_float(h1 << 16));
-        ph[e / 2] = h0 | (h1 << 16);
-        pl[e / 2] = l0 | (l1 << 16);
-      }
-      const bf16x8 ahi = __builtin_bit_cast(bf16x8, u32x4{ph[0], ph[1], ph[2], ph[3]});
-      const bf16x8 alo = __builtin_bit_cast(bf16x8, u32x4{pl[0], pl[1], pl[2], pl[3]});
-#pragma unroll
-      for (int nb = 0; nb < D / 16; ++nb) {
-        short4v b0, b1;
-        lds_tr16_pair(tile_tr4_addr<D>(rows, 32 * ks, nb), tile_tr4_addr<D>(rows, 32 * ks + 16, nb), b0, b1);
-        const short4v b8[2] = {b0, b1};
-        const bf16x8 b = __builtin_bit_cast(bf16x8, b8);
-        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, b, acc[nb], 0, 0, 0);
-        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, b, acc[nb], 0, 0, 0);
-      }
-    }
-  } else {
-    const int g = l >> 4;
-#pragma unroll
-    for (int cb = 0; cb < G::TI / 16; ++cb)
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-#pragma unroll
-        for (int nb = 0; nb < D / 16; ++nb)
-          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-              gv[cb][v], tile_elem<float, D>(rows, 16 * cb + 4 * g + v, 16 * nb + (l & 15)), acc[nb], 0, 0, 0);
+  for (int t = 0; t < 4; ++t) {
+    v[2 * t] = __uint_as_float(u[t] << 16);
+    v[2 * t + 1] = __uint_as_float(u[t] & 0xFFFF0000u);
   }
 }
-
-// ------------------------------------------------------------------ dX
-__host__ __device__ constexpr size_t rows_slot_bytes(size_t row_bytes, int rounds) {
-  return row_bytes + 256 * (size_t)rounds;
+__device__ __forceinline__ void cvt16f(const u32x4 u, float (&v)[4]) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) v[t] = __uint_as_float(u[t]);
 }
-constexpr size_t ROWS_WAVE_LDS = 16 * MAX_ROUNDS * sizeof(PrevRow);
-
-// SCE = true: bucket variant (rows are (bucket, position) slots, window = the
-// bucket's items, output = one partial row per slot, no positive term).
-//
-// Layout: the logit block is computed transposed (items x positions), so lane l
-// holds position l % 16 for items 4*(l/16) + v of every 16-item block.  Those
-// are exactly the values the G . Y product needs as its A operand (k = items,
-// permuted identically on both sides), so G never goes through LDS; the B
-// operand (Y transposed) comes from the row tile with the LDS transpose read.
-template <class E, int D, int NW, bool SCE>
-__global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 512) ? 2 : 1) void k_bwd_rows(BwdArgs p) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  using G = TileGeom<E, D>;
-  constexpr int TI = G::TI;
-  constexpr int NCB = TI / 16;
-  constexpr int TR = 16 * NW;
-  const E* __restrict__ Y = reinterpret_cast<const E*>(p.Y);
-  const E* __restrict__ Xs = reinterpret_cast<const E*>(p.Xs);
-  const E* __restrict__ Ys = reinterpret_cast<const E*>(p.Ys);
-  const int n_c = p.n_c, rho = p.rho;
-  const int64_t s = p.s, C = p.C;
-  const size_t slot_bytes = rows_slot_bytes(G::ROW_BYTES, p.rounds);
-  char* ring = smem;
-  const int w = threadIdx.x >> 6, l = lane_id(), g = l >> 4;
-  PrevRow* prev = reinterpret_cast<PrevRow*>(smem + 3 * slot_bytes + (size_t)w * ROWS_WAVE_LDS);
-
-  const int lb = xcd_block(blockIdx.x, gridDim.x);
-  const int c = lb / p.tiles_per_chunk;
-  const int tile_i = lb % p.tiles_per_chunk;
-  const int64_t x0 = chunk_start(c, s, n_c), x1 = chunk_start(c + 1, s, n_c);
-  const int64_t tile0 = x0 + (int64_t)tile_i * TR;
-  if (tile0 >= x1) return;
-  uint32_t nexact = 0;   // float64 logits computed by this lane
-  const int64_t wrow0 = tile0 + 16 * w;
-  Ranges win;
-  win.init(c, n_c, C, TI, p.nwin);
-  const int ntiles = win.ntiles();
-
-  // this lane's position: row l % 16 of the wave
-  const int64_t pA = wrow0 + (l & 15);
-  const bool rvA = pA < x1;
-  Frag<E, D> afr;
-  afr.load_global(rvA ? Xs + pA * D : nullptr);
-  if (l < 16)
-    for (int r2 = 0; r2 < rho; ++r2) prev[l * MAX_ROUNDS + r2] = rvA ? p.prev[(int64_t)r2 * s + pA] : PrevRow{};
-  const PosRec rc = p.rec[rvA ? pA : x0];
-  const int posA = rvA ? rc.pos : -1;
-  const float lseA = rc.lse, gbA = rc.gb, loA = rc.lo, hiA = rc.hi;
-  const double teA = rc.te;
-  const int tidA = rc.tid, gstA = rc.pad0, gmA = rc.pad1;
-  const E* xrowA = Xs + (rvA ? pA : x0) * D;
-  const PrevRow p0 = rho > 0 ? p.prev[rvA ? pA : x0] : PrevRow{};   // round 0's set of this position
-
-  f32x4 dacc[D / 16];
-#pragma unroll
-  for (int nb = 0; nb < D / 16; ++nb) dacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int ncopies = G::ROW_DMA + 1 + rho;
-  int my_copies = 0;
-  for (int u = w; u < ncopies; u += NW) ++my_copies;
-  __syncthreads();
-  issue_window_tile<E, D, NW>(ring, slot_bytes, win, 0, Ys, p.perm_y, p.cyp, C, rho, w);
-  if (ntiles > 1) issue_window_tile<E, D, NW>(ring, slot_bytes, win, 1, Ys, p.perm_y, p.cyp, C, rho, w);
-  for (int t = 0; t < ntiles; ++t) {
-    wait_vmcnt(t + 1 < ntiles ? my_copies : 0);
-    raw_barrier();
-    if (t + 2 < ntiles) issue_window_tile<E, D, NW>(ring, slot_bytes, win, t + 2, Ys, p.perm_y, p.cyp, C, rho, w);
-    const int64_t q0 = range_tile_start(win, t, TI), q1 = range_tile_end(win, t);
-    const char* slot = ring + (size_t)(t % 3) * slot_bytes;
-    const int32_t* tid_ = reinterpret_cast<const int32_t*>(slot + G::ROW_BYTES);
-    const int32_t* tcy = tid_ + 64;
-    const int nlim = (int)(q1 - q0);   // valid rows of this tile
-    f32x4 acc[NCB];
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      Frag<E, D> bf;
-      TileFrag<E, D>::load(bf, slot, cb * 16 + (l & 15));
-      acc[cb] = mma_block(bf, afr, f32x4{0.f, 0.f, 0.f, 0.f});   // [item 4g+v][position l%16]
-    }
-    float gv[NCB][4];
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      const int n0 = cb * 16 + 4 * g;
-      const u32x4 jj = *reinterpret_cast<const u32x4*>(tid_ + n0);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int n = n0 + v;
-        const int j = (int)jj[v];
-        const float a = acc[cb][v];
-        const bool cand = rvA && n < nlim && j != posA;
-        bool mem = cand && a > hiA;
-        if (cand && !mem && a >= loA)   // inside the float32 bounds: float64 decides (rare)
-          mem = beats<E, D>(a, loA, hiA, teA, tidA, xrowA, Y, j, nexact);
-        if ((SCE || rho > 0) && mem) {
-          if (SCE && gmA > 0 && sce_seen_before(p, gstA, gmA, j)) mem = false;
-          if (rho > 0 && mem && in_window(p0.cx, tcy[n], n_c) &&
-              beats<E, D>(a, p0.lo, p0.hi, p0.te, p0.tid, xrowA, Y, j, nexact))
-            mem = false;   // kept in round 0 (registers); rounds 1 .. rho-1 below
-          for (int r2 = 1; r2 < rho && mem; ++r2) {
-            const PrevRow pr = prev[(l & 15) * MAX_ROUNDS + r2];
-            if (!in_window(pr.cx, tcy[64 * r2 + n], n_c)) continue;
-            if (beats<E, D>(a, pr.lo, pr.hi, pr.te, pr.tid, xrowA, Y, j, nexact)) mem = false;
-          }
-        }
-        gv[cb][v] = mem ? __expf(a - lseA) * gbA : 0.0f;
-      }
-    }
-    accumulate_rows<E, D>(dacc, gv, slot);
-  }
-
-  // write: rows 4g+v, coordinates 16nb + (l & 15); round 0 adds the positive term
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int64_t pr = wrow0 + 4 * g + v;
-    if (pr >= x1) continue;
-    if (SCE) {   // partial row of this slot
-      float* dst = p.dX + pr * D;
-#pragma unroll
-      for (int nb = 0; nb < D / 16; ++nb) dst[16 * nb + (l & 15)] = dacc[nb][v];
-      continue;
-    }
-    const PosRec rv = p.rec[pr];
-    float* dst = p.dX + (int64_t)rv.i * D;
-    float gpos = 0.0f;
-    const int pclamp = rv.pos < 0 ? 0 : (rv.pos >= p.C ? (int)(p.C - 1) : rv.pos);
-    const E* ypos = Y + (int64_t)pclamp * D;
-    if (rho == 0) gpos = (expf(rv.lpos - rv.lse) - 1.0f) * rv.gb;
-#pragma unroll
-    for (int nb = 0; nb < D / 16; ++nb) {
-      const int t = 16 * nb + (l & 15);
-      float val = dacc[nb][v];
-      if (rho == 0)
-        val += gpos * to_f32(ypos[t]);
-      else
-        val += dst[t];
-      dst[t] = val;
-    }
-  }
-  flush_count(p.counters + CNT_LOGIT_EXACT, nexact);
-}
-
-// ------------------------------------------------------------------ dY (negatives)
-template <class E, int D>
-struct ItemsLayout {
-  using G = TileGeom<E, D>;
-  using RC = RecCopy<sizeof(PosRec), G::TI>;
-  using PC = RecCopy<sizeof(PrevRow), G::TI>;
-  static __host__ __device__ constexpr size_t slot_bytes(int rounds) {
-    return (size_t)G::ROW_BYTES + RC::LDS_BYTES + (size_t)(rounds > 1 ? rounds - 1 : 0) * PC::LDS_BYTES;
-  }
-};
-constexpr size_t ITEMS_WAVE_LDS = 16 * MAX_ROUNDS * 4;
-
-// Copies of position tile t: rows of the sorted positions, their records, and their
-// records of each earlier round, into ring slot t % 3.
-template <class E, int D, int NW>
-__device__ __forceinline__ void issue_items_tile(char* ring, size_t slot_bytes, Ranges r, int t, const E* xs,
-                                                 const PosRec* rec, const PrevRow* prev, int64_t s, int rho,
-                                                 int wave) {
-  using G = TileGeom<E, D>;
-  using LY = ItemsLayout<E, D>;
-  const int64_t q0 = range_tile_start(r, t, G::TI), q1 = range_tile_end(r, t);
-  char* slot = ring + (size_t)(t % 3) * slot_bytes;
-  dma_rows<E, D, NW>(slot, xs, q0, q1, wave);
-  char* rb = slot + G::ROW_BYTES;
-  LY::RC::template issue<NW>(rb, rec, q0, q1, G::ROW_DMA, wave);
-  for (int r2 = 0; r2 < rho; ++r2)
-    LY::PC::template issue<NW>(rb + LY::RC::LDS_BYTES + (size_t)r2 * LY::PC::LDS_BYTES, prev + (int64_t)r2 * s, q0,
-                               q1, G::ROW_DMA + LY::RC::COPIES + r2 * LY::PC::COPIES, wave);
-}
-
-// Transposed logit block as in k_bwd_rows: lane l holds item l % 16 of the wave
-// and positions 4*(l/16) + v of every 16-position block of the tile, the A
-// operand of dY = G^T . X; X transposed comes from the tile by transpose reads.
-template <class E, int D, int NW, bool SCE>
-__global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 512) ? 2 : 1) void k_bwd_items(BwdArgs p, int itiles) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  using G = TileGeom<E, D>;
-  using LY = ItemsLayout<E, D>;
-  constexpr int TI = G::TI;
-  constexpr int NCB = TI / 16;
-  constexpr int TR = 16 * NW;
-  const E* __restrict__ Y = reinterpret_cast<const E*>(p.Y);
-  const E* __restrict__ Xs = reinterpret_cast<const E*>(p.Xs);
-  const E* __restrict__ Ys = reinterpret_cast<const E*>(p.Ys);
-  const int n_c = p.n_c, rho = p.rho;
-  const int64_t s = p.s, C = p.C;
-  const size_t slot_bytes = LY::slot_bytes(p.rounds);
-  char* ring = smem;
-  const int w = threadIdx.x >> 6, l = lane_id(), g = l >> 4;
-  int32_t* cy2w = reinterpret_cast<int32_t*>(smem + 3 * slot_bytes + (size_t)w * ITEMS_WAVE_LDS);   // [16][MAX_ROUNDS]
-
-  const int lb = xcd_block(blockIdx.x, gridDim.x);
-  const int c = lb / itiles;
-  const int it = lb % itiles;
-  const int64_t y0 = chunk_start(c, C, n_c), y1 = chunk_start(c + 1, C, n_c);
-  const int64_t tile0 = y0 + (int64_t)it * TR;
-  if (tile0 >= y1) return;
-  uint32_t nexact = 0;   // float64 logits computed by this lane
-  const int64_t wq0 = tile0 + 16 * w;
-  Ranges xr;
-  xr.init(c, n_c, s, TI, p.nwin);   // X-chunks whose window holds item chunk c (the relation is symmetric)
-  const int ntiles = xr.ntiles();
-
-  // this lane's item: row l % 16 of the wave
-  const int64_t qA = wq0 + (l & 15);
-  const bool rvA = qA < y1;
-  const int jA = rvA ? p.perm_y[qA] : -1;
-  const int cy0 = (rho > 0 && rvA) ? p.cyp[qA] : 0;   // this item's chunk in round 0
-  Frag<E, D> afr;
-  afr.load_global(rvA ? Ys + qA * D : nullptr);
-  if (l < 16)
-    for (int r2 = 0; r2 < rho; ++r2) cy2w[l * MAX_ROUNDS + r2] = rvA ? p.cyp[(int64_t)r2 * C + qA] : 0;
-  f32x4 dacc[D / 16];
-#pragma unroll
-  for (int nb = 0; nb < D / 16; ++nb) dacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int ncopies = G::ROW_DMA + LY::RC::COPIES + rho * LY::PC::COPIES;
-  int my_copies = 0;
-  for (int u = w; u < ncopies; u += NW) ++my_copies;
-
-  __syncthreads();
-  issue_items_tile<E, D, NW>(ring, slot_bytes, xr, 0, Xs, p.rec, p.prev, s, rho, w);
-  if (ntiles > 1) issue_items_tile<E, D, NW>(ring, slot_bytes, xr, 1, Xs, p.rec, p.prev, s, rho, w);
-  for (int t = 0; t < ntiles; ++t) {
-    wait_vmcnt(t + 1 < ntiles ? my_copies : 0);
-    raw_barrier();
-    if (t + 2 < ntiles) issue_items_tile<E, D, NW>(ring, slot_bytes, xr, t + 2, Xs, p.rec, p.prev, s, rho, w);
-    const int64_t q0 = range_tile_start(xr, t, TI), q1 = range_tile_end(xr, t);
-    const char* slot = ring + (size_t)(t % 3) * slot_bytes;
-    const PosRec* recs = reinterpret_cast<const PosRec*>(slot + G::ROW_BYTES);
-    const PrevRow* prevs = reinterpret_cast<const PrevRow*>(slot + G::ROW_BYTES + LY::RC::LDS_BYTES);
-    const int nlim = (int)(q1 - q0);   // valid rows of this tile
-    f32x4 acc[NCB];
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      Frag<E, D> bf;
-      TileFrag<E, D>::load(bf, slot, cb * 16 + (l & 15));
-      acc[cb] = mma_block(bf, afr, f32x4{0.f, 0.f, 0.f, 0.f});   // [position 4g+v][item l%16]
-    }
-    float gv[NCB][4];
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int n = cb * 16 + 4 * g + v;
-        const f32x4 hot = *reinterpret_cast<const f32x4*>(&recs[n].lse);   // lse, gb, lo, hi
-        const int pos_n = recs[n].pos;
-        const float a = acc[cb][v];
-        const bool cand = rvA && n < nlim && jA != pos_n;
-        bool mem = cand && a > hot[3];
-        if (cand && !mem && a >= hot[2])   // inside the float32 bounds: float64 decides (rare)
-          mem = beats<E, D>(a, hot[2], hot[3], recs[n].te, recs[n].tid, Xs + (q0 + n) * D, Y, jA, nexact);
-        if ((SCE || rho > 0) && mem) {
-          if (SCE && recs[n].pad1 > 0 && sce_seen_before(p, recs[n].pad0, recs[n].pad1, jA)) mem = false;
-          for (int r2 = 0; r2 < rho && mem; ++r2) {
-            const int cyr = r2 == 0 ? cy0 : cy2w[(l & 15) * MAX_ROUNDS + r2];
-            if (!in_window(prevs[(size_t)r2 * (LY::PC::LDS_BYTES / sizeof(PrevRow)) + n].cx, cyr, n_c)) continue;
-            const PrevRow pr = prevs[(size_t)r2 * (LY::PC::LDS_BYTES / sizeof(PrevRow)) + n];
-            if (beats<E, D>(a, pr.lo, pr.hi, pr.te, pr.tid, Xs + (q0 + n) * D, Y, jA, nexact)) mem = false;
-          }
-        }
-        gv[cb][v] = mem ? __expf(a - hot[0]) * hot[1] : 0.0f;
-      }
-    }
-    accumulate_rows<E, D>(dacc, gv, slot);
-  }
-
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int64_t qr = wq0 + 4 * g + v;
-    if (qr >= y1) continue;
-    float* dst = p.dY + (SCE ? qr : (int64_t)p.perm_y[qr]) * D;
-#pragma unroll
-    for (int nb = 0; nb < D / 16; ++nb) {
-      const int t = 16 * nb + (l & 15);
-      float val = dacc[nb][v];
-      if (rho > 0) val += dst[t];
-      dst[t] = val;
-    }
-  }
-  flush_count(p.counters + CNT_LOGIT_EXACT, nexact);
+template <class E, int N>
+__device__ __forceinline__ void load16f(const E* ptr, float (&v)[N]) {
+  cvt16f(*reinterpret_cast<const u32x4*>(ptr), v);
 }
 
 // ------------------------------------------------------------------ dX from the kept lists
-// Sixteen bytes of a row as floats.
-__device__ __forceinline__ void load16f(const bf16* ptr, float (&v)[8]) {
-  const uint4 u = *reinterpret_cast<const uint4*>(ptr);
-  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    v[2 * t] = __uint_as_float(w[t] << 16);
-    v[2 * t + 1] = __uint_as_float(w[t] & 0xFFFF0000u);
-  }
-}
-__device__ __forceinline__ void load16f(const float* ptr, float (&v)[4]) {
-  const float4 u = *reinterpret_cast<const float4*>(ptr);
-  v[0] = u.x;
-  v[1] = u.y;
-  v[2] = u.z;
-  v[3] = u.w;
-}
-
 // One wave per position i (RECE page, Eq. 4, the position side):
 //   dX_i = sum over the kept pairs (i, j) of every round that no earlier round
 //          kept (list ids >= 0) of gbar_i exp(x_i . y_j - lse_i) y_j
@@ -505,6 +130,7 @@ __global__ __launch_bounds__(256) void k_dx_lists(BwdArgs p) {
   }
 }
 
+// ------------------------------------------------------------------ exports
 __global__ void k_strip_mark(const int32_t* __restrict__ src, int64_t n, int32_t* __restrict__ dst) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t < n) {
@@ -513,320 +139,429 @@ __global__ void k_strip_mark(const int32_t* __restrict__ src, int64_t n, int32_t
   }
 }
 
-// ------------------------------------------------------------------ dY (positives)
-constexpr int PIECE = 64;   // sorted positions per piece (one wave)
+// One wave per position: the ids of its lists of all rounds that no earlier
+// round kept, in (round, list) order, then -1 up to rounds * k entries.
+__global__ __launch_bounds__(256) void k_union_ids(const int32_t* __restrict__ negs, int64_t s, int k, int rounds,
+                                                   int32_t* __restrict__ dst) {
+  const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (i >= s) return;
+  const int l = lane_id();
+  const int64_t width = (int64_t)rounds * k;
+  int32_t* out = dst + i * width;
+  int64_t n = 0;
+  for (int rho = 0; rho < rounds; ++rho) {
+    const int32_t* list = negs + ((int64_t)rho * s + i) * k;
+    for (int e0 = 0; e0 < k; e0 += WAVE) {
+      const int v = e0 + l < k ? list[e0 + l] : -1;
+      const uint64_t m = ballot(v >= 0);
+      if (v >= 0) out[n + popc(m & lanemask_lt())] = v;
+      n += popc(m);
+    }
+  }
+  for (int64_t t = n + l; t < width; t += WAVE) out[t] = -1;
+}
 
-// pflag bits per piece: 1 = head run continues from the previous piece,
-// 2 = head run continues into the next piece, 4 = a tail run starts here and continues.
-// Runs that neither come from the previous piece nor continue into the next are
-// staged (item and row) and added to dY by k_pos_combine: the pieces kernel reads
-// and writes nothing of dY, so it can run while dY is still being written.
-struct PosStage {
-  int32_t* n;       // [npieces] staged runs of each piece
-  int32_t* items;   // [npieces * PIECE]
-  float* rows;      // [npieces * PIECE][D]
+// ------------------------------------------------------------------ pair sort by item
+// Records (key, value): key = item id, value = position id, bit 31 set on the
+// record of a position's positive.  The first pass reads them from the kept
+// lists and the positives (entry t < nl: list entry t, value (t / k) mod s;
+// entry nl + i: the positive of position i) and drops list entries < 0 and
+// ids outside [0, C); later passes read the previous pass's output, whose
+// length the previous scatter stored in ntot.
+struct PairSrc {
+  const int32_t* negs;   // [nl] first pass
+  const int32_t* pos;    // [s]  first pass
+  const int32_t* kin;    // later passes
+  const int32_t* vin;
+  const uint32_t* nin;   // later passes: number of records in kin / vin
+  int64_t nl, s, C;
+  int k;
 };
 
-template <class E, int D>
-__global__ __launch_bounds__(256) void k_pos_pieces(BwdArgs p, const int32_t* __restrict__ sorted,
-                                                    float* __restrict__ partial, int32_t* __restrict__ pitem,
-                                                    int32_t* __restrict__ pflag, PosStage stage, int64_t npieces) {
-  constexpr int PER = (D + 63) / 64;   // coordinates per lane
-  const E* __restrict__ X = reinterpret_cast<const E*>(p.X);
-  const int w = threadIdx.x >> 6, l = lane_id();
-  const int64_t piece = (int64_t)blockIdx.x * 4 + w;
-  if (piece >= npieces) return;
-  const int64_t s = p.s;
-  const int64_t t0 = piece * PIECE, t1 = min(s, t0 + PIECE);
-  float acc[PER];
-#pragma unroll
-  for (int u = 0; u < PER; ++u) acc[u] = 0.0f;
-  int flags = 0;
-  int head_item = -1, tail_item = -1;
-  int nstage = 0;
-  const int prev_item = t0 > 0 ? p.pos[sorted[t0 - 1]] : -1;
-  const int next_item = t1 < s ? p.pos[sorted[t1]] : -1;
-  // lane e holds sorted position t0 + e: its id, positive item and coefficient (all
-  // loads in parallel); the walk below takes them with uniform lane reads
-  const int nt = (int)(t1 - t0);
-  const int i_l = l < nt ? sorted[t0 + l] : 0;
-  const int item_l = l < nt ? p.pos[i_l] : -1;
-  const float gp_l = l < nt ? (expf(p.lpos[i_l] - p.lse[i_l]) - 1.0f) * gbar_of(p, i_l) : 0.0f;
-  int cur = __builtin_amdgcn_readfirstlane(item_l);
-  int64_t run_start = t0;
-  constexpr int BATCH = 8;   // rows of X in flight
-  for (int tb = 0; tb < nt; tb += BATCH) {
-    float xv[BATCH][PER];
-#pragma unroll
-    for (int q = 0; q < BATCH; ++q) {
-      const int i = __builtin_amdgcn_readlane(i_l, tb + q < nt ? tb + q : 0);
-      const E* xr = X + (int64_t)i * D;
-#pragma unroll
-      for (int u = 0; u < PER; ++u) xv[q][u] = (tb + q < nt && l + 64 * u < D) ? to_f32(xr[l + 64 * u]) : 0.0f;
+template <bool FIRST>
+__device__ __forceinline__ bool pair_at(const PairSrc& a, int64_t t, int& key, int& val) {
+  if constexpr (FIRST) {
+    if (t < a.nl) {
+      key = a.negs[t];
+      val = (int)(((uint32_t)t / (uint32_t)a.k) % (uint32_t)a.s);
+    } else {
+      const int64_t i = t - a.nl;
+      key = a.pos[i];
+      val = (int)i | (int)0x80000000u;
     }
-#pragma unroll
-    for (int q = 0; q < BATCH; ++q) {
-      if (tb + q >= nt) break;
-      const int64_t t = t0 + tb + q;
-      const int item = __builtin_amdgcn_readlane(item_l, tb + q);
-      if (item != cur) {
-        // flush the run [run_start, t) of item cur
-        if (run_start == t0 && prev_item == cur) {
-          head_item = cur;
-          flags |= 1;
-#pragma unroll
-          for (int u = 0; u < PER; ++u)
-            if (l + 64 * u < D) partial[(piece * 2 + 0) * D + l + 64 * u] = acc[u];
-        } else if (cur >= 0 && cur < p.C) {
-          const int64_t slot = piece * PIECE + nstage++;
-          if (l == 0) stage.items[slot] = cur;
-#pragma unroll
-          for (int u = 0; u < PER; ++u)
-            if (l + 64 * u < D) stage.rows[slot * D + l + 64 * u] = acc[u];
-        }
-#pragma unroll
-        for (int u = 0; u < PER; ++u) acc[u] = 0.0f;
-        cur = item;
-        run_start = t;
-      }
-      const float gp = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gp_l), tb + q));
-#pragma unroll
-      for (int u = 0; u < PER; ++u) acc[u] = fmaf(gp, xv[q][u], acc[u]);
-    }
-  }
-  // last run [run_start, t1)
-  const bool from_prev = run_start == t0 && prev_item == cur;
-  const bool to_next = next_item == cur;
-  if (from_prev) {
-    head_item = cur;
-    flags |= 1;
-    if (to_next) flags |= 2;
-#pragma unroll
-    for (int u = 0; u < PER; ++u)
-      if (l + 64 * u < D) partial[(piece * 2 + 0) * D + l + 64 * u] = acc[u];
-  } else if (to_next) {
-    tail_item = (cur >= 0 && cur < p.C) ? cur : -1;
-    flags |= 4;
-#pragma unroll
-    for (int u = 0; u < PER; ++u)
-      if (l + 64 * u < D) partial[(piece * 2 + 1) * D + l + 64 * u] = acc[u];
-  } else if (cur >= 0 && cur < p.C) {
-    const int64_t slot = piece * PIECE + nstage++;
-    if (l == 0) stage.items[slot] = cur;
-#pragma unroll
-    for (int u = 0; u < PER; ++u)
-      if (l + 64 * u < D) stage.rows[slot * D + l + 64 * u] = acc[u];
-  }
-  if (l == 0) {
-    pitem[piece * 2 + 0] = head_item;
-    pitem[piece * 2 + 1] = tail_item;
-    pflag[piece] = flags;
-    stage.n[piece] = nstage;
+    return key >= 0 && key < a.C;
+  } else {
+    key = a.kin[t];
+    val = a.vin[t];
+    return true;
   }
 }
 
-// Per piece: add its staged runs to dY (each item's positions form one run, so
-// no other wave writes those rows); then, for a run that starts in this piece and
-// continues, add the head partials of the following pieces, in order, until the
-// run ends.
-template <int D>
-__global__ __launch_bounds__(256) void k_pos_combine(float* __restrict__ dY, const float* __restrict__ partial,
-                                                     const int32_t* __restrict__ pitem,
-                                                     const int32_t* __restrict__ pflag, PosStage stage,
-                                                     int64_t npieces) {
-  constexpr int PER = (D + 63) / 64;
+// Per segment of seg_len records: a histogram of the digit (key >> shift) & mask.
+template <bool FIRST>
+__global__ __launch_bounds__(256) void k_pair_hist(PairSrc a, int64_t n_max, int shift, int nbits, int seg_len,
+                                                   int nseg, uint32_t* __restrict__ counts) {
+  extern __shared__ uint32_t hist[];
+  const int nbins = 1 << nbits;
+  const uint32_t mask = (uint32_t)nbins - 1u;
+  for (int b = threadIdx.x; b < nbins; b += 256) hist[b] = 0u;
+  __syncthreads();
+  const int64_t n = FIRST ? n_max : (int64_t)*a.nin;
+  const int64_t t0 = (int64_t)blockIdx.x * seg_len;
+  const int64_t t1 = min(n, t0 + seg_len);
+  for (int64_t t = t0 + threadIdx.x; t < t1; t += 256) {
+    int key, val;
+    if (pair_at<FIRST>(a, t, key, val)) atomicAdd(&hist[((uint32_t)key >> shift) & mask], 1u);
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b < nbins; b += 256) counts[(int64_t)b * nseg + blockIdx.x] = hist[b];
+  if (blockIdx.x == 0 && threadIdx.x == 0) counts[(int64_t)nbins * nseg] = 0u;   // becomes the total
+}
+
+// One wave per segment walks its records in order, 64 at a time; lanes with
+// equal digits find each other with one ballot per digit bit and take ranks in
+// lane order, so equal digits keep their input order (stable).
+template <bool FIRST>
+__global__ __launch_bounds__(256) void k_pair_scatter(PairSrc a, int64_t n_max, int shift, int nbits, int seg_len,
+                                                      int nseg, const uint32_t* __restrict__ offs,
+                                                      int32_t* __restrict__ kout, int32_t* __restrict__ vout,
+                                                      uint32_t* __restrict__ ntot) {
+  extern __shared__ uint32_t ctr_all[];
+  const int nbins = 1 << nbits;
+  const uint32_t mask = (uint32_t)nbins - 1u;
   const int w = threadIdx.x >> 6, l = lane_id();
-  const int64_t piece = (int64_t)blockIdx.x * 4 + w;
-  if (piece >= npieces) return;
-  {
-    // the piece's staged runs, each added once to its item's row: 16 bytes per lane,
-    // RPI rows per instruction, BATCH instructions in flight
-    static_assert(D % 4 == 0 && D <= 256, "rows of whole 16-byte chunks, at most 64 per row");
-    constexpr int LPR = D / 4, RPI = 64 / LPR, BATCH = 8;
-    const int q = l / LPR, sub = l % LPR;
-    const int ns = stage.n[piece];
-    for (int e0 = 0; e0 < ns; e0 += RPI * BATCH) {
-      float4 rv[BATCH], yv[BATCH];
-      int64_t base[BATCH];
+  if (blockIdx.x == 0 && threadIdx.x == 0) *ntot = offs[(int64_t)nbins * nseg];
+  const int64_t seg = (int64_t)blockIdx.x * 4 + w;
+  if (seg >= nseg) return;   // whole wave leaves; no block barrier below
+  uint32_t* ctr = ctr_all + (int64_t)w * nbins;
+  for (int b = l; b < nbins; b += WAVE) ctr[b] = offs[(int64_t)b * nseg + seg];
+  wave_sync();
+  const int64_t n = FIRST ? n_max : (int64_t)*a.nin;
+  const int64_t t0 = seg * seg_len;
+  const int64_t t1 = min(n, t0 + seg_len);
+  for (int64_t tb = t0; tb < t1; tb += WAVE) {
+    const int64_t t = tb + l;
+    int key = 0, val = 0;
+    const bool valid = t < t1 && pair_at<FIRST>(a, t, key, val);
+    const int dig = valid ? (int)(((uint32_t)key >> shift) & mask) : 0;
+    uint64_t same = ballot(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool on = (dig >> bit) & 1;
+      const uint64_t bm = ballot(on);
+      same &= on ? bm : ~bm;
+    }
+    const int rank = popc(same & lanemask_lt());
+    const int cnt = popc(same);
+    uint32_t base = 0;
+    if (valid) base = ctr[dig];
+    wave_sync();
+    if (valid && rank == 0) ctr[dig] = base + (uint32_t)cnt;
+    wave_sync();
+    if (valid) {
+      const uint32_t slot = base + (uint32_t)rank;
+      kout[slot] = key;
+      vout[slot] = val;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ dY from the sorted pairs
+constexpr int DY_SUB = 256;   // sorted pairs per lane group
+
+// Per sub-piece: flags (1 = its first item started in an earlier sub-piece, 2 = that
+// item also continues into the next one, 4 = its last item starts here and
+// continues), the items of the head and tail partial rows, and the rows.
+struct DyArea {
+  float* partial;    // [nsub][2][D]
+  int32_t* flags;    // [nsub]
+  int32_t* items;    // [nsub][2]
+  int64_t nsub;
+};
+
+// Write (or clear) row j of dY: EPL floats of lane `sub`.
+template <int EPL>
+__device__ __forceinline__ void store_row(float* dst, const float (&v)[EPL]) {
 #pragma unroll
-      for (int e = 0; e < BATCH; ++e) {
-        const int idx = e0 + e * RPI + q;
-        const bool in = q < RPI && idx < ns;
-        const int64_t slot = piece * PIECE + (in ? idx : 0);
-        base[e] = (int64_t)stage.items[slot] * D + 4 * sub;
-        rv[e] = in ? *reinterpret_cast<const float4*>(stage.rows + slot * D + 4 * sub) : float4{0.f, 0.f, 0.f, 0.f};
-        yv[e] = in ? *reinterpret_cast<const float4*>(dY + base[e]) : float4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < EPL / 4; ++t)
+    reinterpret_cast<float4*>(dst)[t] = float4{v[4 * t], v[4 * t + 1], v[4 * t + 2], v[4 * t + 3]};
+}
+
+// One lane group (LPR lanes, 16 bytes of a row each) per sub-piece of DY_SUB sorted
+// pairs.  For each pair (j, i): l = x_i . y_j (float32, the same lane split and
+// order as k_dx_lists), g = gbar_i exp(l - lse_i), or (exp(lpos_i - lse_i) - 1)
+// gbar_i for a positive record, summed as g x_i per item in pair order.  An item
+// wholly inside the sub-piece is written to dY here; an item continuing from the
+// previous or into the next sub-piece leaves a partial row for k_dy_combine.  The
+// items with no pair between two consecutive keys get zero rows from the sub-piece
+// holding the earlier key (sub-piece 0 also clears the items before the first key).
+template <class E, int D>
+__global__ __launch_bounds__(256) void k_dy_pieces(BwdArgs p, const int32_t* __restrict__ K,
+                                                   const int32_t* __restrict__ V, const uint32_t* __restrict__ ntot,
+                                                   DyArea area) {
+  constexpr int EPL = 16 / (int)sizeof(E);
+  constexpr int LPR = D / EPL;
+  constexpr int RPI = WAVE / LPR;
+  constexpr int UNR = 4;
+  const E* __restrict__ X = reinterpret_cast<const E*>(p.X);
+  const E* __restrict__ Y = reinterpret_cast<const E*>(p.Y);
+  const int l = lane_id();
+  const int q = l / LPR, sub = l % LPR;
+  const int64_t piece = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPI + q;
+  const int64_t n = (int64_t)*ntot;
+  const int64_t C = p.C;
+  const int64_t t0 = piece * DY_SUB;
+  if (piece >= area.nsub || (t0 >= n && piece != 0)) return;   // whole groups leave together
+  const int64_t t1 = min(n, t0 + DY_SUB);
+  float zero[EPL];
+#pragma unroll
+  for (int t = 0; t < EPL; ++t) zero[t] = 0.0f;
+  float* dY = p.dY;
+  if (n == 0) {   // no pair at all: piece 0 clears every row
+    for (int64_t j = 0; j < C; ++j) store_row<EPL>(dY + j * D + sub * EPL, zero);
+    if (sub == 0) area.flags[0] = 0;
+    return;
+  }
+  const int prev_key = t0 > 0 ? K[t0 - 1] : -1;
+  const int next_key = t1 < n ? K[t1] : (int)C;   // C: no later key
+  const float gscale = p.dloss_pp ? 0.0f : p.dloss[0] / (float)p.s;
+  int cur = -1;
+  int64_t run_start = t0;
+  int flags = 0, head_item = -1, tail_item = -1;
+  float acc[EPL];
+#pragma unroll
+  for (int t = 0; t < EPL; ++t) acc[t] = 0.0f;
+
+  // rows of items [a, b) cleared
+  auto clear_rows = [&](int64_t a, int64_t b) {
+    for (int64_t j = a; j < b; ++j) store_row<EPL>(dY + j * D + sub * EPL, zero);
+  };
+  // the run of item cur over [run_start, t_end) is complete
+  auto flush = [&](int64_t t_end) {
+    const bool head = run_start == t0 && cur == prev_key;
+    const bool tail = t_end == t1 && t1 < n && cur == next_key;
+    if (!head && !tail) {
+      store_row<EPL>(dY + (int64_t)cur * D + sub * EPL, acc);
+    } else if (head) {
+      store_row<EPL>(area.partial + (piece * 2 + 0) * D + sub * EPL, acc);
+      head_item = cur;
+      flags |= tail ? 3 : 1;
+    } else {
+      store_row<EPL>(area.partial + (piece * 2 + 1) * D + sub * EPL, acc);
+      tail_item = cur;
+      flags |= 4;
+    }
+  };
+
+  for (int64_t tb = t0; tb < t1; tb += UNR) {
+    int key[UNR], val[UNR];
+    u32x4 xr[UNR], yr[UNR];
+    float lse[UNR], gb[UNR], lp[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int64_t t = tb + u;
+      if (t < t1) {
+        key[u] = K[t];
+        val[u] = V[t];
+        const int64_t i = val[u] & 0x7FFFFFFF;
+        xr[u] = *reinterpret_cast<const u32x4*>(X + i * D + sub * EPL);
+        yr[u] = *reinterpret_cast<const u32x4*>(Y + (int64_t)key[u] * D + sub * EPL);
+        lse[u] = p.lse[i];
+        gb[u] = p.dloss_pp ? p.dloss_pp[i] : gscale;
+        lp[u] = p.lpos[i];
+      } else {
+        key[u] = -1;
       }
+    }
 #pragma unroll
-      for (int e = 0; e < BATCH; ++e)
-        if (q < RPI && e0 + e * RPI + q < ns)
-          *reinterpret_cast<float4*>(dY + base[e]) =
-              float4{yv[e].x + rv[e].x, yv[e].y + rv[e].y, yv[e].z + rv[e].z, yv[e].w + rv[e].w};
+    for (int u = 0; u < UNR; ++u) {
+      if (key[u] < 0) break;
+      if (key[u] != cur) {
+        if (cur >= 0) {
+          flush(tb + u);
+          clear_rows(cur + 1, key[u]);
+        } else if (piece == 0) {
+          clear_rows(0, key[u]);
+        }
+        cur = key[u];
+        run_start = tb + u;
+#pragma unroll
+        for (int t = 0; t < EPL; ++t) acc[t] = 0.0f;
+      }
+      float x[EPL], y[EPL];
+      cvt16f(xr[u], x);
+      cvt16f(yr[u], y);
+      float dot = 0.0f;
+#pragma unroll
+      for (int t = 0; t < EPL; ++t) dot = fmaf(x[t], y[t], dot);
+#pragma unroll
+      for (int o = 1; o < LPR; o <<= 1) dot += __shfl_xor(dot, o);
+      const float g = val[u] < 0 ? (expf(lp[u] - lse[u]) - 1.0f) * gb[u] : __expf(dot - lse[u]) * gb[u];
+#pragma unroll
+      for (int t = 0; t < EPL; ++t) acc[t] = fmaf(g, x[t], acc[t]);
     }
   }
-  if (!(pflag[piece] & 4)) return;
-  const int item = pitem[piece * 2 + 1];
-  if (item < 0) return;
-  float acc[PER];
-#pragma unroll
-  for (int u = 0; u < PER; ++u) acc[u] = l + 64 * u < D ? partial[(piece * 2 + 1) * D + l + 64 * u] : 0.0f;
-  // the run covers pieces piece+1 .. the first one whose head run does not continue
-  // (flag 2 clear) or the last piece; 64 flags are read at once, then the partial
-  // rows in order, several loads in flight
-  for (int64_t q0 = piece + 1; q0 < npieces; q0 += WAVE) {
-    const int64_t qq = q0 + l;
-    const int f = qq < npieces ? pflag[qq] : 0;
-    const uint64_t stop = ballot(qq >= npieces || !(f & 2));
-    const int nin = stop ? (int)min((int64_t)__builtin_ctzll(stop) + 1, npieces - q0) : WAVE;
-    constexpr int BATCH = 8;
-    for (int e0 = 0; e0 < nin; e0 += BATCH) {
-      float pv[BATCH][PER];
-#pragma unroll
-      for (int e = 0; e < BATCH; ++e)
-#pragma unroll
-        for (int u = 0; u < PER; ++u)
-          pv[e][u] = (e0 + e < nin && l + 64 * u < D) ? partial[((q0 + e0 + e) * 2 + 0) * D + l + 64 * u] : 0.0f;
-#pragma unroll
-      for (int e = 0; e < BATCH; ++e)
-#pragma unroll
-        for (int u = 0; u < PER; ++u) acc[u] += pv[e][u];
-    }
-    if (stop) break;
+  flush(t1);
+  if (cur != next_key) clear_rows(cur + 1, next_key);
+  if (sub == 0) {
+    area.flags[piece] = flags;
+    area.items[piece * 2 + 0] = head_item;
+    area.items[piece * 2 + 1] = tail_item;
   }
-  float* dst = dY + (int64_t)item * D;
+}
+
+// Items spanning sub-pieces: the sub-piece where such an item starts adds the head
+// rows of the following sub-pieces, in order, to its tail row and writes dY.
+template <int D>
+__global__ __launch_bounds__(256) void k_dy_combine(float* __restrict__ dY, const uint32_t* __restrict__ ntot,
+                                                    DyArea area) {
+  constexpr int EPL = 4;
+  constexpr int LPR = D / EPL;
+  constexpr int RPI = WAVE / LPR > 0 ? WAVE / LPR : 1;
+  const int l = lane_id();
+  const int q = l / LPR, sub = l % LPR;
+  if (q >= RPI) return;
+  const int64_t piece = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPI + q;
+  const int64_t n = (int64_t)*ntot;
+  const int64_t nact = (n + DY_SUB - 1) / DY_SUB;
+  if (piece >= nact || !(area.flags[piece] & 4)) return;
+  float acc[EPL];
+  load16f(area.partial + (piece * 2 + 1) * D + sub * EPL, acc);
+  for (int64_t qq = piece + 1; qq < nact; ++qq) {
+    float h[EPL];
+    load16f(area.partial + (qq * 2 + 0) * D + sub * EPL, h);
 #pragma unroll
-  for (int u = 0; u < PER; ++u)
-    if (l + 64 * u < D) dst[l + 64 * u] += acc[u];
+    for (int t = 0; t < EPL; ++t) acc[t] += h[t];
+    if (!(area.flags[qq] & 2)) break;
+  }
+  store_row<EPL>(dY + (int64_t)area.items[piece * 2 + 1] * D + sub * EPL, acc);
 }
 
 // ------------------------------------------------------------------ launchers
-template <class E, int D>
-static size_t rows_lds(int NW, int rounds) {
-  return 3 * rows_slot_bytes(TileGeom<E, D>::ROW_BYTES, rounds) + (size_t)NW * ROWS_WAVE_LDS;
-}
-template <class E, int D>
-static size_t items_lds(int NW, int rounds) {
-  return 3 * ItemsLayout<E, D>::slot_bytes(rounds) + (size_t)NW * ITEMS_WAVE_LDS;
+static int64_t pair_seg_len(int64_t n) {
+  int64_t L = ((n / 256) + 63) / 64 * 64;
+  return L < 256 ? 256 : (L > 4096 ? 4096 : L);
 }
 
-template <class E, int D, int NW, bool SCE>
-static hipError_t launch_rows_t(const BwdArgs& a, hipStream_t st) {
-  const size_t lds = rows_lds<E, D>(NW, a.rounds);
-  auto kern = k_bwd_rows<E, D, NW, SCE>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+PairSortGeom pair_sort_geom(int64_t E, int64_t C) {
+  PairSortGeom g{};
+  g.E = E;
+  int kb = 1;
+  while (((int64_t)1 << kb) < C) ++kb;
+  g.npass = (kb + 11) / 12;
+  int shift = 0;
+  for (int pss = 0; pss < g.npass; ++pss) {
+    const int left = g.npass - pss;
+    const int b = (kb - shift + left - 1) / left;
+    g.shift[pss] = shift;
+    g.bits[pss] = b;
+    shift += b;
+  }
+  g.seg_len = pair_seg_len(E);
+  g.nseg = (E + g.seg_len - 1) / g.seg_len;
+  int maxbits = 0;
+  for (int pss = 0; pss < g.npass; ++pss) maxbits = g.bits[pss] > maxbits ? g.bits[pss] : maxbits;
+  g.count_words = ((int64_t)1 << maxbits) * g.nseg + 1;
+  const int64_t nb = (g.count_words + 4095) / 4096;
+  g.scratch_bytes = (size_t)(g.count_words + nb + 64 + 8) * 4;
+  return g;
+}
+
+template <bool FIRST>
+static hipError_t pair_pass(const PairSrc& a, const PairSortGeom& g, int pss, uint32_t* counts, uint32_t* bsum,
+                            int32_t* kout, int32_t* vout, uint32_t* ntot, hipStream_t st) {
+  const int nbits = g.bits[pss], nbins = 1 << nbits;
+  hipLaunchKernelGGL(k_pair_hist<FIRST>, dim3((unsigned)g.nseg), dim3(256), nbins * sizeof(uint32_t), st, a, g.E,
+                     g.shift[pss], nbits, (int)g.seg_len, (int)g.nseg, counts);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3((unsigned)((int64_t)a.n_c * a.tiles_per_chunk)), dim3(64 * NW), lds, st, a);
+  e = launch_exclusive_scan(counts, (int64_t)nbins * g.nseg + 1, bsum, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_pair_scatter<FIRST>, dim3((unsigned)((g.nseg + 3) / 4)), dim3(256),
+                     4 * nbins * sizeof(uint32_t), st, a, g.E, g.shift[pss], nbits, (int)g.seg_len, (int)g.nseg,
+                     counts, kout, vout, ntot);
   return hipGetLastError();
 }
-template <class E, int D, int NW, bool SCE>
-static hipError_t launch_items_t(const BwdArgs& a, int itiles, hipStream_t st) {
-  const size_t lds = items_lds<E, D>(NW, a.rounds);
-  auto kern = k_bwd_items<E, D, NW, SCE>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3((unsigned)((int64_t)a.n_c * itiles)), dim3(64 * NW), lds, st, a, itiles);
-  return hipGetLastError();
-}
 
-hipError_t launch_bwd_rows(bool bf16v, int d, int waves, const BwdArgs& a, hipStream_t st) {
-#define RECE_R(E, DD) \
-  if (d == DD) return a.sce ? launch_rows_t<E, DD, 4, true>(a, st) : launch_rows_t<E, DD, 4, false>(a, st);
-  (void)waves;
-  if (bf16v) {
-    RECE_R(bf16, 32) RECE_R(bf16, 64) RECE_R(bf16, 128) RECE_R(bf16, 256)
-  } else {
-    RECE_R(float, 32) RECE_R(float, 64) RECE_R(float, 128) RECE_R(float, 256)
+hipError_t launch_pair_sort(const PairSortGeom& g, const int32_t* negs, int64_t nl, int k, int64_t s,
+                            const int32_t* pos, int64_t C, void* scratch, int32_t* kA, int32_t* vA, int32_t* kB,
+                            int32_t* vB, const int32_t** kout, const int32_t** vout, const uint32_t** nout,
+                            hipStream_t st) {
+  uint32_t* base = static_cast<uint32_t*>(scratch);
+  uint32_t* ntot = base;              // [8] record counts after each pass
+  uint32_t* counts = base + 8;
+  uint32_t* bsum = counts + g.count_words;
+  PairSrc a{};
+  a.negs = negs;
+  a.pos = pos;
+  a.nl = nl;
+  a.s = s;
+  a.C = C;
+  a.k = k > 0 ? k : 1;
+  int32_t* kbuf[2] = {kA, kB};
+  int32_t* vbuf[2] = {vA, vB};
+  for (int pss = 0; pss < g.npass; ++pss) {
+    int32_t* ko = kbuf[pss & 1];
+    int32_t* vo = vbuf[pss & 1];
+    hipError_t e;
+    if (pss == 0) {
+      e = pair_pass<true>(a, g, pss, counts, bsum, ko, vo, ntot + pss, st);
+    } else {
+      a.kin = kbuf[(pss - 1) & 1];
+      a.vin = vbuf[(pss - 1) & 1];
+      a.nin = ntot + pss - 1;
+      e = pair_pass<false>(a, g, pss, counts, bsum, ko, vo, ntot + pss, st);
+    }
+    if (e != hipSuccess) return e;
   }
-#undef RECE_R
-  return hipErrorInvalidValue;
+  *kout = kbuf[(g.npass - 1) & 1];
+  *vout = vbuf[(g.npass - 1) & 1];
+  *nout = ntot + g.npass - 1;
+  return hipSuccess;
 }
 
-hipError_t launch_bwd_items(bool bf16v, int d, int waves, const BwdArgs& a, int itiles, hipStream_t st) {
-#define RECE_I(E, DD) \
-  if (d == DD)                                                                    \
-    return a.sce ? launch_items_t<E, DD, 4, true>(a, itiles, st) : launch_items_t<E, DD, 4, false>(a, itiles, st);
-  (void)waves;
-  if (bf16v) {
-    RECE_I(bf16, 32) RECE_I(bf16, 64) RECE_I(bf16, 128) RECE_I(bf16, 256)
-  } else {
-    RECE_I(float, 32) RECE_I(float, 64) RECE_I(float, 128) RECE_I(float, 256)
-  }
-#undef RECE_I
-  return hipErrorInvalidValue;
+static int64_t dy_nsub(int64_t E) { return (E + DY_SUB - 1) / DY_SUB > 0 ? (E + DY_SUB - 1) / DY_SUB : 1; }
+
+size_t dy_area_bytes(int64_t E, int d) {
+  const int64_t nsub = dy_nsub(E);
+  return (size_t)nsub * 2 * d * 4 + (size_t)nsub * 3 * 4 + 256;
 }
 
-// The work area: head/tail partial rows [npieces][2][D] floats, staged rows
-// [npieces * PIECE][D] floats, then pitem [npieces][2], pflag [npieces], staged
-// counts [npieces] and staged items [npieces * PIECE], all int32.
-struct PosArea {
-  float* partial;
-  int32_t* pitem;
-  int32_t* pflag;
-  PosStage stage;
-  int64_t npieces;
-};
-static PosArea pos_area(float* base, int64_t s, int d) {
-  PosArea a;
-  a.npieces = (s + PIECE - 1) / PIECE;
-  a.partial = base;
-  a.stage.rows = base + a.npieces * 2 * d;
-  a.pitem = reinterpret_cast<int32_t*>(a.stage.rows + a.npieces * PIECE * d);
-  a.pflag = a.pitem + a.npieces * 2;
-  a.stage.n = a.pflag + a.npieces;
-  a.stage.items = a.stage.n + a.npieces;
+static DyArea dy_area(void* base, int64_t E, int d) {
+  DyArea a;
+  a.nsub = dy_nsub(E);
+  a.partial = static_cast<float*>(base);
+  a.flags = reinterpret_cast<int32_t*>(a.partial + a.nsub * 2 * d);
+  a.items = a.flags + a.nsub;
   return a;
 }
 
 template <class E, int D>
-static hipError_t launch_pieces_t(const BwdArgs& a, const int32_t* sorted, float* area, hipStream_t st) {
-  const PosArea w = pos_area(area, a.s, D);
-  const unsigned blocks = (unsigned)((w.npieces + 3) / 4);
-  hipLaunchKernelGGL((k_pos_pieces<E, D>), dim3(blocks), dim3(256), 0, st, a, sorted, w.partial, w.pitem, w.pflag,
-                     w.stage, w.npieces);
-  return hipGetLastError();
-}
-
-template <int D>
-static hipError_t launch_combine_t(int64_t s, float* dY, float* area, hipStream_t st) {
-  const PosArea w = pos_area(area, s, D);
-  const unsigned blocks = (unsigned)((w.npieces + 3) / 4);
-  hipLaunchKernelGGL((k_pos_combine<D>), dim3(blocks), dim3(256), 0, st, dY, w.partial, w.pitem, w.pflag, w.stage,
-                     w.npieces);
-  return hipGetLastError();
-}
-
-hipError_t launch_pos_pieces(bool bf16v, int d, const BwdArgs& a, const int32_t* sorted, float* area,
-                             hipStream_t st) {
-  if (a.s == 0) return hipSuccess;
-#define RECE_P(E, DD) \
-  if (d == DD) return launch_pieces_t<E, DD>(a, sorted, area, st);
-  if (bf16v) {
-    RECE_P(bf16, 32) RECE_P(bf16, 64) RECE_P(bf16, 128) RECE_P(bf16, 256)
-  } else {
-    RECE_P(float, 32) RECE_P(float, 64) RECE_P(float, 128) RECE_P(float, 256)
-  }
-#undef RECE_P
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_pos_combine(int d, int64_t s, float* dY, float* area, hipStream_t st) {
-  if (s == 0) return hipSuccess;
-  switch (d) {
-    case 32: return launch_combine_t<32>(s, dY, area, st);
-    case 64: return launch_combine_t<64>(s, dY, area, st);
-    case 128: return launch_combine_t<128>(s, dY, area, st);
-    case 256: return launch_combine_t<256>(s, dY, area, st);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-hipError_t launch_pos_dy(bool bf16v, int d, const BwdArgs& a, const int32_t* sorted, float* area,
-                         hipStream_t st) {
-  const hipError_t e = launch_pos_pieces(bf16v, d, a, sorted, area, st);
+static hipError_t launch_dy_t(const BwdArgs& a, const int32_t* K, const int32_t* V, const uint32_t* ntot, int64_t En,
+                              void* area, hipStream_t st) {
+  constexpr int RPI = WAVE / (D / (16 / (int)sizeof(E)));
+  const DyArea ar = dy_area(area, En, D);
+  const int64_t groups_per_block = 4 * RPI;
+  hipLaunchKernelGGL((k_dy_pieces<E, D>), dim3((unsigned)((ar.nsub + groups_per_block - 1) / groups_per_block)),
+                     dim3(256), 0, st, a, K, V, ntot, ar);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_pos_combine(d, a.s, a.dY, area, st);
+  constexpr int CRPI = WAVE / (D / 4) > 0 ? WAVE / (D / 4) : 1;
+  hipLaunchKernelGGL((k_dy_combine<D>), dim3((unsigned)((ar.nsub + 4 * CRPI - 1) / (4 * CRPI))), dim3(256), 0, st,
+                     a.dY, ntot, ar);
+  return hipGetLastError();
+}
+
+hipError_t launch_dy(bool bf16v, int d, const BwdArgs& a, const int32_t* K, const int32_t* V, const uint32_t* ntot,
+                     int64_t E, void* area, hipStream_t st) {
+#define RECE_DY(EE, DD) \
+  if (d == DD) return launch_dy_t<EE, DD>(a, K, V, ntot, E, area, st);
+  if (bf16v) {
+    RECE_DY(bf16, 32) RECE_DY(bf16, 64) RECE_DY(bf16, 128) RECE_DY(bf16, 256)
+  } else {
+    RECE_DY(float, 32) RECE_DY(float, 64) RECE_DY(float, 128) RECE_DY(float, 256)
+  }
+#undef RECE_DY
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_dx_lists(bool bf16v, int d, const BwdArgs& a, hipStream_t st) {
@@ -852,9 +587,10 @@ hipError_t launch_strip_mark(const int32_t* src, int64_t n, int32_t* dst, hipStr
   return hipGetLastError();
 }
 
-size_t pos_partial_bytes(int64_t s, int d) {
-  const int64_t npieces = (s + PIECE - 1) / PIECE;
-  return (size_t)npieces * (2 + PIECE) * d * 4 + (size_t)npieces * (4 + PIECE) * 4;
+hipError_t launch_union_ids(const int32_t* negs, int64_t s, int k, int rounds, int32_t* dst, hipStream_t st) {
+  if (s == 0 || k == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_union_ids, dim3((unsigned)((s + 3) / 4)), dim3(256), 0, st, negs, s, k, rounds, dst);
+  return hipGetLastError();
 }
 
 }  // namespace rece

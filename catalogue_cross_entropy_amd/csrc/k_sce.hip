@@ -15,10 +15,8 @@
 //   k_group_bounds    groups of a sorted key list (slots of each position,
 //                     slots of each item);
 //   k_sce_merge       per position, the exact top-k of the union of its bucket
-//                     lists (duplicates removed), its threshold and sums;
-//   k_mark_items      bitmap of the items of every bucket (backward dedup);
-//   k_sce_combine_*   backward: per-slot partial gradient rows summed per
-//                     position / item in slot order (no atomics).
+//                     lists (duplicates removed), its threshold and sums, and
+//                     its kept list, which the backward pass reads as RECE's.
 #include "rece_device.h"
 #include "rece_internal.h"
 #include "rece_kth.h"
@@ -346,24 +344,6 @@ hipError_t launch_col_select(bool is_bf16, int d, const ColSelectArgs& a, hipStr
 }
 
 // ------------------------------------------------------------ small helpers
-__global__ __launch_bounds__(256) void k_mark_items(const int32_t* __restrict__ Q, int64_t total, int b_y,
-                                                    int64_t qwords, uint32_t* __restrict__ qbits) {
-  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (e >= total) return;
-  const int64_t b = e / b_y;
-  const int j = Q[e];
-  atomicOr(qbits + b * qwords + (j >> 5), 1u << (j & 31));
-}
-
-hipError_t launch_mark_items(const int32_t* Q, int n_b, int b_y, int64_t qwords, uint32_t* qbits, hipStream_t st) {
-  hipError_t e = launch_fill_u32(qbits, 0u, (int64_t)n_b * qwords, st);
-  if (e != hipSuccess) return e;
-  const int64_t total = (int64_t)n_b * b_y;
-  hipLaunchKernelGGL(k_mark_items, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, Q, total, b_y, qwords,
-                     qbits);
-  return hipGetLastError();
-}
-
 // start[key], end[key]: the range of sorted positions q whose element keys[sorted[q]] is key.
 __global__ __launch_bounds__(256) void k_group_bounds(const int32_t* __restrict__ keys,
                                                       const int32_t* __restrict__ sorted, int64_t n,
@@ -597,57 +577,6 @@ hipError_t launch_sce_merge(bool is_bf16, int d, const MergeArgs& a, hipStream_t
   }
 #undef RECE_MG
   return hipErrorInvalidValue;
-}
-
-// ------------------------------------------------------------ backward combines
-// out[i][t..t+3] = sum over the group of i (slots in order) of part[slot][t..t+3],
-// plus, for positions, the positive term (e^{l+ - lse} - 1) * gbar * y_pos.
-template <class E>
-__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part, const int32_t* __restrict__ sorted,
-                                                 const int32_t* __restrict__ start, const int32_t* __restrict__ end,
-                                                 int64_t n, int d, BwdArgs b, int with_pos, float* __restrict__ out) {
-  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int q4 = d / 4;
-  if (e >= n * q4) return;
-  const int64_t i = e / q4;
-  const int t = 4 * (int)(e % q4);
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int g1 = end[i];
-  for (int q = start[i]; q < g1; ++q) acc += *reinterpret_cast<const f32x4*>(part + (int64_t)sorted[q] * d + t);
-  if (with_pos) {
-    const float gb = b.dloss_pp ? b.dloss_pp[i] : b.dloss[0] / (float)b.npos;
-    const float gp = (expf(b.lpos[i] - b.lse[i]) - 1.0f) * gb;
-    int j = b.pos[i];
-    j = j < 0 ? 0 : (j >= b.C ? (int)(b.C - 1) : j);
-    const E* y = static_cast<const E*>(b.Y) + (int64_t)j * d + t;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) acc[u] += gp * to_f32(y[u]);
-  }
-  *reinterpret_cast<f32x4*>(out + i * d + t) = acc;
-}
-
-hipError_t launch_sce_combine_rows(int d, const float* part, const int32_t* sorted, const int32_t* start,
-                                   const int32_t* end, int64_t n, const BwdArgs& b, bool is_bf16, float* out,
-                                   hipStream_t st) {
-  const int64_t total = n * (d / 4);
-  if (total <= 0) return hipSuccess;
-  if (is_bf16)
-    hipLaunchKernelGGL(k_combine<bf16>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, part, sorted, start,
-                       end, n, d, b, 1, out);
-  else
-    hipLaunchKernelGGL(k_combine<float>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, part, sorted,
-                       start, end, n, d, b, 1, out);
-  return hipGetLastError();
-}
-
-hipError_t launch_sce_combine_items(int d, const float* part, const int32_t* sorted, const int32_t* start,
-                                    const int32_t* end, int64_t n, float* out, hipStream_t st) {
-  const int64_t total = n * (d / 4);
-  if (total <= 0) return hipSuccess;
-  BwdArgs none{};
-  hipLaunchKernelGGL(k_combine<float>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, part, sorted, start,
-                     end, n, d, none, 0, out);
-  return hipGetLastError();
 }
 
 }  // namespace rece

@@ -1,27 +1,29 @@
 // In-chunk logits and per-position top-k negatives (RECE page, Section 3,
-// Algorithm 1: the chunk, window and "logits for wrong classes" lines, repeated
-// over rounds; the top-k keeps the largest logits, which Section 3 argues carry
-// the largest gradients).
+// Algorithm 1: the chunk, window and wrong-class logit lines, repeated over
+// rounds; the top-k keeps the largest logits, which Section 3 argues carry the
+// largest gradients).
 //
 // Grid: one workgroup per (X-chunk c, tile of 16*NW sorted positions).  Each wave
 // owns 16 positions and keeps their fragments in registers.  The window (item
-// chunks c, c-1, c+1 of the round's sorted order, cyclic) streams through LDS 64
-// items at a time, double-buffered and prefetched one tile ahead; the 16x64 logit
-// block of a wave comes from the matrix cores and never leaves the chip.
+// chunks c - n_ec .. c + n_ec of the round's sorted order, cyclic or clipped; at
+// most two slot ranges) streams through LDS 64 items at a time, double-buffered
+// and prefetched one tile ahead; the 16x64 logit block of a wave comes from the
+// matrix cores and never leaves the chip.
 //
 // Selection, two passes over the window per position:
 //   pass 1: a 256-bin histogram of the float32 logits over [-b_i, b_i]
 //           (b_i >= every |logit| of the row) locates the bin of the k-th largest;
 //           a bin too full for the candidate list is split by further passes;
+//           the counts are 16 bits, two to an LDS word, unless a window can hold
+//           more than 65535 items (WIDE: one 32-bit count per word);
 //   pass 2: the logits are recomputed; a logit above the bin (plus 2*beta, beta
 //           bounding |float32 - float64 logit|) is kept for sure and summed on the
 //           fly; logits within the bin +- 2*beta go to an LDS candidate list.
 // The list then gives the float32 k-th value a_k; the few entries within 2*beta of
 // a_k are recomputed in float64 and ranked (logit desc, id asc).  The k-th kept
-// element (float64 logit, id) is the position's threshold: membership of any
-// later pair is decided against it.  The kept ids themselves are also written
-// out when asked (NEGS), unordered and -1 padded, with their float32 logits when
-// asked (negl).
+// element (float64 logit, id) is the position's threshold; the kept ids are
+// written out, unordered and -1 padded, with their float32 logits when asked
+// (negl).
 //
 // Rounds: every round selects on its own window; which of its kept pairs were
 // already kept in an earlier round (the page's minus-ln(count) rule makes the
@@ -50,8 +52,8 @@ constexpr float LOG2E_F = 1.44269504088896341f;
 
 struct WaveLds {
   double* ce;       // [WL] (in the ring)
-  uint32_t* hist;   // [16][HIST_STRIDE] two 16-bit counts per word (histogram passes),
-                    // aliased by vals/ids (collect pass)
+  uint32_t* hist;   // [16][HistGeom::STRIDE] two 16-bit counts per word, or one 32-bit count
+                    // (WIDE), in the histogram passes; aliased by vals/ids (collect pass)
   float* vals;      // [16][LIST_STRIDE] (SEL_CAP used)
   int32_t* ids;     // [16][LIST_STRIDE]
   int32_t* ci;      // [WL] list index in the row's candidate list (in the ring)
@@ -59,14 +61,15 @@ struct WaveLds {
   int32_t* cr;      // [WL] row (in the ring)
 };
 // Row strides in LDS, padded so that the 16 rows of a wave start in different
-// banks (histogram: 129 words; lists: 68 entries, a multiple of four for the
-// 16-byte reads of the epilogue).
-constexpr int HIST_STRIDE = NBINS / 2 + 1;
+// banks (histogram: 129 words, 257 when WIDE; lists: 68 entries, a multiple of
+// four for the 16-byte reads of the epilogue).
 constexpr int LIST_STRIDE = SEL_CAP + 4;
-constexpr size_t WAVE_UNION = (size_t)16 * HIST_STRIDE * 4 > (size_t)16 * LIST_STRIDE * 8
-                                  ? (size_t)16 * HIST_STRIDE * 4
-                                  : (size_t)16 * LIST_STRIDE * 8;
-constexpr size_t WAVE_LDS = WAVE_UNION;
+template <bool WIDE> struct HistGeom {
+  static constexpr int STRIDE = WIDE ? NBINS + 1 : NBINS / 2 + 1;
+  static constexpr size_t WAVE_LDS = (size_t)16 * STRIDE * 4 > (size_t)16 * LIST_STRIDE * 8
+                                         ? (size_t)16 * STRIDE * 4
+                                         : (size_t)16 * LIST_STRIDE * 8;
+};
 constexpr size_t BATCH_ENTRY = 8 + 4 + 4 + 4;   // ce, ci, cj, cr
 
 // base: the wave's histogram/list region; batch: the wave's part of the ring
@@ -107,7 +110,7 @@ template <class E, int D, int NW> struct SelGeom {
 
 // NEGS: the kept ids are written out (p.negs set); a template flag keeps that
 // code out of the streaming loop when they are not.
-template <class E, int D, int NW, bool NEGS>
+template <class E, int D, int NW, bool NEGS, bool WIDE>
 __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 256) ? 3 : ((D * sizeof(E) <= 512) ? 2 : 1)) void k_select(SelectArgs p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   using G = TileGeom<E, D>;
@@ -125,7 +128,8 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 256) ? 3 : ((D * sizeof(
   constexpr int RING = SelGeom<E, D, NW>::RING, WLIST = SelGeom<E, D, NW>::WL;
   int32_t* wg_flag = reinterpret_cast<int32_t*>(smem + RING * slot_bytes);
   const int w = threadIdx.x >> 6, l = lane_id(), g = l >> 4;
-  WaveLds L = carve(smem + sel_common_lds(G::ROW_BYTES, RING) + (size_t)w * WAVE_LDS,
+  constexpr int HIST_STRIDE = HistGeom<WIDE>::STRIDE;
+  WaveLds L = carve(smem + sel_common_lds(G::ROW_BYTES, RING) + (size_t)w * HistGeom<WIDE>::WAVE_LDS,
                     smem + (size_t)w * WLIST * BATCH_ENTRY, WLIST);
   (void)X;
   (void)n_c;
@@ -142,7 +146,7 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 256) ? 3 : ((D * sizeof(
 
   // window ranges (own chunk first), in tiles of TI items
   Ranges win;
-  win.init(c, n_c, C, TI, p.nwin);
+  win.init(c, n_c, C, TI, p.n_ec, p.wrap);
   const int ntiles = win.ntiles();
 
   // fragments of this wave's 16 positions (sorted copy: contiguous rows)
@@ -229,7 +233,10 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 256) ? 3 : ((D * sizeof(
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
               const int b = (int)__builtin_amdgcn_fmed3f(fmaf(acc[cb][v], sc0, off0), 0.0f, X_TOP);
-              lds_add_u32(hist_row + ((b >> 1) << 2), (int)jj[v] != pos ? 1u << ((b & 1) << 4) : 0u);
+              if (WIDE)
+                lds_add_u32(hist_row + (b << 2), (int)jj[v] != pos ? 1u : 0u);
+              else
+                lds_add_u32(hist_row + ((b >> 1) << 2), (int)jj[v] != pos ? 1u << ((b & 1) << 4) : 0u);
             }
           }
         } else {
@@ -244,7 +251,10 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 256) ? 3 : ((D * sizeof(
               const float y = (x - xa) * mul;
               const bool hit = valid && y >= 0.0f && y < (float)NBINS;
               const int b = hit ? (int)y : 0;
-              lds_add_u32(hist_row + ((b >> 1) << 2), hit ? 1u << ((b & 1) << 4) : 0u);
+              if (WIDE)
+                lds_add_u32(hist_row + (b << 2), hit ? 1u : 0u);
+              else
+                lds_add_u32(hist_row + ((b >> 1) << 2), hit ? 1u << ((b & 1) << 4) : 0u);
             }
           }
         }
@@ -314,7 +324,10 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 256) ? 3 : ((D * sizeof(
       const float xar = lane_val(xa, rr), mulr = lane_val(mul, rr), lo0r = lane_val(lo0, rr);
       const float sc0r = lane_val(sc0, rr), off0r = lane_val(off0, rr), betar = lane_val(beta, rr);
       uint32_t h[4];
-      {
+      if (WIDE) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) h[q] = L.hist[rr * HIST_STRIDE + 4 * l + q];
+      } else {
         const uint32_t w0 = L.hist[rr * HIST_STRIDE + 2 * l], w1 = L.hist[rr * HIST_STRIDE + 2 * l + 1];
         h[0] = w0 & 0xFFFFu;
         h[1] = w0 >> 16;
@@ -600,13 +613,13 @@ __global__ __launch_bounds__(64 * NW, (D * sizeof(E) <= 256) ? 3 : ((D * sizeof(
 }
 
 template <class E, int D>
-static size_t select_lds_bytes_t(int waves) {
-  return sel_common_lds(TileGeom<E, D>::ROW_BYTES, SelGeom<E, D, 4>::RING) + (size_t)waves * WAVE_LDS;
+static size_t select_lds_bytes_t(int waves, bool wide) {
+  return sel_common_lds(TileGeom<E, D>::ROW_BYTES, SelGeom<E, D, 4>::RING) +
+         (size_t)waves * (wide ? HistGeom<true>::WAVE_LDS : HistGeom<false>::WAVE_LDS);
 }
-size_t select_lds_bytes(bool is_bf16, int d, int waves, int rounds) {
-  (void)rounds;   // every round selects on its own: the LDS does not grow with rounds
+size_t select_lds_bytes(bool is_bf16, int d, int waves, bool wide) {
 #define RECE_L(E, DD) \
-  if (d == DD) return select_lds_bytes_t<E, DD>(waves);
+  if (d == DD) return select_lds_bytes_t<E, DD>(waves, wide);
   if (is_bf16) {
     RECE_L(bf16, 32) RECE_L(bf16, 64) RECE_L(bf16, 128) RECE_L(bf16, 256)
   } else {
@@ -618,8 +631,10 @@ size_t select_lds_bytes(bool is_bf16, int d, int waves, int rounds) {
 
 template <class E, int D, int NW>
 static hipError_t launch_sel(const SelectArgs& a, hipStream_t st) {
-  const size_t lds = select_lds_bytes(sizeof(E) == 2, D, NW, a.rounds);
-  auto kern = a.negs ? k_select<E, D, NW, true> : k_select<E, D, NW, false>;
+  const bool wide = a.wide != 0;
+  const size_t lds = select_lds_bytes(sizeof(E) == 2, D, NW, wide);
+  auto kern = wide ? (a.negs ? k_select<E, D, NW, true, true> : k_select<E, D, NW, false, true>)
+                   : (a.negs ? k_select<E, D, NW, true, false> : k_select<E, D, NW, false, false>);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;

@@ -1,5 +1,6 @@
-// Stable counting sort of small integer keys (RECE page, Section 3, Algorithm 1:
-// "X = X[argsort I]", "Y = Y[argsort J]"; stable ascending order).
+// Stable counting sort of small integer keys (RECE page, Section 3, Algorithm 1,
+// the sorting lines: positions and items reordered by bucket index; read as a
+// stable ascending argsort).
 //
 // Three passes over the keys, no atomics on the output path:
 //   1. per segment of keys (256 to SORT_SEG of them), a histogram in LDS -> counts[bin][segment];
@@ -118,6 +119,11 @@ static hipError_t exclusive_scan(uint32_t* a, int64_t n, uint32_t* bsum, hipStre
   hipLaunchKernelGGL(k_scan_top, dim3(1), dim3(256), 0, st, bsum, nb);
   hipLaunchKernelGGL(k_scan_apply, dim3((unsigned)nb), dim3(256), 0, st, a, n, bsum);
   return hipGetLastError();
+}
+
+hipError_t launch_exclusive_scan(uint32_t* a, int64_t n, uint32_t* bsum, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  return exclusive_scan(a, n, bsum, st);
 }
 
 // --- stable scatter: one wave per segment -------------------------------------

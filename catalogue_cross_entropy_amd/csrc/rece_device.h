@@ -249,59 +249,11 @@ __device__ __forceinline__ int chunk_of(int64_t p, int64_t N, int n_c) {
 __host__ __device__ __forceinline__ int64_t chunk_start(int64_t c, int64_t N, int n_c) {
   return (c * N + n_c - 1) / n_c;
 }
-// Is item-chunk cy in the window {cx-1, cx, cx+1} (mod n_c) of position-chunk cx?
-__device__ __forceinline__ bool in_window(int cx, int cy, int n_c) {
-  if (n_c <= 3) return true;
-  int dlt = cy - cx;
-  if (dlt < 0) dlt += n_c;
-  return dlt == 0 || dlt == 1 || dlt == n_c - 1;
-}
-
-// Is pair (i, j) with float32 logit a in a round's kept set?  The set is given by
-// its k-th element (float64 logit te, item id tid) and the float32 bounds
-// lo <= te - beta, hi >= te + beta, beta bounding |a - float64 logit|:
-// above hi -> kept, below lo -> not kept, in between -> float64 comparison in the
-// order (logit desc, id asc).  lo = hi = -inf: every candidate kept; +inf: none.
-// The float64 comparison of beats(): out of line, so the streaming loops that
-// call beats() carry only its float32 fast path.
-template <class E, int D>
-__device__ __attribute__((noinline)) bool beats_exact(double te, int tid, const E* xrow, const E* Y, int j) {
-  const double e = exact_dot<E, D, 2>(xrow, Y + (int64_t)j * D);
-  return e > te || (e == te && j <= tid);
-}
-
-// nexact counts the float64 recomputations (a per-lane tally, flushed by flush_count).
-template <class E, int D>
-__device__ __forceinline__ bool beats(float a, float lo, float hi, double te, int tid, const E* xrow,
-                                      const E* Y, int j, uint32_t& nexact) {
-  if (a > hi) return true;
-  if (a < lo) return false;
-  if (j == tid) return true;
-  ++nexact;
-  return beats_exact<E, D>(te, tid, xrow, Y, j);
-}
 
 // Add a per-lane tally to a device counter: one atomic per wave.
 __device__ __forceinline__ void flush_count(uint32_t* counter, uint32_t v) {
   const int t = wave_sum((int)v);
   if (lane_id() == 0 && t != 0) atomicAdd(counter, (uint32_t)t);
 }
-
-struct PrevRow {   // a position's kept-set threshold in an earlier round (32 bytes)
-  double te;
-  float lo, hi;
-  int tid, cx;
-  int pad0, pad1;
-};
-
-struct PosRec {    // a position's backward data in one round, stored in sorted order (48 bytes)
-  float lse, gb, lo, hi;
-  double te;
-  int tid, pos, i;
-  float lpos;
-  int pad0, pad1;
-};
-static_assert(sizeof(PosRec) == 48, "PosRec is streamed in 16-byte chunks");
-static_assert(sizeof(PrevRow) == 32, "PrevRow is streamed in 16-byte chunks");
 
 }  // namespace rece

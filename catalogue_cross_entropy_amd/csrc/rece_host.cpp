@@ -49,6 +49,8 @@ struct Layout {
   }
 };
 
+constexpr int32_t MAX_N_EC = 1 << 20;
+
 }  // namespace
 
 #define RECE_HIP(call, where)                 \
@@ -91,26 +93,27 @@ struct rece_plan_s {
   int esize;
   int nbits_b;
   int selall;
-  int cap;
+  int wide;
   int waves_sel;
   int tpc_sel;
-  int tpc_bwd;
-  int itiles;
-  int pos_passes;
+  int64_t wmax;       // largest window (items)
   float beta_coef;
-  // saved
-  size_t o_cnt, o_bx, o_by, o_px, o_ix, o_py, o_iy, o_te, o_tid, o_tlo, o_thi, o_msh, o_ssum, o_nmem, o_xnorm,
-      o_ymax, o_lse, o_lpos, o_negs, o_xs, o_ys, o_cyp, o_psort, saved_bytes;
-  // scratch
-  size_t o_bt, o_bnorm, o_und, o_undy, o_sorty, o_sort, o_part, o_pp0, o_pp1, o_ppart, o_rec, o_prev, o_negl,
-      scratch_bytes;
-  int dedup_bits;   // LDS hash size of the round dedup (log2 slots per wave, 0 = list scan)
+  int dedup_bits;     // LDS hash size of the round dedup (log2 slots per wave, 0 = list scan)
+  PairSortGeom pg;    // backward: sort of the (item, position) records
+  int64_t npairs;     // rounds * s * k list entries + s positives
+  // saved (forward -> backward)
+  size_t o_cnt, o_bx, o_by, o_px, o_py, o_te, o_tid, o_tlo, o_thi, o_msh, o_ssum, o_nmem, o_xnorm, o_ymax, o_lse,
+      o_lpos, o_negs, saved_bytes;
+  // forward scratch
+  size_t o_bt, o_bnorm, o_und, o_undy, o_sorty, o_sort, o_part, o_negl, o_xs, o_ys;
+  // backward scratch (the backward reuses the forward's scratch from offset 0)
+  size_t o_pk0, o_pv0, o_pk1, o_pv1, o_psc, o_dya;
+  size_t scratch_bytes;
   // bucket variant: slots = (bucket, position) and (bucket, item) pairs
   int64_t sx, sy;     // n_b * b_x, n_b * b_y
-  int64_t qwords;     // words of one bucket's item bitmap
-  size_t o_R, o_Q, o_xmax, o_ssort, o_sinv, o_pstart, o_pend, o_qbits;                  // saved
-  size_t o_pxt, o_pyt, o_ste, o_stid, o_stlo, o_sthi, o_smsh, o_sssum, o_snmem, o_snegs, o_snegl, o_stmp,
-      o_dxs, o_dys, o_isort, o_itmp, o_istart, o_iend;                                   // scratch
+  size_t o_R, o_Q, o_xmax;                                                                  // saved
+  size_t o_ssort, o_sinv, o_pstart, o_pend, o_pxt, o_pyt, o_ste, o_stid, o_stlo, o_sthi, o_smsh, o_sssum, o_snmem,
+      o_snegs, o_snegl, o_stmp;                                                             // scratch
 };
 
 namespace {
@@ -151,8 +154,13 @@ static rece_status validate_config(const rece_config* c) {
   if (c->d != 32 && c->d != 64 && c->d != 128 && c->d != 256)
     return fail(RECE_ERR_UNSUPPORTED, "d must be one of 32, 64, 128, 256");
   if (c->n_b < 1 || c->n_b > 4096) return fail(RECE_ERR_INVALID_ARGUMENT, "n_b must be in 1..4096");
-  if (c->variant == RECE_VARIANT_RECE && (c->n_c < 1 || c->n_c > c->s || c->n_c > c->C))
-    return fail(RECE_ERR_INVALID_ARGUMENT, "n_c must be in 1..min(s, C)");
+  if (c->variant == RECE_VARIANT_RECE) {
+    if (c->n_c < 1 || c->n_c > c->s || c->n_c > c->C)
+      return fail(RECE_ERR_INVALID_ARGUMENT, "n_c must be in 1..min(s, C)");
+    if (c->n_ec < 0 || c->n_ec > MAX_N_EC) return fail(RECE_ERR_INVALID_ARGUMENT, "n_ec must be in 0..2^20");
+    if (c->window_wrap != 0 && c->window_wrap != 1)
+      return fail(RECE_ERR_INVALID_ARGUMENT, "window_wrap must be 0 (clipped) or 1 (cyclic)");
+  }
   if (c->variant == RECE_VARIANT_SCE) {
     if (c->rounds != 1) return fail(RECE_ERR_INVALID_ARGUMENT, "the bucket variant takes rounds = 1");
     if (c->b_x < 1 || c->b_x > c->s) return fail(RECE_ERR_INVALID_ARGUMENT, "b_x must be in 1..s");
@@ -166,7 +174,26 @@ static rece_status validate_config(const rece_config* c) {
   if (c->dtype != RECE_F32 && c->dtype != RECE_BF16) return fail(RECE_ERR_INVALID_ARGUMENT, "unknown dtype");
   if (c->flags & ~(RECE_FLAG_VALIDATE_IDS | RECE_FLAG_KEEP_STAGES))
     return fail(RECE_ERR_INVALID_ARGUMENT, "unknown flag bits");
+  if ((int64_t)c->rounds * c->s * std::max(c->k, 1) + c->s > ((int64_t)1 << 31) - 1)
+    return fail(RECE_ERR_UNSUPPORTED, "rounds * s * k + s must fit in int32 (the backward's pair records)");
   return RECE_OK;
+}
+
+// Backward scratch of either variant: the sort of the (item, position) records
+// and the dY work area.  Laid out from offset 0: the backward reads nothing of
+// the forward's scratch.
+static size_t plan_backward_scratch(rece_plan_s* p) {
+  const rece_config& c = p->cfg;
+  p->npairs = (int64_t)c.rounds * c.s * c.k + c.s;
+  p->pg = pair_sort_geom(p->npairs, c.C);
+  Layout sc;
+  p->o_pk0 = sc.take((size_t)p->npairs * 4);
+  p->o_pv0 = sc.take((size_t)p->npairs * 4);
+  p->o_pk1 = sc.take((size_t)p->npairs * 4);
+  p->o_pv1 = sc.take((size_t)p->npairs * 4);
+  p->o_psc = sc.take(p->pg.scratch_bytes);
+  p->o_dya = sc.take(dy_area_bytes(p->npairs, c.d));
+  return sc.off;
 }
 
 // Workspace of the bucket variant.
@@ -176,14 +203,11 @@ static void plan_sce_layout(rece_plan_s* p) {
   const int d = c.d, k = std::max(c.k, 1), n_b = c.n_b;
   p->sx = (int64_t)n_b * c.b_x;
   p->sy = (int64_t)n_b * c.b_y;
-  p->qwords = (C + 31) / 32;
   const int64_t sx = p->sx, sy = p->sy;
   Layout sv;
   p->o_cnt = sv.take(NUM_COUNTERS * 4);
   p->o_R = sv.take((size_t)sx * 4);
   p->o_Q = sv.take((size_t)sy * 4);
-  p->o_xs = sv.take((size_t)sx * d * p->esize);
-  p->o_ys = sv.take((size_t)sy * d * p->esize);
   p->o_te = sv.take((size_t)s * 8);
   p->o_tid = sv.take((size_t)s * 4);
   p->o_tlo = sv.take((size_t)s * 4);
@@ -196,27 +220,22 @@ static void plan_sce_layout(rece_plan_s* p) {
   p->o_ymax = sv.take(4);
   p->o_lse = sv.take((size_t)s * 4);
   p->o_lpos = sv.take((size_t)s * 4);
-  p->o_negs = (c.flags & RECE_FLAG_KEEP_STAGES) ? sv.take((size_t)s * k * 4) : 0;
-  p->o_ssort = sv.take((size_t)sx * 4);
-  p->o_sinv = sv.take((size_t)sx * 4);
-  p->o_pstart = sv.take((size_t)s * 4);
-  p->o_pend = sv.take((size_t)s * 4);
-  p->o_qbits = sv.take((size_t)n_b * p->qwords * 4);
+  p->o_negs = sv.take((size_t)s * k * 4);   // the final kept lists: the backward reads them
   p->saved_bytes = sv.off;
 
   Layout sc;
   p->o_bt = sc.take((size_t)n_b * d * p->esize);
   p->o_bnorm = sc.take(4);
   const size_t sort_b = std::max({sort_scratch_bytes(sx, 1 << std::min(12, bits_for(s))),
-                                  sort_scratch_bytes(sy, 1 << std::min(12, bits_for(C))),
-                                  sort_scratch_bytes(s, 1 << std::min(12, bits_for(C)))});
+                                  sort_scratch_bytes(sy, 1 << std::min(12, bits_for(C)))});
   p->o_sort = sc.take(sort_b);
   p->o_part = sc.take((size_t)ce_blocks(s) * 8);
-  p->o_pp0 = sc.take((size_t)s * 4);
-  p->o_pp1 = sc.take((size_t)s * 4);
-  p->o_ppart = sc.take(pos_partial_bytes(s, d));
-  p->o_rec = sc.take((size_t)sx * sizeof(PosRec));
-  p->o_prev = sc.take(sizeof(PrevRow));
+  p->o_xs = sc.take((size_t)sx * d * p->esize);   // rows taken by each bucket, bucket-major
+  p->o_ys = sc.take((size_t)sy * d * p->esize);
+  p->o_ssort = sc.take((size_t)sx * 4);
+  p->o_sinv = sc.take((size_t)sx * 4);
+  p->o_pstart = sc.take((size_t)s * 4);
+  p->o_pend = sc.take((size_t)s * 4);
   p->o_pxt = sc.take((size_t)n_b * s * 4);
   p->o_pyt = sc.take((size_t)n_b * C * 4);
   p->o_ste = sc.take((size_t)sx * 8);
@@ -229,13 +248,7 @@ static void plan_sce_layout(rece_plan_s* p) {
   p->o_snegs = sc.take((size_t)sx * k * 4);
   p->o_snegl = sc.take((size_t)sx * k * 4);
   p->o_stmp = sc.take((size_t)sx * 4);
-  p->o_dxs = sc.take((size_t)sx * d * 4);
-  p->o_dys = sc.take((size_t)sy * d * 4);
-  p->o_isort = sc.take((size_t)sy * 4);
-  p->o_itmp = sc.take((size_t)sy * 4);
-  p->o_istart = sc.take((size_t)C * 4);
-  p->o_iend = sc.take((size_t)C * 4);
-  p->scratch_bytes = sc.off;
+  p->scratch_bytes = std::max(sc.off, plan_backward_scratch(p));
 }
 
 // Stable grouping of n elements by an integer key below `nkeys`: LSD passes of up
@@ -279,12 +292,12 @@ static rece_status sce_forward(const rece_plan_s& p, hipStream_t st, const void*
   RECE_PHASE(RECE_PHASE_OTHER, launch_fill_u32(xmax, 0u, 1, st), "clear norm max");
   RECE_PHASE(RECE_PHASE_OTHER, launch_fill_u32(ymax, 0u, 1, st), "clear norm max");
   RECE_PHASE(RECE_PHASE_OTHER, launch_prep_b(p.bf16, d, B, 1, n_b, Bt, bnorm, 0, st), "prepare projection vectors");
-  // K6a: projection scores of every position and item, one column per bucket
+  // projection scores of every position and item, one column per bucket
   RECE_PHASE(RECE_PHASE_PROJECT, launch_project_scores(p.bf16, d, X, s, Bt, n_b, pxt, xnorm, xmax, st),
              "position scores");
   RECE_PHASE(RECE_PHASE_PROJECT, launch_project_scores(p.bf16, d, Y, C, Bt, n_b, pyt, nullptr, ymax, st),
              "item scores");
-  // K6b: the b_x positions and b_y items of every bucket
+  // the b_x positions and b_y items of every bucket
   ColSelectArgs ca{};
   ca.Bt = Bt;
   ca.n_b = n_b;
@@ -305,12 +318,12 @@ static rece_status sce_forward(const rece_plan_s& p, hipStream_t st, const void*
   ca.vmax_bits = ymax;
   ca.out = Q;
   RECE_PHASE(RECE_PHASE_SORT, launch_col_select(p.bf16, d, ca, st), "bucket items");
-  char* xs = sv + p.o_xs;
-  char* ys = sv + p.o_ys;
+  char* xs = sc + p.o_xs;
+  char* ys = sc + p.o_ys;
   RECE_PHASE(RECE_PHASE_SORT, launch_gather_rows(X, R, p.sx, d * p.esize, xs, st), "bucket position rows");
   RECE_PHASE(RECE_PHASE_SORT, launch_gather_rows(Y, Q, p.sy, d * p.esize, ys, st), "bucket item rows");
 
-  // K6c: per (bucket, position) slot, the top-k of the bucket's items (the chunk kernel,
+  // per (bucket, position) slot, the top-k of the bucket's items (the chunk kernel,
   // one chunk per bucket, window = the chunk's own items)
   SelectArgs a{};
   a.X = X;
@@ -341,15 +354,17 @@ static rece_status sce_forward(const rece_plan_s& p, hipStream_t st, const void*
   a.negs = reinterpret_cast<int32_t*>(sc + p.o_snegs);
   a.negl = reinterpret_cast<float*>(sc + p.o_snegl);
   a.slot_out = 1;
-  a.nwin = 1;
+  a.n_ec = 0;
+  a.wrap = 0;
+  a.wide = p.wide;
   a.counters = counters;
   RECE_PHASE(RECE_PHASE_SELECT, launch_select(p.bf16, d, p.waves_sel, a, st), "bucket logits and top-k");
 
-  // K6d: slots grouped by position (bucket order inside a group), then the merge
-  int32_t* ssort = reinterpret_cast<int32_t*>(sv + p.o_ssort);
-  int32_t* sinv = reinterpret_cast<int32_t*>(sv + p.o_sinv);
-  int32_t* pstart = reinterpret_cast<int32_t*>(sv + p.o_pstart);
-  int32_t* pend = reinterpret_cast<int32_t*>(sv + p.o_pend);
+  // slots grouped by position (bucket order inside a group), then the merge
+  int32_t* ssort = reinterpret_cast<int32_t*>(sc + p.o_ssort);
+  int32_t* sinv = reinterpret_cast<int32_t*>(sc + p.o_sinv);
+  int32_t* pstart = reinterpret_cast<int32_t*>(sc + p.o_pstart);
+  int32_t* pend = reinterpret_cast<int32_t*>(sc + p.o_pend);
   const rece_status gs =
       group_by_key(p, R, p.sx, s, sc + p.o_sort, reinterpret_cast<int32_t*>(sc + p.o_stmp), ssort, sinv, st);
   if (gs != RECE_OK) return gs;
@@ -378,12 +393,9 @@ static rece_status sce_forward(const rece_plan_s& p, hipStream_t st, const void*
   m.mshift = reinterpret_cast<float*>(sv + p.o_msh);
   m.ssum = reinterpret_cast<float*>(sv + p.o_ssum);
   m.nmem = reinterpret_cast<int32_t*>(sv + p.o_nmem);
-  m.negs = p.o_negs ? reinterpret_cast<int32_t*>(sv + p.o_negs) : nullptr;
+  m.negs = reinterpret_cast<int32_t*>(sv + p.o_negs);
   m.counters = counters;
   RECE_PHASE(RECE_PHASE_SELECT, launch_sce_merge(p.bf16, d, m, st), "merge bucket lists");
-  RECE_PHASE(RECE_PHASE_OTHER,
-             launch_mark_items(Q, n_b, c.b_y, p.qwords, reinterpret_cast<uint32_t*>(sv + p.o_qbits), st),
-             "bucket item bitmaps");
 
   CeArgs ce{};
   ce.X = X;
@@ -405,90 +417,6 @@ static rece_status sce_forward(const rece_plan_s& p, hipStream_t st, const void*
   return RECE_OK;
 }
 
-static rece_status sce_backward(const rece_plan_s& p, hipStream_t st, const void* X, const void* Y,
-                                const int32_t* pos, const float* dloss, const float* dloss_pp, char* sc,
-                                const char* sv, float* dX, float* dY) {
-  const rece_config& c = p.cfg;
-  const int64_t s = c.s, C = c.C;
-  const int d = c.d;
-  BwdArgs b{};
-  b.X = X;
-  b.Y = Y;
-  b.Xs = sv + p.o_xs;
-  b.Ys = sv + p.o_ys;
-  b.rounds = 1;
-  b.pos = pos;
-  b.perm_x = reinterpret_cast<const int32_t*>(sv + p.o_R);
-  b.perm_y = reinterpret_cast<const int32_t*>(sv + p.o_Q);
-  b.s = p.sx;
-  b.C = p.sy;
-  b.n_c = c.n_b;
-  b.rho = 0;
-  b.tiles_per_chunk = p.tpc_bwd;
-  b.thr_e = reinterpret_cast<const double*>(sv + p.o_te);
-  b.thr_id = reinterpret_cast<const int32_t*>(sv + p.o_tid);
-  b.thr_lo = reinterpret_cast<const float*>(sv + p.o_tlo);
-  b.thr_hi = reinterpret_cast<const float*>(sv + p.o_thi);
-  b.lse = reinterpret_cast<const float*>(sv + p.o_lse);
-  b.lpos = reinterpret_cast<const float*>(sv + p.o_lpos);
-  b.dloss = dloss;
-  b.dloss_pp = dloss_pp;
-  b.dX = reinterpret_cast<float*>(sc + p.o_dxs);
-  b.dY = reinterpret_cast<float*>(sc + p.o_dys);
-  b.counters = reinterpret_cast<uint32_t*>(const_cast<char*>(sv) + p.o_cnt);
-  b.sce = 1;
-  b.nwin = 1;
-  b.npos = s;
-  b.b_x = c.b_x;
-  b.sce_sorted = reinterpret_cast<const int32_t*>(sv + p.o_ssort);
-  b.sce_pstart = reinterpret_cast<const int32_t*>(sv + p.o_pstart);
-  b.sce_inv = reinterpret_cast<const int32_t*>(sv + p.o_sinv);
-  b.qbits = reinterpret_cast<const uint32_t*>(sv + p.o_qbits);
-  b.qwords = p.qwords;
-  PosRec* recs = reinterpret_cast<PosRec*>(sc + p.o_rec);
-  b.rec = recs;
-  RECE_PHASE(RECE_PHASE_OTHER, launch_bwd_records(b, b.perm_x, 0, recs, nullptr, st), "backward records");
-  RECE_PHASE(RECE_PHASE_BWD_DX, launch_bwd_rows(p.bf16, d, 4, b, st), "dX partial rows");
-  RECE_PHASE(RECE_PHASE_BWD_DY, launch_bwd_items(p.bf16, d, 4, b, p.itiles, st), "dY partial rows");
-  // per position: its slots' partial rows in bucket order, plus the positive term
-  BwdArgs bc = b;
-  bc.C = C;   // the catalogue (bounds of the positive ids), not the item slots
-  RECE_PHASE(RECE_PHASE_BWD_DX,
-             launch_sce_combine_rows(d, b.dX, b.sce_sorted, b.sce_pstart,
-                                     reinterpret_cast<const int32_t*>(sv + p.o_pend), s, bc, p.bf16, dX, st),
-             "dX");
-  // per item: its item slots' partial rows in bucket order
-  int32_t* isort = reinterpret_cast<int32_t*>(sc + p.o_isort);
-  int32_t* istart = reinterpret_cast<int32_t*>(sc + p.o_istart);
-  int32_t* iend = reinterpret_cast<int32_t*>(sc + p.o_iend);
-  const rece_status gs = group_by_key(p, b.perm_y, p.sy, C, sc + p.o_sort, reinterpret_cast<int32_t*>(sc + p.o_itmp),
-                                      isort, nullptr, st);
-  if (gs != RECE_OK) return gs;
-  RECE_PHASE(RECE_PHASE_OTHER, launch_fill_u32(reinterpret_cast<uint32_t*>(istart), 0u, C, st), "clear groups");
-  RECE_PHASE(RECE_PHASE_OTHER, launch_fill_u32(reinterpret_cast<uint32_t*>(iend), 0u, C, st), "clear groups");
-  RECE_PHASE(RECE_PHASE_OTHER, launch_group_bounds(b.perm_y, isort, p.sy, istart, iend, st), "item groups");
-  RECE_PHASE(RECE_PHASE_BWD_DY, launch_sce_combine_items(d, b.dY, isort, istart, iend, C, dY, st), "dY");
-  // positives, as in RECE: positions sorted by positive id, segmented reduction into dY
-  BwdArgs bp = b;
-  bp.s = s;
-  bp.C = C;
-  bp.dY = dY;
-  int32_t* bufs[2] = {reinterpret_cast<int32_t*>(sc + p.o_pp0), reinterpret_cast<int32_t*>(sc + p.o_pp1)};
-  const int total_bits = std::max(1, bits_for(C));
-  const int db = sort_digit_bits(s);
-  const int32_t* sorted = nullptr;
-  for (int pass = 0, shift = 0; shift < total_bits; ++pass, shift += db) {
-    const int nb = std::min(db, total_bits - shift);
-    int32_t* outp = bufs[pass & 1];
-    RECE_PHASE(RECE_PHASE_SORT, launch_counting_sort(pos, sorted, s, shift, nb, sc + p.o_sort, outp, nullptr, st),
-               "sort positives");
-    sorted = outp;
-  }
-  RECE_PHASE(RECE_PHASE_BWD_POS, launch_pos_dy(p.bf16, d, bp, sorted, reinterpret_cast<float*>(sc + p.o_ppart), st),
-             "positive dY");
-  return RECE_OK;
-}
-
 extern "C" {
 
 rece_status rece_plan(const rece_config* cfg, rece_plan_t* out) {
@@ -499,30 +427,39 @@ rece_status rece_plan(const rece_config* cfg, rece_plan_t* out) {
   rece_plan_s* p = new (std::nothrow) rece_plan_s();
   if (!p) return fail(RECE_ERR_INTERNAL, "host allocation failed");
   p->cfg = *cfg;
-  const rece_config& c = p->cfg;
+  rece_config& c = p->cfg;
   const int64_t s = c.s, C = c.C;
   const bool sce = c.variant == RECE_VARIANT_SCE;
-  // bucket variant: a bucket is a chunk of b_x position slots whose window is its b_y item slots
+  if (sce) {   // a bucket is a chunk whose window is its own item list
+    c.n_ec = 0;
+    c.window_wrap = 0;
+  }
   const int d = c.d, r = c.rounds, k = c.k, n_c = sce ? c.n_b : c.n_c;
   p->bf16 = c.dtype == RECE_BF16;
   p->esize = p->bf16 ? 2 : 4;
   p->nbits_b = bits_for(c.n_b);
   const int64_t rows_chunk = sce ? c.b_x : (s + n_c - 1) / n_c;
-  const int64_t items_chunk = sce ? c.b_y : (C + n_c - 1) / n_c;
-  const int64_t wmax = sce ? c.b_y : (n_c <= 3 ? C : std::min<int64_t>(C, 3 * items_chunk));
-  p->selall = sce ? (k >= c.b_y) : ((k >= wmax) || (n_c <= 3 && k >= C - 1));
-  p->cap = 0;
+  // The largest window: every candidate is kept when k reaches it (a window of the
+  // whole catalogue has C - 1 candidates, the positive being excluded).
+  if (sce) {
+    p->wmax = c.b_y;
+    p->selall = k >= c.b_y;
+  } else {
+    const int64_t items_chunk = (C + n_c - 1) / n_c;
+    const int64_t span = 2 * (int64_t)c.n_ec + 1;
+    p->wmax = (c.window_wrap && span >= n_c) ? C : std::min<int64_t>(C, span * items_chunk);
+    p->selall = p->wmax >= C ? (k >= C - 1) : (k >= p->wmax);
+  }
+  // the histogram counts of a row reach the window size: 16-bit counts only below 65536
+  p->wide = (!p->selall && p->wmax > 65535) ? 1 : 0;
   p->waves_sel = 1;
   for (int nw : {4, 2, 1}) {
-    if (select_lds_bytes(p->bf16, d, nw, r) <= 160 * 1024) {
+    if (select_lds_bytes(p->bf16, d, nw, p->wide != 0) <= 160 * 1024) {
       p->waves_sel = nw;
       break;
     }
   }
   p->tpc_sel = (int)((rows_chunk + 16 * p->waves_sel - 1) / (16 * p->waves_sel));
-  p->tpc_bwd = (int)((rows_chunk + 63) / 64);
-  p->itiles = (int)((items_chunk + 63) / 64);
-  p->pos_passes = std::max(1, (bits_for(C) + sort_digit_bits(c.s) - 1) / sort_digit_bits(c.s));
   // |float32 matrix-core dot - float64 coordinate-order dot| <= beta_coef * ||x|| * ||y||:
   // d products and d additions, each with relative error at most 2^-23 (round or
   // chop), doubled for safety; the float64 side adds d * 2^-53.
@@ -538,9 +475,7 @@ rece_status rece_plan(const rece_config* cfg, rece_plan_t* out) {
   p->o_bx = sv.take((size_t)r * s * 4);
   p->o_by = sv.take((size_t)r * C * 4);
   p->o_px = sv.take((size_t)r * s * 4);
-  p->o_ix = sv.take((size_t)r * s * 4);
   p->o_py = sv.take((size_t)r * C * 4);
-  p->o_iy = sv.take((size_t)r * C * 4);
   p->o_te = sv.take((size_t)r * s * 8);
   p->o_tid = sv.take((size_t)r * s * 4);
   p->o_tlo = sv.take((size_t)r * s * 4);
@@ -551,12 +486,8 @@ rece_status rece_plan(const rece_config* cfg, rece_plan_t* out) {
   p->o_xnorm = sv.take((size_t)s * 4);
   p->o_ymax = sv.take(4);
   p->o_lse = sv.take((size_t)s * 4);
-  p->o_psort = sv.take((size_t)s * 4);   // positions sorted by positive id (stable)
   p->o_lpos = sv.take((size_t)s * 4);
-  p->o_negs = sv.take((size_t)r * s * std::max(k, 1) * 4);   // kept lists: dX reads them
-  p->o_xs = sv.take((size_t)r * s * d * p->esize);
-  p->o_ys = sv.take((size_t)r * C * d * p->esize);
-  p->o_cyp = sv.take((size_t)std::max(1, r * (r - 1) / 2) * C * 4);
+  p->o_negs = sv.take((size_t)r * s * std::max(k, 1) * 4);   // kept lists: the backward reads them
   p->saved_bytes = sv.off;
 
   Layout sc;
@@ -565,19 +496,15 @@ rece_status rece_plan(const rece_config* cfg, rece_plan_t* out) {
   p->o_und = sc.take((size_t)s * 4);    // undecided bucketing rows: positions,
   p->o_undy = sc.take((size_t)std::max(s, C) * 4);   // chains on the side stream (items, later positions)
   p->o_sorty = sc.take(std::max(sort_scratch_bytes(C, 1 << p->nbits_b), sort_scratch_bytes(s, 1 << p->nbits_b)));
-  const size_t sort_b = std::max({sort_scratch_bytes(s, 1 << p->nbits_b), sort_scratch_bytes(C, 1 << p->nbits_b),
-                                  sort_scratch_bytes(s, 1 << std::min(12, bits_for(C)))});
-  p->o_sort = sc.take(sort_b);
+  p->o_sort = sc.take(std::max(sort_scratch_bytes(s, 1 << p->nbits_b), sort_scratch_bytes(C, 1 << p->nbits_b)));
   p->o_part = sc.take((size_t)ce_blocks(s) * 8);
-  p->o_pp0 = sc.take((size_t)s * 4);
-  p->o_pp1 = sc.take((size_t)s * 4);
-  p->o_ppart = sc.take(pos_partial_bytes(s, d));
-  p->o_rec = sc.take((size_t)r * s * sizeof(PosRec));
-  p->o_prev = sc.take((size_t)std::max(1, r * (r - 1) / 2) * s * sizeof(PrevRow));
   // float32 logits of the kept lists of rounds >= 1 (the round dedup sums the new pairs)
   p->o_negl = sc.take((size_t)(r - 1) * s * k * 4);
+  // sorted copies of every round (each chunk and window one block of rows)
+  p->o_xs = sc.take((size_t)r * s * d * p->esize);
+  p->o_ys = sc.take((size_t)r * C * d * p->esize);
   p->dedup_bits = dedup_hash_bits(r, k);
-  p->scratch_bytes = sc.off;
+  p->scratch_bytes = std::max(sc.off, plan_backward_scratch(p));
   *out = p;
   return RECE_OK;
 }
@@ -673,13 +600,13 @@ rece_status rece_forward(rece_plan_t plan, void* stream, const void* X, const vo
   RECE_PHASE(RECE_PHASE_OTHER, launch_prep_b(p.bf16, d, B, c.rounds, c.n_b, Bt, bnorm, -1, st),
              "prepare random vectors");
 
-  // Item chain of every round (bucketing, sort, sorted copy, earlier-round chunks)
-  // and the position chains of rounds >= 1 run on the side stream, followed there by
-  // the chunk kernels of rounds >= 1 (a round's selection does not depend on the
-  // other rounds); round 0's position chain and chunk kernel run on the caller's
-  // stream.  Events: fork[rounds] starts the side stream, fork[rounds + 1] marks the
-  // position norms of round 0 (every chunk kernel reads them), fork[0] the end of
-  // round 0's item chain, fork[rounds + 2] the end of the side stream.
+  // Item chain of every round (bucketing, sort, sorted copy) and the position
+  // chains of rounds >= 1 run on the side stream, followed there by the chunk
+  // kernels of rounds >= 1 (a round's selection does not depend on the other
+  // rounds); round 0's position chain and chunk kernel run on the caller's
+  // stream.  Events: fork[rounds] starts the side stream, fork[rounds + 1] marks
+  // the position norms of round 0 (every chunk kernel reads them), fork[0] the end
+  // of round 0's item chain, fork[rounds + 2] the end of the side stream.
   const rece_status ss = ensure_side(p, c.rounds + 3);
   if (ss != RECE_OK) return ss;
   hipStream_t side = p.side.s;
@@ -687,29 +614,22 @@ rece_status rece_forward(rece_plan_t plan, void* stream, const void* X, const vo
   RECE_HIP(hipEventRecord(p.side.fork[c.rounds], st), "fork");
   RECE_HIP(hipStreamWaitEvent(side, p.side.fork[c.rounds], 0), "fork");
 
+  auto xs_of = [&](int rho) { return sc + p.o_xs + (size_t)rho * s * d * p.esize; };
+  auto ys_of = [&](int rho) { return sc + p.o_ys + (size_t)rho * C * d * p.esize; };
   auto select_args = [&](int rho) {
-    char* xs = sv + p.o_xs + (size_t)rho * s * d * p.esize;
-    char* ys = sv + p.o_ys + (size_t)rho * C * d * p.esize;
-    int32_t* px = reinterpret_cast<int32_t*>(sv + p.o_px) + (int64_t)rho * s;
-    int32_t* py = reinterpret_cast<int32_t*>(sv + p.o_py) + (int64_t)rho * C;
-    int32_t* cyp = reinterpret_cast<int32_t*>(sv + p.o_cyp) + (int64_t)(rho * (rho - 1) / 2) * C;
     SelectArgs a{};
     a.X = X;
     a.Y = Y;
-    a.Xs = xs;
-    a.Ys = ys;
-    a.cyp = cyp;
+    a.Xs = xs_of(rho);
+    a.Ys = ys_of(rho);
     a.rounds = c.rounds;
     a.pos = pos;
-    a.perm_x = px;
-    a.perm_y = py;
-    a.inv_x = reinterpret_cast<const int32_t*>(sv + p.o_ix);
-    a.inv_y = reinterpret_cast<const int32_t*>(sv + p.o_iy);
+    a.perm_x = reinterpret_cast<int32_t*>(sv + p.o_px) + (int64_t)rho * s;
+    a.perm_y = reinterpret_cast<int32_t*>(sv + p.o_py) + (int64_t)rho * C;
     a.s = s;
     a.C = C;
     a.n_c = c.n_c;
     a.k = c.k;
-    a.cap = p.cap;
     a.rho = rho;
     a.selall = p.selall;
     a.tiles_per_chunk = p.tpc_sel;
@@ -723,9 +643,11 @@ rece_status rece_forward(rece_plan_t plan, void* stream, const void* X, const vo
     a.mshift = reinterpret_cast<float*>(sv + p.o_msh);
     a.ssum = reinterpret_cast<float*>(sv + p.o_ssum);
     a.nmem = reinterpret_cast<int32_t*>(sv + p.o_nmem);
-    a.negs = p.o_negs ? reinterpret_cast<int32_t*>(sv + p.o_negs) : nullptr;
+    a.negs = reinterpret_cast<int32_t*>(sv + p.o_negs);
     a.slot_out = 0;
-    a.nwin = 3;
+    a.n_ec = c.n_ec;
+    a.wrap = c.window_wrap;
+    a.wide = p.wide;
     a.counters = counters;
     a.negl = rho > 0 ? reinterpret_cast<float*>(sc + p.o_negl) + (int64_t)(rho - 1) * s * c.k : nullptr;
     return a;
@@ -734,51 +656,39 @@ rece_status rece_forward(rece_plan_t plan, void* stream, const void* X, const vo
   {   // round 0's position chain, alongside the first item chain
     int32_t* bx = reinterpret_cast<int32_t*>(sv + p.o_bx);
     int32_t* px = reinterpret_cast<int32_t*>(sv + p.o_px);
-    int32_t* ix = reinterpret_cast<int32_t*>(sv + p.o_ix);
-    char* xs = sv + p.o_xs;
     RECE_PHASE(RECE_PHASE_PROJECT, launch_project_argmax(p.bf16, d, X, s, Bt, c.n_b, bnorm, p.beta_coef, bx,
                                    xnorm, nullptr, und, und_n, counters, st),
                "bucket positions");
     RECE_HIP(hipEventRecord(p.side.fork[c.rounds + 1], st), "position norms");
-    RECE_PHASE(RECE_PHASE_SORT, launch_counting_sort(bx, nullptr, s, 0, p.nbits_b, sc + p.o_sort, px, ix, st),
+    RECE_PHASE(RECE_PHASE_SORT, launch_counting_sort(bx, nullptr, s, 0, p.nbits_b, sc + p.o_sort, px, nullptr, st),
                "sort positions");
-    RECE_PHASE(RECE_PHASE_SORT, launch_gather_rows(X, px, s, d * p.esize, xs, st), "sorted positions");
+    RECE_PHASE(RECE_PHASE_SORT, launch_gather_rows(X, px, s, d * p.esize, xs_of(0), st), "sorted positions");
   }
 
   for (int rho = 0; rho < c.rounds; ++rho) {
     hipStream_t st = side;
     int32_t* by = reinterpret_cast<int32_t*>(sv + p.o_by) + (int64_t)rho * C;
     int32_t* py = reinterpret_cast<int32_t*>(sv + p.o_py) + (int64_t)rho * C;
-    int32_t* iy = reinterpret_cast<int32_t*>(sv + p.o_iy) + (int64_t)rho * C;
     const void* Btr = static_cast<const char*>(Bt) + (size_t)rho * c.n_b * d * p.esize;
     RECE_PHASE(RECE_PHASE_PROJECT, launch_project_argmax(p.bf16, d, Y, C, Btr, c.n_b, bnorm + rho, p.beta_coef, by, nullptr,
                                    rho == 0 ? reinterpret_cast<uint32_t*>(ymax) : nullptr, undy, und_n + 2 * rho + 1,
                                    counters, st),
              "bucket items");
-    RECE_PHASE(RECE_PHASE_SORT, launch_counting_sort(by, nullptr, C, 0, p.nbits_b, sc + p.o_sorty, py, iy, st),
+    RECE_PHASE(RECE_PHASE_SORT, launch_counting_sort(by, nullptr, C, 0, p.nbits_b, sc + p.o_sorty, py, nullptr, st),
                "sort items");
-    char* ys = sv + p.o_ys + (size_t)rho * C * d * p.esize;
-    int32_t* cyp = reinterpret_cast<int32_t*>(sv + p.o_cyp) + (int64_t)(rho * (rho - 1) / 2) * C;
-    RECE_PHASE(RECE_PHASE_SORT, launch_gather_rows(Y, py, C, d * p.esize, ys, st), "sorted items");
-    for (int r2 = 0; r2 < rho; ++r2)   // the backward's earlier-round tests read these
-      RECE_PHASE(RECE_PHASE_SORT,
-                 launch_prev_chunks(py, reinterpret_cast<const int32_t*>(sv + p.o_iy) + (int64_t)r2 * C, C, c.n_c,
-                                    cyp + (int64_t)r2 * C, st),
-                 "earlier-round chunks");
+    RECE_PHASE(RECE_PHASE_SORT, launch_gather_rows(Y, py, C, d * p.esize, ys_of(rho), st), "sorted items");
     if (rho == 0) {
       RECE_HIP(hipEventRecord(p.side.fork[0], side), "item chain done");
       continue;
     }
     int32_t* bx = reinterpret_cast<int32_t*>(sv + p.o_bx) + (int64_t)rho * s;
     int32_t* px = reinterpret_cast<int32_t*>(sv + p.o_px) + (int64_t)rho * s;
-    int32_t* ix = reinterpret_cast<int32_t*>(sv + p.o_ix) + (int64_t)rho * s;
     RECE_PHASE(RECE_PHASE_PROJECT, launch_project_argmax(p.bf16, d, X, s, Btr, c.n_b, bnorm + rho, p.beta_coef,
                                    bx, nullptr, nullptr, undy, und_n + 2 * rho, counters, st),
                "bucket positions");
-    RECE_PHASE(RECE_PHASE_SORT, launch_counting_sort(bx, nullptr, s, 0, p.nbits_b, sc + p.o_sorty, px, ix, st),
+    RECE_PHASE(RECE_PHASE_SORT, launch_counting_sort(bx, nullptr, s, 0, p.nbits_b, sc + p.o_sorty, px, nullptr, st),
                "sort positions");
-    char* xs = sv + p.o_xs + (size_t)rho * s * d * p.esize;
-    RECE_PHASE(RECE_PHASE_SORT, launch_gather_rows(X, px, s, d * p.esize, xs, st), "sorted positions");
+    RECE_PHASE(RECE_PHASE_SORT, launch_gather_rows(X, px, s, d * p.esize, xs_of(rho), st), "sorted positions");
     if (rho == 1) RECE_HIP(hipStreamWaitEvent(side, p.side.fork[c.rounds + 1], 0), "position norms");
     const SelectArgs a = select_args(rho);
     RECE_PHASE(RECE_PHASE_SELECT, launch_select(p.bf16, d, p.waves_sel, a, st), "chunk logits and top-k");
@@ -789,21 +699,6 @@ rece_status rece_forward(rece_plan_t plan, void* stream, const void* X, const vo
   {
     const SelectArgs a = select_args(0);
     RECE_PHASE(RECE_PHASE_SELECT, launch_select(p.bf16, d, p.waves_sel, a, st), "chunk logits and top-k");
-  }
-  {   // positions sorted by positive id (LSD counting sort), for the positive term of dY; it
-      // needs only pos, and this stream would otherwise wait for the second stream here
-    int32_t* bufs[2] = {reinterpret_cast<int32_t*>(sc + p.o_pp0), reinterpret_cast<int32_t*>(sc + p.o_pp1)};
-    int32_t* final_out = reinterpret_cast<int32_t*>(sv + p.o_psort);
-    const int total_bits = std::max(1, bits_for(C));
-    const int db = sort_digit_bits(s);
-    const int32_t* sorted = nullptr;
-    for (int pass = 0, shift = 0; shift < total_bits; ++pass, shift += db) {
-      const int nb = std::min(db, total_bits - shift);
-      int32_t* outp = shift + db >= total_bits ? final_out : bufs[pass & 1];
-      RECE_PHASE(RECE_PHASE_SORT, launch_counting_sort(pos, sorted, s, shift, nb, sc + p.o_sort, outp, nullptr, st),
-                 "sort positives");
-      sorted = outp;
-    }
   }
   RECE_HIP(hipStreamWaitEvent(st, p.side.fork[c.rounds + 2], 0), "join the side stream");
   for (int rho = 1; rho < c.rounds && c.k > 0; ++rho) {
@@ -854,74 +749,46 @@ rece_status rece_backward(rece_plan_t plan, void* stream, const void* X, const v
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const char* sv = static_cast<const char*>(saved);
   char* sc = static_cast<char*>(scratch);
-  const int64_t s = c.s, C = c.C;
-  const int d = c.d;
-  if (c.variant == RECE_VARIANT_SCE) return sce_backward(p, st, X, Y, pos, dloss, dloss_pp, sc, sv, dX, dY);
+  const int rounds = c.variant == RECE_VARIANT_SCE ? 1 : c.rounds;
   std::lock_guard<std::mutex> side_lock(p.side.mu);
 
   BwdArgs b{};
-  b.sce = 0;
-  b.nwin = 3;
-  b.npos = s;
   b.X = X;
   b.Y = Y;
   b.pos = pos;
-  b.inv_x = reinterpret_cast<const int32_t*>(sv + p.o_ix);
-  b.inv_y = reinterpret_cast<const int32_t*>(sv + p.o_iy);
-  b.s = s;
-  b.C = C;
-  b.n_c = c.n_c;
-  b.tiles_per_chunk = p.tpc_bwd;
-  b.thr_e = reinterpret_cast<const double*>(sv + p.o_te);
-  b.thr_id = reinterpret_cast<const int32_t*>(sv + p.o_tid);
-  b.thr_lo = reinterpret_cast<const float*>(sv + p.o_tlo);
-  b.thr_hi = reinterpret_cast<const float*>(sv + p.o_thi);
+  b.s = c.s;
+  b.C = c.C;
+  b.rounds = rounds;
+  b.k = c.k;
+  b.negs = reinterpret_cast<const int32_t*>(sv + p.o_negs);
   b.lse = reinterpret_cast<const float*>(sv + p.o_lse);
   b.lpos = reinterpret_cast<const float*>(sv + p.o_lpos);
   b.dloss = dloss;
   b.dloss_pp = dloss_pp;
   b.dX = dX;
   b.dY = dY;
-  b.counters = reinterpret_cast<uint32_t*>(const_cast<char*>(sv) + p.o_cnt);
-  b.rounds = c.rounds;
-  b.negs = reinterpret_cast<const int32_t*>(sv + p.o_negs);
-  b.k = c.k;
-  PosRec* recs = reinterpret_cast<PosRec*>(sc + p.o_rec);
-  PrevRow* prevs = reinterpret_cast<PrevRow*>(sc + p.o_prev);
-  // dY (rounds in order) runs on the side stream, each round after its records;
-  // dX (from the kept lists) and the positive sums stay on the caller's stream;
-  // the positive term of dY joins them
-  const rece_status ss = ensure_side(p, c.rounds);
+  // dY (the sort of the pairs by item, then the per-item sums) runs on the side
+  // stream while dX runs on the caller's stream; the caller's stream then waits.
+  const rece_status ss = ensure_side(p, 1);
   if (ss != RECE_OK) return ss;
   hipStream_t side = p.side.s;
-  for (int rho = 0; rho < c.rounds; ++rho) {
-    b.rho = rho;
-    b.perm_x = reinterpret_cast<const int32_t*>(sv + p.o_px) + (int64_t)rho * s;
-    b.perm_y = reinterpret_cast<const int32_t*>(sv + p.o_py) + (int64_t)rho * C;
-    b.Xs = sv + p.o_xs + (size_t)rho * s * d * p.esize;
-    b.Ys = sv + p.o_ys + (size_t)rho * C * d * p.esize;
-    b.cyp = reinterpret_cast<const int32_t*>(sv + p.o_cyp) + (int64_t)(rho * (rho - 1) / 2) * C;
-    b.rec = recs + (int64_t)rho * s;
-    b.prev = prevs + (int64_t)(rho * (rho - 1) / 2) * s;
-    RECE_PHASE(RECE_PHASE_OTHER, launch_bwd_records(b, b.perm_x, rho, recs + (int64_t)rho * s,
-                                                    prevs + (int64_t)(rho * (rho - 1) / 2) * s, st),
-               "backward records");
-    RECE_HIP(hipEventRecord(p.side.fork[rho], st), "fork");
-    RECE_HIP(hipStreamWaitEvent(side, p.side.fork[rho], 0), "fork");
-    {
-      hipStream_t st = side;
-      RECE_PHASE(RECE_PHASE_BWD_DY, launch_bwd_items(p.bf16, d, 4, b, p.itiles, st), "dY");
-    }
+  RECE_HIP(hipEventRecord(p.side.fork[0], st), "fork");
+  RECE_HIP(hipStreamWaitEvent(side, p.side.fork[0], 0), "fork");
+  {
+    hipStream_t st = side;
+    const int32_t *K = nullptr, *V = nullptr;
+    const uint32_t* ntot = nullptr;
+    RECE_PHASE(RECE_PHASE_BWD_SORT,
+               launch_pair_sort(p.pg, b.negs, (int64_t)rounds * c.s * c.k, c.k, c.s, pos, c.C, sc + p.o_psc,
+                                reinterpret_cast<int32_t*>(sc + p.o_pk0), reinterpret_cast<int32_t*>(sc + p.o_pv0),
+                                reinterpret_cast<int32_t*>(sc + p.o_pk1), reinterpret_cast<int32_t*>(sc + p.o_pv1), &K,
+                                &V, &ntot, st),
+               "sort pairs by item");
+    RECE_PHASE(RECE_PHASE_BWD_DY, launch_dy(p.bf16, c.d, b, K, V, ntot, p.npairs, sc + p.o_dya, st), "dY");
   }
-  RECE_PHASE(RECE_PHASE_BWD_DX, launch_dx_lists(p.bf16, d, b, st), "dX");
-  // positives: the per-piece sums over the positions the forward pass sorted by
-  // positive id (overlapping the side stream), then, once it is joined, the sums into dY
-  const int32_t* sorted = reinterpret_cast<const int32_t*>(sv + p.o_psort);
-  float* parea = reinterpret_cast<float*>(sc + p.o_ppart);
-  RECE_PHASE(RECE_PHASE_BWD_POS, launch_pos_pieces(p.bf16, d, b, sorted, parea, st), "positive dY");
+  RECE_PHASE(RECE_PHASE_BWD_DX, launch_dx_lists(p.bf16, c.d, b, st), "dX");
   RECE_HIP(hipEventRecord(p.side.join, side), "join");
   RECE_HIP(hipStreamWaitEvent(st, p.side.join, 0), "join");
-  RECE_PHASE(RECE_PHASE_BWD_POS, launch_pos_combine(d, s, dY, parea, st), "positive dY");
   return RECE_OK;
 }
 
@@ -929,6 +796,7 @@ rece_status rece_export_bytes(rece_plan_t plan, int stage, size_t* bytes) {
   if (!plan || !bytes) return fail(RECE_ERR_INVALID_ARGUMENT, "NULL argument");
   const rece_config& c = plan->cfg;
   const bool sce = c.variant == RECE_VARIANT_SCE;
+  const int rounds = sce ? 1 : c.rounds;
   switch (stage) {
     case RECE_STAGE_BUCKET_X:
     case RECE_STAGE_PERM_X:
@@ -952,7 +820,10 @@ rece_status rece_export_bytes(rece_plan_t plan, int stage, size_t* bytes) {
       *bytes = (size_t)c.s * 8;
       break;
     case RECE_STAGE_NEG_IDS:
-      *bytes = (plan->o_negs && (c.flags & RECE_FLAG_KEEP_STAGES)) ? (size_t)c.s * std::max(c.k, 1) * 4 : 0;
+      *bytes = (size_t)c.s * std::max(c.k, 1) * 4;
+      break;
+    case RECE_STAGE_UNION_IDS:
+      *bytes = (size_t)c.s * rounds * std::max(c.k, 1) * 4;
       break;
     case RECE_STAGE_COUNTERS:
       *bytes = NUM_COUNTERS * 4;
@@ -971,10 +842,11 @@ rece_status rece_export(rece_plan_t plan, void* stream, const void* saved, int s
   size_t bytes = 0;
   const rece_status bs = rece_export_bytes(plan, stage, &bytes);
   if (bs != RECE_OK) return bs;
-  if (bytes == 0)
-    return fail(RECE_ERR_INVALID_ARGUMENT, "stage not kept by this plan (variant, or no RECE_FLAG_KEEP_STAGES)");
+  if (bytes == 0) return fail(RECE_ERR_INVALID_ARGUMENT, "stage not kept by this plan's variant");
   const char* sv = static_cast<const char*>(saved);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int64_t s = c.s, C = c.C;
+  const int kk = std::max(c.k, 1);
   size_t off = 0;
   switch (stage) {
     case RECE_STAGE_BUCKET_X: off = p.o_bx + (size_t)round * s * 4; break;
@@ -983,7 +855,8 @@ rece_status rece_export(rece_plan_t plan, void* stream, const void* saved, int s
     case RECE_STAGE_PERM_Y: off = p.o_py + (size_t)round * C * 4; break;
     case RECE_STAGE_THRESH_ID: off = p.o_tid + (size_t)round * s * 4; break;
     case RECE_STAGE_THRESH_LOGIT: off = p.o_te + (size_t)round * s * 8; break;
-    case RECE_STAGE_NEG_IDS: off = p.o_negs + (size_t)round * s * std::max(c.k, 1) * 4; break;
+    case RECE_STAGE_NEG_IDS: off = p.o_negs + (size_t)round * s * kk * 4; break;
+    case RECE_STAGE_UNION_IDS: off = p.o_negs; break;
     case RECE_STAGE_LSE: off = p.o_lse; break;
     case RECE_STAGE_COUNTERS: off = p.o_cnt; break;
     case RECE_STAGE_SCE_ROWS: off = p.o_R; break;
@@ -991,13 +864,27 @@ rece_status rece_export(rece_plan_t plan, void* stream, const void* saved, int s
     default: return fail(RECE_ERR_INVALID_ARGUMENT, "unknown stage");
   }
   if (stage == RECE_STAGE_NEG_IDS) {   // ids without the earlier-round mark
+    if (c.k == 0) {
+      RECE_HIP(launch_fill_u32(static_cast<uint32_t*>(dst), 0xFFFFFFFFu, (int64_t)(bytes / 4), st), "export");
+      return RECE_OK;
+    }
     RECE_HIP(launch_strip_mark(reinterpret_cast<const int32_t*>(sv + off), (int64_t)(bytes / 4),
-                               static_cast<int32_t*>(dst), reinterpret_cast<hipStream_t>(stream)),
+                               static_cast<int32_t*>(dst), st),
              "export");
     return RECE_OK;
   }
-  RECE_HIP(hipMemcpyAsync(dst, sv + off, bytes, hipMemcpyDeviceToDevice, reinterpret_cast<hipStream_t>(stream)),
-           "export");
+  if (stage == RECE_STAGE_UNION_IDS) {
+    const int rounds = c.variant == RECE_VARIANT_SCE ? 1 : c.rounds;
+    if (c.k == 0) {
+      RECE_HIP(launch_fill_u32(static_cast<uint32_t*>(dst), 0xFFFFFFFFu, (int64_t)(bytes / 4), st), "export");
+      return RECE_OK;
+    }
+    RECE_HIP(launch_union_ids(reinterpret_cast<const int32_t*>(sv + off), s, c.k, rounds, static_cast<int32_t*>(dst),
+                              st),
+             "export");
+    return RECE_OK;
+  }
+  RECE_HIP(hipMemcpyAsync(dst, sv + off, bytes, hipMemcpyDeviceToDevice, st), "export");
   return RECE_OK;
 }
 
@@ -1029,6 +916,6 @@ const char* rece_status_string(rece_status status) {
 
 const char* rece_last_error(void) { return g_last_error.c_str(); }
 
-const char* rece_version(void) { return "librece 0.1 (gfx950)"; }
+const char* rece_version(void) { return "librece 0.2 (gfx950)"; }
 
 }  // extern "C"

@@ -29,12 +29,9 @@ struct SelectArgs {
   const void* Y;
   const void* Xs;             // round rho: X rows in sorted order
   const void* Ys;             // round rho: Y rows in sorted order
-  const int32_t* cyp;         // round rho: [rho][C] chunk of item perm_y[q] in rounds 0..rho-1
   const int32_t* pos;
   const int32_t* perm_x;      // round rho
   const int32_t* perm_y;      // round rho
-  const int32_t* inv_x;       // [rounds][s]
-  const int32_t* inv_y;       // [rounds][C]
   int64_t s, C;
   int n_c, k, cap, rho, rounds;
   int selall;                 // 1: every window has at most k candidates; keep all
@@ -52,7 +49,9 @@ struct SelectArgs {
   int32_t* negs;              // [rounds][s][k] kept ids (bit 31: kept in an earlier round; -1 pad) or nullptr
   float* negl;                // [s][k] float32 logits of this round's negs (row = position or slot), or nullptr
   int slot_out;               // 1: outputs indexed by sorted slot, not by position id
-  int nwin;                   // window chunks: 3 (c-1, c, c+1) or 1 (c only)
+  int n_ec;                   // window: chunks c - n_ec .. c + n_ec
+  int wrap;                   // 1: chunk indices modulo n_c (cyclic); 0: clipped to [0, n_c)
+  int wide;                   // 1: 32-bit histogram counts (a window may exceed 65535 items)
   uint32_t* counters;
 };
 
@@ -86,46 +85,31 @@ struct DedupArgs {
   int hash_bits;              // log2 of the LDS hash slots per wave; 0: linear scan of the earlier lists
 };
 
+// Backward pass (both variants): everything is read from the kept lists.
 struct BwdArgs {
   const void* X;
   const void* Y;
-  const void* Xs;             // round rho: X rows in sorted order
-  const void* Ys;             // round rho: Y rows in sorted order
-  const int32_t* cyp;         // round rho: [rho][C] chunk of item perm_y[q] in earlier rounds
-  const PosRec* rec;          // round rho: [s] per sorted position
-  const PrevRow* prev;        // round rho: [rho][s] per sorted position
-  int rounds;
   const int32_t* pos;
-  const int32_t* perm_x;      // round rho
-  const int32_t* perm_y;      // round rho
-  const int32_t* inv_x;       // [rounds][s]
-  const int32_t* inv_y;       // [rounds][C]
   int64_t s, C;
-  int n_c, rho;
-  int tiles_per_chunk;
-  const double* thr_e;
-  const int32_t* thr_id;
-  const float* thr_lo;
-  const float* thr_hi;
-  const float* lse;
-  const float* lpos;
+  int rounds, k;
+  const int32_t* negs;        // [rounds][s][k] kept ids (-1 pad; bit 31: kept in an earlier round)
+  const float* lse;           // [s]
+  const float* lpos;          // [s]
   const float* dloss;         // [1]
   const float* dloss_pp;      // [s] or nullptr
-  float* dX;                  // [s][d]   (bucket variant: [slots][d] partial rows)
-  float* dY;                  // [C][d]   (bucket variant: [item slots][d] partial rows)
-  uint32_t* counters;
-  // bucket variant: slots are (bucket, position) / (bucket, item) pairs, chunk = bucket
-  int sce;                    // 1: bucket variant
-  int nwin;                   // window chunks: 3 or 1
-  int64_t npos;               // positions (scale of dloss)
-  int b_x;                    // positions per bucket
-  const int32_t* sce_sorted;  // [slots] slots grouped by position, in bucket order
-  const int32_t* sce_pstart;  // [s] first index of each position's group in sce_sorted
-  const int32_t* sce_inv;     // [slots] index of each slot in sce_sorted
-  const uint32_t* qbits;      // [n_b][qwords] bit j: item j taken by the bucket
-  int64_t qwords;
-  const int32_t* negs;        // [rounds][s][k] kept ids of the forward pass (dX from the lists)
-  int k;
+  float* dX;                  // [s][d]
+  float* dY;                  // [C][d]
+};
+
+// Stable LSD counting sort of the (item, position) records of the backward pass:
+// npass digit passes over keys below C, segments of seg_len records.
+struct PairSortGeom {
+  int64_t E;                  // records: rounds * s * k list entries + s positives
+  int npass;
+  int shift[4], bits[4];
+  int64_t seg_len, nseg;
+  int64_t count_words;        // count matrix of the widest pass, plus its total
+  size_t scratch_bytes;       // counters, count matrix, scan block sums
 };
 
 // Launchers (defined in the .hip files).  All enqueue on `st`.
@@ -147,35 +131,38 @@ int sort_digit_bits(int64_t n);
 hipError_t launch_counting_sort(const int32_t* keys, const int32_t* in_perm, int64_t n, int shift, int nbits,
                                 void* scratch, int32_t* perm_out, int32_t* inv_out, hipStream_t st);
 hipError_t launch_select(bool is_bf16, int d, int waves, const SelectArgs& a, hipStream_t st);
-size_t select_lds_bytes(bool is_bf16, int d, int waves, int cap);
+size_t select_lds_bytes(bool is_bf16, int d, int waves, bool wide);
 int ce_blocks(int64_t s);
 hipError_t launch_ce(bool is_bf16, int d, const CeArgs& a, float* loss, hipStream_t st);
 // log2 of the per-wave hash slots k_round_dedup uses for rounds earlier lists of k
 // ids (0: too many for LDS, the kernel scans the lists instead).
 int dedup_hash_bits(int rounds, int k);
 hipError_t launch_round_dedup(const DedupArgs& a, hipStream_t st);
-hipError_t launch_bwd_rows(bool is_bf16, int d, int waves, const BwdArgs& a, hipStream_t st);
 // dX of every position from the kept lists of all rounds plus the positive term
 // (writes all s rows of dX).
 hipError_t launch_dx_lists(bool is_bf16, int d, const BwdArgs& a, hipStream_t st);
 // dst[0..n) = src[0..n) with bit 31 cleared, -1 kept (exported kept lists).
 hipError_t launch_strip_mark(const int32_t* src, int64_t n, int32_t* dst, hipStream_t st);
-hipError_t launch_bwd_items(bool is_bf16, int d, int waves, const BwdArgs& a, int item_tiles_per_chunk,
+// dst[s][rounds * k]: per position the ids no earlier round kept, in (round, list) order, -1 padded.
+hipError_t launch_union_ids(const int32_t* negs, int64_t s, int k, int rounds, int32_t* dst, hipStream_t st);
+// Exclusive scan of a[0..n) in place; bsum holds ceil(n / 4096) + 64 words.
+hipError_t launch_exclusive_scan(uint32_t* a, int64_t n, uint32_t* bsum, hipStream_t st);
+PairSortGeom pair_sort_geom(int64_t E, int64_t C);
+// Records of the lists (nl = rounds * s * k entries) and the s positives sorted by item
+// (stable); *kout / *vout point at the sorted keys / values (kA/vA or kB/vB) and *nout
+// at the device count of records (entries < 0 or >= C are dropped).  scratch holds
+// geom.scratch_bytes.
+hipError_t launch_pair_sort(const PairSortGeom& g, const int32_t* negs, int64_t nl, int k, int64_t s,
+                            const int32_t* pos, int64_t C, void* scratch, int32_t* kA, int32_t* vA, int32_t* kB,
+                            int32_t* vB, const int32_t** kout, const int32_t** vout, const uint32_t** nout,
                             hipStream_t st);
-size_t pos_partial_bytes(int64_t s, int d);
+// Work area of launch_dy for at most E sorted records.
+size_t dy_area_bytes(int64_t E, int d);
+// Every row of dY from the sorted records (K, V, *ntot of them); E bounds *ntot.
+hipError_t launch_dy(bool is_bf16, int d, const BwdArgs& a, const int32_t* K, const int32_t* V, const uint32_t* ntot,
+                     int64_t E, void* area, hipStream_t st);
 hipError_t launch_gather_rows(const void* src, const int32_t* perm, int64_t n, int row_bytes, void* dst,
                               hipStream_t st);
-hipError_t launch_prev_chunks(const int32_t* perm_y, const int32_t* inv_y2, int64_t C, int n_c, int32_t* out,
-                              hipStream_t st);
-hipError_t launch_bwd_records(const BwdArgs& a, const int32_t* perm_x, int rho, PosRec* rec, PrevRow* prev,
-                              hipStream_t st);
-// Positive term of dY: the pieces pass reads X and the sorted positions and writes
-// only the work area; the combine pass adds the work area into dY.
-hipError_t launch_pos_pieces(bool is_bf16, int d, const BwdArgs& a, const int32_t* pos_perm, float* area,
-                             hipStream_t st);
-hipError_t launch_pos_combine(int d, int64_t s, float* dY, float* area, hipStream_t st);
-hipError_t launch_pos_dy(bool is_bf16, int d, const BwdArgs& a, const int32_t* pos_perm, float* area,
-                         hipStream_t st);
 
 // Bucket (SCE) variant.
 struct ColSelectArgs {
@@ -194,7 +181,6 @@ struct ColSelectArgs {
 hipError_t launch_project_scores(bool is_bf16, int d, const void* V, int64_t n, const void* Bt, int n_b, float* PT,
                                  float* norms, uint32_t* norm_max_bits, hipStream_t st);
 hipError_t launch_col_select(bool is_bf16, int d, const ColSelectArgs& a, hipStream_t st);
-hipError_t launch_mark_items(const int32_t* Q, int n_b, int b_y, int64_t qwords, uint32_t* qbits, hipStream_t st);
 hipError_t launch_group_bounds(const int32_t* keys, const int32_t* sorted, int64_t n, int32_t* start, int32_t* end,
                                hipStream_t st);
 struct MergeArgs {
@@ -224,10 +210,5 @@ struct MergeArgs {
 };
 size_t merge_lds_bytes(int k);
 hipError_t launch_sce_merge(bool is_bf16, int d, const MergeArgs& a, hipStream_t st);
-hipError_t launch_sce_combine_rows(int d, const float* part, const int32_t* sorted, const int32_t* start,
-                                   const int32_t* end, int64_t n, const BwdArgs& b, bool is_bf16, float* out,
-                                   hipStream_t st);
-hipError_t launch_sce_combine_items(int d, const float* part, const int32_t* sorted, const int32_t* start,
-                                    const int32_t* end, int64_t n, float* out, hipStream_t st);
 
 }  // namespace rece

@@ -171,45 +171,50 @@ struct RecCopy {
   }
 };
 
-// Up to three chunks (chunk c first, then c-1 and c+1, cyclic and distinct) of N
-// sorted slots cut into n_c chunks, walked in tiles of TI slots.  Plain scalar
-// members: an indexed array here would be placed in scratch memory.
+// The window of chunk c: chunks c - n_ec .. c + n_ec of N sorted slots cut into
+// n_c chunks (RECE page, Algorithm 1, the adjacent-chunk line, with n_ec
+// neighbours on each side as in the method paragraph of Section 3).  Cyclic
+// (wrap = 1): chunk indices modulo n_c, taken as a set, so 2 n_ec + 1 >= n_c gives
+// all N slots.  Clipped (wrap = 0): only chunks inside [0, n_c).  Consecutive
+// chunks are consecutive slots, so every window is at most two slot ranges
+// (a cyclic window that passes an end of the order is split there), walked in
+// tiles of TI slots.  Plain scalar members: an indexed array here would be
+// placed in scratch memory.
 struct Ranges {
-  int64_t s0, s1, s2, e0, e1, e2;   // slot ranges [s_q, e_q)
-  int c1, c2, c3;                    // cumulative tile counts
-  // nwin = 3: chunks c, c-1, c+1 (distinct ones); nwin = 1: chunk c only
-  __device__ __forceinline__ void init(int c, int n_c, int64_t N, int TI, int nwin) {
-    const int cm = (c + n_c - 1) % n_c, cp = (c + 1) % n_c;
-    s0 = chunk_start(c, N, n_c);
-    e0 = chunk_start(c + 1, N, n_c);
-    s1 = e1 = s2 = e2 = 0;
-    if (nwin == 1) n_c = 1;   // no neighbours
-    if (n_c >= 2) {
-      s1 = chunk_start(cm, N, n_c);
-      e1 = chunk_start(cm + 1, N, n_c);
-    }
-    if (n_c >= 3) {
-      s2 = chunk_start(cp, N, n_c);
-      e2 = chunk_start(cp + 1, N, n_c);
+  int64_t s0, s1, e0, e1;   // slot ranges [s_q, e_q); the second may be empty
+  int c1, c2;               // cumulative tile counts
+  __device__ __forceinline__ void init(int c, int n_c, int64_t N, int TI, int n_ec, int wrap) {
+    const int lo = c - n_ec, hi = c + n_ec;   // chunks lo .. hi (before the modulo or the clip)
+    s1 = e1 = 0;
+    if (!wrap) {
+      s0 = chunk_start(lo < 0 ? 0 : lo, N, n_c);
+      e0 = chunk_start(hi + 1 > n_c ? n_c : hi + 1, N, n_c);
+    } else if (2 * n_ec + 1 >= n_c) {
+      s0 = 0;
+      e0 = N;
+    } else if (lo < 0) {
+      s0 = chunk_start(lo + n_c, N, n_c);
+      e0 = N;
+      e1 = chunk_start(hi + 1, N, n_c);
+    } else if (hi >= n_c) {
+      s0 = chunk_start(lo, N, n_c);
+      e0 = N;
+      e1 = chunk_start(hi + 1 - n_c, N, n_c);
+    } else {
+      s0 = chunk_start(lo, N, n_c);
+      e0 = chunk_start(hi + 1, N, n_c);
     }
     c1 = (int)((e0 - s0 + TI - 1) / TI);
     c2 = c1 + (int)((e1 - s1 + TI - 1) / TI);
-    c3 = c2 + (int)((e2 - s2 + TI - 1) / TI);
   }
-  __device__ __forceinline__ int ntiles() const { return c3; }
+  __device__ __forceinline__ int ntiles() const { return c2; }
 };
 
 // Slot range [q0, q1_end) of tile t (tile rows are q0 .. q0 + TI - 1, clipped at q1_end).
 __device__ __forceinline__ int64_t range_tile_start(Ranges r, int t, int TI) {
-  const bool in0 = t < r.c1, in1 = t < r.c2;
-  const int64_t st = in0 ? r.s0 : (in1 ? r.s1 : r.s2);
-  const int base = in0 ? 0 : (in1 ? r.c1 : r.c2);
-  return st + (int64_t)(t - base) * TI;
+  return t < r.c1 ? r.s0 + (int64_t)t * TI : r.s1 + (int64_t)(t - r.c1) * TI;
 }
-__device__ __forceinline__ int64_t range_tile_end(Ranges r, int t) {
-  const bool in0 = t < r.c1, in1 = t < r.c2;
-  return in0 ? r.e0 : (in1 ? r.e1 : r.e2);
-}
+__device__ __forceinline__ int64_t range_tile_end(Ranges r, int t) { return t < r.c1 ? r.e0 : r.e1; }
 
 // Issue the copies of window tile t (rows from `rows_src`, then 64 ids from
 // `ids_src`, then `nmaps` chunk maps of C ints from `maps_src`) into ring slot t % RING.

@@ -9,10 +9,11 @@
  *       vectors b of the signed scalar product b.v (ties: lowest index);
  *     positions and items are stably sorted by bucket and cut into n_c equal
  *       chunks (chunk c holds sorted slots p with c*N/n_c <= p < (c+1)*N/n_c);
- *     a position in X-chunk c is scored against the items of chunks c-1, c, c+1
- *       (modulo n_c), its own positive excluded, and keeps the k largest logits
- *       (order: logit descending, item id ascending);
- *   the kept pairs of all rounds form a set (the page's "minus ln(count)" rule
+ *     a position in X-chunk c is scored against the items of chunks
+ *       c-n_ec .. c+n_ec (modulo n_c, or clipped to [0, n_c)), its own positive
+ *       excluded, and keeps the k largest logits (order: logit descending, item
+ *       id ascending);
+ *   the kept pairs of all rounds form a set (the page's minus-ln(count) rule
  *   makes a pair kept in several rounds count once);
  *   loss_i = logsumexp({x_i.y_pos_i} u {x_i.y_j : j kept}) - x_i.y_pos_i,
  *   loss = mean over the s positions.
@@ -65,69 +66,98 @@ typedef enum { RECE_VARIANT_RECE = 0, RECE_VARIANT_SCE = 1 } rece_variant;
 
 /* flags */
 #define RECE_FLAG_VALIDATE_IDS 1u  /* device check that 0 <= pos[i] < C (error word) */
-#define RECE_FLAG_KEEP_STAGES 2u   /* keep per-round kept-negative lists for rece_export */
+#define RECE_FLAG_KEEP_STAGES 2u   /* accepted, no effect: the kept lists are always kept
+                                      (the backward pass reads them) */
 
+/* Loss configuration.  RECE page, Algorithm 1 (input line: positions, items, n_b,
+ * n_c) and the method paragraph of Section 3 (rounds r, neighbouring chunks n_ec,
+ * the duplicate rule); k, the negatives kept per position, is this library's
+ * top-k of the window (the paragraph's "logits with the largest absolute
+ * gradient").  SCE page, abstract, for the bucket variant (b_x, b_y). */
 typedef struct {
   int64_t s;        /* positions (batch x sequence length collapsed), >= 1 */
   int64_t C;        /* catalogue size, >= 2 */
   int32_t d;        /* embedding dimension: 32, 64, 128 or 256 */
   int32_t n_b;      /* random vectors (buckets) per round, 1..4096 */
   int32_t n_c;      /* RECE chunks, 1..min(s, C); ignored by SCE */
+  int32_t n_ec;     /* RECE neighbouring chunks on each side of a window, 0..2^20
+                       (1: chunks c-1, c, c+1 as in Algorithm 1); ignored by SCE */
   int32_t k;        /* negatives kept per position (RECE: per round), 0..C-1 */
   int32_t rounds;   /* RECE rounds r, 1..8; SCE: must be 1 */
   int32_t b_x;      /* SCE: positions per bucket, 1..s; RECE: 0 */
   int32_t b_y;      /* SCE: items per bucket, 1..C; RECE: 0 */
   int32_t dtype;    /* rece_dtype of X, Y and B (float32 or bfloat16 bits) */
   int32_t variant;  /* rece_variant */
+  int32_t window_wrap; /* RECE: 1 = chunk indices taken modulo n_c (cyclic window),
+                          0 = clipped to [0, n_c) (edge chunks see fewer items);
+                          ignored by SCE */
   uint32_t flags;   /* RECE_FLAG_* */
 } rece_config;
 
 typedef struct rece_plan_s* rece_plan_t;
 
 /* Validate `cfg` and build a host-side plan (no GPU work, no device memory).
- * On error *out is NULL.  A plan may be used from several threads (profiling
- * aside, see rece_profile_enable); concurrent calls need their own scratch and
- * saved buffers.  At its first forward or backward call a plan creates one
- * extra HIP stream (default priority) and a few events on the current device,
- * and uses that device from then on: the item-side steps of the forward, the
- * position-side steps and chunk kernels of rounds after the first, and the dY
- * chain of the backward run there, ordered with `stream` by events, so every
- * result is complete in `stream` order when the call's work is.  Calls that
- * use this stream take a per-plan lock while they enqueue.  rece_plan_destroy
- * releases the stream and events (the caller makes sure no call is still
- * running on the device). */
+ * The plan fixes the workspace layout and the launch shapes of Algorithm 1's
+ * steps for this configuration (RECE page, Section 3).  Returns
+ * RECE_ERR_INVALID_ARGUMENT for values outside the ranges above and
+ * RECE_ERR_UNSUPPORTED for valid values this build does not handle (d, sizes
+ * beyond int32 indexing); on error *out is NULL.  A plan may be used from
+ * several threads (profiling aside, see rece_profile_enable); concurrent calls
+ * need their own scratch and saved buffers.  At its first forward or backward
+ * call a plan creates one extra HIP stream (default priority) and a few events
+ * on the current device, and uses that device from then on: the item-side steps
+ * of the forward, the position-side steps and chunk kernels of rounds after the
+ * first, and the dY chain of the backward run there, ordered with `stream` by
+ * events, so every result is complete in `stream` order when the call's work
+ * is.  Calls that use this stream take a per-plan lock while they enqueue.
+ * rece_plan_destroy releases the stream and events (the caller makes sure no
+ * call is still running on the device). */
 rece_status rece_plan(const rece_config* cfg, rece_plan_t* out);
 rece_status rece_plan_destroy(rece_plan_t plan);
 
-/* Bytes of the two caller-provided device buffers:
- *   scratch: temporaries of one call; may be reused freely between calls;
+/* Bytes of the two caller-provided device buffers (owned by the caller):
+ *   scratch: temporaries of one call (sorted copies, histograms, the
+ *            backward's sorted pairs); may be reused freely between calls;
  *   saved:   written by rece_forward, read by rece_backward / rece_export /
- *            rece_check; must stay untouched in between. */
+ *            rece_check; must stay untouched in between.
+ * Neither holds an [s, C] logit block (RECE page, Section 3: the full logit
+ * tensor is what the method avoids). */
 rece_status rece_workspace_bytes(rece_plan_t plan, size_t* scratch_bytes, size_t* saved_bytes);
 
-/* Forward pass.
+/* Forward pass: RECE page, Section 3, Algorithm 1 (every line, repeated over the
+ * rounds, with the duplicate rule of the method paragraph); SCE page, abstract,
+ * for the bucket variant.
  *   X    [s][d]  dtype      hidden states, one row per position
  *   Y    [C][d]  dtype      item embeddings
  *   pos  [s]     int32      positive item id of each position, 0 <= pos < C
  *   B    RECE: [rounds][d][n_b] dtype, column b of slice rho is random vector b
- *        of round rho;  SCE: [d][n_b]
- *   loss [1]     float32    out: mean loss
+ *        of round rho (Algorithm 1's randn line, drawn by the caller);
+ *        SCE: [d][n_b]
+ *   loss [1]     float32    out: mean loss (Algorithm 1, last line)
  *   loss_pp [s]  float32    out: per-position loss, or NULL
- * Uses (overwrites) scratch and saved. */
+ * Uses (overwrites) scratch and saved.  Errors: NULL or misaligned pointers ->
+ * RECE_ERR_INVALID_ARGUMENT, a failed launch -> RECE_ERR_HIP; ids outside [0, C)
+ * are clamped and, with RECE_FLAG_VALIDATE_IDS, reported by rece_check. */
 rece_status rece_forward(rece_plan_t plan, void* stream, const void* X, const void* Y,
                          const int32_t* pos, const void* B, void* scratch, void* saved,
                          float* loss, float* loss_pp);
 
-/* Backward pass of the last rece_forward that wrote `saved` (same X, Y, pos).
+/* Backward pass of the last rece_forward that wrote `saved` (same X, Y, pos):
+ * RECE page, Section 3, Eq. 4 (softmax minus the one-hot of the positive)
+ * restricted to {positive} u the kept set, chained through logit = x . y, with
+ * the selection held fixed.
  *   dloss    [1] float32   upstream gradient of the mean loss (ignored if dloss_pp)
  *   dloss_pp [s] float32   upstream gradient of each per-position loss, or NULL
  *   dX [s][d], dY [C][d] float32   out: overwritten with the gradients (rows of
- *                                  items that no position scored are zero). */
+ *                                  items that no position scored are zero).
+ * Deterministic: no float atomics; two calls give identical bits.  Errors as
+ * for rece_forward. */
 rece_status rece_backward(rece_plan_t plan, void* stream, const void* X, const void* Y,
                           const int32_t* pos, const float* dloss, const float* dloss_pp,
                           void* scratch, const void* saved, float* dX, float* dY);
 
-/* Intermediate results kept in `saved`, copied asynchronously into `dst`. */
+/* Intermediate results kept in `saved` (the steps of Algorithm 1, RECE page,
+ * Section 3), copied asynchronously into the caller's `dst`. */
 typedef enum {
   RECE_STAGE_BUCKET_X = 0,   /* int32 [s]  bucket of each position (round `round`) */
   RECE_STAGE_BUCKET_Y = 1,   /* int32 [C]  bucket of each item */
@@ -135,18 +165,21 @@ typedef enum {
   RECE_STAGE_PERM_Y = 3,     /* int32 [C]  sorted slot -> item */
   RECE_STAGE_THRESH_ID = 4,  /* int32 [s]  id of the k-th kept negative; -1 all kept; -2 none */
   RECE_STAGE_THRESH_LOGIT = 5, /* float64 [s] its logit (float64, coordinate-order sum) */
-  RECE_STAGE_NEG_IDS = 6,    /* int32 [s][k] kept negatives, unordered, -1 padded (KEEP_STAGES) */
+  RECE_STAGE_NEG_IDS = 6,    /* int32 [s][k] kept negatives of round `round`, unordered, -1 padded */
   RECE_STAGE_LSE = 7,        /* float32 [s] log-sum-exp over positive + kept set (round ignored) */
   RECE_STAGE_COUNTERS = 8,   /* uint32 [8] device counters: [0] error bits, [1] argmax rows
                                 decided in float64, [2] top-k rows needing float64 values,
                                 [3] logits recomputed in float64, [4] buffer overflows */
   RECE_STAGE_SCE_ROWS = 9,   /* SCE: int32 [n_b][b_x] positions taken by each bucket (a set per
                                 bucket, in the library's order) */
-  RECE_STAGE_SCE_ITEMS = 10  /* SCE: int32 [n_b][b_y] items taken by each bucket (a set per bucket) */
+  RECE_STAGE_SCE_ITEMS = 10, /* SCE: int32 [n_b][b_y] items taken by each bucket (a set per bucket) */
+  RECE_STAGE_UNION_IDS = 11  /* int32 [s][rounds*k] per position the union over rounds of the kept
+                                negatives, each id once (round order, then list order), -1 padded
+                                (round ignored; SCE: rounds = 1) */
 } rece_stage;
-/* Stages that a plan does not keep (BUCKET_* and PERM_* for SCE, SCE_* for RECE,
- * NEG_IDS without RECE_FLAG_KEEP_STAGES) have 0 bytes; rece_export rejects them.
- * For SCE, THRESH_*, NEG_IDS and LSE describe the final per-position set (round 0). */
+/* Stages that a plan does not keep (BUCKET_* and PERM_* for SCE, SCE_* for RECE)
+ * have 0 bytes; rece_export rejects them.  For SCE, THRESH_*, NEG_IDS and LSE
+ * describe the final per-position set (round 0). */
 
 rece_status rece_export(rece_plan_t plan, void* stream, const void* saved, int stage, int round,
                         void* dst);
@@ -161,18 +194,18 @@ rece_status rece_check(rece_plan_t plan, void* stream, const void* saved);
 /* Kernel timing.  rece_profile_enable(plan, mask) with mask != 0 clears earlier
  * records and, from then on, brackets the kernel launches of every phase p with
  * bit p set in mask (mask = -1: all phases) with HIP events recorded on the
- * caller's stream; mask = 0 stops recording.  rece_profile_read waits for the
- * recorded events and returns the total milliseconds and the number of
- * bracketed launches of one phase.  Profiling state is the one mutable part of
- * a plan: do not profile one plan from two threads at once. */
+ * stream each launch runs on; mask = 0 stops recording.  rece_profile_read
+ * waits for the recorded events and returns the total milliseconds and the
+ * number of bracketed launches of one phase.  Profiling state is the one mutable
+ * part of a plan: do not profile one plan from two threads at once. */
 typedef enum {
   RECE_PHASE_PROJECT = 0,   /* bucketing (projection + argmax) */
-  RECE_PHASE_SORT = 1,      /* counting sorts (buckets and positive ids) */
+  RECE_PHASE_SORT = 1,      /* counting sorts (buckets) and sorted copies */
   RECE_PHASE_SELECT = 2,    /* chunk logits + top-k */
-  RECE_PHASE_LOSS = 3,      /* positive logit, log-sum-exp, mean */
+  RECE_PHASE_LOSS = 3,      /* round dedup, positive logit, log-sum-exp, mean */
   RECE_PHASE_BWD_DX = 4,    /* backward, dX */
-  RECE_PHASE_BWD_DY = 5,    /* backward, dY of the kept negatives */
-  RECE_PHASE_BWD_POS = 6,   /* backward, dY of the positives */
+  RECE_PHASE_BWD_DY = 5,    /* backward, dY from the pairs sorted by item */
+  RECE_PHASE_BWD_SORT = 6,  /* backward, sort of the (item, position) pairs */
   RECE_PHASE_OTHER = 7,     /* small set-up kernels */
   RECE_NUM_PHASES = 8
 } rece_phase;

@@ -20,7 +20,7 @@ only its idea), see ``oracle.sce``.
 """
 from .rece import (  # noqa: F401
     seq_dot, bucket_scores, bucket_ids, stable_argsort, chunk_of, chunk_bounds, chunk_members,
-    window_chunks, round_negatives, rece_forward, rece_backward, full_ce,
+    window_chunks, round_negatives, rece_forward, loss_from_negatives, rece_backward, full_ce,
     full_ce_grad, logsumexp,
 )
 from .sce import (  # noqa: F401

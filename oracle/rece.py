@@ -1,11 +1,13 @@
-"""RECE oracle: Algorithm 1 of the RECE page, step by step, in float64.
+"""RECE oracle: the RECE page's method (Section 3, Algorithm 1), step by step, in float64.
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 Notation follows the RECE page (Section 3, Algorithm 1): positions (batch and
-sequence collapsed) are the rows of X (s = |X| of them), items the rows of Y
-(C of them), logit_{i,j} = x_i . y_j, Z-hat holds the positive (next-item) ids,
-B holds n_b random vectors, n_c is the number of chunks, r the number of rounds.
+sequence collapsed) are the rows of X (s of them), items the rows of Y (C of
+them), a logit is the scalar product of a position row and an item row, pos
+holds each position's positive (next-item) id, B holds n_b random vectors, n_c
+is the number of chunks, n_ec the neighbouring chunks on each side of a window,
+r the number of rounds.
 
 Readings of points the page leaves open (each is listed with its reason in the
 design notes of the repository):
@@ -16,9 +18,11 @@ design notes of the repository):
   * argsort is stable and ascending;
   * chunk c of N sorted elements holds the slots p with c*N/n_c <= p < (c+1)*N/n_c,
     read over the rationals (sizes differ by at most one);
-  * the window of chunk c is the set {c-1, c, c+1} taken modulo n_c (cyclic), so
-    n_c <= 3 gives the whole catalogue;
-  * "logits for wrong classes": the position's own positive item is excluded;
+  * the window of chunk c is the set of chunks c-n_ec .. c+n_ec (n_ec = 1: the
+    current and the two adjacent chunks); cyclic reading: indices taken modulo
+    n_c, so 2*n_ec + 1 >= n_c gives the whole catalogue; clipped reading
+    (wrap=False): only the chunks inside [0, n_c);
+  * only wrong classes are negatives: the position's own positive item is excluded;
   * per position, per round, the k largest window logits are kept, order
     (logit descending, item id ascending); all are kept when there are <= k;
   * rounds use independent random vectors; a pair kept in n rounds enters the
@@ -35,15 +39,17 @@ import numpy as np
 __all__ = [
     "seq_dot", "bucket_scores", "bucket_ids", "stable_argsort", "chunk_of",
     "chunk_bounds", "chunk_members", "window_chunks", "round_negatives",
-    "rece_forward", "rece_backward", "full_ce", "full_ce_grad", "logsumexp",
+    "rece_forward", "loss_from_negatives", "rece_backward", "full_ce", "full_ce_grad",
+    "logsumexp",
 ]
 
 
 def seq_dot(A, Bm, block_elems: int = 1 << 22) -> np.ndarray:
     """out[i, j] = sum over t = 0..d-1 of A[i, t] * Bm[j, t], float64, in index order t.
 
-    RECE page, Section 3: logit_{i,j} = x_i^T y_j; Algorithm 1 (positive logit line)
-    spells the scalar product as the sum over the d coordinates.
+    RECE page, Section 3: a logit is the scalar product of a position's hidden
+    state and an item embedding; Algorithm 1 writes the positive logit as the sum
+    of the d coordinate products, which is the order taken here.
     """
     A = np.asarray(A, dtype=np.float64)
     Bm = np.asarray(Bm, dtype=np.float64)
@@ -64,11 +70,11 @@ def seq_dot(A, Bm, block_elems: int = 1 << 22) -> np.ndarray:
 
 
 def bucket_scores(V, B_round) -> np.ndarray:
-    """Scores b_k . v for every row v of V and every random vector b_k.
+    """Scores b . v for every row v of V and every random vector b.
 
-    B_round has shape [d, n_b]; its column k is b_k (RECE page, Algorithm 1: the
-    random-vector line draws n_b vectors of dimension d; the indexing lines take
-    argmax over B X^T and B Y^T).
+    B_round has shape [d, n_b]; its column b is one random vector (RECE page,
+    Algorithm 1: n_b Gaussian vectors of dimension d are drawn, and every position
+    and item is scored against each of them).
     """
     return seq_dot(V, np.asarray(B_round).T)
 
@@ -76,22 +82,25 @@ def bucket_scores(V, B_round) -> np.ndarray:
 def bucket_ids(V, B_round) -> np.ndarray:
     """Index of the random vector with the largest scalar product (ties: lowest index).
 
-    RECE page, Algorithm 1 (I = argmax_b B X^T, J = argmax_b B Y^T); Section 3
-    calls it the index of the nearest vector from B in terms of dot product.
+    RECE page, Section 3 (method paragraph) and Algorithm 1, the two indexing
+    steps: each position and each item is labelled with the random vector nearest
+    to it by scalar product.
     """
     return np.argmax(bucket_scores(V, B_round), axis=1).astype(np.int64)
 
 
 def stable_argsort(keys) -> np.ndarray:
-    """argsort of the bucket indices (RECE page, Algorithm 1 sorting lines); stable, ascending."""
+    """Order of the elements by bucket label (RECE page, Algorithm 1, the two sorting
+    steps); read as a stable ascending argsort."""
     return np.argsort(np.asarray(keys), kind="stable").astype(np.int64)
 
 
 def chunk_bounds(N: int, n_c: int) -> np.ndarray:
     """Start slots of the n_c chunks (plus N at the end).
 
-    RECE page, Algorithm 1 chunk lines: chunk c holds the sorted slots p with
-    c*N/n_c <= p < (c+1)*N/n_c; the smallest such p is ceil(c*N/n_c).
+    RECE page, Algorithm 1, the chunk step: the sorted order is cut into n_c equal
+    chunks, chunk c holding the slots p with c*N/n_c <= p < (c+1)*N/n_c; the
+    smallest such p is ceil(c*N/n_c).
     """
     c = np.arange(n_c + 1, dtype=np.int64)
     return (c * N + n_c - 1) // n_c
@@ -108,11 +117,17 @@ def chunk_of(p, N: int, n_c: int):
     return (np.asarray(p, dtype=np.int64) * n_c) // N
 
 
-def window_chunks(c: int, n_c: int) -> list:
-    """Chunks whose items X-chunk c is scored against: the current and the two adjacent
-    chunks (RECE page, Algorithm 1 window line J_{c-1} u J_c u J_{c+1}), taken modulo
-    n_c and as a set."""
-    return sorted({(c - 1) % n_c, c % n_c, (c + 1) % n_c})
+def window_chunks(c: int, n_c: int, n_ec: int = 1, wrap: bool = True) -> list:
+    """Chunks whose items the positions of chunk c are scored against.
+
+    RECE page, Algorithm 1 (the current chunk and its neighbours on both sides) and
+    the method paragraph of Section 3 (n_ec, the number of neighbouring chunks
+    looked into).  Chunks c - n_ec .. c + n_ec as a set: modulo n_c when ``wrap``
+    (cyclic reading), else only those inside [0, n_c) (clipped reading).
+    """
+    if wrap:
+        return sorted({(c + t) % n_c for t in range(-n_ec, n_ec + 1)})
+    return [cc for cc in range(c - n_ec, c + n_ec + 1) if 0 <= cc < n_c]
 
 
 def _top_k(ids: np.ndarray, logits: np.ndarray, k: int):
@@ -121,12 +136,14 @@ def _top_k(ids: np.ndarray, logits: np.ndarray, k: int):
     return order[:k]
 
 
-def round_negatives(X, Y, pos, perm_x, perm_y, n_c: int, k: int, rows=None):
+def round_negatives(X, Y, pos, perm_x, perm_y, n_c: int, k: int, rows=None, n_ec: int = 1,
+                    wrap: bool = True):
     """Negatives of one round for every position (or for the positions in ``rows``).
 
-    For X-chunk c (RECE page, Algorithm 1 chunk/window/logit lines): the logits of its
-    positions against the items of the window chunks, the position's own positive
-    excluded ("logits for wrong classes"), then the k largest per position.
+    For position chunk c (RECE page, Algorithm 1, the chunk, window and negative-logit
+    steps): the logits of its positions against the items of the window chunks, the
+    position's own positive excluded (only wrong classes are negatives), then the k
+    largest per position.
 
     Returns a dict  i -> (ids, logits, threshold)  where ids/logits are in rank order
     and threshold is (logit, id) of the k-th kept candidate when more than k
@@ -145,7 +162,7 @@ def round_negatives(X, Y, pos, perm_x, perm_y, n_c: int, k: int, rows=None):
         if len(I) == 0:
             continue
         J = np.concatenate([np.asarray(perm_y)[chunk_members(cc, C, n_c)]
-                            for cc in window_chunks(c, n_c)])
+                            for cc in window_chunks(c, n_c, n_ec, wrap)])
         L = seq_dot(X[I], Y[J])
         for r, i in enumerate(I):
             keep = J != pos[i]
@@ -165,55 +182,94 @@ def logsumexp(v) -> float:
     return float(m + np.log(np.sum(np.exp(v - m))))
 
 
-def rece_forward(X, Y, pos, B, n_c: int, k: int, rows=None) -> dict:
-    """RECE loss (RECE page, Algorithm 1 and the rounds paragraph of Section 3).
+def rece_forward(X, Y, pos, B, n_c: int, k: int, rows=None, n_ec: int = 1, wrap: bool = True,
+                 buckets=None) -> dict:
+    """RECE loss (RECE page, Section 3: Algorithm 1 and the rounds paragraph).
 
     B has shape [r, d, n_b] (one independent draw of the random vectors per round).
+    Per round: bucket labels of positions and items, their stable orders, chunks,
+    each chunk's window, the k largest negatives of every position; then the loss
+    of every position over its positive and the union of its rounds' negatives.
     With ``rows`` the per-position work (negatives, loss) is done for those
     positions only and the mean is taken over them; bucketing and sorting always
-    cover every position and item, since they decide the chunks.
+    cover every position and item, since they decide the chunks.  ``buckets``
+    (optional, one (bx, by) pair per round) replaces the bucket labels: the steps
+    after the labelling are then recomputed from the given labels.
     """
     X = np.asarray(X, dtype=np.float64)
     Y = np.asarray(Y, dtype=np.float64)
     pos = np.asarray(pos, dtype=np.int64)
     B = np.asarray(B, dtype=np.float64)
-    s, C = X.shape[0], Y.shape[0]
     rounds = B.shape[0]
-    rows = np.arange(s) if rows is None else np.asarray(rows, dtype=np.int64)
-
     st = {"bx": [], "by": [], "perm_x": [], "perm_y": [], "negs": []}
     for rho in range(rounds):
-        bx = bucket_ids(X, B[rho])                  # I = argmax_b B X^T
-        by = bucket_ids(Y, B[rho])                  # J = argmax_b B Y^T
-        px = stable_argsort(bx)                     # X = X[argsort I]
-        py = stable_argsort(by)                     # Y = Y[argsort J]
+        if buckets is None:
+            bx, by = bucket_ids(X, B[rho]), bucket_ids(Y, B[rho])
+        else:
+            bx, by = (np.asarray(v, dtype=np.int64) for v in buckets[rho])
+        px, py = stable_argsort(bx), stable_argsort(by)
         st["bx"].append(bx)
         st["by"].append(by)
         st["perm_x"].append(px)
         st["perm_y"].append(py)
-        st["negs"].append(round_negatives(X, Y, pos, px, py, n_c, k, rows))
+        st["negs"].append(round_negatives(X, Y, pos, px, py, n_c, k, rows, n_ec, wrap))
+    st.update(_loss(X, Y, pos, st["negs"], rows))
+    return st
 
-    # Positive logit: sum_k X[i]_k * Y[Z-hat[i]]_k, original item id of the positive.
+
+def loss_from_negatives(X, Y, pos, negs, rows=None) -> dict:
+    """The loss given each round's negative sets, the steps after the selection.
+
+    ``negs[rho]`` maps a position id to the item ids it kept in round rho (any
+    order).  Logits are recomputed here in float64; the result has the fields of
+    ``rece_forward`` that ``rece_backward`` reads.  This is the injection point
+    for sets produced elsewhere (for example read back from another
+    implementation after checking them on samples).
+    """
+    X = np.asarray(X, dtype=np.float64)
+    Y = np.asarray(Y, dtype=np.float64)
+    pos = np.asarray(pos, dtype=np.int64)
+    full = []
+    for per in negs:
+        d = {}
+        for i, ids in per.items():
+            ids = np.asarray(ids, dtype=np.int64)
+            lg = seq_dot(X[int(i)], Y[ids])[0] if len(ids) else np.zeros(0)
+            d[int(i)] = (ids, lg, None)
+        full.append(d)
+    st = {"negs": full}
+    st.update(_loss(X, Y, pos, full, rows))
+    return st
+
+
+def _loss(X, Y, pos, negs, rows) -> dict:
+    """Per-position loss over the positive and the rounds' negatives (RECE page,
+    Algorithm 1, the positive-logit, loss and mean steps; Section 3, the duplicate
+    rule for pairs kept in several rounds)."""
+    s = X.shape[0]
+    rounds = len(negs)
+    rows = np.arange(s) if rows is None else np.asarray(rows, dtype=np.int64)
+    # positive logit: the scalar product with the positive's own (original) item row
     l_pos = np.array([seq_dot(X[i], Y[pos[i]][None, :])[0, 0] for i in rows])
-
     lse = np.empty(len(rows))
     loss = np.empty(len(rows))
     union, mult = [], []
     for n, i in enumerate(rows):
         i = int(i)
-        copy_ids = np.concatenate([st["negs"][rho][i][0] for rho in range(rounds)])
-        copy_lg = np.concatenate([st["negs"][rho][i][1] for rho in range(rounds)])
+        copy_ids = np.concatenate([np.asarray(negs[rho][i][0], dtype=np.int64) for rho in range(rounds)])
+        copy_lg = np.concatenate([np.asarray(negs[rho][i][1], dtype=np.float64) for rho in range(rounds)])
         uniq, cnt = np.unique(copy_ids, return_counts=True)
         count = dict(zip(uniq.tolist(), cnt.tolist()))
-        # Duplicate rule: each copy's logit minus ln(number of rounds that kept the pair).
+        # duplicate rule: every copy of a pair enters with its logit lowered by the log
+        # of the number of rounds that kept the pair
         adj = np.array([lg - np.log(count[int(j)]) for j, lg in zip(copy_ids, copy_lg)])
         lse[n] = logsumexp(np.concatenate([[l_pos[n]], adj]))
-        loss[n] = lse[n] - l_pos[n]             # -log(exp(l+) / (exp(l+) + sum exp(l-)))
+        # negative log of the positive's softmax share over the scored set
+        loss[n] = lse[n] - l_pos[n]
         union.append(uniq.astype(np.int64))
         mult.append(cnt.astype(np.int64))
-    st.update(rows=rows, l_pos=l_pos, lse=lse, loss_pp=loss, union=union, mult=mult,
-              loss=float(np.mean(loss)) if len(rows) else 0.0)
-    return st
+    return dict(rows=rows, l_pos=l_pos, lse=lse, loss_pp=loss, union=union, mult=mult,
+                loss=float(np.mean(loss)) if len(rows) else 0.0)
 
 
 def rece_backward(X, Y, pos, fwd: dict, dloss: float = 1.0, dloss_pp=None):
@@ -222,12 +278,13 @@ def rece_backward(X, Y, pos, fwd: dict, dloss: float = 1.0, dloss_pp=None):
     RECE page Eq. (4) restricted to the scored set: d loss_i / d logit_{i,j} is the
     softmax over {positive} + copies minus 1 for the positive.  A pair kept in n
     rounds contributes n copies of exp(l - ln n)/Z, i.e. exp(l)/Z in total.
-    Upstream gradient: dloss (of the mean) or dloss_pp[i] per position.
+    Upstream gradient: dloss (of the mean) or dloss_pp[i] per position.  One
+    position at a time; inside a round's list every item appears once, so the
+    item rows it touches are updated together.
     """
     X = np.asarray(X, dtype=np.float64)
     Y = np.asarray(Y, dtype=np.float64)
     pos = np.asarray(pos, dtype=np.int64)
-    s = X.shape[0]
     rounds = len(fwd["negs"])
     dX = np.zeros_like(X)
     dY = np.zeros_like(Y)
@@ -241,10 +298,13 @@ def rece_backward(X, Y, pos, fwd: dict, dloss: float = 1.0, dloss_pp=None):
         dY[pos[i]] += gbar * g_pos * X[i]
         for rho in range(rounds):
             ids, lg, _ = fwd["negs"][rho][i]
-            for j, l in zip(ids, lg):
-                g = np.exp(l - np.log(count[int(j)]) - lse)
-                dX[i] += gbar * g * Y[j]
-                dY[j] += gbar * g * X[i]
+            ids = np.asarray(ids, dtype=np.int64)
+            if len(ids) == 0:
+                continue
+            mult = np.array([count[int(j)] for j in ids], dtype=np.float64)
+            g = gbar * np.exp(np.asarray(lg, dtype=np.float64) - np.log(mult) - lse)
+            dX[i] += g @ Y[ids]
+            dY[ids] += g[:, None] * X[i][None, :]
     return dX, dY
 
 

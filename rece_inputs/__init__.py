@@ -55,6 +55,8 @@ class Workload:
     popular_scale: float = 1.0     # factor applied to the C//100 most popular rows of Y
     seed: int = 0
     b_seed: Optional[int] = None   # separate seed for B only (None: same stream as the rest)
+    n_ec: int = 1                  # RECE: neighbouring chunks on each side of a window
+    window_wrap: bool = True       # RECE: window chunk indices modulo n_c (else clipped)
 
     @property
     def s(self) -> int:

@@ -20,9 +20,9 @@ def run_rece(inp, keep_stages=True, backward=True, dloss_pp=None, tensors=None):
     w = inp.w
     X, Y, pos, B = tensors if tensors is not None else to_device(inp)
     plan = rece.Plan(w.s, w.C, w.d, w.n_b, w.n_c, w.k, w.rounds, dtype=w.dtype,
-                     keep_stages=keep_stages, validate_ids=True)
-    print(f"[gpu] rece s={w.s} C={w.C} d={w.d} n_b={w.n_b} n_c={w.n_c} k={w.k} r={w.rounds} "
-          f"dtype={w.dtype} seed={w.seed}", flush=True)
+                     keep_stages=keep_stages, validate_ids=True, n_ec=w.n_ec, window_wrap=w.window_wrap)
+    print(f"[gpu] rece s={w.s} C={w.C} d={w.d} n_b={w.n_b} n_c={w.n_c} n_ec={w.n_ec} "
+          f"wrap={int(w.window_wrap)} k={w.k} r={w.rounds} dtype={w.dtype} seed={w.seed}", flush=True)
     loss, lpp, scratch, saved = plan.forward(X, Y, pos, B)
     out = {"loss": None}
     if backward:
@@ -37,6 +37,7 @@ def run_rece(inp, keep_stages=True, backward=True, dloss_pp=None, tensors=None):
         out["dY"] = dY.cpu().numpy()
     out["counters"] = plan.export(saved, "counters").cpu().numpy()
     out["lse"] = plan.export(saved, "lse").cpu().numpy()
+    out["union_ids"] = plan.export(saved, "union_ids").cpu().numpy()
     for r in range(w.rounds):
         for st in ("bucket_x", "bucket_y", "perm_x", "perm_y", "thresh_id", "thresh_logit"):
             out[(st, r)] = plan.export(saved, st, r).cpu().numpy()
@@ -68,7 +69,7 @@ def run_sce(inp, keep_stages=True, backward=True, dloss_pp=None):
     if backward:
         out["dX"] = dX.cpu().numpy()
         out["dY"] = dY.cpu().numpy()
-    for st in ("counters", "lse", "thresh_id", "thresh_logit", "sce_rows", "sce_items"):
+    for st in ("counters", "lse", "thresh_id", "thresh_logit", "sce_rows", "sce_items", "union_ids"):
         out[st] = plan.export(saved, st).cpu().numpy()
     if keep_stages:
         out["neg_ids"] = plan.export(saved, "neg_ids").cpu().numpy()

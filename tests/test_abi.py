@@ -55,6 +55,10 @@ def _plan(**kw):
     (dict(variant="sce", b_x=4, b_y=2001), 1),       # b_y in 1..C
     (dict(variant="sce", b_x=4, b_y=8, rounds=2), 1),
     (dict(variant="sce", b_x=4, b_y=1500, k=1025), 2),   # k above the merge capacity
+    (dict(n_ec=-1), 1),                                  # neighbouring chunks >= 0
+    (dict(n_ec=(1 << 20) + 1), 1),
+    (dict(window_wrap=2), 1),                            # 0 (clipped) or 1 (cyclic)
+    (dict(s=1 << 20, C=1 << 20, n_c=16, k=2047, rounds=1), 2),   # s * k + s beyond int32 pair records
 ])
 def test_plan_rejects_invalid(bad, status):
     with pytest.raises(rece.ReceError) as ei:
@@ -67,7 +71,8 @@ def test_plan_null_arguments():
     L = rece.lib()
     h = ctypes.c_void_p()
     assert L.rece_plan(None, ctypes.byref(h)) == 1
-    cfg = rece.ReceConfig(256, 2000, 64, 16, 16, 32, 1, 0, 0, 0, 0, 0)
+    # s, C, d, n_b, n_c, n_ec, k, rounds, b_x, b_y, dtype, variant, window_wrap, flags
+    cfg = rece.ReceConfig(256, 2000, 64, 16, 16, 1, 32, 1, 0, 0, 0, 0, 1, 0)
     assert L.rece_plan(ctypes.byref(cfg), None) == 1
     assert L.rece_plan(ctypes.byref(cfg), ctypes.byref(h)) == 0
     # forward with NULL pointers fails before touching the GPU
@@ -87,10 +92,28 @@ def test_workspace_never_holds_a_logit_tensor(name):
     # no buffer of s*C*2 bytes (a bf16 [s, C] logit tensor) is ever needed; what the
     # forward pass keeps grows with the kept negatives (one int32 id per position,
     # round and kept pair), not with the catalogue
-    lists = w.rounds * w.s * w.k * 4 if w.variant == "rece" else 0
-    assert p.scratch_bytes < w.s * w.C * 2
+    rounds = w.rounds if w.variant == "rece" else 1
+    lists = rounds * w.s * w.k * 4
+    es = 2 if w.dtype == "bf16" else 4
+    # scratch: the sorted copies of every round (rows), the backward's pair records
+    # (four int32 arrays over the kept pairs and positives, plus the dY work area of two
+    # float32 rows per 256 pairs) and small per-element arrays
+    pairs = rounds * w.s * w.k + w.s
+    rows = rounds * (w.s + w.C) * w.d * es
+    slots = w.n_b * (w.b_x + w.b_y) * (w.d * es + 64) + w.n_b * (w.s + w.C) * 4
+    assert p.scratch_bytes <= rows + slots + pairs * (16 + 2 * w.d * 4 // 256 + 1) + 16 * (w.s + w.C) * rounds \
+        + (32 << 20)
+    if w.k * 8 < w.C:   # a reduced set (not the full-CE twin): far below a dense logit tensor
+        assert p.scratch_bytes < w.s * w.C * 2
     assert p.saved_bytes - lists < w.s * w.C * 2
     assert p.scratch_bytes > 0 and p.saved_bytes > 0
+    # saved holds no row of X or Y: the per-round labels, orders and thresholds, the
+    # kept lists and per-position values (int32 / float32 / float64 scalars)
+    # (per position and round: bucket, order slot, threshold and sums, 40 bytes; per item and
+    # round: bucket and order slot, 8 bytes)
+    assert p.saved_bytes < lists + rounds * (40 * w.s + 8 * w.C) + 16 * w.s + (1 << 16) \
+        + w.n_b * (w.b_x + w.b_y) * 4
+    assert p.saved_bytes < (w.s + w.C) * w.d * es + lists
 
 
 def test_export_sizes():
@@ -98,12 +121,34 @@ def test_export_sizes():
     L = rece.lib()
     nb = ctypes.c_size_t()
     for stage, want in (("bucket_x", 256 * 4), ("bucket_y", 2000 * 4), ("perm_y", 2000 * 4),
-                        ("thresh_logit", 256 * 8), ("neg_ids", 256 * 32 * 4), ("counters", 32)):
+                        ("thresh_logit", 256 * 8), ("neg_ids", 256 * 32 * 4), ("counters", 32),
+                        ("union_ids", 256 * 2 * 32 * 4)):
         assert L.rece_export_bytes(p._h, rece.STAGES[stage], ctypes.byref(nb)) == 0
         assert nb.value == want
-    q = _plan()
-    assert L.rece_export_bytes(q._h, rece.STAGES["neg_ids"], ctypes.byref(nb)) == 0 and nb.value == 0
+    q = _plan()   # the kept lists are always kept: the backward pass reads them
+    assert L.rece_export_bytes(q._h, rece.STAGES["neg_ids"], ctypes.byref(nb)) == 0 and nb.value == 256 * 32 * 4
+    assert L.rece_export_bytes(q._h, rece.STAGES["union_ids"], ctypes.byref(nb)) == 0 and nb.value == 256 * 32 * 4
     assert L.rece_export_bytes(q._h, 99, ctypes.byref(nb)) == 1
+
+
+@pytest.mark.parametrize("kw", [
+    dict(n_ec=0), dict(n_ec=2), dict(n_ec=7), dict(n_ec=3, window_wrap=False), dict(n_c=1, n_ec=0),
+    dict(n_ec=1 << 20),
+])
+def test_window_options_accepted(kw):
+    p = _plan(**kw)
+    assert p.cfg.n_ec == kw.get("n_ec", 1)
+    assert p.cfg.window_wrap == (0 if kw.get("window_wrap") is False else 1)
+
+
+def test_windows_beyond_16_bit_histogram_counts_are_planned():
+    """A window of more than 65535 items (here the whole catalogue of 70000) would
+    wrap a 16-bit histogram bin; the plan accepts it (the chunk kernel then counts
+    in 32 bits), with and without a top-k that keeps every candidate."""
+    for k in (16, 69999):
+        p = rece.Plan(64, 70000, 32, 1, 1, k, 1, dtype="f32")
+        assert p.scratch_bytes > 0
+    rece.Plan(64, 200000, 32, 8, 2, 16, 1, dtype="bf16", n_ec=0)   # two chunks of 100000 items
 
 
 def test_product_path_has_no_fallback():
@@ -127,5 +172,6 @@ def test_sce_plan_and_exports():
     assert sizes["sce_rows"] == 16 * 40 * 4 and sizes["sce_items"] == 16 * 300 * 4
     assert sizes["bucket_x"] == sizes["perm_y"] == 0       # not kept by the bucket variant
     assert sizes["neg_ids"] == 256 * 16 * 4 and sizes["lse"] == 256 * 4
+    assert sizes["union_ids"] == 256 * 16 * 4
     r = _plan(keep_stages=True)
     assert L.rece_export_bytes(r._h, rece.STAGES["sce_rows"], ctypes.byref(nb)) == 0 and nb.value == 0

@@ -35,6 +35,14 @@ CASES = {
     # earlier rounds' kept ids too many for the dedup's LDS tables ((rounds - 1) * k > 2048):
     # the dedup scans the earlier lists; windows of three of four chunks overlap partly
     "dedup_scan": scaled("tiny", seqs=1, seqlen=64, C=4000, n_b=4, n_c=4, k=2100, rounds=2),
+    # windows of n_ec neighbouring chunks on each side, cyclic and clipped
+    "own_chunk_only": scaled("sasrec", seqs=2, seqlen=150, C=3001, n_b=12, n_c=12, k=20, rounds=2, n_ec=0),
+    "two_neighbours": scaled("sasrec", seqs=3, seqlen=128, C=6007, n_b=16, n_c=16, k=48, rounds=2, n_ec=2),
+    "clipped": scaled("sasrec", seqs=3, seqlen=100, C=4001, n_b=10, n_c=10, k=40, rounds=2,
+                      window_wrap=False),
+    "clipped_wide": scaled("tiny", seqs=2, seqlen=90, C=2500, d=32, n_b=9, n_c=9, k=30, rounds=1, n_ec=3,
+                           window_wrap=False),
+    "neighbours_cover_all": scaled("sasrec", seqs=1, seqlen=128, C=1500, n_b=5, n_c=5, k=60, rounds=2, n_ec=2),
 }
 
 
@@ -64,6 +72,10 @@ def _compare(name, inp, g, fwd):
     assert lpp_err <= tol, (name, lpp_err)
     c = g["counters"]
     assert c[0] == 0 and c[4] == 0, (name, c)
+    # the union over rounds, each id once
+    for n, i in enumerate(fwd["rows"]):
+        u = g["union_ids"][int(i)]
+        assert np.array_equal(np.sort(u[u >= 0]), fwd["union"][n]), (name, i)
 
 
 @pytest.mark.parametrize("name", list(CASES))
@@ -71,7 +83,7 @@ def test_forward_backward_parity(name):
     w = CASES[name]
     inp = make_inputs(w)
     g = run_rece(inp)
-    fwd = oracle.rece_forward(inp.X, inp.Y, inp.pos, inp.B, w.n_c, w.k)
+    fwd = oracle.rece_forward(inp.X, inp.Y, inp.pos, inp.B, w.n_c, w.k, n_ec=w.n_ec, wrap=w.window_wrap)
     _compare(name, inp, g, fwd)
     gX, gY = oracle.rece_backward(inp.X, inp.Y, inp.pos, fwd)
     if w.k == 0:
@@ -141,5 +153,23 @@ def test_exact_topk_ties_from_duplicate_items():
                         for c in (thr[1] % U + U * np.arange(4)))
     assert tied > w.s // 4, tied
     assert g["counters"][2] > 0   # rows whose k-th element needed the float64 ranking
+    gX, gY = oracle.rece_backward(inp.X, inp.Y, inp.pos, fwd)
+    assert grad_err(g["dX"], gX) <= 2e-3 and grad_err(g["dY"], gY) <= 2e-3
+
+
+def test_histogram_bin_above_16_bits():
+    """A window of 70,000 items of which 66,000 are zero rows: every position's
+    logit-0 histogram bin holds more than 65,535 entries, which 16-bit counts would
+    wrap; the plan switches the chunk kernel to 32-bit counts and the selection
+    matches the oracle exactly."""
+    w = scaled("tiny", seqs=1, seqlen=64, C=70000, d=32, n_b=1, n_c=1, k=40, rounds=1)
+    inp = make_inputs(w)
+    Y = inp.Y.copy()
+    Y[:66000] = 0.0
+    inp = dataclasses.replace(inp, Y=Y)
+    print("[gpu] window of 70000 items, 66000 zero rows", flush=True)
+    g = run_rece(inp)
+    fwd = oracle.rece_forward(inp.X, inp.Y, inp.pos, inp.B, w.n_c, w.k)
+    _compare("bin_above_16_bits", inp, g, fwd)
     gX, gY = oracle.rece_backward(inp.X, inp.Y, inp.pos, fwd)
     assert grad_err(g["dX"], gX) <= 2e-3 and grad_err(g["dY"], gY) <= 2e-3

@@ -47,6 +47,8 @@ def _check(name, inp, g, fwd):
             assert tid[i] == thr[0] and te[i] == thr[1], (name, i, tid[i], te[i], thr)
         gs = np.sort(negs[i][negs[i] >= 0]) if w.k > 0 else np.array([], dtype=np.int64)
         assert np.array_equal(gs, np.sort(ids)), (name, i)
+        u = g["union_ids"][i] if w.k > 0 else np.array([], dtype=np.int64)
+        assert np.array_equal(np.sort(u[u >= 0]), np.sort(ids)), (name, i)
     rel = abs(g["loss"] - fwd["loss"]) / max(abs(fwd["loss"]), 1e-30)
     assert rel <= tol, (name, g["loss"], fwd["loss"])
     lpp_err = np.max(np.abs(g["loss_pp"] - fwd["loss_pp"]) / np.maximum(np.abs(fwd["loss_pp"]), 1.0))

@@ -119,6 +119,100 @@ def test_window_cyclic():
             assert oracle.window_chunks(c, n_c) == list(range(n_c))
 
 
+def test_window_neighbour_count_and_clipping():
+    # n_ec neighbouring chunks on each side (RECE page, Section 3, method paragraph)
+    assert oracle.window_chunks(2, 7, n_ec=0) == [2]
+    assert oracle.window_chunks(3, 9, n_ec=2) == [1, 2, 3, 4, 5]
+    assert oracle.window_chunks(0, 9, n_ec=2) == [0, 1, 2, 7, 8]
+    assert oracle.window_chunks(8, 9, n_ec=3) == [0, 1, 2, 5, 6, 7, 8]
+    for n_c in range(1, 8):   # 2 n_ec + 1 >= n_c: every chunk
+        for c in range(n_c):
+            assert oracle.window_chunks(c, n_c, n_ec=(n_c - 1 + 1) // 2) == list(range(n_c))
+    # clipped: the chunks inside [0, n_c) only
+    assert oracle.window_chunks(0, 5, wrap=False) == [0, 1]
+    assert oracle.window_chunks(4, 5, wrap=False) == [3, 4]
+    assert oracle.window_chunks(2, 5, wrap=False) == [1, 2, 3]
+    assert oracle.window_chunks(1, 6, n_ec=3, wrap=False) == [0, 1, 2, 3, 4]
+    # the two readings agree away from the ends and for a single chunk
+    for n_ec in range(4):
+        assert oracle.window_chunks(0, 1, n_ec, True) == oracle.window_chunks(0, 1, n_ec, False) == [0]
+        for c in range(n_ec, 12 - n_ec):
+            assert oracle.window_chunks(c, 12, n_ec, True) == oracle.window_chunks(c, 12, n_ec, False)
+
+
+@pytest.mark.parametrize("n_ec,wrap", [(0, True), (2, True), (1, False), (2, False), (0, False)])
+def test_windows_brute_force(n_ec, wrap):
+    """Each position's candidates, straight from the definitions: every sorted item
+    slot whose chunk is within n_ec of the position's chunk (cyclic distance, or
+    plain distance when clipped), the positive left out; then the k largest."""
+    s, C, n_c, k = 21, 47, 7, 4
+    X, Y, pos, B = _rand_case(60 + n_ec + 10 * wrap, s=s, C=C, d=4, n_b=3, rounds=1)
+    px = oracle.stable_argsort(oracle.bucket_ids(X, B[0]))
+    py = oracle.stable_argsort(oracle.bucket_ids(Y, B[0]))
+    negs = oracle.round_negatives(X, Y, pos, px, py, n_c, k, n_ec=n_ec, wrap=wrap)
+    for slot, i in enumerate(px):
+        c = slot * n_c // s
+        cand = []
+        for q in range(C):
+            cq = q * n_c // C
+            dist = abs(cq - c)
+            if wrap:
+                dist = min(dist, n_c - dist)
+            if dist <= n_ec and py[q] != pos[i]:
+                cand.append(int(py[q]))
+        lg = {j: sum(X[i, t] * Y[j, t] for t in range(4)) for j in cand}
+        want = sorted(cand, key=lambda j: (-lg[j], j))[:k]
+        assert negs[int(i)][0].tolist() == want
+
+
+@pytest.mark.parametrize("n_c,n_ec,n_b", [(5, 2, 3), (7, 3, 4), (4, 5, 2)])
+def test_wide_cyclic_window_is_full_ce(n_c, n_ec, n_b):
+    # 2 n_ec + 1 >= n_c: every window is the whole catalogue, so k = C - 1 is full CE (Eq. 3)
+    X, Y, pos, B = _rand_case(70 + n_c, s=20, C=37, d=5, n_b=n_b, rounds=1)
+    fwd = oracle.rece_forward(X, Y, pos, B, n_c=n_c, k=36, n_ec=n_ec)
+    assert np.allclose(fwd["loss_pp"], oracle.full_ce(X, Y, pos), rtol=1e-12, atol=1e-12)
+
+
+def test_loss_grows_with_the_window():
+    # one round: the i-th largest of a larger window is no smaller, so each position's
+    # top-k sum grows (over several rounds the union may overlap more and need not)
+    X, Y, pos, B = _rand_case(75, s=30, C=90, d=6, n_b=5, rounds=1)
+    prev = None
+    for n_ec in range(0, 5):
+        cur = oracle.rece_forward(X, Y, pos, B, n_c=9, k=5, n_ec=n_ec)["loss_pp"]
+        if prev is not None:
+            assert np.all(cur >= prev - 1e-12)
+        prev = cur
+    clipped = oracle.rece_forward(X, Y, pos, B, n_c=9, k=5, n_ec=2, wrap=False)["loss_pp"]
+    cyclic = oracle.rece_forward(X, Y, pos, B, n_c=9, k=5, n_ec=2, wrap=True)["loss_pp"]
+    assert np.all(cyclic >= clipped - 1e-12)
+
+
+def test_injected_sets_and_buckets():
+    X, Y, pos, B = _rand_case(76, s=24, C=50, d=5, n_b=4, rounds=2)
+    fwd = oracle.rece_forward(X, Y, pos, B, n_c=4, k=6)
+    # the loss from the forward pass's own sets is the forward pass's loss
+    sets = [{i: fwd["negs"][r][i][0] for i in range(24)} for r in range(2)]
+    inj = oracle.loss_from_negatives(X, Y, pos, sets)
+    assert np.array_equal(inj["loss_pp"], fwd["loss_pp"]) and np.array_equal(inj["lse"], fwd["lse"])
+    g1, g2 = oracle.rece_backward(X, Y, pos, fwd), oracle.rece_backward(X, Y, pos, inj)
+    assert np.allclose(g1[0], g2[0], atol=1e-15) and np.allclose(g1[1], g2[1], atol=1e-15)
+    # a hand-chosen set: the loss is the closed-form log-sum-exp over it
+    hand = [{0: [3, 7]}, {0: [7, 11]}]
+    one = oracle.loss_from_negatives(X, Y, pos, hand, rows=[0])
+    L = X[0] @ Y.T
+    want = np.log(np.exp(L[pos[0]]) + np.exp(L[[3, 7, 11]]).sum()) - L[pos[0]]
+    assert math.isclose(one["loss_pp"][0], want, rel_tol=1e-13)
+    # bucket labels given: the same result as computing them, and labels of one's own choice
+    # give the chunks they define
+    same = oracle.rece_forward(X, Y, pos, B, n_c=4, k=6, buckets=list(zip(fwd["bx"], fwd["by"])))
+    assert np.array_equal(same["loss_pp"], fwd["loss_pp"])
+    bx, by = np.arange(24) % 3, (np.arange(50) * 7) % 5
+    other = oracle.rece_forward(X, Y, pos, B[:1], n_c=4, k=6, buckets=[(bx, by)])
+    assert other["perm_x"][0].tolist() == sorted(range(24), key=lambda i: (bx[i], i))
+    assert other["perm_y"][0].tolist() == sorted(range(50), key=lambda j: (by[j], j))
+
+
 # ---------------------------------------------------------------- top-k
 
 def test_topk_brute_force():
