@@ -26,7 +26,7 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too sm
           4: "HIP runtime error", 5: "device check failed", 6: "internal error"}
 
 EXPORTED = ["rece_plan", "rece_plan_destroy", "rece_workspace_bytes", "rece_forward",
-            "rece_backward", "rece_export", "rece_export_bytes", "rece_check",
+            "rece_forward_static", "rece_backward", "rece_export", "rece_export_bytes", "rece_check",
             "rece_profile_enable", "rece_profile_read",
             "rece_status_string", "rece_last_error", "rece_version"]
 PHASES = ["project", "sort", "select", "loss", "bwd_dx", "bwd_dy", "bwd_sort", "other"]
@@ -62,6 +62,7 @@ def lib() -> ctypes.CDLL:
         L.rece_plan_destroy.argtypes = [vp]
         L.rece_workspace_bytes.argtypes = [vp, sz, sz]
         L.rece_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.rece_forward_static.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.rece_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.rece_export.argtypes = [vp, vp, vp, i32, i32, vp]
         L.rece_export_bytes.argtypes = [vp, i32, sz]
@@ -74,7 +75,7 @@ def lib() -> ctypes.CDLL:
         L.rece_last_error.restype = ctypes.c_char_p
         L.rece_version.restype = ctypes.c_char_p
         for name in ("rece_plan", "rece_plan_destroy", "rece_workspace_bytes", "rece_forward",
-                     "rece_backward", "rece_export", "rece_export_bytes", "rece_check",
+                     "rece_forward_static", "rece_backward", "rece_export", "rece_export_bytes", "rece_check",
                      "rece_profile_enable", "rece_profile_read"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -164,6 +165,25 @@ class Plan:
         _check(lib().rece_forward(self._h, _stream(stream), _ptr(X), _ptr(Y), _ptr(pos), _ptr(B),
                                   _ptr(scratch), _ptr(saved), _ptr(loss), _ptr(lpp)))
         return loss, lpp, scratch, saved
+
+    def forward_static(self, X, Y, pos, B, saved=None, loss=None, loss_pp=None, stream=None):
+        """rece_forward_static: the forward pass on the library's static scratch array.
+        saved, loss [1] and loss_pp [s] (optional) are the caller's; returns (loss, loss_pp, saved)."""
+        import torch
+        self._check_inputs(X, Y, pos, B)
+        if saved is None:
+            saved = torch.empty(max(self.saved_bytes, 16), dtype=torch.uint8, device=X.device)
+        if loss is None:
+            loss = torch.empty(1, dtype=torch.float32, device=X.device)
+        for name, t, shape in (("loss", loss, (1,)), ("loss_pp", loss_pp, (self.cfg.s,))):
+            if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != shape or not t.is_contiguous()
+                                  or t.device != X.device):
+                raise ValueError(f"{name} must be a contiguous float32 tensor of shape {shape} on {X.device}")
+        if saved.device != X.device or saved.numel() * saved.element_size() < self.saved_bytes:
+            raise ValueError(f"saved must hold at least {self.saved_bytes} bytes on {X.device}")
+        _check(lib().rece_forward_static(self._h, _stream(stream), _ptr(X), _ptr(Y), _ptr(pos), _ptr(B),
+                                         _ptr(saved), _ptr(loss), _ptr(loss_pp)))
+        return loss, loss_pp, saved
 
     def backward(self, X, Y, pos, scratch, saved, dloss=None, dloss_pp=None, dX=None, dY=None,
                  stream=None):

@@ -109,6 +109,7 @@ struct rece_plan_s {
   // backward scratch (the backward reuses the forward's scratch from offset 0)
   size_t o_pk0, o_pv0, o_pk1, o_pv1, o_psc, o_dya;
   size_t scratch_bytes;
+  size_t scratch_fwd_bytes;   // what the forward pass alone uses of scratch
   // bucket variant: slots = (bucket, position) and (bucket, item) pairs
   int64_t sx, sy;     // n_b * b_x, n_b * b_y
   size_t o_R, o_Q, o_xmax;                                                                  // saved
@@ -248,6 +249,7 @@ static void plan_sce_layout(rece_plan_s* p) {
   p->o_snegs = sc.take((size_t)sx * k * 4);
   p->o_snegl = sc.take((size_t)sx * k * 4);
   p->o_stmp = sc.take((size_t)sx * 4);
+  p->scratch_fwd_bytes = sc.off;
   p->scratch_bytes = std::max(sc.off, plan_backward_scratch(p));
 }
 
@@ -504,6 +506,7 @@ rece_status rece_plan(const rece_config* cfg, rece_plan_t* out) {
   p->o_xs = sc.take((size_t)r * s * d * p->esize);
   p->o_ys = sc.take((size_t)r * C * d * p->esize);
   p->dedup_bits = dedup_hash_bits(r, k);
+  p->scratch_fwd_bytes = sc.off;
   p->scratch_bytes = std::max(sc.off, plan_backward_scratch(p));
   *out = p;
   return RECE_OK;
@@ -569,18 +572,12 @@ rece_status rece_workspace_bytes(rece_plan_t plan, size_t* scratch_bytes, size_t
   return RECE_OK;
 }
 
-rece_status rece_forward(rece_plan_t plan, void* stream, const void* X, const void* Y, const int32_t* pos,
-                         const void* B, void* scratch, void* saved, float* loss, float* loss_pp) {
-  if (!plan) return fail(RECE_ERR_INVALID_ARGUMENT, "plan is NULL");
-  if (!X || !Y || !pos || !B || !scratch || !saved || !loss)
-    return fail(RECE_ERR_INVALID_ARGUMENT, "NULL pointer argument");
-  if (!aligned16(X) || !aligned16(Y) || !aligned16(B) || !aligned16(scratch) || !aligned16(saved))
-    return fail(RECE_ERR_INVALID_ARGUMENT, "X, Y, B, scratch and saved must be 16-byte aligned");
-  const rece_plan_s& p = *plan;
+// The forward pass.  single: everything on `st` (no side stream, no events), for
+// callers that may create no HIP object.
+static rece_status forward_impl(const rece_plan_s& p, hipStream_t st, const void* X, const void* Y,
+                                const int32_t* pos, const void* B, char* sc, char* sv, float* loss, float* loss_pp,
+                                bool single) {
   const rece_config& c = p.cfg;
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  char* sv = static_cast<char*>(saved);
-  char* sc = static_cast<char*>(scratch);
   const int64_t s = c.s, C = c.C;
   const int d = c.d;
   uint32_t* counters = reinterpret_cast<uint32_t*>(sv + p.o_cnt);
@@ -590,7 +587,8 @@ rece_status rece_forward(rece_plan_t plan, void* stream, const void* X, const vo
   void* Bt = sc + p.o_bt;
 
   if (c.variant == RECE_VARIANT_SCE) return sce_forward(p, st, X, Y, pos, B, sc, sv, loss, loss_pp);
-  std::lock_guard<std::mutex> side_lock(p.side.mu);
+  std::unique_lock<std::mutex> side_lock(p.side.mu, std::defer_lock);
+  if (!single) side_lock.lock();
   uint32_t* und_n = reinterpret_cast<uint32_t*>(bnorm + c.rounds);   // cleared with the norms
   int32_t* und = reinterpret_cast<int32_t*>(sc + p.o_und);
   RECE_PHASE(RECE_PHASE_OTHER,
@@ -607,12 +605,18 @@ rece_status rece_forward(rece_plan_t plan, void* stream, const void* X, const vo
   // stream.  Events: fork[rounds] starts the side stream, fork[rounds + 1] marks
   // the position norms of round 0 (every chunk kernel reads them), fork[0] the end
   // of round 0's item chain, fork[rounds + 2] the end of the side stream.
-  const rece_status ss = ensure_side(p, c.rounds + 3);
-  if (ss != RECE_OK) return ss;
-  hipStream_t side = p.side.s;
+  hipStream_t side = st;
+  if (!single) {
+    const rece_status ss = ensure_side(p, c.rounds + 3);
+    if (ss != RECE_OK) return ss;
+    side = p.side.s;
+  }
+  // event record / wait between the two streams (nothing when single)
+  auto record = [&](int e, hipStream_t on) { return single ? hipSuccess : hipEventRecord(p.side.fork[e], on); };
+  auto wait = [&](hipStream_t on, int e) { return single ? hipSuccess : hipStreamWaitEvent(on, p.side.fork[e], 0); };
   int32_t* undy = reinterpret_cast<int32_t*>(sc + p.o_undy);
-  RECE_HIP(hipEventRecord(p.side.fork[c.rounds], st), "fork");
-  RECE_HIP(hipStreamWaitEvent(side, p.side.fork[c.rounds], 0), "fork");
+  RECE_HIP(record(c.rounds, st), "fork");
+  RECE_HIP(wait(side, c.rounds), "fork");
 
   auto xs_of = [&](int rho) { return sc + p.o_xs + (size_t)rho * s * d * p.esize; };
   auto ys_of = [&](int rho) { return sc + p.o_ys + (size_t)rho * C * d * p.esize; };
@@ -659,7 +663,7 @@ rece_status rece_forward(rece_plan_t plan, void* stream, const void* X, const vo
     RECE_PHASE(RECE_PHASE_PROJECT, launch_project_argmax(p.bf16, d, X, s, Bt, c.n_b, bnorm, p.beta_coef, bx,
                                    xnorm, nullptr, und, und_n, counters, st),
                "bucket positions");
-    RECE_HIP(hipEventRecord(p.side.fork[c.rounds + 1], st), "position norms");
+    RECE_HIP(record(c.rounds + 1, st), "position norms");
     RECE_PHASE(RECE_PHASE_SORT, launch_counting_sort(bx, nullptr, s, 0, p.nbits_b, sc + p.o_sort, px, nullptr, st),
                "sort positions");
     RECE_PHASE(RECE_PHASE_SORT, launch_gather_rows(X, px, s, d * p.esize, xs_of(0), st), "sorted positions");
@@ -678,7 +682,7 @@ rece_status rece_forward(rece_plan_t plan, void* stream, const void* X, const vo
                "sort items");
     RECE_PHASE(RECE_PHASE_SORT, launch_gather_rows(Y, py, C, d * p.esize, ys_of(rho), st), "sorted items");
     if (rho == 0) {
-      RECE_HIP(hipEventRecord(p.side.fork[0], side), "item chain done");
+      RECE_HIP(record(0, side), "item chain done");
       continue;
     }
     int32_t* bx = reinterpret_cast<int32_t*>(sv + p.o_bx) + (int64_t)rho * s;
@@ -689,18 +693,18 @@ rece_status rece_forward(rece_plan_t plan, void* stream, const void* X, const vo
     RECE_PHASE(RECE_PHASE_SORT, launch_counting_sort(bx, nullptr, s, 0, p.nbits_b, sc + p.o_sorty, px, nullptr, st),
                "sort positions");
     RECE_PHASE(RECE_PHASE_SORT, launch_gather_rows(X, px, s, d * p.esize, xs_of(rho), st), "sorted positions");
-    if (rho == 1) RECE_HIP(hipStreamWaitEvent(side, p.side.fork[c.rounds + 1], 0), "position norms");
+    if (rho == 1) RECE_HIP(wait(side, c.rounds + 1), "position norms");
     const SelectArgs a = select_args(rho);
     RECE_PHASE(RECE_PHASE_SELECT, launch_select(p.bf16, d, p.waves_sel, a, st), "chunk logits and top-k");
   }
-  RECE_HIP(hipEventRecord(p.side.fork[c.rounds + 2], side), "side stream done");
+  RECE_HIP(record(c.rounds + 2, side), "side stream done");
 
-  RECE_HIP(hipStreamWaitEvent(st, p.side.fork[0], 0), "join the first item chain");
+  RECE_HIP(wait(st, 0), "join the first item chain");
   {
     const SelectArgs a = select_args(0);
     RECE_PHASE(RECE_PHASE_SELECT, launch_select(p.bf16, d, p.waves_sel, a, st), "chunk logits and top-k");
   }
-  RECE_HIP(hipStreamWaitEvent(st, p.side.fork[c.rounds + 2], 0), "join the side stream");
+  RECE_HIP(wait(st, c.rounds + 2), "join the side stream");
   for (int rho = 1; rho < c.rounds && c.k > 0; ++rho) {
     DedupArgs dd{};
     dd.negs = reinterpret_cast<int32_t*>(sv + p.o_negs);
@@ -734,6 +738,42 @@ rece_status rece_forward(rece_plan_t plan, void* stream, const void* X, const vo
   RECE_PHASE(RECE_PHASE_LOSS, launch_ce(p.bf16, d, ce, loss, st), "loss");
   return RECE_OK;
 }
+
+static rece_status check_forward_args(rece_plan_t plan, const void* X, const void* Y, const int32_t* pos,
+                                      const void* B, const void* scratch, const void* saved, const float* loss) {
+  if (!plan) return fail(RECE_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (!X || !Y || !pos || !B || !scratch || !saved || !loss)
+    return fail(RECE_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  if (!aligned16(X) || !aligned16(Y) || !aligned16(B) || !aligned16(scratch) || !aligned16(saved))
+    return fail(RECE_ERR_INVALID_ARGUMENT, "X, Y, B, scratch and saved must be 16-byte aligned");
+  return RECE_OK;
+}
+
+rece_status rece_forward(rece_plan_t plan, void* stream, const void* X, const void* Y, const int32_t* pos,
+                         const void* B, void* scratch, void* saved, float* loss, float* loss_pp) {
+  const rece_status cs = check_forward_args(plan, X, Y, pos, B, scratch, saved, loss);
+  if (cs != RECE_OK) return cs;
+  return forward_impl(*plan, reinterpret_cast<hipStream_t>(stream), X, Y, pos, B, static_cast<char*>(scratch),
+                      static_cast<char*>(saved), loss, loss_pp, false);
+}
+
+}  // extern "C"
+
+namespace rece {
+size_t plan_forward_scratch_bytes(rece_plan_t plan) { return plan->scratch_fwd_bytes; }
+
+rece_status forward_single_stream(rece_plan_t plan, void* stream, const void* X, const void* Y, const int32_t* pos,
+                                  const void* B, void* scratch, void* saved, float* loss, float* loss_pp) {
+  const rece_status cs = check_forward_args(plan, X, Y, pos, B, scratch, saved, loss);
+  if (cs != RECE_OK) return cs;
+  return forward_impl(*plan, reinterpret_cast<hipStream_t>(stream), X, Y, pos, B, static_cast<char*>(scratch),
+                      static_cast<char*>(saved), loss, loss_pp, true);
+}
+
+rece_status set_last_error(rece_status st, const char* msg) { return fail(st, msg); }
+}  // namespace rece
+
+extern "C" {
 
 rece_status rece_backward(rece_plan_t plan, void* stream, const void* X, const void* Y, const int32_t* pos,
                           const float* dloss, const float* dloss_pp, void* scratch, const void* saved, float* dX,

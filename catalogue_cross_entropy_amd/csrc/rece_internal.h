@@ -209,6 +209,13 @@ struct MergeArgs {
   uint32_t* counters;
 };
 size_t merge_lds_bytes(int k);
+
+// Host side (rece_host.cpp), for entry points defined in other files.
+size_t plan_forward_scratch_bytes(rece_plan_t plan);      // scratch the forward pass alone uses
+// rece_forward with every launch on `stream` (no second stream, no events created).
+rece_status forward_single_stream(rece_plan_t plan, void* stream, const void* X, const void* Y, const int32_t* pos,
+                                  const void* B, void* scratch, void* saved, float* loss, float* loss_pp);
+rece_status set_last_error(rece_status st, const char* msg);   // sets rece_last_error(); returns st
 hipError_t launch_sce_merge(bool is_bf16, int d, const MergeArgs& a, hipStream_t st);
 
 }  // namespace rece

@@ -34,7 +34,8 @@
  *
  * Conventions for every entry point:
  *   - device pointers are caller-owned, contiguous, row-major and at least
- *     16-byte aligned; the library never allocates device memory;
+ *     16-byte aligned; the library never allocates device memory (its one
+ *     static scratch array aside, see rece_forward_static);
  *   - `stream` is a hipStream_t (NULL = the default stream); every call that
  *     takes a stream only enqueues work on it and returns without waiting,
  *     except rece_check, which waits for the stream;
@@ -141,6 +142,24 @@ rece_status rece_workspace_bytes(rece_plan_t plan, size_t* scratch_bytes, size_t
 rece_status rece_forward(rece_plan_t plan, void* stream, const void* X, const void* Y,
                          const int32_t* pos, const void* B, void* scratch, void* saved,
                          float* loss, float* loss_pp);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): rece_forward with its
+ * scratch memory taken from a static device array of the library
+ * (RECE_STATIC_SCRATCH_BYTES per GPU, held from the library's first use of that
+ * GPU until the process ends) instead of a caller buffer.  The caller still
+ * passes the inputs and the outputs (saved, loss, loss_pp; saved feeds
+ * rece_backward as usual).  Every launch goes on `stream`: no second stream or
+ * event is created, and no device memory is allocated or freed.  A plan whose
+ * forward pass needs more scratch than the array holds is rejected with
+ * RECE_ERR_WORKSPACE_TOO_SMALL.  Every call on one GPU shares that GPU's array,
+ * which keeps the last call's contents (the forward pass clears what it needs
+ * cleared): calls that overlap on one GPU race and must be serialised by the
+ * caller (one stream, or events).  Results equal rece_forward's. */
+#define RECE_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+rece_status rece_forward_static(rece_plan_t plan, void* stream, const void* X, const void* Y,
+                                const int32_t* pos, const void* B, void* saved, float* loss,
+                                float* loss_pp);
 
 /* Backward pass of the last rece_forward that wrote `saved` (same X, Y, pos):
  * RECE page, Section 3, Eq. 4 (softmax minus the one-hot of the positive)

@@ -175,3 +175,15 @@ def test_sce_plan_and_exports():
     assert sizes["union_ids"] == 256 * 16 * 4
     r = _plan(keep_stages=True)
     assert L.rece_export_bytes(r._h, rece.STAGES["sce_rows"], ctypes.byref(nb)) == 0 and nb.value == 0
+
+
+def test_static_forward_rejects_plans_beyond_its_array():
+    """rece_forward_static checks the plan's forward scratch against the static
+    array before any GPU call: the ten-million-item plan needs gigabytes."""
+    from rece_inputs import WORKLOADS
+    w = WORKLOADS["tenmillion"]
+    p = rece.Plan(w.s, w.C, w.d, w.n_b, w.n_c, w.k, w.rounds, dtype=w.dtype)
+    L = rece.lib()
+    assert L.rece_forward_static(p._h, None, 16, 16, 16, 16, 16, 16, None) == 3
+    assert "static scratch" in L.rece_last_error().decode()
+    assert L.rece_forward_static(None, None, 16, 16, 16, 16, 16, 16, None) == 1
