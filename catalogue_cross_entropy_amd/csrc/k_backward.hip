@@ -197,71 +197,134 @@ __device__ __forceinline__ bool pair_at(const PairSrc& a, int64_t t, int& key, i
   }
 }
 
-// Per segment of seg_len records: a histogram of the digit (key >> shift) & mask.
+// Each pass is one stable counting sort on a digit of at most 8 bits, over tiles
+// of RS_TILE records (one 256-thread workgroup each):
+//   k_pair_hist     per tile, the count of every digit -> counts[digit][tile];
+//   (an exclusive scan of counts in (digit, tile) order: every (digit, tile) gets
+//    its first output slot);
+//   k_pair_scatter  per tile: the records are ranked in input order (each wave
+//                   takes 64 consecutive records at a time; lanes with equal
+//                   digits find each other with one ballot per digit bit; the
+//                   per-group digit counts are scanned across the tile's groups
+//                   in LDS), placed in LDS in digit order, and written out from
+//                   there so that consecutive lanes write consecutive slots.
+constexpr int RS_THREADS = 256;
+constexpr int RS_GROUPS_PER_WAVE = 16;
+constexpr int RS_GROUPS = 4 * RS_GROUPS_PER_WAVE;   // groups of 64 records per tile
+constexpr int RS_TILE = RS_GROUPS * WAVE;           // 4096 records
+constexpr int RS_BINS = 256;
+
 template <bool FIRST>
-__global__ __launch_bounds__(256) void k_pair_hist(PairSrc a, int64_t n_max, int shift, int nbits, int seg_len,
-                                                   int nseg, uint32_t* __restrict__ counts) {
-  extern __shared__ uint32_t hist[];
+__global__ __launch_bounds__(RS_THREADS) void k_pair_hist(PairSrc a, int64_t n_max, int shift, int nbits, int ntiles,
+                                                          uint32_t* __restrict__ counts) {
+  __shared__ uint32_t hist[RS_BINS];
   const int nbins = 1 << nbits;
   const uint32_t mask = (uint32_t)nbins - 1u;
-  for (int b = threadIdx.x; b < nbins; b += 256) hist[b] = 0u;
+  hist[threadIdx.x] = 0u;
   __syncthreads();
   const int64_t n = FIRST ? n_max : (int64_t)*a.nin;
-  const int64_t t0 = (int64_t)blockIdx.x * seg_len;
-  const int64_t t1 = min(n, t0 + seg_len);
-  for (int64_t t = t0 + threadIdx.x; t < t1; t += 256) {
-    int key, val;
-    if (pair_at<FIRST>(a, t, key, val)) atomicAdd(&hist[((uint32_t)key >> shift) & mask], 1u);
+  const int64_t t0 = (int64_t)blockIdx.x * RS_TILE;
+  int dig[RS_TILE / RS_THREADS];
+#pragma unroll
+  for (int u = 0; u < RS_TILE / RS_THREADS; ++u) {
+    const int64_t t = t0 + u * RS_THREADS + threadIdx.x;
+    int key = 0, val = 0;
+    dig[u] = (t < n && pair_at<FIRST>(a, t, key, val)) ? (int)(((uint32_t)key >> shift) & mask) : -1;
   }
+#pragma unroll
+  for (int u = 0; u < RS_TILE / RS_THREADS; ++u)
+    if (dig[u] >= 0) atomicAdd(&hist[dig[u]], 1u);
   __syncthreads();
-  for (int b = threadIdx.x; b < nbins; b += 256) counts[(int64_t)b * nseg + blockIdx.x] = hist[b];
-  if (blockIdx.x == 0 && threadIdx.x == 0) counts[(int64_t)nbins * nseg] = 0u;   // becomes the total
+  if ((int)threadIdx.x < nbins) counts[(int64_t)threadIdx.x * ntiles + blockIdx.x] = hist[threadIdx.x];
+  if (blockIdx.x == 0 && threadIdx.x == 0) counts[(int64_t)nbins * ntiles] = 0u;   // becomes the total
 }
 
-// One wave per segment walks its records in order, 64 at a time; lanes with
-// equal digits find each other with one ballot per digit bit and take ranks in
-// lane order, so equal digits keep their input order (stable).
 template <bool FIRST>
-__global__ __launch_bounds__(256) void k_pair_scatter(PairSrc a, int64_t n_max, int shift, int nbits, int seg_len,
-                                                      int nseg, const uint32_t* __restrict__ offs,
-                                                      int32_t* __restrict__ kout, int32_t* __restrict__ vout,
-                                                      uint32_t* __restrict__ ntot) {
-  extern __shared__ uint32_t ctr_all[];
+__global__ __launch_bounds__(RS_THREADS) void k_pair_scatter(PairSrc a, int64_t n_max, int shift, int nbits,
+                                                             int ntiles, const uint32_t* __restrict__ offs,
+                                                             int32_t* __restrict__ kout, int32_t* __restrict__ vout,
+                                                             uint32_t* __restrict__ ntot) {
+  __shared__ uint16_t gcnt[RS_GROUPS][RS_BINS];   // per group: count, then prefix over earlier groups
+  __shared__ uint32_t dstart[RS_BINS];            // first local slot of each digit
+  __shared__ uint32_t gbase[RS_BINS];             // first global slot of each digit (this tile)
+  __shared__ uint32_t wsum[4];
+  __shared__ int32_t skey[RS_TILE];
+  __shared__ int32_t sval[RS_TILE];
   const int nbins = 1 << nbits;
   const uint32_t mask = (uint32_t)nbins - 1u;
-  const int w = threadIdx.x >> 6, l = lane_id();
-  if (blockIdx.x == 0 && threadIdx.x == 0) *ntot = offs[(int64_t)nbins * nseg];
-  const int64_t seg = (int64_t)blockIdx.x * 4 + w;
-  if (seg >= nseg) return;   // whole wave leaves; no block barrier below
-  uint32_t* ctr = ctr_all + (int64_t)w * nbins;
-  for (int b = l; b < nbins; b += WAVE) ctr[b] = offs[(int64_t)b * nseg + seg];
-  wave_sync();
+  const int tid = threadIdx.x, w = tid >> 6, l = lane_id();
+  if (blockIdx.x == 0 && tid == 0) *ntot = offs[(int64_t)nbins * ntiles];
+  {
+    uint32_t* g32 = reinterpret_cast<uint32_t*>(&gcnt[0][0]);
+    for (int q = tid; q < RS_GROUPS * RS_BINS / 2; q += RS_THREADS) g32[q] = 0u;
+  }
+  gbase[tid] = tid < nbins ? offs[(int64_t)tid * ntiles + blockIdx.x] : 0u;
+  __syncthreads();
   const int64_t n = FIRST ? n_max : (int64_t)*a.nin;
-  const int64_t t0 = seg * seg_len;
-  const int64_t t1 = min(n, t0 + seg_len);
-  for (int64_t tb = t0; tb < t1; tb += WAVE) {
-    const int64_t t = tb + l;
+  const int64_t t0 = (int64_t)blockIdx.x * RS_TILE;
+  // rank within each group of 64 consecutive records (wave w: groups 16w .. 16w + 15)
+  int rkey[RS_GROUPS_PER_WAVE], rval[RS_GROUPS_PER_WAVE], rinfo[RS_GROUPS_PER_WAVE];   // info: digit | rank << 8, -1 invalid
+#pragma unroll
+  for (int it = 0; it < RS_GROUPS_PER_WAVE; ++it) {
+    const int g = w * RS_GROUPS_PER_WAVE + it;
+    const int64_t t = t0 + (int64_t)g * WAVE + l;
     int key = 0, val = 0;
-    const bool valid = t < t1 && pair_at<FIRST>(a, t, key, val);
-    const int dig = valid ? (int)(((uint32_t)key >> shift) & mask) : 0;
+    const bool valid = t < n && pair_at<FIRST>(a, t, key, val);
+    const int dg = valid ? (int)(((uint32_t)key >> shift) & mask) : 0;
     uint64_t same = ballot(valid);
     for (int bit = 0; bit < nbits; ++bit) {
-      const bool on = (dig >> bit) & 1;
+      const bool on = (dg >> bit) & 1;
       const uint64_t bm = ballot(on);
       same &= on ? bm : ~bm;
     }
     const int rank = popc(same & lanemask_lt());
-    const int cnt = popc(same);
-    uint32_t base = 0;
-    if (valid) base = ctr[dig];
-    wave_sync();
-    if (valid && rank == 0) ctr[dig] = base + (uint32_t)cnt;
-    wave_sync();
-    if (valid) {
-      const uint32_t slot = base + (uint32_t)rank;
-      kout[slot] = key;
-      vout[slot] = val;
+    if (valid && rank == 0) gcnt[g][dg] = (uint16_t)popc(same);
+    rkey[it] = key;
+    rval[it] = val;
+    rinfo[it] = valid ? (dg | (rank << 8)) : -1;
+  }
+  __syncthreads();
+  // per digit: exclusive prefix over the groups, and the tile total
+  uint32_t tot = 0;
+  if (tid < nbins) {
+    for (int g = 0; g < RS_GROUPS; ++g) {
+      const uint32_t c = gcnt[g][tid];
+      gcnt[g][tid] = (uint16_t)tot;
+      tot += c;
     }
+  }
+  // exclusive scan of the totals over the digits
+  {
+    uint32_t x = tot;
+#pragma unroll
+    for (int o = 1; o < WAVE; o <<= 1) {
+      const uint32_t y = __shfl_up(x, o);
+      if (l >= o) x += y;
+    }
+    if (l == WAVE - 1) wsum[w] = x;
+    __syncthreads();
+    uint32_t pre = 0;
+    for (int q = 0; q < w; ++q) pre += wsum[q];
+    dstart[tid] = pre + x - tot;
+  }
+  __syncthreads();
+  const uint32_t nvalid = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+#pragma unroll
+  for (int it = 0; it < RS_GROUPS_PER_WAVE; ++it) {
+    if (rinfo[it] < 0) continue;
+    const int g = w * RS_GROUPS_PER_WAVE + it;
+    const int dg = rinfo[it] & 0xFF;
+    const uint32_t local = dstart[dg] + gcnt[g][dg] + (uint32_t)(rinfo[it] >> 8);
+    skey[local] = rkey[it];
+    sval[local] = rval[it];
+  }
+  __syncthreads();
+  for (uint32_t q = tid; q < nvalid; q += RS_THREADS) {
+    const int key = skey[q];
+    const int dg = (int)(((uint32_t)key >> shift) & mask);
+    const uint32_t slot = gbase[dg] + (q - dstart[dg]);
+    kout[slot] = key;
+    vout[slot] = sval[q];
   }
 }
 
@@ -437,17 +500,12 @@ __global__ __launch_bounds__(256) void k_dy_combine(float* __restrict__ dY, cons
 }
 
 // ------------------------------------------------------------------ launchers
-static int64_t pair_seg_len(int64_t n) {
-  int64_t L = ((n / 256) + 63) / 64 * 64;
-  return L < 256 ? 256 : (L > 4096 ? 4096 : L);
-}
-
 PairSortGeom pair_sort_geom(int64_t E, int64_t C) {
   PairSortGeom g{};
   g.E = E;
   int kb = 1;
   while (((int64_t)1 << kb) < C) ++kb;
-  g.npass = (kb + 11) / 12;
+  g.npass = (kb + 7) / 8;
   int shift = 0;
   for (int pss = 0; pss < g.npass; ++pss) {
     const int left = g.npass - pss;
@@ -456,11 +514,9 @@ PairSortGeom pair_sort_geom(int64_t E, int64_t C) {
     g.bits[pss] = b;
     shift += b;
   }
-  g.seg_len = pair_seg_len(E);
-  g.nseg = (E + g.seg_len - 1) / g.seg_len;
-  int maxbits = 0;
-  for (int pss = 0; pss < g.npass; ++pss) maxbits = g.bits[pss] > maxbits ? g.bits[pss] : maxbits;
-  g.count_words = ((int64_t)1 << maxbits) * g.nseg + 1;
+  g.seg_len = RS_TILE;
+  g.nseg = (E + RS_TILE - 1) / RS_TILE;
+  g.count_words = (int64_t)RS_BINS * g.nseg + 1;
   const int64_t nb = (g.count_words + 4095) / 4096;
   g.scratch_bytes = (size_t)(g.count_words + nb + 64 + 8) * 4;
   return g;
@@ -470,15 +526,14 @@ template <bool FIRST>
 static hipError_t pair_pass(const PairSrc& a, const PairSortGeom& g, int pss, uint32_t* counts, uint32_t* bsum,
                             int32_t* kout, int32_t* vout, uint32_t* ntot, hipStream_t st) {
   const int nbits = g.bits[pss], nbins = 1 << nbits;
-  hipLaunchKernelGGL(k_pair_hist<FIRST>, dim3((unsigned)g.nseg), dim3(256), nbins * sizeof(uint32_t), st, a, g.E,
-                     g.shift[pss], nbits, (int)g.seg_len, (int)g.nseg, counts);
+  hipLaunchKernelGGL(k_pair_hist<FIRST>, dim3((unsigned)g.nseg), dim3(RS_THREADS), 0, st, a, g.E, g.shift[pss],
+                     nbits, (int)g.nseg, counts);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = launch_exclusive_scan(counts, (int64_t)nbins * g.nseg + 1, bsum, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_pair_scatter<FIRST>, dim3((unsigned)((g.nseg + 3) / 4)), dim3(256),
-                     4 * nbins * sizeof(uint32_t), st, a, g.E, g.shift[pss], nbits, (int)g.seg_len, (int)g.nseg,
-                     counts, kout, vout, ntot);
+  hipLaunchKernelGGL(k_pair_scatter<FIRST>, dim3((unsigned)g.nseg), dim3(RS_THREADS), 0, st, a, g.E, g.shift[pss],
+                     nbits, (int)g.nseg, counts, kout, vout, ntot);
   return hipGetLastError();
 }
 
