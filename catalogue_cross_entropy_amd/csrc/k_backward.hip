@@ -26,6 +26,16 @@ __device__ __forceinline__ float gbar_of(const BwdArgs& p, int64_t i) {
   return p.dloss_pp ? p.dloss_pp[i] : p.dloss[0] / (float)p.s;
 }
 
+// Per position: {lse, upstream gradient, coefficient of the positive (Eq. 4: its
+// softmax share minus one, times the upstream gradient), 0}, read by both sides.
+__global__ __launch_bounds__(256) void k_pos_coef(BwdArgs p, float4* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= p.s) return;
+  const float lse = p.lse[i];
+  const float gb = gbar_of(p, i);
+  out[i] = float4{lse, gb, (expf(p.lpos[i] - lse) - 1.0f) * gb, 0.0f};
+}
+
 // Sixteen bytes of a row as floats.
 __device__ __forceinline__ void cvt16f(const u32x4 u, float (&v)[8]) {
 #pragma unroll
@@ -67,8 +77,8 @@ __global__ __launch_bounds__(256) void k_dx_lists(BwdArgs p) {
   const int q = l / LPR, sub = l % LPR;
   float x[EPL];
   load16f(X + i * D + sub * EPL, x);
-  const float lse = p.lse[i];
-  const float gb = gbar_of(p, i);
+  const float4 pci = reinterpret_cast<const float4*>(p.pcoef)[i];
+  const float lse = pci.x, gb = pci.y;
   float acc[EPL];
 #pragma unroll
   for (int t = 0; t < EPL; ++t) acc[t] = 0.0f;
@@ -113,7 +123,7 @@ __global__ __launch_bounds__(256) void k_dx_lists(BwdArgs p) {
   if (q == 0) {
     const int pj = p.pos[i];
     const int pc = pj < 0 ? 0 : (pj >= p.C ? (int)(p.C - 1) : pj);
-    const float gpos = (expf(p.lpos[i] - lse) - 1.0f) * gb;
+    const float gpos = pci.z;
     float yp[EPL];
     load16f(Y + (int64_t)pc * D + sub * EPL, yp);
 #pragma unroll
@@ -178,22 +188,25 @@ struct PairSrc {
   int k;
 };
 
+// Record t of the pass's input (t < n), loaded without branches so that the loads
+// of many records can be in flight at once: addresses are clamped into range and
+// the choice between a list entry and a positive is a select.  n >= 1.
 template <bool FIRST>
-__device__ __forceinline__ bool pair_at(const PairSrc& a, int64_t t, int& key, int& val) {
+__device__ __forceinline__ bool pair_at(const PairSrc& a, int64_t t, int64_t n, int& key, int& val) {
+  const int64_t tc = t < n ? t : n - 1;
   if constexpr (FIRST) {
-    if (t < a.nl) {
-      key = a.negs[t];
-      val = (int)(((uint32_t)t / (uint32_t)a.k) % (uint32_t)a.s);
-    } else {
-      const int64_t i = t - a.nl;
-      key = a.pos[i];
-      val = (int)i | (int)0x80000000u;
-    }
-    return key >= 0 && key < a.C;
+    const bool isl = tc < a.nl;
+    const int64_t il = isl ? tc : 0;
+    const int64_t ip = isl ? 0 : tc - a.nl;
+    const int kn = a.negs[il];
+    const int kp = a.pos[ip];
+    key = isl ? kn : kp;
+    val = isl ? (int)(((uint32_t)tc / (uint32_t)a.k) % (uint32_t)a.s) : ((int)ip | (int)0x80000000u);
+    return t < n && key >= 0 && key < a.C;
   } else {
-    key = a.kin[t];
-    val = a.vin[t];
-    return true;
+    key = a.kin[tc];
+    val = a.vin[tc];
+    return t < n;
   }
 }
 
@@ -203,11 +216,12 @@ __device__ __forceinline__ bool pair_at(const PairSrc& a, int64_t t, int& key, i
 //   (an exclusive scan of counts in (digit, tile) order: every (digit, tile) gets
 //    its first output slot);
 //   k_pair_scatter  per tile: the records are ranked in input order (each wave
-//                   takes 64 consecutive records at a time; lanes with equal
-//                   digits find each other with one ballot per digit bit; the
-//                   per-group digit counts are scanned across the tile's groups
-//                   in LDS), placed in LDS in digit order, and written out from
-//                   there so that consecutive lanes write consecutive slots.
+//                   takes a quarter of the tile, 64 consecutive records at a time;
+//                   lanes with equal digits find each other with one ballot per
+//                   digit bit and advance the wave's running digit counts; the four
+//                   waves' counts are then combined in order), placed in LDS in
+//                   digit order, and written out from there so that consecutive
+//                   lanes write consecutive slots.
 constexpr int RS_THREADS = 256;
 constexpr int RS_GROUPS_PER_WAVE = 16;
 constexpr int RS_GROUPS = 4 * RS_GROUPS_PER_WAVE;   // groups of 64 records per tile
@@ -225,11 +239,17 @@ __global__ __launch_bounds__(RS_THREADS) void k_pair_hist(PairSrc a, int64_t n_m
   const int64_t n = FIRST ? n_max : (int64_t)*a.nin;
   const int64_t t0 = (int64_t)blockIdx.x * RS_TILE;
   int dig[RS_TILE / RS_THREADS];
+  if (n > 0) {
 #pragma unroll
-  for (int u = 0; u < RS_TILE / RS_THREADS; ++u) {
-    const int64_t t = t0 + u * RS_THREADS + threadIdx.x;
-    int key = 0, val = 0;
-    dig[u] = (t < n && pair_at<FIRST>(a, t, key, val)) ? (int)(((uint32_t)key >> shift) & mask) : -1;
+    for (int u = 0; u < RS_TILE / RS_THREADS; ++u) {
+      const int64_t t = t0 + u * RS_THREADS + threadIdx.x;
+      int key, val;
+      const bool ok = pair_at<FIRST>(a, t, n, key, val);
+      dig[u] = ok ? (int)(((uint32_t)key >> shift) & mask) : -1;
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < RS_TILE / RS_THREADS; ++u) dig[u] = -1;
   }
 #pragma unroll
   for (int u = 0; u < RS_TILE / RS_THREADS; ++u)
@@ -244,9 +264,9 @@ __global__ __launch_bounds__(RS_THREADS) void k_pair_scatter(PairSrc a, int64_t 
                                                              int ntiles, const uint32_t* __restrict__ offs,
                                                              int32_t* __restrict__ kout, int32_t* __restrict__ vout,
                                                              uint32_t* __restrict__ ntot) {
-  __shared__ uint16_t gcnt[RS_GROUPS][RS_BINS];   // per group: count, then prefix over earlier groups
-  __shared__ uint32_t dstart[RS_BINS];            // first local slot of each digit
-  __shared__ uint32_t gbase[RS_BINS];             // first global slot of each digit (this tile)
+  __shared__ uint32_t wcnt[4][RS_BINS];   // per wave: running count of each digit, then its prefix over waves
+  __shared__ uint32_t dstart[RS_BINS];    // first local slot of each digit
+  __shared__ uint32_t gbase[RS_BINS];     // first global slot of each digit (this tile)
   __shared__ uint32_t wsum[4];
   __shared__ int32_t skey[RS_TILE];
   __shared__ int32_t sval[RS_TILE];
@@ -254,23 +274,29 @@ __global__ __launch_bounds__(RS_THREADS) void k_pair_scatter(PairSrc a, int64_t 
   const uint32_t mask = (uint32_t)nbins - 1u;
   const int tid = threadIdx.x, w = tid >> 6, l = lane_id();
   if (blockIdx.x == 0 && tid == 0) *ntot = offs[(int64_t)nbins * ntiles];
-  {
-    uint32_t* g32 = reinterpret_cast<uint32_t*>(&gcnt[0][0]);
-    for (int q = tid; q < RS_GROUPS * RS_BINS / 2; q += RS_THREADS) g32[q] = 0u;
-  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) wcnt[q][tid] = 0u;
   gbase[tid] = tid < nbins ? offs[(int64_t)tid * ntiles + blockIdx.x] : 0u;
-  __syncthreads();
   const int64_t n = FIRST ? n_max : (int64_t)*a.nin;
   const int64_t t0 = (int64_t)blockIdx.x * RS_TILE;
-  // rank within each group of 64 consecutive records (wave w: groups 16w .. 16w + 15)
+  // wave w ranks records 1024 w .. 1024 w + 1023 of the tile, 64 at a time in input
+  // order, against its own running digit counts
   int rkey[RS_GROUPS_PER_WAVE], rval[RS_GROUPS_PER_WAVE], rinfo[RS_GROUPS_PER_WAVE];   // info: digit | rank << 8, -1 invalid
+  bool rok[RS_GROUPS_PER_WAVE];
+#pragma unroll
+  for (int it = 0; it < RS_GROUPS_PER_WAVE; ++it) rkey[it] = rval[it] = 0;
+  // all the wave's records first (every load in flight), then the ranks
 #pragma unroll
   for (int it = 0; it < RS_GROUPS_PER_WAVE; ++it) {
-    const int g = w * RS_GROUPS_PER_WAVE + it;
-    const int64_t t = t0 + (int64_t)g * WAVE + l;
-    int key = 0, val = 0;
-    const bool valid = t < n && pair_at<FIRST>(a, t, key, val);
-    const int dg = valid ? (int)(((uint32_t)key >> shift) & mask) : 0;
+    const int64_t t = t0 + (int64_t)(w * RS_GROUPS_PER_WAVE + it) * WAVE + l;
+    rok[it] = n > 0 && pair_at<FIRST>(a, t, n > 0 ? n : 1, rkey[it], rval[it]);
+  }
+  __syncthreads();   // counters cleared
+  uint32_t* ctr = wcnt[w];
+#pragma unroll
+  for (int it = 0; it < RS_GROUPS_PER_WAVE; ++it) {
+    const bool valid = rok[it];
+    const int dg = valid ? (int)(((uint32_t)rkey[it] >> shift) & mask) : 0;
     uint64_t same = ballot(valid);
     for (int bit = 0; bit < nbits; ++bit) {
       const bool on = (dg >> bit) & 1;
@@ -278,22 +304,25 @@ __global__ __launch_bounds__(RS_THREADS) void k_pair_scatter(PairSrc a, int64_t 
       same &= on ? bm : ~bm;
     }
     const int rank = popc(same & lanemask_lt());
-    if (valid && rank == 0) gcnt[g][dg] = (uint16_t)popc(same);
-    rkey[it] = key;
-    rval[it] = val;
-    rinfo[it] = valid ? (dg | (rank << 8)) : -1;
+    uint32_t base = 0;
+    if (valid) base = ctr[dg];
+    wave_sync();
+    if (valid && rank == 0) ctr[dg] = base + (uint32_t)popc(same);
+    wave_sync();
+    rinfo[it] = valid ? (dg | (int)((base + (uint32_t)rank) << 8)) : -1;
   }
   __syncthreads();
-  // per digit: exclusive prefix over the groups, and the tile total
+  // per digit: prefix over the waves and the tile total; then an exclusive scan of
+  // the totals over the digits
   uint32_t tot = 0;
   if (tid < nbins) {
-    for (int g = 0; g < RS_GROUPS; ++g) {
-      const uint32_t c = gcnt[g][tid];
-      gcnt[g][tid] = (uint16_t)tot;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t c = wcnt[q][tid];
+      wcnt[q][tid] = tot;
       tot += c;
     }
   }
-  // exclusive scan of the totals over the digits
   {
     uint32_t x = tot;
 #pragma unroll
@@ -312,9 +341,8 @@ __global__ __launch_bounds__(RS_THREADS) void k_pair_scatter(PairSrc a, int64_t 
 #pragma unroll
   for (int it = 0; it < RS_GROUPS_PER_WAVE; ++it) {
     if (rinfo[it] < 0) continue;
-    const int g = w * RS_GROUPS_PER_WAVE + it;
     const int dg = rinfo[it] & 0xFF;
-    const uint32_t local = dstart[dg] + gcnt[g][dg] + (uint32_t)(rinfo[it] >> 8);
+    const uint32_t local = dstart[dg] + wcnt[w][dg] + ((uint32_t)rinfo[it] >> 8);
     skey[local] = rkey[it];
     sval[local] = rval[it];
   }
@@ -351,8 +379,8 @@ __device__ __forceinline__ void store_row(float* dst, const float (&v)[EPL]) {
 
 // One lane group (LPR lanes, 16 bytes of a row each) per sub-piece of DY_SUB sorted
 // pairs.  For each pair (j, i): l = x_i . y_j (float32, the same lane split and
-// order as k_dx_lists), g = gbar_i exp(l - lse_i), or (exp(lpos_i - lse_i) - 1)
-// gbar_i for a positive record, summed as g x_i per item in pair order.  An item
+// order as k_dx_lists), g = gbar_i exp(l - lse_i), or the position's positive
+// coefficient for a positive record, summed as g x_i per item in pair order.  An item
 // wholly inside the sub-piece is written to dY here; an item continuing from the
 // previous or into the next sub-piece leaves a partial row for k_dy_combine.  The
 // items with no pair between two consecutive keys get zero rows from the sub-piece
@@ -386,7 +414,7 @@ __global__ __launch_bounds__(256) void k_dy_pieces(BwdArgs p, const int32_t* __r
   }
   const int prev_key = t0 > 0 ? K[t0 - 1] : -1;
   const int next_key = t1 < n ? K[t1] : (int)C;   // C: no later key
-  const float gscale = p.dloss_pp ? 0.0f : p.dloss[0] / (float)p.s;
+  const float4* __restrict__ PC = reinterpret_cast<const float4*>(p.pcoef);
   int cur = -1;
   int64_t run_start = t0;
   int flags = 0, head_item = -1, tail_item = -1;
@@ -414,27 +442,41 @@ __global__ __launch_bounds__(256) void k_dy_pieces(BwdArgs p, const int32_t* __r
       flags |= 4;
     }
   };
-
-  for (int64_t tb = t0; tb < t1; tb += UNR) {
-    int key[UNR], val[UNR];
-    u32x4 xr[UNR], yr[UNR];
-    float lse[UNR], gb[UNR], lp[UNR];
+  // keys and values of the batch at tb (key -1 past the sub-piece; addresses clamped)
+  auto load_kv = [&](int64_t tb, int (&kk)[UNR], int (&vv)[UNR]) {
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const int64_t t = tb + u;
-      if (t < t1) {
-        key[u] = K[t];
-        val[u] = V[t];
-        const int64_t i = val[u] & 0x7FFFFFFF;
-        xr[u] = *reinterpret_cast<const u32x4*>(X + i * D + sub * EPL);
-        yr[u] = *reinterpret_cast<const u32x4*>(Y + (int64_t)key[u] * D + sub * EPL);
-        lse[u] = p.lse[i];
-        gb[u] = p.dloss_pp ? p.dloss_pp[i] : gscale;
-        lp[u] = p.lpos[i];
-      } else {
-        key[u] = -1;
-      }
+      const int64_t tc = t < t1 ? t : t1 - 1;
+      kk[u] = K[tc];
+      vv[u] = V[tc];
+      if (t >= t1) kk[u] = -1;
     }
+  };
+
+  // Pipelined: the rows and coefficients of batch b are requested before the keys
+  // and values of batch b + 1, which then arrive while batch b is summed.  An item
+  // row is fetched only for a record whose key differs from the one before it.
+  int kn[UNR], vn[UNR];
+  load_kv(t0, kn, vn);
+  int ykey = -1;
+  u32x4 ycur = u32x4{0u, 0u, 0u, 0u};
+  for (int64_t tb = t0; tb < t1; tb += UNR) {
+    int key[UNR], val[UNR];
+    u32x4 xr[UNR], yr[UNR];
+    float4 pc[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      key[u] = kn[u];
+      val[u] = vn[u];
+      const int64_t i = key[u] >= 0 ? (int64_t)(val[u] & 0x7FFFFFFF) : 0;
+      xr[u] = *reinterpret_cast<const u32x4*>(X + i * D + sub * EPL);
+      pc[u] = PC[i];
+      const int kprev = u == 0 ? ykey : key[u - 1];
+      yr[u] = u32x4{0u, 0u, 0u, 0u};
+      if (key[u] >= 0 && key[u] != kprev) yr[u] = *reinterpret_cast<const u32x4*>(Y + (int64_t)key[u] * D + sub * EPL);
+    }
+    load_kv(tb + UNR, kn, vn);
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       if (key[u] < 0) break;
@@ -450,15 +492,19 @@ __global__ __launch_bounds__(256) void k_dy_pieces(BwdArgs p, const int32_t* __r
 #pragma unroll
         for (int t = 0; t < EPL; ++t) acc[t] = 0.0f;
       }
+      if (key[u] != ykey) {
+        ycur = yr[u];
+        ykey = key[u];
+      }
       float x[EPL], y[EPL];
       cvt16f(xr[u], x);
-      cvt16f(yr[u], y);
+      cvt16f(ycur, y);
       float dot = 0.0f;
 #pragma unroll
       for (int t = 0; t < EPL; ++t) dot = fmaf(x[t], y[t], dot);
 #pragma unroll
       for (int o = 1; o < LPR; o <<= 1) dot += __shfl_xor(dot, o);
-      const float g = val[u] < 0 ? (expf(lp[u] - lse[u]) - 1.0f) * gb[u] : __expf(dot - lse[u]) * gb[u];
+      const float g = val[u] < 0 ? pc[u].z : __expf(dot - pc[u].x) * pc[u].y;
 #pragma unroll
       for (int t = 0; t < EPL; ++t) acc[t] = fmaf(g, x[t], acc[t]);
     }
@@ -617,6 +663,13 @@ hipError_t launch_dy(bool bf16v, int d, const BwdArgs& a, const int32_t* K, cons
   }
 #undef RECE_DY
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_pos_coef(const BwdArgs& a, float* out, hipStream_t st) {
+  if (a.s == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_pos_coef, dim3((unsigned)((a.s + 255) / 256)), dim3(256), 0, st, a,
+                     reinterpret_cast<float4*>(out));
+  return hipGetLastError();
 }
 
 hipError_t launch_dx_lists(bool bf16v, int d, const BwdArgs& a, hipStream_t st) {

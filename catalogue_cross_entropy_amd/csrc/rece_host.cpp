@@ -107,7 +107,7 @@ struct rece_plan_s {
   // forward scratch
   size_t o_bt, o_bnorm, o_und, o_undy, o_sorty, o_sort, o_part, o_negl, o_xs, o_ys;
   // backward scratch (the backward reuses the forward's scratch from offset 0)
-  size_t o_pk0, o_pv0, o_pk1, o_pv1, o_psc, o_dya;
+  size_t o_pk0, o_pv0, o_pk1, o_pv1, o_psc, o_dya, o_pcoef;
   size_t scratch_bytes;
   size_t scratch_fwd_bytes;   // what the forward pass alone uses of scratch
   // bucket variant: slots = (bucket, position) and (bucket, item) pairs
@@ -194,6 +194,7 @@ static size_t plan_backward_scratch(rece_plan_s* p) {
   p->o_pv1 = sc.take((size_t)p->npairs * 4);
   p->o_psc = sc.take(p->pg.scratch_bytes);
   p->o_dya = sc.take(dy_area_bytes(p->npairs, c.d));
+  p->o_pcoef = sc.take((size_t)c.s * 16);
   return sc.off;
 }
 
@@ -807,6 +808,9 @@ rece_status rece_backward(rece_plan_t plan, void* stream, const void* X, const v
   b.dloss_pp = dloss_pp;
   b.dX = dX;
   b.dY = dY;
+  b.pcoef = reinterpret_cast<const float*>(sc + p.o_pcoef);
+  RECE_PHASE(RECE_PHASE_OTHER, launch_pos_coef(b, reinterpret_cast<float*>(sc + p.o_pcoef), st),
+             "per-position coefficients");
   // dY (the sort of the pairs by item, then the per-item sums) runs on the side
   // stream while dX runs on the caller's stream; the caller's stream then waits.
   const rece_status ss = ensure_side(p, 1);

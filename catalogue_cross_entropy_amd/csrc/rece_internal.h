@@ -97,6 +97,7 @@ struct BwdArgs {
   const float* lpos;          // [s]
   const float* dloss;         // [1]
   const float* dloss_pp;      // [s] or nullptr
+  const float* pcoef;         // [s][4]: lse, upstream gradient, positive coefficient, 0 (launch_pos_coef)
   float* dX;                  // [s][d]
   float* dY;                  // [C][d]
 };
@@ -138,6 +139,8 @@ hipError_t launch_ce(bool is_bf16, int d, const CeArgs& a, float* loss, hipStrea
 // ids (0: too many for LDS, the kernel scans the lists instead).
 int dedup_hash_bits(int rounds, int k);
 hipError_t launch_round_dedup(const DedupArgs& a, hipStream_t st);
+// out[s][4] = {lse, upstream gradient, positive coefficient, 0} per position (read by dX and dY).
+hipError_t launch_pos_coef(const BwdArgs& a, float* out, hipStream_t st);
 // dX of every position from the kept lists of all rounds plus the positive term
 // (writes all s rows of dX).
 hipError_t launch_dx_lists(bool is_bf16, int d, const BwdArgs& a, hipStream_t st);
