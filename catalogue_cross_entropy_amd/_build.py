@@ -9,6 +9,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(os.path.dirname(PKG), "_build")
 LIB = os.path.join(PKG, "librece.so")
+PEAKS_SRC = os.path.join(CSRC, "probes", "peaks.hip")
+PEAKS_LIB = os.path.join(PKG, "libpeaks.so")
 ARCH = "gfx950"
 
 # Packed float32 instructions are kept out of every kernel (the compiler would
@@ -48,7 +50,20 @@ def build_library(jobs: int = 8) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
     os.replace(tmp, LIB)
+    build_peaks()
     return LIB
+
+
+def build_peaks() -> str:
+    """The device peak probes (matrix-core loop, plain copy) as libpeaks.so."""
+    os.makedirs(BUILD, exist_ok=True)
+    tmp = PEAKS_LIB + ".tmp"
+    cmd = [_hipcc(), *HIP_FLAGS, "-shared", PEAKS_SRC, "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {PEAKS_SRC}:\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, PEAKS_LIB)
+    return PEAKS_LIB
 
 
 if __name__ == "__main__":

@@ -117,10 +117,10 @@ __device__ __forceinline__ int argmax_exact_wave(const E* __restrict__ x, const 
 // second-best scores are kept branch-free (the second best is the median of
 // best, second and the new score); equal scores leave best = second, which
 // sends the row to the float64 decision (lowest index among exact ties).
-// 256-byte rows: three workgroups per CU (168 registers, a few spilled), which
-// hides more latency than the fourth of the registers it gives up.
+// 256-byte rows: at least two workgroups per CU, with registers to spare (a
+// spill reload inside the tile loop would wait for every copy in flight).
 template <class E, int D, int RF>
-__global__ __launch_bounds__(256, (D * sizeof(E) == 256) ? 3 : 1) void k_project_argmax(
+__global__ __launch_bounds__(256, (D * sizeof(E) == 256) ? 2 : 1) void k_project_argmax(
     const E* __restrict__ V, int64_t n, const E* __restrict__ Bt, int n_b,
     const float* __restrict__ bnorm_max, float beta_coef, int32_t* __restrict__ ids,
     float* __restrict__ norms, uint32_t* __restrict__ norm_max_bits, int32_t* __restrict__ und,
@@ -135,7 +135,7 @@ __global__ __launch_bounds__(256, (D * sizeof(E) == 256) ? 3 : 1) void k_project
 
   // the first two tiles of vectors are on their way while the rows load; every
   // tile takes the same number of copies from this wave
-  const int my_copies = dma_rows<E, D, NW>(ring, Bt, 0, n_b, w);
+  dma_rows<E, D, NW>(ring, Bt, 0, n_b, w);
   if (nt > 1) dma_rows<E, D, NW>(ring + G::ROW_BYTES, Bt, G::TI, n_b, w);
 
   Frag<E, D> a[RF];
@@ -145,6 +145,7 @@ __global__ __launch_bounds__(256, (D * sizeof(E) == 256) ? 3 : 1) void k_project
     const int64_t rA = ((int64_t)blockIdx.x * NW + w) * 16 * RF + 16 * f + (l & 15);
     const E* rp = rA < n ? V + rA * D : nullptr;
     a[f].load_global(rp);
+    a[f].settle();
     // squared norm of row (l & 15) from the fragment: each lane sums its part, then the 4 lanes of the row
     float ss = 0.0f;
 #pragma unroll
@@ -182,7 +183,10 @@ __global__ __launch_bounds__(256, (D * sizeof(E) == 256) ? 3 : 1) void k_project
   asm volatile("" : "+v"(top));
   for (int t = 0; t < nt; ++t) {
     // tile t's copies are complete once only tile t+1's remain outstanding
-    wait_vmcnt(t + 1 < nt ? my_copies : 0);
+    if (t + 1 < nt)
+      wait_vmcnt_c<G::ROW_DMA / NW>();   // the fewest copies any wave issues per tile
+    else
+      wait_vmcnt_c<0>();
     raw_barrier();   // every wave's copies of tile t landed; slot (t+2) % 3 is free
     if (t + 2 < nt)
       dma_rows<E, D, NW>(ring + (size_t)((t + 2) % 3) * G::ROW_BYTES, Bt, (int64_t)(t + 2) * G::TI, n_b, w);

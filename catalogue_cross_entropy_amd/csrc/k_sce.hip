@@ -364,99 +364,8 @@ hipError_t launch_group_bounds(const int32_t* keys, const int32_t* sorted, int64
 }
 
 // ------------------------------------------------------------ merge per position
-constexpr int MG_NEAR = 256;   // near-tie entries ranked in float64 per step
-
-struct MergeLds {
-  int32_t* ids;    // [2k]
-  float* vals;     // [2k]
-  uint32_t* khist; // [256]
-  float* cv;       // [64]
-  int32_t* ci;     // [MG_NEAR] list index
-  double* ce;      // [MG_NEAR] float64 logit
-};
-__host__ __device__ constexpr size_t merge_wave_bytes(int k) {
-  return (size_t)2 * k * 8 + 256 * 4 + 64 * 4 + MG_NEAR * 4 + MG_NEAR * 8;
-}
+__host__ __device__ constexpr size_t merge_wave_bytes(int k) { return topk_wave_bytes(2 * k); }
 size_t merge_lds_bytes(int k) { return 4 * ((merge_wave_bytes(k) + 15) / 16 * 16); }
-
-// Keep the k best of list[0..n) (n > k) in (float64 logit desc, id asc) order,
-// compacted to the front; returns the k-th kept element's float64 logit and id.
-template <class E, int D>
-__device__ void reduce_to_k(const MergeLds& L, int n, int k, float beta, const E* xrow, const E* Y, double& te,
-                            int& tid, uint32_t& nexact, uint32_t* counters) {
-  const int l = lane_id();
-  const float ak = wave_kth_largest(L.vals, n, k, L.khist, L.cv);
-  const float lo = f_down((double)ak - 2.0 * (double)beta);
-  const float hi = f_up((double)ak + 2.0 * (double)beta);
-  int nabove = 0, na = 0;
-  for (int base = 0; base < n; base += WAVE) {
-    const int t = base + l;
-    const float v = t < n ? L.vals[t] : NEG_INF;
-    nabove += popc(ballot(t < n && v > hi));
-    const bool nr = t < n && v >= lo && v <= hi;
-    const uint64_t mk = ballot(nr);
-    if (nr) {
-      const int dst = na + popc(mk & lanemask_lt());
-      if (dst < MG_NEAR) L.ci[dst] = t;
-    }
-    na += popc(mk);
-  }
-  if (na > MG_NEAR) {
-    if (l == 0) {
-      atomicAdd(counters + CNT_OVERFLOW, 1u);
-      atomicOr(counters + CNT_ERROR, (uint32_t)ERRBIT_OVERFLOW);
-    }
-    na = MG_NEAR;
-  }
-  wave_sync();
-  for (int e = l; e < na; e += WAVE) L.ce[e] = exact_dot<E, D>(xrow, Y + (int64_t)L.ids[L.ci[e]] * D);
-  if (l == 0) nexact += (uint32_t)na;
-  wave_sync();
-  const int need = k - nabove;   // near-ties kept (>= 1)
-  te = 0.0;
-  tid = 0;
-  for (int a0 = 0; a0 < na; a0 += WAVE) {
-    const int e = a0 + l;
-    int rank = 0;
-    double me = 0.0;
-    int mj = 0;
-    if (e < na) {
-      me = L.ce[e];
-      mj = L.ids[L.ci[e]];
-      for (int u = 0; u < na; ++u) {
-        const double eu = L.ce[u];
-        const int ju = L.ids[L.ci[u]];
-        rank += (eu > me) || (eu == me && ju < mj);
-      }
-    }
-    const uint64_t tm = ballot(e < na && rank == need - 1);
-    if (tm) {
-      const int tl = __builtin_ctzll(tm);
-      te = __shfl(me, tl);
-      tid = __shfl(mj, tl);
-    }
-    wave_sync();
-    if (e < na && rank >= need) L.vals[L.ci[e]] = NEG_INF;   // ranked out
-  }
-  wave_sync();
-  // compact the kept entries (value >= lo after the ranked-out near-ties were dropped)
-  int kept = 0;
-  for (int base = 0; base < n; base += WAVE) {
-    const int t = base + l;
-    const float v = t < n ? L.vals[t] : NEG_INF;
-    const int j = t < n ? L.ids[t] : -1;
-    const bool keep = t < n && v >= lo && v != NEG_INF;
-    const uint64_t mk = ballot(keep);
-    wave_sync();
-    if (keep) {
-      const int dst = kept + popc(mk & lanemask_lt());   // dst <= t: in-place is safe chunk by chunk
-      L.vals[dst] = v;
-      L.ids[dst] = j;
-    }
-    kept += popc(mk);
-    wave_sync();
-  }
-}
 
 template <class E, int D>
 __global__ __launch_bounds__(256) void k_sce_merge(MergeArgs a) {
@@ -466,13 +375,7 @@ __global__ __launch_bounds__(256) void k_sce_merge(MergeArgs a) {
   if (i >= a.s) return;   // whole wave leaves; no block barrier in this kernel
   const int k = a.k;
   char* base = smem + (size_t)w * ((merge_wave_bytes(k) + 15) / 16 * 16);
-  MergeLds L;
-  L.ids = reinterpret_cast<int32_t*>(base);
-  L.vals = reinterpret_cast<float*>(base + (size_t)2 * k * 4);
-  L.khist = reinterpret_cast<uint32_t*>(base + (size_t)2 * k * 8);
-  L.cv = reinterpret_cast<float*>(base + (size_t)2 * k * 8 + 1024);
-  L.ci = reinterpret_cast<int32_t*>(base + (size_t)2 * k * 8 + 1280);
-  L.ce = reinterpret_cast<double*>(base + (size_t)2 * k * 8 + 1280 + MG_NEAR * 4);
+  const MergeLds L = carve_topk(base, 2 * k);
   const E* X = static_cast<const E*>(a.X);
   const E* Y = static_cast<const E*>(a.Y);
   const E* xrow = X + i * D;

@@ -54,6 +54,20 @@ __device__ __forceinline__ float wave_min(float v) {
   for (int o = 32; o >= 1; o >>= 1) v = fminf(v, __shfl_xor(v, o));
   return v;
 }
+// Hand a value loaded from memory on as a plain register value (the compiler
+// waits for the load here, once, instead of at every use inside a later loop,
+// where the wait would also cover every asynchronous copy in flight).
+template <class T>
+__device__ __forceinline__ T settled(T v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+__device__ __forceinline__ int wave_max_i(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o));
+  return v;
+}
 __device__ __forceinline__ int wave_sum(int v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
@@ -183,6 +197,14 @@ template <class E, int D> struct Frag;
 template <int D> struct Frag<bf16, D> {
   static constexpr int KS = D / 32;
   bf16x8 v[KS];
+  // After a global load: wait for it here, once, and hand the registers on as
+  // plain values.  A loop that uses the fragment then carries no pending load,
+  // which the compiler would otherwise wait for (with every copy in flight) at
+  // each use.
+  __device__ __forceinline__ void settle() {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(v[ks]));
+  }
   // Load the fragment of one row (row pointer; nullptr -> zeros).
   __device__ __forceinline__ void load_global(const bf16* row) {
     const int q = lane_id() >> 4;
@@ -209,6 +231,10 @@ template <int D> struct Frag<bf16, D> {
 template <int D> struct Frag<float, D> {
   static constexpr int KS = D / 4;
   float v[KS];
+  __device__ __forceinline__ void settle() {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(v[ks]));
+  }
   __device__ __forceinline__ void load_global(const float* row) {
     const int q = lane_id() >> 4;
 #pragma unroll

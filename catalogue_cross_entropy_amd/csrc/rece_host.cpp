@@ -92,8 +92,8 @@ struct rece_plan_s {
   bool bf16;
   int esize;
   int nbits_b;
-  int selall;
-  int wide;
+  int cap;            // entries of a row's candidate list in the chunk kernels
+  int selall;         // every window has at most k candidates
   int waves_sel;
   int tpc_sel;
   int64_t wmax;       // largest window (items)
@@ -105,7 +105,8 @@ struct rece_plan_s {
   size_t o_cnt, o_bx, o_by, o_px, o_py, o_te, o_tid, o_tlo, o_thi, o_msh, o_ssum, o_nmem, o_xnorm, o_ymax, o_lse,
       o_lpos, o_negs, saved_bytes;
   // forward scratch
-  size_t o_bt, o_bnorm, o_und, o_undy, o_sorty, o_sort, o_part, o_negl, o_xs, o_ys;
+  size_t o_bt, o_bnorm, o_und, o_undy, o_sorty, o_sort, o_part, o_negl, o_xs, o_ys, o_cl0, o_cl1, o_cn0, o_cn1, o_cd0,
+      o_cd1, o_clo0, o_clo1;
   // backward scratch (the backward reuses the forward's scratch from offset 0)
   size_t o_pk0, o_pv0, o_pk1, o_pv1, o_psc, o_dya, o_pcoef;
   size_t scratch_bytes;
@@ -250,6 +251,10 @@ static void plan_sce_layout(rece_plan_s* p) {
   p->o_snegs = sc.take((size_t)sx * k * 4);
   p->o_snegl = sc.take((size_t)sx * k * 4);
   p->o_stmp = sc.take((size_t)sx * 4);
+  p->o_cl0 = sc.take((size_t)sx * p->cap * 8);
+  p->o_cn0 = sc.take((size_t)sx * 4);
+  p->o_clo0 = sc.take((size_t)sx * 4);
+  p->o_cd0 = sc.take((size_t)n_b * p->tpc_sel * p->waves_sel * p->cap * 8);
   p->scratch_fwd_bytes = sc.off;
   p->scratch_bytes = std::max(sc.off, plan_backward_scratch(p));
 }
@@ -342,7 +347,6 @@ static rece_status sce_forward(const rece_plan_s& p, hipStream_t st, const void*
   a.n_c = n_b;
   a.k = k;
   a.rho = 0;
-  a.selall = p.selall;
   a.tiles_per_chunk = p.tpc_sel;
   a.beta_coef = p.beta_coef;
   a.xnorm = xnorm;
@@ -359,7 +363,12 @@ static rece_status sce_forward(const rece_plan_s& p, hipStream_t st, const void*
   a.slot_out = 1;
   a.n_ec = 0;
   a.wrap = 0;
-  a.wide = p.wide;
+  a.cap = p.cap;
+  a.selall = p.selall;
+  a.clist = reinterpret_cast<int2*>(sc + p.o_cl0);
+  a.clist_n = reinterpret_cast<int32_t*>(sc + p.o_cn0);
+  a.clist_lo = reinterpret_cast<float*>(sc + p.o_clo0);
+  a.cdbl = reinterpret_cast<double*>(sc + p.o_cd0);
   a.counters = counters;
   RECE_PHASE(RECE_PHASE_SELECT, launch_select(p.bf16, d, p.waves_sel, a, st), "bucket logits and top-k");
 
@@ -442,25 +451,35 @@ rece_status rece_plan(const rece_config* cfg, rece_plan_t* out) {
   p->esize = p->bf16 ? 2 : 4;
   p->nbits_b = bits_for(c.n_b);
   const int64_t rows_chunk = sce ? c.b_x : (s + n_c - 1) / n_c;
-  // The largest window: every candidate is kept when k reaches it (a window of the
-  // whole catalogue has C - 1 candidates, the positive being excluded).
+  // the largest window (items)
   if (sce) {
     p->wmax = c.b_y;
-    p->selall = k >= c.b_y;
   } else {
     const int64_t items_chunk = (C + n_c - 1) / n_c;
     const int64_t span = 2 * (int64_t)c.n_ec + 1;
     p->wmax = (c.window_wrap && span >= n_c) ? C : std::min<int64_t>(C, span * items_chunk);
-    p->selall = p->wmax >= C ? (k >= C - 1) : (k >= p->wmax);
   }
-  // the histogram counts of a row reach the window size: 16-bit counts only below 65536
-  p->wide = (!p->selall && p->wmax > 65535) ? 1 : 0;
-  p->waves_sel = 1;
-  for (int nw : {4, 2, 1}) {
-    if (select_lds_bytes(p->bf16, d, nw, p->wide != 0) <= 160 * 1024) {
-      p->waves_sel = nw;
-      break;
-    }
+  // every candidate is kept when k reaches the largest window (a window of the whole
+  // catalogue has C - 1 candidates, the positive being excluded); the candidate lists
+  // then hold whole windows and are never compacted
+  p->selall = sce ? (k >= c.b_y) : (p->wmax >= C ? (k >= C - 1) : (k >= p->wmax));
+  p->cap = p->selall ? (int)std::max<int64_t>(p->wmax, 1) : select_list_cap(k, d, p->bf16);
+  if (p->selall && p->wmax >= ((int64_t)1 << 30)) {   // list lengths share a word with two flag bits
+    delete p;
+    return fail(RECE_ERR_UNSUPPORTED, "k covers a window of 2^30 or more items");
+  }
+  const int cap_lds = p->selall ? 0 : p->cap;
+  if (!p->selall && select_finish_waves(cap_lds) == 0) {
+    delete p;
+    return fail(RECE_ERR_UNSUPPORTED, "k too large for a selection list held in LDS (k must cover the window, "
+                                      "or stay below about 9000)");
+  }
+  // waves per chunk-kernel workgroup: 16 positions each, no more than a chunk has
+  p->waves_sel = rows_chunk <= 16 ? 1 : (rows_chunk <= 32 ? 2 : 4);
+  while (p->waves_sel > 1 && select_lds_bytes(p->bf16, d, p->waves_sel, cap_lds) > 160 * 1024) p->waves_sel /= 2;
+  if (select_lds_bytes(p->bf16, d, p->waves_sel, cap_lds) > 160 * 1024) {
+    delete p;
+    return fail(RECE_ERR_UNSUPPORTED, "k too large for the chunk kernel's LDS");
   }
   p->tpc_sel = (int)((rows_chunk + 16 * p->waves_sel - 1) / (16 * p->waves_sel));
   // |float32 matrix-core dot - float64 coordinate-order dot| <= beta_coef * ||x|| * ||y||:
@@ -506,6 +525,16 @@ rece_status rece_plan(const rece_config* cfg, rece_plan_t* out) {
   // sorted copies of every round (each chunk and window one block of rows)
   p->o_xs = sc.take((size_t)r * s * d * p->esize);
   p->o_ys = sc.take((size_t)r * C * d * p->esize);
+  // candidate lists of the chunk kernels: round 0 (caller's stream), rounds >= 1 (side stream, in turn)
+  p->o_cl0 = sc.take((size_t)s * p->cap * 8);
+  p->o_cn0 = sc.take((size_t)s * 4);
+  p->o_cl1 = r > 1 ? sc.take((size_t)s * p->cap * 8) : p->o_cl0;
+  p->o_cn1 = r > 1 ? sc.take((size_t)s * 4) : p->o_cn0;
+  p->o_clo0 = sc.take((size_t)s * 4);
+  p->o_clo1 = r > 1 ? sc.take((size_t)s * 4) : p->o_clo0;
+  const size_t cd = (size_t)c.n_c * p->tpc_sel * p->waves_sel * p->cap * 8;   // per chunk-kernel wave
+  p->o_cd0 = sc.take(cd);
+  p->o_cd1 = r > 1 ? sc.take(cd) : p->o_cd0;
   p->dedup_bits = dedup_hash_bits(r, k);
   p->scratch_fwd_bytes = sc.off;
   p->scratch_bytes = std::max(sc.off, plan_backward_scratch(p));
@@ -636,7 +665,6 @@ static rece_status forward_impl(const rece_plan_s& p, hipStream_t st, const void
     a.n_c = c.n_c;
     a.k = c.k;
     a.rho = rho;
-    a.selall = p.selall;
     a.tiles_per_chunk = p.tpc_sel;
     a.beta_coef = p.beta_coef;
     a.xnorm = xnorm;
@@ -652,7 +680,12 @@ static rece_status forward_impl(const rece_plan_s& p, hipStream_t st, const void
     a.slot_out = 0;
     a.n_ec = c.n_ec;
     a.wrap = c.window_wrap;
-    a.wide = p.wide;
+    a.cap = p.cap;
+    a.selall = p.selall;
+    a.clist = reinterpret_cast<int2*>(sc + (rho == 0 ? p.o_cl0 : p.o_cl1));
+    a.clist_n = reinterpret_cast<int32_t*>(sc + (rho == 0 ? p.o_cn0 : p.o_cn1));
+    a.clist_lo = reinterpret_cast<float*>(sc + (rho == 0 ? p.o_clo0 : p.o_clo1));
+    a.cdbl = reinterpret_cast<double*>(sc + (rho == 0 ? p.o_cd0 : p.o_cd1));
     a.counters = counters;
     a.negl = rho > 0 ? reinterpret_cast<float*>(sc + p.o_negl) + (int64_t)(rho - 1) * s * c.k : nullptr;
     return a;

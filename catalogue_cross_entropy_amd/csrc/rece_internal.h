@@ -33,8 +33,8 @@ struct SelectArgs {
   const int32_t* perm_x;      // round rho
   const int32_t* perm_y;      // round rho
   int64_t s, C;
-  int n_c, k, cap, rho, rounds;
-  int selall;                 // 1: every window has at most k candidates; keep all
+  int n_c, k, cap, rho, rounds;   // cap: entries of a row's candidate list
+  int selall;                 // 1: every window has at most k candidates (lists never compacted)
   int tiles_per_chunk;
   float beta_coef;            // error-bound coefficient of a float32 logit
   const float* xnorm;         // [s]
@@ -51,7 +51,10 @@ struct SelectArgs {
   int slot_out;               // 1: outputs indexed by sorted slot, not by position id
   int n_ec;                   // window: chunks c - n_ec .. c + n_ec
   int wrap;                   // 1: chunk indices modulo n_c (cyclic); 0: clipped to [0, n_c)
-  int wide;                   // 1: 32-bit histogram counts (a window may exceed 65535 items)
+  int2* clist;                // [rows][cap] candidate lists (item id, float32 logit bits)
+  int32_t* clist_n;           // [rows] entries in each list; bit 31: compacted or raised, bit 30: redo
+  float* clist_lo;            // [rows] each row's final threshold (no kept entry lies below it)
+  double* cdbl;               // [blocks * waves][cap] float64 scratch of each chunk-kernel wave
   uint32_t* counters;
 };
 
@@ -132,7 +135,9 @@ int sort_digit_bits(int64_t n);
 hipError_t launch_counting_sort(const int32_t* keys, const int32_t* in_perm, int64_t n, int shift, int nbits,
                                 void* scratch, int32_t* perm_out, int32_t* inv_out, hipStream_t st);
 hipError_t launch_select(bool is_bf16, int d, int waves, const SelectArgs& a, hipStream_t st);
-size_t select_lds_bytes(bool is_bf16, int d, int waves, bool wide);
+size_t select_lds_bytes(bool is_bf16, int d, int waves, int cap_lds);
+int select_list_cap(int k, int d, bool bf16);   // entries of a row's candidate list
+int select_finish_waves(int cap_lds);            // 0: a list of cap_lds entries does not fit in LDS
 int ce_blocks(int64_t s);
 hipError_t launch_ce(bool is_bf16, int d, const CeArgs& a, float* loss, hipStream_t st);
 // log2 of the per-wave hash slots k_round_dedup uses for rounds earlier lists of k

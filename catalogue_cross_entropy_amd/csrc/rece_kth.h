@@ -1,6 +1,8 @@
-// Exact k-th largest float of a short list held in LDS, computed by one wave.
+// Exact k-th largest float of a short list held in LDS, computed by one wave, and
+// the exact top-k of such a list (float64 near-tie ranking).
 #pragma once
 #include "rece_device.h"
+#include "rece_internal.h"
 
 namespace rece {
 
@@ -127,6 +129,114 @@ __device__ inline float wave_kth_largest(const float* vals, int n, int k, uint32
     }
   }
   return result;
+}
+
+constexpr int MG_NEAR = 256;   // near-tie entries ranked in float64 per step
+
+struct MergeLds {
+  int32_t* ids;    // [cap]
+  float* vals;     // [cap]
+  uint32_t* khist; // [256]
+  float* cv;       // [64]
+  int32_t* ci;     // [MG_NEAR] list index
+  double* ce;      // [MG_NEAR] float64 logit
+};
+// LDS of one wave for a list of up to cap entries.
+__host__ __device__ constexpr size_t topk_wave_bytes(int cap) {
+  return (size_t)cap * 8 + 256 * 4 + 64 * 4 + MG_NEAR * 4 + MG_NEAR * 8;
+}
+
+__device__ inline MergeLds carve_topk(char* base, int cap) {
+  MergeLds L;
+  L.ids = reinterpret_cast<int32_t*>(base);
+  L.vals = reinterpret_cast<float*>(base + (size_t)cap * 4);
+  L.khist = reinterpret_cast<uint32_t*>(base + (size_t)cap * 8);
+  L.cv = reinterpret_cast<float*>(base + (size_t)cap * 8 + 1024);
+  L.ci = reinterpret_cast<int32_t*>(base + (size_t)cap * 8 + 1280);
+  L.ce = reinterpret_cast<double*>(base + (size_t)cap * 8 + 1280 + MG_NEAR * 4);
+  return L;
+}
+
+// Keep the k best of list[0..n) (n >= k) in (float64 logit desc, id asc) order,
+// compacted to the front; returns the k-th kept element's float64 logit and id.
+// The float32 k-th value a_k decides every entry more than 2*beta away from it;
+// the entries within 2*beta of a_k are ranked on float64 values (coordinate-order
+// scalar products), so the kept set is the one float64 values define.
+template <class E, int D>
+__device__ void reduce_to_k(const MergeLds& L, int n, int k, float beta, const E* xrow, const E* Y, double& te,
+                            int& tid, uint32_t& nexact, uint32_t* counters) {
+  const int l = lane_id();
+  const float ak = wave_kth_largest(L.vals, n, k, L.khist, L.cv);
+  const float lo = f_down((double)ak - 2.0 * (double)beta);
+  const float hi = f_up((double)ak + 2.0 * (double)beta);
+  int nabove = 0, na = 0;
+  for (int base = 0; base < n; base += WAVE) {
+    const int t = base + l;
+    const float v = t < n ? L.vals[t] : NEG_INF;
+    nabove += popc(ballot(t < n && v > hi));
+    const bool nr = t < n && v >= lo && v <= hi;
+    const uint64_t mk = ballot(nr);
+    if (nr) {
+      const int dst = na + popc(mk & lanemask_lt());
+      if (dst < MG_NEAR) L.ci[dst] = t;
+    }
+    na += popc(mk);
+  }
+  if (na > MG_NEAR) {
+    if (l == 0) {
+      atomicAdd(counters + CNT_OVERFLOW, 1u);
+      atomicOr(counters + CNT_ERROR, (uint32_t)ERRBIT_OVERFLOW);
+    }
+    na = MG_NEAR;
+  }
+  wave_sync();
+  for (int e = l; e < na; e += WAVE) L.ce[e] = exact_dot<E, D>(xrow, Y + (int64_t)L.ids[L.ci[e]] * D);
+  if (l == 0) nexact += (uint32_t)na;
+  wave_sync();
+  const int need = k - nabove;   // near-ties kept (>= 1)
+  te = 0.0;
+  tid = 0;
+  for (int a0 = 0; a0 < na; a0 += WAVE) {
+    const int e = a0 + l;
+    int rank = 0;
+    double me = 0.0;
+    int mj = 0;
+    if (e < na) {
+      me = L.ce[e];
+      mj = L.ids[L.ci[e]];
+      for (int u = 0; u < na; ++u) {
+        const double eu = L.ce[u];
+        const int ju = L.ids[L.ci[u]];
+        rank += (eu > me) || (eu == me && ju < mj);
+      }
+    }
+    const uint64_t tm = ballot(e < na && rank == need - 1);
+    if (tm) {
+      const int tl = __builtin_ctzll(tm);
+      te = __shfl(me, tl);
+      tid = __shfl(mj, tl);
+    }
+    wave_sync();
+    if (e < na && rank >= need) L.vals[L.ci[e]] = NEG_INF;   // ranked out
+  }
+  wave_sync();
+  // compact the kept entries (value >= lo after the ranked-out near-ties were dropped)
+  int kept = 0;
+  for (int base = 0; base < n; base += WAVE) {
+    const int t = base + l;
+    const float v = t < n ? L.vals[t] : NEG_INF;
+    const int j = t < n ? L.ids[t] : -1;
+    const bool keep = t < n && v >= lo && v != NEG_INF;
+    const uint64_t mk = ballot(keep);
+    wave_sync();
+    if (keep) {
+      const int dst = kept + popc(mk & lanemask_lt());   // dst <= t: in-place is safe chunk by chunk
+      L.vals[dst] = v;
+      L.ids[dst] = j;
+    }
+    kept += popc(mk);
+    wave_sync();
+  }
 }
 
 }  // namespace rece

@@ -52,6 +52,13 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 #undef RECE_VMCNT_CASE
 }
 
+// s_waitcnt vmcnt(N) for a compile-time N.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_c() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
+}
+
 // LDS stores, atomics and transpose reads issued inside the streaming loops.
 // The compiler cannot tell that their addresses lie outside the destinations of
 // the asynchronous tile copies in flight, and would wait for every copy before
@@ -237,29 +244,83 @@ __device__ __forceinline__ void issue_window_tile(char* ring, size_t slot_bytes,
   }
 }
 
+// Reads of tile data from LDS as inline assembly, waiting for their own results
+// inside the block.  As plain loads the compiler cannot tell that they miss the
+// destinations of the asynchronous copies in flight and waits for every copy
+// before each of them, which would drain the prefetch ring at every tile.
+template <int N> struct LdsRead128;
+template <> struct LdsRead128<1> {
+  static __device__ __forceinline__ void run(const uint32_t* a, u32x4* r) {
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(r[0]) : "v"(a[0]) : "memory");
+  }
+};
+template <> struct LdsRead128<2> {
+  static __device__ __forceinline__ void run(const uint32_t* a, u32x4* r) {
+    asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(r[0]), "=&v"(r[1]) : "v"(a[0]), "v"(a[1]) : "memory");
+  }
+};
+template <> struct LdsRead128<4> {
+  static __device__ __forceinline__ void run(const uint32_t* a, u32x4* r) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+        : "memory");
+  }
+};
+template <> struct LdsRead128<8> {
+  static __device__ __forceinline__ void run(const uint32_t* a, u32x4* r) {
+    LdsRead128<4>::run(a, r);
+    LdsRead128<4>::run(a + 4, r + 4);
+  }
+};
+// Eight dwords from LDS (addresses a[0..7]), one wait.
+__device__ __forceinline__ void lds_read_b32x8(const uint32_t* a, float* r) {
+  asm volatile(
+      "ds_read_b32 %0, %8\n\tds_read_b32 %1, %9\n\tds_read_b32 %2, %10\n\tds_read_b32 %3, %11\n\t"
+      "ds_read_b32 %4, %12\n\tds_read_b32 %5, %13\n\tds_read_b32 %6, %14\n\tds_read_b32 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+      : "memory");
+}
+
 // Matrix-core fragment of tile row n (B operand, "row = vector" layout).
 template <class E, int D> struct TileFrag;
 
 template <int D> struct TileFrag<bf16, D> {
   static __device__ __forceinline__ void load(Frag<bf16, D>& f, const char* rows, int n) {
     using G = TileGeom<bf16, D>;
+    constexpr int KS = D / 32;
     const int q = lane_id() >> 4;
+    uint32_t a[KS];
+    u32x4 raw[KS];
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
       const int c = (4 * ks + q) ^ (n & G::SWM);
-      const u32x4 raw = *reinterpret_cast<const u32x4*>(rows + n * G::RB + c * 16);
-      f.v[ks] = __builtin_bit_cast(bf16x8, raw);
+      a[ks] = lds_addr(rows + n * G::RB + c * 16);
     }
+    LdsRead128<KS>::run(a, raw);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) f.v[ks] = __builtin_bit_cast(bf16x8, raw[ks]);
   }
 };
 template <int D> struct TileFrag<float, D> {
   static __device__ __forceinline__ void load(Frag<float, D>& f, const char* rows, int n) {
     using G = TileGeom<float, D>;
+    constexpr int KS = D / 4;
     const int q = lane_id() >> 4;
 #pragma unroll
-    for (int ks = 0; ks < D / 4; ++ks) {
-      const int c = ks ^ (n & G::SWM);
-      f.v[ks] = *reinterpret_cast<const float*>(rows + n * G::RB + c * 16 + 4 * q);
+    for (int k0 = 0; k0 < KS; k0 += 8) {
+      uint32_t a[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int c = (k0 + u) ^ (n & G::SWM);
+        a[u] = lds_addr(rows + n * G::RB + c * 16 + 4 * q);
+      }
+      lds_read_b32x8(a, &f.v[k0]);
     }
   }
 };

@@ -26,6 +26,22 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(rece.EXPORTED)
 
 
+def test_peaks_library_exports_every_declared_symbol():
+    from catalogue_cross_entropy_amd import peaks
+    with open(os.path.join(ROOT, "include", "peaks.h")) as f:
+        text = f.read()
+    names = set(re.findall(r"^\s*(?:int|double)\s+(rece_\w+)\s*\(", text, re.M))
+    assert names == set(peaks.EXPORTED)
+    L = peaks.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    # host-side arithmetic only: 8 chains x 4 waves of 16x16x32 multiply-adds per iteration
+    assert L.rece_peak_mfma_flops(3, 5) == 2.0 * 16 * 16 * 32 * 8 * 4 * 5 * 3
+    # argument checks return before anything is enqueued
+    assert L.rece_peak_copy(None, None, None, 16) != 0
+    assert L.rece_peak_mfma_bf16(None, 0, 1, None) != 0
+
+
 def test_version_and_status_strings():
     assert "gfx950" in rece.version()
     L = rece.lib()
@@ -101,8 +117,13 @@ def test_workspace_never_holds_a_logit_tensor(name):
     pairs = rounds * w.s * w.k + w.s
     rows = rounds * (w.s + w.C) * w.d * es
     slots = w.n_b * (w.b_x + w.b_y) * (w.d * es + 64) + w.n_b * (w.s + w.C) * 4
-    assert p.scratch_bytes <= rows + slots + pairs * (16 + 2 * w.d * 4 // 256 + 1) + 16 * (w.s + w.C) * rounds \
-        + (32 << 20)
+    # the chunk kernels' candidate lists: per row (position, or bucket slot) 3k + 2 tiles of
+    # (id, logit) entries, its length and threshold, and per wave of 16 rows as many
+    # float64 values for the exact pass; two sets for RECE (its rounds run on two streams)
+    list_rows = 2 * w.s if w.variant == "rece" else w.n_b * w.b_x
+    cand = list_rows * ((3 * w.k + 128) * 8 * 9 // 8 + 8)
+    assert p.scratch_bytes <= rows + slots + cand + pairs * (16 + 2 * w.d * 4 // 256 + 1) \
+        + 16 * (w.s + w.C) * rounds + (32 << 20)
     if w.k * 8 < w.C:   # a reduced set (not the full-CE twin): far below a dense logit tensor
         assert p.scratch_bytes < w.s * w.C * 2
     assert p.saved_bytes - lists < w.s * w.C * 2
