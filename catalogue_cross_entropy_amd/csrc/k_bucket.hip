@@ -7,9 +7,12 @@
 // and never stored.  The decision is the argmax of the float64 coordinate-order
 // sums: a row whose float32 top-2 gap exceeds twice the error bound is decided
 // by the float32 argmax; the others (rare) are appended to a list, and a second
-// kernel recomputes all n_b scores of each listed row in float64, one wave per
-// row, so the slow rows neither stall the matrix-core kernel nor sit on its
-// critical path.
+// kernel decides them in float64 from the few vectors within twice the bound of
+// the row's float32 maximum, so the slow rows neither stall the matrix-core
+// kernel nor sit on its critical path.  (Small inputs decide their undecided
+// rows inside the matrix-core kernel, all vectors in float64.)
+#include <algorithm>
+
 #include "rece_device.h"
 #include "rece_internal.h"
 #include "rece_stream.h"
@@ -287,22 +290,95 @@ __global__ __launch_bounds__(256, (D * sizeof(E) == 256) ? 2 : 1) void k_project
   }
 }
 
-// Float64 argmax of the listed rows: one wave per row (grid-stride over the list).
+// Float64 decision of the listed rows, 16 rows per wave (grid-stride over the
+// list).  The float32 scores of every vector are recomputed on the matrix cores
+// to find each row's float32 maximum m; then only the vectors scoring at least
+// m - 2*beta are scored in float64.  The float64 argmax is among them: its
+// float32 score is at least its float64 score less beta, and that is at least
+// the float64 score of the float32 winner, which is at least m - beta.  Exact
+// float64 ties go to the lowest index, as in the oracle.
 template <class E, int D>
-__global__ __launch_bounds__(256) void k_argmax_exact(const E* __restrict__ V, const E* __restrict__ Bt, int n_b,
-                                                      const int32_t* __restrict__ und,
-                                                      const uint32_t* __restrict__ und_n, int32_t* __restrict__ ids,
-                                                      uint32_t* __restrict__ counters) {
-  const int l = lane_id();
-  const uint32_t nund = *und_n;
-  const uint32_t wv = blockIdx.x * 4 + (threadIdx.x >> 6), nwv = gridDim.x * 4;
+__global__ __launch_bounds__(256) void k_argmax_near(const E* __restrict__ V, const E* __restrict__ Bt, int n_b,
+                                                     const float* __restrict__ bnorm_max, float beta_coef,
+                                                     const int32_t* __restrict__ und,
+                                                     const uint32_t* __restrict__ und_n, int32_t* __restrict__ ids,
+                                                     uint32_t* __restrict__ counters) {
+  constexpr int UB = D * (int)sizeof(E) >= 512 ? 1 : (D * (int)sizeof(E) >= 256 ? 2 : 4);   // blocks in flight
+  const int l = lane_id(), r = l & 15, g = l >> 4;
+  const int64_t nund = *und_n;
+  const int64_t wv = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6), nwv = (int64_t)gridDim.x * 4;
+  const float bmax = bnorm_max[0];
   uint32_t done = 0;
-  for (uint32_t u = wv; u < nund; u += nwv) {
-    const int64_t row = und[u];
-    int bi = argmax_exact_wave<E, D>(V + row * D, Bt, n_b);
-    if (bi >= n_b) bi = 0;   // only reachable with NaN scores
-    if (l == 0) ids[row] = bi;
-    ++done;
+  for (int64_t g0 = wv * 16; g0 < nund; g0 += nwv * 16) {
+    const bool rv = g0 + r < nund;
+    const int64_t row = rv ? und[g0 + r] : 0;
+    Frag<E, D> afr;
+    afr.load_global(rv ? V + row * D : nullptr);
+    // the row's norm from its fragment (spread over the row's four lanes), as in
+    // the matrix-core kernel
+    float ss = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < Frag<E, D>::KS; ++ks) {
+      if constexpr (sizeof(E) == 2) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const float x = to_f32(afr.v[ks][t]);
+          ss = fmaf(x, x, ss);
+        }
+      } else {
+        ss = fmaf(afr.v[ks], afr.v[ks], ss);
+      }
+    }
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    const double beta = (double)beta_coef * (double)(sqrtf(ss) * (1.0f + 0.0005f)) * (double)bmax;
+    float mx = NEG_INF, lo = 0.0f;
+    double be = -__builtin_huge_val();
+    int bi = 0x7fffffff;
+    for (int pass = 0; pass < 2; ++pass) {
+      for (int b0 = 0; b0 < n_b; b0 += 16 * UB) {
+        Frag<E, D> bf[UB];
+#pragma unroll
+        for (int u = 0; u < UB; ++u) {
+          const int b = b0 + 16 * u + r;   // the vector of this lane's operand row
+          bf[u].load_global(b < n_b ? Bt + (int64_t)b * D : nullptr);
+        }
+#pragma unroll
+        for (int u = 0; u < UB; ++u) {
+          const f32x4 acc = mma_block(bf[u], afr, f32x4{0.f, 0.f, 0.f, 0.f});   // [vector 4g+v][row r]
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int b = b0 + 16 * u + 4 * g + v;
+            if (b >= n_b) continue;
+            if (pass == 0) {
+              mx = fmaxf(mx, acc[v]);
+            } else if (rv && acc[v] >= lo) {
+              const double e = exact_dot<E, D, 4>(V + row * D, Bt + (int64_t)b * D);
+              if (e > be || (e == be && b < bi)) {
+                be = e;
+                bi = b;
+              }
+            }
+          }
+        }
+      }
+      if (pass == 0) {
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        lo = f_down((double)mx - 2.0 * beta);
+      }
+    }
+#pragma unroll
+    for (int o = 16; o <= 32; o <<= 1) {
+      const double oe = __shfl_xor(be, o);
+      const int ob = __shfl_xor(bi, o);
+      if (oe > be || (oe == be && ob < bi)) {
+        be = oe;
+        bi = ob;
+      }
+    }
+    if (rv && g == 0) ids[row] = bi < n_b ? bi : 0;   // no candidate only with NaN scores
+    done += (uint32_t)popc(ballot(rv && g == 0));
   }
   if (l == 0 && done) atomicAdd(counters + CNT_ARGMAX_EXACT, done);
 }
@@ -320,10 +396,11 @@ static hipError_t launch_pa(const void* V, int64_t n, const void* Bt, int n_b, c
                        n_b, bmax, beta, ids, norms, nmax, und, und_n, counters);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // the listed rows: a wave per row, about one row in 2048 expected
-    const int64_t eb = n / 2048 > 2048 ? 2048 : n / 2048;
-    hipLaunchKernelGGL((k_argmax_exact<E, D>), dim3((unsigned)eb), dim3(256), 0, st, (const E*)V, (const E*)Bt, n_b,
-                       und, und_n, ids, counters);
+    // the listed rows, 16 per wave: about one row in 2048 expected, a few times
+    // that many waves
+    const int64_t eb = std::min<int64_t>(1024, std::max<int64_t>(16, n / 16384));
+    hipLaunchKernelGGL((k_argmax_near<E, D>), dim3((unsigned)eb), dim3(256), 0, st, (const E*)V, (const E*)Bt, n_b,
+                       bmax, beta, und, und_n, ids, counters);
   } else {   // small input: undecided rows are decided inside the kernel
     const unsigned blocks = (unsigned)((n + 63) / 64);
     hipLaunchKernelGGL((k_project_argmax<E, D, 1>), dim3(blocks), dim3(256), 0, st, (const E*)V, n, (const E*)Bt,

@@ -38,6 +38,8 @@
 // multiset of copies a set) does not change its selection, only which pairs its
 // sum counts, so that is settled afterwards from the kept lists (k_round_dedup)
 // and the rounds need not wait for one another.
+#include <algorithm>
+
 #include "rece_device.h"
 #include "rece_internal.h"
 #include "rece_kth.h"
@@ -476,12 +478,8 @@ __global__ __launch_bounds__(64 * NW) void k_sel_stream(SelectArgs p) {
 }
 
 template <class E, int D>
-__global__ __launch_bounds__(256) void k_sel_finish(SelectArgs p) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  const int nw = blockDim.x >> 6;
-  const int w = threadIdx.x >> 6, l = lane_id();
-  const int64_t row = (int64_t)blockIdx.x * nw + w;
-  if (row >= p.s) return;   // whole wave leaves; no block barrier in this kernel
+__device__ __forceinline__ void sel_finish_row(const SelectArgs& p, char* smem, int w, int64_t row) {
+  const int l = lane_id();
   const int k = p.k, cap = p.cap;
   const int64_t i = p.slot_out ? (int64_t)p.perm_x[row] : row;   // position id
   const E* X = reinterpret_cast<const E*>(p.X);
@@ -580,6 +578,17 @@ __global__ __launch_bounds__(256) void k_sel_finish(SelectArgs p) {
   flush_count(p.counters + CNT_LOGIT_EXACT, nexact);
 }
 
+template <class E, int D>
+__global__ __launch_bounds__(256, 4) void k_sel_finish(SelectArgs p) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int nw = blockDim.x >> 6;
+  const int w = threadIdx.x >> 6;
+  // a fixed grid: each wave takes rows w0, w0 + waves, ... (no block barrier in
+  // this kernel, so the waves of a workgroup run their rows independently)
+  const int64_t waves = (int64_t)gridDim.x * nw;
+  for (int64_t row = (int64_t)blockIdx.x * nw + w; row < p.s; row += waves) sel_finish_row<E, D>(p, smem, w, row);
+}
+
 template <class E, int D, int NW>
 static size_t stream_lds_bytes(int cap_lds) {
   return (size_t)SEL_RING * sel_slot_bytes(TileGeom<E, D>::ROW_BYTES) + (size_t)NW * sel_wave_bytes(cap_lds);
@@ -635,7 +644,16 @@ static hipError_t launch_sel(const SelectArgs& a, hipStream_t st) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fin),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fin, dim3((unsigned)((a.s + nwf - 1) / nwf)), dim3(64 * nwf), lds, st, a);
+  // as many workgroups as fit on the device at once (each wave loops over rows)
+  int dev = 0, cus = 0, per_cu = 0;
+  e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fin), 64 * nwf, lds);
+  if (e != hipSuccess) return e;
+  const int64_t want = (a.s + nwf - 1) / nwf;
+  const int64_t fit = (int64_t)std::max(cus, 1) * std::max(per_cu, 1);
+  hipLaunchKernelGGL(fin, dim3((unsigned)std::max<int64_t>(1, std::min(want, fit))), dim3(64 * nwf), lds, st, a);
   return hipGetLastError();
 }
 
