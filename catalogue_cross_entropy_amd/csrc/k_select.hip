@@ -478,7 +478,8 @@ __global__ __launch_bounds__(64 * NW) void k_sel_stream(SelectArgs p) {
 }
 
 template <class E, int D>
-__device__ __forceinline__ void sel_finish_row(const SelectArgs& p, char* smem, int w, int64_t row) {
+__device__ __forceinline__ void sel_finish_row(const SelectArgs& p, char* smem, int w, int64_t row, uint32_t& nexact,
+                                               uint32_t& nnear) {
   const int l = lane_id();
   const int k = p.k, cap = p.cap;
   const int64_t i = p.slot_out ? (int64_t)p.perm_x[row] : row;   // position id
@@ -487,7 +488,6 @@ __device__ __forceinline__ void sel_finish_row(const SelectArgs& p, char* smem, 
   const E* xrow = X + i * D;
   const float beta = p.beta_coef * p.xnorm[i] * p.ynorm_max[0];
   const int64_t o = p.slot_out ? row : (int64_t)p.rho * p.s + row;   // output row
-  uint32_t nexact = 0;
 
   const uint32_t nf = k > 0 ? (uint32_t)p.clist_n[row] : 0u;
   const int n = (int)(nf & ~(LIST_COMPACTED | LIST_REDO));
@@ -545,7 +545,7 @@ __device__ __forceinline__ void sel_finish_row(const SelectArgs& p, char* smem, 
     const uint32_t before = nexact;
     reduce_to_k<E, D>(L, nk, k, beta, xrow, Y, te, tid, nexact, p.counters);
     kept = k;
-    if (l == 0 && nexact - before > 1) atomicAdd(p.counters + CNT_TOPK_EXACT, 1u);
+    if (nexact - before > 1) ++nnear;   // lane 0 holds the counts
     for (int t = l; t < kept; t += WAVE) mx = fmaxf(mx, L.vals[t]);
     mx = wave_max(mx);
     for (int t = l; t < kept; t += WAVE) {
@@ -575,7 +575,6 @@ __device__ __forceinline__ void sel_finish_row(const SelectArgs& p, char* smem, 
     p.ssum[o] = kept > 0 ? se : 0.0f;
     p.nmem[o] = kept;
   }
-  flush_count(p.counters + CNT_LOGIT_EXACT, nexact);
 }
 
 template <class E, int D>
@@ -586,7 +585,12 @@ __global__ __launch_bounds__(256, 4) void k_sel_finish(SelectArgs p) {
   // a fixed grid: each wave takes rows w0, w0 + waves, ... (no block barrier in
   // this kernel, so the waves of a workgroup run their rows independently)
   const int64_t waves = (int64_t)gridDim.x * nw;
-  for (int64_t row = (int64_t)blockIdx.x * nw + w; row < p.s; row += waves) sel_finish_row<E, D>(p, smem, w, row);
+  // counts flushed once per wave (one address shared by every wave)
+  uint32_t nexact = 0, nnear = 0;
+  for (int64_t row = (int64_t)blockIdx.x * nw + w; row < p.s; row += waves)
+    sel_finish_row<E, D>(p, smem, w, row, nexact, nnear);
+  flush_count(p.counters + CNT_LOGIT_EXACT, nexact);
+  flush_count(p.counters + CNT_TOPK_EXACT, nnear);
 }
 
 template <class E, int D, int NW>
