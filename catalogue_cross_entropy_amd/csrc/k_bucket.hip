@@ -85,6 +85,9 @@ hipError_t launch_prep_b(bool is_bf16, int d, const void* B, int rounds, int n_b
   return hipGetLastError();
 }
 
+// Median of three integers (one v_med3_i32).
+__device__ __forceinline__ int med3_i(int a, int b, int c) { return max(min(a, b), min(max(a, b), c)); }
+
 // Wave-collective float64 argmax of x . b over the n_b vectors (lowest index
 // among ties): every lane scores n_b / 64 of them in coordinate order.
 template <class E, int D>
@@ -123,7 +126,7 @@ __device__ __forceinline__ int argmax_exact_wave(const E* __restrict__ x, const 
 // 256-byte rows: at least two workgroups per CU, with registers to spare (a
 // spill reload inside the tile loop would wait for every copy in flight).
 template <class E, int D, int RF>
-__global__ __launch_bounds__(256, (D * sizeof(E) == 256) ? 2 : 1) void k_project_argmax(
+__global__ __launch_bounds__(256, (D * sizeof(E) == 256) ? 3 : 1) void k_project_argmax(
     const E* __restrict__ V, int64_t n, const E* __restrict__ Bt, int n_b,
     const float* __restrict__ bnorm_max, float beta_coef, int32_t* __restrict__ ids,
     float* __restrict__ norms, uint32_t* __restrict__ norm_max_bits, int32_t* __restrict__ und,
@@ -169,21 +172,22 @@ __global__ __launch_bounds__(256, (D * sizeof(E) == 256) ? 2 : 1) void k_project
     my_norm[f] = sqrtf(ss) * (1.0f + 0.0005f);
   }
 
-  float best1[RF][4], best2[RF][4];
-  int idx1[RF][4];
+  // Running top-2 per output element as integer keys: the score's float32 bits with
+  // the low `ib` bits replaced by the vector index.  Non-negative floats order like
+  // their bits, so among non-negative scores the keys order as the truncated scores
+  // (ties broken by index); negative scores order below every non-negative one.
+  // Per score: one and-or, one max, one med3.
+  const int ib = n_b > 1 ? 32 - __builtin_clz((unsigned)(n_b - 1)) : 0;
+  const int imask = (1 << ib) - 1;
+  int best1[RF][4], best2[RF][4];
 #pragma unroll
   for (int f = 0; f < RF; ++f)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      best1[f][v] = NEG_INF;
-      best2[f][v] = NEG_INF;
-      idx1[f][v] = 0;
+      best1[f][v] = INT32_MIN;
+      best2[f][v] = INT32_MIN;
     }
 
-  // +inf in a register the compiler cannot see through: med3(x, y, top) is max(x, y)
-  // without the canonicalising moves a folded maxnum would carry
-  float top = __builtin_huge_valf();
-  asm volatile("" : "+v"(top));
   for (int t = 0; t < nt; ++t) {
     // tile t's copies are complete once only tile t+1's remain outstanding
     if (t + 1 < nt)
@@ -201,18 +205,17 @@ __global__ __launch_bounds__(256, (D * sizeof(E) == 256) ? 2 : 1) void k_project
     for (int cb = 0; cb < G::TI / 16; ++cb) {
       Frag<E, D> bf;
       TileFrag<E, D>::load(bf, rows, cb * 16 + (l & 15));
-      const int bcol = b0 + cb * 16 + (l & 15);
+      // the vector index as one register (one and-or per score below)
+      const int bcol = settled(b0 + cb * 16 + (l & 15));
       const float pad = cb * 16 + (l & 15) < nvalid ? 0.0f : NEG_INF;
 #pragma unroll
       for (int f = 0; f < RF; ++f) {
         const f32x4 acc = mma_block(a[f], bf, f32x4{pad, pad, pad, pad});
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          // med3 forms of max and second-best
-          const float sc = acc[v];
-          idx1[f][v] = sc > best1[f][v] ? bcol : idx1[f][v];
-          best2[f][v] = __builtin_amdgcn_fmed3f(best1[f][v], best2[f][v], sc);
-          best1[f][v] = __builtin_amdgcn_fmed3f(best1[f][v], sc, top);
+          const int key = (__float_as_int(acc[v]) & ~imask) | bcol;
+          best2[f][v] = med3_i(best1[f][v], best2[f][v], key);
+          best1[f][v] = max(best1[f][v], key);
         }
       }
     }
@@ -222,21 +225,15 @@ __global__ __launch_bounds__(256, (D * sizeof(E) == 256) ? 2 : 1) void k_project
 #pragma unroll
   for (int f = 0; f < RF; ++f) {
     const int64_t row0 = ((int64_t)blockIdx.x * NW + w) * 16 * RF + 16 * f;
-    // Merge the top-2 summaries of the 16 lanes that hold each row.
+    // Merge the top-2 keys of the 16 lanes that hold each row.
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
 #pragma unroll
       for (int o = 1; o < 16; o <<= 1) {
-        const float ob1 = __shfl_xor(best1[f][v], o);
-        const float ob2 = __shfl_xor(best2[f][v], o);
-        const int oi = __shfl_xor(idx1[f][v], o);
-        const float lo1 = fminf(best1[f][v], ob1);
-        const bool take = ob1 > best1[f][v] || (ob1 == best1[f][v] && oi < idx1[f][v]);
-        best2[f][v] = fmaxf(lo1, fmaxf(best2[f][v], ob2));
-        if (take) {
-          best1[f][v] = ob1;
-          idx1[f][v] = oi;
-        }
+        const int ob1 = __shfl_xor(best1[f][v], o);
+        const int ob2 = __shfl_xor(best2[f][v], o);
+        best2[f][v] = max(min(best1[f][v], ob1), max(best2[f][v], ob2));
+        best1[f][v] = max(best1[f][v], ob1);
       }
     }
     uint64_t need_all = 0;
@@ -247,8 +244,13 @@ __global__ __launch_bounds__(256, (D * sizeof(E) == 256) ? 2 : 1) void k_project
       const int64_t row = row0 + r;
       // |float32 score - float64 score| <= beta (matrix-core accumulation bound + float64 rounding)
       const double beta = (double)beta_coef * (double)nrm * (double)bmax;
-      const bool decided = (double)best1[f][v] - (double)best2[f][v] > 2.0 * beta;
-      if (decided && (l & 15) == 0 && row < n) ids[row] = idx1[f][v];
+      // the winner's float32 score is at least s1; every other one is below s2 plus
+      // the truncation (at most s2 * 2^(ib - 23)), or negative when the second key is
+      const int k1 = best1[f][v], k2 = best2[f][v];
+      const double s1 = (double)__int_as_float(k1 & ~imask), s2 = (double)__int_as_float(k2 & ~imask);
+      const double other = k2 < 0 ? 0.0 : s2 + s2 * ldexp(1.0, ib - 22);
+      const bool decided = k1 >= 0 && s1 - other > 2.0 * beta;
+      if (decided && (l & 15) == 0 && row < n) ids[row] = k1 & imask;
       const uint64_t und = ballot(!decided && row < n);
       need_all |= (und & 0x0001000100010001ull) << v;    // bit 16*g + v
     }

@@ -281,7 +281,7 @@ constexpr int SEL_RAISE_EVERY = 32;   // insertions between two threshold raises
 // EXACT = true: only the flagged rows (a workgroup without one leaves at once), from
 //   the start of the window, with the exact compaction; rare (ties by the hundred).
 template <class E, int D, int NW, bool EXACT>
-__global__ __launch_bounds__(64 * NW) void k_sel_stream(SelectArgs p) {
+__global__ __launch_bounds__(64 * NW, 2) void k_sel_stream(SelectArgs p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   using G = TileGeom<E, D>;
   constexpr int TI = G::TI;
@@ -325,8 +325,6 @@ __global__ __launch_bounds__(64 * NW) void k_sel_stream(SelectArgs p) {
   // 16-item block; a row's four lanes are r, r+16, r+32, r+48.  Row state is one
   // scalar per lane, kept equal in the row's four lanes (vmx, the largest value
   // listed, is per lane: each covers the entries its lane wrote).
-  const uint64_t rowbits = 0x0001000100010001ull << r;   // the row's lanes
-  const uint64_t row_lt = rowbits & lanemask_lt();      // the row's lanes below this one
   const int pos = settled(rv ? p.pos[iA] : -1);
   const float bnd = settled(rv ? p.xnorm[iA] * p.ynorm_max[0] : 0.0f);   // every |logit| of the row is below
   const float beta = p.beta_coef * bnd;
@@ -434,6 +432,10 @@ __global__ __launch_bounds__(64 * NW) void k_sel_stream(SelectArgs p) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) any |= acc[cb][v] >= lo;
       if (ballot(any)) {
+        // this lane's candidates of the tile (bit 4 cb + v), counted once; the row's
+        // lanes then write to consecutive slots, lane g after lanes 0 .. g-1 of the
+        // row, each in (block, v) order
+        uint32_t cm = 0;
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
           u32x4 jj;
@@ -442,19 +444,31 @@ __global__ __launch_bounds__(64 * NW) void k_sel_stream(SelectArgs p) {
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             const int n = cb * 16 + 4 * g + v;
-            const int j = (int)jj[v];
-            const float a = acc[cb][v];
-            const bool cand = a >= lo && (full || n < nlim) && j != pos;
-            const uint64_t m2 = ballot(cand);
-            if (cand) {
-              const int slotn = cnt + popc(m2 & row_lt);
-              if (slotn < cap) list[slotn] = int2{j, __float_as_int(a)};
+            const bool cand = acc[cb][v] >= lo && (full || n < nlim) && (int)jj[v] != pos;
+            cm |= (uint32_t)cand << (4 * cb + v);
+          }
+        }
+        const int c0 = popc(cm);
+        const int c1 = __shfl_xor(c0, 16), c2 = __shfl_xor(c0, 32), c3 = __shfl_xor(c0, 48);   // lanes g^1, g^2, g^3
+        int slotn = cnt + ((g & 1) ? c1 : 0) + ((g & 2) ? c2 + c3 : 0);
+        cnt += c0 + c1 + c2 + c3;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          if (!((cm >> (4 * cb)) & 15u)) continue;
+          u32x4 jj;
+          const uint32_t ja = lds_addr(tid_ + cb * 16 + 4 * g);
+          LdsRead128<1>::run(&ja, &jj);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            if ((cm >> (4 * cb + v)) & 1u) {
+              const float a = acc[cb][v];
+              if (slotn < cap) list[slotn] = int2{(int)jj[v], __float_as_int(a)};
+              ++slotn;
               if constexpr (!EXACT) {
                 vmx = fmaxf(vmx, a);
                 lds_add_u32(hist_r + sel_bin(a, hlo, hsc), 1u);
               }
             }
-            cnt += popc(m2 & rowbits);
           }
         }
       }
