@@ -28,6 +28,7 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too sm
 EXPORTED = ["rece_plan", "rece_plan_destroy", "rece_workspace_bytes", "rece_forward",
             "rece_forward_static", "rece_backward", "rece_export", "rece_export_bytes", "rece_check",
             "rece_profile_enable", "rece_profile_read",
+            "rece_full_ce_workspace_bytes", "rece_full_ce_forward", "rece_full_ce_backward",
             "rece_status_string", "rece_last_error", "rece_version"]
 PHASES = ["project", "sort", "select", "loss", "bwd_dx", "bwd_dy", "bwd_sort", "other"]
 
@@ -70,13 +71,19 @@ def lib() -> ctypes.CDLL:
         L.rece_profile_enable.argtypes = [vp, i32]
         L.rece_profile_read.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_double),
                                         ctypes.POINTER(ctypes.c_int64)]
+        i64 = ctypes.c_int64
+        L.rece_full_ce_workspace_bytes.argtypes = [i64, sz]
+        L.rece_full_ce_forward.argtypes = [vp, i64, i64, i32, i32, vp, vp, vp, vp, ctypes.c_size_t, vp, vp]
+        L.rece_full_ce_backward.argtypes = [vp, i64, i64, i32, i32, vp, vp, vp, vp, ctypes.c_size_t, vp, vp, vp,
+                                            vp]
         L.rece_status_string.argtypes = [i32]
         L.rece_status_string.restype = ctypes.c_char_p
         L.rece_last_error.restype = ctypes.c_char_p
         L.rece_version.restype = ctypes.c_char_p
         for name in ("rece_plan", "rece_plan_destroy", "rece_workspace_bytes", "rece_forward",
                      "rece_forward_static", "rece_backward", "rece_export", "rece_export_bytes", "rece_check",
-                     "rece_profile_enable", "rece_profile_read"):
+                     "rece_profile_enable", "rece_profile_read", "rece_full_ce_workspace_bytes",
+                     "rece_full_ce_forward", "rece_full_ce_backward"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -254,6 +261,69 @@ class Plan:
 
     def check(self, saved, stream=None):
         _check(lib().rece_check(self._h, _stream(stream), _ptr(saved)))
+
+
+class FullCE:
+    """Exact full cross-entropy over the whole catalogue (no [s, C] tensor): the
+    forward pass leaves each position's log-sum-exp in `workspace` for the backward
+    pass.  Marshalling only; the sweeps run in librece's kernels."""
+
+    def __init__(self, s: int, C: int, d: int, dtype: str = "bf16"):
+        self.s, self.C, self.d, self.dtype = s, C, d, dtype
+        n = ctypes.c_size_t()
+        _check(lib().rece_full_ce_workspace_bytes(s, ctypes.byref(n)))
+        self.workspace_bytes = n.value
+
+    def _check_inputs(self, X, Y, pos, workspace):
+        import torch
+        want = torch.bfloat16 if self.dtype == "bf16" else torch.float32
+        if X.shape != (self.s, self.d) or Y.shape != (self.C, self.d) or pos.shape != (self.s,):
+            raise ValueError("X, Y, pos shapes do not match the full cross-entropy sizes")
+        if X.dtype != want or Y.dtype != want or pos.dtype != torch.int32:
+            raise ValueError("X, Y must have the plan dtype and pos int32")
+        if not (X.is_contiguous() and Y.is_contiguous() and pos.is_contiguous()):
+            raise ValueError("X, Y, pos must be contiguous")
+        if workspace.numel() * workspace.element_size() < self.workspace_bytes:
+            raise ValueError("workspace too small")
+        devs = {t.device for t in (X, Y, pos, workspace)}
+        if len(devs) != 1 or next(iter(devs)).type != "cuda":
+            raise ValueError("all tensors must be on one GPU")
+
+    def forward(self, X, Y, pos, workspace=None, loss_pp=True, stream=None):
+        import torch
+        dev = X.device
+        if workspace is None:
+            workspace = torch.empty(self.workspace_bytes, dtype=torch.uint8, device=dev)
+        self._check_inputs(X, Y, pos, workspace)
+        loss = torch.empty(1, dtype=torch.float32, device=dev)
+        lpp = torch.empty(self.s, dtype=torch.float32, device=dev) if loss_pp else None
+        _check(lib().rece_full_ce_forward(_stream(stream), self.s, self.C, self.d,
+                                          RECE_BF16 if self.dtype == "bf16" else RECE_F32, _ptr(X), _ptr(Y),
+                                          _ptr(pos), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                          _ptr(loss), _ptr(lpp)))
+        return loss, lpp, workspace
+
+    def backward(self, X, Y, pos, workspace, dloss=None, dloss_pp=None, dX=None, dY=None, stream=None):
+        import torch
+        dev = X.device
+        self._check_inputs(X, Y, pos, workspace)
+        if dloss is None and dloss_pp is None:
+            dloss = torch.ones(1, dtype=torch.float32, device=dev)
+        for t, n in ((dloss, 1), (dloss_pp, self.s)):
+            if t is not None and (t.dtype != torch.float32 or t.numel() != n or not t.is_contiguous()):
+                raise ValueError("dloss / dloss_pp must be contiguous float32 of 1 / s elements")
+        if dX is None:
+            dX = torch.empty((self.s, self.d), dtype=torch.float32, device=dev)
+        if dY is None:
+            dY = torch.empty((self.C, self.d), dtype=torch.float32, device=dev)
+        if dX.shape != (self.s, self.d) or dY.shape != (self.C, self.d) or dX.dtype != torch.float32 \
+                or dY.dtype != torch.float32 or not (dX.is_contiguous() and dY.is_contiguous()):
+            raise ValueError("dX, dY must be contiguous float32 [s, d] and [C, d]")
+        _check(lib().rece_full_ce_backward(_stream(stream), self.s, self.C, self.d,
+                                           RECE_BF16 if self.dtype == "bf16" else RECE_F32, _ptr(X), _ptr(Y),
+                                           _ptr(pos), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                           _ptr(dloss), _ptr(dloss_pp), _ptr(dX), _ptr(dY)))
+        return dX, dY
 
 
 def version() -> str:

@@ -595,6 +595,52 @@ rece_status rece_profile_read(rece_plan_t plan, int phase, double* total_ms, int
   return RECE_OK;
 }
 
+static rece_status check_full_ce(int64_t s, int64_t C, int32_t d, int32_t dtype, const void* X, const void* Y,
+                                 const int32_t* pos, const void* ws, size_t ws_bytes) {
+  if (s < 1 || C < 1) return fail(RECE_ERR_INVALID_ARGUMENT, "s and C must be >= 1");
+  if (s > ((int64_t)1 << 31) - 1 || C > ((int64_t)1 << 31) - 1)
+    return fail(RECE_ERR_UNSUPPORTED, "s and C must fit in int32");
+  if (d != 32 && d != 64 && d != 128 && d != 256) return fail(RECE_ERR_UNSUPPORTED, "d must be one of 32, 64, 128, 256");
+  if (dtype != RECE_F32 && dtype != RECE_BF16) return fail(RECE_ERR_UNSUPPORTED, "dtype must be RECE_F32 or RECE_BF16");
+  if (!X || !Y || !pos || !ws) return fail(RECE_ERR_INVALID_ARGUMENT, "NULL input or workspace pointer");
+  if ((reinterpret_cast<uintptr_t>(X) | reinterpret_cast<uintptr_t>(Y) | reinterpret_cast<uintptr_t>(ws)) % 16)
+    return fail(RECE_ERR_INVALID_ARGUMENT, "X, Y and workspace must be 16-byte aligned");
+  if (ws_bytes < rece::full_ce_workspace_bytes(s))
+    return fail(RECE_ERR_WORKSPACE_TOO_SMALL, "workspace smaller than rece_full_ce_workspace_bytes(s)");
+  return RECE_OK;
+}
+
+rece_status rece_full_ce_workspace_bytes(int64_t s, size_t* bytes) {
+  if (s < 1 || !bytes) return fail(RECE_ERR_INVALID_ARGUMENT, "s must be >= 1 and bytes non-NULL");
+  *bytes = rece::full_ce_workspace_bytes(s);
+  return RECE_OK;
+}
+
+rece_status rece_full_ce_forward(void* stream, int64_t s, int64_t C, int32_t d, int32_t dtype, const void* X,
+                                 const void* Y, const int32_t* pos, void* workspace, size_t workspace_bytes,
+                                 float* loss, float* loss_pp) {
+  const rece_status v = check_full_ce(s, C, d, dtype, X, Y, pos, workspace, workspace_bytes);
+  if (v != RECE_OK) return v;
+  if (!loss) return fail(RECE_ERR_INVALID_ARGUMENT, "loss is NULL");
+  RECE_HIP(rece::full_ce_forward(dtype == RECE_BF16, d, s, C, X, Y, pos, workspace, loss, loss_pp,
+                                 static_cast<hipStream_t>(stream)),
+           "full cross-entropy forward");
+  return RECE_OK;
+}
+
+rece_status rece_full_ce_backward(void* stream, int64_t s, int64_t C, int32_t d, int32_t dtype, const void* X,
+                                  const void* Y, const int32_t* pos, void* workspace, size_t workspace_bytes,
+                                  const float* dloss, const float* dloss_pp, float* dX, float* dY) {
+  const rece_status v = check_full_ce(s, C, d, dtype, X, Y, pos, workspace, workspace_bytes);
+  if (v != RECE_OK) return v;
+  if (!dloss && !dloss_pp) return fail(RECE_ERR_INVALID_ARGUMENT, "dloss and dloss_pp are both NULL");
+  if (!dX || !dY) return fail(RECE_ERR_INVALID_ARGUMENT, "dX or dY is NULL");
+  RECE_HIP(rece::full_ce_backward(dtype == RECE_BF16, d, s, C, X, Y, pos, workspace, dloss, dloss_pp, dX, dY,
+                                  static_cast<hipStream_t>(stream)),
+           "full cross-entropy backward");
+  return RECE_OK;
+}
+
 rece_status rece_workspace_bytes(rece_plan_t plan, size_t* scratch_bytes, size_t* saved_bytes) {
   if (!plan) return fail(RECE_ERR_INVALID_ARGUMENT, "plan is NULL");
   if (scratch_bytes) *scratch_bytes = plan->scratch_bytes;

@@ -135,6 +135,13 @@ int sort_digit_bits(int64_t n);
 hipError_t launch_counting_sort(const int32_t* keys, const int32_t* in_perm, int64_t n, int shift, int nbits,
                                 void* scratch, int32_t* perm_out, int32_t* inv_out, hipStream_t st);
 hipError_t launch_select(bool is_bf16, int d, int waves, const SelectArgs& a, hipStream_t st);
+// Exact full cross-entropy (k_fullce.hip): workspace = [2][s] float32 (log-sum-exp,
+// upstream gradient) + per-wave float64 loss sums.
+size_t full_ce_workspace_bytes(int64_t s);
+hipError_t full_ce_forward(bool bf16v, int d, int64_t s, int64_t C, const void* X, const void* Y, const int32_t* pos,
+                           void* ws, float* loss, float* loss_pp, hipStream_t st);
+hipError_t full_ce_backward(bool bf16v, int d, int64_t s, int64_t C, const void* X, const void* Y, const int32_t* pos,
+                            void* ws, const float* dloss, const float* dloss_pp, float* dX, float* dY, hipStream_t st);
 size_t select_lds_bytes(bool is_bf16, int d, int waves, int cap_lds);
 int select_list_cap(int k, int d, bool bf16);   // entries of a row's candidate list
 int select_finish_waves(int cap_lds);            // 0: a list of cap_lds entries does not fit in LDS

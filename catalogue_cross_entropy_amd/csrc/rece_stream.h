@@ -287,6 +287,36 @@ __device__ __forceinline__ void lds_read_b32x8(const uint32_t* a, float* r) {
       : "memory");
 }
 
+// N dwords from LDS (N = 2, 4, 8, 16), waited for inside.
+template <int N> struct LdsReadB32;
+template <> struct LdsReadB32<8> {
+  static __device__ __forceinline__ void run(const uint32_t* a, float* r) { lds_read_b32x8(a, r); }
+};
+template <> struct LdsReadB32<16> {
+  static __device__ __forceinline__ void run(const uint32_t* a, float* r) {
+    lds_read_b32x8(a, r);
+    lds_read_b32x8(a + 8, r + 8);
+  }
+};
+template <> struct LdsReadB32<4> {
+  static __device__ __forceinline__ void run(const uint32_t* a, float* r) {
+    asm volatile(
+        "ds_read_b32 %0, %4\n\tds_read_b32 %1, %5\n\tds_read_b32 %2, %6\n\tds_read_b32 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+        : "memory");
+  }
+};
+template <> struct LdsReadB32<2> {
+  static __device__ __forceinline__ void run(const uint32_t* a, float* r) {
+    asm volatile("ds_read_b32 %0, %2\n\tds_read_b32 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(r[0]), "=&v"(r[1])
+                 : "v"(a[0]), "v"(a[1])
+                 : "memory");
+  }
+};
+
 // Matrix-core fragment of tile row n (B operand, "row = vector" layout).
 template <class E, int D> struct TileFrag;
 

@@ -175,6 +175,34 @@ rece_status rece_backward(rece_plan_t plan, void* stream, const void* X, const v
                           const int32_t* pos, const float* dloss, const float* dloss_pp,
                           void* scratch, const void* saved, float* dX, float* dY);
 
+/* Exact full cross-entropy over the whole catalogue, the dense loss the reduced
+ * ones approximate: RECE page, Section 3, Eq. 3 (loss_i = log sum_j exp(x_i . y_j)
+ * - x_i . y_pos(i), mean over positions) and Eq. 4 (its gradient, softmax minus
+ * the one-hot of the positive).  Every logit is formed on the matrix cores and
+ * consumed on chip; nothing of size s x C is ever stored.  Three sweeps over the
+ * s x C logits: log-sum-exp (forward), then dX and dY (backward).
+ *   s, C, d, dtype  as in rece_config (d in {32, 64, 128, 256}; dtype RECE_F32 or
+ *                   RECE_BF16 for X and Y; float32 accumulation)
+ *   X [s][d], Y [C][d], pos [s] (0 <= pos < C, not checked)
+ *   workspace       caller-owned device buffer of rece_full_ce_workspace_bytes(s)
+ *                   bytes; the forward call leaves each position's log-sum-exp in
+ *                   it for the backward call (same X, Y, pos), untouched between
+ *   loss [1], loss_pp [s] (or NULL)       forward outputs, float32
+ *   dloss [1] / dloss_pp [s] (or NULL)    upstream gradient of the mean loss / of
+ *                                         each per-position loss (dloss_pp wins)
+ *   dX [s][d], dY [C][d] float32          backward outputs, overwritten
+ * Deterministic (no atomics).  Errors: NULL pointers, bad sizes or a workspace
+ * smaller than required -> RECE_ERR_INVALID_ARGUMENT / RECE_ERR_WORKSPACE_TOO_SMALL;
+ * unsupported d, dtype or sizes -> RECE_ERR_UNSUPPORTED; a failed launch ->
+ * RECE_ERR_HIP.  Host work only for the size query. */
+rece_status rece_full_ce_workspace_bytes(int64_t s, size_t* bytes);
+rece_status rece_full_ce_forward(void* stream, int64_t s, int64_t C, int32_t d, int32_t dtype, const void* X,
+                                 const void* Y, const int32_t* pos, void* workspace, size_t workspace_bytes,
+                                 float* loss, float* loss_pp);
+rece_status rece_full_ce_backward(void* stream, int64_t s, int64_t C, int32_t d, int32_t dtype, const void* X,
+                                  const void* Y, const int32_t* pos, void* workspace, size_t workspace_bytes,
+                                  const float* dloss, const float* dloss_pp, float* dX, float* dY);
+
 /* Intermediate results kept in `saved` (the steps of Algorithm 1, RECE page,
  * Section 3), copied asynchronously into the caller's `dst`. */
 typedef enum {

@@ -208,3 +208,32 @@ def test_static_forward_rejects_plans_beyond_its_array():
     assert L.rece_forward_static(p._h, None, 16, 16, 16, 16, 16, 16, None) == 3
     assert "static scratch" in L.rece_last_error().decode()
     assert L.rece_forward_static(None, None, 16, 16, 16, 16, 16, 16, None) == 1
+
+
+def test_full_ce_entry_points_reject_bad_arguments():
+    import ctypes as C
+    L = rece.lib()
+    n = C.c_size_t()
+    assert L.rece_full_ce_workspace_bytes(0, C.byref(n)) == 1
+    assert L.rece_full_ce_workspace_bytes(1000, C.byref(n)) == 0
+    # log-sum-exp and upstream gradient per position, plus the per-wave loss sums
+    assert n.value >= 1000 * 8
+    fake = C.c_void_p(1 << 20)   # never dereferenced: the checks come before any launch
+    args = dict(s=1000, C=5000, d=64, dtype=rece.RECE_BF16)
+
+    def fwd(**kw):
+        a = dict(args, **kw)
+        return L.rece_full_ce_forward(None, a["s"], a["C"], a["d"], a["dtype"], fake, fake, fake,
+                                      kw.get("ws", fake), kw.get("wsb", n.value), kw.get("loss", fake), None)
+
+    assert fwd(d=48) == 2                      # unsupported d
+    assert fwd(dtype=7) == 2                   # unsupported dtype
+    assert fwd(s=0) == 1 and fwd(C=0) == 1     # empty
+    assert fwd(s=1 << 31) == 2                 # beyond int32 ids
+    assert fwd(ws=None) == 1                   # NULL workspace
+    assert fwd(wsb=n.value - 1) == 3           # workspace too small
+    assert fwd(loss=None) == 1                 # NULL loss
+    assert L.rece_full_ce_backward(None, 1000, 5000, 64, rece.RECE_BF16, fake, fake, fake, fake, n.value,
+                                   None, None, fake, fake) == 1   # no upstream gradient
+    assert L.rece_full_ce_backward(None, 1000, 5000, 64, rece.RECE_BF16, fake, fake, fake, fake, n.value,
+                                   fake, None, None, fake) == 1   # NULL dX
