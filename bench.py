@@ -291,6 +291,34 @@ def cpu_baseline(inp, per_worker_items=8192, chunks_per_worker=2, seed=0):
            "math": "NumPy float64 elementwise (no BLAS call on the timed path)"}
 
 
+def time_full_ce(w, X, Y, pos, steps):
+    """The exact full cross-entropy (every item scored, no [s, C] tensor) on the same
+    inputs: one untimed step, then `steps` timed fwd+bwd steps."""
+    import torch
+    import catalogue_cross_entropy_amd as rece
+    f = rece.FullCE(w.s, w.C, w.d, dtype=w.dtype)
+    ws = torch.empty(f.workspace_bytes, dtype=torch.uint8, device=X.device)
+    dX = torch.empty((w.s, w.d), dtype=torch.float32, device=X.device)
+    dY = torch.empty((w.C, w.d), dtype=torch.float32, device=X.device)
+
+    def step():
+        f.forward(X, Y, pos, ws, loss_pp=False)
+        f.backward(X, Y, pos, ws, dX=dX, dY=dY)
+
+    step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    flops = 2.0 * w.s * w.C * w.d * 5     # logits (3 sweeps) and the two gradient products
+    return {"ms_per_step": round(ms, 3), "value": w.s / (ms * 1e-3), "unit": "positions/s", "steps": steps,
+            "workspace_bytes": f.workspace_bytes, "mfma_frac": round(flops / (ms * 1e-3) / 1e12 /
+                                                                     (SPEC_BF16_TFLOPS if w.dtype == "bf16"
+                                                                      else SPEC_FP32_TFLOPS), 4)}
+
+
 def measure_peaks(dev):
     from catalogue_cross_entropy_amd import peaks
     return {"bf16_tflops": round(peaks.mfma_bf16_tflops(dev), 1), "copy_gbs": round(peaks.copy_gbs(dev), 1),
@@ -305,6 +333,8 @@ def main():
     ap.add_argument("--workload", default="tenmillion")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true", help="skip the device peak probes")
+    ap.add_argument("--full-ce-steps", type=int, default=1,
+                    help="exact full cross-entropy fwd+bwd steps timed next to the reduced loss (0: skip)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after the run, one device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -388,6 +418,7 @@ def main():
     plan.check(saved)
     counters = plan.export(saved, "counters").cpu().tolist()
 
+    full = time_full_ce(w, X, Y, pos, args.full_ce_steps) if args.full_ce_steps > 0 else None
     peaks = None if args.no_peaks else measure_peaks(dev)
 
     ms_step = elapsed * 1e3 / args.steps
@@ -443,6 +474,9 @@ def main():
         "counters": {"argmax_rows_float64": counters[1], "topk_rows_near_tie": counters[2],
                      "logits_float64": counters[3], "overflows": counters[4]},
     }
+    if full is not None:
+        full["rece_speedup"] = round(full["ms_per_step"] / ms_step, 2)
+        out["full_ce"] = full
     if cpu is not None:
         out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)

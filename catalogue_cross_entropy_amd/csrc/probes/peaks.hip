@@ -27,20 +27,47 @@ __global__ __launch_bounds__(THREADS) void k_mfma_loop(int iters, float* __restr
     a[t] = (__bf16)((float)((threadIdx.x + t) & 7) * 0.0078125f);
     b[t] = (__bf16)((float)((threadIdx.x * 3 + t) & 7) * 0.0078125f);
   }
-  f32x4 acc[CHAINS];
-  for (int c = 0; c < CHAINS; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // eight named accumulators (an indexed array invites register shuffles between
+  // iterations)
+  const float z = (float)threadIdx.x * 0x1p-40f;   // distinct starting values keep them apart
+  f32x4 c0 = {z, 0.f, 0.f, 0.f}, c1 = {0.f, z, 0.f, 0.f}, c2 = {0.f, 0.f, z, 0.f}, c3 = {0.f, 0.f, 0.f, z};
+  f32x4 c4 = {2 * z, 0.f, 0.f, 0.f}, c5 = {0.f, 2 * z, 0.f, 0.f}, c6 = {0.f, 0.f, 2 * z, 0.f}, c7 = {0.f, 0.f, 0.f, 2 * z};
+  // as one assembly block: the compiler otherwise moves the accumulators between
+  // register files on every iteration.  Wait states around the block (the
+  // compiler's hazard checks do not see into it): after the plain writes of the
+  // starting values, and before the results are read.
+  asm volatile("s_nop 7" ::);
   for (int it = 0; it < iters; ++it) {
-#pragma unroll
-    for (int c = 0; c < CHAINS; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[c], 0, 0, 0);
+    asm volatile(
+        "v_mfma_f32_16x16x32_bf16 %0, %8, %9, %0\n\t"
+        "v_mfma_f32_16x16x32_bf16 %1, %8, %9, %1\n\t"
+        "v_mfma_f32_16x16x32_bf16 %2, %8, %9, %2\n\t"
+        "v_mfma_f32_16x16x32_bf16 %3, %8, %9, %3\n\t"
+        "v_mfma_f32_16x16x32_bf16 %4, %8, %9, %4\n\t"
+        "v_mfma_f32_16x16x32_bf16 %5, %8, %9, %5\n\t"
+        "v_mfma_f32_16x16x32_bf16 %6, %8, %9, %6\n\t"
+        "v_mfma_f32_16x16x32_bf16 %7, %8, %9, %7"
+        : "+v"(c0), "+v"(c1), "+v"(c2), "+v"(c3), "+v"(c4), "+v"(c5), "+v"(c6), "+v"(c7)
+        : "v"(a), "v"(b));
   }
-  float s = 0.f;
-  for (int c = 0; c < CHAINS; ++c) s += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::);
+  const f32x4 t = ((c0 + c1) + (c2 + c3)) + ((c4 + c5) + (c6 + c7));
+  const float s = t[0] + t[1] + t[2] + t[3];
   sink[(size_t)blockIdx.x * THREADS + threadIdx.x] = s;
 }
 
+// Four 16-byte loads in flight per thread, then their four stores.
 __global__ __launch_bounds__(THREADS) void k_copy16(const uint4* __restrict__ src, uint4* __restrict__ dst, size_t n) {
   const size_t stride = (size_t)gridDim.x * THREADS;
-  for (size_t i = (size_t)blockIdx.x * THREADS + threadIdx.x; i < n; i += stride) dst[i] = src[i];
+  size_t i = (size_t)blockIdx.x * THREADS + threadIdx.x;
+  for (; i + 3 * stride < n; i += 4 * stride) {
+    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+    dst[i] = a;
+    dst[i + stride] = b;
+    dst[i + 2 * stride] = c;
+    dst[i + 3 * stride] = d;
+  }
+  for (; i < n; i += stride) dst[i] = src[i];
 }
 
 }  // namespace
