@@ -17,6 +17,8 @@
 //   k_sce_merge       per position, the exact top-k of the union of its bucket
 //                     lists (duplicates removed), its threshold and sums, and
 //                     its kept list, which the backward pass reads as RECE's.
+#include <algorithm>
+
 #include "rece_device.h"
 #include "rece_internal.h"
 #include "rece_kth.h"
@@ -368,11 +370,8 @@ __host__ __device__ constexpr size_t merge_wave_bytes(int k) { return topk_wave_
 size_t merge_lds_bytes(int k) { return 4 * ((merge_wave_bytes(k) + 15) / 16 * 16); }
 
 template <class E, int D>
-__global__ __launch_bounds__(256) void k_sce_merge(MergeArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  const int w = threadIdx.x >> 6, l = lane_id();
-  const int64_t i = (int64_t)blockIdx.x * 4 + w;
-  if (i >= a.s) return;   // whole wave leaves; no block barrier in this kernel
+__device__ __forceinline__ void sce_merge_row(const MergeArgs& a, char* smem, int w, int64_t i, uint32_t& nexact) {
+  const int l = lane_id();
   const int k = a.k;
   char* base = smem + (size_t)w * ((merge_wave_bytes(k) + 15) / 16 * 16);
   const MergeLds L = carve_topk(base, 2 * k);
@@ -380,7 +379,6 @@ __global__ __launch_bounds__(256) void k_sce_merge(MergeArgs a) {
   const E* Y = static_cast<const E*>(a.Y);
   const E* xrow = X + i * D;
   const float beta = a.beta_coef * a.xnorm[i] * __uint_as_float(a.ymax_bits[0]);
-  uint32_t nexact = 0;
 
   const int g0 = a.pstart[i], g1 = a.pend[i];
   int cnt = 0;
@@ -456,6 +454,17 @@ __global__ __launch_bounds__(256) void k_sce_merge(MergeArgs a) {
     a.ssum[i] = cnt > 0 ? se : 0.0f;
     a.nmem[i] = cnt;
   }
+}
+
+// A fixed grid: each wave takes positions w0, w0 + waves, ... (no block barrier in
+// this kernel); the float64 count is flushed once per wave (one shared address).
+template <class E, int D>
+__global__ __launch_bounds__(256) void k_sce_merge(MergeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int w = threadIdx.x >> 6;
+  const int64_t waves = (int64_t)gridDim.x * 4;
+  uint32_t nexact = 0;
+  for (int64_t i = (int64_t)blockIdx.x * 4 + w; i < a.s; i += waves) sce_merge_row<E, D>(a, smem, w, i, nexact);
   flush_count(a.counters + CNT_LOGIT_EXACT, nexact);
 }
 
@@ -466,7 +475,11 @@ static hipError_t launch_mg(const MergeArgs& a, hipStream_t st) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3((unsigned)((a.s + 3) / 4)), dim3(256), lds, st, a);
+  int64_t fit = 0;
+  e = resident_blocks(reinterpret_cast<const void*>(kern), 256, lds, &fit);
+  if (e != hipSuccess) return e;
+  const int64_t want = (a.s + 3) / 4;
+  hipLaunchKernelGGL(kern, dim3((unsigned)std::max<int64_t>(1, std::min(want, fit))), dim3(256), lds, st, a);
   return hipGetLastError();
 }
 

@@ -663,16 +663,22 @@ static hipError_t launch_sel(const SelectArgs& a, hipStream_t st) {
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   // as many workgroups as fit on the device at once (each wave loops over rows)
-  int dev = 0, cus = 0, per_cu = 0;
-  e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e == hipSuccess)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fin), 64 * nwf, lds);
+  int64_t fit = 0;
+  e = resident_blocks(reinterpret_cast<const void*>(fin), 64 * nwf, lds, &fit);
   if (e != hipSuccess) return e;
   const int64_t want = (a.s + nwf - 1) / nwf;
-  const int64_t fit = (int64_t)std::max(cus, 1) * std::max(per_cu, 1);
   hipLaunchKernelGGL(fin, dim3((unsigned)std::max<int64_t>(1, std::min(want, fit))), dim3(64 * nwf), lds, st, a);
   return hipGetLastError();
+}
+
+hipError_t resident_blocks(const void* kernel, int threads, size_t lds, int64_t* out) {
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds);
+  if (e != hipSuccess) return e;
+  *out = (int64_t)std::max(cus, 1) * std::max(per_cu, 1);
+  return hipSuccess;
 }
 
 hipError_t launch_select(bool is_bf16, int d, int waves, const SelectArgs& a, hipStream_t st) {

@@ -135,6 +135,8 @@ int sort_digit_bits(int64_t n);
 hipError_t launch_counting_sort(const int32_t* keys, const int32_t* in_perm, int64_t n, int shift, int nbits,
                                 void* scratch, int32_t* perm_out, int32_t* inv_out, hipStream_t st);
 hipError_t launch_select(bool is_bf16, int d, int waves, const SelectArgs& a, hipStream_t st);
+// Workgroups of `kernel` (threads, dynamic LDS bytes) resident on the current device at once.
+hipError_t resident_blocks(const void* kernel, int threads, size_t lds, int64_t* out);
 // Exact full cross-entropy (k_fullce.hip): workspace = [2][s] float32 (log-sum-exp,
 // upstream gradient) + per-wave float64 loss sums.
 size_t full_ce_workspace_bytes(int64_t s);
