@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librece.so"
 
 RECE_F32, RECE_BF16 = 0, 1
 RECE_VARIANT_RECE, RECE_VARIANT_SCE = 0, 1
-FLAG_VALIDATE_IDS, FLAG_KEEP_STAGES = 1, 2
+FLAG_VALIDATE_IDS, FLAG_KEEP_STAGES, FLAG_IGNORE_NEGATIVE_POS, FLAG_BF16_GRADS = 1, 2, 4, 8
 
 STAGES = {
     "bucket_x": 0, "bucket_y": 1, "perm_x": 2, "perm_y": 3, "thresh_id": 4,
@@ -110,13 +110,16 @@ class Plan:
     def __init__(self, s: int, C: int, d: int, n_b: int, n_c: int, k: int, rounds: int = 1,
                  dtype: str = "bf16", variant: str = "rece", b_x: int = 0, b_y: int = 0,
                  keep_stages: bool = False, validate_ids: bool = False, n_ec: int = 1,
-                 window_wrap: bool = True):
+                 window_wrap: bool = True, ignore_negative_pos: bool = False, bf16_grads: bool = False):
         self.cfg = ReceConfig(s, C, d, n_b, n_c, n_ec, k, rounds, b_x, b_y,
                               RECE_BF16 if dtype == "bf16" else RECE_F32,
                               RECE_VARIANT_SCE if variant == "sce" else RECE_VARIANT_RECE,
                               int(window_wrap),
                               (FLAG_KEEP_STAGES if keep_stages else 0)
-                              | (FLAG_VALIDATE_IDS if validate_ids else 0))
+                              | (FLAG_VALIDATE_IDS if validate_ids else 0)
+                              | (FLAG_IGNORE_NEGATIVE_POS if ignore_negative_pos else 0)
+                              | (FLAG_BF16_GRADS if bf16_grads else 0))
+        self.bf16_grads = bool(bf16_grads)
         self.dtype = dtype
         self._h = ctypes.c_void_p()
         _check(lib().rece_plan(ctypes.byref(self.cfg), ctypes.byref(self._h)))
@@ -194,23 +197,24 @@ class Plan:
 
     def backward(self, X, Y, pos, scratch, saved, dloss=None, dloss_pp=None, dX=None, dY=None,
                  stream=None):
-        """Returns (dX [s, d] float32, dY [C, d] float32)."""
+        """Returns (dX [s, d], dY [C, d]): float32, or bf16 for a plan made with bf16_grads."""
         import torch
         self._check_inputs(X, Y, pos)
         c = self.cfg
+        gdt = torch.bfloat16 if self.bf16_grads else torch.float32
         if dloss is None and dloss_pp is None:
             dloss = torch.ones(1, dtype=torch.float32, device=X.device)
         if dX is None:
-            dX = torch.empty((c.s, c.d), dtype=torch.float32, device=X.device)
+            dX = torch.empty((c.s, c.d), dtype=gdt, device=X.device)
         if dY is None:
-            dY = torch.empty((c.C, c.d), dtype=torch.float32, device=X.device)
-        for name, t, shape in (("dX", dX, (c.s, c.d)), ("dY", dY, (c.C, c.d)), ("dloss", dloss, (1,)),
-                               ("dloss_pp", dloss_pp, (c.s,))):
+            dY = torch.empty((c.C, c.d), dtype=gdt, device=X.device)
+        for name, t, shape, dt in (("dX", dX, (c.s, c.d), gdt), ("dY", dY, (c.C, c.d), gdt),
+                                   ("dloss", dloss, (1,), torch.float32),
+                                   ("dloss_pp", dloss_pp, (c.s,), torch.float32)):
             if t is None:
                 continue
-            if (t.dtype != torch.float32 or tuple(t.shape) != shape or not t.is_contiguous()
-                    or t.device != X.device):
-                raise ValueError(f"{name} must be a contiguous float32 tensor of shape {shape} on {X.device}")
+            if t.dtype != dt or tuple(t.shape) != shape or not t.is_contiguous() or t.device != X.device:
+                raise ValueError(f"{name} must be a contiguous {dt} tensor of shape {shape} on {X.device}")
         self._check_workspace(scratch, saved, X.device)
         _check(lib().rece_backward(self._h, _stream(stream), _ptr(X), _ptr(Y), _ptr(pos),
                                    _ptr(dloss), _ptr(dloss_pp), _ptr(scratch), _ptr(saved),
@@ -261,6 +265,48 @@ class Plan:
 
     def check(self, saved, stream=None):
         _check(lib().rece_check(self._h, _stream(stream), _ptr(saved)))
+
+
+class ReceLossFunction:
+    """torch.autograd.Function over a Plan: forward = rece_forward (mean loss),
+    backward = rece_backward with the incoming gradient of the loss.  The random
+    vectors B (RECE: [rounds, d, n_b]; SCE: [d, n_b]) are an input: the caller
+    draws them (fresh per step, as the method does) and they get no gradient.
+    Gradients come back in the plan's gradient dtype (bf16_grads: bf16), which must
+    match X and Y's dtype for autograd."""
+
+    _fn = None
+
+    @classmethod
+    def get(cls):
+        if cls._fn is None:
+            import torch
+
+            class _F(torch.autograd.Function):
+                @staticmethod
+                def forward(ctx, X, Y, pos, B, plan):
+                    loss, _, scratch, saved = plan.forward(X, Y, pos, B, loss_pp=False)
+                    ctx.save_for_backward(X, Y, pos)
+                    ctx.plan, ctx.scratch, ctx.saved = plan, scratch, saved
+                    return loss.reshape(())
+
+                @staticmethod
+                def backward(ctx, g):
+                    X, Y, pos = ctx.saved_tensors
+                    dloss = g.reshape(1).to(torch.float32).contiguous()
+                    dX, dY = ctx.plan.backward(X, Y, pos, ctx.scratch, ctx.saved, dloss=dloss)
+                    ctx.scratch = ctx.saved = None
+                    return (dX if ctx.needs_input_grad[0] else None, dY if ctx.needs_input_grad[1] else None,
+                            None, None, None)
+
+            cls._fn = _F
+        return cls._fn
+
+
+def rece_loss(X, Y, pos, B, plan: "Plan"):
+    """Mean RECE (or SCE) loss with autograd: X [s, d], Y [C, d], pos [s] int32 (with
+    a plan made with ignore_negative_pos, negative ids mark padding)."""
+    return ReceLossFunction.get().apply(X, Y, pos, B, plan)
 
 
 class FullCE:

@@ -21,8 +21,39 @@
 
 namespace rece {
 
-// Upstream gradient of position i's loss.
+// Write (or clear) row j of dY: EPL floats of lane `sub`.
+template <int EPL>
+__device__ __forceinline__ void store_row(float* dst, const float (&v)[EPL]) {
+#pragma unroll
+  for (int t = 0; t < EPL / 4; ++t)
+    reinterpret_cast<float4*>(dst)[t] = float4{v[4 * t], v[4 * t + 1], v[4 * t + 2], v[4 * t + 3]};
+}
+
+// EPL gradient values at element `off` of a float32 or (b16) bf16 output.
+template <int EPL>
+__device__ __forceinline__ void store_grad(void* base, int64_t off, const float (&v)[EPL], bool b16) {
+  if (b16) {
+    uint32_t w[EPL / 2];
+#pragma unroll
+    for (int t = 0; t < EPL / 2; ++t) w[t] = bf16_bits_rne(v[2 * t]) | (bf16_bits_rne(v[2 * t + 1]) << 16);
+    uint16_t* d = static_cast<uint16_t*>(base) + off;
+    if constexpr (EPL == 8)
+      *reinterpret_cast<u32x4*>(d) = u32x4{w[0], w[1], w[2], w[3]};
+    else
+#pragma unroll
+      for (int t = 0; t < EPL / 2; ++t) reinterpret_cast<uint32_t*>(d)[t] = w[t];
+  } else {
+    store_row<EPL>(static_cast<float*>(base) + off, v);
+  }
+}
+
+// Upstream gradient of position i's loss (0 for padding under the mask, whose
+// mean counts only the other positions).
 __device__ __forceinline__ float gbar_of(const BwdArgs& p, int64_t i) {
+  if (p.ignore) {
+    if (p.pos[i] < 0) return 0.0f;
+    return p.dloss_pp ? p.dloss_pp[i] : p.dloss[0] * p.wmean[0];
+  }
   return p.dloss_pp ? p.dloss_pp[i] : p.dloss[0] / (float)p.s;
 }
 
@@ -133,11 +164,7 @@ __global__ __launch_bounds__(256) void k_dx_lists(BwdArgs p) {
   for (int o = LPR; o < WAVE; o <<= 1)
 #pragma unroll
     for (int t = 0; t < EPL; ++t) acc[t] += __shfl_xor(acc[t], o);
-  if (q == 0) {
-    float4* dst = reinterpret_cast<float4*>(p.dX + i * D + sub * EPL);
-#pragma unroll
-    for (int t = 0; t < EPL / 4; ++t) dst[t] = float4{acc[4 * t], acc[4 * t + 1], acc[4 * t + 2], acc[4 * t + 3]};
-  }
+  if (q == 0) store_grad<EPL>(p.dX, i * D + sub * EPL, acc, p.grad_bf16 != 0);
 }
 
 // ------------------------------------------------------------------ exports
@@ -369,14 +396,6 @@ struct DyArea {
   int64_t nsub;
 };
 
-// Write (or clear) row j of dY: EPL floats of lane `sub`.
-template <int EPL>
-__device__ __forceinline__ void store_row(float* dst, const float (&v)[EPL]) {
-#pragma unroll
-  for (int t = 0; t < EPL / 4; ++t)
-    reinterpret_cast<float4*>(dst)[t] = float4{v[4 * t], v[4 * t + 1], v[4 * t + 2], v[4 * t + 3]};
-}
-
 // One lane group (LPR lanes, 16 bytes of a row each) per sub-piece of DY_SUB sorted
 // pairs.  For each pair (j, i): l = x_i . y_j (float32, the same lane split and
 // order as k_dx_lists), g = gbar_i exp(l - lse_i), or the position's positive
@@ -406,9 +425,10 @@ __global__ __launch_bounds__(256) void k_dy_pieces(BwdArgs p, const int32_t* __r
   float zero[EPL];
 #pragma unroll
   for (int t = 0; t < EPL; ++t) zero[t] = 0.0f;
-  float* dY = p.dY;
+  void* dY = p.dY;
+  const bool b16 = p.grad_bf16 != 0;
   if (n == 0) {   // no pair at all: piece 0 clears every row
-    for (int64_t j = 0; j < C; ++j) store_row<EPL>(dY + j * D + sub * EPL, zero);
+    for (int64_t j = 0; j < C; ++j) store_grad<EPL>(dY, j * D + sub * EPL, zero, b16);
     if (sub == 0) area.flags[0] = 0;
     return;
   }
@@ -424,14 +444,14 @@ __global__ __launch_bounds__(256) void k_dy_pieces(BwdArgs p, const int32_t* __r
 
   // rows of items [a, b) cleared
   auto clear_rows = [&](int64_t a, int64_t b) {
-    for (int64_t j = a; j < b; ++j) store_row<EPL>(dY + j * D + sub * EPL, zero);
+    for (int64_t j = a; j < b; ++j) store_grad<EPL>(dY, j * D + sub * EPL, zero, b16);
   };
   // the run of item cur over [run_start, t_end) is complete
   auto flush = [&](int64_t t_end) {
     const bool head = run_start == t0 && cur == prev_key;
     const bool tail = t_end == t1 && t1 < n && cur == next_key;
     if (!head && !tail) {
-      store_row<EPL>(dY + (int64_t)cur * D + sub * EPL, acc);
+      store_grad<EPL>(dY, (int64_t)cur * D + sub * EPL, acc, b16);
     } else if (head) {
       store_row<EPL>(area.partial + (piece * 2 + 0) * D + sub * EPL, acc);
       head_item = cur;
@@ -521,7 +541,7 @@ __global__ __launch_bounds__(256) void k_dy_pieces(BwdArgs p, const int32_t* __r
 // Items spanning sub-pieces: the sub-piece where such an item starts adds the head
 // rows of the following sub-pieces, in order, to its tail row and writes dY.
 template <int D>
-__global__ __launch_bounds__(256) void k_dy_combine(float* __restrict__ dY, const uint32_t* __restrict__ ntot,
+__global__ __launch_bounds__(256) void k_dy_combine(void* __restrict__ dY, int b16, const uint32_t* __restrict__ ntot,
                                                     DyArea area) {
   constexpr int EPL = 4;
   constexpr int LPR = D / EPL;
@@ -542,7 +562,7 @@ __global__ __launch_bounds__(256) void k_dy_combine(float* __restrict__ dY, cons
     for (int t = 0; t < EPL; ++t) acc[t] += h[t];
     if (!(area.flags[qq] & 2)) break;
   }
-  store_row<EPL>(dY + (int64_t)area.items[piece * 2 + 1] * D + sub * EPL, acc);
+  store_grad<EPL>(dY, (int64_t)area.items[piece * 2 + 1] * D + sub * EPL, acc, b16 != 0);
 }
 
 // ------------------------------------------------------------------ launchers
@@ -648,7 +668,7 @@ static hipError_t launch_dy_t(const BwdArgs& a, const int32_t* K, const int32_t*
   if (e != hipSuccess) return e;
   constexpr int CRPI = WAVE / (D / 4) > 0 ? WAVE / (D / 4) : 1;
   hipLaunchKernelGGL((k_dy_combine<D>), dim3((unsigned)((ar.nsub + 4 * CRPI - 1) / (4 * CRPI))), dim3(256), 0, st,
-                     a.dY, ntot, ar);
+                     a.dY, a.grad_bf16, ntot, ar);
   return hipGetLastError();
 }
 

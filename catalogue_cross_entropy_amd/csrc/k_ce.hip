@@ -17,6 +17,7 @@ constexpr int CE_POS_PER_BLOCK = 16;   // 4 waves x 4 positions, 16 lanes each
 template <class E, int D>
 __global__ __launch_bounds__(256) void k_ce(CeArgs a) {
   __shared__ double part[CE_POS_PER_BLOCK];
+  __shared__ float cnt[CE_POS_PER_BLOCK];
   const E* X = reinterpret_cast<const E*>(a.X);
   const E* Y = reinterpret_cast<const E*>(a.Y);
   const int l = lane_id(), w = threadIdx.x >> 6;
@@ -24,10 +25,12 @@ __global__ __launch_bounds__(256) void k_ce(CeArgs a) {
   const int slot = w * 4 + sub;
   const int64_t i = (int64_t)blockIdx.x * CE_POS_PER_BLOCK + slot;
   float loss = 0.0f;
+  float counted = 0.0f;
   if (i < a.s) {
     int j = a.pos[i];
+    const bool pad = a.ignore && j < 0;
     if (j < 0 || j >= a.C) {
-      if (a.validate && li == 0) atomicOr(a.counters + CNT_ERROR, (uint32_t)ERRBIT_BAD_ID);
+      if (a.validate && !pad && li == 0) atomicOr(a.counters + CNT_ERROR, (uint32_t)ERRBIT_BAD_ID);
       j = j < 0 ? 0 : (int)(a.C - 1);
     }
     const E* x = X + i * D;
@@ -47,35 +50,58 @@ __global__ __launch_bounds__(256) void k_ce(CeArgs a) {
       const int64_t o = (int64_t)r * a.s + i;
       if (a.nmem[o] > 0) Z += a.ssum[o] * expf(a.mshift[o] - m);
     }
+    // (a padding position keeps a proper log-sum-exp, with item 0 standing in for its
+    // positive, so that exp(logit - lse) stays bounded; its loss is 0)
     const float lse = m + logf(Z);
-    loss = lse - lpos;
+    loss = pad ? 0.0f : lse - lpos;
+    counted = pad ? 0.0f : 1.0f;
     if (li == 0) {
       a.lse[i] = lse;
       a.lpos[i] = lpos;
       if (a.loss_pp) a.loss_pp[i] = loss;
     }
   }
-  if (li == 0) part[slot] = (double)loss;
+  if (li == 0) {
+    part[slot] = (double)loss;
+    cnt[slot] = counted;
+  }
   __syncthreads();
   if (threadIdx.x == 0) {
-    double t = 0.0;
-    for (int q = 0; q < CE_POS_PER_BLOCK; ++q) t += part[q];
-    reinterpret_cast<double*>(a.partial)[blockIdx.x] = t;
+    double t = 0.0, n = 0.0;
+    for (int q = 0; q < CE_POS_PER_BLOCK; ++q) {
+      t += part[q];
+      n += cnt[q];
+    }
+    reinterpret_cast<double*>(a.partial)[2 * blockIdx.x] = t;
+    reinterpret_cast<double*>(a.partial)[2 * blockIdx.x + 1] = n;
   }
 }
 
-__global__ __launch_bounds__(256) void k_mean(const double* __restrict__ partial, int nb, int64_t s,
-                                              float* __restrict__ loss) {
-  __shared__ double sh[256];
-  double t = 0.0;
-  for (int q = threadIdx.x; q < nb; q += 256) t += partial[q];
+// Mean over the positions counted (all of them without the padding mask; none
+// counted gives 0), fixed order; also the weight 1 / count of a position in it.
+__global__ __launch_bounds__(256) void k_mean(const double* __restrict__ partial, int nb, int64_t s, int ignore,
+                                              float* __restrict__ loss, float* __restrict__ wmean) {
+  __shared__ double sh[256], shn[256];
+  double t = 0.0, c = 0.0;
+  for (int q = threadIdx.x; q < nb; q += 256) {
+    t += partial[2 * q];
+    c += partial[2 * q + 1];
+  }
   sh[threadIdx.x] = t;
+  shn[threadIdx.x] = c;
   __syncthreads();
   for (int off = 128; off >= 1; off >>= 1) {
-    if ((int)threadIdx.x < off) sh[threadIdx.x] += sh[threadIdx.x + off];
+    if ((int)threadIdx.x < off) {
+      sh[threadIdx.x] += sh[threadIdx.x + off];
+      shn[threadIdx.x] += shn[threadIdx.x + off];
+    }
     __syncthreads();
   }
-  if (threadIdx.x == 0) loss[0] = (float)(sh[0] / (double)s);
+  if (threadIdx.x == 0) {
+    const double n = ignore ? shn[0] : (double)s;
+    loss[0] = n > 0.0 ? (float)(sh[0] / n) : 0.0f;
+    if (wmean) wmean[0] = n > 0.0 ? (float)(1.0 / n) : 0.0f;
+  }
 }
 
 // Rounds (RECE page, Section 3: the procedure repeated over rounds, with a
@@ -295,7 +321,8 @@ template <class E, int D>
 static hipError_t launch_ce_t(const CeArgs& a, float* loss, hipStream_t st) {
   const int nb = ce_blocks(a.s);
   hipLaunchKernelGGL((k_ce<E, D>), dim3(nb), dim3(256), 0, st, a);
-  hipLaunchKernelGGL(k_mean, dim3(1), dim3(256), 0, st, reinterpret_cast<const double*>(a.partial), nb, a.s, loss);
+  hipLaunchKernelGGL(k_mean, dim3(1), dim3(256), 0, st, reinterpret_cast<const double*>(a.partial), nb, a.s, a.ignore,
+                     loss, a.wmean);
   return hipGetLastError();
 }
 

@@ -40,11 +40,6 @@ __host__ __device__ constexpr size_t fce_slot_bytes() {
   return (size_t)TileGeom<E, D>::ROW_BYTES + 3 * 256;
 }
 
-__device__ __forceinline__ uint32_t bf16_rne(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
 typedef __attribute__((address_space(3))) short4v lds_short4;
 
 // Four 16-bit values of coordinate 16*nb + (l % 16) for rows r0 .. r0 + 3 of a
@@ -82,8 +77,8 @@ __device__ __forceinline__ void accumulate_rows(f32x4 (&acc)[D / 16], const floa
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
         const float g0 = gv[2 * ks + (e >> 2)][e & 3], g1 = gv[2 * ks + (e >> 2)][(e & 3) + 1];
-        const uint32_t h0 = bf16_rne(g0), h1 = bf16_rne(g1);
-        const uint32_t l0 = bf16_rne(g0 - __uint_as_float(h0 << 16)), l1 = bf16_rne(g1 - __uint_as_float(h1 << 16));
+        const uint32_t h0 = bf16_bits_rne(g0), h1 = bf16_bits_rne(g1);
+        const uint32_t l0 = bf16_bits_rne(g0 - __uint_as_float(h0 << 16)), l1 = bf16_bits_rne(g1 - __uint_as_float(h1 << 16));
         ph[e / 2] = h0 | (h1 << 16);
         pl[e / 2] = l0 | (l1 << 16);
       }

@@ -179,6 +179,12 @@ __device__ __forceinline__ int xcd_block(int b, int nblocks) {
 }
 
 // Outward rounding of a float64 interval end to float32.
+// bf16 bit pattern of x, rounded to nearest even.
+__device__ __forceinline__ uint32_t bf16_bits_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
 __device__ __forceinline__ float f_down(double v) { return __double2float_rd(v); }
 __device__ __forceinline__ float f_up(double v) { return __double2float_ru(v); }
 

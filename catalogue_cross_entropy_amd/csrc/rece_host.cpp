@@ -103,7 +103,7 @@ struct rece_plan_s {
   int64_t npairs;     // rounds * s * k list entries + s positives
   // saved (forward -> backward)
   size_t o_cnt, o_bx, o_by, o_px, o_py, o_te, o_tid, o_tlo, o_thi, o_msh, o_ssum, o_nmem, o_xnorm, o_ymax, o_lse,
-      o_lpos, o_negs, saved_bytes;
+      o_lpos, o_wmean, o_negs, saved_bytes;
   // forward scratch
   size_t o_bt, o_bnorm, o_und, o_undy, o_sorty, o_sort, o_part, o_negl, o_xs, o_ys, o_cl0, o_cl1, o_cn0, o_cn1, o_cd0,
       o_cd1, o_clo0, o_clo1;
@@ -174,7 +174,8 @@ static rece_status validate_config(const rece_config* c) {
   if (c->k < 0 || c->k > c->C - 1) return fail(RECE_ERR_INVALID_ARGUMENT, "k must be in 0..C-1");
   if (c->rounds < 1 || c->rounds > MAX_ROUNDS) return fail(RECE_ERR_INVALID_ARGUMENT, "rounds must be in 1..8");
   if (c->dtype != RECE_F32 && c->dtype != RECE_BF16) return fail(RECE_ERR_INVALID_ARGUMENT, "unknown dtype");
-  if (c->flags & ~(RECE_FLAG_VALIDATE_IDS | RECE_FLAG_KEEP_STAGES))
+  if (c->flags & ~(RECE_FLAG_VALIDATE_IDS | RECE_FLAG_KEEP_STAGES | RECE_FLAG_IGNORE_NEGATIVE_POS |
+                   RECE_FLAG_BF16_GRADS))
     return fail(RECE_ERR_INVALID_ARGUMENT, "unknown flag bits");
   if ((int64_t)c->rounds * c->s * std::max(c->k, 1) + c->s > ((int64_t)1 << 31) - 1)
     return fail(RECE_ERR_UNSUPPORTED, "rounds * s * k + s must fit in int32 (the backward's pair records)");
@@ -223,6 +224,7 @@ static void plan_sce_layout(rece_plan_s* p) {
   p->o_ymax = sv.take(4);
   p->o_lse = sv.take((size_t)s * 4);
   p->o_lpos = sv.take((size_t)s * 4);
+  p->o_wmean = sv.take(16);
   p->o_negs = sv.take((size_t)s * k * 4);   // the final kept lists: the backward reads them
   p->saved_bytes = sv.off;
 
@@ -232,7 +234,7 @@ static void plan_sce_layout(rece_plan_s* p) {
   const size_t sort_b = std::max({sort_scratch_bytes(sx, 1 << std::min(12, bits_for(s))),
                                   sort_scratch_bytes(sy, 1 << std::min(12, bits_for(C)))});
   p->o_sort = sc.take(sort_b);
-  p->o_part = sc.take((size_t)ce_blocks(s) * 8);
+  p->o_part = sc.take((size_t)ce_blocks(s) * 16);
   p->o_xs = sc.take((size_t)sx * d * p->esize);   // rows taken by each bucket, bucket-major
   p->o_ys = sc.take((size_t)sy * d * p->esize);
   p->o_ssort = sc.take((size_t)sx * 4);
@@ -425,6 +427,8 @@ static rece_status sce_forward(const rece_plan_s& p, hipStream_t st, const void*
   ce.partial = reinterpret_cast<float*>(sc + p.o_part);
   ce.counters = counters;
   ce.validate = (c.flags & RECE_FLAG_VALIDATE_IDS) ? 1 : 0;
+  ce.ignore = (c.flags & RECE_FLAG_IGNORE_NEGATIVE_POS) ? 1 : 0;
+  ce.wmean = reinterpret_cast<float*>(sv + p.o_wmean);
   RECE_PHASE(RECE_PHASE_LOSS, launch_ce(p.bf16, d, ce, loss, st), "loss");
   return RECE_OK;
 }
@@ -509,6 +513,7 @@ rece_status rece_plan(const rece_config* cfg, rece_plan_t* out) {
   p->o_ymax = sv.take(4);
   p->o_lse = sv.take((size_t)s * 4);
   p->o_lpos = sv.take((size_t)s * 4);
+  p->o_wmean = sv.take(16);
   p->o_negs = sv.take((size_t)r * s * std::max(k, 1) * 4);   // kept lists: the backward reads them
   p->saved_bytes = sv.off;
 
@@ -519,7 +524,7 @@ rece_status rece_plan(const rece_config* cfg, rece_plan_t* out) {
   p->o_undy = sc.take((size_t)std::max(s, C) * 4);   // chains on the side stream (items, later positions)
   p->o_sorty = sc.take(std::max(sort_scratch_bytes(C, 1 << p->nbits_b), sort_scratch_bytes(s, 1 << p->nbits_b)));
   p->o_sort = sc.take(std::max(sort_scratch_bytes(s, 1 << p->nbits_b), sort_scratch_bytes(C, 1 << p->nbits_b)));
-  p->o_part = sc.take((size_t)ce_blocks(s) * 8);
+  p->o_part = sc.take((size_t)ce_blocks(s) * 16);
   // float32 logits of the kept lists of rounds >= 1 (the round dedup sums the new pairs)
   p->o_negl = sc.take((size_t)(r - 1) * s * k * 4);
   // sorted copies of every round (each chunk and window one block of rows)
@@ -815,6 +820,8 @@ static rece_status forward_impl(const rece_plan_s& p, hipStream_t st, const void
   ce.partial = reinterpret_cast<float*>(sc + p.o_part);
   ce.counters = counters;
   ce.validate = (c.flags & RECE_FLAG_VALIDATE_IDS) ? 1 : 0;
+  ce.ignore = (c.flags & RECE_FLAG_IGNORE_NEGATIVE_POS) ? 1 : 0;
+  ce.wmean = reinterpret_cast<float*>(sv + p.o_wmean);
   RECE_PHASE(RECE_PHASE_LOSS, launch_ce(p.bf16, d, ce, loss, st), "loss");
   return RECE_OK;
 }
@@ -856,8 +863,8 @@ rece_status set_last_error(rece_status st, const char* msg) { return fail(st, ms
 extern "C" {
 
 rece_status rece_backward(rece_plan_t plan, void* stream, const void* X, const void* Y, const int32_t* pos,
-                          const float* dloss, const float* dloss_pp, void* scratch, const void* saved, float* dX,
-                          float* dY) {
+                          const float* dloss, const float* dloss_pp, void* scratch, const void* saved, void* dX,
+                          void* dY) {
   if (!plan) return fail(RECE_ERR_INVALID_ARGUMENT, "plan is NULL");
   if (!X || !Y || !pos || !scratch || !saved || !dX || !dY || (!dloss && !dloss_pp))
     return fail(RECE_ERR_INVALID_ARGUMENT, "NULL pointer argument");
@@ -885,6 +892,9 @@ rece_status rece_backward(rece_plan_t plan, void* stream, const void* X, const v
   b.lpos = reinterpret_cast<const float*>(sv + p.o_lpos);
   b.dloss = dloss;
   b.dloss_pp = dloss_pp;
+  b.wmean = reinterpret_cast<const float*>(sv + p.o_wmean);
+  b.ignore = (c.flags & RECE_FLAG_IGNORE_NEGATIVE_POS) ? 1 : 0;
+  b.grad_bf16 = (c.flags & RECE_FLAG_BF16_GRADS) ? 1 : 0;
   b.dX = dX;
   b.dY = dY;
   b.pcoef = reinterpret_cast<const float*>(sc + p.o_pcoef);

@@ -70,9 +70,11 @@ struct CeArgs {
   float* lse;
   float* lpos;
   float* loss_pp;             // nullable
-  float* partial;             // [num blocks]
+  float* partial;             // [num blocks][2] float64: loss sum, positions counted
+  float* wmean;               // [1] out: the mean's weight of a position (1 / positions counted)
   uint32_t* counters;
   int validate;
+  int ignore;                 // pos < 0 marks padding (no loss, not counted)
 };
 
 // Round dedup (rounds >= 1): the pairs of round rho's kept list that an earlier
@@ -101,8 +103,11 @@ struct BwdArgs {
   const float* dloss;         // [1]
   const float* dloss_pp;      // [s] or nullptr
   const float* pcoef;         // [s][4]: lse, upstream gradient, positive coefficient, 0 (launch_pos_coef)
-  float* dX;                  // [s][d]
-  float* dY;                  // [C][d]
+  const float* wmean;         // [1] the mean's weight of a position (forward pass)
+  int ignore;                 // pos < 0 marks padding: upstream gradient 0
+  int grad_bf16;              // dX, dY written as bf16
+  void* dX;                   // [s][d] float32 (or bf16)
+  void* dY;                   // [C][d] float32 (or bf16)
 };
 
 // Stable LSD counting sort of the (item, position) records of the backward pass:

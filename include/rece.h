@@ -67,6 +67,12 @@ typedef enum { RECE_VARIANT_RECE = 0, RECE_VARIANT_SCE = 1 } rece_variant;
 
 /* flags */
 #define RECE_FLAG_VALIDATE_IDS 1u  /* device check that 0 <= pos[i] < C (error word) */
+#define RECE_FLAG_IGNORE_NEGATIVE_POS 4u  /* padding mask: positions with pos[i] < 0 are padding.
+                                            They stay rows of X (bucketed, sorted and chunked
+                                            like the others) but have loss 0, no gradient, and
+                                            the mean is over the other positions (0 if none). */
+#define RECE_FLAG_BF16_GRADS 8u    /* rece_backward writes dX and dY as bf16 (round to
+                                      nearest even) instead of float32 */
 #define RECE_FLAG_KEEP_STAGES 2u   /* accepted, no effect: the kept lists are always kept
                                       (the backward pass reads them) */
 
@@ -167,13 +173,15 @@ rece_status rece_forward_static(rece_plan_t plan, void* stream, const void* X, c
  * the selection held fixed.
  *   dloss    [1] float32   upstream gradient of the mean loss (ignored if dloss_pp)
  *   dloss_pp [s] float32   upstream gradient of each per-position loss, or NULL
- *   dX [s][d], dY [C][d] float32   out: overwritten with the gradients (rows of
- *                                  items that no position scored are zero).
+ *   dX [s][d], dY [C][d] float32 (bf16 with RECE_FLAG_BF16_GRADS)   out: overwritten
+ *                                  with the gradients (rows of items that no position
+ *                                  scored are zero; padding positions' rows are zero
+ *                                  under RECE_FLAG_IGNORE_NEGATIVE_POS).
  * Deterministic: no float atomics; two calls give identical bits.  Errors as
  * for rece_forward. */
 rece_status rece_backward(rece_plan_t plan, void* stream, const void* X, const void* Y,
                           const int32_t* pos, const float* dloss, const float* dloss_pp,
-                          void* scratch, const void* saved, float* dX, float* dY);
+                          void* scratch, const void* saved, void* dX, void* dY);
 
 /* Exact full cross-entropy over the whole catalogue, the dense loss the reduced
  * ones approximate: RECE page, Section 3, Eq. 3 (loss_i = log sum_j exp(x_i . y_j)

@@ -183,7 +183,7 @@ def logsumexp(v) -> float:
 
 
 def rece_forward(X, Y, pos, B, n_c: int, k: int, rows=None, n_ec: int = 1, wrap: bool = True,
-                 buckets=None) -> dict:
+                 buckets=None, ignore_negative: bool = False) -> dict:
     """RECE loss (RECE page, Section 3: Algorithm 1 and the rounds paragraph).
 
     B has shape [r, d, n_b] (one independent draw of the random vectors per round).
@@ -195,6 +195,9 @@ def rece_forward(X, Y, pos, B, n_c: int, k: int, rows=None, n_ec: int = 1, wrap:
     cover every position and item, since they decide the chunks.  ``buckets``
     (optional, one (bx, by) pair per round) replaces the bucket labels: the steps
     after the labelling are then recomputed from the given labels.
+    ``ignore_negative``: a position with a negative positive id is padding; it is
+    bucketed, sorted and chunked like any other row of X (and no item is excluded
+    from its candidates), but its loss is 0 and the mean is over the other positions.
     """
     X = np.asarray(X, dtype=np.float64)
     Y = np.asarray(Y, dtype=np.float64)
@@ -213,11 +216,11 @@ def rece_forward(X, Y, pos, B, n_c: int, k: int, rows=None, n_ec: int = 1, wrap:
         st["perm_x"].append(px)
         st["perm_y"].append(py)
         st["negs"].append(round_negatives(X, Y, pos, px, py, n_c, k, rows, n_ec, wrap))
-    st.update(_loss(X, Y, pos, st["negs"], rows))
+    st.update(_loss(X, Y, pos, st["negs"], rows, ignore_negative))
     return st
 
 
-def loss_from_negatives(X, Y, pos, negs, rows=None) -> dict:
+def loss_from_negatives(X, Y, pos, negs, rows=None, ignore_negative: bool = False) -> dict:
     """The loss given each round's negative sets, the steps after the selection.
 
     ``negs[rho]`` maps a position id to the item ids it kept in round rho (any
@@ -238,19 +241,21 @@ def loss_from_negatives(X, Y, pos, negs, rows=None) -> dict:
             d[int(i)] = (ids, lg, None)
         full.append(d)
     st = {"negs": full}
-    st.update(_loss(X, Y, pos, full, rows))
+    st.update(_loss(X, Y, pos, full, rows, ignore_negative))
     return st
 
 
-def _loss(X, Y, pos, negs, rows) -> dict:
+def _loss(X, Y, pos, negs, rows, ignore_negative=False) -> dict:
     """Per-position loss over the positive and the rounds' negatives (RECE page,
     Algorithm 1, the positive-logit, loss and mean steps; Section 3, the duplicate
-    rule for pairs kept in several rounds)."""
+    rule for pairs kept in several rounds).  Padding positions (``ignore_negative``
+    and a negative positive id) have loss 0 and stay out of the mean."""
     s = X.shape[0]
     rounds = len(negs)
     rows = np.arange(s) if rows is None else np.asarray(rows, dtype=np.int64)
+    pad = np.array([bool(ignore_negative) and pos[i] < 0 for i in rows], dtype=bool)
     # positive logit: the scalar product with the positive's own (original) item row
-    l_pos = np.array([seq_dot(X[i], Y[pos[i]][None, :])[0, 0] for i in rows])
+    l_pos = np.array([0.0 if pad[n] else seq_dot(X[i], Y[pos[i]][None, :])[0, 0] for n, i in enumerate(rows)])
     lse = np.empty(len(rows))
     loss = np.empty(len(rows))
     union, mult = [], []
@@ -265,11 +270,12 @@ def _loss(X, Y, pos, negs, rows) -> dict:
         adj = np.array([lg - np.log(count[int(j)]) for j, lg in zip(copy_ids, copy_lg)])
         lse[n] = logsumexp(np.concatenate([[l_pos[n]], adj]))
         # negative log of the positive's softmax share over the scored set
-        loss[n] = lse[n] - l_pos[n]
+        loss[n] = 0.0 if pad[n] else lse[n] - l_pos[n]
         union.append(uniq.astype(np.int64))
         mult.append(cnt.astype(np.int64))
-    return dict(rows=rows, l_pos=l_pos, lse=lse, loss_pp=loss, union=union, mult=mult,
-                loss=float(np.mean(loss)) if len(rows) else 0.0)
+    counted = int(np.sum(~pad))
+    return dict(rows=rows, l_pos=l_pos, lse=lse, loss_pp=loss, union=union, mult=mult, pad=pad,
+                loss=float(np.sum(loss) / counted) if counted else 0.0)
 
 
 def rece_backward(X, Y, pos, fwd: dict, dloss: float = 1.0, dloss_pp=None):
@@ -288,9 +294,13 @@ def rece_backward(X, Y, pos, fwd: dict, dloss: float = 1.0, dloss_pp=None):
     rounds = len(fwd["negs"])
     dX = np.zeros_like(X)
     dY = np.zeros_like(Y)
+    pad = fwd.get("pad", np.zeros(len(fwd["rows"]), dtype=bool))
+    counted = int(np.sum(~pad))
     for n, i in enumerate(fwd["rows"]):
         i = int(i)
-        gbar = (dloss / len(fwd["rows"])) if dloss_pp is None else float(dloss_pp[i])
+        if pad[n]:   # padding: no gradient
+            continue
+        gbar = (dloss / counted) if dloss_pp is None else float(dloss_pp[i])
         lse = fwd["lse"][n]
         count = dict(zip(fwd["union"][n].tolist(), fwd["mult"][n].tolist()))
         g_pos = np.exp(fwd["l_pos"][n] - lse) - 1.0

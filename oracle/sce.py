@@ -113,9 +113,12 @@ def merge_negatives(per_bucket: dict, s: int, k: int):
     return out
 
 
-def sce_forward(X, Y, pos, B, b_x: int, b_y: int, k: int) -> dict:
+def sce_forward(X, Y, pos, B, b_x: int, b_y: int, k: int, ignore_negative: bool = False) -> dict:
     """SCE bucket-variant loss; B has shape [d, n_b].  The result uses the same
-    keys as the RECE oracle (one round), so its backward applies unchanged."""
+    keys as the RECE oracle (one round), so its backward applies unchanged.
+    ``ignore_negative``: positions with a negative positive id are padding, taken
+    by buckets like any other row (nothing excluded from their candidates), with
+    loss 0 and outside the mean."""
     X = np.asarray(X, dtype=np.float64)
     Y = np.asarray(Y, dtype=np.float64)
     pos = np.asarray(pos, dtype=np.int64)
@@ -123,14 +126,16 @@ def sce_forward(X, Y, pos, B, b_x: int, b_y: int, k: int) -> dict:
     R, Q = bucket_lists(X, Y, B, b_x, b_y)
     negs = merge_negatives(bucket_negatives(X, Y, pos, R, Q, k), s, k)
     rows = np.arange(s)
-    l_pos = np.array([seq_dot(X[i], Y[pos[i]][None, :])[0, 0] for i in rows])
+    pad = np.array([bool(ignore_negative) and pos[i] < 0 for i in rows], dtype=bool)
+    l_pos = np.array([0.0 if pad[i] else seq_dot(X[i], Y[pos[i]][None, :])[0, 0] for i in rows])
     lse = np.array([logsumexp(np.concatenate([[l_pos[i]], negs[i][1]])) for i in rows])
-    loss = lse - l_pos
+    loss = np.where(pad, 0.0, lse - l_pos)
     union = [negs[i][0] for i in rows]
     mult = [np.ones(len(u), dtype=np.int64) for u in union]
+    counted = int(np.sum(~pad))
     return {"R": R, "Q": Q, "negs": [negs], "rows": rows, "l_pos": l_pos, "lse": lse,
-            "loss_pp": loss, "union": union, "mult": mult,
-            "loss": float(np.mean(loss)) if s else 0.0}
+            "loss_pp": loss, "union": union, "mult": mult, "pad": pad,
+            "loss": float(np.sum(loss) / counted) if counted else 0.0}
 
 
 def sce_backward(X, Y, pos, fwd: dict, dloss: float = 1.0, dloss_pp=None):

@@ -411,3 +411,35 @@ def test_full_ce_matches_plain_definition():
     gX, gY = oracle.full_ce_grad(X, Y, pos)
     # Eq. 4 range: every logit gradient in (-1, 1) / s, chained: check gY sums to zero over items
     assert np.allclose(gY.sum(axis=0), 0.0, atol=1e-14)
+
+
+def test_padding_mask_equals_weighted_unmasked_loss():
+    """Padding (a negative positive id, the mask reading): the masked loss is the mean,
+    over the other positions, of the per-position losses of a run in which the
+    padding rows carry any positive (a row's selection depends only on its own
+    positive), and the masked gradients are that run's gradients with upstream
+    weights 1/n_valid on the other positions and 0 on padding."""
+    import numpy as np
+    import oracle
+    from rece_inputs import make_inputs, scaled
+    w = scaled("tiny", seqs=2, seqlen=40, C=300, n_b=4, n_c=4, k=12, rounds=2, seed=31)
+    inp = make_inputs(w)
+    rng = np.random.default_rng(4)
+    pad = rng.random(w.s) < 0.25
+    pos_m = inp.pos.copy()
+    pos_m[pad] = -1
+    pos_u = inp.pos.copy()                                  # padding rows given their original positive
+    f_m = oracle.rece_forward(inp.X, inp.Y, pos_m, inp.B, w.n_c, w.k, ignore_negative=True)
+    f_u = oracle.rece_forward(inp.X, inp.Y, pos_u, inp.B, w.n_c, w.k)
+    nv = int((~pad).sum())
+    assert np.all(f_m["loss_pp"][pad] == 0.0)
+    assert np.allclose(f_m["loss_pp"][~pad], f_u["loss_pp"][~pad], rtol=1e-12, atol=0)
+    assert abs(f_m["loss"] - f_u["loss_pp"][~pad].mean()) <= 1e-12 * max(1.0, abs(f_m["loss"]))
+    gX_m, gY_m = oracle.rece_backward(inp.X, inp.Y, pos_m, f_m)
+    wts = np.where(pad, 0.0, 1.0 / nv)
+    gX_u, gY_u = oracle.rece_backward(inp.X, inp.Y, pos_u, f_u, dloss_pp=wts)
+    assert np.all(gX_m[pad] == 0.0)
+    assert np.allclose(gX_m, gX_u, rtol=1e-12, atol=1e-15) and np.allclose(gY_m, gY_u, rtol=1e-12, atol=1e-15)
+    # without padding ids the mask changes nothing
+    f_0 = oracle.rece_forward(inp.X, inp.Y, pos_u, inp.B, w.n_c, w.k, ignore_negative=True)
+    assert f_0["loss"] == f_u["loss"]
