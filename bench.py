@@ -387,7 +387,10 @@ def main():
     logit_bytes = 2 * w.s * w.C
     largest = max(scratch.numel(), saved.numel(), dX.numel() * 4, dY.numel() * 4,
                   X.numel() * X.element_size(), Y.numel() * Y.element_size())
+    model = rece.auto_size(w.s, w.C, w.n_ec, w.n_b / max(w.n_c, 1), w.rounds) if w.variant == "rece" else None
     memory = {"scratch_bytes": plan.scratch_bytes, "saved_bytes": plan.saved_bytes,
+              "pages_memory_model_bytes_4B": None if model is None else 4 * model["model_elems"],
+              "pages_optimal_n_b": None if model is None else model["n_b"],
               "peak_allocated_bytes": torch.cuda.max_memory_allocated(dev),
               "largest_buffer_bytes": largest, "dense_logits_bf16_bytes": logit_bytes,
               "no_dense_logits": largest < logit_bytes}

@@ -28,7 +28,7 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too sm
 EXPORTED = ["rece_plan", "rece_plan_destroy", "rece_workspace_bytes", "rece_forward",
             "rece_forward_static", "rece_backward", "rece_export", "rece_export_bytes", "rece_check",
             "rece_profile_enable", "rece_profile_read",
-            "rece_full_ce_workspace_bytes", "rece_full_ce_forward", "rece_full_ce_backward",
+            "rece_full_ce_workspace_bytes", "rece_full_ce_forward", "rece_full_ce_backward", "rece_auto_size",
             "rece_status_string", "rece_last_error", "rece_version"]
 PHASES = ["project", "sort", "select", "loss", "bwd_dx", "bwd_dy", "bwd_sort", "other"]
 
@@ -76,6 +76,9 @@ def lib() -> ctypes.CDLL:
         L.rece_full_ce_forward.argtypes = [vp, i64, i64, i32, i32, vp, vp, vp, vp, ctypes.c_size_t, vp, vp]
         L.rece_full_ce_backward.argtypes = [vp, i64, i64, i32, i32, vp, vp, vp, vp, ctypes.c_size_t, vp, vp, vp,
                                             vp]
+        L.rece_auto_size.argtypes = [i64, i64, i32, ctypes.c_double, i32, ctypes.POINTER(ctypes.c_int32),
+                                     ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double),
+                                     ctypes.POINTER(ctypes.c_double)]
         L.rece_status_string.argtypes = [i32]
         L.rece_status_string.restype = ctypes.c_char_p
         L.rece_last_error.restype = ctypes.c_char_p
@@ -83,7 +86,7 @@ def lib() -> ctypes.CDLL:
         for name in ("rece_plan", "rece_plan_destroy", "rece_workspace_bytes", "rece_forward",
                      "rece_forward_static", "rece_backward", "rece_export", "rece_export_bytes", "rece_check",
                      "rece_profile_enable", "rece_profile_read", "rece_full_ce_workspace_bytes",
-                     "rece_full_ce_forward", "rece_full_ce_backward"):
+                     "rece_full_ce_forward", "rece_full_ce_backward", "rece_auto_size"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -265,6 +268,22 @@ class Plan:
 
     def check(self, saved, stream=None):
         _check(lib().rece_check(self._h, _stream(stream), _ptr(saved)))
+
+
+def auto_size(s: int, C: int, n_ec: int = 1, alpha_bc: float = 1.0, rounds: int = 1) -> dict:
+    """The RECE page's sizing rule (n_b*, n_c) and memory model; see rece_auto_size."""
+    nb, nc = ctypes.c_int32(), ctypes.c_int32()
+    me, fr = ctypes.c_double(), ctypes.c_double()
+    _check(lib().rece_auto_size(s, C, n_ec, float(alpha_bc), rounds, ctypes.byref(nb), ctypes.byref(nc),
+                                ctypes.byref(me), ctypes.byref(fr)))
+    return {"n_b": nb.value, "n_c": nc.value, "model_elems": me.value, "full_ratio": fr.value}
+
+
+def auto_plan(s: int, C: int, d: int, k: int, rounds: int = 1, n_ec: int = 1, alpha_bc: float = 1.0,
+              **kw) -> "Plan":
+    """A Plan with n_b and n_c from the page's rule for the lowest peak memory."""
+    a = auto_size(s, C, n_ec, alpha_bc, rounds)
+    return Plan(s, C, d, a["n_b"], a["n_c"], k, rounds, n_ec=n_ec, **kw)
 
 
 class ReceLossFunction:

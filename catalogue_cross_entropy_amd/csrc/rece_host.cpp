@@ -600,6 +600,22 @@ rece_status rece_profile_read(rece_plan_t plan, int phase, double* total_ms, int
   return RECE_OK;
 }
 
+rece_status rece_auto_size(int64_t s, int64_t C, int32_t n_ec, double alpha_bc, int32_t rounds, int32_t* n_b,
+                           int32_t* n_c, double* model_elems, double* full_ratio) {
+  if (s < 1 || C < 1 || n_ec < 0 || !(alpha_bc > 0.0) || rounds < 1)
+    return fail(RECE_ERR_INVALID_ARGUMENT, "need s, C, rounds >= 1, n_ec >= 0 and alpha_bc > 0");
+  const double mn = (double)std::min(C, s), mx = (double)std::max(C, s);
+  const double span = 1.0 + 2.0 * (double)n_ec;
+  const double nb = std::sqrt(4.0 * alpha_bc * span * mn);
+  const int32_t nbi = (int32_t)std::max(1.0, std::min(std::floor(nb + 0.5), 2147483647.0));
+  if (n_b) *n_b = nbi;
+  if (n_c) *n_c = (int32_t)std::max(1.0, std::min(std::floor(nbi / alpha_bc + 0.5), 2147483647.0));
+  const double root = std::sqrt(alpha_bc * span * mn);
+  if (model_elems) *model_elems = 2.0 * rounds * root * mx;
+  if (full_ratio) *full_ratio = std::sqrt(mn) / (2.0 * rounds * std::sqrt(alpha_bc * span));
+  return RECE_OK;
+}
+
 static rece_status check_full_ce(int64_t s, int64_t C, int32_t d, int32_t dtype, const void* X, const void* Y,
                                  const int32_t* pos, const void* ws, size_t ws_bytes) {
   if (s < 1 || C < 1) return fail(RECE_ERR_INVALID_ARGUMENT, "s and C must be >= 1");

@@ -122,6 +122,20 @@ typedef struct rece_plan_s* rece_plan_t;
 rece_status rece_plan(const rece_config* cfg, rece_plan_t* out);
 rece_status rece_plan_destroy(rece_plan_t plan);
 
+/* Plan sizing by the RECE page's rule (Section 3, the sentences on the optimal
+ * number of random vectors and on memory complexity), host only:
+ *   n_b* = sqrt(4 alpha_bc (1 + 2 n_ec) min(C, s))   (s = batch x sequence length,
+ *          alpha_bc = n_b / n_c), rounded to the nearest integer, at least 1;
+ *   n_c  = n_b* / alpha_bc, rounded, at least 1;
+ *   model_elems = 2 r sqrt(alpha_bc (1 + 2 n_ec) min(C, s)) max(C, s), the page's
+ *          peak-memory model (elements of the method's intermediate arrays);
+ *   full_ratio  = sqrt(min(C, s)) / (2 r sqrt(alpha_bc (1 + 2 n_ec))), the page's
+ *          ratio of full cross-entropy's memory to that model.
+ * Any output pointer may be NULL.  Errors: s, C < 1, n_ec < 0, alpha_bc <= 0 or
+ * rounds < 1 -> RECE_ERR_INVALID_ARGUMENT. */
+rece_status rece_auto_size(int64_t s, int64_t C, int32_t n_ec, double alpha_bc, int32_t rounds, int32_t* n_b,
+                           int32_t* n_c, double* model_elems, double* full_ratio);
+
 /* Bytes of the two caller-provided device buffers (owned by the caller):
  *   scratch: temporaries of one call (sorted copies, histograms, the
  *            backward's sorted pairs); may be reused freely between calls;

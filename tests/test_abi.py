@@ -237,3 +237,46 @@ def test_full_ce_entry_points_reject_bad_arguments():
                                    None, None, fake, fake) == 1   # no upstream gradient
     assert L.rece_full_ce_backward(None, 1000, 5000, 64, rece.RECE_BF16, fake, fake, fake, fake, n.value,
                                    fake, None, None, fake) == 1   # NULL dX
+
+
+def test_auto_size_follows_the_pages_rule():
+    import math
+    # n_b* = sqrt(4 alpha (1 + 2 n_ec) min(C, s)); the model 2 r sqrt(alpha (1 + 2 n_ec) min) max
+    a = rece.auto_size(32768, 10_000_000, n_ec=1, alpha_bc=1.0, rounds=3)
+    assert a["n_b"] == round(math.sqrt(4 * 3 * 32768)) == 627 and a["n_c"] == 627
+    assert a["model_elems"] == pytest.approx(2 * 3 * math.sqrt(3 * 32768) * 10_000_000)
+    assert a["full_ratio"] == pytest.approx(math.sqrt(32768) / (2 * 3 * math.sqrt(3)))
+    # the model times the ratio is full cross-entropy's s x C
+    assert a["model_elems"] * a["full_ratio"] == pytest.approx(32768 * 10_000_000)
+    b = rece.auto_size(51200, 30000, n_ec=2, alpha_bc=0.5, rounds=2)
+    assert b["n_b"] == round(math.sqrt(4 * 0.5 * 5 * 30000)) and b["n_c"] == round(b["n_b"] / 0.5)
+    for bad in (dict(s=0), dict(C=0), dict(n_ec=-1), dict(alpha_bc=0.0), dict(rounds=0)):
+        args = dict(s=10, C=10, n_ec=1, alpha_bc=1.0, rounds=1)
+        args.update(bad)
+        with pytest.raises(rece.ReceError):
+            rece.auto_size(**args)
+
+
+@pytest.mark.parametrize("name,below", [("sasrec", False), ("million", True), ("tenmillion", True)])
+def test_workspace_against_the_pages_memory_model(name, below):
+    """The page's model counts the method's intermediate arrays (chunk logit blocks
+    among them) at its optimal n_b, in elements (taken as 4 bytes).  This
+    implementation never stores a logit: at a million items and more its two
+    workspaces together stay several times below the model, at the auto-sized plan
+    and at the workload's own n_b.  At 30,000 items the model is small and the
+    candidate lists (3k + 2 tiles of 8-byte entries per position, two sets for the
+    rounds running side by side) take more; there the workspace stays within 3x."""
+    from rece_inputs import WORKLOADS
+    w = WORKLOADS[name]
+    a = rece.auto_size(w.s, w.C, w.n_ec, 1.0, w.rounds)
+    p = rece.auto_plan(w.s, w.C, w.d, w.k, w.rounds, n_ec=w.n_ec, dtype=w.dtype)
+    assert (p.cfg.n_b, p.cfg.n_c) == (a["n_b"], a["n_c"])
+    q = rece.Plan(w.s, w.C, w.d, w.n_b, w.n_c, w.k, w.rounds, dtype=w.dtype)
+    model = 4 * a["model_elems"]
+    for plan in (p, q):
+        ws = plan.scratch_bytes + plan.saved_bytes
+        if below:
+            assert ws < model / 4
+        else:
+            assert ws < 3 * model
+        assert ws < 4 * w.s * w.C            # always far below full cross-entropy's s x C logits

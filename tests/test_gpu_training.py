@@ -115,3 +115,17 @@ def test_autograd_wrapper():
     f = oracle.rece_forward(inb.X, inb.Y, inb.pos, inb.B, wb.n_c, wb.k)
     gX, gY = oracle.rece_backward(inb.X, inb.Y, inb.pos, f)
     assert grad_err(Xb.grad.float().cpu().numpy(), gX) <= 5e-3
+
+
+def test_auto_sized_plan_matches_oracle():
+    """A plan sized by the page's rule (n_b* and n_c from rece_auto_size) on a small
+    workload: the GPU result equals the oracle's at those sizes."""
+    base = scaled("sasrec", seqs=4, seqlen=64, C=3000, n_b=8, n_c=8, k=16, rounds=2, seed=45)
+    a = rece.auto_size(base.s, base.C, base.n_ec, 1.0, base.rounds)
+    w = base.with_(n_b=a["n_b"], n_c=a["n_c"])
+    inp = make_inputs(w)
+    loss, lpp, dX, dY = _run(w, inp)
+    f = oracle.rece_forward(inp.X, inp.Y, inp.pos, inp.B, w.n_c, w.k)
+    gX, gY = oracle.rece_backward(inp.X, inp.Y, inp.pos, f)
+    assert np.max(np.abs(lpp.numpy() - f["loss_pp"]) / np.maximum(np.abs(f["loss_pp"]), 1.0)) <= 1e-3
+    assert grad_err(dX.numpy(), gX) <= 2e-3 and grad_err(dY.numpy(), gY) <= 2e-3
