@@ -15,6 +15,7 @@ phase's algorithmic work, against the datasheet peaks and against the peaks that
 a matrix-core loop and a plain copy reach on the device in the same run.
 """
 import argparse
+import glob
 import json
 import os
 import platform
@@ -31,7 +32,7 @@ SPEC_FP32_TFLOPS = 157.3
 
 # phases the library times, and the kernels each one launches
 PHASE_KERNELS = {
-    "project": "k_project_argmax, k_argmax_exact",
+    "project": "k_project_argmax, k_argmax_near",
     "sort": "k_seg_hist, k_scan_*, k_seg_scatter*, k_gather_rows",
     "select": "k_sel_stream (histogram pass, exact pass), k_sel_finish",
     "loss": "k_round_dedup, k_ce, k_mean",
@@ -39,8 +40,11 @@ PHASE_KERNELS = {
     "bwd_sort": "k_pair_hist, k_pair_scatter",
     "bwd_dy": "k_dy_pieces, k_dy_combine",
 }
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "select_tenmillion_hbm_traffic.md")
-SELECT_SOURCES = ["k_select.hip", "rece_stream.h", "rece_device.h", "rece_internal.h", "rece_kth.h"]
+# sources of each phase's kernels: a counter summary is used only while their digest matches
+PHASE_SOURCES = {
+    "project": ["k_bucket.hip", "rece_stream.h", "rece_device.h", "rece_internal.h"],
+    "select": ["k_select.hip", "rece_stream.h", "rece_device.h", "rece_internal.h", "rece_kth.h"],
+}
 
 
 def chunk_starts(N, n_c):
@@ -143,18 +147,19 @@ def source_digest(names):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel):
-    """HBM bytes per launch of the select phase from the committed counter summary, or
-    None when that summary is missing or was taken on other kernel sources."""
-    try:
-        text = open(TRAFFIC_FILE).read()
-    except OSError:
+def measured_traffic(phase, workload):
+    """HBM bytes per launch of a phase from the committed counter summaries
+    (profiles/*_hbm_traffic.md), or None when none covers it or the one that does
+    was taken on other kernel sources."""
+    if phase not in PHASE_SOURCES:
         return None
-    for line in text.splitlines():
-        if line.startswith("TRAFFIC "):
-            rec = json.loads(line[len("TRAFFIC "):])
-            if rec.get("kernel") == kernel and rec.get("sources") == source_digest(SELECT_SOURCES):
-                return rec["bytes_per_launch"]
+    digest = source_digest(PHASE_SOURCES[phase])
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_hbm_traffic.md"))):
+        for line in open(path).read().splitlines():
+            if line.startswith("TRAFFIC "):
+                rec = json.loads(line[len("TRAFFIC "):])
+                if rec.get("kernel") == f"{phase}:{workload}" and rec.get("sources") == digest:
+                    return rec["bytes_per_launch"]
     return None
 
 
@@ -325,6 +330,11 @@ def measure_peaks(dev):
             "note": "bf16 matrix-core loop with no memory traffic; 1 GiB device copy, read + write bytes"}
 
 
+def note(msg):
+    """Progress line on stderr (the JSON line alone goes to stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -350,6 +360,7 @@ def main():
 
     w = WORKLOADS[args.workload]
     inp = make_inputs(w)
+    note(f"inputs of {w.name} generated")
     # the CPU baseline forks worker processes: it runs before anything touches the GPU
     cpu = None
     if not args.no_cpu_baseline and w.variant == "rece":
@@ -381,6 +392,7 @@ def main():
         step()
     torch.cuda.synchronize()
     plan.check(saved)
+    note(f"{args.warmup} warm-up steps done")
     # device memory of a whole step: the library allocates nothing itself, so torch's peak
     # covers inputs, outputs and the two workspaces; a dense bf16 [s, C] logit tensor must
     # be larger than every buffer the step holds
@@ -417,6 +429,7 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     dom_ms, dom_launches = plan.profile_read()[dom]
+    note(f"{args.steps} timed steps: {elapsed * 1e3 / args.steps:.3f} ms per step")
     plan.profile(enable=False)
     plan.check(saved)
     counters = plan.export(saved, "counters").cpu().tolist()
@@ -438,7 +451,7 @@ def main():
               "frac": fr["hbm_frac"]}
     rl.update(kernel=f"{dom} ({PHASE_KERNELS.get(dom, dom)})", ms_per_launch=round(ms_launch, 4),
               launches_per_step=per_launch, other_roof=fr,
-              traffic=measured_traffic(f"select:{w.name}") if dom == "select" else None)
+              traffic=measured_traffic(dom, w.name))
 
     breakdown = {}
     for name, (f, b) in work.items():
@@ -475,7 +488,8 @@ def main():
         "phases": breakdown,
         "memory": memory,
         "counters": {"argmax_rows_float64": counters[1], "topk_rows_near_tie": counters[2],
-                     "logits_float64": counters[3], "overflows": counters[4]},
+                     "logits_float64": counters[3], "overflows": counters[4],
+                     "select_rows_exact_pass": counters[5]},
     }
     if full is not None:
         full["rece_speedup"] = round(full["ms_per_step"] / ms_step, 2)
