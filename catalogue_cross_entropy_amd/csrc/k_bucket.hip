@@ -12,12 +12,24 @@
 // kernel nor sit on its critical path.  (Small inputs decide their undecided
 // rows inside the matrix-core kernel, all vectors in float64.)
 #include <algorithm>
+#include <type_traits>
+#include <utility>
 
 #include "rece_device.h"
 #include "rece_internal.h"
 #include "rece_stream.h"
 
 namespace rece {
+
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>), unrolled at compile time.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_seq(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_seq(f, std::make_integer_sequence<int, N>{});
+}
 
 __global__ void k_fill_u32(uint32_t* p, uint32_t v, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -188,39 +200,93 @@ __global__ __launch_bounds__(256, (D * sizeof(E) == 256) ? 3 : 1) void k_project
       best2[f][v] = INT32_MIN;
     }
 
+  if constexpr (sizeof(E) == 2) {
+    // bf16: every fragment read is this lane's address for its k-step in the tile's
+    // ring slot (one add per k-step and tile) plus the 16-row block as an immediate
+    // offset; only a last tile that passes n_b pads its scores.
+    constexpr int KS = Frag<E, D>::KS;
+    constexpr int NCB = G::TI / 16;
+    const int q = l >> 4, n0 = l & 15;
+    uint32_t fa0[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) fa0[ks] = lds_addr(ring + n0 * G::RB + (((4 * ks + q) ^ (n0 & G::SWM)) * 16));
+    auto tile = [&](auto pad_c, int t) {
+      constexpr bool PAD = decltype(pad_c)::value;
+      if (t + 1 < nt)
+        wait_vmcnt_c<G::ROW_DMA / NW>();   // the fewest copies any wave issues per tile
+      else
+        wait_vmcnt_c<0>();
+      raw_barrier();   // every wave's copies of tile t landed; slot (t+2) % 3 is free
+      const int slot = t % 3;
+      if (t + 2 < nt)
+        dma_rows<E, D, NW>(ring + (size_t)((t + 2) % 3) * G::ROW_BYTES, Bt, (int64_t)(t + 2) * G::TI, n_b, w);
+      uint32_t fa[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) fa[ks] = fa0[ks] + (uint32_t)(slot * G::ROW_BYTES);
+      const int vb = t * G::TI + n0;
+      static_for<NCB>([&](auto cb_c) {
+        constexpr int cb = decltype(cb_c)::value;
+        Frag<E, D> bf;
+        u32x4 raw[KS];
+        LdsReadOff128<KS, cb * 16 * G::RB>::run(fa, raw);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) bf.v[ks] = __builtin_bit_cast(bf16x8, raw[ks]);
+        const int bcol = vb + cb * 16;
+        f32x4 c0{0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (PAD) {
+          const float pad = bcol < n_b ? 0.0f : NEG_INF;
+          c0 = f32x4{pad, pad, pad, pad};
+        }
+#pragma unroll
+        for (int f = 0; f < RF; ++f) {
+          const f32x4 acc = mma_block(a[f], bf, c0);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int key = (__float_as_int(acc[v]) & ~imask) | bcol;
+            best2[f][v] = med3_i(best1[f][v], best2[f][v], key);
+            best1[f][v] = max(best1[f][v], key);
+          }
+        }
+      });
+    };
+    const int nfull = n_b % G::TI != 0 ? nt - 1 : nt;   // tiles without padding
+    for (int t = 0; t < nfull; ++t) tile(std::false_type{}, t);
+    if (nfull < nt) tile(std::true_type{}, nfull);
+  } else {
   for (int t = 0; t < nt; ++t) {
-    // tile t's copies are complete once only tile t+1's remain outstanding
-    if (t + 1 < nt)
-      wait_vmcnt_c<G::ROW_DMA / NW>();   // the fewest copies any wave issues per tile
-    else
-      wait_vmcnt_c<0>();
-    raw_barrier();   // every wave's copies of tile t landed; slot (t+2) % 3 is free
-    if (t + 2 < nt)
-      dma_rows<E, D, NW>(ring + (size_t)((t + 2) % 3) * G::ROW_BYTES, Bt, (int64_t)(t + 2) * G::TI, n_b, w);
-    const char* rows = ring + (size_t)(t % 3) * G::ROW_BYTES;
-    const int b0 = t * G::TI;
-    // vectors past n_b (last tile only) score -inf
-    const int nvalid = n_b - b0;
-#pragma unroll
-    for (int cb = 0; cb < G::TI / 16; ++cb) {
-      Frag<E, D> bf;
-      TileFrag<E, D>::load(bf, rows, cb * 16 + (l & 15));
-      // the vector index as one register (one and-or per score below)
-      const int bcol = settled(b0 + cb * 16 + (l & 15));
-      const float pad = cb * 16 + (l & 15) < nvalid ? 0.0f : NEG_INF;
-#pragma unroll
-      for (int f = 0; f < RF; ++f) {
-        const f32x4 acc = mma_block(a[f], bf, f32x4{pad, pad, pad, pad});
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int key = (__float_as_int(acc[v]) & ~imask) | bcol;
-          best2[f][v] = med3_i(best1[f][v], best2[f][v], key);
-          best1[f][v] = max(best1[f][v], key);
+      // tile t's copies are complete once only tile t+1's remain outstanding
+      if (t + 1 < nt)
+        wait_vmcnt_c<G::ROW_DMA / NW>();   // the fewest copies any wave issues per tile
+      else
+        wait_vmcnt_c<0>();
+      raw_barrier();   // every wave's copies of tile t landed; slot (t+2) % 3 is free
+      if (t + 2 < nt)
+        dma_rows<E, D, NW>(ring + (size_t)((t + 2) % 3) * G::ROW_BYTES, Bt, (int64_t)(t + 2) * G::TI, n_b, w);
+      const char* rows = ring + (size_t)(t % 3) * G::ROW_BYTES;
+      const int b0 = t * G::TI;
+      // vectors past n_b (last tile only) score -inf
+      const int nvalid = n_b - b0;
+  #pragma unroll
+      for (int cb = 0; cb < G::TI / 16; ++cb) {
+        Frag<E, D> bf;
+        TileFrag<E, D>::load(bf, rows, cb * 16 + (l & 15));
+        // the vector index as one register (one and-or per score below)
+        const int bcol = settled(b0 + cb * 16 + (l & 15));
+        const float pad = cb * 16 + (l & 15) < nvalid ? 0.0f : NEG_INF;
+  #pragma unroll
+        for (int f = 0; f < RF; ++f) {
+          const f32x4 acc = mma_block(a[f], bf, f32x4{pad, pad, pad, pad});
+  #pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int key = (__float_as_int(acc[v]) & ~imask) | bcol;
+            best2[f][v] = med3_i(best1[f][v], best2[f][v], key);
+            best1[f][v] = max(best1[f][v], key);
+          }
         }
       }
     }
+  
   }
-
   const float bmax = bnorm_max[0];
 #pragma unroll
   for (int f = 0; f < RF; ++f) {

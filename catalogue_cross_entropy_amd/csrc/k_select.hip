@@ -309,7 +309,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_sel_stream(SelectArgs p) {
   const int64_t wrow0 = tile0 + 16 * w;
 
   Ranges win;
-  win.init(c, n_c, C, TI, p.n_ec, p.wrap);
+  win.init(c, n_c, C, TI, p.n_ec, p.wrap, window_rotation(p.win_order, c, p.n_ec));
   const int ntiles = win.ntiles();
 
   // fragments of this wave's 16 positions (sorted copy: contiguous rows)
@@ -488,6 +488,10 @@ __global__ __launch_bounds__(64 * NW, 2) void k_sel_stream(SelectArgs p) {
   if (rv && g == 0 && (!EXACT || take)) {
     p.clist_n[lrow] = (int)(redo ? LIST_REDO : ((uint32_t)(cnt < cap ? cnt : cap) | (compacted ? LIST_COMPACTED : 0u)));
     p.clist_lo[lrow] = redo ? NEG_INF : lo;
+  }
+  if constexpr (!EXACT) {
+    const uint32_t nredo = (uint32_t)popc(ballot(rv && g == 0 && redo));
+    if (nredo && l == 0) atomicAdd(p.counters + CNT_SEL_REDO, nredo);
   }
 }
 

@@ -95,6 +95,7 @@ struct rece_plan_s {
   int cap;            // entries of a row's candidate list in the chunk kernels
   int selall;         // every window has at most k candidates
   int waves_sel;
+  int win_order;   // walking order of a window's chunks (window_rotation)
   int tpc_sel;
   int64_t wmax;       // largest window (items)
   float beta_coef;
@@ -480,6 +481,15 @@ rece_status rece_plan(const rece_config* cfg, rece_plan_t* out) {
   }
   // waves per chunk-kernel workgroup: 16 positions each, no more than a chunk has
   p->waves_sel = rows_chunk <= 16 ? 1 : (rows_chunk <= 32 ? 2 : 4);
+  // Window walking order: with item chunks of a megabyte or more, by chunk index
+  // modulo 2 n_ec + 1 (the workgroups of neighbouring chunks read each item chunk
+  // at the same time, one HBM read for the windows that share it through the L2);
+  // smaller chunks are L2-resident anyway and start with their own chunk, whose
+  // logits raise the thresholds soonest.
+  {
+    const int64_t chunk_bytes = (sce ? c.b_y : (C + n_c - 1) / n_c) * (int64_t)d * p->esize;
+    p->win_order = sce ? 0 : (chunk_bytes >= ((int64_t)1 << 20) ? 2 : 1);
+  }
   while (p->waves_sel > 1 && select_lds_bytes(p->bf16, d, p->waves_sel, cap_lds) > 160 * 1024) p->waves_sel /= 2;
   if (select_lds_bytes(p->bf16, d, p->waves_sel, cap_lds) > 160 * 1024) {
     delete p;
@@ -747,6 +757,7 @@ static rece_status forward_impl(const rece_plan_s& p, hipStream_t st, const void
     a.slot_out = 0;
     a.n_ec = c.n_ec;
     a.wrap = c.window_wrap;
+    a.win_order = p.win_order;
     a.cap = p.cap;
     a.selall = p.selall;
     a.clist = reinterpret_cast<int2*>(sc + (rho == 0 ? p.o_cl0 : p.o_cl1));

@@ -16,6 +16,7 @@ enum Counter {
   CNT_TOPK_EXACT = 2,     // rows whose k-th element needed more than one float64 value
   CNT_LOGIT_EXACT = 3,    // logits recomputed in float64 (selection and dedup tests)
   CNT_OVERFLOW = 4,       // selection buffers that could not be compacted
+  CNT_SEL_REDO = 5,       // rows whose candidate list went to the exact pass (ties by the hundred)
   NUM_COUNTERS = 8
 };
 enum ErrBit : uint32_t { ERRBIT_BAD_ID = 1u, ERRBIT_OVERFLOW = 2u };
@@ -51,6 +52,7 @@ struct SelectArgs {
   int slot_out;               // 1: outputs indexed by sorted slot, not by position id
   int n_ec;                   // window: chunks c - n_ec .. c + n_ec
   int wrap;                   // 1: chunk indices modulo n_c (cyclic); 0: clipped to [0, n_c)
+  int win_order;              // walking order of the window's chunks (window_rotation)
   int2* clist;                // [rows][cap] candidate lists (item id, float32 logit bits)
   int32_t* clist_n;           // [rows] entries in each list; bit 31: compacted or raised, bit 30: redo
   float* clist_lo;            // [rows] each row's final threshold (no kept entry lies below it)

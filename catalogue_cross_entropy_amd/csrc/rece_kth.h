@@ -157,6 +157,61 @@ __device__ inline MergeLds carve_topk(char* base, int cap) {
   return L;
 }
 
+// Rank the near-tie band {t : lo <= vals[t] <= hi} of list[0..n) when it holds
+// more entries than MG_NEAR: no float64 buffer, every comparison recomputes the
+// other entry's float64 logit (64 at a time, one per lane).  Quadratic in the band
+// and slow, but exact; reached only with hundreds of equal or nearly equal logits
+// at the k-th place (repeated item vectors).  Entries ranked at or beyond `need`
+// get value -inf; returns the element ranked need - 1 (te, tid).
+template <class E, int D>
+__device__ __forceinline__ void rank_band_wide(const MergeLds& L, int n, int need, float lo, float hi,
+                                                         const E* xrow, const E* Y, double& te, int& tid,
+                                                         uint32_t& nexact) {
+  const int l = lane_id();
+  constexpr uint32_t OUT = 0x80000000u;   // ranked out (ids are non-negative)
+  uint32_t ndot = 0;
+  for (int eb = 0; eb < n; eb += WAVE) {
+    const int t = eb + l;
+    const bool mine = t < n && L.vals[t] >= lo && L.vals[t] <= hi;
+    const int mj = mine ? (int)((uint32_t)L.ids[t] & ~OUT) : 0;
+    const double me = mine ? exact_dot<E, D>(xrow, Y + (int64_t)mj * D) : 0.0;
+    int rank = 0;
+    for (int ub = 0; ub < n; ub += WAVE) {
+      const int u = ub + l;
+      const bool inb = u < n && L.vals[u] >= lo && L.vals[u] <= hi;
+      const int uj = inb ? (int)((uint32_t)L.ids[u] & ~OUT) : 0;
+      const double ue = inb ? exact_dot<E, D>(xrow, Y + (int64_t)uj * D) : 0.0;
+      uint64_t m = ballot(inb);
+      ndot += (uint32_t)popc(m);
+      while (m) {   // uniform loop over the batch's band entries
+        const int q = __builtin_ctzll(m);
+        m &= m - 1;
+        const double eu = lane_val(ue, q);
+        const int ju = lane_val(uj, q);
+        rank += (eu > me) || (eu == me && ju < mj);
+      }
+    }
+    const uint64_t tm = ballot(mine && rank == need - 1);
+    if (tm) {
+      const int tl = __builtin_ctzll(tm);
+      te = __shfl(me, tl);
+      tid = __shfl(mj, tl);
+    }
+    // marks go on the ids, so the band stays the same for the later batches
+    if (mine && rank >= need) L.ids[t] = (int32_t)((uint32_t)mj | OUT);
+    wave_sync();
+  }
+  for (int t = l; t < n; t += WAVE) {
+    const uint32_t j = (uint32_t)L.ids[t];
+    if (j & OUT) {
+      L.ids[t] = (int32_t)(j & ~OUT);
+      L.vals[t] = NEG_INF;
+    }
+  }
+  wave_sync();
+  if (l == 0) nexact += ndot;   // lane 0 keeps the wave's count
+}
+
 // Keep the k best of list[0..n) (n >= k) in (float64 logit desc, id asc) order,
 // compacted to the front; returns the k-th kept element's float64 logit and id.
 // The float32 k-th value a_k decides every entry more than 2*beta away from it;
@@ -165,6 +220,7 @@ __device__ inline MergeLds carve_topk(char* base, int cap) {
 template <class E, int D>
 __device__ void reduce_to_k(const MergeLds& L, int n, int k, float beta, const E* xrow, const E* Y, double& te,
                             int& tid, uint32_t& nexact, uint32_t* counters) {
+  (void)counters;
   const int l = lane_id();
   const float ak = wave_kth_largest(L.vals, n, k, L.khist, L.cv);
   const float lo = f_down((double)ak - 2.0 * (double)beta);
@@ -182,42 +238,39 @@ __device__ void reduce_to_k(const MergeLds& L, int n, int k, float beta, const E
     }
     na += popc(mk);
   }
-  if (na > MG_NEAR) {
-    if (l == 0) {
-      atomicAdd(counters + CNT_OVERFLOW, 1u);
-      atomicOr(counters + CNT_ERROR, (uint32_t)ERRBIT_OVERFLOW);
-    }
-    na = MG_NEAR;
-  }
-  wave_sync();
-  for (int e = l; e < na; e += WAVE) L.ce[e] = exact_dot<E, D>(xrow, Y + (int64_t)L.ids[L.ci[e]] * D);
-  if (l == 0) nexact += (uint32_t)na;
-  wave_sync();
   const int need = k - nabove;   // near-ties kept (>= 1)
   te = 0.0;
   tid = 0;
-  for (int a0 = 0; a0 < na; a0 += WAVE) {
-    const int e = a0 + l;
-    int rank = 0;
-    double me = 0.0;
-    int mj = 0;
-    if (e < na) {
-      me = L.ce[e];
-      mj = L.ids[L.ci[e]];
-      for (int u = 0; u < na; ++u) {
-        const double eu = L.ce[u];
-        const int ju = L.ids[L.ci[u]];
-        rank += (eu > me) || (eu == me && ju < mj);
-      }
-    }
-    const uint64_t tm = ballot(e < na && rank == need - 1);
-    if (tm) {
-      const int tl = __builtin_ctzll(tm);
-      te = __shfl(me, tl);
-      tid = __shfl(mj, tl);
-    }
+  wave_sync();
+  if (na > MG_NEAR) {
+    rank_band_wide<E, D>(L, n, need, lo, hi, xrow, Y, te, tid, nexact);
+  } else {
+    for (int e = l; e < na; e += WAVE) L.ce[e] = exact_dot<E, D>(xrow, Y + (int64_t)L.ids[L.ci[e]] * D);
+    if (l == 0) nexact += (uint32_t)na;
     wave_sync();
-    if (e < na && rank >= need) L.vals[L.ci[e]] = NEG_INF;   // ranked out
+    for (int a0 = 0; a0 < na; a0 += WAVE) {
+      const int e = a0 + l;
+      int rank = 0;
+      double me = 0.0;
+      int mj = 0;
+      if (e < na) {
+        me = L.ce[e];
+        mj = L.ids[L.ci[e]];
+        for (int u = 0; u < na; ++u) {
+          const double eu = L.ce[u];
+          const int ju = L.ids[L.ci[u]];
+          rank += (eu > me) || (eu == me && ju < mj);
+        }
+      }
+      const uint64_t tm = ballot(e < na && rank == need - 1);
+      if (tm) {
+        const int tl = __builtin_ctzll(tm);
+        te = __shfl(me, tl);
+        tid = __shfl(mj, tl);
+      }
+      wave_sync();
+      if (e < na && rank >= need) L.vals[L.ci[e]] = NEG_INF;   // ranked out
+    }
   }
   wave_sync();
   // compact the kept entries (value >= lo after the ranked-out near-ties were dropped)

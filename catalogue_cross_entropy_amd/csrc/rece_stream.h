@@ -183,22 +183,31 @@ struct RecCopy {
 // neighbours on each side as in the method paragraph of Section 3).  Cyclic
 // (wrap = 1): chunk indices modulo n_c, taken as a set, so 2 n_ec + 1 >= n_c gives
 // all N slots.  Clipped (wrap = 0): only chunks inside [0, n_c).  Consecutive
-// chunks are consecutive slots, so every window is at most two slot ranges
-// (a cyclic window that passes an end of the order is split there), walked in
-// tiles of TI slots.  Plain scalar members: an indexed array here would be
-// placed in scratch memory.
+// chunks are consecutive slots, so every window is at most two slot ranges,
+// walked in tiles of TI slots: ascending (a cyclic window that passes an end of
+// the order is split there), or, with rot > 0 and a window that passes no end,
+// rotated: chunks lo + rot .. hi, then lo .. lo + rot - 1.  Plain scalar members
+// assigned in branches: other forms (an indexed array, references to members)
+// put the struct in scratch memory.
 struct Ranges {
   int64_t s0, s1, e0, e1;   // slot ranges [s_q, e_q); the second may be empty
   int c1, c2;               // cumulative tile counts
-  __device__ __forceinline__ void init(int c, int n_c, int64_t N, int TI, int n_ec, int wrap) {
+  __device__ __forceinline__ void init(int c, int n_c, int64_t N, int TI, int n_ec, int wrap, int rot) {
     const int lo = c - n_ec, hi = c + n_ec;   // chunks lo .. hi (before the modulo or the clip)
     s1 = e1 = 0;
-    if (!wrap) {
-      s0 = chunk_start(lo < 0 ? 0 : lo, N, n_c);
-      e0 = chunk_start(hi + 1 > n_c ? n_c : hi + 1, N, n_c);
-    } else if (2 * n_ec + 1 >= n_c) {
+    if (wrap && 2 * n_ec + 1 >= n_c) {
       s0 = 0;
       e0 = N;
+    } else if (rot > 0 && (!wrap || (lo >= 0 && hi < n_c))) {
+      const int a0 = lo + rot < 0 ? 0 : lo + rot, b0 = hi > n_c - 1 ? n_c - 1 : hi;
+      const int a1 = lo < 0 ? 0 : lo, b1 = lo + rot - 1 > n_c - 1 ? n_c - 1 : lo + rot - 1;
+      s0 = a0 <= b0 ? chunk_start(a0, N, n_c) : 0;
+      e0 = a0 <= b0 ? chunk_start(b0 + 1, N, n_c) : 0;
+      s1 = a1 <= b1 ? chunk_start(a1, N, n_c) : 0;
+      e1 = a1 <= b1 ? chunk_start(b1 + 1, N, n_c) : 0;
+    } else if (!wrap) {
+      s0 = chunk_start(lo < 0 ? 0 : lo, N, n_c);
+      e0 = chunk_start(hi + 1 > n_c ? n_c : hi + 1, N, n_c);
     } else if (lo < 0) {
       s0 = chunk_start(lo + n_c, N, n_c);
       e0 = N;
@@ -216,6 +225,17 @@ struct Ranges {
   }
   __device__ __forceinline__ int ntiles() const { return c2; }
 };
+
+// Rotation of chunk c's window for a walking order: 0 ascending; 1 the chunk's own
+// items first; 2 by chunk index modulo 2 n_ec + 1, so that at any time the
+// workgroups of neighbouring chunks read the same item chunk (one HBM read serves
+// the 2 n_ec + 1 windows that contain it, through the L2).
+__host__ __device__ __forceinline__ int window_rotation(int order, int c, int n_ec) {
+  const int m = 2 * n_ec + 1;
+  if (order == 1) return n_ec;
+  if (order == 2) return (int)((((int64_t)n_ec - c) % m + m) % m);
+  return 0;
+}
 
 // Slot range [q0, q1_end) of tile t (tile rows are q0 .. q0 + TI - 1, clipped at q1_end).
 __device__ __forceinline__ int64_t range_tile_start(Ranges r, int t, int TI) {
@@ -272,10 +292,51 @@ template <> struct LdsRead128<4> {
 };
 template <> struct LdsRead128<8> {
   static __device__ __forceinline__ void run(const uint32_t* a, u32x4* r) {
-    LdsRead128<4>::run(a, r);
-    LdsRead128<4>::run(a + 4, r + 4);
+    asm volatile(
+        "ds_read_b128 %0, %8\n\tds_read_b128 %1, %9\n\tds_read_b128 %2, %10\n\tds_read_b128 %3, %11\n\t"
+        "ds_read_b128 %4, %12\n\tds_read_b128 %5, %13\n\tds_read_b128 %6, %14\n\tds_read_b128 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+        : "memory");
   }
 };
+template <> struct LdsRead128<16> {
+  static __device__ __forceinline__ void run(const uint32_t* a, u32x4* r) {
+    LdsRead128<8>::run(a, r);
+    LdsRead128<8>::run(a + 8, r + 8);
+  }
+};
+// KS 16-byte reads from LDS at a[ks] + OFF (an immediate), one wait.
+template <int KS, int OFF> struct LdsReadOff128;
+template <int OFF> struct LdsReadOff128<1, OFF> {
+  static __device__ __forceinline__ void run(const uint32_t* a, u32x4* r) {
+    asm volatile("ds_read_b128 %0, %1 offset:%2\n\ts_waitcnt lgkmcnt(0)" : "=&v"(r[0]) : "v"(a[0]), "i"(OFF) : "memory");
+  }
+};
+template <int OFF> struct LdsReadOff128<2, OFF> {
+  static __device__ __forceinline__ void run(const uint32_t* a, u32x4* r) {
+    asm volatile("ds_read_b128 %0, %2 offset:%4\n\tds_read_b128 %1, %3 offset:%4\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(r[0]), "=&v"(r[1]) : "v"(a[0]), "v"(a[1]), "i"(OFF) : "memory");
+  }
+};
+template <int OFF> struct LdsReadOff128<4, OFF> {
+  static __device__ __forceinline__ void run(const uint32_t* a, u32x4* r) {
+    asm volatile(
+        "ds_read_b128 %0, %4 offset:%8\n\tds_read_b128 %1, %5 offset:%8\n\tds_read_b128 %2, %6 offset:%8\n\t"
+        "ds_read_b128 %3, %7 offset:%8\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(OFF)
+        : "memory");
+  }
+};
+template <int OFF> struct LdsReadOff128<8, OFF> {
+  static __device__ __forceinline__ void run(const uint32_t* a, u32x4* r) {
+    LdsReadOff128<4, OFF>::run(a, r);
+    LdsReadOff128<4, OFF>::run(a + 4, r + 4);
+  }
+};
+
 // Eight dwords from LDS (addresses a[0..7]), one wait.
 __device__ __forceinline__ void lds_read_b32x8(const uint32_t* a, float* r) {
   asm volatile(
@@ -321,6 +382,28 @@ template <> struct LdsReadB32<2> {
 template <class E, int D> struct TileFrag;
 
 template <int D> struct TileFrag<bf16, D> {
+  // Fragments of rows n, n + 16, ..., n + 16 (NF - 1), read together (one wait).
+  template <int NF>
+  static __device__ __forceinline__ void load_n(Frag<bf16, D> (&f)[NF], const char* rows, int n) {
+    using G = TileGeom<bf16, D>;
+    constexpr int KS = D / 32;
+    const int q = lane_id() >> 4;
+    uint32_t a[NF * KS];
+    u32x4 raw[NF * KS];
+#pragma unroll
+    for (int j = 0; j < NF; ++j)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int nn = n + 16 * j;
+        const int c = (4 * ks + q) ^ (nn & G::SWM);
+        a[j * KS + ks] = lds_addr(rows + nn * G::RB + c * 16);
+      }
+    LdsRead128<NF * KS>::run(a, raw);
+#pragma unroll
+    for (int j = 0; j < NF; ++j)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) f[j].v[ks] = __builtin_bit_cast(bf16x8, raw[j * KS + ks]);
+  }
   static __device__ __forceinline__ void load(Frag<bf16, D>& f, const char* rows, int n) {
     using G = TileGeom<bf16, D>;
     constexpr int KS = D / 32;
@@ -338,6 +421,11 @@ template <int D> struct TileFrag<bf16, D> {
   }
 };
 template <int D> struct TileFrag<float, D> {
+  template <int NF>
+  static __device__ __forceinline__ void load_n(Frag<float, D> (&f)[NF], const char* rows, int n) {
+#pragma unroll
+    for (int j = 0; j < NF; ++j) load(f[j], rows, n + 16 * j);
+  }
   static __device__ __forceinline__ void load(Frag<float, D>& f, const char* rows, int n) {
     using G = TileGeom<float, D>;
     constexpr int KS = D / 4;

@@ -238,7 +238,9 @@ typedef enum {
   RECE_STAGE_LSE = 7,        /* float32 [s] log-sum-exp over positive + kept set (round ignored) */
   RECE_STAGE_COUNTERS = 8,   /* uint32 [8] device counters: [0] error bits, [1] argmax rows
                                 decided in float64, [2] top-k rows needing float64 values,
-                                [3] logits recomputed in float64, [4] buffer overflows */
+                                [3] logits recomputed in float64, [4] buffer overflows,
+                                [5] rows whose top-k candidates went through the exact
+                                pass (hundreds of ties near the k-th logit) */
   RECE_STAGE_SCE_ROWS = 9,   /* SCE: int32 [n_b][b_x] positions taken by each bucket (a set per
                                 bucket, in the library's order) */
   RECE_STAGE_SCE_ITEMS = 10, /* SCE: int32 [n_b][b_y] items taken by each bucket (a set per bucket) */

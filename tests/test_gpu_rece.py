@@ -157,11 +157,9 @@ def test_exact_topk_ties_from_duplicate_items():
     assert grad_err(g["dX"], gX) <= 2e-3 and grad_err(g["dY"], gY) <= 2e-3
 
 
-def test_histogram_bin_above_16_bits():
-    """A window of 70,000 items of which 66,000 are zero rows: every position's
-    logit-0 histogram bin holds more than 65,535 entries, which 16-bit counts would
-    wrap; the plan switches the chunk kernel to 32-bit counts and the selection
-    matches the oracle exactly."""
+def test_window_of_mostly_zero_rows():
+    """A window of 70,000 items of which 66,000 are zero rows (66,000 equal logits
+    of 0 in every row): the selection matches the oracle exactly."""
     w = scaled("tiny", seqs=1, seqlen=64, C=70000, d=32, n_b=1, n_c=1, k=40, rounds=1)
     inp = make_inputs(w)
     Y = inp.Y.copy()
@@ -171,5 +169,27 @@ def test_histogram_bin_above_16_bits():
     g = run_rece(inp)
     fwd = oracle.rece_forward(inp.X, inp.Y, inp.pos, inp.B, w.n_c, w.k)
     _compare("bin_above_16_bits", inp, g, fwd)
+    gX, gY = oracle.rece_backward(inp.X, inp.Y, inp.pos, fwd)
+    assert grad_err(g["dX"], gX) <= 2e-3 and grad_err(g["dY"], gY) <= 2e-3
+
+
+@pytest.mark.parametrize("k", [32, 128])
+def test_hundreds_of_ties_take_the_exact_pass(k):
+    """The catalogue is 10 distinct rows repeated 600 times each, so every position
+    scores 600 equal copies of its best row: far more ties at the k-th logit than a
+    candidate list holds (3k + 2 tiles), which no histogram compaction can shrink.
+    Those rows are redone by the chunk kernel's exact pass, which ranks the ties in
+    float64 and by id; at k = 128 the finishing kernel then ranks more near-ties
+    than its float64 buffer holds (the recomputing path).  The kept sets (the k
+    lowest ids among the copies) must equal the oracle's."""
+    w = scaled("sasrec", seqs=2, seqlen=64, C=6000, n_b=2, n_c=1, k=k, rounds=1)
+    inp = make_inputs(w)
+    Y = np.ascontiguousarray(inp.Y[np.arange(w.C) % 10])
+    inp = dataclasses.replace(inp, Y=Y)
+    print(f"[gpu] 10 distinct rows x 600 copies, k={k}", flush=True)
+    g = run_rece(inp)
+    fwd = oracle.rece_forward(inp.X, inp.Y, inp.pos, inp.B, w.n_c, w.k)
+    _compare("exact_pass", inp, g, fwd)
+    assert g["counters"][5] > w.s // 2, g["counters"]   # rows redone by the exact pass
     gX, gY = oracle.rece_backward(inp.X, inp.Y, inp.pos, fwd)
     assert grad_err(g["dX"], gX) <= 2e-3 and grad_err(g["dY"], gY) <= 2e-3

@@ -74,6 +74,24 @@ def test_sce_parity(name):
     assert ex <= 2e-3 and ey <= 2e-3, (name, ex, ey)
 
 
+def test_sce_hundreds_of_ties():
+    """10 distinct item rows repeated 600 times: every bucket's item boundary falls
+    inside 600 equal projection scores, every slot's top-k inside 600 equal logits
+    (the chunk kernel's exact pass), and the merge of a position's buckets ranks
+    more near-ties than its float64 buffer holds (the recomputing path).  Every
+    selection must equal the oracle's: ties to the lowest index."""
+    import dataclasses
+    w = scaled("sce", seqs=2, seqlen=64, C=6000, d=64, n_b=6, b_x=48, b_y=1000, k=128)
+    inp = make_inputs(w)
+    inp = dataclasses.replace(inp, Y=np.ascontiguousarray(inp.Y[np.arange(w.C) % 10]))
+    print("[gpu] sce: 10 distinct rows x 600 copies, k=128", flush=True)
+    g = run_sce(inp)
+    fwd = oracle.sce_forward(inp.X, inp.Y, inp.pos, inp.B[0], w.b_x, w.b_y, w.k)
+    _check("sce_ties", inp, g, fwd)
+    gX, gY = oracle.sce_backward(inp.X, inp.Y, inp.pos, fwd)
+    assert grad_err(g["dX"], gX) <= 2e-3 and grad_err(g["dY"], gY) <= 2e-3
+
+
 def test_sce_full_ce_equals_dense_cross_entropy():
     w = CASES["sce_full_ce"]
     inp = make_inputs(w)
