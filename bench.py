@@ -33,7 +33,7 @@ SPEC_FP32_TFLOPS = 157.3
 # phases the library times, and the kernels each one launches
 PHASE_KERNELS = {
     "project": "k_project_argmax, k_argmax_near",
-    "sort": "k_seg_hist, k_scan_*, k_seg_scatter*, k_gather_rows",
+    "sort": "k_seg_hist, k_scan_*, k_seg_scatter*",
     "select": "k_sel_stream (histogram pass, exact pass), k_sel_finish",
     "loss": "k_round_dedup, k_ce, k_mean",
     "bwd_dx": "k_dx_lists",

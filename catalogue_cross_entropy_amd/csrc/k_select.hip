@@ -47,9 +47,12 @@
 
 namespace rece {
 
-// One ring slot: the tile's rows, then 64 item ids.
-__host__ __device__ constexpr size_t sel_slot_bytes(size_t row_bytes) { return row_bytes + 256; }
+// The row ring: SEL_RING slots of a tile's rows, gathered from the item table by
+// id.  The id ring: SEL_IDS slots of 64 item ids, filled one tile further ahead
+// (the row copies of a tile read its ids from LDS).
 constexpr int SEL_RING = 3;   // tiles t+1 and t+2 in flight while tile t is scored
+constexpr int SEL_IDS = 4;    // ids of tiles t .. t+3
+constexpr size_t SEL_IDS_BYTES = SEL_IDS * 256;
 constexpr int SEL_NB = 64;    // histogram bins of a row's list compaction
 // Per wave: the 16 rows' compaction histograms; for the exact fallback (one row at
 // a time) the float32 values of the row's list and the k-th search's histogram and
@@ -287,14 +290,15 @@ __global__ __launch_bounds__(64 * NW, 2) void k_sel_stream(SelectArgs p) {
   constexpr int TI = G::TI;
   constexpr int NCB = TI / 16;                // 16-column blocks per tile
   constexpr int TR = 16 * NW;
-  const E* __restrict__ Xs = reinterpret_cast<const E*>(p.Xs);
-  const E* __restrict__ Ys = reinterpret_cast<const E*>(p.Ys);
+  const E* __restrict__ X = reinterpret_cast<const E*>(p.X);
+  const E* __restrict__ Y = reinterpret_cast<const E*>(p.Y);
   const int k = p.k, n_c = p.n_c, cap = p.cap;
   const int64_t s = p.s, C = p.C;
-  const size_t slot_bytes = sel_slot_bytes(G::ROW_BYTES);
+  constexpr size_t slot_bytes = G::ROW_BYTES;
   char* ring = smem;
+  int32_t* idring = reinterpret_cast<int32_t*>(smem + SEL_RING * slot_bytes);
   const int w = threadIdx.x >> 6, l = lane_id(), g = l >> 4, r = l & 15;
-  char* wscr = smem + SEL_RING * slot_bytes + (size_t)w * sel_wave_bytes(p.selall ? 0 : cap);
+  char* wscr = smem + SEL_RING * slot_bytes + SEL_IDS_BYTES + (size_t)w * sel_wave_bytes(p.selall ? 0 : cap);
   uint32_t* hist_r = reinterpret_cast<uint32_t*>(wscr) + r * SEL_NB;
   float* cvals = reinterpret_cast<float*>(wscr);
   uint32_t* khist = reinterpret_cast<uint32_t*>(wscr + (size_t)cap * 4);
@@ -317,7 +321,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_sel_stream(SelectArgs p) {
   const bool rv = pA < x1;
   const int iA = settled(rv ? p.perm_x[pA] : -1);
   Frag<E, D> afr;
-  afr.load_global(rv ? Xs + pA * D : nullptr);
+  afr.load_global(rv ? X + (int64_t)iA * D : nullptr);
   afr.settle();
 
   // Layout: logit blocks are computed transposed (items x positions), so lane l
@@ -345,9 +349,18 @@ __global__ __launch_bounds__(64 * NW, 2) void k_sel_stream(SelectArgs p) {
   float vmx = NEG_INF;
   float hlo = -bnd, hsc = bnd > 0.0f ? (float)SEL_NB / (2.0f * bnd) : 0.0f;
   uint32_t nexact = 0;
-  // copies of one tile issued by the wave with the fewest (waiting for that many
-  // outstanding at most is enough for every wave)
-  constexpr int MINC = NW == 1 ? G::ROW_DMA + 1 : G::ROW_DMA / NW;
+  // Copies per tile: each wave its ROW_DMA / NW row copies, wave 0 also the ids
+  // of the tile three ahead, issued before the rows of the tile two ahead.  Once
+  // only the row copies of tile t+1 remain outstanding, tile t's rows and the ids
+  // of tile t+2 have landed (loads complete in order).
+  constexpr int MINC = G::ROW_DMA / NW;
+  auto issue_ids = [&](int tt) {
+    if (w == 0)
+      dma_ints(idring + (tt % SEL_IDS) * 64, p.perm_y, range_tile_start(win, tt, TI), range_tile_end(win, tt));
+  };
+  auto issue_rows = [&](int tt) {
+    dma_rows_gather<E, D, NW>(ring + (size_t)(tt % SEL_RING) * slot_bytes, Y, idring + (tt % SEL_IDS) * 64, w);
+  };
   if constexpr (!EXACT) {
 #pragma unroll
     for (int b = 0; b < SEL_NB / 4; ++b) hist_r[g * (SEL_NB / 4) + b] = 0u;
@@ -355,23 +368,25 @@ __global__ __launch_bounds__(64 * NW, 2) void k_sel_stream(SelectArgs p) {
   }
 
   if (k > 0) {
-    for (int t0 = 0; t0 < SEL_RING - 1 && t0 < ntiles; ++t0)
-      issue_window_tile<E, D, NW, SEL_RING>(ring, slot_bytes, win, t0, Ys, p.perm_y, nullptr, C, 0, w);
+    // the ids of tiles 0 .. 2, then the rows of tiles 0 and 1
+    for (int t0 = 0; t0 < SEL_RING && t0 < ntiles; ++t0) issue_ids(t0);
+    wait_vmcnt_c<0>();
+    raw_barrier();
+    for (int t0 = 0; t0 < SEL_RING - 1 && t0 < ntiles; ++t0) issue_rows(t0);
     for (int t = 0; t < ntiles; ++t) {
-      // tile t's copies are complete once only those of the tiles issued after it
-      // remain outstanding (loads complete in order)
-      static_assert(SEL_RING == 3, "one tile issued after the one waited for");
+      static_assert(SEL_RING == 3 && SEL_IDS == 4, "rows two tiles ahead, ids three");
       if (t + 1 < ntiles)
         wait_vmcnt_c<MINC>();
       else
         wait_vmcnt_c<0>();
-      raw_barrier();   // every wave's copies of tile t landed; slot (t - 1) % RING is free
-      if (t + SEL_RING - 1 < ntiles)
-        issue_window_tile<E, D, NW, SEL_RING>(ring, slot_bytes, win, t + SEL_RING - 1, Ys, p.perm_y, nullptr, C, 0,
-                                              w);
+      // every wave's copies of tile t and the ids of tile t+2 landed; row slot
+      // (t - 1) % RING and id slot (t - 1) % IDS are free
+      raw_barrier();
+      if (t + SEL_RING < ntiles) issue_ids(t + SEL_RING);
+      if (t + SEL_RING - 1 < ntiles) issue_rows(t + SEL_RING - 1);
       const int64_t q0 = range_tile_start(win, t, TI), q1 = range_tile_end(win, t);
       const char* slot = ring + (size_t)(t % SEL_RING) * slot_bytes;
-      const int32_t* tid_ = reinterpret_cast<const int32_t*>(slot + G::ROW_BYTES);
+      const int32_t* tid_ = idring + (t % SEL_IDS) * 64;
       const int nlim = (int)(q1 - q0);   // valid items of this tile
       const bool full = nlim >= TI;
 
@@ -405,7 +420,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_sel_stream(SelectArgs p) {
           for (int rr = 0; rr < 16; ++rr) {
             if (lane_val(cnt, rr) <= cap - TI) continue;
             int2* lrr = p.clist + (int64_t)lane_val((int)lrow, rr) * cap;
-            const E* xrr = Xs + (wrow0 + rr) * D;
+            const E* xrr = X + (int64_t)lane_val(iA, rr) * D;
             double te_n;
             int tid_n;
             compact_exact<E, D>(lrr, lane_val(cnt, rr), k, lane_val(beta, rr), xrr,
@@ -613,7 +628,7 @@ __global__ __launch_bounds__(256, 4) void k_sel_finish(SelectArgs p) {
 
 template <class E, int D, int NW>
 static size_t stream_lds_bytes(int cap_lds) {
-  return (size_t)SEL_RING * sel_slot_bytes(TileGeom<E, D>::ROW_BYTES) + (size_t)NW * sel_wave_bytes(cap_lds);
+  return (size_t)SEL_RING * TileGeom<E, D>::ROW_BYTES + SEL_IDS_BYTES + (size_t)NW * sel_wave_bytes(cap_lds);
 }
 
 // Waves per workgroup of the finishing kernel (LDS holds each wave's list), 0 if

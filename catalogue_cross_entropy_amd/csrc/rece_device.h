@@ -253,16 +253,6 @@ template <int D> struct Frag<float, D> {
   }
 };
 
-// One k-step of the block product (acc += A[:, ks] B[:, ks]^T).
-template <int D>
-__device__ __forceinline__ f32x4 mma_step(const Frag<bf16, D>& a, const Frag<bf16, D>& b, int ks, f32x4 acc) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v[ks], b.v[ks], acc, 0, 0, 0);
-}
-template <int D>
-__device__ __forceinline__ f32x4 mma_step(const Frag<float, D>& a, const Frag<float, D>& b, int ks, f32x4 acc) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[ks], b.v[ks], acc, 0, 0, 0);
-}
-
 template <int D>
 __device__ __forceinline__ f32x4 mma_block(const Frag<bf16, D>& a, const Frag<bf16, D>& b, f32x4 acc) {
 #pragma unroll

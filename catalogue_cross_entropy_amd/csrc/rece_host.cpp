@@ -106,7 +106,7 @@ struct rece_plan_s {
   size_t o_cnt, o_bx, o_by, o_px, o_py, o_te, o_tid, o_tlo, o_thi, o_msh, o_ssum, o_nmem, o_xnorm, o_ymax, o_lse,
       o_lpos, o_wmean, o_negs, saved_bytes;
   // forward scratch
-  size_t o_bt, o_bnorm, o_und, o_undy, o_sorty, o_sort, o_part, o_negl, o_xs, o_ys, o_cl0, o_cl1, o_cn0, o_cn1, o_cd0,
+  size_t o_bt, o_bnorm, o_und, o_undy, o_sorty, o_sort, o_part, o_negl, o_cl0, o_cl1, o_cn0, o_cn1, o_cd0,
       o_cd1, o_clo0, o_clo1;
   // backward scratch (the backward reuses the forward's scratch from offset 0)
   size_t o_pk0, o_pv0, o_pk1, o_pv1, o_psc, o_dya, o_pcoef;
@@ -236,8 +236,6 @@ static void plan_sce_layout(rece_plan_s* p) {
                                   sort_scratch_bytes(sy, 1 << std::min(12, bits_for(C)))});
   p->o_sort = sc.take(sort_b);
   p->o_part = sc.take((size_t)ce_blocks(s) * 16);
-  p->o_xs = sc.take((size_t)sx * d * p->esize);   // rows taken by each bucket, bucket-major
-  p->o_ys = sc.take((size_t)sy * d * p->esize);
   p->o_ssort = sc.take((size_t)sx * 4);
   p->o_sinv = sc.take((size_t)sx * 4);
   p->o_pstart = sc.take((size_t)s * 4);
@@ -329,18 +327,12 @@ static rece_status sce_forward(const rece_plan_s& p, hipStream_t st, const void*
   ca.vmax_bits = ymax;
   ca.out = Q;
   RECE_PHASE(RECE_PHASE_SORT, launch_col_select(p.bf16, d, ca, st), "bucket items");
-  char* xs = sc + p.o_xs;
-  char* ys = sc + p.o_ys;
-  RECE_PHASE(RECE_PHASE_SORT, launch_gather_rows(X, R, p.sx, d * p.esize, xs, st), "bucket position rows");
-  RECE_PHASE(RECE_PHASE_SORT, launch_gather_rows(Y, Q, p.sy, d * p.esize, ys, st), "bucket item rows");
 
   // per (bucket, position) slot, the top-k of the bucket's items (the chunk kernel,
   // one chunk per bucket, window = the chunk's own items)
   SelectArgs a{};
   a.X = X;
   a.Y = Y;
-  a.Xs = xs;
-  a.Ys = ys;
   a.rounds = 1;
   a.pos = pos;
   a.perm_x = R;
@@ -537,9 +529,6 @@ rece_status rece_plan(const rece_config* cfg, rece_plan_t* out) {
   p->o_part = sc.take((size_t)ce_blocks(s) * 16);
   // float32 logits of the kept lists of rounds >= 1 (the round dedup sums the new pairs)
   p->o_negl = sc.take((size_t)(r - 1) * s * k * 4);
-  // sorted copies of every round (each chunk and window one block of rows)
-  p->o_xs = sc.take((size_t)r * s * d * p->esize);
-  p->o_ys = sc.take((size_t)r * C * d * p->esize);
   // candidate lists of the chunk kernels: round 0 (caller's stream), rounds >= 1 (side stream, in turn)
   p->o_cl0 = sc.take((size_t)s * p->cap * 8);
   p->o_cn0 = sc.take((size_t)s * 4);
@@ -725,14 +714,10 @@ static rece_status forward_impl(const rece_plan_s& p, hipStream_t st, const void
   RECE_HIP(record(c.rounds, st), "fork");
   RECE_HIP(wait(side, c.rounds), "fork");
 
-  auto xs_of = [&](int rho) { return sc + p.o_xs + (size_t)rho * s * d * p.esize; };
-  auto ys_of = [&](int rho) { return sc + p.o_ys + (size_t)rho * C * d * p.esize; };
   auto select_args = [&](int rho) {
     SelectArgs a{};
     a.X = X;
     a.Y = Y;
-    a.Xs = xs_of(rho);
-    a.Ys = ys_of(rho);
     a.rounds = c.rounds;
     a.pos = pos;
     a.perm_x = reinterpret_cast<int32_t*>(sv + p.o_px) + (int64_t)rho * s;
@@ -778,7 +763,6 @@ static rece_status forward_impl(const rece_plan_s& p, hipStream_t st, const void
     RECE_HIP(record(c.rounds + 1, st), "position norms");
     RECE_PHASE(RECE_PHASE_SORT, launch_counting_sort(bx, nullptr, s, 0, p.nbits_b, sc + p.o_sort, px, nullptr, st),
                "sort positions");
-    RECE_PHASE(RECE_PHASE_SORT, launch_gather_rows(X, px, s, d * p.esize, xs_of(0), st), "sorted positions");
   }
 
   for (int rho = 0; rho < c.rounds; ++rho) {
@@ -792,7 +776,6 @@ static rece_status forward_impl(const rece_plan_s& p, hipStream_t st, const void
              "bucket items");
     RECE_PHASE(RECE_PHASE_SORT, launch_counting_sort(by, nullptr, C, 0, p.nbits_b, sc + p.o_sorty, py, nullptr, st),
                "sort items");
-    RECE_PHASE(RECE_PHASE_SORT, launch_gather_rows(Y, py, C, d * p.esize, ys_of(rho), st), "sorted items");
     if (rho == 0) {
       RECE_HIP(record(0, side), "item chain done");
       continue;
@@ -804,7 +787,6 @@ static rece_status forward_impl(const rece_plan_s& p, hipStream_t st, const void
                "bucket positions");
     RECE_PHASE(RECE_PHASE_SORT, launch_counting_sort(bx, nullptr, s, 0, p.nbits_b, sc + p.o_sorty, px, nullptr, st),
                "sort positions");
-    RECE_PHASE(RECE_PHASE_SORT, launch_gather_rows(X, px, s, d * p.esize, xs_of(rho), st), "sorted positions");
     if (rho == 1) RECE_HIP(wait(side, c.rounds + 1), "position norms");
     const SelectArgs a = select_args(rho);
     RECE_PHASE(RECE_PHASE_SELECT, launch_select(p.bf16, d, p.waves_sel, a, st), "chunk logits and top-k");

@@ -28,8 +28,6 @@ constexpr int ALIST = 64;           // near-tie list capacity at the k-th bounda
 struct SelectArgs {
   const void* X;
   const void* Y;
-  const void* Xs;             // round rho: X rows in sorted order
-  const void* Ys;             // round rho: Y rows in sorted order
   const int32_t* pos;
   const int32_t* perm_x;      // round rho
   const int32_t* perm_y;      // round rho
@@ -185,9 +183,6 @@ size_t dy_area_bytes(int64_t E, int d);
 // Every row of dY from the sorted records (K, V, *ntot of them); E bounds *ntot.
 hipError_t launch_dy(bool is_bf16, int d, const BwdArgs& a, const int32_t* K, const int32_t* V, const uint32_t* ntot,
                      int64_t E, void* area, hipStream_t st);
-hipError_t launch_gather_rows(const void* src, const int32_t* perm, int64_t n, int row_bytes, void* dst,
-                              hipStream_t st);
-
 // Bucket (SCE) variant.
 struct ColSelectArgs {
   const float* PT;            // [n_b][N] projection scores, one column per bucket

@@ -301,12 +301,6 @@ template <> struct LdsRead128<8> {
         : "memory");
   }
 };
-template <> struct LdsRead128<16> {
-  static __device__ __forceinline__ void run(const uint32_t* a, u32x4* r) {
-    LdsRead128<8>::run(a, r);
-    LdsRead128<8>::run(a + 8, r + 8);
-  }
-};
 // KS 16-byte reads from LDS at a[ks] + OFF (an immediate), one wait.
 template <int KS, int OFF> struct LdsReadOff128;
 template <int OFF> struct LdsReadOff128<1, OFF> {
@@ -369,6 +363,11 @@ template <> struct LdsReadB32<4> {
         : "memory");
   }
 };
+template <> struct LdsReadB32<1> {
+  static __device__ __forceinline__ void run(const uint32_t* a, float* r) {
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(r[0]) : "v"(a[0]) : "memory");
+  }
+};
 template <> struct LdsReadB32<2> {
   static __device__ __forceinline__ void run(const uint32_t* a, float* r) {
     asm volatile("ds_read_b32 %0, %2\n\tds_read_b32 %1, %3\n\ts_waitcnt lgkmcnt(0)"
@@ -378,32 +377,38 @@ template <> struct LdsReadB32<2> {
   }
 };
 
+// Gather rows into a swizzled LDS row block: row n of the block is row
+// ids[n] of `src` (ids in LDS, TileGeom<E, D>::TI of them); the same copy
+// numbering and swizzle as dma_rows (copy u by wave u % NW).  Callers mask rows
+// past the end of their range (their ids repeat the last one).
+template <class E, int D, int NW>
+__device__ __forceinline__ void dma_rows_gather(char* lds_rows, const E* __restrict__ src, const int32_t* lds_ids,
+                                                int wave) {
+  using G = TileGeom<E, D>;
+  constexpr int LRB = ilog2(G::RB);
+  constexpr int NQ = G::ROW_DMA / NW;   // copies of this wave
+  static_assert(G::ROW_DMA % NW == 0 && NQ >= 1, "whole copies per wave");
+  const int l = lane_id();
+  uint32_t a[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) a[q] = lds_addr(lds_ids + (((wave + q * NW) * 1024 + 16 * l) >> LRB));
+  float idf[NQ];
+  LdsReadB32<NQ>::run(a, idf);
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int u = wave + q * NW;
+    const int byte = u * 1024 + 16 * l;
+    const int n = byte >> LRB;
+    const int off = byte ^ ((n & G::SWM) << 4);   // chunk c of row n stored at c ^ (n & SWM)
+    const char* g = reinterpret_cast<const char*>(src) + (int64_t)__float_as_int(idf[q]) * G::RB + (off & (G::RB - 1));
+    __builtin_amdgcn_global_load_lds(g, (lds_void*)(lds_rows + u * 1024), 16, 0, 0);
+  }
+}
+
 // Matrix-core fragment of tile row n (B operand, "row = vector" layout).
 template <class E, int D> struct TileFrag;
 
 template <int D> struct TileFrag<bf16, D> {
-  // Fragments of rows n, n + 16, ..., n + 16 (NF - 1), read together (one wait).
-  template <int NF>
-  static __device__ __forceinline__ void load_n(Frag<bf16, D> (&f)[NF], const char* rows, int n) {
-    using G = TileGeom<bf16, D>;
-    constexpr int KS = D / 32;
-    const int q = lane_id() >> 4;
-    uint32_t a[NF * KS];
-    u32x4 raw[NF * KS];
-#pragma unroll
-    for (int j = 0; j < NF; ++j)
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int nn = n + 16 * j;
-        const int c = (4 * ks + q) ^ (nn & G::SWM);
-        a[j * KS + ks] = lds_addr(rows + nn * G::RB + c * 16);
-      }
-    LdsRead128<NF * KS>::run(a, raw);
-#pragma unroll
-    for (int j = 0; j < NF; ++j)
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) f[j].v[ks] = __builtin_bit_cast(bf16x8, raw[j * KS + ks]);
-  }
   static __device__ __forceinline__ void load(Frag<bf16, D>& f, const char* rows, int n) {
     using G = TileGeom<bf16, D>;
     constexpr int KS = D / 32;
@@ -421,11 +426,6 @@ template <int D> struct TileFrag<bf16, D> {
   }
 };
 template <int D> struct TileFrag<float, D> {
-  template <int NF>
-  static __device__ __forceinline__ void load_n(Frag<float, D> (&f)[NF], const char* rows, int n) {
-#pragma unroll
-    for (int j = 0; j < NF; ++j) load(f[j], rows, n + 16 * j);
-  }
   static __device__ __forceinline__ void load(Frag<float, D>& f, const char* rows, int n) {
     using G = TileGeom<float, D>;
     constexpr int KS = D / 4;
