@@ -489,7 +489,7 @@ def main():
         "memory": memory,
         "counters": {"argmax_rows_float64": counters[1], "topk_rows_near_tie": counters[2],
                      "logits_float64": counters[3], "overflows": counters[4],
-                     "select_rows_exact_pass": counters[5]},
+                     "select_rows_exact_pass": counters[5], "select_list_entries": counters[6]},
     }
     if full is not None:
         full["rece_speedup"] = round(full["ms_per_step"] / ms_step, 2)

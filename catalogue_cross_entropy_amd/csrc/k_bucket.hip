@@ -358,30 +358,46 @@ __global__ __launch_bounds__(256, (D * sizeof(E) == 256) ? 3 : 1) void k_project
   }
 }
 
-// Float64 decision of the listed rows, 16 rows per wave (grid-stride over the
-// list).  The float32 scores of every vector are recomputed on the matrix cores
-// to find each row's float32 maximum m; then only the vectors scoring at least
-// m - 2*beta are scored in float64.  The float64 argmax is among them: its
-// float32 score is at least its float64 score less beta, and that is at least
-// the float64 score of the float32 winner, which is at least m - beta.  Exact
-// float64 ties go to the lowest index, as in the oracle.
+// Float64 decision of the listed rows.  A workgroup takes 64 listed rows at a
+// time (16 per wave); the vectors stream once through an LDS ring shared by the
+// four waves, and each score is computed on the matrix cores as in the main
+// kernel (vectors x rows: lane l holds row l % 16 and vectors 4 (l / 16) + v of
+// every 16-block).  Per lane the four largest keys of its share of the vectors
+// are kept (score bits, vector index in the low bits).  The float64 argmax is
+// among the vectors whose float32 score is at least m - 2 beta (m the row's
+// float32 maximum): its float32 score is at least its float64 score less beta,
+// which is at least the float64 score of the float32 winner, at least m - beta.
+// When m - 2 beta > 0 those vectors score above zero, where keys order like
+// scores, so each lane's band members are among its four keys unless its fourth
+// key is itself inside the band; those (and rows with m - 2 beta <= 0) are redone
+// by the wave over every vector in float64.  Band members are scored in float64;
+// exact ties go to the lowest index, as in the oracle.
 template <class E, int D>
 __global__ __launch_bounds__(256) void k_argmax_near(const E* __restrict__ V, const E* __restrict__ Bt, int n_b,
                                                      const float* __restrict__ bnorm_max, float beta_coef,
                                                      const int32_t* __restrict__ und,
                                                      const uint32_t* __restrict__ und_n, int32_t* __restrict__ ids,
                                                      uint32_t* __restrict__ counters) {
-  constexpr int UB = D * (int)sizeof(E) >= 512 ? 1 : (D * (int)sizeof(E) >= 256 ? 2 : 4);   // blocks in flight
+  using G = TileGeom<E, D>;
+  constexpr int NW = 4;
+  constexpr int NCB = G::TI / 16;
+  __shared__ __attribute__((aligned(1024))) char ring[3 * G::ROW_BYTES];
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l = lane_id(), r = l & 15, g = l >> 4;
   const int64_t nund = *und_n;
-  const int64_t wv = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6), nwv = (int64_t)gridDim.x * 4;
+  const int nt = (n_b + G::TI - 1) / G::TI;
+  const int ib = n_b > 1 ? 32 - __builtin_clz((unsigned)(n_b - 1)) : 0;
+  const int imask = (1 << ib) - 1;
+  const double tau = ldexp(1.0, ib - 23);   // relative truncation of a key's score
   const float bmax = bnorm_max[0];
   uint32_t done = 0;
-  for (int64_t g0 = wv * 16; g0 < nund; g0 += nwv * 16) {
-    const bool rv = g0 + r < nund;
-    const int64_t row = rv ? und[g0 + r] : 0;
+  for (int64_t g0 = (int64_t)blockIdx.x * 64; g0 < nund; g0 += (int64_t)gridDim.x * 64) {
+    const int64_t slot = g0 + 16 * w + r;
+    const bool rv = slot < nund;
+    const int64_t row = rv ? und[slot] : 0;
     Frag<E, D> afr;
     afr.load_global(rv ? V + row * D : nullptr);
+    afr.settle();
     // the row's norm from its fragment (spread over the row's four lanes), as in
     // the matrix-core kernel
     float ss = 0.0f;
@@ -400,40 +416,67 @@ __global__ __launch_bounds__(256) void k_argmax_near(const E* __restrict__ V, co
     ss += __shfl_xor(ss, 16);
     ss += __shfl_xor(ss, 32);
     const double beta = (double)beta_coef * (double)(sqrtf(ss) * (1.0f + 0.0005f)) * (double)bmax;
-    float mx = NEG_INF, lo = 0.0f;
-    double be = -__builtin_huge_val();
-    int bi = 0x7fffffff;
-    for (int pass = 0; pass < 2; ++pass) {
-      for (int b0 = 0; b0 < n_b; b0 += 16 * UB) {
-        Frag<E, D> bf[UB];
+
+    int k1 = INT32_MIN, k2 = INT32_MIN, k3 = INT32_MIN, k4 = INT32_MIN;
+    __syncthreads();   // the previous group's reads of the ring are done
+    dma_rows<E, D, NW>(ring, Bt, 0, n_b, w);
+    if (nt > 1) dma_rows<E, D, NW>(ring + G::ROW_BYTES, Bt, G::TI, n_b, w);
+    for (int t = 0; t < nt; ++t) {
+      if (t + 1 < nt)
+        wait_vmcnt_c<G::ROW_DMA / NW>();
+      else
+        wait_vmcnt_c<0>();
+      raw_barrier();
+      if (t + 2 < nt)
+        dma_rows<E, D, NW>(ring + (size_t)((t + 2) % 3) * G::ROW_BYTES, Bt, (int64_t)(t + 2) * G::TI, n_b, w);
+      const char* rows = ring + (size_t)(t % 3) * G::ROW_BYTES;
+      const bool pad = (t + 1) * G::TI > n_b;
 #pragma unroll
-        for (int u = 0; u < UB; ++u) {
-          const int b = b0 + 16 * u + r;   // the vector of this lane's operand row
-          bf[u].load_global(b < n_b ? Bt + (int64_t)b * D : nullptr);
+      for (int cb = 0; cb < NCB; ++cb) {
+        Frag<E, D> bf;
+        TileFrag<E, D>::load(bf, rows, cb * 16 + r);
+        const int b0 = t * G::TI + cb * 16 + 4 * g;   // vector of element v: b0 + v
+        f32x4 c0{0.0f, 0.0f, 0.0f, 0.0f};
+        if (pad) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) c0[v] = b0 + v < n_b ? 0.0f : NEG_INF;
         }
+        const f32x4 acc = mma_block(bf, afr, c0);   // [vector 4g+v][row r]
 #pragma unroll
-        for (int u = 0; u < UB; ++u) {
-          const f32x4 acc = mma_block(bf[u], afr, f32x4{0.f, 0.f, 0.f, 0.f});   // [vector 4g+v][row r]
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int b = b0 + 16 * u + 4 * g + v;
-            if (b >= n_b) continue;
-            if (pass == 0) {
-              mx = fmaxf(mx, acc[v]);
-            } else if (rv && acc[v] >= lo) {
-              const double e = exact_dot<E, D, 4>(V + row * D, Bt + (int64_t)b * D);
-              if (e > be || (e == be && b < bi)) {
-                be = e;
-                bi = b;
-              }
-            }
-          }
+        for (int v = 0; v < 4; ++v) {
+          const int key = (__float_as_int(acc[v]) & ~imask) | (b0 + v);
+          k4 = med3_i(k3, k4, key);
+          k3 = med3_i(k2, k3, key);
+          k2 = med3_i(k1, k2, key);
+          k1 = max(k1, key);
         }
       }
-      if (pass == 0) {
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        lo = f_down((double)mx - 2.0 * beta);
+    }
+    // the band [m - 2 beta, m] of the row, from its largest key
+    int km = max(k1, __shfl_xor(k1, 16));
+    km = max(km, __shfl_xor(km, 32));
+    const double sm = (double)__int_as_float(km & ~imask);   // m is at least this
+    const double thr = sm - 2.0 * beta;
+    auto in_band = [&](int kq) {
+      const double sq = (double)__int_as_float(kq & ~imask);
+      return kq >= 0 && sq + fabs(sq) * tau >= thr;   // the key's score is at most sq + |sq| tau
+    };
+    bool redo = !(km >= 0 && thr > 0.0) || in_band(k4);
+    redo = redo || __shfl_xor(redo, 16);
+    redo = redo || __shfl_xor(redo, 32);
+    double be = -__builtin_huge_val();
+    int bi = 0x7fffffff;
+    if (rv && !redo) {
+      const int kk[3] = {k1, k2, k3};   // the fourth key is outside the band here
+#pragma unroll
+      for (int q = 0; q < 3; ++q) {
+        if (!in_band(kk[q])) continue;
+        const int b = kk[q] & imask;
+        const double e = exact_dot<E, D, 4>(V + row * D, Bt + (int64_t)b * D);
+        if (e > be || (e == be && b < bi)) {
+          be = e;
+          bi = b;
+        }
       }
     }
 #pragma unroll
@@ -445,7 +488,17 @@ __global__ __launch_bounds__(256) void k_argmax_near(const E* __restrict__ V, co
         bi = ob;
       }
     }
-    if (rv && g == 0) ids[row] = bi < n_b ? bi : 0;   // no candidate only with NaN scores
+    if (rv && !redo && g == 0) ids[row] = bi < n_b ? bi : 0;
+    // rows the four keys cannot settle: every vector in float64, one row at a time
+    uint64_t rm = ballot(rv && redo && g == 0);
+    while (rm) {
+      const int rr = __builtin_ctzll(rm);
+      rm &= rm - 1;
+      const int64_t rrow = lane_val((int)row, rr);
+      int bx = argmax_exact_wave<E, D>(V + rrow * D, Bt, n_b);
+      if (bx >= n_b) bx = 0;   // only reachable with NaN scores
+      if (l == 0) ids[rrow] = bx;
+    }
     done += (uint32_t)popc(ballot(rv && g == 0));
   }
   if (l == 0 && done) atomicAdd(counters + CNT_ARGMAX_EXACT, done);

@@ -116,7 +116,7 @@ __device__ __attribute__((noinline)) void compact_exact(int2* list, int n, int k
     }
     nb += popc(mk);
   }
-  nexact += (uint32_t)nb;
+  if (l == 0) nexact += (uint32_t)nb;   // lane 0 keeps the wave's count
   wave_sync();
   const int need = k - nabove;   // band entries kept (>= 1)
   double te = 0.0;
@@ -346,6 +346,8 @@ __global__ __launch_bounds__(64 * NW, 2) void k_sel_stream(SelectArgs p) {
   float lo = take ? NEG_INF : __builtin_huge_valf();
   int cnt = 0, last_raise = 0;
   int compacted = 0, redo = 0;
+  int fine = 0;   // the row's histogram map has been rebuilt around its k-th value
+  uint32_t nlisted = 0;   // entries this lane appended to lists
   float vmx = NEG_INF;
   float hlo = -bnd, hsc = bnd > 0.0f ? (float)SEL_NB / (2.0f * bnd) : 0.0f;
   uint32_t nexact = 0;
@@ -391,8 +393,21 @@ __global__ __launch_bounds__(64 * NW, 2) void k_sel_stream(SelectArgs p) {
       const bool full = nlim >= TI;
 
       if constexpr (!EXACT) {
-        // threshold raises, from the histograms (no list traffic)
-        if (!p.selall && ballot(cnt > k && cnt - last_raise >= SEL_RAISE_EVERY)) {
+        // The first raise of a row compacts its list, which rebuilds the histogram
+        // on [threshold, largest value]: the initial map spans every possible logit
+        // and its bins are far too coarse to follow the k-th value, so the threshold
+        // would lag behind it and let through several times the candidates.
+        if (!p.selall && ballot(take && !fine && cnt > k)) {
+          wait_vmcnt(0);   // this wave's list stores have reached memory
+          const bool act = take && !fine && cnt > k;
+          compact_hist(list, act, cnt, k, beta, lo, hlo, hsc, vmx, hist_r);
+          if (act) {
+            fine = 1;
+            last_raise = cnt;
+            compacted = 1;
+          }
+        } else if (!p.selall && ballot(cnt > k && cnt - last_raise >= SEL_RAISE_EVERY)) {
+          // threshold raises, from the histograms (no list traffic)
           const int found = row_kth_bin(hist_r, g, r, k);
           if (take && cnt > k && cnt - last_raise >= SEL_RAISE_EVERY) {
             raise_from_bin(found, hlo, hsc, beta, lo);
@@ -467,6 +482,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_sel_stream(SelectArgs p) {
         const int c1 = __shfl_xor(c0, 16), c2 = __shfl_xor(c0, 32), c3 = __shfl_xor(c0, 48);   // lanes g^1, g^2, g^3
         int slotn = cnt + ((g & 1) ? c1 : 0) + ((g & 2) ? c2 + c3 : 0);
         cnt += c0 + c1 + c2 + c3;
+        nlisted += (uint32_t)c0;
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
           if (!((cm >> (4 * cb)) & 15u)) continue;
@@ -490,6 +506,7 @@ __global__ __launch_bounds__(64 * NW, 2) void k_sel_stream(SelectArgs p) {
     }
   }
   flush_count(p.counters + CNT_LOGIT_EXACT, nexact);
+  flush_count(p.counters + CNT_LISTED, nlisted);
   if constexpr (!EXACT) {
     // the tightest threshold for the finishing kernel's filter
     if (!p.selall && ballot(take && cnt > k && cnt > last_raise)) {

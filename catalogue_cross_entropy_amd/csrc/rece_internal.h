@@ -17,6 +17,7 @@ enum Counter {
   CNT_LOGIT_EXACT = 3,    // logits recomputed in float64 (selection and dedup tests)
   CNT_OVERFLOW = 4,       // selection buffers that could not be compacted
   CNT_SEL_REDO = 5,       // rows whose candidate list went to the exact pass (ties by the hundred)
+  CNT_LISTED = 6,         // candidate entries appended to the selection lists
   NUM_COUNTERS = 8
 };
 enum ErrBit : uint32_t { ERRBIT_BAD_ID = 1u, ERRBIT_OVERFLOW = 2u };

@@ -240,7 +240,8 @@ typedef enum {
                                 decided in float64, [2] top-k rows needing float64 values,
                                 [3] logits recomputed in float64, [4] buffer overflows,
                                 [5] rows whose top-k candidates went through the exact
-                                pass (hundreds of ties near the k-th logit) */
+                                pass (hundreds of ties near the k-th logit), [6] candidate
+                                entries appended to the selection lists */
   RECE_STAGE_SCE_ROWS = 9,   /* SCE: int32 [n_b][b_x] positions taken by each bucket (a set per
                                 bucket, in the library's order) */
   RECE_STAGE_SCE_ITEMS = 10, /* SCE: int32 [n_b][b_y] items taken by each bucket (a set per bucket) */

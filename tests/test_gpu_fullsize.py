@@ -282,3 +282,29 @@ def test_bucketing_ties_on_large_input_decided_in_float64():
     sy = np.concatenate([rng.choice(tied, 256, replace=False), rng.choice(w.C, 2048, replace=False)])
     assert np.array_equal(by[sy], oracle.bucket_ids(inp.Y[sy], inp.B[0]))
     assert cnt[1] >= len(tied)                 # each of them went through the float64 decision
+
+
+def test_bucketing_many_equal_vectors_on_large_input():
+    """Random vector 0 is copied to vectors 1, 2, 3, 16, 17, 18 and 19, which one
+    lane of the float64 list kernel scores together: rows whose best vector is a
+    copy have eight equal float32 scores in that lane's share, more than its four
+    kept keys, so they take the kernel's fallback over every vector in float64.
+    Each must get index 0 (lowest index among equal float64 scores)."""
+    w = scaled("million", seqs=16, seqlen=256, C=600_000, n_b=64, n_c=64, k=32, rounds=1)
+    inp = make_inputs(w)
+    for j in (1, 2, 3, 16, 17, 18, 19):
+        inp.B[0][:, j] = inp.B[0][:, 0]
+    X, Y, pos, B = to_device(inp)
+    plan = rece.Plan(w.s, w.C, w.d, w.n_b, w.n_c, w.k, w.rounds, dtype=w.dtype, keep_stages=True,
+                     validate_ids=True)
+    print("[gpu] bucketing, eight equal vectors, C=600000", flush=True)
+    loss, lpp, scratch, saved = plan.forward(X, Y, pos, B)
+    plan.check(saved)
+    by = plan.export(saved, "bucket_y", 0).cpu().numpy()
+    torch.cuda.synchronize()
+    assert not np.any(np.isin(by, [1, 2, 3, 16, 17, 18, 19]))   # a copy never wins
+    rng = np.random.default_rng(12)
+    tied = np.flatnonzero(by == 0)
+    assert len(tied) > 1000
+    sy = np.concatenate([rng.choice(tied, 256, replace=False), rng.choice(w.C, 2048, replace=False)])
+    assert np.array_equal(by[sy], oracle.bucket_ids(inp.Y[sy], inp.B[0]))
