@@ -49,9 +49,22 @@ def build_library(jobs: int = 8) -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
+    _check_stubs(tmp)
     os.replace(tmp, LIB)
     build_peaks()
     return LIB
+
+
+def _check_stubs(path: str) -> None:
+    """Fail when a kernel's host launch stub is missing from the library: hipcc drops
+    the stub of a kernel template whose body the host pass cannot instantiate (for
+    example a device builtin called straight from a lambda) without an error, and
+    the library then fails to load."""
+    res = subprocess.run(["nm", "-D", "--undefined-only", path], capture_output=True, text=True)
+    missing = [ln.split()[-1] for ln in res.stdout.splitlines() if "__device_stub__" in ln]
+    if missing:
+        raise RuntimeError("kernel launch stubs missing from the library (host pass failed to instantiate):\n  "
+                           + "\n  ".join(missing[:10]))
 
 
 def build_peaks() -> str:

@@ -169,11 +169,10 @@ __global__ __launch_bounds__(256, (D * sizeof(E) == 256) ? 3 : 1) void k_project
 #pragma unroll
     for (int ks = 0; ks < Frag<E, D>::KS; ++ks) {
       if constexpr (sizeof(E) == 2) {
+        // pairs of squares per instruction (exact products, float32 sums)
+        const u32x4 w4 = __builtin_bit_cast(u32x4, a[f].v[ks]);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const float x = to_f32(a[f].v[ks][t]);
-          ss = fmaf(x, x, ss);
-        }
+        for (int t = 0; t < 4; ++t) ss = bf16_pair_sq_acc(w4[t], ss);
       } else {
         ss = fmaf(a[f].v[ks], a[f].v[ks], ss);
       }
@@ -210,6 +209,18 @@ __global__ __launch_bounds__(256, (D * sizeof(E) == 256) ? 3 : 1) void k_project
     uint32_t fa0[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) fa0[ks] = lds_addr(ring + n0 * G::RB + (((4 * ks + q) ^ (n0 & G::SWM)) * 16));
+    // this wave's copies of a tile: per-lane source offsets inside the tile's rows,
+    // advanced by whole tiles (tiles that pass n_b take dma_rows, which clamps)
+    constexpr int NQ = G::ROW_DMA / NW;
+    static_assert(G::ROW_DMA % NW == 0, "whole copies per wave");
+    constexpr int LRB = ilog2(G::RB);
+    const char* gq[NQ];
+#pragma unroll
+    for (int qq = 0; qq < NQ; ++qq) {
+      const int byte = (w + qq * NW) * 1024 + 16 * l;
+      gq[qq] = reinterpret_cast<const char*>(Bt) + (byte ^ (((byte >> LRB) & G::SWM) << 4));
+    }
+    const int nfull_t = n_b / G::TI;   // tiles with no row past n_b
     auto tile = [&](auto pad_c, int t) {
       constexpr bool PAD = decltype(pad_c)::value;
       if (t + 1 < nt)
@@ -218,8 +229,15 @@ __global__ __launch_bounds__(256, (D * sizeof(E) == 256) ? 3 : 1) void k_project
         wait_vmcnt_c<0>();
       raw_barrier();   // every wave's copies of tile t landed; slot (t+2) % 3 is free
       const int slot = t % 3;
-      if (t + 2 < nt)
+      if (t + 2 < nfull_t) {
+        char* dst = ring + (size_t)((t + 2) % 3) * G::ROW_BYTES;
+        const int64_t adv = (int64_t)(t + 2) * G::ROW_BYTES;
+#pragma unroll
+        for (int qq = 0; qq < NQ; ++qq)
+          dma_copy16(gq[qq] + adv, dst + (w + qq * NW) * 1024);
+      } else if (t + 2 < nt) {
         dma_rows<E, D, NW>(ring + (size_t)((t + 2) % 3) * G::ROW_BYTES, Bt, (int64_t)(t + 2) * G::TI, n_b, w);
+      }
       uint32_t fa[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) fa[ks] = fa0[ks] + (uint32_t)(slot * G::ROW_BYTES);

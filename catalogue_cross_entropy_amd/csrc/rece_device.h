@@ -178,6 +178,13 @@ __device__ __forceinline__ int xcd_block(int b, int nblocks) {
   return x * per + (x < rem ? x : rem) + b / NX;
 }
 
+// acc + lo^2 + hi^2 for the two bf16 values packed in w (one v_dot2 instruction).
+__device__ __forceinline__ float bf16_pair_sq_acc(uint32_t w, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 x2 = __builtin_bit_cast(bf16x2, w);
+  return __builtin_amdgcn_fdot2_f32_bf16(x2, x2, acc, false);
+}
+
 // Outward rounding of a float64 interval end to float32.
 // bf16 bit pattern of x, rounded to nearest even.
 __device__ __forceinline__ uint32_t bf16_bits_rne(float x) {

@@ -98,6 +98,11 @@ __device__ __forceinline__ void raw_barrier() {
 
 __host__ __device__ constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
 
+// One wave copy: 16 bytes per lane from g into LDS at lds (lane l at lds + 16 l).
+__device__ __forceinline__ void dma_copy16(const char* g, char* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
+}
+
 // Copy rows [r0, r0 + TI) of `src` (row-major, RB bytes per row) into a swizzled
 // LDS row block; rows at or beyond r_end repeat row r_end - 1 (callers mask them).
 // Copy u (0 <= u < ROW_DMA) is issued by wave (u % NW); returns this wave's count.
