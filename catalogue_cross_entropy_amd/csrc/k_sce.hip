@@ -366,7 +366,29 @@ hipError_t launch_group_bounds(const int32_t* keys, const int32_t* sorted, int64
 }
 
 // ------------------------------------------------------------ merge per position
-__host__ __device__ constexpr size_t merge_wave_bytes(int k) { return topk_wave_bytes(2 * k); }
+// Per wave: the merge list (up to 2k entries, as topk_wave_bytes), then a hash set of
+// the ids in the list (open addressing, at most a quarter full).
+__host__ __device__ constexpr int merge_hash_size(int k) {
+  int h = 256;
+  while (h < 4 * k) h *= 2;
+  return h;
+}
+__host__ __device__ constexpr size_t merge_list_bytes(int k) { return (topk_wave_bytes(2 * k) + 15) / 16 * 16; }
+__host__ __device__ constexpr size_t merge_wave_bytes(int k) {
+  return merge_list_bytes(k) + (size_t)merge_hash_size(k) * 4;
+}
+constexpr uint32_t HASH_EMPTY = 0xFFFFFFFFu;
+
+// Insert item id j (>= 0) into the wave's hash set; true if it was not there.
+__device__ __forceinline__ bool hash_insert(uint32_t* tab, int hmask, int j) {
+  int h = (int)(((uint32_t)j * 2654435761u) >> 8) & hmask;
+  while (true) {
+    const uint32_t old = atomicCAS(tab + h, HASH_EMPTY, (uint32_t)j);
+    if (old == HASH_EMPTY) return true;
+    if (old == (uint32_t)j) return false;
+    h = (h + 1) & hmask;
+  }
+}
 size_t merge_lds_bytes(int k) { return 4 * ((merge_wave_bytes(k) + 15) / 16 * 16); }
 
 template <class E, int D>
@@ -375,6 +397,10 @@ __device__ __forceinline__ void sce_merge_row(const MergeArgs& a, char* smem, in
   const int k = a.k;
   char* base = smem + (size_t)w * ((merge_wave_bytes(k) + 15) / 16 * 16);
   const MergeLds L = carve_topk(base, 2 * k);
+  uint32_t* tab = reinterpret_cast<uint32_t*>(base + merge_list_bytes(k));   // the ids in L
+  const int hmask = merge_hash_size(k) - 1;
+  for (int t = l; t <= hmask; t += WAVE) tab[t] = HASH_EMPTY;
+  wave_sync();
   const E* X = static_cast<const E*>(a.X);
   const E* Y = static_cast<const E*>(a.Y);
   const E* xrow = X + i * D;
@@ -392,17 +418,10 @@ __device__ __forceinline__ void sce_merge_row(const MergeArgs& a, char* smem, in
       if (!truncated) trunc_slot = slot;
       truncated = true;
     }
-    const int before = cnt;
     for (int e0 = 0; e0 < k; e0 += WAVE) {
       const int e = e0 + l;
       const int j = e < k ? a.slot_negs[(int64_t)slot * k + e] : -1;
-      bool keep = j >= 0;
-      if (keep)
-        for (int u = 0; u < before; ++u)
-          if (L.ids[u] == j) {
-            keep = false;
-            break;
-          }
+      const bool keep = j >= 0 && hash_insert(tab, hmask, j);   // ids already in L are dropped
       const uint64_t mk = ballot(keep);
       if (keep) {
         const int dst = cnt + popc(mk & lanemask_lt());
@@ -417,6 +436,11 @@ __device__ __forceinline__ void sce_merge_row(const MergeArgs& a, char* smem, in
       reduce_to_k<E, D>(L, cnt, k, beta, xrow, Y, te, tid, nexact, a.counters);
       cnt = k;
       reduced = true;
+      // the set again holds exactly the ids left in L
+      for (int t = l; t <= hmask; t += WAVE) tab[t] = HASH_EMPTY;
+      wave_sync();
+      for (int t = l; t < cnt; t += WAVE) hash_insert(tab, hmask, L.ids[t]);
+      wave_sync();
     }
   }
   if (!reduced && truncated) {   // the union is one bucket's list: its threshold stands
