@@ -369,6 +369,67 @@ __global__ __launch_bounds__(64 * NW, 2) void k_sel_stream(SelectArgs p) {
     wave_sync();
   }
 
+  if constexpr (!EXACT) {
+    if (p.prepass && k > 0 && !p.selall) {
+      // Pass 0 (windows of a few k): every logit of the row's window, the positive
+      // included and items past a range's end left out, into the row's histogram
+      // on [0, bound].  The bin of the (k+1)-th largest then bounds the k-th
+      // largest negative from below, and the listing pass starts with its
+      // threshold there instead of at -inf (far fewer entries listed).
+      hlo = 0.0f;
+      hsc = bnd > 0.0f ? (float)SEL_NB / bnd : 0.0f;
+      for (int t0 = 0; t0 < SEL_RING && t0 < ntiles; ++t0) issue_ids(t0);
+      wait_vmcnt_c<0>();
+      raw_barrier();
+      for (int t0 = 0; t0 < SEL_RING - 1 && t0 < ntiles; ++t0) issue_rows(t0);
+      for (int t = 0; t < ntiles; ++t) {
+        if (t + 1 < ntiles)
+          wait_vmcnt_c<MINC>();
+        else
+          wait_vmcnt_c<0>();
+        raw_barrier();
+        if (t + SEL_RING < ntiles) issue_ids(t + SEL_RING);
+        if (t + SEL_RING - 1 < ntiles) issue_rows(t + SEL_RING - 1);
+        const int64_t q0 = range_tile_start(win, t, TI), q1 = range_tile_end(win, t);
+        const char* slot = ring + (size_t)(t % SEL_RING) * slot_bytes;
+        const int nlim = (int)(q1 - q0);
+        const bool full = nlim >= TI;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          Frag<E, D> bf;
+          TileFrag<E, D>::load(bf, slot, cb * 16 + r);
+          const f32x4 a4 = mma_block(bf, afr, f32x4{0.f, 0.f, 0.f, 0.f});   // [item 4g+v][row r]
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            if (take && (full || cb * 16 + 4 * g + v < nlim)) {
+              vmx = __builtin_amdgcn_fmed3f(vmx, a4[v], __builtin_huge_valf());
+              lds_add_u32(hist_r + sel_bin(a4[v], hlo, hsc), 1u);
+            }
+          }
+        }
+      }
+      raw_barrier();   // every wave is done with the ring before the listing pass refills it
+      const int found = row_kth_bin(hist_r, g, r, k + 1);
+      if (take) raise_from_bin(found, hlo, hsc, beta, lo);
+      float rmx = fmaxf(vmx, __shfl_xor(vmx, 16));
+      rmx = fmaxf(rmx, __shfl_xor(rmx, 32));
+      if (take && lo > NEG_INF) {   // a fine map from the threshold to the row's largest logit
+        hlo = lo;
+        hsc = rmx > lo ? (float)SEL_NB / (rmx - lo) : 0.0f;
+        fine = 1;
+        compacted = 1;   // the list leaves out entries below a threshold: the finish ranks it
+      } else {   // no threshold: the listing pass as without this pass
+        hlo = -bnd;
+        hsc = bnd > 0.0f ? (float)SEL_NB / (2.0f * bnd) : 0.0f;
+      }
+      wave_sync();
+#pragma unroll
+      for (int b = 0; b < SEL_NB / 4; ++b) hist_r[g * (SEL_NB / 4) + b] = 0u;
+      wave_sync();
+      vmx = NEG_INF;
+    }
+  }
+
   if (k > 0) {
     // the ids of tiles 0 .. 2, then the rows of tiles 0 and 1
     for (int t0 = 0; t0 < SEL_RING && t0 < ntiles; ++t0) issue_ids(t0);

@@ -94,6 +94,7 @@ struct rece_plan_s {
   int nbits_b;
   int cap;            // entries of a row's candidate list in the chunk kernels
   int selall;         // every window has at most k candidates
+  int prepass;        // windows of a few k: the chunk kernel's histogram pass sets the first threshold
   int waves_sel;
   int win_order;   // walking order of a window's chunks (window_rotation)
   int tpc_sel;
@@ -357,6 +358,7 @@ static rece_status sce_forward(const rece_plan_s& p, hipStream_t st, const void*
   a.negl = reinterpret_cast<float*>(sc + p.o_snegl);
   a.slot_out = 1;
   a.n_ec = 0;
+  a.prepass = p.prepass;
   a.wrap = 0;
   a.cap = p.cap;
   a.selall = p.selall;
@@ -460,6 +462,10 @@ rece_status rece_plan(const rece_config* cfg, rece_plan_t* out) {
   // catalogue has C - 1 candidates, the positive being excluded); the candidate lists
   // then hold whole windows and are never compacted
   p->selall = sce ? (k >= c.b_y) : (p->wmax >= C ? (k >= C - 1) : (k >= p->wmax));
+  // Windows of up to 24 k: a first pass over the window (histogram only) lists a few
+  // k entries per row instead of about k (1 + ln(W / k)) with a threshold that
+  // starts at -inf; with larger windows the extra pass costs more than it saves.
+  p->prepass = !p->selall && k > 0 && p->wmax <= 24 * (int64_t)k;
   p->cap = p->selall ? (int)std::max<int64_t>(p->wmax, 1) : select_list_cap(k, d, p->bf16);
   if (p->selall && p->wmax >= ((int64_t)1 << 30)) {   // list lengths share a word with two flag bits
     delete p;
@@ -743,6 +749,7 @@ static rece_status forward_impl(const rece_plan_s& p, hipStream_t st, const void
     a.n_ec = c.n_ec;
     a.wrap = c.window_wrap;
     a.win_order = p.win_order;
+    a.prepass = p.prepass;
     a.cap = p.cap;
     a.selall = p.selall;
     a.clist = reinterpret_cast<int2*>(sc + (rho == 0 ? p.o_cl0 : p.o_cl1));

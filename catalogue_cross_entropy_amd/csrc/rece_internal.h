@@ -52,6 +52,7 @@ struct SelectArgs {
   int n_ec;                   // window: chunks c - n_ec .. c + n_ec
   int wrap;                   // 1: chunk indices modulo n_c (cyclic); 0: clipped to [0, n_c)
   int win_order;              // walking order of the window's chunks (window_rotation)
+  int prepass;                // 1: a histogram pass over the window sets the first threshold
   int2* clist;                // [rows][cap] candidate lists (item id, float32 logit bits)
   int32_t* clist_n;           // [rows] entries in each list; bit 31: compacted or raised, bit 30: redo
   float* clist_lo;            // [rows] each row's final threshold (no kept entry lies below it)
