@@ -229,7 +229,7 @@ __device__ __forceinline__ bool pair_at(const PairSrc& a, int64_t t, int64_t n, 
     const int kp = a.pos[ip];
     key = isl ? kn : kp;
     val = isl ? (int)(((uint32_t)tc / (uint32_t)a.k) % (uint32_t)a.s) : ((int)ip | (int)0x80000000u);
-    return t < n && key >= 0 && key < a.C;
+    return (int)(t < n) & (int)(key >= 0) & (int)(key < a.C);   // no short-circuit: no branch between loads
   } else {
     key = a.kin[tc];
     val = a.vin[tc];
