@@ -97,6 +97,7 @@ struct rece_plan_s {
   int prepass;        // windows of a few k: the chunk kernel's histogram pass sets the first threshold
   int waves_sel;
   int win_order;   // walking order of a window's chunks (window_rotation)
+  int items_ahead;    // forward stream arrangement: item chains ahead of the chunk kernels
   int tpc_sel;
   int64_t wmax;       // largest window (items)
   float beta_coef;
@@ -488,6 +489,12 @@ rece_status rece_plan(const rece_config* cfg, rece_plan_t* out) {
     const int64_t chunk_bytes = (sce ? c.b_y : (C + n_c - 1) / n_c) * (int64_t)d * p->esize;
     p->win_order = sce ? 0 : (chunk_bytes >= ((int64_t)1 << 20) ? 2 : 1);
   }
+  // The item chains go ahead of the chunk kernels when the bucketing of the items
+  // (C n_b products per round) outweighs the chunk logits (s times the window) four
+  // times over: the chunk kernels then wait the least with one round's chain hidden
+  // behind the previous round's chunk kernel.  Below that the chunk kernels of
+  // different rounds are better run side by side.
+  p->items_ahead = !sce && (int64_t)C * c.n_b >= 4 * (int64_t)s * p->wmax;
   while (p->waves_sel > 1 && select_lds_bytes(p->bf16, d, p->waves_sel, cap_lds) > 160 * 1024) p->waves_sel /= 2;
   if (select_lds_bytes(p->bf16, d, p->waves_sel, cap_lds) > 160 * 1024) {
     delete p;
@@ -700,13 +707,18 @@ static rece_status forward_impl(const rece_plan_s& p, hipStream_t st, const void
   RECE_PHASE(RECE_PHASE_OTHER, launch_prep_b(p.bf16, d, B, c.rounds, c.n_b, Bt, bnorm, -1, st),
              "prepare random vectors");
 
-  // Item chain of every round (bucketing, sort, sorted copy) and the position
-  // chains of rounds >= 1 run on the side stream, followed there by the chunk
-  // kernels of rounds >= 1 (a round's selection does not depend on the other
-  // rounds); round 0's position chain and chunk kernel run on the caller's
-  // stream.  Events: fork[rounds] starts the side stream, fork[rounds + 1] marks
-  // the position norms of round 0 (every chunk kernel reads them), fork[0] the end
-  // of round 0's item chain, fork[rounds + 2] the end of the side stream.
+  // Two streams.  With a catalogue much larger than the rounds' windows
+  // (items_ahead), the item chain of every round (bucketing and sort of the C
+  // items, then the largest part of the forward pass) runs on the side stream
+  // ahead of the chunk kernels, which run in turn on the caller's stream after the
+  // position chains: the chain of round rho + 1 runs while the chunk kernel of
+  // round rho does.  Otherwise the side stream takes the item chains, the position
+  // chains of rounds >= 1 and the chunk kernels of rounds >= 1, while round 0's
+  // position chain and chunk kernel run on the caller's stream (the chunk kernels
+  // of different rounds then run at the same time).  Events: fork[rounds] starts
+  // the side stream, fork[rho] marks the end of round rho's item chain,
+  // fork[rounds + 1] the position norms (second arrangement), fork[rounds + 2]
+  // the end of the side stream.
   hipStream_t side = st;
   if (!single) {
     const rece_status ss = ensure_side(p, c.rounds + 3);
@@ -761,51 +773,98 @@ static rece_status forward_impl(const rece_plan_s& p, hipStream_t st, const void
     return a;
   };
 
-  {   // round 0's position chain, alongside the first item chain
-    int32_t* bx = reinterpret_cast<int32_t*>(sv + p.o_bx);
-    int32_t* px = reinterpret_cast<int32_t*>(sv + p.o_px);
-    RECE_PHASE(RECE_PHASE_PROJECT, launch_project_argmax(p.bf16, d, X, s, Bt, c.n_b, bnorm, p.beta_coef, bx,
-                                   xnorm, nullptr, und, und_n, counters, st),
-               "bucket positions");
-    RECE_HIP(record(c.rounds + 1, st), "position norms");
-    RECE_PHASE(RECE_PHASE_SORT, launch_counting_sort(bx, nullptr, s, 0, p.nbits_b, sc + p.o_sort, px, nullptr, st),
-               "sort positions");
-  }
-
-  for (int rho = 0; rho < c.rounds; ++rho) {
-    hipStream_t st = side;
-    int32_t* by = reinterpret_cast<int32_t*>(sv + p.o_by) + (int64_t)rho * C;
-    int32_t* py = reinterpret_cast<int32_t*>(sv + p.o_py) + (int64_t)rho * C;
-    const void* Btr = static_cast<const char*>(Bt) + (size_t)rho * c.n_b * d * p.esize;
-    RECE_PHASE(RECE_PHASE_PROJECT, launch_project_argmax(p.bf16, d, Y, C, Btr, c.n_b, bnorm + rho, p.beta_coef, by, nullptr,
-                                   rho == 0 ? reinterpret_cast<uint32_t*>(ymax) : nullptr, undy, und_n + 2 * rho + 1,
-                                   counters, st),
-             "bucket items");
-    RECE_PHASE(RECE_PHASE_SORT, launch_counting_sort(by, nullptr, C, 0, p.nbits_b, sc + p.o_sorty, py, nullptr, st),
-               "sort items");
-    if (rho == 0) {
-      RECE_HIP(record(0, side), "item chain done");
-      continue;
+  if (p.items_ahead) {
+    // position chains of every round (the caller's stream; round 0's bucketing also
+    // writes the position norms every chunk kernel reads)
+    for (int rho = 0; rho < c.rounds; ++rho) {
+      int32_t* bx = reinterpret_cast<int32_t*>(sv + p.o_bx) + (int64_t)rho * s;
+      int32_t* px = reinterpret_cast<int32_t*>(sv + p.o_px) + (int64_t)rho * s;
+      const void* Btr = static_cast<const char*>(Bt) + (size_t)rho * c.n_b * d * p.esize;
+      RECE_PHASE(RECE_PHASE_PROJECT, launch_project_argmax(p.bf16, d, X, s, Btr, c.n_b, bnorm + rho, p.beta_coef, bx,
+                                     rho == 0 ? xnorm : nullptr, nullptr, und, und_n + 2 * rho, counters, st),
+                 "bucket positions");
+      RECE_PHASE(RECE_PHASE_SORT, launch_counting_sort(bx, nullptr, s, 0, p.nbits_b, sc + p.o_sort, px, nullptr, st),
+                 "sort positions");
     }
-    int32_t* bx = reinterpret_cast<int32_t*>(sv + p.o_bx) + (int64_t)rho * s;
-    int32_t* px = reinterpret_cast<int32_t*>(sv + p.o_px) + (int64_t)rho * s;
-    RECE_PHASE(RECE_PHASE_PROJECT, launch_project_argmax(p.bf16, d, X, s, Btr, c.n_b, bnorm + rho, p.beta_coef,
-                                   bx, nullptr, nullptr, undy, und_n + 2 * rho, counters, st),
-               "bucket positions");
-    RECE_PHASE(RECE_PHASE_SORT, launch_counting_sort(bx, nullptr, s, 0, p.nbits_b, sc + p.o_sorty, px, nullptr, st),
-               "sort positions");
-    if (rho == 1) RECE_HIP(wait(side, c.rounds + 1), "position norms");
-    const SelectArgs a = select_args(rho);
-    RECE_PHASE(RECE_PHASE_SELECT, launch_select(p.bf16, d, p.waves_sel, a, st), "chunk logits and top-k");
-  }
-  RECE_HIP(record(c.rounds + 2, side), "side stream done");
+    // item chain of round rho on the side stream; round 0's also takes the largest
+    // item norm
+    auto item_chain = [&](int rho) -> rece_status {
+      hipStream_t st = side;
+      int32_t* by = reinterpret_cast<int32_t*>(sv + p.o_by) + (int64_t)rho * C;
+      int32_t* py = reinterpret_cast<int32_t*>(sv + p.o_py) + (int64_t)rho * C;
+      const void* Btr = static_cast<const char*>(Bt) + (size_t)rho * c.n_b * d * p.esize;
+      RECE_PHASE(RECE_PHASE_PROJECT, launch_project_argmax(p.bf16, d, Y, C, Btr, c.n_b, bnorm + rho, p.beta_coef, by, nullptr,
+                                     rho == 0 ? reinterpret_cast<uint32_t*>(ymax) : nullptr, undy, und_n + 2 * rho + 1,
+                                     counters, st),
+                 "bucket items");
+      RECE_PHASE(RECE_PHASE_SORT, launch_counting_sort(by, nullptr, C, 0, p.nbits_b, sc + p.o_sorty, py, nullptr, st),
+                 "sort items");
+      RECE_HIP(record(rho, side), "item chain done");
+      return RECE_OK;
+    };
+    {
+      const rece_status e0 = item_chain(0);
+      if (e0 != RECE_OK) return e0;
+    }
+    for (int rho = 0; rho < c.rounds; ++rho) {
+      // enqueued in this order, a single stream also runs every chain before its use
+      if (rho + 1 < c.rounds) {
+        const rece_status e1 = item_chain(rho + 1);
+        if (e1 != RECE_OK) return e1;
+      }
+      RECE_HIP(wait(st, rho), "join the item chain");
+      const SelectArgs a = select_args(rho);
+      RECE_PHASE(RECE_PHASE_SELECT, launch_select(p.bf16, d, p.waves_sel, a, st), "chunk logits and top-k");
+    }
+    RECE_HIP(record(c.rounds + 2, side), "side stream done");
+    RECE_HIP(wait(st, c.rounds + 2), "join the side stream");
+  } else {
+    {   // round 0's position chain, alongside the first item chain
+      int32_t* bx = reinterpret_cast<int32_t*>(sv + p.o_bx);
+      int32_t* px = reinterpret_cast<int32_t*>(sv + p.o_px);
+      RECE_PHASE(RECE_PHASE_PROJECT, launch_project_argmax(p.bf16, d, X, s, Bt, c.n_b, bnorm, p.beta_coef, bx,
+                                     xnorm, nullptr, und, und_n, counters, st),
+                 "bucket positions");
+      RECE_HIP(record(c.rounds + 1, st), "position norms");
+      RECE_PHASE(RECE_PHASE_SORT, launch_counting_sort(bx, nullptr, s, 0, p.nbits_b, sc + p.o_sort, px, nullptr, st),
+                 "sort positions");
+    }
 
-  RECE_HIP(wait(st, 0), "join the first item chain");
-  {
-    const SelectArgs a = select_args(0);
-    RECE_PHASE(RECE_PHASE_SELECT, launch_select(p.bf16, d, p.waves_sel, a, st), "chunk logits and top-k");
+    for (int rho = 0; rho < c.rounds; ++rho) {
+      hipStream_t st = side;
+      int32_t* by = reinterpret_cast<int32_t*>(sv + p.o_by) + (int64_t)rho * C;
+      int32_t* py = reinterpret_cast<int32_t*>(sv + p.o_py) + (int64_t)rho * C;
+      const void* Btr = static_cast<const char*>(Bt) + (size_t)rho * c.n_b * d * p.esize;
+      RECE_PHASE(RECE_PHASE_PROJECT, launch_project_argmax(p.bf16, d, Y, C, Btr, c.n_b, bnorm + rho, p.beta_coef, by, nullptr,
+                                     rho == 0 ? reinterpret_cast<uint32_t*>(ymax) : nullptr, undy, und_n + 2 * rho + 1,
+                                     counters, st),
+               "bucket items");
+      RECE_PHASE(RECE_PHASE_SORT, launch_counting_sort(by, nullptr, C, 0, p.nbits_b, sc + p.o_sorty, py, nullptr, st),
+                 "sort items");
+      if (rho == 0) {
+        RECE_HIP(record(0, side), "item chain done");
+        continue;
+      }
+      int32_t* bx = reinterpret_cast<int32_t*>(sv + p.o_bx) + (int64_t)rho * s;
+      int32_t* px = reinterpret_cast<int32_t*>(sv + p.o_px) + (int64_t)rho * s;
+      RECE_PHASE(RECE_PHASE_PROJECT, launch_project_argmax(p.bf16, d, X, s, Btr, c.n_b, bnorm + rho, p.beta_coef,
+                                     bx, nullptr, nullptr, undy, und_n + 2 * rho, counters, st),
+                 "bucket positions");
+      RECE_PHASE(RECE_PHASE_SORT, launch_counting_sort(bx, nullptr, s, 0, p.nbits_b, sc + p.o_sorty, px, nullptr, st),
+                 "sort positions");
+      if (rho == 1) RECE_HIP(wait(side, c.rounds + 1), "position norms");
+      const SelectArgs a = select_args(rho);
+      RECE_PHASE(RECE_PHASE_SELECT, launch_select(p.bf16, d, p.waves_sel, a, st), "chunk logits and top-k");
+    }
+    RECE_HIP(record(c.rounds + 2, side), "side stream done");
+
+    RECE_HIP(wait(st, 0), "join the first item chain");
+    {
+      const SelectArgs a = select_args(0);
+      RECE_PHASE(RECE_PHASE_SELECT, launch_select(p.bf16, d, p.waves_sel, a, st), "chunk logits and top-k");
+    }
+    RECE_HIP(wait(st, c.rounds + 2), "join the side stream");
   }
-  RECE_HIP(wait(st, c.rounds + 2), "join the side stream");
   for (int rho = 1; rho < c.rounds && c.k > 0; ++rho) {
     DedupArgs dd{};
     dd.negs = reinterpret_cast<int32_t*>(sv + p.o_negs);
