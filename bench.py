@@ -112,7 +112,7 @@ def algorithmic_work_sce(w):
     sx, sy = nb * w.b_x, nb * w.b_y
     return {
         "project": (2.0 * d * nb * (s + C), (s + C) * d * es),
-        "sort": (0.0, nb * (s + C) * 4 + (sx + sy) * (d * es + 8)),      # score columns, bucket rows
+        "sort": (0.0, (sx + sy) * 4),      # the bucket lists (the scores need not be stored)
         "select": (2.0 * d * sx * w.b_y, (sx + sy) * d * es + sx * w.k * 8),
         "loss": (2.0 * d * s, s * (2 * d * es + 24)),
         **backward_work(w, 1),

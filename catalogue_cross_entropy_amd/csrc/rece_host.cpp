@@ -117,9 +117,21 @@ struct rece_plan_s {
   // bucket variant: slots = (bucket, position) and (bucket, item) pairs
   int64_t sx, sy;     // n_b * b_x, n_b * b_y
   size_t o_R, o_Q, o_xmax;                                                                  // saved
-  size_t o_ssort, o_sinv, o_pstart, o_pend, o_pxt, o_pyt, o_ste, o_stid, o_stlo, o_sthi, o_smsh, o_sssum, o_snmem,
+  size_t o_ssort, o_sinv, o_pstart, o_pend, o_ste, o_stid, o_stlo, o_sthi, o_smsh, o_sssum, o_snmem,
       o_snegs, o_snegl, o_stmp;                                                             // scratch
+  // the b_x positions (csx) and b_y items (csy) of every bucket
+  struct ColSel {
+    int mode;           // COLSEL_ALL, COLSEL_LISTED or COLSEL_DENSE
+    int64_t N;
+    int m;
+    int64_t rows_pb, capl;
+    int n_rb, cg, n_g, nb_pad;
+    size_t o_cs, o_keys, o_act, o_hist, o_above, o_offs, o_lidx, o_lval, o_pt;   // scratch
+  } csx, csy;
 };
+// A bucket takes every row; the b largest through histogram passes and a list
+// (b <= COL_LIST_MAX_M); through the stored score matrix (larger b).
+enum { COLSEL_ALL = 0, COLSEL_LISTED = 1, COLSEL_DENSE = 2 };
 
 namespace {
 // Brackets the launches of one phase with events when profiling is on.
@@ -242,8 +254,34 @@ static void plan_sce_layout(rece_plan_s* p) {
   p->o_sinv = sc.take((size_t)sx * 4);
   p->o_pstart = sc.take((size_t)s * 4);
   p->o_pend = sc.take((size_t)s * 4);
-  p->o_pxt = sc.take((size_t)n_b * s * 4);
-  p->o_pyt = sc.take((size_t)n_b * C * 4);
+  auto colsel = [&](rece_plan_s::ColSel& q, int64_t N, int m) {
+    q = rece_plan_s::ColSel{};
+    q.N = N;
+    q.m = m;
+    q.nb_pad = (n_b + 15) / 16 * 16;
+    q.mode = (int64_t)m >= N ? COLSEL_ALL : (m <= COL_LIST_MAX_M ? COLSEL_LISTED : COLSEL_DENSE);
+    col_pass_shape(p->bf16, d, N, q.nb_pad, &q.rows_pb, &q.n_rb, &q.cg, &q.n_g);
+    // the list of a column: the m members, the rest of the boundary bin and the bin
+    // below it (the column's score range cut in 32 bins); a finer level is taken
+    // when that is more than the capacity
+    q.capl = std::min<int64_t>(N, 3 * (int64_t)m + 16384);
+    if (q.mode == COLSEL_DENSE) {
+      q.o_pt = sc.take((size_t)n_b * N * 4);
+    } else {
+      q.o_keys = sc.take((size_t)q.nb_pad * 8);
+    }
+    if (q.mode == COLSEL_LISTED) {
+      q.o_cs = sc.take((size_t)q.nb_pad * sizeof(ColState));
+      q.o_act = sc.take((COL_LEVELS + 1) * 4);
+      q.o_hist = sc.take((size_t)q.n_rb * q.nb_pad * COL_BINS * 4);
+      q.o_above = sc.take((size_t)q.nb_pad * q.n_rb * 4);
+      q.o_offs = sc.take((size_t)q.nb_pad * q.n_rb * 4);
+      q.o_lidx = sc.take((size_t)q.nb_pad * q.capl * 4);
+      q.o_lval = sc.take((size_t)q.nb_pad * q.capl * 4);
+    }
+  };
+  colsel(p->csx, s, c.b_x);
+  colsel(p->csy, C, c.b_y);
   p->o_ste = sc.take((size_t)sx * 8);
   p->o_stid = sc.take((size_t)sx * 4);
   p->o_stlo = sc.take((size_t)sx * 4);
@@ -281,6 +319,92 @@ static rece_status group_by_key(const rece_plan_s& p, const int32_t* keys, int64
   return RECE_OK;
 }
 
+// The m rows of largest projection score in every bucket column (SCE page, the
+// bucket procedure), with the rows' norms and their largest norm.
+static rece_status sce_col_select(const rece_plan_s& p, const rece_plan_s::ColSel& q, const void* V, const void* Bt,
+                                  const float* bnorm, float* norms, uint32_t* vmax, int32_t* out, uint32_t* counters,
+                                  char* sc, hipStream_t st) {
+  const rece_config& c = p.cfg;
+  const int d = c.d, n_b = c.n_b;
+  ColSelectArgs ca{};
+  ca.V = V;
+  ca.Bt = Bt;
+  ca.N = q.N;
+  ca.m = q.m;
+  ca.n_b = n_b;
+  ca.beta_coef = p.beta_coef;
+  ca.vmax_bits = vmax;
+  ca.bnorm_max = bnorm;
+  ca.out = out;
+  ca.counters = counters;
+  if (q.mode == COLSEL_DENSE) {
+    float* pt = reinterpret_cast<float*>(sc + q.o_pt);
+    RECE_PHASE(RECE_PHASE_PROJECT, launch_project_scores(p.bf16, d, V, q.N, Bt, n_b, pt, norms, vmax, st),
+               "projection scores");
+    ca.PT = pt;
+    RECE_PHASE(RECE_PHASE_SORT, launch_col_select(p.bf16, d, ca, st), "bucket columns");
+    return RECE_OK;
+  }
+  uint32_t* keys = reinterpret_cast<uint32_t*>(sc + q.o_keys);
+  ColPassArgs pa{};
+  pa.V = V;
+  pa.N = q.N;
+  pa.Bt = Bt;
+  pa.n_b = n_b;
+  pa.nb_pad = q.nb_pad;
+  pa.cg = q.cg;
+  pa.n_g = q.n_g;
+  pa.rows_pb = q.rows_pb;
+  pa.n_rb = q.n_rb;
+  pa.norms = norms;
+  pa.norm_max_bits = vmax;
+  pa.key_max = keys;
+  pa.key_min = keys + q.nb_pad;
+  RECE_PHASE(RECE_PHASE_OTHER, launch_fill_u32(keys, 0u, 2 * q.nb_pad, st), "clear column ranges");
+  RECE_PHASE(RECE_PHASE_PROJECT, launch_col_pass(p.bf16, d, CP_MINMAX, pa, st), "row norms and column ranges");
+  if (q.mode == COLSEL_LISTED) {
+    ColState* cs = reinterpret_cast<ColState*>(sc + q.o_cs);
+    uint32_t* act = reinterpret_cast<uint32_t*>(sc + q.o_act);
+    pa.cs = cs;
+    pa.hist = reinterpret_cast<uint32_t*>(sc + q.o_hist);
+    pa.offs = reinterpret_cast<int32_t*>(sc + q.o_offs);
+    pa.lidx = reinterpret_cast<int32_t*>(sc + q.o_lidx);
+    pa.lval = reinterpret_cast<float*>(sc + q.o_lval);
+    pa.capl = q.capl;
+    pa.active = act;
+    ColThreshArgs ta{};
+    ta.cs = cs;
+    ta.hist = pa.hist;
+    ta.above_r = reinterpret_cast<int32_t*>(sc + q.o_above);
+    ta.offs = reinterpret_cast<int32_t*>(sc + q.o_offs);
+    ta.active = act;
+    ta.n_b = n_b;
+    ta.nb_pad = q.nb_pad;
+    ta.n_rb = q.n_rb;
+    ta.m = q.m;
+    ta.N = q.N;
+    ta.capl = q.capl;
+    ta.beta_coef = p.beta_coef;
+    ta.vmax_bits = vmax;
+    ta.bnorm_max = bnorm;
+    ta.counters = counters;
+    RECE_PHASE(RECE_PHASE_OTHER, launch_col_init(cs, pa.key_max, pa.key_min, act, n_b, st), "column ranges");
+    for (int lvl = 1; lvl <= COL_LEVELS; ++lvl) {
+      pa.level = lvl;
+      ta.level = lvl;
+      RECE_PHASE(RECE_PHASE_PROJECT, launch_col_pass(p.bf16, d, CP_HIST, pa, st), "column histograms");
+      RECE_PHASE(RECE_PHASE_SORT, launch_col_thresh(ta, st), "column thresholds");
+    }
+    RECE_PHASE(RECE_PHASE_PROJECT, launch_col_pass(p.bf16, d, CP_LIST, pa, st), "column lists");
+    ca.lidx = pa.lidx;
+    ca.lval = pa.lval;
+    ca.cs = cs;
+    ca.capl = q.capl;
+  }
+  RECE_PHASE(RECE_PHASE_SORT, launch_col_select(p.bf16, d, ca, st), "bucket columns");
+  return RECE_OK;
+}
+
 // Forward pass of the bucket variant (SCE page, abstract; the bucket procedure
 // is described with the kernels).
 static rece_status sce_forward(const rece_plan_s& p, hipStream_t st, const void* X, const void* Y,
@@ -296,39 +420,20 @@ static rece_status sce_forward(const rece_plan_s& p, hipStream_t st, const void*
   void* Bt = sc + p.o_bt;
   int32_t* R = reinterpret_cast<int32_t*>(sv + p.o_R);
   int32_t* Q = reinterpret_cast<int32_t*>(sv + p.o_Q);
-  float* pxt = reinterpret_cast<float*>(sc + p.o_pxt);
-  float* pyt = reinterpret_cast<float*>(sc + p.o_pyt);
 
   RECE_PHASE(RECE_PHASE_OTHER, launch_fill_u32(counters, 0u, NUM_COUNTERS, st), "clear counters");
   RECE_PHASE(RECE_PHASE_OTHER, launch_fill_u32(xmax, 0u, 1, st), "clear norm max");
   RECE_PHASE(RECE_PHASE_OTHER, launch_fill_u32(ymax, 0u, 1, st), "clear norm max");
   RECE_PHASE(RECE_PHASE_OTHER, launch_prep_b(p.bf16, d, B, 1, n_b, Bt, bnorm, 0, st), "prepare projection vectors");
-  // projection scores of every position and item, one column per bucket
-  RECE_PHASE(RECE_PHASE_PROJECT, launch_project_scores(p.bf16, d, X, s, Bt, n_b, pxt, xnorm, xmax, st),
-             "position scores");
-  RECE_PHASE(RECE_PHASE_PROJECT, launch_project_scores(p.bf16, d, Y, C, Bt, n_b, pyt, nullptr, ymax, st),
-             "item scores");
-  // the b_x positions and b_y items of every bucket
-  ColSelectArgs ca{};
-  ca.Bt = Bt;
-  ca.n_b = n_b;
-  ca.beta_coef = p.beta_coef;
-  ca.bnorm_max = bnorm;
-  ca.counters = counters;
-  ca.PT = pxt;
-  ca.V = X;
-  ca.N = s;
-  ca.m = c.b_x;
-  ca.vmax_bits = xmax;
-  ca.out = R;
-  RECE_PHASE(RECE_PHASE_SORT, launch_col_select(p.bf16, d, ca, st), "bucket positions");
-  ca.PT = pyt;
-  ca.V = Y;
-  ca.N = C;
-  ca.m = c.b_y;
-  ca.vmax_bits = ymax;
-  ca.out = Q;
-  RECE_PHASE(RECE_PHASE_SORT, launch_col_select(p.bf16, d, ca, st), "bucket items");
+  // the b_x positions and b_y items of every bucket (row norms on the way)
+  {
+    const rece_status e = sce_col_select(p, p.csx, X, Bt, bnorm, xnorm, xmax, R, counters, sc, st);
+    if (e != RECE_OK) return e;
+  }
+  {
+    const rece_status e = sce_col_select(p, p.csy, Y, Bt, bnorm, nullptr, ymax, Q, counters, sc, st);
+    if (e != RECE_OK) return e;
+  }
 
   // per (bucket, position) slot, the top-k of the bucket's items (the chunk kernel,
   // one chunk per bucket, window = the chunk's own items)

@@ -18,6 +18,7 @@ enum Counter {
   CNT_OVERFLOW = 4,       // selection buffers that could not be compacted
   CNT_SEL_REDO = 5,       // rows whose candidate list went to the exact pass (ties by the hundred)
   CNT_LISTED = 6,         // candidate entries appended to the selection lists
+  CNT_COL_REFINE = 7,     // bucket columns whose selection took a finer histogram level
   NUM_COUNTERS = 8
 };
 enum ErrBit : uint32_t { ERRBIT_BAD_ID = 1u, ERRBIT_OVERFLOW = 2u };
@@ -186,8 +187,74 @@ size_t dy_area_bytes(int64_t E, int d);
 hipError_t launch_dy(bool is_bf16, int d, const BwdArgs& a, const int32_t* K, const int32_t* V, const uint32_t* ntot,
                      int64_t E, void* area, hipStream_t st);
 // Bucket (SCE) variant.
+// Per bucket column of a listed selection (k_col_pass / k_col_thresh): the
+// histogram coordinate of a float32 score v is x = med3(v * sc + nlsc, 0, 32 -)
+// (one fma) and, at the current level, y = x * mul + nxm (exactly (x - xa) * mul);
+// bins are floor(y) in [0, 32).
+struct ColState {
+  float lo, sc, nlsc;   // smallest score of the column, 32 / (largest - smallest), -lo * sc
+  float xa, mul, nxm;   // level origin (x units), scale, -xa * mul
+  float tlo;            // listing threshold of the last decided level (value space)
+  float vgate;          // smallest float32 score with y >= 0 at the current level
+  float vlist;          // smallest float32 score with y >= bl (listed entries: score >= vlist)
+  int level;            // level whose histogram is taken next; 0 once decided
+  int bl;               // listing bin (COL_NONE: none)
+  int nlist;            // entries listed, -1 when they exceed the list capacity
+  int above;            // entries above the current level's range (y >= 32)
+  int pad[3];
+};
+constexpr int COL_BINS = 32;      // bins of a histogram level
+constexpr int COL_LEVELS = 3;     // levels at most
+constexpr int COL_NONE = 1 << 30;
+constexpr int COL_LIST_MAX_M = 4096;   // listed selections take at most this many entries per bucket
+struct ColPassArgs {
+  const void* V;              // [N][d] rows
+  int64_t N;
+  const void* Bt;             // [n_b][d] projection vectors
+  int n_b, nb_pad;            // buckets, padded to 16
+  int cg, n_g;                // columns per workgroup group, groups
+  int64_t rows_pb;            // rows per row block (a multiple of 64)
+  int n_rb;                   // row blocks
+  int level;                  // histogram level of a CP_HIST pass
+  float* norms;               // [N] row norms (nullptr: not stored)
+  uint32_t* norm_max_bits;    // [1] largest row norm
+  uint32_t* key_max;          // [nb_pad] order keys of the column maxima
+  uint32_t* key_min;          // [nb_pad] complemented order keys of the column minima
+  const ColState* cs;         // [n_b]
+  uint32_t* hist;             // [n_rb][nb_pad][COL_BINS]
+  const int32_t* offs;        // [nb_pad][n_rb] first list slot of each row block
+  int32_t* lidx;              // [nb_pad][capl] listed rows
+  float* lval;                // [nb_pad][capl] their float32 scores
+  int64_t capl;
+  const uint32_t* active;     // [COL_LEVELS + 1]: a column waits for level l
+};
+struct ColThreshArgs {
+  ColState* cs;
+  const uint32_t* hist;
+  int32_t* above_r;           // [nb_pad][n_rb] entries above the level's range, per row block
+  int32_t* offs;              // [nb_pad][n_rb]
+  uint32_t* active;
+  int n_b, nb_pad, n_rb, level, m;
+  int64_t N, capl;
+  float beta_coef;
+  const uint32_t* vmax_bits;
+  const float* bnorm_max;
+  uint32_t* counters;
+};
+enum ColPassMode { CP_MINMAX = 0, CP_HIST = 1, CP_LIST = 2 };
+// Row blocks of a listed selection over n rows (rows per block, a multiple of 64,
+// and their count) and column groups (width, count).
+void col_pass_shape(bool is_bf16, int d, int64_t n, int nb_pad, int64_t* rows_pb, int* n_rb, int* cg, int* n_g);
+hipError_t launch_col_pass(bool is_bf16, int d, int mode, const ColPassArgs& a, hipStream_t st);
+hipError_t launch_col_init(ColState* cs, const uint32_t* key_max, const uint32_t* key_min, uint32_t* active, int n_b,
+                           hipStream_t st);
+hipError_t launch_col_thresh(const ColThreshArgs& a, hipStream_t st);
 struct ColSelectArgs {
-  const float* PT;            // [n_b][N] projection scores, one column per bucket
+  const float* PT;            // [n_b][N] projection scores, one column per bucket (dense selection)
+  const int32_t* lidx;        // listed selection: [n_b][capl] rows and
+  const float* lval;          //   their scores, nlist of ColState each
+  const ColState* cs;
+  int64_t capl;
   const void* V;              // [N][d] rows (float64 recomputation)
   const void* Bt;             // [n_b][d] projection vectors
   int64_t N;
@@ -201,6 +268,7 @@ struct ColSelectArgs {
 };
 hipError_t launch_project_scores(bool is_bf16, int d, const void* V, int64_t n, const void* Bt, int n_b, float* PT,
                                  float* norms, uint32_t* norm_max_bits, hipStream_t st);
+// Dense selection (PT set) or listed selection (lidx set; output in index order).
 hipError_t launch_col_select(bool is_bf16, int d, const ColSelectArgs& a, hipStream_t st);
 hipError_t launch_group_bounds(const int32_t* keys, const int32_t* sorted, int64_t n, int32_t* start, int32_t* end,
                                hipStream_t st);

@@ -241,7 +241,8 @@ typedef enum {
                                 [3] logits recomputed in float64, [4] buffer overflows,
                                 [5] rows whose top-k candidates went through the exact
                                 pass (hundreds of ties near the k-th logit), [6] candidate
-                                entries appended to the selection lists */
+                                entries appended to the selection lists, [7] SCE: bucket
+                                columns whose selection took a finer histogram level */
   RECE_STAGE_SCE_ROWS = 9,   /* SCE: int32 [n_b][b_x] positions taken by each bucket (a set per
                                 bucket, in the library's order) */
   RECE_STAGE_SCE_ITEMS = 10, /* SCE: int32 [n_b][b_y] items taken by each bucket (a set per bucket) */

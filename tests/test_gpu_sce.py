@@ -22,6 +22,10 @@ CASES = {
     "sce_lists_below_k": scaled("sce", seqs=2, seqlen=100, C=3000, d=64, n_b=10, b_x=60, b_y=30, k=40),
     "sce_k_one": scaled("sce", seqs=2, seqlen=64, C=2000, d=64, n_b=8, b_x=32, b_y=200, k=1),
     "sce_k_zero": scaled("sce", seqs=2, seqlen=64, C=2000, d=64, n_b=8, b_x=32, b_y=200, k=0),
+    # buckets taking most of their rows: the boundary lies low in every column's score range
+    "sce_most_rows": scaled("sce", seqs=2, seqlen=100, C=2000, d=64, n_b=5, b_x=150, b_y=1200, k=48),
+    # more than 4096 items per bucket: the stored-score selection instead of the listed one
+    "sce_wide_buckets": scaled("sce", seqs=2, seqlen=64, C=12000, d=64, n_b=3, b_x=32, b_y=5000, k=32),
     # one bucket taking everything with k = C - 1 is full cross-entropy
     "sce_full_ce": scaled("sce", seqs=2, seqlen=128, C=700, d=64, dtype="f32", n_b=1, b_x=256, b_y=700, k=699),
 }
@@ -113,3 +117,23 @@ def test_sce_per_position_upstream_and_repeatable():
     fwd = oracle.sce_forward(inp.X, inp.Y, inp.pos, inp.B[0], w.b_x, w.b_y, w.k)
     gX, gY = oracle.sce_backward(inp.X, inp.Y, inp.pos, fwd, dloss_pp=dpp.astype(np.float32))
     assert grad_err(a["dX"], gX) <= 2e-3 and grad_err(a["dY"], gY) <= 2e-3
+
+
+def test_sce_one_far_item_takes_a_finer_level():
+    """One item row 64 times longer than the others stretches every bucket column's
+    score range, so the first 32-bin histogram leaves nearly all 20,000 items in the
+    listing bins, more than a column's list holds: those columns take the next
+    histogram level (counter 7) and the selection must still equal the oracle's."""
+    import dataclasses
+    w = scaled("sce", seqs=2, seqlen=64, C=20000, d=64, n_b=4, b_x=32, b_y=256, k=32)
+    inp = make_inputs(w)
+    Y = inp.Y.copy()
+    Y[1234] *= 64.0   # a power of two: the row stays exactly representable in bfloat16
+    inp = dataclasses.replace(inp, Y=Y)
+    print("[gpu] sce: one item row x64, C=20000, b_y=256", flush=True)
+    g = run_sce(inp)
+    fwd = oracle.sce_forward(inp.X, inp.Y, inp.pos, inp.B[0], w.b_x, w.b_y, w.k)
+    _check("sce_far_item", inp, g, fwd)
+    assert g["counters"][7] >= 1, g["counters"]   # columns nearly orthogonal to the row need not
+    gX, gY = oracle.sce_backward(inp.X, inp.Y, inp.pos, fwd)
+    assert grad_err(g["dX"], gX) <= 2e-3 and grad_err(g["dY"], gY) <= 2e-3
