@@ -407,8 +407,10 @@ static rece_status sce_col_select(const rece_plan_s& p, const rece_plan_s::ColSe
 
 // Forward pass of the bucket variant (SCE page, abstract; the bucket procedure
 // is described with the kernels).
+static rece_status ensure_side(const rece_plan_s& p, int nfork);
 static rece_status sce_forward(const rece_plan_s& p, hipStream_t st, const void* X, const void* Y,
-                               const int32_t* pos, const void* B, char* sc, char* sv, float* loss, float* loss_pp) {
+                               const int32_t* pos, const void* B, char* sc, char* sv, float* loss, float* loss_pp,
+                               bool single) {
   const rece_config& c = p.cfg;
   const int64_t s = c.s, C = c.C;
   const int d = c.d, k = c.k, n_b = c.n_b;
@@ -425,14 +427,27 @@ static rece_status sce_forward(const rece_plan_s& p, hipStream_t st, const void*
   RECE_PHASE(RECE_PHASE_OTHER, launch_fill_u32(xmax, 0u, 1, st), "clear norm max");
   RECE_PHASE(RECE_PHASE_OTHER, launch_fill_u32(ymax, 0u, 1, st), "clear norm max");
   RECE_PHASE(RECE_PHASE_OTHER, launch_prep_b(p.bf16, d, B, 1, n_b, Bt, bnorm, 0, st), "prepare projection vectors");
-  // the b_x positions and b_y items of every bucket (row norms on the way)
+  // the b_x positions and b_y items of every bucket (row norms on the way): the
+  // positions on the side stream (unless single), alongside the items
   {
-    const rece_status e = sce_col_select(p, p.csx, X, Bt, bnorm, xnorm, xmax, R, counters, sc, st);
-    if (e != RECE_OK) return e;
-  }
-  {
-    const rece_status e = sce_col_select(p, p.csy, Y, Bt, bnorm, nullptr, ymax, Q, counters, sc, st);
-    if (e != RECE_OK) return e;
+    std::unique_lock<std::mutex> side_lock(p.side.mu, std::defer_lock);
+    hipStream_t side = st;
+    if (!single) {
+      side_lock.lock();
+      const rece_status ss = ensure_side(p, 2);
+      if (ss != RECE_OK) return ss;
+      side = p.side.s;
+      RECE_HIP(hipEventRecord(p.side.fork[0], st), "fork");
+      RECE_HIP(hipStreamWaitEvent(side, p.side.fork[0], 0), "fork");
+    }
+    const rece_status ex = sce_col_select(p, p.csx, X, Bt, bnorm, xnorm, xmax, R, counters, sc, side);
+    if (ex != RECE_OK) return ex;
+    const rece_status ey = sce_col_select(p, p.csy, Y, Bt, bnorm, nullptr, ymax, Q, counters, sc, st);
+    if (ey != RECE_OK) return ey;
+    if (!single) {
+      RECE_HIP(hipEventRecord(p.side.fork[1], side), "join");
+      RECE_HIP(hipStreamWaitEvent(st, p.side.fork[1], 0), "join");
+    }
   }
 
   // per (bucket, position) slot, the top-k of the bucket's items (the chunk kernel,
@@ -800,7 +815,7 @@ static rece_status forward_impl(const rece_plan_s& p, hipStream_t st, const void
   float* bnorm = reinterpret_cast<float*>(sc + p.o_bnorm);
   void* Bt = sc + p.o_bt;
 
-  if (c.variant == RECE_VARIANT_SCE) return sce_forward(p, st, X, Y, pos, B, sc, sv, loss, loss_pp);
+  if (c.variant == RECE_VARIANT_SCE) return sce_forward(p, st, X, Y, pos, B, sc, sv, loss, loss_pp, single);
   std::unique_lock<std::mutex> side_lock(p.side.mu, std::defer_lock);
   if (!single) side_lock.lock();
   uint32_t* und_n = reinterpret_cast<uint32_t*>(bnorm + c.rounds);   // cleared with the norms
