@@ -594,50 +594,19 @@ __global__ __launch_bounds__(64 * NW, 2) void k_sel_stream(SelectArgs p) {
   }
 }
 
-// What a row's finish reads first (its list length and flags, the first 256 list
-// entries, the position and its norm), loaded one row ahead so that the loads of
-// the next row are in flight while this one is finished.
-constexpr int FIN_LB = 4;   // list entries per lane loaded ahead: FIN_LB * 64
-struct FinishAhead {
-  uint32_t nf;
-  int2 e[FIN_LB];
-  int64_t i;
-  float xn;
-};
-
-__device__ __forceinline__ void finish_load_ahead(const SelectArgs& p, int64_t row, FinishAhead& f) {
-  if (row >= p.s) return;
-  const int l = lane_id();
-  f.nf = p.k > 0 ? (uint32_t)p.clist_n[row] : 0u;
-  const int2* list = p.clist + row * (int64_t)p.cap;
-#pragma unroll
-  for (int q = 0; q < FIN_LB; ++q) {
-    const int t = q * WAVE + l;
-    f.e[q] = (p.k > 0 && t < p.cap) ? list[t] : int2{0, 0};
-  }
-  f.i = p.slot_out ? (int64_t)p.perm_x[row] : row;
-  f.xn = p.xnorm[f.i];
-}
-
 template <class E, int D>
-__device__ __forceinline__ void sel_finish_row(const SelectArgs& p, char* smem, int w, int64_t row, int64_t next_row,
-                                               FinishAhead& ahead, uint32_t& nexact, uint32_t& nnear) {
+__device__ __forceinline__ void sel_finish_row(const SelectArgs& p, char* smem, int w, int64_t row, uint32_t& nexact,
+                                               uint32_t& nnear) {
   const int l = lane_id();
   const int k = p.k, cap = p.cap;
-  // this row's first reads (loaded ahead), then the next row's
-  const int64_t i = ahead.i;   // position id
-  const float xn = ahead.xn;
-  const uint32_t nf = ahead.nf;
-  int2 head[FIN_LB];
-#pragma unroll
-  for (int q = 0; q < FIN_LB; ++q) head[q] = ahead.e[q];
-  finish_load_ahead(p, next_row, ahead);
+  const int64_t i = p.slot_out ? (int64_t)p.perm_x[row] : row;   // position id
   const E* X = reinterpret_cast<const E*>(p.X);
   const E* Y = reinterpret_cast<const E*>(p.Y);
   const E* xrow = X + i * D;
-  const float beta = p.beta_coef * xn * p.ynorm_max[0];
+  const float beta = p.beta_coef * p.xnorm[i] * p.ynorm_max[0];
   const int64_t o = p.slot_out ? row : (int64_t)p.rho * p.s + row;   // output row
 
+  const uint32_t nf = k > 0 ? (uint32_t)p.clist_n[row] : 0u;
   const int n = (int)(nf & ~(LIST_COMPACTED | LIST_REDO));
   const bool compacted = (nf & LIST_COMPACTED) != 0u;
   const int2* list = p.clist + row * (int64_t)cap;
@@ -668,13 +637,13 @@ __device__ __forceinline__ void sel_finish_row(const SelectArgs& p, char* smem, 
     // beat each of them (at least k entries remain)
     const float flo = p.clist_lo[row];
     int nk = 0;
-    constexpr int LB = FIN_LB;
+    constexpr int LB = 4;
     for (int base = 0; base < n; base += LB * WAVE) {
       int2 e[LB];
 #pragma unroll
       for (int q = 0; q < LB; ++q) {
         const int t = base + q * WAVE + l;
-        e[q] = base == 0 ? head[q] : (t < n ? list[t] : int2{0, 0});
+        e[q] = t < n ? list[t] : int2{0, 0};
       }
 #pragma unroll
       for (int q = 0; q < LB; ++q) {
@@ -735,11 +704,8 @@ __global__ __launch_bounds__(256, 4) void k_sel_finish(SelectArgs p) {
   const int64_t waves = (int64_t)gridDim.x * nw;
   // counts flushed once per wave (one address shared by every wave)
   uint32_t nexact = 0, nnear = 0;
-  FinishAhead ahead;
-  const int64_t row0 = (int64_t)blockIdx.x * nw + w;
-  finish_load_ahead(p, row0, ahead);
-  for (int64_t row = row0; row < p.s; row += waves)
-    sel_finish_row<E, D>(p, smem, w, row, row + waves, ahead, nexact, nnear);
+  for (int64_t row = (int64_t)blockIdx.x * nw + w; row < p.s; row += waves)
+    sel_finish_row<E, D>(p, smem, w, row, nexact, nnear);
   flush_count(p.counters + CNT_LOGIT_EXACT, nexact);
   flush_count(p.counters + CNT_TOPK_EXACT, nnear);
 }
