@@ -157,30 +157,12 @@ __global__ __launch_bounds__(256, (D * sizeof(E) == 256) ? 3 : 1) void k_project
   if (nt > 1) dma_rows<E, D, NW>(ring + G::ROW_BYTES, Bt, G::TI, n_b, w);
 
   Frag<E, D> a[RF];
-  float my_norm[RF];
 #pragma unroll
   for (int f = 0; f < RF; ++f) {
     const int64_t rA = ((int64_t)blockIdx.x * NW + w) * 16 * RF + 16 * f + (l & 15);
     const E* rp = rA < n ? V + rA * D : nullptr;
     a[f].load_global(rp);
     a[f].settle();
-    // squared norm of row (l & 15) from the fragment: each lane sums its part, then the 4 lanes of the row
-    float ss = 0.0f;
-#pragma unroll
-    for (int ks = 0; ks < Frag<E, D>::KS; ++ks) {
-      if constexpr (sizeof(E) == 2) {
-        // pairs of squares per instruction (exact products, float32 sums)
-        const u32x4 w4 = __builtin_bit_cast(u32x4, a[f].v[ks]);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) ss = bf16_pair_sq_acc(w4[t], ss);
-      } else {
-        ss = fmaf(a[f].v[ks], a[f].v[ks], ss);
-      }
-    }
-    ss += __shfl_xor(ss, 16);
-    ss += __shfl_xor(ss, 32);
-    // float32 sum of squares has relative error below d * 2^-24 < 2^-12 for d <= 512.
-    my_norm[f] = sqrtf(ss) * (1.0f + 0.0005f);
   }
 
   // Running top-2 per output element as integer keys: the score's float32 bits with
@@ -214,39 +196,28 @@ __global__ __launch_bounds__(256, (D * sizeof(E) == 256) ? 3 : 1) void k_project
     constexpr int NQ = G::ROW_DMA / NW;
     static_assert(G::ROW_DMA % NW == 0, "whole copies per wave");
     constexpr int LRB = ilog2(G::RB);
-    const char* gq[NQ];
+    uint32_t goff[NQ];   // byte offset of this lane's 16 bytes of copy qq inside a tile
 #pragma unroll
     for (int qq = 0; qq < NQ; ++qq) {
       const int byte = (w + qq * NW) * 1024 + 16 * l;
-      gq[qq] = reinterpret_cast<const char*>(Bt) + (byte ^ (((byte >> LRB) & G::SWM) << 4));
+      goff[qq] = (uint32_t)(byte ^ (((byte >> LRB) & G::SWM) << 4));
     }
     const int nfull_t = n_b / G::TI;   // tiles with no row past n_b
-    auto tile = [&](auto pad_c, int t) {
+    // One tile: wait for its copies, meet the other waves, issue the copies of tile
+    // t + 2, then score its NCB blocks of 16 vectors.  SLOT >= 0: the ring slot is
+    // known at compile time, so every fragment read is an immediate offset from
+    // this lane's slot-0 address, and the copies of a full tile t + 2 go out as a
+    // uniform tile address plus this lane's 32-bit offset.  SLOT < 0: the general
+    // form (runtime slot, clamped copies near the end of the vectors).
+    auto score = [&](auto pad_c, auto off_c, const uint32_t* fa, int t) {
       constexpr bool PAD = decltype(pad_c)::value;
-      if (t + 1 < nt)
-        wait_vmcnt_c<G::ROW_DMA / NW>();   // the fewest copies any wave issues per tile
-      else
-        wait_vmcnt_c<0>();
-      raw_barrier();   // every wave's copies of tile t landed; slot (t+2) % 3 is free
-      const int slot = t % 3;
-      if (t + 2 < nfull_t) {
-        char* dst = ring + (size_t)((t + 2) % 3) * G::ROW_BYTES;
-        const int64_t adv = (int64_t)(t + 2) * G::ROW_BYTES;
-#pragma unroll
-        for (int qq = 0; qq < NQ; ++qq)
-          dma_copy16(gq[qq] + adv, dst + (w + qq * NW) * 1024);
-      } else if (t + 2 < nt) {
-        dma_rows<E, D, NW>(ring + (size_t)((t + 2) % 3) * G::ROW_BYTES, Bt, (int64_t)(t + 2) * G::TI, n_b, w);
-      }
-      uint32_t fa[KS];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) fa[ks] = fa0[ks] + (uint32_t)(slot * G::ROW_BYTES);
+      constexpr int OFF = decltype(off_c)::value;
       const int vb = t * G::TI + n0;
       static_for<NCB>([&](auto cb_c) {
         constexpr int cb = decltype(cb_c)::value;
         Frag<E, D> bf;
         u32x4 raw[KS];
-        LdsReadOff128<KS, cb * 16 * G::RB>::run(fa, raw);
+        LdsReadOff128<KS, OFF + cb * 16 * G::RB>::run(fa, raw);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) bf.v[ks] = __builtin_bit_cast(bf16x8, raw[ks]);
         const int bcol = vb + cb * 16;
@@ -267,8 +238,46 @@ __global__ __launch_bounds__(256, (D * sizeof(E) == 256) ? 3 : 1) void k_project
         }
       });
     };
+    auto tile_fixed = [&](auto slot_c, int t) {   // t % 3 == SLOT and t + 2 < nfull_t
+      constexpr int SLOT = decltype(slot_c)::value;
+      wait_vmcnt_c<G::ROW_DMA / NW>();   // only tile t + 1's copies may remain
+      raw_barrier();
+      const char* src = reinterpret_cast<const char*>(Bt) + (int64_t)(t + 2) * G::ROW_BYTES;
+      char* dst = ring + ((SLOT + 2) % 3) * G::ROW_BYTES;
+#pragma unroll
+      for (int qq = 0; qq < NQ; ++qq) dma_copy16(src + goff[qq], dst + (w + qq * NW) * 1024);
+      score(std::false_type{}, std::integral_constant<int, SLOT * G::ROW_BYTES>{}, fa0, t);
+    };
+    auto tile = [&](auto pad_c, int t) {
+      if (t + 1 < nt)
+        wait_vmcnt_c<G::ROW_DMA / NW>();   // the fewest copies any wave issues per tile
+      else
+        wait_vmcnt_c<0>();
+      raw_barrier();   // every wave's copies of tile t landed; slot (t+2) % 3 is free
+      const int slot = t % 3;
+      if (t + 2 < nfull_t) {
+        char* dst = ring + (size_t)((t + 2) % 3) * G::ROW_BYTES;
+        const char* src = reinterpret_cast<const char*>(Bt) + (int64_t)(t + 2) * G::ROW_BYTES;
+#pragma unroll
+        for (int qq = 0; qq < NQ; ++qq) dma_copy16(src + goff[qq], dst + (w + qq * NW) * 1024);
+      } else if (t + 2 < nt) {
+        dma_rows<E, D, NW>(ring + (size_t)((t + 2) % 3) * G::ROW_BYTES, Bt, (int64_t)(t + 2) * G::TI, n_b, w);
+      }
+      uint32_t fa[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) fa[ks] = fa0[ks] + (uint32_t)(slot * G::ROW_BYTES);
+      score(pad_c, std::integral_constant<int, 0>{}, fa, t);
+    };
+    // tiles [0, tmain) in groups of three ring slots, the rest in the general form
+    const int tmain = nfull_t >= 2 ? (nfull_t - 2) / 3 * 3 : 0;
+    int t0 = 0;
+    for (; t0 < tmain; t0 += 3) {
+      tile_fixed(std::integral_constant<int, 0>{}, t0);
+      tile_fixed(std::integral_constant<int, 1>{}, t0 + 1);
+      tile_fixed(std::integral_constant<int, 2>{}, t0 + 2);
+    }
     const int nfull = n_b % G::TI != 0 ? nt - 1 : nt;   // tiles without padding
-    for (int t = 0; t < nfull; ++t) tile(std::false_type{}, t);
+    for (int t = t0; t < nfull; ++t) tile(std::false_type{}, t);
     if (nfull < nt) tile(std::true_type{}, nfull);
   } else {
   for (int t = 0; t < nt; ++t) {
@@ -304,6 +313,28 @@ __global__ __launch_bounds__(256, (D * sizeof(E) == 256) ? 3 : 1) void k_project
       }
     }
   
+  }
+  // Row norms from the fragments, after the scan (no registers held across it):
+  // each lane sums the squares of its part of row (l & 15), then the row's 4 lanes add.
+  float my_norm[RF];
+#pragma unroll
+  for (int f = 0; f < RF; ++f) {
+    float ss = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < Frag<E, D>::KS; ++ks) {
+      if constexpr (sizeof(E) == 2) {
+        // pairs of squares per instruction (exact products, float32 sums)
+        const u32x4 w4 = __builtin_bit_cast(u32x4, a[f].v[ks]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) ss = bf16_pair_sq_acc(w4[t], ss);
+      } else {
+        ss = fmaf(a[f].v[ks], a[f].v[ks], ss);
+      }
+    }
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    // float32 sum of squares has relative error below d * 2^-24 < 2^-12 for d <= 512.
+    my_norm[f] = sqrtf(ss) * (1.0f + 0.0005f);
   }
   const float bmax = bnorm_max[0];
 #pragma unroll
