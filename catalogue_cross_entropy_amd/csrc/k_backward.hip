@@ -213,7 +213,20 @@ struct PairSrc {
   const uint32_t* nin;   // later passes: number of records in kin / vin
   int64_t nl, s, C;
   int k;
+  double rk, rs;         // 1 / k, 1 / s (first pass)
 };
+
+// floor(n / d) for 0 <= n < 2^32 and d >= 1, given rd = 1 / d rounded to double:
+// the double product is within 2^-20 of n / d, so its truncation is off by at most
+// one either way, which one exact check corrects.  No branch and no integer
+// division (a software division per record would make the compiler branch around
+// it, and wait for each record's loads at the join).
+__device__ __forceinline__ uint32_t udiv_rd(uint32_t n, uint32_t d, double rd) {
+  int64_t q = (int64_t)((double)n * rd);
+  const int64_t r = (int64_t)n - q * (int64_t)d;
+  q += (r >= (int64_t)d ? 1 : 0) - (r < 0 ? 1 : 0);
+  return (uint32_t)q;
+}
 
 // Record t of the pass's input (t < n), loaded without branches so that the loads
 // of many records can be in flight at once: addresses are clamped into range and
@@ -228,7 +241,10 @@ __device__ __forceinline__ bool pair_at(const PairSrc& a, int64_t t, int64_t n, 
     const int kn = a.negs[il];
     const int kp = a.pos[ip];
     key = isl ? kn : kp;
-    val = isl ? (int)(((uint32_t)tc / (uint32_t)a.k) % (uint32_t)a.s) : ((int)ip | (int)0x80000000u);
+    // list entry t belongs to position (t / k) mod s (lists are [round][position][k])
+    const uint32_t q = udiv_rd((uint32_t)il, (uint32_t)a.k, a.rk);
+    const uint32_t i = q - (uint32_t)a.s * udiv_rd(q, (uint32_t)a.s, a.rs);
+    val = isl ? (int)i : ((int)ip | (int)0x80000000u);
     return (int)(t < n) & (int)(key >= 0) & (int)(key < a.C);   // no short-circuit: no branch between loads
   } else {
     key = a.kin[tc];
@@ -316,7 +332,8 @@ __global__ __launch_bounds__(RS_THREADS) void k_pair_scatter(PairSrc a, int64_t 
 #pragma unroll
   for (int it = 0; it < RS_GROUPS_PER_WAVE; ++it) {
     const int64_t t = t0 + (int64_t)(w * RS_GROUPS_PER_WAVE + it) * WAVE + l;
-    rok[it] = n > 0 && pair_at<FIRST>(a, t, n > 0 ? n : 1, rkey[it], rval[it]);
+    const bool okr = pair_at<FIRST>(a, t, n > 0 ? n : 1, rkey[it], rval[it]);
+    rok[it] = (n > 0) & okr;   // no short-circuit: no branch between the records' loads
   }
   __syncthreads();   // counters cleared
   uint32_t* ctr = wcnt[w];
@@ -618,6 +635,8 @@ hipError_t launch_pair_sort(const PairSortGeom& g, const int32_t* negs, int64_t 
   a.s = s;
   a.C = C;
   a.k = k > 0 ? k : 1;
+  a.rk = 1.0 / (double)a.k;
+  a.rs = 1.0 / (double)(s > 0 ? s : 1);
   int32_t* kbuf[2] = {kA, kB};
   int32_t* vbuf[2] = {vA, vB};
   for (int pss = 0; pss < g.npass; ++pss) {
