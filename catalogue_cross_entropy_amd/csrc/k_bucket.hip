@@ -99,6 +99,13 @@ hipError_t launch_prep_b(bool is_bf16, int d, const void* B, int rounds, int n_b
 
 // Median of three integers (one v_med3_i32).
 __device__ __forceinline__ int med3_i(int a, int b, int c) { return max(min(a, b), min(max(a, b), c)); }
+// Maximum of three integers as one v_max3_i32 (the compiler splits max(max(a, b), c)
+// into two instructions when it shares max(b, c) with a neighbouring med3).
+__device__ __forceinline__ int max3_i(int a, int b, int c) {
+  int r;
+  asm("v_max3_i32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 
 // Wave-collective float64 argmax of x . b over the n_b vectors (lowest index
 // among ties): every lane scores n_b / 64 of them in coordinate order.
@@ -172,14 +179,24 @@ __global__ __launch_bounds__(256, (D * sizeof(E) == 256) ? 3 : 1) void k_project
   // Per score: one and-or, one max, one med3.
   const int ib = n_b > 1 ? 32 - __builtin_clz((unsigned)(n_b - 1)) : 0;
   const int imask = (1 << ib) - 1;
+  // bf16: the products are taken vectors x rows, so a lane's four scores of a block
+  // belong to one row (l & 15) and four vectors (4g + v); the running top-2 is one
+  // pair of keys per fragment (t1, t2), updated two keys at a time:
+  //   top-2 of {t1 >= t2, kA, kB} = (max3(t1, kA, kB), max(t2, med3(t1, kA, kB))).
+  // float32: vectors as columns (one vector, four rows per lane) and a pair of keys
+  // per output element (best1, best2).
+  int t1[RF], t2[RF];
   int best1[RF][4], best2[RF][4];
 #pragma unroll
-  for (int f = 0; f < RF; ++f)
+  for (int f = 0; f < RF; ++f) {
+    t1[f] = INT32_MIN;
+    t2[f] = INT32_MIN;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       best1[f][v] = INT32_MIN;
       best2[f][v] = INT32_MIN;
     }
+  }
 
   if constexpr (sizeof(E) == 2) {
     // bf16: every fragment read is this lane's address for its k-step in the tile's
@@ -212,7 +229,7 @@ __global__ __launch_bounds__(256, (D * sizeof(E) == 256) ? 3 : 1) void k_project
     auto score = [&](auto pad_c, auto off_c, const uint32_t* fa, int t) {
       constexpr bool PAD = decltype(pad_c)::value;
       constexpr int OFF = decltype(off_c)::value;
-      const int vb = t * G::TI + n0;
+      const int tb = t * G::TI + 4 * g;   // vector of element v of the tile's first block: tb + v
       static_for<NCB>([&](auto cb_c) {
         constexpr int cb = decltype(cb_c)::value;
         Frag<E, D> bf;
@@ -220,20 +237,23 @@ __global__ __launch_bounds__(256, (D * sizeof(E) == 256) ? 3 : 1) void k_project
         LdsReadOff128<KS, OFF + cb * 16 * G::RB>::run(fa, raw);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) bf.v[ks] = __builtin_bit_cast(bf16x8, raw[ks]);
-        const int bcol = vb + cb * 16;
+        const int i0 = tb + cb * 16;
         f32x4 c0{0.0f, 0.0f, 0.0f, 0.0f};
         if constexpr (PAD) {
-          const float pad = bcol < n_b ? 0.0f : NEG_INF;
-          c0 = f32x4{pad, pad, pad, pad};
+#pragma unroll
+          for (int v = 0; v < 4; ++v) c0[v] = i0 + v < n_b ? 0.0f : NEG_INF;
         }
 #pragma unroll
         for (int f = 0; f < RF; ++f) {
-          const f32x4 acc = mma_block(a[f], bf, c0);
+          const f32x4 acc = mma_block(bf, a[f], c0);   // [vector 4g + v][row l & 15]
+          int key[4];
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int key = (__float_as_int(acc[v]) & ~imask) | bcol;
-            best2[f][v] = med3_i(best1[f][v], best2[f][v], key);
-            best1[f][v] = max(best1[f][v], key);
+          for (int v = 0; v < 4; ++v) key[v] = (__float_as_int(acc[v]) & ~imask) | (i0 + v);
+#pragma unroll
+          for (int h = 0; h < 4; h += 2) {
+            const int m = med3_i(t1[f], key[h], key[h + 1]);
+            t1[f] = max3_i(t1[f], key[h], key[h + 1]);
+            t2[f] = max(t2[f], m);
           }
         }
       });
@@ -337,38 +357,62 @@ __global__ __launch_bounds__(256, (D * sizeof(E) == 256) ? 3 : 1) void k_project
     my_norm[f] = sqrtf(ss) * (1.0f + 0.0005f);
   }
   const float bmax = bnorm_max[0];
+  // Decision of one row from its top-2 keys: the winner's float32 score is at least
+  // s1; every other one is below s2 plus the truncation (at most s2 * 2^(ib - 23)),
+  // or negative when the second key is; |float32 score - float64 score| <= beta
+  // (matrix-core accumulation bound + float64 rounding).
+  auto decided_row = [&](int k1, int k2, float nrm) {
+    const double beta = (double)beta_coef * (double)nrm * (double)bmax;
+    const double s1 = (double)__int_as_float(k1 & ~imask), s2 = (double)__int_as_float(k2 & ~imask);
+    const double other = k2 < 0 ? 0.0 : s2 + s2 * ldexp(1.0, ib - 22);
+    return k1 >= 0 && s1 - other > 2.0 * beta;
+  };
 #pragma unroll
   for (int f = 0; f < RF; ++f) {
     const int64_t row0 = ((int64_t)blockIdx.x * NW + w) * 16 * RF + 16 * f;
-    // Merge the top-2 keys of the 16 lanes that hold each row.
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        const int ob1 = __shfl_xor(best1[f][v], o);
-        const int ob2 = __shfl_xor(best2[f][v], o);
-        best2[f][v] = max(min(best1[f][v], ob1), max(best2[f][v], ob2));
-        best1[f][v] = max(best1[f][v], ob1);
-      }
-    }
+    // need_all: the fragment's undecided rows, bit b standing for row row0 + rowof(b)
     uint64_t need_all = 0;
+    int shift_g = 0;   // rowof(b) = 4 (b >> 4) + (b & 15) (float32), b (bf16)
+    if constexpr (sizeof(E) == 2) {
+      // Merge the top-2 keys of the four lanes (l & 15) + 16 g that hold the row.
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int r = 4 * g + v;                       // row of this output element within the fragment
-      const float nrm = __shfl(my_norm[f], r);       // lane r holds row r's norm
-      const int64_t row = row0 + r;
-      // |float32 score - float64 score| <= beta (matrix-core accumulation bound + float64 rounding)
-      const double beta = (double)beta_coef * (double)nrm * (double)bmax;
-      // the winner's float32 score is at least s1; every other one is below s2 plus
-      // the truncation (at most s2 * 2^(ib - 23)), or negative when the second key is
-      const int k1 = best1[f][v], k2 = best2[f][v];
-      const double s1 = (double)__int_as_float(k1 & ~imask), s2 = (double)__int_as_float(k2 & ~imask);
-      const double other = k2 < 0 ? 0.0 : s2 + s2 * ldexp(1.0, ib - 22);
-      const bool decided = k1 >= 0 && s1 - other > 2.0 * beta;
-      if (decided && (l & 15) == 0 && row < n) ids[row] = k1 & imask;
-      const uint64_t und = ballot(!decided && row < n);
-      need_all |= (und & 0x0001000100010001ull) << v;    // bit 16*g + v
+      for (int o = 16; o < 64; o <<= 1) {
+        const int o1 = __shfl_xor(t1[f], o);
+        const int o2 = __shfl_xor(t2[f], o);
+        t2[f] = max(min(t1[f], o1), max(t2[f], o2));
+        t1[f] = max(t1[f], o1);
+      }
+      const int64_t row = row0 + (l & 15);
+      const bool decided = decided_row(t1[f], t2[f], my_norm[f]);
+      if (decided && g == 0 && row < n) ids[row] = t1[f] & imask;
+      need_all = ballot(!decided && row < n) & 0xFFFFull;   // bit r: row row0 + r
+    } else {
+      // Merge the top-2 keys of the 16 lanes that hold each row.
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+          const int ob1 = __shfl_xor(best1[f][v], o);
+          const int ob2 = __shfl_xor(best2[f][v], o);
+          best2[f][v] = max(min(best1[f][v], ob1), max(best2[f][v], ob2));
+          best1[f][v] = max(best1[f][v], ob1);
+        }
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = 4 * g + v;                       // row of this output element within the fragment
+        const float nrm = __shfl(my_norm[f], r);       // lane r holds row r's norm
+        const int64_t row = row0 + r;
+        const bool decided = decided_row(best1[f][v], best2[f][v], nrm);
+        if (decided && (l & 15) == 0 && row < n) ids[row] = best1[f][v] & imask;
+        const uint64_t und = ballot(!decided && row < n);
+        need_all |= (und & 0x0001000100010001ull) << v;    // bit 16*g + v
+      }
+      shift_g = 1;
     }
+    auto row_of = [&](int bit) -> int64_t {
+      return row0 + (shift_g ? 4 * (bit >> 4) + (bit & 15) : bit);
+    };
     // undecided rows: decided here by the whole wave (small inputs), or listed for
     // the float64 kernel (one atomic per wave)
     if (need_all && !und) {
@@ -376,7 +420,7 @@ __global__ __launch_bounds__(256, (D * sizeof(E) == 256) ? 3 : 1) void k_project
       while (need_all) {
         const int bit = __builtin_ctzll(need_all);
         need_all &= need_all - 1;
-        const int64_t row = row0 + 4 * (bit >> 4) + (bit & 15);
+        const int64_t row = row_of(bit);
         int bi = argmax_exact_wave<E, D>(V + row * D, Bt, n_b);
         if (bi >= n_b) bi = 0;   // only reachable with NaN scores
         if (l == 0) ids[row] = bi;
@@ -391,7 +435,7 @@ __global__ __launch_bounds__(256, (D * sizeof(E) == 256) ? 3 : 1) void k_project
       for (int e = 0; need_all; ++e) {
         const int bit = __builtin_ctzll(need_all);
         need_all &= need_all - 1;
-        if (l == 0) und[base + e] = (int32_t)(row0 + 4 * (bit >> 4) + (bit & 15));
+        if (l == 0) und[base + e] = (int32_t)row_of(bit);
       }
     }
     const int64_t rA = row0 + (l & 15);
