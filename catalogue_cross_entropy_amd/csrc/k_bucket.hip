@@ -243,12 +243,21 @@ __global__ __launch_bounds__(256, (D * sizeof(E) == 256) ? 3 : 1) void k_project
 #pragma unroll
           for (int v = 0; v < 4; ++v) c0[v] = i0 + v < n_b ? 0.0f : NEG_INF;
         }
+        // the RF product chains k-step outer (independent chains back to back), then
+        // the updates
+        f32x4 acc[RF];
+#pragma unroll
+        for (int f = 0; f < RF; ++f) acc[f] = c0;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+          for (int f = 0; f < RF; ++f)
+            acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf.v[ks], a[f].v[ks], acc[f], 0, 0, 0);
 #pragma unroll
         for (int f = 0; f < RF; ++f) {
-          const f32x4 acc = mma_block(bf, a[f], c0);   // [vector 4g + v][row l & 15]
-          int key[4];
+          int key[4];   // acc[f][v]: vector 4g + v, row l & 15
 #pragma unroll
-          for (int v = 0; v < 4; ++v) key[v] = (__float_as_int(acc[v]) & ~imask) | (i0 + v);
+          for (int v = 0; v < 4; ++v) key[v] = (__float_as_int(acc[f][v]) & ~imask) | (i0 + v);
 #pragma unroll
           for (int h = 0; h < 4; h += 2) {
             const int m = med3_i(t1[f], key[h], key[h + 1]);
