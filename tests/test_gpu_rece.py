@@ -43,6 +43,9 @@ CASES = {
     "clipped_wide": scaled("tiny", seqs=2, seqlen=90, C=2500, d=32, n_b=9, n_c=9, k=30, rounds=1, n_ec=3,
                            window_wrap=False),
     "neighbours_cover_all": scaled("sasrec", seqs=1, seqlen=128, C=1500, n_b=5, n_c=5, k=60, rounds=2, n_ec=2),
+    # one chunk: every window is the whole catalogue of 70001 items, more than a 16-bit
+    # histogram bin can count (the chunk kernel counts in 32 bits); many compactions
+    "window_over_16_bits": scaled("tiny", seqs=1, seqlen=96, C=70001, d=32, n_b=3, n_c=1, k=40, rounds=1),
 }
 
 
