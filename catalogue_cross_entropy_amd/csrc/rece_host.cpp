@@ -995,7 +995,9 @@ static rece_status forward_impl(const rece_plan_s& p, hipStream_t st, const void
     dd.s = s;
     dd.k = c.k;
     dd.rho = rho;
-    dd.hash_bits = p.dedup_bits;
+    // a table sized for this round's earlier ids (rho k): smaller tables for the
+    // early rounds, so more workgroups share a CU (the table size bounds occupancy)
+    dd.hash_bits = p.dedup_bits ? dedup_hash_bits(rho + 1, c.k) : 0;
     RECE_PHASE(RECE_PHASE_LOSS, launch_round_dedup(dd, st), "round dedup");
   }
 
