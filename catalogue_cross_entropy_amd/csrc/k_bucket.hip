@@ -138,12 +138,12 @@ __device__ __forceinline__ int argmax_exact_wave(const E* __restrict__ x, const 
 // fragments of its rows in registers.  The random vectors stream through a
 // ring of three LDS tiles fed by asynchronous copies two tiles ahead, every
 // tile used by all the workgroup's rows (RF > 1 for large inputs: fewer loads
-// of the vectors per row).  Per output element the running best and
-// second-best scores are kept branch-free (the second best is the median of
-// best, second and the new score); equal scores leave best = second, which
-// sends the row to the float64 decision (lowest index among exact ties).
-// 256-byte rows: at least two workgroups per CU, with registers to spare (a
-// spill reload inside the tile loop would wait for every copy in flight).
+// of the vectors per row).  Each lane keeps the running best and second-best
+// scores of its share branch-free, as integer keys (max3 / med3 / max); equal
+// scores leave best = second, which sends the row to the float64 decision
+// (lowest index among exact ties).  256-byte rows: three workgroups per CU,
+// with no spills (a spill reload inside the tile loop would wait for every
+// copy in flight).
 template <class E, int D, int RF>
 __global__ __launch_bounds__(256, (D * sizeof(E) == 256) ? 3 : 1) void k_project_argmax(
     const E* __restrict__ V, int64_t n, const E* __restrict__ Bt, int n_b,
@@ -176,15 +176,16 @@ __global__ __launch_bounds__(256, (D * sizeof(E) == 256) ? 3 : 1) void k_project
   // the low `ib` bits replaced by the vector index.  Non-negative floats order like
   // their bits, so among non-negative scores the keys order as the truncated scores
   // (ties broken by index); negative scores order below every non-negative one.
-  // Per score: one and-or, one max, one med3.
   const int ib = n_b > 1 ? 32 - __builtin_clz((unsigned)(n_b - 1)) : 0;
   const int imask = (1 << ib) - 1;
   // bf16: the products are taken vectors x rows, so a lane's four scores of a block
   // belong to one row (l & 15) and four vectors (4g + v); the running top-2 is one
   // pair of keys per fragment (t1, t2), updated two keys at a time:
   //   top-2 of {t1 >= t2, kA, kB} = (max3(t1, kA, kB), max(t2, med3(t1, kA, kB))).
-  // float32: vectors as columns (one vector, four rows per lane) and a pair of keys
-  // per output element (best1, best2).
+  // Per score: one and-or and, per two scores, one med3, one max3 and half of a
+  // max3.  float32: vectors as columns (one vector, four rows per lane) and a pair
+  // of keys per output element (best1, best2): one and-or, one max, one med3 per
+  // score.
   int t1[RF], t2[RF];
   int best1[RF][4], best2[RF][4];
 #pragma unroll
@@ -199,17 +200,17 @@ __global__ __launch_bounds__(256, (D * sizeof(E) == 256) ? 3 : 1) void k_project
   }
 
   if constexpr (sizeof(E) == 2) {
-    // bf16: every fragment read is this lane's address for its k-step in the tile's
-    // ring slot (one add per k-step and tile) plus the 16-row block as an immediate
-    // offset; only a last tile that passes n_b pads its scores.
+    // bf16: every fragment read is this lane's slot-0 address for its k-step plus
+    // an immediate offset (the ring slot where it is known at compile time, and the
+    // 16-vector block); only a last tile that passes n_b pads its scores.
     constexpr int KS = Frag<E, D>::KS;
     constexpr int NCB = G::TI / 16;
     const int q = l >> 4, n0 = l & 15;
     uint32_t fa0[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) fa0[ks] = lds_addr(ring + n0 * G::RB + (((4 * ks + q) ^ (n0 & G::SWM)) * 16));
-    // this wave's copies of a tile: per-lane source offsets inside the tile's rows,
-    // advanced by whole tiles (tiles that pass n_b take dma_rows, which clamps)
+    // this wave's copies of a tile: a uniform tile address plus this lane's 32-bit
+    // offset inside the tile (tiles that pass n_b take dma_rows, which clamps)
     constexpr int NQ = G::ROW_DMA / NW;
     static_assert(G::ROW_DMA % NW == 0, "whole copies per wave");
     constexpr int LRB = ilog2(G::RB);
@@ -220,12 +221,12 @@ __global__ __launch_bounds__(256, (D * sizeof(E) == 256) ? 3 : 1) void k_project
       goff[qq] = (uint32_t)(byte ^ (((byte >> LRB) & G::SWM) << 4));
     }
     const int nfull_t = n_b / G::TI;   // tiles with no row past n_b
-    // One tile: wait for its copies, meet the other waves, issue the copies of tile
-    // t + 2, then score its NCB blocks of 16 vectors.  SLOT >= 0: the ring slot is
-    // known at compile time, so every fragment read is an immediate offset from
-    // this lane's slot-0 address, and the copies of a full tile t + 2 go out as a
-    // uniform tile address plus this lane's 32-bit offset.  SLOT < 0: the general
-    // form (runtime slot, clamped copies near the end of the vectors).
+    // score: the NCB blocks of 16 vectors of tile t, fragment reads at offset OFF
+    // from the addresses fa.  A tile: wait for its copies, meet the other waves,
+    // issue the copies of tile t + 2, then score.  tile_fixed: the ring slot is
+    // known at compile time (immediate offsets from the slot-0 addresses) and tile
+    // t + 2 is full.  tile: the general form (runtime slot, clamped copies near the
+    // end of the vectors, padded scores in a last partial tile).
     auto score = [&](auto pad_c, auto off_c, const uint32_t* fa, int t) {
       constexpr bool PAD = decltype(pad_c)::value;
       constexpr int OFF = decltype(off_c)::value;
