@@ -152,7 +152,11 @@ __global__ __launch_bounds__(256, (D * sizeof(E) == 256) ? 3 : 1) void k_project
     uint32_t* __restrict__ und_n, uint32_t* __restrict__ counters) {
   using G = TileGeom<E, D>;
   constexpr int NW = 4;
-  __shared__ __attribute__((aligned(1024))) char ring[3 * G::ROW_BYTES];
+  // bf16: a ring of two tiles, copies one tile ahead (16 KB at 256-byte vectors; the
+  // random vectors stay in the L2, so one tile of lead hides their copies, and the
+  // smaller footprint leaves LDS to a kernel running beside this one); float32: three
+  constexpr int RING = sizeof(E) == 2 ? 2 : 3;
+  __shared__ __attribute__((aligned(1024))) char ring[RING * G::ROW_BYTES];
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l = lane_id();
   const int g = l >> 4;
@@ -161,7 +165,7 @@ __global__ __launch_bounds__(256, (D * sizeof(E) == 256) ? 3 : 1) void k_project
   // the first two tiles of vectors are on their way while the rows load; every
   // tile takes the same number of copies from this wave
   dma_rows<E, D, NW>(ring, Bt, 0, n_b, w);
-  if (nt > 1) dma_rows<E, D, NW>(ring + G::ROW_BYTES, Bt, G::TI, n_b, w);
+  if (RING == 3 && nt > 1) dma_rows<E, D, NW>(ring + G::ROW_BYTES, Bt, G::TI, n_b, w);
 
   Frag<E, D> a[RF];
 #pragma unroll
@@ -268,43 +272,39 @@ __global__ __launch_bounds__(256, (D * sizeof(E) == 256) ? 3 : 1) void k_project
         }
       });
     };
-    auto tile_fixed = [&](auto slot_c, int t) {   // t % 3 == SLOT and t + 2 < nfull_t
+    auto tile_fixed = [&](auto slot_c, int t) {   // t % 2 == SLOT and t + 1 < nfull_t
       constexpr int SLOT = decltype(slot_c)::value;
-      wait_vmcnt_c<G::ROW_DMA / NW>();   // only tile t + 1's copies may remain
-      raw_barrier();
-      const char* src = reinterpret_cast<const char*>(Bt) + (int64_t)(t + 2) * G::ROW_BYTES;
-      char* dst = ring + ((SLOT + 2) % 3) * G::ROW_BYTES;
+      wait_vmcnt_c<0>();   // tile t's copies (the only ones outstanding) landed
+      raw_barrier();       // ... for every wave, and every wave is done with slot (t + 1) % 2
+      const char* src = reinterpret_cast<const char*>(Bt) + (int64_t)(t + 1) * G::ROW_BYTES;
+      char* dst = ring + ((SLOT + 1) % 2) * G::ROW_BYTES;
 #pragma unroll
       for (int qq = 0; qq < NQ; ++qq) dma_copy16(src + goff[qq], dst + (w + qq * NW) * 1024);
       score(std::false_type{}, std::integral_constant<int, SLOT * G::ROW_BYTES>{}, fa0, t);
     };
     auto tile = [&](auto pad_c, int t) {
-      if (t + 1 < nt)
-        wait_vmcnt_c<G::ROW_DMA / NW>();   // the fewest copies any wave issues per tile
-      else
-        wait_vmcnt_c<0>();
-      raw_barrier();   // every wave's copies of tile t landed; slot (t+2) % 3 is free
-      const int slot = t % 3;
-      if (t + 2 < nfull_t) {
-        char* dst = ring + (size_t)((t + 2) % 3) * G::ROW_BYTES;
-        const char* src = reinterpret_cast<const char*>(Bt) + (int64_t)(t + 2) * G::ROW_BYTES;
+      wait_vmcnt_c<0>();
+      raw_barrier();   // every wave's copies of tile t landed; slot (t + 1) % 2 is free
+      const int slot = t % 2;
+      if (t + 1 < nfull_t) {
+        char* dst = ring + (size_t)((t + 1) % 2) * G::ROW_BYTES;
+        const char* src = reinterpret_cast<const char*>(Bt) + (int64_t)(t + 1) * G::ROW_BYTES;
 #pragma unroll
         for (int qq = 0; qq < NQ; ++qq) dma_copy16(src + goff[qq], dst + (w + qq * NW) * 1024);
-      } else if (t + 2 < nt) {
-        dma_rows<E, D, NW>(ring + (size_t)((t + 2) % 3) * G::ROW_BYTES, Bt, (int64_t)(t + 2) * G::TI, n_b, w);
+      } else if (t + 1 < nt) {
+        dma_rows<E, D, NW>(ring + (size_t)((t + 1) % 2) * G::ROW_BYTES, Bt, (int64_t)(t + 1) * G::TI, n_b, w);
       }
       uint32_t fa[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) fa[ks] = fa0[ks] + (uint32_t)(slot * G::ROW_BYTES);
       score(pad_c, std::integral_constant<int, 0>{}, fa, t);
     };
-    // tiles [0, tmain) in groups of three ring slots, the rest in the general form
-    const int tmain = nfull_t >= 2 ? (nfull_t - 2) / 3 * 3 : 0;
+    // tiles [0, tmain) in pairs of ring slots, the rest in the general form
+    const int tmain = nfull_t >= 1 ? (nfull_t - 1) / 2 * 2 : 0;
     int t0 = 0;
-    for (; t0 < tmain; t0 += 3) {
+    for (; t0 < tmain; t0 += 2) {
       tile_fixed(std::integral_constant<int, 0>{}, t0);
       tile_fixed(std::integral_constant<int, 1>{}, t0 + 1);
-      tile_fixed(std::integral_constant<int, 2>{}, t0 + 2);
     }
     const int nfull = n_b % G::TI != 0 ? nt - 1 : nt;   // tiles without padding
     for (int t = t0; t < nfull; ++t) tile(std::false_type{}, t);
